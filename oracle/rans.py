@@ -1,0 +1,198 @@
+"""Tile rANS coder (oracle), vectorised across independent chains.
+
+[SUM]: the final coordinates are coded with rANS in independently decodable
+tiles; [ABS]: "entropy-coded in independently decodable tiles".  Parameters
+(pages silent; ours): 32-bit state x in [L, 2^32) with L = 2^16, 16-bit
+words, P = 11 (M = 2048 slots).  Reference: J. Duda, "Asymmetric numeral
+systems" (arXiv 1311.2540), range variant.
+
+Decoding one symbol of table T:
+    slot = x mod M; find s with cum_s <= slot < cum_s + f_s;
+    x <- f_s * floor(x / M) + slot - cum_s;  if x < L: x <- x * 2^16 + next word.
+Decoding b <= 16 raw bits (bypass):
+    r = x mod 2^b;  x <- floor(x / 2^b);      if x < L: x <- x * 2^16 + next word.
+Raw fields wider than 16 bits are two bypasses, low 16 bits first.
+
+The encoder runs the chain's operations in reverse from x = L, emitting a word
+whenever the next step would leave [L, 2^32); its final state is stored and
+the decoder must end at exactly x = L.
+
+Pins (tests): round trip on random tables including escapes and partial
+tiles; final state L; code length within the ideal sum of -log2(f/M) plus the
+per-chain flush bound.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .model import P, M, Model
+
+L = 1 << 16
+WORD = 16
+OPS_PER_COORD = 3     # symbol + up to two bypasses
+
+
+def _ops_for_group(sym, g, i):
+    """Per-op arrays for coordinate i of the groups g (in decoding order)."""
+    ctx = sym["ctx"][g, i]
+    ids = sym["id"][g, i]
+    rv = sym["rawval"][g, i]
+    rb = sym["rawbits"][g, i]
+    lo_b = np.minimum(rb, 16)
+    hi_b = np.maximum(rb - 16, 0)
+    lo_v = rv & 0xFFFF
+    hi_v = rv >> 16
+    return ctx, ids, lo_b, lo_v, hi_b, hi_v
+
+
+def encode_chains(sym, model: Model, chain_groups):
+    """Encode every chain.
+
+    ``chain_groups`` is an (n_chains, steps) int64 array of global group
+    indices in decoding order, -1 where a chain has no more groups.
+    Returns (states uint32[n_chains], list of uint16 word arrays in decoding order).
+    """
+    n_ch, steps = chain_groups.shape
+    x = np.full(n_ch, L, dtype=np.uint64)
+    cap = steps * 8 * OPS_PER_COORD + 1
+    buf = np.zeros((n_ch, cap), dtype=np.uint64)
+    cnt = np.zeros(n_ch, dtype=np.int64)
+    F, CUM = model.F, model.CUM
+
+    def emit(idx, mask):
+        if mask.any():
+            sel = idx[mask]
+            buf[sel, cnt[sel]] = x[sel] & 0xFFFF
+            cnt[sel] += 1
+            x[sel] >>= np.uint64(16)
+
+    def bypass(idx, b, v):
+        act = b > 0
+        if not act.any():
+            return
+        bb = b.astype(np.uint64)
+        lim = np.left_shift(np.uint64(1), np.uint64(32) - bb)
+        emit(idx, act & (x[idx] >= lim))
+        xs = x[idx]
+        x[idx] = np.where(act, np.left_shift(xs, bb) | v.astype(np.uint64), xs)
+
+    for s in range(steps - 1, -1, -1):
+        g = chain_groups[:, s]
+        idx = np.nonzero(g >= 0)[0]
+        if idx.size == 0:
+            continue
+        gg = g[idx]
+        for i in range(7, -1, -1):
+            ctx, ids, lo_b, lo_v, hi_b, hi_v = _ops_for_group(sym, gg, i)
+            bypass(idx, hi_b, hi_v)
+            bypass(idx, lo_b, lo_v)
+            f = F[ctx, ids].astype(np.uint64)
+            cum = CUM[ctx, ids].astype(np.uint64)
+            assert (f > 0).all()
+            emit(idx, x[idx] >= np.left_shift(f, np.uint64(21)))
+            xs = x[idx]
+            x[idx] = (xs // f) * np.uint64(M) + (xs % f) + cum
+    states = x.astype(np.uint32)
+    assert (x < (1 << 32)).all() and (x >= L).all()
+    words = [buf[c, :cnt[c]][::-1].astype(np.uint16) for c in range(n_ch)]
+    return states, words
+
+
+class WordReader:
+    """Per-chain word cursors into the blob stream (forward or backward)."""
+
+    def __init__(self, stream: np.ndarray, start: np.ndarray, step: np.ndarray, lo: np.ndarray, hi: np.ndarray):
+        self.stream = stream
+        self.ptr = start.astype(np.int64).copy()
+        self.step = step.astype(np.int64)
+        self.lo, self.hi = lo, hi     # allowed [lo, hi) per chain
+        self.overrun = np.zeros(len(start), dtype=bool)
+
+    def take(self, idx):
+        p = self.ptr[idx]
+        bad = (p < self.lo[idx]) | (p >= self.hi[idx])
+        self.overrun[idx[bad]] = True
+        pc = np.clip(p, 0, max(len(self.stream) - 1, 0))
+        w = self.stream[pc].astype(np.uint64) if len(self.stream) else np.zeros(len(idx), np.uint64)
+        w[bad] = 0
+        self.ptr[idx] = p + self.step[idx]
+        return w
+
+
+def decode_chains(model: Model, states, chain_groups, reader: WordReader, n_groups: int):
+    """Decode chains; returns (u int64 (n_groups, 8) filled at decoded groups, final x)."""
+    k = model.k
+    K = 1 << k
+    n_ch, steps = chain_groups.shape
+    x = np.asarray(states, dtype=np.uint64).copy()
+    u_out = np.zeros((n_groups, 8), dtype=np.int64)
+    F, CUM, S2I = model.F, model.CUM, model.SLOT2ID
+
+    def renorm(idx):
+        low = x[idx] < L
+        if low.any():
+            sel = idx[low]
+            w = reader.take(sel)
+            x[sel] = (x[sel] << np.uint64(16)) | w
+
+    def bypass(idx, b):
+        r = np.zeros(len(idx), dtype=np.int64)
+        act = b > 0
+        if act.any():
+            sel = idx[act]
+            bb = b[act].astype(np.uint64)
+            r[act] = (x[sel] & ((np.uint64(1) << bb) - np.uint64(1))).astype(np.int64)
+            x[sel] = x[sel] >> bb
+            renorm(sel)
+        return r
+
+    for s in range(steps):
+        g = chain_groups[:, s]
+        idx = np.nonzero(g >= 0)[0]
+        if idx.size == 0:
+            continue
+        c = np.zeros(len(idx), dtype=np.int64)
+        pi = np.zeros(len(idx), dtype=np.int64)
+        urow = np.zeros((len(idx), 8), dtype=np.int64)
+        for i in range(8):
+            if i == 0:
+                ctx = np.zeros(len(idx), dtype=np.int64)
+            elif i < 7:
+                ctx = 1 + c
+            else:
+                ctx = 3 + 2 * c + pi
+            slot = (x[idx] & np.uint64(M - 1)).astype(np.int64)
+            ids = S2I[ctx, slot]
+            f = F[ctx, ids].astype(np.uint64)
+            cum = CUM[ctx, ids].astype(np.uint64)
+            x[idx] = f * (x[idx] >> np.uint64(P)) + slot.astype(np.uint64) - cum
+            renorm(idx)
+            if i == 0:
+                c = ids >> 9
+                sid = ids & 511
+            else:
+                sid = ids
+            msym = sid >> 1
+            neg = sid & 1
+            big = msym >= K
+            e = k + (msym - K) // 4
+            top2 = (msym - K) % 4
+            nb = np.where(big, e - 2 - (1 if i == 7 else 0), 0)
+            lo = bypass(idx, np.minimum(nb, 16))
+            hi = bypass(idx, np.maximum(nb - 16, 0))
+            raw = lo | (hi << 16)
+            if i == 7:
+                rho = np.where(c == 0, pi, pi ^ neg)
+                raw = np.where(big, (raw << 1) | rho, raw)
+            m = np.where(big, (np.int64(1) << np.where(big, e, 0)) | (top2 << np.where(big, e - 2, 0)) | raw, msym)
+            u = (2 * m + c) * np.where(neg == 1, -1, 1)
+            urow[:, i] = u
+            if i < 7:
+                pi = pi ^ np.mod(u >> 1, 2)
+        u_out[g[idx]] = urow
+    return u_out, x
+
+
+def ideal_bits(sym, model: Model) -> float:
+    f = model.F[sym["ctx"], sym["id"]].astype(np.float64)
+    return float(np.sum(P - np.log2(f)) + sym["rawbits"].sum())

@@ -1,0 +1,62 @@
+"""Pins for the oracle's tile rANS coder: round trip (escapes, partial tiles,
+every chain count), final state L, and code length near the ideal."""
+import numpy as np
+import pytest
+
+from oracle import model as mdl
+from oracle import rans
+from oracle.codec import chain_layout, _layout_regions, Blob, chain_readers
+from oracle.e8 import e8_nearest_doubled
+
+
+def _random_points(n, scale, seed, heavy=False):
+    rng = np.random.default_rng(seed)
+    y = rng.standard_normal((n, 8)) * scale
+    if heavy:
+        # heavy tails: force escapes with wide raw fields (up to ~2^28)
+        idx = rng.random(n) < 0.05
+        y[idx] *= 2.0 ** rng.integers(4, 20, size=(idx.sum(), 1))
+    return e8_nearest_doubled(y)
+
+
+@pytest.mark.parametrize("S,n_groups,scale,k,heavy", [
+    (1, 700, 2.0, 3, False),
+    (2, 1100, 6.0, 4, True),
+    (4, 1536, 30.0, 5, True),
+    (8, 2048 + 77, 3.0, 4, True),
+    (8, 9, 1.0, 3, False),          # fewer groups than chains: empty chains
+    (64, 1024 + 5, 200.0, 7, True),
+])
+def test_round_trip(S, n_groups, scale, k, heavy):
+    u = _random_points(n_groups, scale, seed=S * 1000 + n_groups, heavy=heavy)
+    sym = mdl.group_symbols(u, k)
+    model = mdl.build_model(k, *mdl.count_symbols(sym, mdl.n_msym(k)))
+    n_tiles, cg = chain_layout(n_groups, S)
+    states, words = rans.encode_chains(sym, model, cg)
+    rl, stream, ck = _layout_regions(words, n_tiles * S)
+    b = Blob(1, S, k, 0, 1, 8 * n_groups, np.float32(1), n_tiles, np.zeros(1, np.uint16), model,
+             model.to_bytes(), ck, rl, states, stream)
+    reader = chain_readers(b)
+    u2, xend = rans.decode_chains(model, states, cg, reader, n_groups)
+    assert np.array_equal(u2, u)
+    assert (xend == rans.L).all()
+    assert not reader.overrun.any()
+    # code length: 16 W bits within the ideal plus a per-symbol slack of 0.06 bit
+    # and one 16-bit flush per chain (the final state carries the rest)
+    n_ops = sym["ctx"].size + int((sym["rawbits"] > 0).sum()) + int((sym["rawbits"] > 16).sum())
+    total_words = sum(len(w) for w in words)
+    assert 16 * total_words <= rans.ideal_bits(sym, model) + 0.06 * n_ops + 16 * len(words)
+
+
+def test_state_range_and_word_counts():
+    u = _random_points(4096, 4.0, seed=5)
+    k = 4
+    sym = mdl.group_symbols(u, k)
+    model = mdl.build_model(k, *mdl.count_symbols(sym, mdl.n_msym(k)))
+    _, cg = chain_layout(4096, 8)
+    states, words = rans.encode_chains(sym, model, cg)
+    assert (states >= rans.L).all()
+    # on typical data the coder loses well under 0.01 bit per symbol
+    n_sym = sym["ctx"].size
+    excess = 16 * sum(len(w) for w in words) + 32 * len(words) - rans.ideal_bits(sym, model)
+    assert excess / n_sym < 0.05 + 40 * len(words) / n_sym
