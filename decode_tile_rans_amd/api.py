@@ -1,0 +1,181 @@
+"""High-level Python API over the C ABI ([README] 快速开始: compress / decompress /
+CompressedLinear.from_linear; [NEWS]: results stored through state_dict).
+
+Marshalling only: tensors are handed to the library as raw pointers; torch
+provides device memory and the current HIP stream.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as L
+from ._lib import EPError
+
+_TORCH_TO_EP = {torch.bfloat16: L.EP_BF16, torch.float16: L.EP_FP16, torch.float32: L.EP_FP32,
+                torch.float8_e4m3fn: L.EP_FP8_E4M3FN, torch.int8: L.EP_INT8}
+_EP_TO_TORCH = {v: k for k, v in _TORCH_TO_EP.items()}
+
+
+def _stream_ptr(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+class Compressed:
+    """A compressed 2-D tensor (owns an ep_blob: host bytes + device copy)."""
+
+    def __init__(self, handle: int):
+        self._h = handle
+        self.shape = L.ep_blob_shape(handle)
+        self.ep_dtype = L.ep_blob_dtype(handle)
+        self.dtype = _EP_TO_TORCH[self.ep_dtype]
+        self.chains_per_tile, self.k_log2, self.flags = L.ep_blob_params(handle)
+
+    @property
+    def handle(self) -> int:
+        return self._h
+
+    @property
+    def actual_bpp(self) -> float:
+        """Stored bits per parameter including all metadata ([README] 快速开始)."""
+        return L.ep_actual_bpp(self._h)
+
+    @property
+    def nbytes(self) -> int:
+        return L.ep_serialized_size(self._h)
+
+    def to_bytes(self) -> bytes:
+        return L.ep_serialize(self._h)
+
+    @classmethod
+    def from_bytes(cls, data: bytes) -> "Compressed":
+        return cls(L.ep_deserialize(bytes(data)))
+
+    def upload(self, stream=None):
+        L.ep_blob_upload(self._h, _stream_ptr(stream))
+        return self
+
+    def device_errors(self) -> int:
+        return L.ep_blob_device_errors(self._h)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            try:
+                L.ep_blob_free(h)
+            except Exception:
+                pass
+
+
+def compress(x, target_bpp: float, dtype=None, chains_per_tile: int = 0) -> Compressed:
+    """Compress a 2-D tensor (torch on any device, or numpy with ``dtype`` = torch dtype)."""
+    if isinstance(x, np.ndarray):
+        if dtype is None:
+            raise ValueError("numpy input needs dtype= (a torch dtype)")
+        host = np.ascontiguousarray(x)
+        ep_dt = _TORCH_TO_EP[dtype]
+        ptr = host.ctypes.data
+    else:
+        if x.dim() != 2:
+            raise EPError(-4, "lossy compression takes 2-D tensors only")
+        if x.dtype not in _TORCH_TO_EP:
+            raise EPError(-3, f"unsupported dtype {x.dtype}")
+        host = x.detach().to("cpu").contiguous()
+        ep_dt = _TORCH_TO_EP[x.dtype]
+        ptr = host.data_ptr()
+    if len(host.shape) != 2:
+        raise EPError(-4, "lossy compression takes 2-D tensors only")
+    h = L.ep_compress(ptr, ep_dt, host.shape[0], host.shape[1], float(target_bpp), chains_per_tile)
+    return Compressed(h)
+
+
+def decompress(c: Compressed, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode on the current GPU into a new (or given) tensor of the original shape/dtype."""
+    c.upload(stream)
+    if out is None:
+        out = torch.empty(c.shape, dtype=c.dtype, device="cuda")
+    L.ep_decompress(c.handle, out.data_ptr(), _stream_ptr(stream))
+    return out
+
+
+def decompress_batch(cs, outs=None, stream=None):
+    for c in cs:
+        c.upload(stream)
+    if outs is None:
+        outs = [torch.empty(c.shape, dtype=c.dtype, device="cuda") for c in cs]
+    L.ep_decompress_batch([c.handle for c in cs], [o.data_ptr() for o in outs], _stream_ptr(stream))
+    return outs
+
+
+def gemm_bf16_nt(x: torch.Tensor, w: torch.Tensor, bias=None, out=None, stream=None) -> torch.Tensor:
+    T, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    L.ep_gemm_bf16_nt(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
+                      out.data_ptr(), T, N, K, _stream_ptr(stream))
+    return out
+
+
+def gemm_fp8_nt(xq: torch.Tensor, wq: torch.Tensor, a_x: float, a_w: torch.Tensor, out=None, stream=None):
+    T, K = xq.shape
+    N = wq.shape[0]
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=xq.device)
+    L.ep_gemm_fp8_nt(xq.data_ptr(), wq.data_ptr(), float(a_x), a_w.data_ptr(), out.data_ptr(), T, N, K,
+                     _stream_ptr(stream))
+    return out
+
+
+class CompressedLinear(torch.nn.Module):
+    """Drop-in replacement of a BF16 ``torch.nn.Linear`` whose weight is stored compressed.
+
+    forward(x) decodes the weight into a workspace and runs the MFMA GEMM
+    (ep_compressed_linear_forward).  The compressed bytes live in the
+    ``packed`` buffer so they travel with ``state_dict``.
+    """
+
+    def __init__(self, c: Compressed, bias: torch.Tensor | None = None):
+        super().__init__()
+        self._c = c
+        self.out_features, self.in_features = c.shape
+        self.register_buffer("packed", torch.frombuffer(bytearray(c.to_bytes()), dtype=torch.uint8))
+        self.register_buffer("bias", bias)
+        self._ws = None
+
+    @classmethod
+    def from_linear(cls, linear: torch.nn.Linear, target_bpp: float = 4.0, chains_per_tile: int = 0):
+        w = linear.weight.detach()
+        if w.dtype != torch.bfloat16:
+            w = w.to(torch.bfloat16)
+        c = compress(w, target_bpp, chains_per_tile=chains_per_tile)
+        b = None
+        if linear.bias is not None:
+            b = linear.bias.detach().to(torch.bfloat16).to(linear.weight.device)
+        return cls(c, b)
+
+    @property
+    def compressed_bits(self) -> float:
+        return self._c.actual_bpp
+
+    def _load_from_state_dict(self, state_dict, prefix, *args, **kwargs):
+        super()._load_from_state_dict(state_dict, prefix, *args, **kwargs)
+        key = prefix + "packed"
+        if key in state_dict:
+            self._c = Compressed.from_bytes(state_dict[key].cpu().numpy().tobytes())
+            self.out_features, self.in_features = self._c.shape
+            self._ws = None
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, self.in_features).to(torch.bfloat16).contiguous()
+        self._c.upload()
+        need = L.ep_linear_workspace_bytes(self._c.handle)
+        if self._ws is None or self._ws.numel() < need or self._ws.device != x2.device:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=x2.device)
+        y = torch.empty((x2.shape[0], self.out_features), dtype=torch.bfloat16, device=x2.device)
+        b = self.bias.data_ptr() if self.bias is not None else None
+        L.ep_compressed_linear_forward(self._c.handle, x2.data_ptr(), x2.shape[0], b, y.data_ptr(),
+                                       self._ws.data_ptr(), need, _stream_ptr())
+        return y.reshape(*lead, self.out_features)

@@ -1,0 +1,182 @@
+// Blob v1 parsing / validation and the host-only C ABI entry points.
+//
+// Layout (little-endian, packed; this project's format — the pages only say the
+// stream is tile-wise rANS and that actual_bpp counts metadata, [README] 快速开始):
+//   header 48 B | bf16 row scales[R] | model | u32 checkpoints[n_blocks] |
+//   u16 region lengths[ceil(n_chains/2)] | u32 states[n_chains] | u16 stream[n_words]
+#include <cmath>
+
+#include "ep_internal.h"
+
+namespace ep {
+
+const char* last_error_cstr();
+int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_req, std::vector<uint8_t>* out);
+
+namespace {
+template <class T>
+T rd(const std::vector<uint8_t>& b, size_t off) {
+  T v;
+  std::memcpy(&v, &b[off], sizeof(T));
+  return v;
+}
+}  // namespace
+
+int parse_blob(std::vector<uint8_t>&& bytes, Blob* out) {
+  Blob& b = *out;
+  b.bytes = std::move(bytes);
+  const auto& by = b.bytes;
+  if (by.size() < (size_t)kHeaderBytes) return fail(EP_E_CORRUPT, "blob truncated");
+  if (std::memcmp(&by[0], "EPK1", 4) != 0) return fail(EP_E_CORRUPT, "bad magic");
+  if (rd<uint16_t>(by, 4) != 1) return fail(EP_E_CORRUPT, "unsupported version");
+  b.dtype = by[6];
+  int P = by[7];
+  b.S = by[8];
+  b.k = by[9];
+  b.flags = by[10];
+  int tl = by[11];
+  b.R = rd<uint32_t>(by, 12);
+  b.C = rd<uint32_t>(by, 16);
+  b.delta = rd<float>(by, 20);
+  b.n_tiles = rd<uint32_t>(by, 24);
+  b.n_blocks = rd<uint32_t>(by, 28);
+  b.n_words = rd<uint64_t>(by, 32);
+  b.model_bytes = rd<uint32_t>(by, 40);
+  if (P != kP || tl != 12 || rd<uint32_t>(by, 44) != 0) return fail(EP_E_CORRUPT, "bad header constants");
+  if (b.dtype < EP_BF16 || b.dtype > EP_INT8) return fail(EP_E_CORRUPT, "bad dtype");
+  if (b.S < 1 || b.S > 64 || (b.S & (b.S - 1))) return fail(EP_E_CORRUPT, "bad chains per tile");
+  if (b.k < 3 || b.k > 7 || b.flags > 3) return fail(EP_E_CORRUPT, "bad header fields");
+  if (b.R < 1 || b.C < 1) return fail(EP_E_CORRUPT, "bad shape");
+  if (!(std::isfinite(b.delta) && b.delta > 0.f)) return fail(EP_E_CORRUPT, "bad resolution");
+  const int64_t ng = b.n_groups();
+  if (b.n_tiles != std::max<int64_t>(1, (ng + kTileGroups - 1) / kTileGroups)) return fail(EP_E_CORRUPT, "bad tile count");
+  b.n_chains = b.n_tiles * b.S;
+  if (b.n_blocks != (b.n_chains + kBlockChains - 1) / kBlockChains) return fail(EP_E_CORRUPT, "bad block count");
+  b.n_regions = (b.n_chains + 1) / 2;
+  b.off_scales = kHeaderBytes;
+  b.off_model = b.off_scales + 2 * (size_t)b.R;
+  b.off_ckpt = b.off_model + b.model_bytes;
+  b.off_rlen = b.off_ckpt + 4 * (size_t)b.n_blocks;
+  b.off_states = b.off_rlen + 2 * (size_t)b.n_regions;
+  b.off_stream = b.off_states + 4 * (size_t)b.n_chains;
+  if (b.n_words > (uint64_t)1 << 40 || by.size() != b.off_stream + 2 * (size_t)b.n_words)
+    return fail(EP_E_CORRUPT, "blob size mismatch");
+  for (int64_t r = 0; r < b.R; ++r) {
+    uint16_t s = rd<uint16_t>(by, b.off_scales + 2 * (size_t)r);
+    if ((s & 0x8000) || ((s >> 7) & 0xFF) == 0xFF) return fail(EP_E_CORRUPT, "bad row scale");
+  }
+  std::string err;
+  if (!Model::from_bytes(&by[b.off_model], b.model_bytes, b.k, &b.model, &err)) return fail(EP_E_CORRUPT, err);
+  uint64_t pos = 0;
+  b.max_span_words = 0;
+  uint64_t blk_start = 0;
+  for (int64_t r = 0; r < b.n_regions; ++r) {
+    if (r % (kBlockChains / 2) == 0) {
+      int64_t blk = r / (kBlockChains / 2);
+      if (rd<uint32_t>(by, b.off_ckpt + 4 * (size_t)blk) != pos) return fail(EP_E_CORRUPT, "checkpoint mismatch");
+      if (blk > 0) b.max_span_words = std::max<uint32_t>(b.max_span_words, (uint32_t)(pos - blk_start));
+      blk_start = pos;
+    }
+    uint16_t l = rd<uint16_t>(by, b.off_rlen + 2 * (size_t)r);
+    if (l & 1) return fail(EP_E_CORRUPT, "odd region length");
+    pos += l;
+  }
+  b.max_span_words = std::max<uint32_t>(b.max_span_words, (uint32_t)(pos - blk_start));
+  if (pos != b.n_words) return fail(EP_E_CORRUPT, "region lengths do not cover the stream");
+  if (pos > 0xFFFFFFFFull) return fail(EP_E_CORRUPT, "stream too long");
+  for (int64_t c = 0; c < b.n_chains; ++c)
+    if (rd<uint32_t>(by, b.off_states + 4 * (size_t)c) < kL) return fail(EP_E_CORRUPT, "state below L");
+  return EP_OK;
+}
+
+void half_scales(const Blob& b, float* hr) {
+  for (int64_t r = 0; r < b.R; ++r) {
+    uint16_t s;
+    std::memcpy(&s, &b.bytes[b.off_scales + 2 * (size_t)r], 2);
+    hr[r] = bf16_to_f32(s) * b.delta;
+  }
+}
+
+}  // namespace ep
+
+using namespace ep;
+
+void ep_device_release(ep::Blob* b);   // decode.hip
+
+extern "C" {
+
+int ep_compress_ex(const void* src, int dtype, int64_t rows, int64_t cols, double target_bpp, int S,
+                   ep_blob** out) {
+  set_error("");
+  if (!out) return fail(EP_E_ARG, "null output pointer");
+  *out = nullptr;
+  std::vector<uint8_t> bytes;
+  int rc = ep::compress(src, dtype, rows, cols, target_bpp, S, &bytes);
+  if (rc) return rc;
+  ep_blob* blob = new (std::nothrow) ep_blob();
+  if (!blob) return fail(EP_E_NOMEM, "out of host memory");
+  rc = parse_blob(std::move(bytes), &blob->b);
+  if (rc) {
+    delete blob;
+    return rc;
+  }
+  *out = blob;
+  return EP_OK;
+}
+
+int ep_compress(const void* src, int dtype, int64_t rows, int64_t cols, double target_bpp, ep_blob** out) {
+  return ep_compress_ex(src, dtype, rows, cols, target_bpp, 0, out);
+}
+
+int ep_deserialize(const void* src, size_t size, ep_blob** out) {
+  set_error("");
+  if (!out || (!src && size)) return fail(EP_E_ARG, "null pointer");
+  *out = nullptr;
+  ep_blob* blob = new (std::nothrow) ep_blob();
+  if (!blob) return fail(EP_E_NOMEM, "out of host memory");
+  std::vector<uint8_t> bytes((const uint8_t*)src, (const uint8_t*)src + size);
+  int rc = parse_blob(std::move(bytes), &blob->b);
+  if (rc) {
+    delete blob;
+    return rc;
+  }
+  *out = blob;
+  return EP_OK;
+}
+
+size_t ep_serialized_size(const ep_blob* blob) { return blob ? blob->b.bytes.size() : 0; }
+
+int ep_serialize(const ep_blob* blob, void* dst, size_t cap) {
+  if (!blob || !dst) return fail(EP_E_ARG, "null pointer");
+  if (cap < blob->b.bytes.size()) return fail(EP_E_ARG, "destination too small");
+  std::memcpy(dst, blob->b.bytes.data(), blob->b.bytes.size());
+  return EP_OK;
+}
+
+double ep_actual_bpp(const ep_blob* blob) {
+  if (!blob) return 0.0;
+  return 8.0 * (double)blob->b.bytes.size() / ((double)blob->b.R * (double)blob->b.C);
+}
+
+void ep_blob_shape(const ep_blob* blob, int64_t* rows, int64_t* cols) {
+  if (rows) *rows = blob ? blob->b.R : 0;
+  if (cols) *cols = blob ? blob->b.C : 0;
+}
+
+int ep_blob_dtype(const ep_blob* blob) { return blob ? blob->b.dtype : 0; }
+
+void ep_blob_params(const ep_blob* blob, int* S, int* k, int* flags) {
+  if (S) *S = blob ? blob->b.S : 0;
+  if (k) *k = blob ? blob->b.k : 0;
+  if (flags) *flags = blob ? blob->b.flags : 0;
+}
+
+void ep_blob_free(ep_blob* blob) {
+  if (!blob) return;
+  ep_device_release(&blob->b);
+  delete blob;
+}
+
+const char* ep_last_error(void) { return ep::last_error_cstr(); }
+
+}  // extern "C"

@@ -1,0 +1,627 @@
+// Host encoder: ep_compress.
+//
+// Steps ([ABS]: row-normalised E8 quantisation, conditional model, sampled rate
+// selection, tile entropy coding; [README] 快速开始: target_bpp in [0.001, 11],
+// actual_bpp includes metadata; [NEWS]: 2-D tensors only):
+//   1. validate; widen the container values to double
+//   2. row scale s_r = BF16(fl32(sqrt(sum_c w^2 / C))), sum left to right
+//   3. resolution: half-step delta (float32) found by bracketing over powers of two and
+//      bisecting the float32 bit pattern, each probe estimating the sample's code
+//      length with the sample's own tables (no full encode per probe)
+//   4. quantise every 8-wide group: y = w / (2 h_r), h_r = fl32(s_r delta); nearest E8
+//      point (Conway & Sloane 1982 decoder), doubled coordinates u = 2p
+//   5. model from the full-data symbol counts; 6. rANS-encode every chain; 7. pack.
+// Determinism: float64 arithmetic without contraction (this file is built with
+// -ffp-contract=off), fixed summation orders, integer rate estimates, per-thread
+// partial results merged in a fixed order.
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <thread>
+
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+int num_threads() {
+  int n = (int)std::thread::hardware_concurrency();
+  if (n < 1) n = 1;
+  if (const char* e = std::getenv("EP_NUM_THREADS")) {
+    int v = std::atoi(e);
+    if (v >= 1) n = std::min(n, v);
+  }
+  return std::min(n, 64);
+}
+
+template <class Fn>
+void parallel_for(int64_t n, Fn fn, int64_t min_chunk = 1) {
+  int nt = num_threads();
+  if (n <= 0) return;
+  int64_t chunks = std::min<int64_t>(nt, (n + min_chunk - 1) / min_chunk);
+  if (chunks <= 1) {
+    fn(0, n, 0);
+    return;
+  }
+  std::vector<std::thread> th;
+  for (int64_t t = 0; t < chunks; ++t) {
+    int64_t b = n * t / chunks, e = n * (t + 1) / chunks;
+    th.emplace_back([=, &fn] { fn(b, e, (int)t); });
+  }
+  for (auto& x : th) x.join();
+}
+
+// ------------------------------------------------------------------ containers
+double fp8_e4m3fn_value(uint8_t b) {
+  int e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 0) v = std::ldexp(m / 8.0, -6);
+  else v = std::ldexp(1.0 + m / 8.0, e - 7);
+  if (e == 15 && m == 7) v = NAN;
+  return (b & 0x80) ? -v : v;
+}
+
+double fp16_value(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0) v = std::ldexp((double)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = std::ldexp(1.0 + m / 1024.0, e - 15);
+  return s ? -v : v;
+}
+
+void widen(const void* src, int dtype, int64_t n, double* out) {
+  switch (dtype) {
+    case EP_BF16: {
+      auto p = (const uint16_t*)src;
+      for (int64_t i = 0; i < n; ++i) out[i] = (double)bf16_to_f32(p[i]);
+      break;
+    }
+    case EP_FP16: {
+      auto p = (const uint16_t*)src;
+      for (int64_t i = 0; i < n; ++i) out[i] = fp16_value(p[i]);
+      break;
+    }
+    case EP_FP32: {
+      auto p = (const float*)src;
+      for (int64_t i = 0; i < n; ++i) out[i] = (double)p[i];
+      break;
+    }
+    case EP_FP8_E4M3FN: {
+      auto p = (const uint8_t*)src;
+      for (int64_t i = 0; i < n; ++i) out[i] = fp8_e4m3fn_value(p[i]);
+      break;
+    }
+    case EP_INT8: {
+      auto p = (const int8_t*)src;
+      for (int64_t i = 0; i < n; ++i) out[i] = (double)p[i];
+      break;
+    }
+  }
+}
+
+double container_max(int dtype) {
+  switch (dtype) {
+    case EP_BF16: return (double)bf16_to_f32(0x7F7F);
+    case EP_FP16: return 65504.0;
+    case EP_FP8_E4M3FN: return 448.0;
+    case EP_INT8: return 127.0;
+    default: return 3.4028234663852886e38;
+  }
+}
+
+// ------------------------------------------------------------------ E8
+inline void d8_nearest(const double* v, double* f) {
+  double s = 0.0;
+  for (int i = 0; i < 8; ++i) {
+    f[i] = std::nearbyint(v[i]);
+    s += f[i];
+  }
+  if (std::fmod(s, 2.0) != 0.0) {
+    int best = 0;
+    double be = std::fabs(v[0] - f[0]);
+    for (int i = 1; i < 8; ++i) {
+      double e = std::fabs(v[i] - f[i]);
+      if (e > be) {
+        be = e;
+        best = i;
+      }
+    }
+    f[best] += (v[best] - f[best] >= 0.0) ? 1.0 : -1.0;
+  }
+}
+
+inline void e8_doubled(const double* y, int32_t* u) {
+  double p0[8], p1[8], ym[8];
+  d8_nearest(y, p0);
+  for (int i = 0; i < 8; ++i) ym[i] = y[i] - 0.5;
+  d8_nearest(ym, p1);
+  for (int i = 0; i < 8; ++i) p1[i] += 0.5;
+  double t = y[0] - p0[0];
+  double d0 = t * t;
+  for (int i = 1; i < 8; ++i) {
+    t = y[i] - p0[i];
+    d0 = d0 + t * t;
+  }
+  t = y[0] - p1[0];
+  double d1 = t * t;
+  for (int i = 1; i < 8; ++i) {
+    t = y[i] - p1[i];
+    d1 = d1 + t * t;
+  }
+  const double* p = (d1 < d0) ? p1 : p0;
+  for (int i = 0; i < 8; ++i) u[i] = (int32_t)(2.0 * p[i]);
+}
+
+// ------------------------------------------------------------------ symbols
+struct Sym {
+  int ctx, id, rawbits;
+  uint32_t rawval;
+};
+
+inline int ilog2(uint32_t v) { return 31 - __builtin_clz(v); }
+
+// u -> 8 coded symbols in decoding order; returns coset; msym[] for counting.
+inline int symbolize(const int32_t* u, int k, Sym* s, int* msym) {
+  const int K = 1 << k;
+  int c = u[0] & 1;
+  int q_sum = 0;
+  int neg[8], raw_rb[8];
+  uint32_t raw[8];
+  for (int i = 0; i < 8; ++i) {
+    int a = u[i] < 0 ? -u[i] : u[i];
+    uint32_t m = (uint32_t)((a - c) >> 1);
+    neg[i] = u[i] < 0;
+    if ((int64_t)m < K) {
+      msym[i] = (int)m;
+      raw[i] = 0;
+      raw_rb[i] = 0;
+    } else {
+      int e = ilog2(m);
+      int top2 = (m >> (e - 2)) & 3;
+      msym[i] = K + 4 * (e - k) + top2;
+      raw[i] = m & ((1u << (e - 2)) - 1u);
+      raw_rb[i] = e - 2;
+    }
+    if (i < 7) q_sum += (u[i] >> 1);
+  }
+  int pi = q_sum & 1;
+  for (int i = 0; i < 8; ++i) {
+    int sid = 2 * msym[i] + neg[i];
+    s[i].ctx = i == 0 ? 0 : (i < 7 ? 1 + c : 3 + 2 * c + pi);
+    s[i].id = i == 0 ? 512 * c + sid : sid;
+    s[i].rawval = raw[i];
+    s[i].rawbits = raw_rb[i];
+  }
+  if (msym[7] >= K) {           // the low raw bit of the last coordinate is implied
+    s[7].rawval >>= 1;
+    s[7].rawbits -= 1;
+  }
+  return c;
+}
+
+// ------------------------------------------------------------------ row geometry
+struct Matrix {
+  int64_t R, C, G;             // G = groups per row
+  std::vector<double> w;       // R x C
+  std::vector<uint16_t> s_bits;
+  std::vector<float> s;
+  std::vector<double> amax;
+};
+
+inline float f32_from_bits(uint32_t b) {
+  float f;
+  std::memcpy(&f, &b, 4);
+  return f;
+}
+inline uint32_t f32_bits(float f) {
+  uint32_t b;
+  std::memcpy(&b, &f, 4);
+  return b;
+}
+
+// Quantise row r into groups (G x 8 doubled coordinates).
+void quantize_row(const Matrix& mx, int64_t r, float delta, int32_t* u_out) {
+  float h = mx.s[r] * delta;
+  double den = 2.0 * (double)h;
+  const double* wr = &mx.w[r * mx.C];
+  double y[8];
+  for (int64_t g = 0; g < mx.G; ++g) {
+    for (int i = 0; i < 8; ++i) {
+      int64_t col = g * 8 + i;
+      double v = col < mx.C ? wr[col] : 0.0;
+      y[i] = (den != 0.0) ? v / den : 0.0;
+    }
+    e8_doubled(y, u_out + g * 8);
+  }
+}
+
+bool admissible(const Matrix& mx, float delta) {
+  for (int64_t r = 0; r < mx.R; ++r) {
+    if (!(mx.s[r] > 0.f)) continue;
+    float h = mx.s[r] * delta;
+    if (!(h > 0.f) || !std::isfinite(h)) return false;
+    if (!(mx.amax[r] / (2.0 * (double)h) < 536870912.0)) return false;
+  }
+  return true;
+}
+
+struct Estimate {
+  int64_t est;
+  int k;
+};
+
+// est(delta) over the sample rows.
+Estimate estimate(const Matrix& mx, const std::vector<int64_t>& rows, float delta) {
+  const int64_t G = mx.G;
+  const int64_t ng = (int64_t)rows.size() * G;
+  std::vector<int32_t> u((size_t)ng * 8);
+  parallel_for((int64_t)rows.size(), [&](int64_t b, int64_t e, int) {
+    for (int64_t i = b; i < e; ++i) quantize_row(mx, rows[i], delta, &u[(size_t)(i * G * 8)]);
+  }, 8);
+  // choose k: smallest k with #(m >= 2^k) * 1024 <= #coords
+  int64_t ge[8] = {0};
+  for (int64_t gi = 0; gi < ng; ++gi) {
+    const int32_t* ug = &u[gi * 8];
+    int c = ug[0] & 1;
+    for (int i = 0; i < 8; ++i) {
+      int a = ug[i] < 0 ? -ug[i] : ug[i];
+      int64_t m = (a - c) >> 1;
+      for (int kk = 3; kk <= 7; ++kk) ge[kk] += m >= (1 << kk);
+    }
+  }
+  int k = 7;
+  for (int kk = 3; kk <= 7; ++kk)
+    if (ge[kk] * 1024 <= ng * 8) {
+      k = kk;
+      break;
+    }
+  const int nm = n_msym(k);
+  int64_t cc[2] = {0, 0};
+  std::vector<int64_t> mag0(nm, 0), mag1(nm, 0);
+  Sym s[8];
+  int ms[8];
+  for (int64_t gi = 0; gi < ng; ++gi) {
+    int c = symbolize(&u[gi * 8], k, s, ms);
+    cc[c]++;
+    auto& mg = c ? mag1 : mag0;
+    for (int i = 0; i < 8; ++i) mg[ms[i]]++;
+  }
+  Model m = build_model(k, cc, mag0.data(), mag1.data());
+  const int32_t* lq = log2q_table();
+  int64_t est = 0;
+  for (int64_t gi = 0; gi < ng; ++gi) {
+    symbolize(&u[gi * 8], k, s, ms);
+    for (int i = 0; i < 8; ++i) {
+      int32_t f = m.F[s[i].ctx][s[i].id];
+      est += (int64_t)kP * 65536 - lq[f];
+      est += (int64_t)65536 * s[i].rawbits;
+    }
+  }
+  return {est, k};
+}
+
+// ------------------------------------------------------------------ rANS encoder
+struct ChainOut {
+  std::vector<uint16_t> words;   // decoding order
+  uint32_t state;
+};
+
+void encode_chain(const int32_t* u_all, const Model& m, int64_t t, int j, int S, int64_t n_groups,
+                  ChainOut* out) {
+  int64_t gt = std::min<int64_t>(kTileGroups, n_groups - (int64_t)kTileGroups * t);
+  int ngr = gt > j ? (int)((gt - j + S - 1) / S) : 0;
+  uint64_t x = kL;
+  std::vector<uint16_t>& w = out->words;
+  w.clear();
+  auto emit = [&]() {
+    w.push_back((uint16_t)(x & 0xFFFFu));
+    x >>= 16;
+  };
+  auto bypass = [&](uint32_t v, int b) {
+    if (x >= (1ull << (32 - b))) emit();
+    x = (x << b) | v;
+  };
+  Sym s[8];
+  int ms[8];
+  for (int kk = ngr - 1; kk >= 0; --kk) {
+    int64_t g = (int64_t)kTileGroups * t + j + (int64_t)kk * S;
+    symbolize(u_all + g * 8, m.k, s, ms);
+    for (int i = 7; i >= 0; --i) {
+      int rb = s[i].rawbits;
+      if (rb > 16) bypass(s[i].rawval >> 16, rb - 16);
+      if (rb > 0) bypass(s[i].rawval & 0xFFFFu, std::min(rb, 16));
+      uint64_t f = (uint64_t)m.F[s[i].ctx][s[i].id];
+      uint64_t cum = (uint64_t)m.CUM[s[i].ctx][s[i].id];
+      if (x >= (f << 21)) emit();
+      x = (x / f) * (uint64_t)kM + (x % f) + cum;
+    }
+  }
+  std::reverse(w.begin(), w.end());
+  out->state = (uint32_t)x;
+}
+
+void put_u16(std::vector<uint8_t>& b, size_t off, uint16_t v) { std::memcpy(&b[off], &v, 2); }
+void put_u32(std::vector<uint8_t>& b, size_t off, uint32_t v) { std::memcpy(&b[off], &v, 4); }
+void put_u64(std::vector<uint8_t>& b, size_t off, uint64_t v) { std::memcpy(&b[off], &v, 8); }
+
+}  // namespace
+
+int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_req,
+             std::vector<uint8_t>* out) {
+  if (!src || !out) return fail(EP_E_ARG, "null pointer");
+  if (dtype < EP_BF16 || dtype > EP_INT8) return fail(EP_E_DTYPE, "unsupported dtype");
+  if (R < 1 || C < 1) return fail(EP_E_ARG, "rows and cols must be >= 1");
+  if (R > 0xFFFFFFFFll || C > 0xFFFFFFFFll) return fail(EP_E_ARG, "rows/cols exceed 2^32-1");
+  if (!std::isfinite(t) || t < 0.001 || t > 11.0)
+    return fail(EP_E_RANGE, "target_bpp must be finite and in [0.001, 11]");
+  if ((dtype == EP_FP8_E4M3FN || dtype == EP_INT8) && t > 8.0)
+    return fail(EP_E_RANGE, "target_bpp above 8 for an 8-bit container");
+  if (S_req != 0 && S_req != 1 && S_req != 2 && S_req != 4 && S_req != 8 && S_req != 16 &&
+      S_req != 32 && S_req != 64)
+    return fail(EP_E_ARG, "chains_per_tile must be 0 or a power of two <= 64");
+
+  Matrix mx;
+  mx.R = R;
+  mx.C = C;
+  mx.G = (C + 7) / 8;
+  const int64_t N = R * C;
+  try {
+    mx.w.resize((size_t)N);
+  } catch (...) {
+    return fail(EP_E_NOMEM, "out of host memory");
+  }
+  parallel_for(R, [&](int64_t b, int64_t e, int) {
+    size_t esz = dtype == EP_FP32 ? 4 : (dtype == EP_BF16 || dtype == EP_FP16 ? 2 : 1);
+    widen((const uint8_t*)src + (size_t)(b * C) * esz, dtype, (e - b) * C, &mx.w[(size_t)(b * C)]);
+  }, 64);
+  std::atomic<bool> nonfinite{false};
+  mx.s_bits.resize(R);
+  mx.s.resize(R);
+  mx.amax.resize(R);
+  std::atomic<bool> tiny{false};
+  parallel_for(R, [&](int64_t b, int64_t e, int) {
+    for (int64_t r = b; r < e; ++r) {
+      const double* wr = &mx.w[(size_t)(r * C)];
+      double acc = 0.0, am = 0.0;
+      bool live = false;
+      for (int64_t c = 0; c < C; ++c) {
+        double v = wr[c];
+        if (!std::isfinite(v)) nonfinite = true;
+        acc = acc + v * v;
+        double a = std::fabs(v);
+        if (a > am) am = a;
+        live |= v != 0.0;
+      }
+      double rms = std::sqrt(acc / (double)C);
+      uint16_t sb = f32_to_bf16_rne((float)rms);
+      mx.s_bits[r] = sb;
+      mx.s[r] = bf16_to_f32(sb);
+      mx.amax[r] = am;
+      if (live && ((sb >> 7) & 0xFF) == 0) tiny = true;
+    }
+  }, 16);
+  if (nonfinite) return fail(EP_E_NONFINITE, "input holds NaN or Inf");
+  if (tiny) return fail(EP_E_RANGE, "a nonzero row has an RMS below the BF16 normal range");
+
+  // ---- sample rows
+  std::vector<int64_t> rows;
+  const int64_t kSample = 1 << 18;
+  if (N <= kSample) {
+    for (int64_t r = 0; r < R; ++r) rows.push_back(r);
+  } else {
+    int64_t ks = N / kSample;
+    for (int64_t r = 0; r < R; r += ks) rows.push_back(r);
+  }
+  const int64_t n_sample = (int64_t)rows.size() * C;
+  const int64_t T = (int64_t)std::ceil(t * 65536.0 * (double)n_sample);
+
+  // ---- resolution search
+  struct Probe {
+    uint32_t bits;
+    Estimate e;
+  };
+  std::vector<Probe> cache;
+  auto est_at = [&](uint32_t bits) -> Estimate {
+    for (auto& p : cache)
+      if (p.bits == bits) return p.e;
+    Estimate e = estimate(mx, rows, f32_from_bits(bits));
+    cache.push_back({bits, e});
+    return e;
+  };
+  auto ok = [&](uint32_t bits) { return est_at(bits).est >= T; };
+  auto pow2bits = [](int j) { return f32_bits(std::ldexp(1.0f, j)); };
+  const int jmax = 4;
+  int jmin = 999;
+  for (int j = -126; j <= jmax; ++j)
+    if (admissible(mx, std::ldexp(1.0f, j))) {
+      jmin = j;
+      break;
+    }
+  if (jmin == 999) return fail(EP_E_RANGE, "no admissible resolution");
+  int j0 = (int)std::floor(1.0 - t);
+  j0 = std::min(std::max(j0, jmin), jmax);
+  uint32_t dbits;
+  bool done = false;
+  uint32_t lo = 0, hi = 0;
+  if (ok(pow2bits(j0))) {
+    int j = j0;
+    while (j < jmax && ok(pow2bits(j + 1))) ++j;
+    if (j == jmax) {
+      dbits = pow2bits(j);
+      done = true;
+    } else {
+      lo = pow2bits(j);
+      hi = pow2bits(j + 1);
+    }
+  } else {
+    int j = j0 - 1;
+    while (j >= jmin && !ok(pow2bits(j))) --j;
+    if (j < jmin) {
+      dbits = pow2bits(jmin);
+      done = true;
+    } else {
+      lo = pow2bits(j);
+      hi = pow2bits(j + 1);
+    }
+  }
+  if (!done) {
+    while (hi - lo > 1) {
+      uint32_t mid = lo + ((hi - lo) >> 1);
+      if (ok(mid)) lo = mid;
+      else hi = mid;
+    }
+    dbits = lo;
+  }
+  const float delta = f32_from_bits(dbits);
+  const int k = est_at(dbits).k;
+
+  // ---- full quantisation
+  const int64_t n_groups = R * mx.G;
+  std::vector<int32_t> u;
+  try {
+    u.resize((size_t)n_groups * 8);
+  } catch (...) {
+    return fail(EP_E_NOMEM, "out of host memory");
+  }
+  parallel_for(R, [&](int64_t b, int64_t e, int) {
+    for (int64_t r = b; r < e; ++r) quantize_row(mx, r, delta, &u[(size_t)(r * mx.G * 8)]);
+  }, 4);
+  // ---- counts (per-thread partials merged in order)
+  const int nm = n_msym(k);
+  const int nt = num_threads();
+  std::vector<std::vector<int64_t>> part(nt, std::vector<int64_t>(2 * nm + 3, 0));
+  parallel_for(n_groups, [&](int64_t b, int64_t e, int tid) {
+    auto& p = part[tid];
+    Sym s[8];
+    int ms[8];
+    for (int64_t g = b; g < e; ++g) {
+      int c = symbolize(&u[(size_t)(g * 8)], k, s, ms);
+      p[c]++;
+      for (int i = 0; i < 8; ++i) {
+        p[2 + c * nm + ms[i]]++;
+        if (ms[i] >= (1 << k)) p[2 + 2 * nm] = 1;
+      }
+    }
+  }, 4096);
+  int64_t cc[2] = {0, 0};
+  std::vector<int64_t> mag0(nm, 0), mag1(nm, 0);
+  bool any_esc = false;
+  for (auto& p : part) {
+    cc[0] += p[0];
+    cc[1] += p[1];
+    for (int i = 0; i < nm; ++i) {
+      mag0[i] += p[2 + i];
+      mag1[i] += p[2 + nm + i];
+    }
+    any_esc |= p[2 + 2 * nm] != 0;
+  }
+  Model m = build_model(k, cc, mag0.data(), mag1.data());
+
+  // ---- chains
+  const int S = S_req ? S_req : (N >= (1ll << 22) ? 8 : 1);
+  const int64_t n_tiles = std::max<int64_t>(1, (n_groups + kTileGroups - 1) / kTileGroups);
+  const int64_t n_chains = n_tiles * S;
+  std::vector<ChainOut> chains((size_t)n_chains);
+  parallel_for(n_chains, [&](int64_t b, int64_t e, int) {
+    for (int64_t ch = b; ch < e; ++ch) encode_chain(u.data(), m, ch / S, (int)(ch % S), S, n_groups, &chains[ch]);
+  }, 64);
+
+  // ---- saturation flag
+  std::atomic<bool> sat{false};
+  if (dtype != EP_FP32) {
+    const double cmax = container_max(dtype);
+    parallel_for(R, [&](int64_t b, int64_t e, int) {
+      for (int64_t r = b; r < e && !sat; ++r) {
+        float h = mx.s[r] * delta;
+        for (int64_t c = 0; c < C; ++c) {
+          float v = h * (float)u[(size_t)(r * mx.G * 8 + c)];
+          double dv = (double)v;
+          bool out_of_range = dtype == EP_INT8 ? (std::nearbyint(dv) > 127.0 || std::nearbyint(dv) < -128.0)
+                                               : std::fabs(dv) > cmax;
+          if (out_of_range) {
+            sat = true;
+            break;
+          }
+        }
+      }
+    }, 16);
+  }
+
+  // ---- regions, checkpoints, stream
+  const int64_t n_regions = (n_chains + 1) / 2;
+  const int64_t n_blocks = (n_chains + kBlockChains - 1) / kBlockChains;
+  std::vector<uint16_t> rlen((size_t)n_regions);
+  uint64_t n_words = 0;
+  for (int64_t r = 0; r < n_regions; ++r) {
+    size_t a = chains[2 * r].words.size();
+    size_t bsz = (2 * r + 1 < n_chains) ? chains[2 * r + 1].words.size() : 0;
+    size_t len = a + bsz + ((a + bsz) & 1);
+    if (len > 0xFFFF) return fail(EP_E_ARG, "region longer than 65535 words");
+    rlen[r] = (uint16_t)len;
+    n_words += len;
+  }
+  const std::vector<uint8_t> mbytes = m.to_bytes();
+  const size_t total = kHeaderBytes + 2 * (size_t)R + mbytes.size() + 4 * (size_t)n_blocks + 2 * (size_t)n_regions +
+                       4 * (size_t)n_chains + 2 * (size_t)n_words;
+  std::vector<uint8_t>& b = *out;
+  try {
+    b.assign(total, 0);
+  } catch (...) {
+    return fail(EP_E_NOMEM, "out of host memory");
+  }
+  std::memcpy(&b[0], "EPK1", 4);
+  put_u16(b, 4, 1);
+  b[6] = (uint8_t)dtype;
+  b[7] = (uint8_t)kP;
+  b[8] = (uint8_t)S;
+  b[9] = (uint8_t)k;
+  b[10] = (uint8_t)((any_esc ? kFlagEsc : 0) | (sat ? kFlagSat : 0));
+  b[11] = 12;
+  put_u32(b, 12, (uint32_t)R);
+  put_u32(b, 16, (uint32_t)C);
+  put_u32(b, 20, dbits);
+  put_u32(b, 24, (uint32_t)n_tiles);
+  put_u32(b, 28, (uint32_t)n_blocks);
+  put_u64(b, 32, n_words);
+  put_u32(b, 40, (uint32_t)mbytes.size());
+  put_u32(b, 44, 0);
+  size_t off = kHeaderBytes;
+  for (int64_t r = 0; r < R; ++r, off += 2) put_u16(b, off, mx.s_bits[r]);
+  std::memcpy(&b[off], mbytes.data(), mbytes.size());
+  off += mbytes.size();
+  const size_t off_ck = off;
+  off += 4 * (size_t)n_blocks;
+  const size_t off_rl = off;
+  off += 2 * (size_t)n_regions;
+  const size_t off_st = off;
+  off += 4 * (size_t)n_chains;
+  const size_t off_stream = off;
+  uint64_t pos = 0;
+  for (int64_t r = 0; r < n_regions; ++r) {
+    if ((r % (kBlockChains / 2)) == 0) put_u32(b, off_ck + 4 * (size_t)(r / (kBlockChains / 2)), (uint32_t)pos);
+    put_u16(b, off_rl + 2 * (size_t)r, rlen[r]);
+    const auto& wa = chains[2 * r].words;
+    size_t q = off_stream + 2 * (size_t)pos;
+    for (uint16_t v : wa) {
+      std::memcpy(&b[q], &v, 2);
+      q += 2;
+    }
+    size_t nb = 0;
+    if (2 * r + 1 < n_chains) nb = chains[2 * r + 1].words.size();
+    if ((wa.size() + nb) & 1) q += 2;   // zero pad word
+    if (2 * r + 1 < n_chains) {
+      const auto& wb = chains[2 * r + 1].words;
+      for (size_t i = wb.size(); i-- > 0;) {
+        std::memcpy(&b[q], &wb[i], 2);
+        q += 2;
+      }
+    }
+    pos += rlen[r];
+  }
+  for (int64_t ch = 0; ch < n_chains; ++ch) put_u32(b, off_st + 4 * (size_t)ch, chains[ch].state);
+  return EP_OK;
+}
+
+}  // namespace ep

@@ -1,0 +1,119 @@
+// Internal declarations shared by the host encoder, the blob code and the HIP
+// decode/GEMM units of libentropack_hip.so.
+//
+// Format constants (this project's reading of the pages; see include/entropack.h
+// for the page keys):
+//   P = 11 (2048 slots per table), 32-bit rANS state in [2^16, 2^32), 16-bit words;
+//   tiles of 512 groups x 8 columns (4096 coordinates), S chains per tile, chain j
+//   decodes the tile's groups j, j+S, ...; chains 2i / 2i+1 share a region (forward
+//   / backward), one region length (u16, even) per pair, one checkpoint (u32 word
+//   offset) per 64 chains.
+#pragma once
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/entropack.h"
+
+namespace ep {
+
+constexpr int kP = 11;
+constexpr int kM = 1 << kP;          // 2048
+constexpr int kHalf = kM >> 1;       // 1024
+constexpr int kNumCtx = 7;
+constexpr int kIdSpace = 1024;
+constexpr int kMaxE = 28;
+constexpr uint32_t kL = 1u << 16;
+constexpr int kTileGroups = 512;
+constexpr int kBlockChains = 64;
+constexpr int kHeaderBytes = 48;
+constexpr uint8_t kFlagEsc = 1;
+constexpr uint8_t kFlagSat = 2;
+
+inline int n_msym(int k) { return (1 << k) + 4 * (kMaxE + 1 - k); }
+
+// thread-local error message
+void set_error(const std::string& msg);
+int fail(int code, const std::string& msg);
+
+// Frequency quantiser Q (see model.cpp).
+void quantize_freqs(const int64_t* w, int n, int total, int32_t* f_out);
+
+// Stored model + derived decode frequencies for the 7 contexts.
+struct Model {
+  int k = 3;
+  int nm = 0;
+  int w[2] = {0, 0};
+  std::vector<int32_t> g[2];           // magnitude frequencies (sum 1024)
+  int32_t F[kNumCtx][kIdSpace];        // frequency per symbol id
+  int32_t CUM[kNumCtx][kIdSpace];      // first slot per symbol id
+  bool last_ok(int c, int pi, int sid) const;
+  void derive();                       // fill F, CUM from w, g
+  std::vector<uint8_t> to_bytes() const;
+  static bool from_bytes(const uint8_t* p, size_t n, int k, Model* out, std::string* err);
+};
+
+Model build_model(int k, const int64_t coset_counts[2], const int64_t* mag0, const int64_t* mag1);
+
+extern const int32_t* log2q_table();   // floor(2^16 log2 f + 1/2), f in [0, 2048]
+
+// Packed decode-table entry (device tables, one u32 per slot):
+//   bits  0..10  f      (1..2047)
+//   bits 11..21  bias   (slot - cum)
+//   bit  22      escape (bucket symbol: raw bits follow)
+//   bits 23..31  direct symbol: doubled coordinate u (signed 9 bit);
+//                escape: c | neg<<1 | top2<<2 | (e-k)<<4
+void build_slot_tables(const Model& m, uint32_t* out /* 7*2048 */);
+
+// Parsed blob (host side) + device mirror.
+struct Blob {
+  std::vector<uint8_t> bytes;          // serialized form
+  int dtype = 0, S = 0, k = 0, flags = 0;
+  int64_t R = 0, C = 0;
+  float delta = 0.f;
+  int64_t n_tiles = 0, n_blocks = 0, n_chains = 0, n_regions = 0;
+  uint64_t n_words = 0;
+  size_t off_scales = 0, off_model = 0, off_ckpt = 0, off_rlen = 0, off_states = 0, off_stream = 0;
+  uint32_t model_bytes = 0;
+  Model model;
+  uint32_t max_span_words = 0;         // largest block span (words)
+  // device mirror
+  int device = -1;
+  void* d_base = nullptr;              // one allocation
+  const uint16_t* d_stream = nullptr;
+  const uint32_t* d_states = nullptr;
+  const uint16_t* d_rlen = nullptr;
+  const uint32_t* d_ckpt = nullptr;    // n_blocks + 1 entries
+  const float* d_hr = nullptr;         // per-row half scales h_r
+  const uint32_t* d_tab = nullptr;     // 7 x 2048 packed entries
+  uint32_t* d_err = nullptr;
+  int64_t n_groups() const { return R * ((C + 7) / 8); }
+};
+
+// Parse + validate serialized bytes (takes ownership of `bytes`).
+int parse_blob(std::vector<uint8_t>&& bytes, Blob* out);
+
+// Host reference pieces reused by upload: h_r = fl32(s_r * delta).
+void half_scales(const Blob& b, float* hr_out);
+
+inline float bf16_to_f32(uint16_t b) {
+  uint32_t u = uint32_t(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  uint32_t lsb = (u >> 16) & 1u;
+  return uint16_t((uint64_t(u) + 0x7FFFu + lsb) >> 16);
+}
+
+int hip_check(int err, const char* what);
+
+}  // namespace ep
+
+struct ep_blob {
+  ep::Blob b;
+};

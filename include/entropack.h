@@ -1,0 +1,158 @@
+/*
+ * entropack.h — C ABI of libentropack_hip.so, a gfx950 (MI355X) implementation of
+ * EntroPack-style lossy weight compression: row-normalised E8 lattice quantisation,
+ * a conditional model of the lattice coordinates, rANS in independently decodable
+ * tiles, and fused GPU decode (symbol decode, algebraic inverse-lattice
+ * reconstruction, per-row rescale, container cast) feeding an MFMA GEMM.
+ *
+ * Sources (the only specification; cited by page title and section):
+ *  [ABS]    "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary
+ *           Bitrates", English abstract (arxivdaily.com / modelscope.ai paper pages):
+ *           E8 + conditional model, sampled rate selection, independently decodable
+ *           tiles, BF16/FP16/FP8/INT8 containers, decode cost grows with weight count.
+ *  [SUM]    same paper, modelscope.ai page, section "摘要": rANS tiles; symbol decode,
+ *           algebraic inverse-lattice reconstruction and row rescale fused on the GPU
+ *           with no intermediate symbol tensor and no reconstruction codebook.
+ *  [README] EntroPack README_zh.md, section "快速开始": compress/decompress restore shape
+ *           and dtype; 0.001 <= target_bpp <= 11 (finite, non-integer allowed);
+ *           actual_bpp includes metadata; CompressedLinear.from_linear / layer(x).
+ *           Section "Config：压缩配置": lossy mode for 2-D float and integer tensors.
+ *  [NEWS]   techmoon.xyz, "EntroPack 開源模型壓縮…", section "任意位元率的本體…": lossy
+ *           mode only for 2-D tensors; results saved with state_dict; FP8@5 packs use
+ *           an FP8 GEMM at inference.
+ *
+ * Conventions
+ *  - Every function returning int returns EP_OK (0) or a negative EP_E_* code; the
+ *    calling thread's message is available from ep_last_error().
+ *  - "host" pointers are CPU memory, "dev" pointers are device memory of the current
+ *    HIP device.  The caller owns every pointer it passes; the library owns ep_blob
+ *    (host bytes + device copy) and frees both in ep_blob_free().
+ *  - GPU work is asynchronous on the given hipStream_t (NULL = default stream);
+ *    device-side errors (a corrupt stream failing the final-state check) are counted
+ *    in the blob and read back by ep_blob_device_errors() after synchronisation.
+ *  - Matrices are row-major.  BF16/FP16/FP8 elements are passed as their bit patterns.
+ */
+#ifndef ENTROPACK_H
+#define ENTROPACK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ep_blob ep_blob;
+typedef struct ihipStream_t* ep_stream;   /* a hipStream_t */
+
+enum {
+  EP_BF16 = 1,          /* bfloat16 */
+  EP_FP16 = 2,          /* IEEE binary16 */
+  EP_FP32 = 3,          /* IEEE binary32 */
+  EP_FP8_E4M3FN = 4,    /* OCP FP8 E4M3FN (bias 7, max 448, no Inf) */
+  EP_INT8 = 5           /* two's complement int8 */
+};
+
+enum {
+  EP_OK = 0,
+  EP_E_ARG = -1,        /* null pointer, rows/cols < 1, bad option */
+  EP_E_RANGE = -2,      /* target_bpp not finite / outside [0.001, 11] / above the 8-bit
+                           container cap of 8; or a nonzero row whose RMS is below the
+                           BF16 normal range */
+  EP_E_DTYPE = -3,      /* container not one of the five above */
+  EP_E_SHAPE = -4,      /* not a 2-D tensor (raised by the Python layer) */
+  EP_E_NONFINITE = -5,  /* NaN or Inf in the input */
+  EP_E_CORRUPT = -6,    /* blob failed validation */
+  EP_E_NOMEM = -7,      /* host or device allocation failed */
+  EP_E_DEVICE = -8,     /* a HIP runtime error */
+  EP_E_WORKSPACE = -9,  /* workspace smaller than ep_linear_workspace_bytes() */
+  EP_E_STATE = -10      /* blob not uploaded to the device */
+};
+
+/* ---------------------------------------------------------------- compression
+ * ep_compress — [ABS], [README] 快速开始, [NEWS].
+ * Compress a rows x cols host matrix of container `dtype` at `target_bpp` bits per
+ * parameter (the data part; actual_bpp adds the metadata).  Runs on the host CPU
+ * (multi-threaded; EP_NUM_THREADS caps the thread count) and is deterministic: the
+ * same input gives the same bytes on any machine.  `chains_per_tile` = 0 picks the
+ * default (8 for rows*cols >= 2^22, else 1); otherwise one of 1,2,4,8,16,32,64.
+ * On success *out owns a host-only blob (call ep_blob_upload before decoding). */
+int ep_compress(const void* host_src, int dtype, int64_t rows, int64_t cols,
+                double target_bpp, ep_blob** out);
+int ep_compress_ex(const void* host_src, int dtype, int64_t rows, int64_t cols,
+                   double target_bpp, int chains_per_tile, ep_blob** out);
+
+/* Copy the blob's stream, tile tables, row scales and the 7 expanded 2048-slot decode
+ * tables to the current device (one H2D copy, enqueued on `stream`; the host side
+ * waits for it).  Idempotent.  The device copy lives until ep_blob_free(). */
+int ep_blob_upload(ep_blob* blob, ep_stream stream);
+
+/* ---------------------------------------------------------------- decode
+ * ep_decompress — [SUM]: fused symbol decode + algebraic inverse lattice + row rescale.
+ * Writes rows*cols elements of the blob's container dtype, row-major, to dev_dst.
+ * No intermediate symbol or coordinate tensor is written. */
+int ep_decompress(const ep_blob* blob, void* dev_dst, ep_stream stream);
+
+/* Decode only tiles [tile_begin, tile_end) (each 4096 coordinates = 512 groups of
+ * 8 columns, row-major) into dev_dst; other elements are left untouched.  This is
+ * the tile-independence of [ABS]. */
+int ep_decompress_tiles(const ep_blob* blob, int64_t tile_begin, int64_t tile_end,
+                        void* dev_dst, ep_stream stream);
+
+/* Decode n blobs in one launch (e.g. all matrices of one transformer block);
+ * dev_dsts[i] receives blob i.  Same results as n ep_decompress calls. */
+int ep_decompress_batch(const ep_blob* const* blobs, void* const* dev_dsts, int n,
+                        ep_stream stream);
+
+/* Test hook: write the doubled lattice coordinates u (int32, rows*cols, u = 2p for
+ * the E8 point p) instead of weights.  Same kernel, coordinate-emitting variant. */
+int ep_test_decode_coords(const ep_blob* blob, int32_t* dev_u, ep_stream stream);
+
+/* Device-side error count of the blob (decodes whose rANS chains did not end in the
+ * initial state).  Synchronises the device. */
+int64_t ep_blob_device_errors(const ep_blob* blob);
+
+/* ---------------------------------------------------------------- compressed linear
+ * [README] 快速开始 (CompressedLinear.from_linear, layer(x)): y = x W^T (+ bias).
+ * W is the decoded BF16 blob (rows = out features, cols = in features); x is T x cols
+ * BF16, y is T x rows BF16, bias is rows BF16 or NULL.  The decode goes to dev_ws
+ * (>= ep_linear_workspace_bytes bytes), then an MFMA BF16 GEMM with fp32
+ * accumulation runs on the same stream. */
+size_t ep_linear_workspace_bytes(const ep_blob* blob);
+int ep_compressed_linear_forward(const ep_blob* w, const void* dev_x, int64_t T,
+                                 const void* dev_bias, void* dev_y,
+                                 void* dev_ws, size_t ws_bytes, ep_stream stream);
+
+/* Plain BF16 "NT" GEMM on MFMA: y[T x N] = x[T x K] w[N x K]^T (+ bias[N]), fp32
+ * accumulate, BF16 out.  The uncompressed baseline of the linear layer. */
+int ep_gemm_bf16_nt(const void* dev_x, const void* dev_w, const void* dev_bias,
+                    void* dev_y, int64_t T, int64_t N, int64_t K, ep_stream stream);
+
+/* FP8 (E4M3FN) "NT" GEMM on MFMA ([NEWS]/[README] FP8@5: FP8 W8A8 codes, FP8 GEMM):
+ * y[T x N] (BF16) = (xq[T x K] wq[N x K]^T) * a_x * a_w[N], fp32 accumulate.
+ * a_w is a device float array (per output row), a_x a host float. */
+int ep_gemm_fp8_nt(const void* dev_xq, const void* dev_wq, float a_x, const float* dev_aw,
+                   void* dev_y, int64_t T, int64_t N, int64_t K, ep_stream stream);
+
+/* ---------------------------------------------------------------- blob accessors
+ * actual_bpp = 8 * serialized bytes / (rows * cols)  ([README]: includes metadata). */
+double ep_actual_bpp(const ep_blob* blob);
+void ep_blob_shape(const ep_blob* blob, int64_t* rows, int64_t* cols);
+int ep_blob_dtype(const ep_blob* blob);
+/* chains per tile, K_LOG2, flags (bit0 escapes present, bit1 clamping needed) */
+void ep_blob_params(const ep_blob* blob, int* chains_per_tile, int* k_log2, int* flags);
+
+/* Serialise (the blob v1 bytes; what a state_dict stores, [NEWS]) / deserialise
+ * with full validation (EP_E_CORRUPT on any inconsistency). */
+size_t ep_serialized_size(const ep_blob* blob);
+int ep_serialize(const ep_blob* blob, void* host_dst, size_t capacity);
+int ep_deserialize(const void* host_src, size_t size, ep_blob** out);
+void ep_blob_free(ep_blob* blob);
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char* ep_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ENTROPACK_H */

@@ -214,6 +214,8 @@ def parse_blob(buf: bytes) -> Blob:
     if len(buf) != need:
         raise ValueError("blob size mismatch")
     s_bits = np.frombuffer(buf, "<u2", R, off).copy(); off += 2 * R
+    if ((s_bits & 0x8000) != 0).any() or (((s_bits >> 7) & 0xFF) == 0xFF).any():
+        raise ValueError("bad row scale")
     mbytes = bytes(buf[off:off + mb]); off += mb
     model = Model.from_bytes(mbytes, k)
     ck = np.frombuffer(buf, "<u4", n_blocks, off).copy(); off += 4 * n_blocks

@@ -1,0 +1,80 @@
+"""Helpers for the GPU parity tests (device buffers through torch, calls through the C ABI)."""
+import os
+import sys
+
+import numpy as np
+
+import oracle
+from oracle import numerics as nx
+
+TORCH_DT = None
+
+
+def torch_dtype(dt):
+    import torch
+    return {nx.DT_BF16: torch.bfloat16, nx.DT_FP16: torch.float16, nx.DT_FP32: torch.float32,
+            nx.DT_FP8: torch.uint8, nx.DT_INT8: torch.int8}[dt]
+
+
+def np_view(dt):
+    return {nx.DT_BF16: np.uint16, nx.DT_FP16: np.uint16, nx.DT_FP32: np.float32,
+            nx.DT_FP8: np.uint8, nx.DT_INT8: np.int8}[dt]
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def stream_ptr():
+    import torch
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+class DevBlob:
+    """An ep_blob made from serialized bytes and uploaded to the current GPU."""
+
+    def __init__(self, data: bytes):
+        from decode_tile_rans_amd import _lib as L
+        self.L = L
+        self.data = data
+        self.h = L.ep_deserialize(data)
+        L.ep_blob_upload(self.h, stream_ptr())
+        self.R, self.C = L.ep_blob_shape(self.h)
+        self.dt = L.ep_blob_dtype(self.h)
+
+    def empty_out(self, fill=0):
+        import torch
+        t = torch.empty((self.R, self.C), dtype=torch_dtype(self.dt), device="cuda")
+        t.view(torch.uint8).fill_(fill) if t.dtype != torch.uint8 else t.fill_(fill)
+        return t
+
+    def decode(self, fill=0):
+        import torch
+        out = self.empty_out(fill)
+        self.L.ep_decompress(self.h, out.data_ptr(), stream_ptr())
+        torch.cuda.synchronize()
+        return out.cpu().numpy().view(np_view(self.dt))
+
+    def decode_tiles(self, t0, t1, fill=0):
+        import torch
+        out = self.empty_out(fill)
+        self.L.ep_decompress_tiles(self.h, t0, t1, out.data_ptr(), stream_ptr())
+        torch.cuda.synchronize()
+        return out.cpu().numpy().view(np_view(self.dt))
+
+    def coords(self):
+        import torch
+        out = torch.zeros((self.R, self.C), dtype=torch.int32, device="cuda")
+        self.L.ep_test_decode_coords(self.h, out.data_ptr(), stream_ptr())
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def errors(self):
+        return self.L.ep_blob_device_errors(self.h)
+
+    def __del__(self):
+        try:
+            self.L.ep_blob_free(self.h)
+        except Exception:
+            pass

@@ -1,0 +1,150 @@
+"""CPU tests of the C ABI: every declared symbol is exported, the host encoder's
+blobs are byte-identical to the oracle's, validation errors and blob parsing.
+
+No GPU work is launched here (ep_compress / ep_serialize / ep_deserialize are host code).
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+import oracle
+from oracle import numerics as nx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+L = pytest.importorskip("decode_tile_rans_amd._lib")
+if not os.path.exists(L.LIB_PATH):
+    pytest.skip("libentropack_hip.so not built", allow_module_level=True)
+
+
+def declared_symbols():
+    txt = open(os.path.join(ROOT, "include", "entropack.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    lib = L.lib()
+    names = declared_symbols()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
+
+
+def lib_blob(src, dt, t, S=0):
+    src = np.ascontiguousarray(src)
+    h = L.ep_compress(src.ctypes.data, dt, src.shape[0], src.shape[1], t, S)
+    try:
+        return L.ep_serialize(h), L.ep_actual_bpp(h)
+    finally:
+        L.ep_blob_free(h)
+
+
+CASES = [
+    ("small_gauss_3.5", lambda: synth.small_gauss(), nx.DT_BF16, 3.5, 0),
+    ("odd_37x13", lambda: synth.rowscaled(37, 13, 5), nx.DT_BF16, 4.0, 0),
+    ("r512_8", lambda: synth.rowscaled(512, 512, 70), nx.DT_BF16, 8.0, 0),
+    ("r512_2.3", lambda: synth.rowscaled(512, 512, 30), nx.DT_BF16, 2.3, 0),
+    ("r512_11", lambda: synth.rowscaled(256, 512, 31), nx.DT_BF16, 11.0, 0),
+    ("S8", lambda: synth.rowscaled(300, 520, 32), nx.DT_BF16, 4.0, 8),
+    ("S64", lambda: synth.rowscaled(200, 512, 33), nx.DT_BF16, 3.0, 64),
+    ("S2", lambda: synth.rowscaled(129, 777, 34), nx.DT_BF16, 5.0, 2),
+    ("fp16", lambda: synth.rowscaled_f32(96, 200, 4).astype(np.float16).view(np.uint16), nx.DT_FP16, 4.0, 0),
+    ("fp32", lambda: synth.rowscaled_f32(64, 256, 4), nx.DT_FP32, 6.0, 0),
+    ("fp8", lambda: synth.fp8_codes(128, 256, 4)[0], nx.DT_FP8, 5.0, 0),
+    ("int8", lambda: synth.int8_codes(128, 256, 4)[0], nx.DT_INT8, 4.0, 0),
+    ("zeros", lambda: np.zeros((40, 48), np.uint16), nx.DT_BF16, 2.0, 0),
+    ("low", lambda: synth.rowscaled(64, 256, 9), nx.DT_BF16, 0.001, 0),
+    ("1x1", lambda: synth.rowscaled(1, 1, 9), nx.DT_BF16, 4.0, 0),
+]
+
+
+@pytest.mark.parametrize("name,gen,dt,t,S", CASES, ids=[c[0] for c in CASES])
+def test_encoder_byte_parity(name, gen, dt, t, S):
+    src = gen()
+    want = oracle.compress(src, dt, t, chains_per_tile=S or None)
+    got, bpp = lib_blob(src, dt, t, S)
+    assert got == want
+    assert abs(bpp - 8.0 * len(want) / src.size) < 1e-12
+
+
+def test_encoder_byte_parity_random_small():
+    rng = np.random.default_rng(2024)
+    for i in range(25):
+        R = int(rng.integers(1, 90))
+        C = int(rng.integers(1, 300))
+        t = float(rng.choice([0.7, 1.0, 2.3, 3.5, 4.0, 6.0, 9.0]))
+        S = int(rng.choice([0, 1, 2, 4, 8, 16]))
+        src = synth.rowscaled(R, C, 500 + i, outlier_frac=0.01 if i % 3 == 0 else 0.0)
+        assert lib_blob(src, nx.DT_BF16, t, S)[0] == oracle.compress(src, nx.DT_BF16, t, chains_per_tile=S or None), \
+            (R, C, t, S)
+
+
+@pytest.mark.slow
+def test_encoder_byte_parity_config2():
+    src = synth.rowscaled(3072, 3072, 2, 0.001)
+    got, bpp = lib_blob(src, nx.DT_BF16, 4.0)
+    assert got == oracle.compress(src, nx.DT_BF16, 4.0)
+    assert 4.0 <= bpp <= 4.1
+
+
+def test_validation_codes():
+    src = np.ascontiguousarray(synth.small_gauss(8, 8))
+    p = src.ctypes.data
+    for t in (0.0005, 11.01, float("nan"), float("inf")):
+        with pytest.raises(L.EPError) as e:
+            L.ep_compress(p, nx.DT_BF16, 8, 8, t)
+        assert e.value.name == "EP_E_RANGE"
+    with pytest.raises(L.EPError) as e:
+        L.ep_compress(p, 9, 8, 8, 4.0)
+    assert e.value.name == "EP_E_DTYPE"
+    with pytest.raises(L.EPError) as e:
+        L.ep_compress(p, nx.DT_BF16, 0, 8, 4.0)
+    assert e.value.name == "EP_E_ARG"
+    with pytest.raises(L.EPError) as e:
+        L.ep_compress(p, nx.DT_BF16, 8, 8, 4.0, 3)
+    assert e.value.name == "EP_E_ARG"
+    bad = src.copy()
+    bad[3, 3] = 0x7F80   # +Inf
+    with pytest.raises(L.EPError) as e:
+        L.ep_compress(bad.ctypes.data, nx.DT_BF16, 8, 8, 4.0)
+    assert e.value.name == "EP_E_NONFINITE"
+    i8 = np.ones((4, 4), np.int8)
+    with pytest.raises(L.EPError) as e:
+        L.ep_compress(i8.ctypes.data, nx.DT_INT8, 4, 4, 8.5)
+    assert e.value.name == "EP_E_RANGE"
+    assert "target_bpp" in L.ep_last_error()
+
+
+def test_serialize_deserialize_and_corruption():
+    src = synth.small_gauss()
+    blob, _ = lib_blob(src, nx.DT_BF16, 3.5)
+    h = L.ep_deserialize(blob)
+    assert L.ep_serialize(h) == blob
+    assert L.ep_blob_shape(h) == (256, 256)
+    assert L.ep_blob_dtype(h) == nx.DT_BF16
+    S, k, flags = L.ep_blob_params(h)
+    ob = oracle.parse_blob(blob)
+    assert (S, k, flags) == (ob.S, ob.k, ob.flags)
+    L.ep_blob_free(h)
+    bad = [blob[:-2], b"XXXX" + blob[4:], blob + b"\0\0"]
+    b2 = bytearray(blob)
+    b2[44] = 1                              # reserved field
+    bad.append(bytes(b2))
+    b3 = bytearray(blob)
+    off = 48 + 2 * 256 + ob.model_bytes.__len__()
+    b3[off] ^= 2                            # checkpoint 0 no longer 0
+    bad.append(bytes(b3))
+    b4 = bytearray(blob)
+    b4[48 + 1] |= 0x80                      # negative row scale
+    bad.append(bytes(b4))
+    for bb in bad:
+        with pytest.raises(L.EPError) as e:
+            L.ep_deserialize(bb)
+        assert e.value.name == "EP_E_CORRUPT"
+        with pytest.raises(ValueError):
+            oracle.parse_blob(bb)

@@ -1,0 +1,172 @@
+"""GPU parity of the fused decode kernel against the oracle.
+
+Blobs are made by the oracle (so no oracle input comes from the product); the
+GPU decodes them through the C ABI.  Integer results (doubled lattice
+coordinates, container bit patterns) must match bit for bit; every rANS chain
+must end in its initial state (device error count 0).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+import oracle
+from oracle import numerics as nx
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import DevBlob, say  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU test run without a GPU"
+    from decode_tile_rans_amd import _lib as L
+    L.lib()        # fails loudly when the HIP library is missing
+    yield
+
+
+def _check(name, src, dt, t, S=None, env=None):
+    say(name, src.shape, dt, t, S, env)
+    blob = oracle.compress(src, dt, t, chains_per_tile=S)
+    u_o, out_o, info = oracle.decode(blob)
+    assert info["final_state_ok"]
+    old = {}
+    for k, v in (env or {}).items():
+        old[k] = os.environ.get(k)
+        os.environ[k] = v
+    try:
+        db = DevBlob(blob)
+        u_g = db.coords()
+        assert np.array_equal(u_g, u_o), f"{name}: coords differ at {np.argwhere(u_g != u_o)[:5]}"
+        out_g = db.decode()
+        assert np.array_equal(out_g.view(np.uint8), out_o.view(np.uint8)), f"{name}: container values differ"
+        assert db.errors() == 0
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    return blob, u_o, out_o
+
+
+def test_small_gauss_config():
+    _check("small_gauss 256x256 @3.5", synth.small_gauss(), nx.DT_BF16, 3.5)
+
+
+def test_rowscaled_outliers_3072():
+    _check("rowscaled+outliers 3072x3072 @4.0", synth.rowscaled(3072, 3072, 2, 0.001), nx.DT_BF16, 4.0)
+
+
+@pytest.mark.parametrize("R,C", [(1, 1), (37, 13), (5, 4097), (600, 7), (3, 8), (129, 1000)])
+def test_ragged_shapes(R, C):
+    _check(f"ragged {R}x{C}", synth.rowscaled(R, C, R + C), nx.DT_BF16, 4.0)
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 8, 16, 32, 64])
+def test_chains_per_tile(S):
+    _check(f"S={S}", synth.rowscaled(200, 512 + 24, 90 + S), nx.DT_BF16, 3.0, S=S)
+
+
+@pytest.mark.parametrize("t", [0.001, 0.5, 2.3, 8.0, 11.0])
+def test_rates_and_escapes(t):
+    blob, _, _ = _check(f"rate {t}", synth.rowscaled(256, 512, 120), nx.DT_BF16, t, S=8)
+    if t >= 8:
+        assert oracle.parse_blob(blob).flags & 1      # escapes exercised
+
+
+def test_global_word_path():
+    _check("global words", synth.rowscaled(300, 1024, 7), nx.DT_BF16, 5.0, S=8, env={"EP_DECODE_SPAN": "global"})
+    _check("global words S1", synth.small_gauss(), nx.DT_BF16, 3.5, env={"EP_DECODE_SPAN": "global"})
+
+
+@pytest.mark.parametrize("waves", ["1", "2", "3"])
+def test_workgroup_sizes(waves):
+    _check(f"waves={waves}", synth.rowscaled(257, 1024, 8), nx.DT_BF16, 4.0, S=8, env={"EP_DECODE_WAVES": waves})
+
+
+@pytest.mark.parametrize("dt", [nx.DT_FP16, nx.DT_FP32, nx.DT_FP8, nx.DT_INT8])
+def test_containers(dt):
+    R, C = 512, 520
+    if dt == nx.DT_FP8:
+        src, t = synth.fp8_codes(R, C, 4)[0], 5.0
+    elif dt == nx.DT_INT8:
+        src, t = synth.int8_codes(R, C, 4)[0], 4.0
+    elif dt == nx.DT_FP16:
+        src, t = synth.rowscaled_f32(R, C, 4).astype(np.float16).view(np.uint16), 4.0
+    else:
+        src, t = synth.rowscaled_f32(R, C, 4), 6.0
+    _check(f"container {dt}", src, dt, t, S=8)
+
+
+def test_saturating_bf16():
+    # rows near the BF16 maximum force the clamping variant of the kernel
+    w = synth.rowscaled_f32(64, 256, 11) * np.float32(1e38 / 0.02)
+    w = np.clip(w, -3.3e38, 3.3e38).astype(np.float32)
+    src = synth.f32_to_bf16_bits(w)
+    blob, _, _ = _check("bf16 near max", src, nx.DT_BF16, 2.0)
+
+
+def test_tile_independence():
+    src = synth.rowscaled(512, 1032, 12)
+    blob = oracle.compress(src, nx.DT_BF16, 4.0, chains_per_tile=8)
+    b = oracle.parse_blob(blob)
+    db = DevBlob(blob)
+    full = db.decode()
+    G = -(-b.C // 8)
+    rng = np.random.default_rng(0)
+    ranges = [(0, 1), (b.n_tiles - 1, b.n_tiles), (3, 9), (b.n_tiles // 2, b.n_tiles)]
+    ranges += [tuple(sorted(rng.integers(0, b.n_tiles, 2) + np.array([0, 1]))) for _ in range(4)]
+    for (t0, t1) in ranges:
+        say("tiles", t0, t1)
+        part = db.decode_tiles(int(t0), int(t1), fill=0xA5)
+        gm = np.zeros(b.R * G, dtype=bool)
+        gm[512 * t0: 512 * t1] = True
+        cm = np.repeat(gm, 8).reshape(b.R, G * 8)[:, :b.C]
+        assert np.array_equal(part[cm], full[cm])
+        assert (part.view(np.uint8).reshape(b.R, -1)[np.repeat(~cm, 2, axis=1)] == 0xA5).all()
+        # the oracle decoding only these tiles agrees too
+        _, out_o, _ = oracle.decode(blob, tiles=range(t0, t1))
+        assert np.array_equal(part[cm], out_o[cm])
+    assert db.errors() == 0
+
+
+def test_batch_matches_single():
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    from gpu_util import stream_ptr
+    shapes = [(256, 512, 3.0, 8), (100, 200, 4.0, 1), (64, 4096, 5.0, 8), (513, 264, 2.3, 8), (1, 8, 4.0, 1),
+              (300, 300, 8.0, 8), (128, 1024, 4.0, 2), (77, 640, 4.5, 8), (512, 512, 3.5, 64),
+              (40, 2000, 4.0, 8), (1000, 24, 4.0, 4), (64, 64, 1.0, 1), (200, 200, 6.0, 16)]
+    dbs, refs = [], []
+    for i, (R, C, t, S) in enumerate(shapes):
+        blob = oracle.compress(synth.rowscaled(R, C, 700 + i), nx.DT_BF16, t, chains_per_tile=S)
+        dbs.append(DevBlob(blob))
+        refs.append(oracle.decode(blob)[1])
+    outs = [torch.zeros((d.R, d.C), dtype=torch.bfloat16, device="cuda") for d in dbs]
+    say("batch of", len(dbs))
+    L.ep_decompress_batch([d.h for d in dbs], [o.data_ptr() for o in outs], stream_ptr())
+    torch.cuda.synchronize()
+    for d, o, r in zip(dbs, outs, refs):
+        assert np.array_equal(o.cpu().view(torch.int16).numpy().view(np.uint16), r)
+        assert d.errors() == 0
+
+
+def test_corrupt_stream_flags_error():
+    src = synth.rowscaled(256, 1024, 13)
+    blob = bytearray(oracle.compress(src, nx.DT_BF16, 4.0, chains_per_tile=8))
+    b = oracle.parse_blob(bytes(blob))
+    nw = len(b.stream)
+    stream_off = len(blob) - 2 * nw
+    for q in (nw // 3, nw // 2, 2 * nw // 3):
+        blob[stream_off + 2 * q] ^= 0x5A
+    blob = bytes(blob)
+    _, _, info = oracle.decode(blob)
+    assert not info["final_state_ok"]
+    say("corrupt stream")
+    db = DevBlob(blob)
+    db.decode()
+    assert db.errors() > 0
