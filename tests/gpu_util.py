@@ -21,6 +21,13 @@ def np_view(dt):
             nx.DT_FP8: np.uint8, nx.DT_INT8: np.int8}[dt]
 
 
+def to_np(t, dt):
+    """Device tensor -> numpy array of the container's raw element type."""
+    import torch
+    shape = tuple(t.shape)
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy().view(np_view(dt)).reshape(shape)
+
+
 def say(*a):
     print("[case]", *a, flush=True)
     sys.stdout.flush()
@@ -46,7 +53,7 @@ class DevBlob:
     def empty_out(self, fill=0):
         import torch
         t = torch.empty((self.R, self.C), dtype=torch_dtype(self.dt), device="cuda")
-        t.view(torch.uint8).fill_(fill) if t.dtype != torch.uint8 else t.fill_(fill)
+        t.view(torch.uint8).fill_(fill)
         return t
 
     def decode(self, fill=0):
@@ -54,14 +61,14 @@ class DevBlob:
         out = self.empty_out(fill)
         self.L.ep_decompress(self.h, out.data_ptr(), stream_ptr())
         torch.cuda.synchronize()
-        return out.cpu().numpy().view(np_view(self.dt))
+        return to_np(out, self.dt)
 
     def decode_tiles(self, t0, t1, fill=0):
         import torch
         out = self.empty_out(fill)
         self.L.ep_decompress_tiles(self.h, t0, t1, out.data_ptr(), stream_ptr())
         torch.cuda.synchronize()
-        return out.cpu().numpy().view(np_view(self.dt))
+        return to_np(out, self.dt)
 
     def coords(self):
         import torch

@@ -16,7 +16,7 @@ from oracle import numerics as nx
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import DevBlob, say  # noqa: E402
+from gpu_util import DevBlob, say, to_np  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -151,7 +151,7 @@ def test_batch_matches_single():
     L.ep_decompress_batch([d.h for d in dbs], [o.data_ptr() for o in outs], stream_ptr())
     torch.cuda.synchronize()
     for d, o, r in zip(dbs, outs, refs):
-        assert np.array_equal(o.cpu().view(torch.int16).numpy().view(np.uint16), r)
+        assert np.array_equal(to_np(o, nx.DT_BF16), r)
         assert d.errors() == 0
 
 

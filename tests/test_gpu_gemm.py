@@ -101,7 +101,7 @@ def test_python_api_module_and_state_dict():
     assert layer._c.to_bytes() == blob
     _, w_hat, _ = oracle.decode(blob)
     ref = linear_ref(x.float().cpu().numpy().astype(np.float64), nx.bf16_to_f64(w_hat),
-                     lin.bias.float().cpu().numpy())
+                     lin.bias.detach().float().cpu().numpy())
     assert rel_l2(y.float().cpu().numpy(), ref) <= TOL
     sd = layer.state_dict()
     layer2 = ep.CompressedLinear(ep.Compressed.from_bytes(blob), torch.zeros(384, dtype=torch.bfloat16, device="cuda"))
