@@ -1,0 +1,241 @@
+"""Benchmark: GPU weight decode of the 276-matrix DiT-shaped stack on one MI355X.
+
+One step = decode every matrix of the stack (6 281 625 600 BF16 parameters,
+target 4.0 bpp) from its resident compressed blob into its own BF16 buffer,
+block by block: one launch per transformer block (9 matrices: q, k, v, o, w1,
+w3, w2, mod1, mod2), 31 launches per step.  Inputs are seeded synthetic
+matrices drawn on the GPU and compressed by the library's host encoder before
+timing; blobs and output buffers are resident in HBM when the timed region
+starts.
+
+Printed as one JSON line: value = BF16 output GB/s of the whole step; also the
+HBM roofline of the decode kernel (algorithmic bytes = compressed bytes read +
+BF16 bytes written, per launch, over the HIP-event launch time), the oracle
+decoder timed on the host, the per-layer (one launch per matrix) variant and the
+fused compressed-linear prefill overhead (14336 x 4096 weight, 4096 tokens).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--target-bpp", type=float, default=4.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-linear", action="store_true")
+    p.add_argument("--no-layer-mode", action="store_true")
+    p.add_argument("--matrices", type=int, default=276, help="first N matrices of the stack (profiling runs)")
+    return p.parse_args()
+
+
+def build_stack(n, target_bpp):
+    """Draw the stack on the GPU, compress on the host (all cores), upload blobs."""
+    import torch
+    import synth
+    import decode_tile_rans_amd as ep
+    shapes = synth.dit_stack_shapes()[:n]
+    ncpu = max(1, min(16, os.cpu_count() or 1))
+    os.environ["EP_NUM_THREADS"] = "1"
+    t0 = time.time()
+
+    def job(i):
+        w = synth.dit_stack_torch(i).cpu()
+        return ep.compress(w, target_bpp)
+
+    with ThreadPoolExecutor(ncpu) as pool:
+        comps = list(pool.map(job, range(n)))
+    os.environ.pop("EP_NUM_THREADS", None)
+    for c in comps:
+        c.upload()
+    torch.cuda.synchronize()
+    log(f"compressed {n} matrices in {time.time() - t0:.1f}s on {ncpu} threads")
+    blocks = {}
+    for i, (_, _, _, b) in enumerate(shapes):
+        blocks.setdefault(b, []).append(i)
+    return comps, [blocks[b] for b in sorted(blocks)]
+
+
+def time_stack(comps, blocks, outs, steps, warmup, per_layer=False):
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    st = torch.cuda.current_stream()
+    sp = int(st.cuda_stream)
+    handles = [c.handle for c in comps]
+    ptrs = [o.data_ptr() for o in outs]
+    units = [[i] for i in range(len(comps))] if per_layer else blocks
+
+    def launch(u):
+        if len(u) == 1:
+            L.ep_decompress(handles[u[0]], ptrs[u[0]], sp)
+        else:
+            L.ep_decompress_batch([handles[i] for i in u], [ptrs[i] for i in u], sp)
+
+    for _ in range(warmup):
+        for u in units:
+            launch(u)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in units]
+    launch_ms = []
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for k, u in enumerate(units):
+            if s == steps - 1:
+                ev[k][0].record(st)
+            launch(u)
+            if s == steps - 1:
+                ev[k][1].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    return wall / steps * 1e3, launch_ms, units
+
+
+def cpu_baseline(target_bpp):
+    """The oracle decoder (NumPy, single process) on one 3840 x 3840 stack matrix."""
+    import numpy as np
+    import oracle
+    import synth
+    from oracle import numerics as nx
+    w = synth.dit_stack_torch(0).cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+    blob = oracle.compress(w, nx.DT_BF16, target_bpp)
+    n = 0
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < 10.0 or reps < 1:
+        oracle.decode(blob)
+        n += w.size
+        reps += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * n / dt / 1e9, 4), "unit": "GB/s (BF16 out)", "cores": 1, "kind": "oracle",
+            "sample": f"oracle.decode of one 3840x3840 stack matrix (14.7M params, {reps} repetitions, "
+                      f"{dt:.1f}s), NumPy single process",
+            "coords_per_s": round(n / dt, 1)}
+
+
+def fused_linear(target_bpp, reps=10):
+    """CompressedLinear prefill: W 14336x4096 (row-scaled, seed 5), X 4096x4096 N(0,1) (seed 50)."""
+    import numpy as np
+    import torch
+    import synth
+    import decode_tile_rans_amd as ep
+    from decode_tile_rans_amd import _lib as L
+    R, C, T = 14336, 4096, 4096
+    wbits = synth.rowscaled(R, C, 5)
+    os.environ["EP_NUM_THREADS"] = str(min(16, os.cpu_count() or 1))
+    c = ep.compress(wbits, target_bpp, dtype=torch.bfloat16)
+    os.environ.pop("EP_NUM_THREADS", None)
+    c.upload()
+    x = torch.from_numpy(synth.activations(T, C, 50)).view(torch.bfloat16).cuda()
+    w = torch.from_numpy(wbits).view(torch.bfloat16).cuda()
+    y = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
+    need = L.ep_linear_workspace_bytes(c.handle)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream()
+    sp = int(st.cuda_stream)
+    wd = ws.data_ptr() + ((256 - ws.data_ptr() % 256) % 256)
+
+    def timeit(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_fused = timeit(lambda: L.ep_compressed_linear_forward(c.handle, x.data_ptr(), T, None, y.data_ptr(),
+                                                            ws.data_ptr(), need, sp))
+    t_dec = timeit(lambda: L.ep_decompress(c.handle, wd, sp))
+    t_gemm = timeit(lambda: L.ep_gemm_bf16_nt(x.data_ptr(), w.data_ptr(), None, y.data_ptr(), T, R, C, sp))
+    t_torch = timeit(lambda: torch.matmul(x, w.t()))
+    flops = 2.0 * T * R * C
+    return {
+        "workload": "CompressedLinear prefill 14336x4096 weight @%.1f bpp, 4096 tokens" % target_bpp,
+        "actual_bpp": round(c.actual_bpp, 4),
+        "ms_decode_plus_gemm": round(t_fused, 4), "ms_decode": round(t_dec, 4), "ms_gemm_plain_bf16": round(t_gemm, 4),
+        "ms_torch_matmul_hipblaslt": round(t_torch, 4),
+        "overhead_pct_vs_our_gemm": round(100.0 * (t_fused / t_gemm - 1.0), 2),
+        "overhead_pct_vs_hipblaslt": round(100.0 * (t_fused / t_torch - 1.0), 2),
+        "gemm_mfma_util": round(flops / (t_gemm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "gemm_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 1),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); multi-GPU decode is not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    comps, blocks = build_stack(a.matrices, a.target_bpp)
+    outs = [torch.empty(c.shape, dtype=torch.bfloat16, device="cuda") for c in comps]
+    n_params = sum(c.shape[0] * c.shape[1] for c in comps)
+    blob_bytes = sum(c.nbytes for c in comps)
+    out_bytes = 2 * n_params
+
+    ms, launch_ms, units = time_stack(comps, blocks, outs, a.steps, a.warmup)
+    errs = sum(c.device_errors() for c in comps)
+    if errs:
+        raise SystemExit(f"decode reported {errs} failed chains")
+    kern_ms = sum(launch_ms)
+    alg_bytes = blob_bytes + out_bytes
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    result = {
+        "metric": "weight decode GB/s (BF16 out) & % HBM roofline; fused-linear overhead %",
+        "value": round(out_bytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
+        "data": "synthetic (seeded; trained weights unavailable)",
+        "config": {"workload": f"{len(comps)}-matrix DiT-shaped BF16 stack (30 blocks x q,k,v,o 3840^2, w1,w3 "
+                               f"10240x3840, w2 3840x10240, mod1,mod2 3840^2 + 6 x 3840^2), target "
+                               f"{a.target_bpp} bpp, decoded block by block (one launch per 9-matrix block)",
+                   "params": n_params, "compressed_bytes": blob_bytes,
+                   "actual_bpp": round(8.0 * blob_bytes / n_params, 4), "launches_per_step": len(units)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel (BF16 out)", "avg_launch_ms": round(kern_ms / len(units), 5),
+                     "algorithmic_bytes_per_launch": round(alg_bytes / len(units))},
+    }
+    if not a.no_layer_mode:
+        ms_l, lms, units_l = time_stack(comps, blocks, outs, max(2, a.steps // 2), 1, per_layer=True)
+        result["per_layer_mode"] = {"ms_per_step": round(ms_l, 4),
+                                    "bf16_out_GBps": round(out_bytes / (ms_l * 1e-3) / 1e9, 2),
+                                    "hbm_frac": round(alg_bytes / (sum(lms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                    "launches_per_step": len(units_l)}
+    del outs
+    torch.cuda.empty_cache()
+    if not a.no_linear:
+        result["fused_linear"] = fused_linear(a.target_bpp)
+    if not a.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(a.target_bpp)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

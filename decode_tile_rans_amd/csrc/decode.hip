@@ -40,11 +40,6 @@ enum OutKind { OUT_BF16 = 0, OUT_BF16_SAT = 1, OUT_FP16 = 2, OUT_FP32 = 3, OUT_F
 constexpr int kTabWords = kNumCtx * kM;          // 14336 u32
 constexpr int kTabBytes = kTabWords * 4;         // 57344 B
 constexpr uint32_t kEscBit = 1u << 22;
-// LDS span slack (dwords) on each side of a wave's staged stream span.  A lane moves at
-// most 3 words per coordinate (symbol + two bypasses), 24 per group, and its pointer is
-// clamped to its own region at every group boundary, so even a corrupt stream never
-// reads outside [span - 64 words, span + len + 64 words).
-constexpr int kSlackDw = 32;
 
 struct DecJob {
   const uint16_t* stream;
@@ -159,60 +154,44 @@ __device__ inline void store_group(void* out, int64_t base, const int32_t* u, fl
 
 // ---------------------------------------------------------------- the decode kernel
 constexpr int kMaxBatch = 12;
+constexpr int kRingWords = 32;                  // per-lane LDS ring (16-bit words)
+constexpr int kRingDw = kRingWords / 2;
+constexpr int kWaveRingBytes = 64 * kRingWords * 2;   // 4 KB per wave
+constexpr int kMaxWaves = 16;
 
 // Job descriptors travel by value in the kernel arguments (no per-launch copy).
 struct DecBatch {
   DecJob j[kMaxBatch];
   int n;
-  int span_stride_dw;
 };
 
-template <int OUT, bool ESC, bool LDS_SPAN>
-__global__ void __launch_bounds__(256) decode_kernel(const DecBatch B) {
+template <int OUT, bool ESC>
+__global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   extern __shared__ __align__(16) uint32_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int nwaves = blockDim.x >> 6;
 
-  const int span_stride_dw = B.span_stride_dw;
   // which job (uniform per workgroup)
   int ji = 0;
   for (int q = 1; q < B.n; ++q)
     if (B.j[q].wg_begin <= (int64_t)blockIdx.x) ji = q;
   const DecJob& J = B.j[ji];
   const int64_t blk = J.block_lo + ((int64_t)blockIdx.x - J.wg_begin) * nwaves + wave;
-  const bool blk_ok = blk < J.n_blocks;
 
-  // stage the decode tables
+  // stage the decode tables (shared by the workgroup's waves)
   {
     const uint4* src = (const uint4*)J.tab;
     uint4* dst = (uint4*)smem;
     for (int i = tid; i < kTabWords / 4; i += blockDim.x) dst[i] = src[i];
   }
-  // stage this wave's stream span [ckpt[blk], ckpt[blk+1]) (both even)
-  uint16_t* span = nullptr;
-  int64_t span_word0 = 0;   // stream word index held at span[0]
-  if (LDS_SPAN) {
-    uint32_t* sdw = smem + kTabWords + wave * span_stride_dw;
-    span = (uint16_t*)(sdw + kSlackDw);   // front slack
-    if (blk_ok) {
-      uint32_t w0 = J.ckpt[blk], w1 = J.ckpt[blk + 1];
-      uint32_t d0 = (w0 >> 1) & ~3u;            // 16-byte aligned start (dwords)
-      uint32_t d1 = (w1 >> 1);
-      uint32_t n16 = (d1 - d0 + 3) >> 2;
-      const uint4* src = (const uint4*)((const uint32_t*)J.stream + d0);
-      uint4* dst = (uint4*)(sdw + kSlackDw);
-      for (uint32_t i = lane; i < n16; i += 64) dst[i] = src[i];
-      span_word0 = (int64_t)d0 * 2;
-    }
-  }
   __syncthreads();
-  if (!blk_ok) return;
+  if (blk >= J.n_blocks) return;
 
   const int S = 1 << J.log2S;
   const int64_t chain = blk * 64 + lane;
-  // region start via wave prefix sum of the 32 region lengths
+  // region start via a wave prefix sum of the block's 32 region lengths
   const int64_t reg = blk * 32 + (lane >> 1);
   const uint32_t rl = (reg < J.n_regions) ? (uint32_t)J.rlen[reg] : 0u;
   uint32_t v = (lane & 1) ? 0u : rl;
@@ -221,22 +200,10 @@ __global__ void __launch_bounds__(256) decode_kernel(const DecBatch B) {
     uint32_t t = __shfl_up(v, d, 64);
     if (lane >= d) v += t;
   }
-  const uint32_t rstart = v - rl;
+  const uint32_t rstart = J.ckpt[blk] + v - rl;      // absolute word index of the region start
+  const uint32_t rend = rstart + rl;                 // one past the region
   const bool fwd = (lane & 1) == 0;
   const int dir = fwd ? 1 : -1;
-  const int64_t blk_word0 = J.ckpt[blk];
-  // word index relative to span[0] (LDS) or absolute (global)
-  int64_t ptr = blk_word0 + (fwd ? (int64_t)rstart : (int64_t)rstart + rl - 1) - span_word0;
-  const int64_t gmax = (int64_t)J.n_words - 1;
-  // the lane's region in the same coordinates (valid decodes stay within [lo-1, hi])
-  const int64_t reg_lo = blk_word0 + (int64_t)rstart - span_word0 - 1;
-  const int64_t reg_hi = reg_lo + 1 + rl;
-
-  auto load_word = [&](int64_t p) -> uint32_t {
-    if (LDS_SPAN) return (uint32_t)span[p];
-    int64_t q = p < 0 ? 0 : (p > gmax ? gmax : p);
-    return gmax >= 0 ? (uint32_t)J.stream[q] : 0u;
-  };
 
   const bool live = chain < J.n_chains && chain >= J.chain_lo && chain < J.chain_hi;
   const int64_t t = chain >> J.log2S;
@@ -245,17 +212,69 @@ __global__ void __launch_bounds__(256) decode_kernel(const DecBatch B) {
   if (gt > kTileGroups) gt = kTileGroups;
   const int ngr = (live && gt > j) ? (int)((gt - j + S - 1) >> J.log2S) : 0;
   uint32_t x = (chain < J.n_chains) ? J.states[chain] : kL;
+
+  // ---- per-lane ring of stream words: word w lives in ring[w % 32].
+  // Invariant: whenever the lane reads word `pos` from the ring, it is resident.  A group
+  // consumes at most 8 words for its symbols, so each group starts with >= 9 resident
+  // words ahead; an escape consumes at most 2 more, so escapes top up to >= 11 first.
+  // 16-byte chunks (8 words, 16-byte aligned) are loaded one group ahead of use.
+  uint16_t* ring = (uint16_t*)(smem + kTabWords + (wave * 64 + lane) * kRingDw);
+  const uint4* chunks = (const uint4*)J.stream;
+  // fwd: fetched words end at `fetch` (multiple of 8); bwd: fetched words begin at `fetch`
+  uint32_t pos = fwd ? rstart : rend - 1;            // next word to consume
+  uint32_t fetch = fwd ? (rstart & ~7u) : ((rend + 7u) & ~7u);
+  const uint32_t lim_hi = (rend + 7u) & ~7u;
+  const uint32_t lim_lo = rstart & ~7u;
+  uint4 pend = make_uint4(0, 0, 0, 0);
+  uint32_t pend_c = 0;
+  bool have_pend = false;
+  auto resident = [&]() -> int {                     // words from pos on that are in the ring
+    int a = fwd ? (int)(fetch - pos) : (int)(pos + 1 - fetch);
+    return have_pend ? a - 8 : a;
+  };
+  auto more = [&]() -> bool { return fwd ? fetch < lim_hi : fetch > lim_lo; };
+  auto next_chunk = [&]() -> uint32_t {
+    uint32_t c = fwd ? fetch : fetch - 8u;
+    fetch = fwd ? fetch + 8u : fetch - 8u;
+    return c;
+  };
+  auto put = [&](uint32_t c, uint4 d) { *(uint4*)(ring + (c & (kRingWords - 1))) = d; };
+  auto flush_pend = [&]() {
+    if (have_pend) {
+      put(pend_c, pend);
+      have_pend = false;
+    }
+  };
+  auto top_up = [&](int need) {                      // synchronous; rare after the prime
+    flush_pend();
+    while (resident() < need && more()) {
+      uint32_t c = next_chunk();
+      put(c, chunks[c >> 3]);
+    }
+  };
+  if (live && rl) {
+    // prime: two chunks loaded together (>= 9 words ahead of any start position)
+    uint4 d0 = make_uint4(0, 0, 0, 0), d1 = d0;
+    uint32_t c0 = 0, c1 = 0;
+    bool h0 = false, h1 = false;
+    if (more()) { c0 = next_chunk(); d0 = chunks[c0 >> 3]; h0 = true; }
+    if (more()) { c1 = next_chunk(); d1 = chunks[c1 >> 3]; h1 = true; }
+    if (h0) put(c0, d0);
+    if (h1) put(c1, d1);
+    top_up(9);
+  }
+  uint32_t nw = ring[pos & (kRingWords - 1)];
+
   int64_t g = (t << 9) + j;
   int64_t row = live ? g / J.G : 0;
   int64_t col = g - row * J.G;
-  uint32_t nw = live ? load_word(ptr) : 0u;
   const int k = J.k;
 
   auto renorm = [&]() {
     if (x < kL) {
       x = (x << 16) | nw;
-      ptr += dir;
-      nw = load_word(ptr);
+      pos += dir;
+      nw = ring[pos & (kRingWords - 1)];
     }
   };
   auto step = [&](const uint32_t* tb) -> uint32_t {
@@ -271,6 +290,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const DecBatch B) {
     return r;
   };
   auto escape = [&](uint32_t e, int last, int pi) -> int32_t {
+    if (resident() < 11) top_up(11);
     uint32_t info = e >> 23;
     int c = (int)(info & 1u), neg = (int)((info >> 1) & 1u), top2 = (int)((info >> 2) & 3u);
     int ex = k + (int)(info >> 4);
@@ -283,10 +303,25 @@ __global__ void __launch_bounds__(256) decode_kernel(const DecBatch B) {
     return neg ? -uu : uu;
   };
 
-  const int steps = kTileGroups >> J.log2S;
-  for (int kk = 0; kk < steps; ++kk) {
-    if (kk >= ngr) break;
-    const float h = J.hr[row];
+  float h = ngr > 0 ? J.hr[row] : 0.f;
+  for (int kk = 0; kk < ngr; ++kk) {
+    // ---- keep the ring fed: land last group's chunk, guarantee 9 resident words,
+    // then start loading the next chunk if its ring slots are already consumed
+    flush_pend();
+    if (resident() < 9) top_up(9);
+    if ((fwd ? (int)(fetch - pos) : (int)(pos + 1 - fetch)) <= kRingWords - 8 && more()) {
+      pend_c = next_chunk();
+      pend = chunks[pend_c >> 3];
+      have_pend = true;
+    }
+    // ---- row scale of the next group, loaded one group ahead
+    int64_t nrow = row, ncol = col + S;
+    while (ncol >= J.G) {
+      ncol -= J.G;
+      ++nrow;
+    }
+    const float h_next = (kk + 1 < ngr) ? J.hr[nrow] : 0.f;
+
     int32_t u[8];
     uint32_t e = step(smem);
     u[0] = (int32_t)e >> 23;
@@ -309,12 +344,9 @@ __global__ void __launch_bounds__(256) decode_kernel(const DecBatch B) {
     const int64_t c0 = col * 8;
     const bool full = J.c8 || (c0 + 8 <= J.C);
     store_group<OUT>(J.out, row * J.C + c0, u, h, full, J.C - c0);
-    ptr = ptr < reg_lo ? reg_lo : (ptr > reg_hi ? reg_hi : ptr);
-    col += S;
-    while (col >= J.G) {
-      col -= J.G;
-      ++row;
-    }
+    row = nrow;
+    col = ncol;
+    h = h_next;
   }
   if (live && x != kL) atomicAdd(J.err, 1u);
 }
@@ -332,10 +364,10 @@ int lds_max_bytes() {
   return v;
 }
 
-template <int OUT, bool ESC, bool LDS_SPAN>
+template <int OUT, bool ESC>
 int launch_t(const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
-  auto kern = decode_kernel<OUT, ESC, LDS_SPAN>;
-  size_t lds = (size_t)kTabBytes + (LDS_SPAN ? (size_t)waves * B.span_stride_dw * 4 : 0);
+  auto kern = decode_kernel<OUT, ESC>;
+  size_t lds = (size_t)kTabBytes + (size_t)waves * kWaveRingBytes;
   static std::once_flag once;
   std::call_once(once, [&] {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max_bytes());
@@ -344,22 +376,21 @@ int launch_t(const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
   return hip_check(hipGetLastError(), "decode launch");
 }
 
-template <bool ESC, bool LDS_SPAN>
+template <bool ESC>
 int launch_out(int out, const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
   switch (out) {
-    case OUT_BF16: return launch_t<OUT_BF16, ESC, LDS_SPAN>(B, n_wg, waves, st);
-    case OUT_BF16_SAT: return launch_t<OUT_BF16_SAT, ESC, LDS_SPAN>(B, n_wg, waves, st);
-    case OUT_FP16: return launch_t<OUT_FP16, ESC, LDS_SPAN>(B, n_wg, waves, st);
-    case OUT_FP32: return launch_t<OUT_FP32, ESC, LDS_SPAN>(B, n_wg, waves, st);
-    case OUT_FP8: return launch_t<OUT_FP8, ESC, LDS_SPAN>(B, n_wg, waves, st);
-    case OUT_INT8: return launch_t<OUT_INT8, ESC, LDS_SPAN>(B, n_wg, waves, st);
-    default: return launch_t<OUT_COORDS, ESC, LDS_SPAN>(B, n_wg, waves, st);
+    case OUT_BF16: return launch_t<OUT_BF16, ESC>(B, n_wg, waves, st);
+    case OUT_BF16_SAT: return launch_t<OUT_BF16_SAT, ESC>(B, n_wg, waves, st);
+    case OUT_FP16: return launch_t<OUT_FP16, ESC>(B, n_wg, waves, st);
+    case OUT_FP32: return launch_t<OUT_FP32, ESC>(B, n_wg, waves, st);
+    case OUT_FP8: return launch_t<OUT_FP8, ESC>(B, n_wg, waves, st);
+    case OUT_INT8: return launch_t<OUT_INT8, ESC>(B, n_wg, waves, st);
+    default: return launch_t<OUT_COORDS, ESC>(B, n_wg, waves, st);
   }
 }
 
-int launch_any(int out, bool esc, bool lds_span, const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
-  if (esc) return lds_span ? launch_out<true, true>(out, B, n_wg, waves, st) : launch_out<true, false>(out, B, n_wg, waves, st);
-  return lds_span ? launch_out<false, true>(out, B, n_wg, waves, st) : launch_out<false, false>(out, B, n_wg, waves, st);
+int launch_any(int out, bool esc, const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
+  return esc ? launch_out<true>(out, B, n_wg, waves, st) : launch_out<false>(out, B, n_wg, waves, st);
 }
 
 int out_kind(const Blob& b) {
@@ -399,39 +430,19 @@ DecJob make_job(const Blob& b, void* out) {
   return j;
 }
 
-// span staging: words + up to 6 alignment words, slack on both sides
-int span_stride_dw(uint32_t max_span_words) {
-  uint32_t dw = (max_span_words + 8 + 1) / 2 + 2 * kSlackDw;
-  return (int)((dw + 3) & ~3u);
-}
-
-struct LaunchShape {
-  bool lds_span;
-  int waves;
-  int sdw;
-};
-
-LaunchShape pick_shape(uint32_t max_span_words) {
-  LaunchShape s;
-  s.sdw = span_stride_dw(max_span_words);
-  const int budget = lds_max_bytes() - kTabBytes;
-  const int per_wave = s.sdw * 4;
-  int w = budget / per_wave;
+// Waves per workgroup.  One table copy (56 KB of LDS) serves the workgroup; each wave
+// adds a 4 KB ring.  Small launches use small workgroups so the blocks spread over all
+// 256 CUs; big launches use up to 16 waves (4 per SIMD) to hide the per-step latency.
+int pick_waves(int64_t n_blocks) {
+  const int cus = 256;
+  int w = (int)std::min<int64_t>(kMaxWaves, std::max<int64_t>(1, (n_blocks + cus - 1) / cus));
+  const int by_lds = (lds_max_bytes() - kTabBytes) / kWaveRingBytes;
+  w = std::min(w, by_lds);
   if (const char* e = std::getenv("EP_DECODE_WAVES")) {
     int v = std::atoi(e);
-    if (v >= 1 && v <= 4) w = std::min(w, v);
+    if (v >= 1 && v <= kMaxWaves) w = std::min(v, by_lds);
   }
-  const char* sp = std::getenv("EP_DECODE_SPAN");    // "global": read words from HBM/L2
-  if (sp && std::strcmp(sp, "global") == 0) w = 0;
-  if (w >= 1) {
-    s.lds_span = true;
-    s.waves = std::min(w, 4);
-  } else {
-    s.lds_span = false;
-    s.waves = 4;
-    s.sdw = 0;
-  }
-  return s;
+  return std::max(w, 1);
 }
 
 int check_uploaded(const Blob& b) {
@@ -455,15 +466,14 @@ int decode_one(const Blob& b, void* dst, int64_t chain_lo, int64_t chain_hi, int
   const int64_t bhi = (chain_hi + kBlockChains - 1) / kBlockChains;
   if (bhi <= blo) return EP_OK;
   j.block_lo = blo;
-  LaunchShape s = pick_shape(b.max_span_words);
   const int64_t nblk = bhi - blo;
-  const int64_t n_wg = (nblk + s.waves - 1) / s.waves;
+  const int waves = pick_waves(nblk);
+  const int64_t n_wg = (nblk + waves - 1) / waves;
   j.n_blocks = bhi;   // blocks beyond the range are skipped
   DecBatch B{};
   B.j[0] = j;
   B.n = 1;
-  B.span_stride_dw = s.sdw;
-  return launch_any(out, (b.flags & kFlagEsc) != 0, s.lds_span, B, n_wg, s.waves, st);
+  return launch_any(out, (b.flags & kFlagEsc) != 0, B, n_wg, waves, st);
 }
 
 }  // namespace
@@ -566,7 +576,7 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
   // all blobs of one launch share the container kind and the escape path
   int out = -1;
   bool esc = false;
-  uint32_t max_span = 0;
+  int64_t total_blocks = 0;
   for (int i = 0; i < n; ++i) {
     if (!blobs[i] || !dsts[i]) return fail(EP_E_ARG, "null blob or destination");
     const Blob& b = blobs[i]->b;
@@ -580,21 +590,20 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
       out = (out == OUT_BF16_SAT || o == OUT_BF16_SAT) ? OUT_BF16_SAT : OUT_BF16;
     else if (o != out) return fail(EP_E_ARG, "batch mixes container dtypes");
     esc |= (b.flags & kFlagEsc) != 0;
-    max_span = std::max(max_span, b.max_span_words);
+    total_blocks += b.n_blocks;
   }
-  LaunchShape s = pick_shape(max_span);
+  const int waves = pick_waves(total_blocks);
   // up to kMaxBatch blobs per launch
   for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
     DecBatch B{};
     B.n = std::min(kMaxBatch, n - i0);
-    B.span_stride_dw = s.sdw;
     int64_t wg = 0;
     for (int q = 0; q < B.n; ++q) {
       B.j[q] = make_job(blobs[i0 + q]->b, dsts[i0 + q]);
       B.j[q].wg_begin = wg;
-      wg += (B.j[q].n_blocks + s.waves - 1) / s.waves;
+      wg += (B.j[q].n_blocks + waves - 1) / waves;
     }
-    int rc = launch_any(out, esc, s.lds_span, B, wg, s.waves, (hipStream_t)stream);
+    int rc = launch_any(out, esc, B, wg, waves, (hipStream_t)stream);
     if (rc) return rc;
   }
   return EP_OK;

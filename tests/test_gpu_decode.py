@@ -78,12 +78,7 @@ def test_rates_and_escapes(t):
         assert oracle.parse_blob(blob).flags & 1      # escapes exercised
 
 
-def test_global_word_path():
-    _check("global words", synth.rowscaled(300, 1024, 7), nx.DT_BF16, 5.0, S=8, env={"EP_DECODE_SPAN": "global"})
-    _check("global words S1", synth.small_gauss(), nx.DT_BF16, 3.5, env={"EP_DECODE_SPAN": "global"})
-
-
-@pytest.mark.parametrize("waves", ["1", "2", "3"])
+@pytest.mark.parametrize("waves", ["1", "2", "5", "16"])
 def test_workgroup_sizes(waves):
     _check(f"waves={waves}", synth.rowscaled(257, 1024, 8), nx.DT_BF16, 4.0, S=8, env={"EP_DECODE_WAVES": waves})
 
