@@ -45,7 +45,24 @@ def parse():
     p.add_argument("--no-linear", action="store_true")
     p.add_argument("--no-layer-mode", action="store_true")
     p.add_argument("--matrices", type=int, default=276, help="first N matrices of the stack (profiling runs)")
+    p.add_argument("--streams", type=int, default=2, help="HIP streams the block launches rotate over")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration(reps=5):
+    """A plain copy kernel of known size: FETCH_SIZE / WRITE_SIZE of this run give the
+    counter scale (bytes moved per counted KiB) for the decode kernel's traffic."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": reps}))
 
 
 def build_stack(n, target_bpp):
@@ -75,35 +92,55 @@ def build_stack(n, target_bpp):
     return comps, [blocks[b] for b in sorted(blocks)]
 
 
-def time_stack(comps, blocks, outs, steps, warmup, per_layer=False):
+def time_stack(comps, blocks, outs, steps, warmup, per_layer=False, n_streams=1):
+    """Time `steps` passes over the stack.  Consecutive launches rotate over n_streams
+    streams (default priority) so one launch's tail overlaps the next one's start; every
+    pass ends with all streams joined."""
     import torch
     from decode_tile_rans_amd import _lib as L
-    st = torch.cuda.current_stream()
-    sp = int(st.cuda_stream)
+    main = torch.cuda.current_stream()
+    streams = [main] + [torch.cuda.Stream() for _ in range(n_streams - 1)]
     handles = [c.handle for c in comps]
     ptrs = [o.data_ptr() for o in outs]
     units = [[i] for i in range(len(comps))] if per_layer else blocks
 
-    def launch(u):
+    def launch(k, u):
+        sp = int(streams[k % n_streams].cuda_stream)
         if len(u) == 1:
             L.ep_decompress(handles[u[0]], ptrs[u[0]], sp)
         else:
             L.ep_decompress_batch([handles[i] for i in u], [ptrs[i] for i in u], sp)
 
+    def fork():
+        ev = torch.cuda.Event()
+        ev.record(main)
+        for s in streams[1:]:
+            s.wait_event(ev)
+
+    def join():
+        for s in streams[1:]:
+            ev = torch.cuda.Event()
+            ev.record(s)
+            main.wait_event(ev)
+
     for _ in range(warmup):
-        for u in units:
-            launch(u)
+        fork()
+        for k, u in enumerate(units):
+            launch(k, u)
+        join()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in units]
-    launch_ms = []
     t0 = time.perf_counter()
     for s in range(steps):
+        fork()
         for k, u in enumerate(units):
+            st = streams[k % n_streams]
             if s == steps - 1:
                 ev[k][0].record(st)
-            launch(u)
+            launch(k, u)
             if s == steps - 1:
                 ev[k][1].record(st)
+        join()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = [a.elapsed_time(b) for a, b in ev]
@@ -192,13 +229,18 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
+    if a.copy_calibration:
+        copy_calibration()
+        return
     comps, blocks = build_stack(a.matrices, a.target_bpp)
     outs = [torch.empty(c.shape, dtype=torch.bfloat16, device="cuda") for c in comps]
     n_params = sum(c.shape[0] * c.shape[1] for c in comps)
     blob_bytes = sum(c.nbytes for c in comps)
     out_bytes = 2 * n_params
 
-    ms, launch_ms, units = time_stack(comps, blocks, outs, a.steps, a.warmup)
+    ms, _, units = time_stack(comps, blocks, outs, a.steps, a.warmup, n_streams=a.streams)
+    # per-launch kernel time for the roofline: one stream, launches back to back
+    _, launch_ms, _ = time_stack(comps, blocks, outs, 2, 1, n_streams=1)
     errs = sum(c.device_errors() for c in comps)
     if errs:
         raise SystemExit(f"decode reported {errs} failed chains")
@@ -216,18 +258,21 @@ def main():
                                f"10240x3840, w2 3840x10240, mod1,mod2 3840^2 + 6 x 3840^2), target "
                                f"{a.target_bpp} bpp, decoded block by block (one launch per 9-matrix block)",
                    "params": n_params, "compressed_bytes": blob_bytes,
-                   "actual_bpp": round(8.0 * blob_bytes / n_params, 4), "launches_per_step": len(units)},
+                   "actual_bpp": round(8.0 * blob_bytes / n_params, 4), "launches_per_step": len(units),
+                   "streams": a.streams},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "decode_kernel (BF16 out)", "avg_launch_ms": round(kern_ms / len(units), 5),
-                     "algorithmic_bytes_per_launch": round(alg_bytes / len(units))},
+                     "algorithmic_bytes_per_launch": round(alg_bytes / len(units)),
+                     "step_effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1)},
     }
     if not a.no_layer_mode:
-        ms_l, lms, units_l = time_stack(comps, blocks, outs, max(2, a.steps // 2), 1, per_layer=True)
+        ms_l, lms, units_l = time_stack(comps, blocks, outs, max(2, a.steps // 2), 1, per_layer=True,
+                                        n_streams=max(a.streams, 4))
         result["per_layer_mode"] = {"ms_per_step": round(ms_l, 4),
                                     "bf16_out_GBps": round(out_bytes / (ms_l * 1e-3) / 1e9, 2),
                                     "hbm_frac": round(alg_bytes / (sum(lms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                    "launches_per_step": len(units_l)}
+                                    "launches_per_step": len(units_l), "streams": max(a.streams, 4)}
     del outs
     torch.cuda.empty_cache()
     if not a.no_linear:

@@ -39,7 +39,9 @@ enum OutKind { OUT_BF16 = 0, OUT_BF16_SAT = 1, OUT_FP16 = 2, OUT_FP32 = 3, OUT_F
 
 constexpr int kTabWords = kNumCtx * kM;          // 14336 u32
 constexpr int kTabBytes = kTabWords * 4;         // 57344 B
-constexpr uint32_t kEscBit = 1u << 22;
+// packed table entry: f (bits 0..10) | bias (11..21) | value (22..30) | escape (31);
+// value = doubled coordinate u (signed 9 bit) or, for escapes, c | neg<<1 | top2<<2 | (e-k)<<4
+constexpr int kValShift = 22;
 
 struct DecJob {
   const uint16_t* stream;
@@ -56,6 +58,8 @@ struct DecJob {
   int64_t wg_begin;          // batch: first workgroup of this job
   uint32_t n_words;
   int log2S, k, c8;
+  uint32_t s_div_g, s_mod_g;   // S = s_div_g * G + s_mod_g (group stride in rows / columns)
+  uint32_t R;
 };
 
 // ---------------------------------------------------------------- container stores
@@ -98,11 +102,17 @@ __device__ inline uint32_t f32_to_i8(float v) {
   return (uint32_t)((int32_t)r) & 0xFFu;
 }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Write one group: v = reconstructed fp32 weights, u = doubled coordinates (COORDS).
 template <int OUT>
-__device__ inline void store_group(void* out, int64_t base, const int32_t* u, float h, bool full, int64_t nvalid) {
+__device__ inline void store_group(void* out, int64_t base, const float* vin, const int32_t* u, bool full,
+                                   int64_t nvalid) {
   float v[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = h * (float)u[i];
+  for (int i = 0; i < 8; ++i) v[i] = vin[i];
   if (OUT == OUT_BF16_SAT) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = fminf(fmaxf(v[i], -3.38953139e38f), 3.38953139e38f);
@@ -110,19 +120,30 @@ __device__ inline void store_group(void* out, int64_t base, const int32_t* u, fl
   if (OUT == OUT_BF16 || OUT == OUT_BF16_SAT || OUT == OUT_FP16) {
     uint32_t p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      p[i] = (OUT == OUT_FP16) ? pack_f16x2(v[2 * i], v[2 * i + 1]) : pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    for (int i = 0; i < 4; ++i) {
+      if (OUT == OUT_FP16) {
+        p[i] = pack_f16x2(v[2 * i], v[2 * i + 1]);
+      } else {
+        f32x2 fv = {v[2 * i], v[2 * i + 1]};
+        p[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(fv, bf16x2));
+      }
+    }
     uint16_t* o = (uint16_t*)out + base;
     if (full) {
-      *(uint4*)o = make_uint4(p[0], p[1], p[2], p[3]);
+      // streaming store: the weights are written once, so they should not evict the
+      // compressed stream's lines from L2 (the lanes re-read those lines chunk by chunk)
+      u32x4 pv = {p[0], p[1], p[2], p[3]};
+      __builtin_nontemporal_store(pv, (u32x4*)o);
     } else {
       for (int i = 0; i < nvalid; ++i) o[i] = (uint16_t)(p[i >> 1] >> ((i & 1) * 16));
     }
   } else if (OUT == OUT_FP32) {
     float* o = (float*)out + base;
     if (full) {
-      *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
-      *(float4*)(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      typedef __attribute__((ext_vector_type(4))) float f32x4;
+      f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+      __builtin_nontemporal_store(a, (f32x4*)o);
+      __builtin_nontemporal_store(b, (f32x4*)(o + 4));
     } else {
       for (int i = 0; i < nvalid; ++i) o[i] = v[i];
     }
@@ -137,7 +158,9 @@ __device__ inline void store_group(void* out, int64_t base, const int32_t* u, fl
     }
     uint8_t* o = (uint8_t*)out + base;
     if (full) {
-      *(uint2*)o = make_uint2(lo, hi);
+      typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+      u32x2 pv = {lo, hi};
+      __builtin_nontemporal_store(pv, (u32x2*)o);
     } else {
       for (int i = 0; i < nvalid; ++i) o[i] = (uint8_t)((i < 4 ? lo : hi) >> (8 * (i & 3)));
     }
@@ -154,7 +177,16 @@ __device__ inline void store_group(void* out, int64_t base, const int32_t* u, fl
 
 // ---------------------------------------------------------------- the decode kernel
 constexpr int kMaxBatch = 12;
-constexpr int kRingWords = 32;                  // per-lane LDS ring (16-bit words)
+#ifndef EP_RING_WORDS
+#define EP_RING_WORDS 32
+#endif
+#ifndef EP_CHUNK_WORDS
+#define EP_CHUNK_WORDS 8
+#endif
+constexpr int kRingWords = EP_RING_WORDS;       // per-lane LDS ring (16-bit words)
+constexpr int kChunkWords = EP_CHUNK_WORDS;     // words per stream load (multiple of 8)
+constexpr int kChunkVec = kChunkWords / 8;      // 16-byte loads per chunk
+static_assert(kRingWords - kChunkWords >= 17, "ring too small for two groups plus a chunk");
 constexpr int kRingDw = kRingWords / 2;
 constexpr int kWaveRingBytes = 64 * kRingWords * 2;   // 4 KB per wave
 constexpr int kMaxWaves = 16;
@@ -165,8 +197,43 @@ struct DecBatch {
   int n;
 };
 
-template <int OUT, bool ESC>
+// Entry layouts (chosen per blob when its tables are expanded):
+//   wide   (K = 128): f 0..10 | bias 11..21 | u or escape info 22..30 (9 bit) | escape 31
+//   narrow (K <= 64): f 0..10 | bias 11..21 | c 22 | escape 23 | u + 128 or escape info 24..31
+// In both, bit 22 is the coset of a FIRST symbol.  The parity of floor(u/2) (bit 1 of u)
+// sits at bit 23 (wide) or 25 (narrow).
+template <bool NARROW>
+struct EntryLayout {
+  static constexpr uint32_t kEsc = NARROW ? (1u << 23) : (1u << 31);
+  static constexpr int kPar = NARROW ? 25 : 23;
+  __device__ static int32_t u_of(uint32_t e) {
+    return NARROW ? (int32_t)(e >> 24) - 128 : __builtin_amdgcn_sbfe((int32_t)e, 22, 9);
+  }
+  // fl32(h * u) for a direct symbol: narrow uses the exact fma(u + 128, h, -128 h)
+  __device__ static float w_of(uint32_t e, float h, float nh128) {
+    return NARROW ? __builtin_fmaf((float)(e >> 24), h, nh128) : h * (float)u_of(e);
+  }
+  // escape info: c, neg, top2, e - k
+  __device__ static void esc_info(uint32_t e, int& c, int& neg, int& top2, int& er) {
+    if (NARROW) {
+      uint32_t b = e >> 24;
+      c = (int)((e >> 22) & 1u);
+      neg = (int)(b & 1u);
+      top2 = (int)((b >> 1) & 3u);
+      er = (int)(b >> 3);
+    } else {
+      uint32_t i = (e >> 22) & 0x1FFu;
+      c = (int)(i & 1u);
+      neg = (int)((i >> 1) & 1u);
+      top2 = (int)((i >> 2) & 3u);
+      er = (int)(i >> 4);
+    }
+  }
+};
+
+template <int OUT, bool ESC, bool C8, bool NARROW>
 __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
+  using LY = EntryLayout<NARROW>;
   extern __shared__ __align__(16) uint32_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -201,9 +268,9 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
     if (lane >= d) v += t;
   }
   const uint32_t rstart = J.ckpt[blk] + v - rl;      // absolute word index of the region start
-  const uint32_t rend = rstart + rl;                 // one past the region
-  const bool fwd = (lane & 1) == 0;
-  const int dir = fwd ? 1 : -1;
+  const bool fwd = (lane & 1) == 0;                  // even chain reads up, odd chain reads down
+  const int32_t dir = fwd ? 1 : -1;
+  const uint32_t p0 = fwd ? rstart : rstart + rl - 1;   // the lane's first word
 
   const bool live = chain < J.n_chains && chain >= J.chain_lo && chain < J.chain_hi;
   const int64_t t = chain >> J.log2S;
@@ -213,32 +280,34 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   const int ngr = (live && gt > j) ? (int)((gt - j + S - 1) >> J.log2S) : 0;
   uint32_t x = (chain < J.n_chains) ? J.states[chain] : kL;
 
-  // ---- per-lane ring of stream words: word w lives in ring[w % 32].
-  // Invariant: whenever the lane reads word `pos` from the ring, it is resident.  A group
-  // consumes at most 8 words for its symbols, so each group starts with >= 9 resident
-  // words ahead; an escape consumes at most 2 more, so escapes top up to >= 11 first.
-  // 16-byte chunks (8 words, 16-byte aligned) are loaded one group ahead of use.
-  uint16_t* ring = (uint16_t*)(smem + kTabWords + (wave * 64 + lane) * kRingDw);
+  // ---- per-lane ring of stream words: word w lives at ring byte offset 2 (w % 32).
+  // q = words consumed, F = words resident from p0 on in the lane's direction, next = the
+  // next 16-byte chunk.  Invariant: the lane only reads resident words.  The ring is
+  // serviced every second group: at that point >= 17 words are resident (two groups'
+  // symbols consume <= 16); an escape consumes <= 2 more and tops up to >= 11 first.
+  // Chunks are loaded two groups before they are written into the ring.
+  const uint32_t ring_base = (uint32_t)(kTabBytes + (wave * 64 + lane) * kRingWords * 2);
+  uint8_t* const lds8 = (uint8_t*)smem;
   const uint4* chunks = (const uint4*)J.stream;
-  // fwd: fetched words end at `fetch` (multiple of 8); bwd: fetched words begin at `fetch`
-  uint32_t pos = fwd ? rstart : rend - 1;            // next word to consume
-  uint32_t fetch = fwd ? (rstart & ~7u) : ((rend + 7u) & ~7u);
-  const uint32_t lim_hi = (rend + 7u) & ~7u;
-  const uint32_t lim_lo = rstart & ~7u;
-  uint4 pend = make_uint4(0, 0, 0, 0);
+  uint32_t next = p0 & ~(uint32_t)(kChunkWords - 1);
+  int32_t F = fwd ? -(int32_t)(p0 & (kChunkWords - 1)) : (int32_t)(p0 & (kChunkWords - 1)) - (kChunkWords - 1);
+  const int32_t Fmax = (int32_t)rl;                 // region words in the lane's direction
+  const int32_t stepc = kChunkWords * dir;
+  uint4 pend[kChunkVec];
   uint32_t pend_c = 0;
   bool have_pend = false;
-  auto resident = [&]() -> int {                     // words from pos on that are in the ring
-    int a = fwd ? (int)(fetch - pos) : (int)(pos + 1 - fetch);
-    return have_pend ? a - 8 : a;
+  uint32_t a2 = 2u * p0;                            // 2 * (word index of the next word)
+  auto q_now = [&]() -> int32_t { return (int32_t)(a2 - 2u * p0) / 2 * dir; };
+  auto resident = [&]() -> int32_t { return F - q_now() - (have_pend ? kChunkWords : 0); };
+  auto put = [&](uint32_t c, const uint4* d) {
+#pragma unroll
+    for (int v = 0; v < kChunkVec; ++v)
+      *(uint4*)(lds8 + ring_base + (((c + 8u * v) & (kRingWords - 1)) << 1)) = d[v];
   };
-  auto more = [&]() -> bool { return fwd ? fetch < lim_hi : fetch > lim_lo; };
-  auto next_chunk = [&]() -> uint32_t {
-    uint32_t c = fwd ? fetch : fetch - 8u;
-    fetch = fwd ? fetch + 8u : fetch - 8u;
-    return c;
+  auto load = [&](uint32_t c, uint4* d) {
+#pragma unroll
+    for (int v = 0; v < kChunkVec; ++v) d[v] = chunks[(c >> 3) + v];
   };
-  auto put = [&](uint32_t c, uint4 d) { *(uint4*)(ring + (c & (kRingWords - 1))) = d; };
   auto flush_pend = [&]() {
     if (have_pend) {
       put(pend_c, pend);
@@ -247,34 +316,32 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   };
   auto top_up = [&](int need) {                      // synchronous; rare after the prime
     flush_pend();
-    while (resident() < need && more()) {
-      uint32_t c = next_chunk();
-      put(c, chunks[c >> 3]);
+    const int32_t q = q_now();
+    while (F - q < need && F < Fmax) {
+      uint32_t c = next;
+      next += stepc;
+      F += kChunkWords;
+      uint4 d[kChunkVec];
+      load(c, d);
+      put(c, d);
     }
   };
-  if (live && rl) {
-    // prime: two chunks loaded together (>= 9 words ahead of any start position)
-    uint4 d0 = make_uint4(0, 0, 0, 0), d1 = d0;
-    uint32_t c0 = 0, c1 = 0;
-    bool h0 = false, h1 = false;
-    if (more()) { c0 = next_chunk(); d0 = chunks[c0 >> 3]; h0 = true; }
-    if (more()) { c1 = next_chunk(); d1 = chunks[c1 >> 3]; h1 = true; }
-    if (h0) put(c0, d0);
-    if (h1) put(c1, d1);
-    top_up(9);
-  }
-  uint32_t nw = ring[pos & (kRingWords - 1)];
+  if (live && rl) top_up(17);
+  const int32_t a2step = 2 * dir;
+  auto ring_word = [&]() -> uint32_t { return *(const uint16_t*)(lds8 + (ring_base | (a2 & 62u))); };
+  uint32_t nw = ring_word();
 
-  int64_t g = (t << 9) + j;
-  int64_t row = live ? g / J.G : 0;
-  int64_t col = g - row * J.G;
+  // ---- output position
+  const int64_t g0 = (t << 9) + j;
+  uint32_t row = live ? (uint32_t)(g0 / J.G) : 0u;
+  uint32_t col = live ? (uint32_t)(g0 - (int64_t)row * J.G) : 0u;
   const int k = J.k;
 
   auto renorm = [&]() {
     if (x < kL) {
       x = (x << 16) | nw;
-      pos += dir;
-      nw = ring[pos & (kRingWords - 1)];
+      a2 += a2step;
+      nw = ring_word();
     }
   };
   auto step = [&](const uint32_t* tb) -> uint32_t {
@@ -289,11 +356,12 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
     renorm();
     return r;
   };
+  // escape symbol (careful path): raw bits follow; returns the doubled coordinate
   auto escape = [&](uint32_t e, int last, int pi) -> int32_t {
     if (resident() < 11) top_up(11);
-    uint32_t info = e >> 23;
-    int c = (int)(info & 1u), neg = (int)((info >> 1) & 1u), top2 = (int)((info >> 2) & 3u);
-    int ex = k + (int)(info >> 4);
+    int c, neg, top2, er;
+    LY::esc_info(e, c, neg, top2, er);
+    int ex = k + er;
     int nb = ex - 2 - last;
     uint32_t raw = bypass(nb < 16 ? nb : 16);
     if (nb > 16) raw |= bypass(nb - 16) << 16;
@@ -303,47 +371,91 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
     return neg ? -uu : uu;
   };
 
+  char* outp = (char*)J.out;
+  constexpr int ESZ = (OUT == OUT_FP32 || OUT == OUT_COORDS) ? 4 : ((OUT == OUT_FP8 || OUT == OUT_INT8) ? 1 : 2);
+  char* optr = outp + (int64_t)(g0 * 8) * ESZ;      // C % 8 == 0: groups are contiguous
+  const int64_t ostep = (int64_t)S * 8 * ESZ;
   float h = ngr > 0 ? J.hr[row] : 0.f;
+  // a chunk load that is not needed reads the stream's first chunk: one line shared by
+  // every lane, always cached, always inside the stream allocation
+  const uint32_t safe_chunk = 0;
+
   for (int kk = 0; kk < ngr; ++kk) {
-    // ---- keep the ring fed: land last group's chunk, guarantee 9 resident words,
-    // then start loading the next chunk if its ring slots are already consumed
-    flush_pend();
-    if (resident() < 9) top_up(9);
-    if ((fwd ? (int)(fetch - pos) : (int)(pos + 1 - fetch)) <= kRingWords - 8 && more()) {
-      pend_c = next_chunk();
-      pend = chunks[pend_c >> 3];
-      have_pend = true;
+    // ---- ring service every second group (a fixed VMEM pattern: one chunk load)
+    if ((kk & 1) == 0) {
+      flush_pend();
+      if (F - q_now() < 17) top_up(17);
+      const bool issue = F - q_now() <= kRingWords - kChunkWords && F < Fmax;
+      pend_c = next;
+      load(issue ? next : safe_chunk, pend);
+      if (issue) {
+        next += stepc;
+        F += kChunkWords;
+      }
+      have_pend = issue;
     }
     // ---- row scale of the next group, loaded one group ahead
-    int64_t nrow = row, ncol = col + S;
-    while (ncol >= J.G) {
-      ncol -= J.G;
+    uint32_t nrow = row + J.s_div_g, ncol = col + J.s_mod_g;
+    if (ncol >= (uint32_t)J.G) {
+      ncol -= (uint32_t)J.G;
       ++nrow;
     }
-    const float h_next = (kk + 1 < ngr) ? J.hr[nrow] : 0.f;
+    const float h_next = J.hr[nrow < J.R ? nrow : J.R - 1];
 
-    int32_t u[8];
-    uint32_t e = step(smem);
-    u[0] = (int32_t)e >> 23;
-    if (ESC && (e & kEscBit)) u[0] = escape(e, 0, 0);
-    const int c = (int)((e >> 23) & 1u);
+    // ---- fast path: eight symbols, no escape handling
+    const uint32_t x_s = x, a2_s = a2, nw_s = nw;
+    uint32_t e[8];
+    e[0] = step(smem);
+    const int c = (int)((e[0] >> 22) & 1u);
     const uint32_t* tf = smem + ((1 + c) << 11);
-    int par = u[0] >> 1;
 #pragma unroll
-    for (int i = 1; i < 7; ++i) {
-      e = step(tf);
-      u[i] = (int32_t)e >> 23;
-      if (ESC && (e & kEscBit)) u[i] = escape(e, 0, 0);
-      par ^= u[i] >> 1;
+    for (int i = 1; i < 7; ++i) e[i] = step(tf);
+    const uint32_t par = e[0] ^ e[1] ^ e[2] ^ e[3] ^ e[4] ^ e[5] ^ e[6];
+    const int pi = (int)((par >> LY::kPar) & 1u);
+    e[7] = step(smem + ((3 + 2 * c + pi) << 11));
+    float w[8];
+    int32_t u[8];
+    bool slow = false;
+    if (ESC) {
+      const uint32_t any = (e[0] | e[1] | e[2]) | (e[3] | e[4] | e[5]) | (e[6] | e[7]);
+      slow = (any & LY::kEsc) != 0;
     }
-    const int pi = par & 1;
-    e = step(smem + ((3 + 2 * c + pi) << 11));
-    u[7] = (int32_t)e >> 23;
-    if (ESC && (e & kEscBit)) u[7] = escape(e, 1, pi);
+    if (!slow) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (OUT == OUT_COORDS) u[i] = LY::u_of(e[i]);
+        else w[i] = LY::w_of(e[i], h, -128.f * h);
+      }
+    } else {
+      // ---- careful path: replay the group from its start with escape handling
+      x = x_s;
+      a2 = a2_s;
+      nw = nw_s;
+      uint32_t ee = step(smem);
+      const int cc = (int)((ee >> 22) & 1u);
+      u[0] = (ee & LY::kEsc) ? escape(ee, 0, 0) : LY::u_of(ee);
+      int pp = u[0] >> 1;
+      const uint32_t* tf2 = smem + ((1 + cc) << 11);
+      for (int i = 1; i < 7; ++i) {
+        ee = step(tf2);
+        u[i] = (ee & LY::kEsc) ? escape(ee, 0, 0) : LY::u_of(ee);
+        pp ^= u[i] >> 1;
+      }
+      const int pi2 = pp & 1;
+      ee = step(smem + ((3 + 2 * cc + pi2) << 11));
+      u[7] = (ee & LY::kEsc) ? escape(ee, 1, pi2) : LY::u_of(ee);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = h * (float)u[i];
+      top_up(17);
+    }
 
-    const int64_t c0 = col * 8;
-    const bool full = J.c8 || (c0 + 8 <= J.C);
-    store_group<OUT>(J.out, row * J.C + c0, u, h, full, J.C - c0);
+    if (C8) {
+      store_group<OUT>(optr, 0, w, u, true, 8);
+    } else {
+      const int64_t c0 = (int64_t)col * 8;
+      store_group<OUT>(outp, (int64_t)row * J.C + c0, w, u, c0 + 8 <= J.C, J.C - c0);
+    }
+    optr += ostep;
     row = nrow;
     col = ncol;
     h = h_next;
@@ -364,9 +476,9 @@ int lds_max_bytes() {
   return v;
 }
 
-template <int OUT, bool ESC>
+template <int OUT, bool ESC, bool C8, bool NARROW>
 int launch_t(const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
-  auto kern = decode_kernel<OUT, ESC>;
+  auto kern = decode_kernel<OUT, ESC, C8, NARROW>;
   size_t lds = (size_t)kTabBytes + (size_t)waves * kWaveRingBytes;
   static std::once_flag once;
   std::call_once(once, [&] {
@@ -376,21 +488,29 @@ int launch_t(const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
   return hip_check(hipGetLastError(), "decode launch");
 }
 
-template <bool ESC>
+template <bool ESC, bool C8, bool NARROW>
 int launch_out(int out, const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
   switch (out) {
-    case OUT_BF16: return launch_t<OUT_BF16, ESC>(B, n_wg, waves, st);
-    case OUT_BF16_SAT: return launch_t<OUT_BF16_SAT, ESC>(B, n_wg, waves, st);
-    case OUT_FP16: return launch_t<OUT_FP16, ESC>(B, n_wg, waves, st);
-    case OUT_FP32: return launch_t<OUT_FP32, ESC>(B, n_wg, waves, st);
-    case OUT_FP8: return launch_t<OUT_FP8, ESC>(B, n_wg, waves, st);
-    case OUT_INT8: return launch_t<OUT_INT8, ESC>(B, n_wg, waves, st);
-    default: return launch_t<OUT_COORDS, ESC>(B, n_wg, waves, st);
+    case OUT_BF16: return launch_t<OUT_BF16, ESC, C8, NARROW>(B, n_wg, waves, st);
+    case OUT_BF16_SAT: return launch_t<OUT_BF16_SAT, ESC, C8, NARROW>(B, n_wg, waves, st);
+    case OUT_FP16: return launch_t<OUT_FP16, ESC, C8, NARROW>(B, n_wg, waves, st);
+    case OUT_FP32: return launch_t<OUT_FP32, ESC, C8, NARROW>(B, n_wg, waves, st);
+    case OUT_FP8: return launch_t<OUT_FP8, ESC, C8, NARROW>(B, n_wg, waves, st);
+    case OUT_INT8: return launch_t<OUT_INT8, ESC, C8, NARROW>(B, n_wg, waves, st);
+    default: return launch_t<OUT_COORDS, ESC, C8, NARROW>(B, n_wg, waves, st);
   }
 }
 
-int launch_any(int out, bool esc, const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
-  return esc ? launch_out<true>(out, B, n_wg, waves, st) : launch_out<false>(out, B, n_wg, waves, st);
+template <bool NARROW>
+int launch_n(int out, bool esc, bool c8, const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
+  if (c8) return esc ? launch_out<true, true, NARROW>(out, B, n_wg, waves, st)
+                     : launch_out<false, true, NARROW>(out, B, n_wg, waves, st);
+  return esc ? launch_out<true, false, NARROW>(out, B, n_wg, waves, st)
+             : launch_out<false, false, NARROW>(out, B, n_wg, waves, st);
+}
+
+int launch_any(int out, bool esc, bool c8, bool narrow, const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
+  return narrow ? launch_n<true>(out, esc, c8, B, n_wg, waves, st) : launch_n<false>(out, esc, c8, B, n_wg, waves, st);
 }
 
 int out_kind(const Blob& b) {
@@ -427,6 +547,9 @@ DecJob make_job(const Blob& b, void* out) {
   j.log2S = __builtin_ctz((unsigned)b.S);
   j.k = b.k;
   j.c8 = (b.C % 8) == 0;
+  j.s_div_g = (uint32_t)(b.S / j.G);
+  j.s_mod_g = (uint32_t)(b.S % j.G);
+  j.R = (uint32_t)b.R;
   return j;
 }
 
@@ -473,7 +596,7 @@ int decode_one(const Blob& b, void* dst, int64_t chain_lo, int64_t chain_hi, int
   DecBatch B{};
   B.j[0] = j;
   B.n = 1;
-  return launch_any(out, (b.flags & kFlagEsc) != 0, B, n_wg, waves, st);
+  return launch_any(out, (b.flags & kFlagEsc) != 0, (b.C % 8) == 0, b.k <= 6, B, n_wg, waves, st);
 }
 
 }  // namespace
@@ -508,14 +631,14 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
   const size_t o_rl = o_ck + al(4 * (size_t)(b.n_blocks + 1));
   const size_t o_err = o_rl + al(2 * (size_t)b.n_regions);
   const size_t o_stream = o_err + 256;
-  const size_t total = o_stream + al(2 * (size_t)b.n_words + 64);
+  const size_t total = o_stream + al(2 * (size_t)b.n_words + 256);
   std::vector<uint8_t> host;
   try {
     host.assign(total, 0);
   } catch (...) {
     return fail(EP_E_NOMEM, "out of host memory");
   }
-  build_slot_tables(b.model, (uint32_t*)&host[o_tab]);
+  build_slot_tables(b.model, (uint32_t*)&host[o_tab], b.k <= 6);
   half_scales(b, (float*)&host[o_hr]);
   std::memcpy(&host[o_st], &b.bytes[b.off_states], 4 * (size_t)b.n_chains);
   std::memcpy(&host[o_ck], &b.bytes[b.off_ckpt], 4 * (size_t)b.n_blocks);
@@ -575,7 +698,7 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
   if (n == 0) return EP_OK;
   // all blobs of one launch share the container kind and the escape path
   int out = -1;
-  bool esc = false;
+  bool esc = false, c8 = true;
   int64_t total_blocks = 0;
   for (int i = 0; i < n; ++i) {
     if (!blobs[i] || !dsts[i]) return fail(EP_E_ARG, "null blob or destination");
@@ -590,21 +713,29 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
       out = (out == OUT_BF16_SAT || o == OUT_BF16_SAT) ? OUT_BF16_SAT : OUT_BF16;
     else if (o != out) return fail(EP_E_ARG, "batch mixes container dtypes");
     esc |= (b.flags & kFlagEsc) != 0;
+    c8 &= (b.C % 8) == 0;
     total_blocks += b.n_blocks;
   }
   const int waves = pick_waves(total_blocks);
-  // up to kMaxBatch blobs per launch
-  for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
-    DecBatch B{};
-    B.n = std::min(kMaxBatch, n - i0);
-    int64_t wg = 0;
-    for (int q = 0; q < B.n; ++q) {
-      B.j[q] = make_job(blobs[i0 + q]->b, dsts[i0 + q]);
-      B.j[q].wg_begin = wg;
-      wg += (B.j[q].n_blocks + waves - 1) / waves;
+  // blobs whose tables use the narrow / wide entry layout go to separate launches,
+  // each of up to kMaxBatch blobs
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool narrow = pass == 0;
+    std::vector<int> idx;
+    for (int i = 0; i < n; ++i)
+      if ((blobs[i]->b.k <= 6) == narrow) idx.push_back(i);
+    for (size_t i0 = 0; i0 < idx.size(); i0 += kMaxBatch) {
+      DecBatch B{};
+      B.n = (int)std::min<size_t>(kMaxBatch, idx.size() - i0);
+      int64_t wg = 0;
+      for (int q = 0; q < B.n; ++q) {
+        B.j[q] = make_job(blobs[idx[i0 + q]]->b, dsts[idx[i0 + q]]);
+        B.j[q].wg_begin = wg;
+        wg += (B.j[q].n_blocks + waves - 1) / waves;
+      }
+      int rc = launch_any(out, esc, c8, narrow, B, wg, waves, (hipStream_t)stream);
+      if (rc) return rc;
     }
-    int rc = launch_any(out, esc, B, wg, waves, (hipStream_t)stream);
-    if (rc) return rc;
   }
   return EP_OK;
 }

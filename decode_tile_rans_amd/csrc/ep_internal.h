@@ -61,10 +61,14 @@ extern const int32_t* log2q_table();   // floor(2^16 log2 f + 1/2), f in [0, 204
 // Packed decode-table entry (device tables, one u32 per slot):
 //   bits  0..10  f      (1..2047)
 //   bits 11..21  bias   (slot - cum)
-//   bit  22      escape (bucket symbol: raw bits follow)
-//   bits 23..31  direct symbol: doubled coordinate u (signed 9 bit);
-//                escape: c | neg<<1 | top2<<2 | (e-k)<<4
-void build_slot_tables(const Model& m, uint32_t* out /* 7*2048 */);
+//   wide layout (K = 128):
+//     bits 22..30  direct symbol: doubled coordinate u (signed 9 bit; bit 22 = coset,
+//                  bit 23 = parity of floor(u/2)); escape: c | neg<<1 | top2<<2 | (e-k)<<4
+//     bit  31      escape (bucket symbol: raw bits follow)
+//   narrow layout (K <= 64, |u| <= 127):
+//     bit 22 coset, bit 23 escape, bits 24..31 u + 128 (direct) or
+//     neg | top2<<1 | (e-k)<<3 (escape)
+void build_slot_tables(const Model& m, uint32_t* out /* 7*2048 */, bool narrow);
 
 // Parsed blob (host side) + device mirror.
 struct Blob {

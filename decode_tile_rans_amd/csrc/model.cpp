@@ -261,7 +261,7 @@ const int32_t* log2q_table() {
   return t;
 }
 
-void build_slot_tables(const Model& m, uint32_t* out) {
+void build_slot_tables(const Model& m, uint32_t* out, bool narrow) {
   const int K = 1 << m.k;
   for (int t = 0; t < kNumCtx; ++t) {
     for (int id = 0; id < kIdSpace; ++id) {
@@ -276,21 +276,20 @@ void build_slot_tables(const Model& m, uint32_t* out) {
         sid = id;
       }
       int msym = sid >> 1, neg = sid & 1;
-      uint32_t top;
-      uint32_t esc = 0;
+      uint32_t hi;   // bits 22..31
       if (msym < K) {
         int u = 2 * msym + c;
         if (neg) u = -u;
-        top = uint32_t(u) & 0x1FFu;
+        hi = narrow ? (uint32_t(c) | (uint32_t(u + 128) << 2)) : (uint32_t(u) & 0x1FFu);
       } else {
         int er = (msym - K) >> 2, top2 = (msym - K) & 3;
-        top = uint32_t(c | (neg << 1) | (top2 << 2) | (er << 4));
-        esc = 1;
+        hi = narrow ? (uint32_t(c) | (1u << 1) | (uint32_t(neg | (top2 << 1) | (er << 3)) << 2))
+                    : (uint32_t(c | (neg << 1) | (top2 << 2) | (er << 4)) | (1u << 9));
       }
       int32_t cum = m.CUM[t][id];
       for (int s = cum; s < cum + f; ++s) {
         uint32_t bias = uint32_t(s - cum);
-        out[t * kM + s] = uint32_t(f) | (bias << 11) | (esc << 22) | (top << 23);
+        out[t * kM + s] = uint32_t(f) | (bias << 11) | (hi << 22);
       }
     }
   }
