@@ -147,6 +147,20 @@ def time_stack(comps, blocks, outs, steps, warmup, per_layer=False, n_streams=1)
     return wall / steps * 1e3, launch_ms, units
 
 
+def traffic_per_launch(coords_per_launch):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
+    or None when the decode kernel source changed since those counters were taken."""
+    import hashlib
+    try:
+        info = json.load(open(os.path.join(ROOT, "profiles", "decode_traffic.json")))
+        src = open(os.path.join(ROOT, "decode_tile_rans_amd", "csrc", "decode.hip"), "rb").read()
+    except OSError:
+        return None
+    if hashlib.sha1(src).hexdigest() != info.get("decode_source_sha1"):
+        return None
+    return (info["fetch_bytes_per_param"] + info["write_bytes_per_param"]) * coords_per_launch
+
+
 def cpu_baseline(target_bpp):
     """The oracle decoder (NumPy, single process) on one 3840 x 3840 stack matrix."""
     import numpy as np
@@ -261,7 +275,8 @@ def main():
                    "actual_bpp": round(8.0 * blob_bytes / n_params, 4), "launches_per_step": len(units),
                    "streams": a.streams},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (lambda t: round(t) if t else None)(traffic_per_launch(n_params / len(units))),
                      "kernel": "decode_kernel (BF16 out)", "avg_launch_ms": round(kern_ms / len(units), 5),
                      "algorithmic_bytes_per_launch": round(alg_bytes / len(units)),
                      "step_effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1)},
