@@ -5,16 +5,17 @@
 // codebook.  [ABS]: tiles are independently decodable; containers BF16/FP16/FP8/INT8.
 //
 // Work mapping (MI355X-first, not the pages' H20 design):
-//   * one wavefront = one block of 64 rANS chains, one chain per lane (64/S tiles);
-//     the wave's prefix sum over its 32 region lengths gives every lane its stream
-//     start, so only one u32 checkpoint per 64 chains is stored;
+//   * one wavefront = one block of 64 rANS chains, one chain per lane (64/S tiles), or two
+//     blocks with two chains per lane; the wave's prefix sum over the block's 32 region
+//     lengths gives every chain its stream start, so only one u32 checkpoint per 64
+//     chains is stored;
 //   * a workgroup of W waves stages the 7 decode tables (7 x 2048 packed u32 = 56 KB)
-//     into LDS once; each wave copies its block's contiguous stream span into LDS
-//     with coalesced 16-byte loads; lanes then read their own words from LDS;
+//     into LDS once; every chain keeps a 64-byte ring of stream words in LDS, fed by
+//     16-byte loads issued two groups ahead of use;
 //   * per coordinate: one LDS table read, x = f (x >> 11) + bias (24-bit mad), a
-//     16-bit renormalisation from a prefetched word, the doubled coordinate taken
-//     straight from the table entry (escapes: bypass bits, rare), h_r * u in fp32,
-//     container cast, one 16-byte store per 8-coordinate group (BF16);
+//     16-bit renormalisation from a prefetched ring word, the doubled coordinate taken
+//     straight from the table entry (escapes: bypass bits, replayed on a careful path),
+//     h_r * u in fp32, container cast, one 16-byte store per 8-coordinate group (BF16);
 //   * nothing but the final weights is written to HBM.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -177,19 +178,11 @@ __device__ inline void store_group(void* out, int64_t base, const float* vin, co
 
 // ---------------------------------------------------------------- the decode kernel
 constexpr int kMaxBatch = 12;
-#ifndef EP_RING_WORDS
-#define EP_RING_WORDS 32
-#endif
-#ifndef EP_CHUNK_WORDS
-#define EP_CHUNK_WORDS 8
-#endif
-constexpr int kRingWords = EP_RING_WORDS;       // per-lane LDS ring (16-bit words)
-constexpr int kChunkWords = EP_CHUNK_WORDS;     // words per stream load (multiple of 8)
-constexpr int kChunkVec = kChunkWords / 8;      // 16-byte loads per chunk
-static_assert(kRingWords - kChunkWords >= 17, "ring too small for two groups plus a chunk");
-constexpr int kRingDw = kRingWords / 2;
-constexpr int kWaveRingBytes = 64 * kRingWords * 2;   // 4 KB per wave
+constexpr int kRingWords = 32;                   // per-chain LDS ring (16-bit words)
+constexpr int kChunkWords = 8;                   // one 16-byte stream load
+constexpr int kChainRingBytes = kRingWords * 2;  // 64 B per chain
 constexpr int kMaxWaves = 16;
+static_assert(kRingWords - kChunkWords >= 17, "ring too small for two groups plus a chunk");
 
 // Job descriptors travel by value in the kernel arguments (no per-launch copy).
 struct DecBatch {
@@ -231,7 +224,158 @@ struct EntryLayout {
   }
 };
 
-template <int OUT, bool ESC, bool C8, bool NARROW>
+// ---- one rANS chain: its state and its stream reader
+//
+// Each chain owns a ring of 32 stream words in LDS; stream word w sits at ring byte
+// 2 (w mod 32).  Words are fetched in aligned 16-byte chunks.  q = words consumed,
+// F = words fetched from the chain's first word on in reading order (the chunk in
+// flight included), next = the next chunk.  Invariant: the chain only reads words
+// already written to its ring.  The ring is serviced every second group: at that point
+// >= 17 words are resident (two groups' symbols consume <= 16); an escape consumes <= 2
+// more and tops up to >= 11 first.  A chunk is written to the ring two groups after its
+// load was issued.
+struct Chain {
+  uint32_t x;       // rANS state
+  uint32_t a2;      // 2 x (index of the next stream word); moves by a2step per word
+  uint32_t nw;      // that word, already read from the ring
+  uint32_t rb;      // LDS byte address of the ring (64-byte aligned)
+  uint32_t a2_0;    // a2 at the chain's first word
+  uint32_t sgn;     // 0 reading up, ~0 reading down: 2q = ((a2 - a2_0) ^ sgn) - sgn
+  int32_t a2step;   // +2 / -2
+  uint32_t next;    // first word of the next chunk
+  int32_t stepc;    // +8 / -8
+  int32_t F;
+  int32_t Fmax;     // words of the region in reading order
+  uint4 pend;       // chunk in flight
+  uint32_t pend_c;
+  bool have_pend;
+};
+
+__device__ __forceinline__ int32_t ch_q(const Chain& r) {
+  return (int32_t)(((r.a2 - r.a2_0) ^ r.sgn) - r.sgn) >> 1;
+}
+__device__ __forceinline__ void ch_put(uint8_t* lds8, const Chain& r, uint32_t c, uint4 d) {
+  *(uint4*)(lds8 + r.rb + ((c & (kRingWords - 1)) << 1)) = d;
+}
+__device__ __forceinline__ void ch_flush(uint8_t* lds8, Chain& r) {
+  if (r.have_pend) {
+    ch_put(lds8, r, r.pend_c, r.pend);
+    r.have_pend = false;
+  }
+}
+// synchronous; rare after the prime
+__device__ __forceinline__ void ch_top_up(uint8_t* lds8, const uint4* chunks, Chain& r, int need) {
+  ch_flush(lds8, r);
+  const int32_t q = ch_q(r);
+  while (r.F - q < need && r.F < r.Fmax) {
+    const uint32_t c = r.next;
+    r.next += r.stepc;
+    r.F += kChunkWords;
+    ch_put(lds8, r, c, chunks[c >> 3]);
+  }
+}
+__device__ __forceinline__ uint32_t ch_word(const uint8_t* lds8, const Chain& r) {
+  return *(const uint16_t*)(lds8 + (r.rb | (r.a2 & 62u)));
+}
+__device__ __forceinline__ void ch_renorm_if(const uint8_t* lds8, Chain& r, bool need) {
+  if (need) {
+    r.x = (r.x << 16) | r.nw;
+    r.a2 += r.a2step;
+    r.nw = ch_word(lds8, r);
+  }
+}
+__device__ __forceinline__ void ch_renorm(const uint8_t* lds8, Chain& r) { ch_renorm_if(lds8, r, r.x < kL); }
+// Renormalise ILP chains: all conditions first, so that no chain's state update is
+// sunk below another chain's (conditional) ring read.
+template <int ILP>
+__device__ __forceinline__ void ch_renorm_all(const uint8_t* lds8, Chain* rd) {
+  bool need[ILP];
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) {
+    // pin the state update here (an empty asm that reads it), ahead of every ring read
+    if (ILP > 1) asm volatile("" ::"v"(rd[c].x));
+    need[c] = rd[c].x < kL;
+  }
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) ch_renorm_if(lds8, rd[c], need[c]);
+}
+// table read of one symbol step (issued before the other chain's step finishes)
+__device__ __forceinline__ uint32_t ch_entry(const uint32_t* tb, const Chain& r) { return tb[r.x & (kM - 1)]; }
+// x = f (x >> P) + (slot - cum)
+__device__ __forceinline__ void ch_decode(Chain& r, uint32_t e) {
+  r.x = __umul24(e & 2047u, r.x >> 11) + ((e >> 11) & 2047u);
+}
+__device__ __forceinline__ void ch_advance(const uint8_t* lds8, Chain& r, uint32_t e) {
+  ch_decode(r, e);
+  ch_renorm(lds8, r);
+}
+__device__ __forceinline__ uint32_t ch_bypass(const uint8_t* lds8, Chain& r, int nb) {
+  const uint32_t v = r.x & ((1u << nb) - 1u);
+  r.x >>= nb;
+  ch_renorm(lds8, r);
+  return v;
+}
+// ring service every second group: write the chunk in flight, top up if short, and
+// issue the next chunk load.  The load pattern is fixed (one 16-byte load per service);
+// a load that is not needed reads the stream's first chunk, one line shared by every
+// lane, always inside the allocation.
+__device__ __forceinline__ void ch_service(uint8_t* lds8, const uint4* chunks, Chain& r) {
+  ch_flush(lds8, r);
+  if (r.F - ch_q(r) < 17) ch_top_up(lds8, chunks, r, 17);
+  const bool issue = r.F - ch_q(r) <= kRingWords - kChunkWords && r.F < r.Fmax;
+  r.pend_c = r.next;
+  r.pend = chunks[issue ? (r.next >> 3) : 0u];
+  if (issue) {
+    r.next += r.stepc;
+    r.F += kChunkWords;
+  }
+  r.have_pend = issue;
+}
+// escape symbol: raw bits follow; returns the doubled coordinate
+template <class LY>
+__device__ __forceinline__ int32_t ch_escape(uint8_t* lds8, const uint4* chunks, Chain& r, uint32_t e, int k,
+                                             int last, int pi) {
+  if (r.F - ch_q(r) - (r.have_pend ? kChunkWords : 0) < 11) ch_top_up(lds8, chunks, r, 11);
+  int c, neg, top2, er;
+  LY::esc_info(e, c, neg, top2, er);
+  const int ex = k + er;
+  const int nb = ex - 2 - last;
+  uint32_t raw = ch_bypass(lds8, r, nb < 16 ? nb : 16);
+  if (nb > 16) raw |= ch_bypass(lds8, r, nb - 16) << 16;
+  if (last) raw = (raw << 1) | (uint32_t)(c == 0 ? pi : (pi ^ neg));
+  const uint32_t m = (1u << ex) | ((uint32_t)top2 << (ex - 2)) | raw;
+  const int32_t uu = (int32_t)(2u * m + (uint32_t)c);
+  return neg ? -uu : uu;
+}
+// careful decode of one group (the chain's state is at the group's start): FIRST,
+// six FREE, LAST with escapes; tops the ring up again afterwards
+template <class LY>
+__device__ __forceinline__ void ch_group_careful(const uint32_t* smem, uint8_t* lds8, const uint4* chunks, Chain& r,
+                                                 int k, int32_t* u) {
+  uint32_t ee = ch_entry(smem, r);
+  ch_advance(lds8, r, ee);
+  const int cc = (int)((ee >> 22) & 1u);
+  u[0] = (ee & LY::kEsc) ? ch_escape<LY>(lds8, chunks, r, ee, k, 0, 0) : LY::u_of(ee);
+  int pp = u[0] >> 1;
+  const uint32_t* tf = smem + ((1 + cc) << 11);
+  for (int i = 1; i < 7; ++i) {
+    ee = ch_entry(tf, r);
+    ch_advance(lds8, r, ee);
+    u[i] = (ee & LY::kEsc) ? ch_escape<LY>(lds8, chunks, r, ee, k, 0, 0) : LY::u_of(ee);
+    pp ^= u[i] >> 1;
+  }
+  const int pi = pp & 1;
+  ee = ch_entry(smem + ((3 + 2 * cc + pi) << 11), r);
+  ch_advance(lds8, r, ee);
+  u[7] = (ee & LY::kEsc) ? ch_escape<LY>(lds8, chunks, r, ee, k, 1, pi) : LY::u_of(ee);
+  ch_top_up(lds8, chunks, r, 17);
+}
+
+// One wave decodes ILP blocks of 64 chains.  ILP = 1: lane l runs chain l of its block
+// (even lanes read their region up, odd lanes down).  ILP = 2: lane l runs both chains
+// of region l & 31 of block (l >> 5), the forward and the backward one, interleaved step
+// by step so that one chain's table read is in flight while the other one computes.
+template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
 __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   using LY = EntryLayout<NARROW>;
   extern __shared__ __align__(16) uint32_t smem[];
@@ -245,7 +389,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   for (int q = 1; q < B.n; ++q)
     if (B.j[q].wg_begin <= (int64_t)blockIdx.x) ji = q;
   const DecJob& J = B.j[ji];
-  const int64_t blk = J.block_lo + ((int64_t)blockIdx.x - J.wg_begin) * nwaves + wave;
+  const int64_t blk0 = J.block_lo + (((int64_t)blockIdx.x - J.wg_begin) * nwaves + wave) * ILP;
 
   // stage the decode tables (shared by the workgroup's waves)
   {
@@ -254,213 +398,205 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
     for (int i = tid; i < kTabWords / 4; i += blockDim.x) dst[i] = src[i];
   }
   __syncthreads();
-  if (blk >= J.n_blocks) return;
+  if (blk0 >= J.n_blocks) return;
 
-  const int S = 1 << J.log2S;
-  const int64_t chain = blk * 64 + lane;
-  // region start via a wave prefix sum of the block's 32 region lengths
-  const int64_t reg = blk * 32 + (lane >> 1);
-  const uint32_t rl = (reg < J.n_regions) ? (uint32_t)J.rlen[reg] : 0u;
-  uint32_t v = (lane & 1) ? 0u : rl;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
-  const uint32_t rstart = J.ckpt[blk] + v - rl;      // absolute word index of the region start
-  const bool fwd = (lane & 1) == 0;                  // even chain reads up, odd chain reads down
-  const int32_t dir = fwd ? 1 : -1;
-  const uint32_t p0 = fwd ? rstart : rstart + rl - 1;   // the lane's first word
-
-  const bool live = chain < J.n_chains && chain >= J.chain_lo && chain < J.chain_hi;
-  const int64_t t = chain >> J.log2S;
-  const int j = (int)(chain & (S - 1));
-  int64_t gt = J.n_groups - (t << 9);
-  if (gt > kTileGroups) gt = kTileGroups;
-  const int ngr = (live && gt > j) ? (int)((gt - j + S - 1) >> J.log2S) : 0;
-  uint32_t x = (chain < J.n_chains) ? J.states[chain] : kL;
-
-  // ---- per-lane ring of stream words: word w lives at ring byte offset 2 (w % 32).
-  // q = words consumed, F = words resident from p0 on in the lane's direction, next = the
-  // next 16-byte chunk.  Invariant: the lane only reads resident words.  The ring is
-  // serviced every second group: at that point >= 17 words are resident (two groups'
-  // symbols consume <= 16); an escape consumes <= 2 more and tops up to >= 11 first.
-  // Chunks are loaded two groups before they are written into the ring.
-  const uint32_t ring_base = (uint32_t)(kTabBytes + (wave * 64 + lane) * kRingWords * 2);
   uint8_t* const lds8 = (uint8_t*)smem;
   const uint4* chunks = (const uint4*)J.stream;
-  uint32_t next = p0 & ~(uint32_t)(kChunkWords - 1);
-  int32_t F = fwd ? -(int32_t)(p0 & (kChunkWords - 1)) : (int32_t)(p0 & (kChunkWords - 1)) - (kChunkWords - 1);
-  const int32_t Fmax = (int32_t)rl;                 // region words in the lane's direction
-  const int32_t stepc = kChunkWords * dir;
-  uint4 pend[kChunkVec];
-  uint32_t pend_c = 0;
-  bool have_pend = false;
-  uint32_t a2 = 2u * p0;                            // 2 * (word index of the next word)
-  auto q_now = [&]() -> int32_t { return (int32_t)(a2 - 2u * p0) / 2 * dir; };
-  auto resident = [&]() -> int32_t { return F - q_now() - (have_pend ? kChunkWords : 0); };
-  auto put = [&](uint32_t c, const uint4* d) {
-#pragma unroll
-    for (int v = 0; v < kChunkVec; ++v)
-      *(uint4*)(lds8 + ring_base + (((c + 8u * v) & (kRingWords - 1)) << 1)) = d[v];
-  };
-  auto load = [&](uint32_t c, uint4* d) {
-#pragma unroll
-    for (int v = 0; v < kChunkVec; ++v) d[v] = chunks[(c >> 3) + v];
-  };
-  auto flush_pend = [&]() {
-    if (have_pend) {
-      put(pend_c, pend);
-      have_pend = false;
-    }
-  };
-  auto top_up = [&](int need) {                      // synchronous; rare after the prime
-    flush_pend();
-    const int32_t q = q_now();
-    while (F - q < need && F < Fmax) {
-      uint32_t c = next;
-      next += stepc;
-      F += kChunkWords;
-      uint4 d[kChunkVec];
-      load(c, d);
-      put(c, d);
-    }
-  };
-  if (live && rl) top_up(17);
-  const int32_t a2step = 2 * dir;
-  auto ring_word = [&]() -> uint32_t { return *(const uint16_t*)(lds8 + (ring_base | (a2 & 62u))); };
-  uint32_t nw = ring_word();
+  const int S = 1 << J.log2S;
 
-  // ---- output position
-  const int64_t g0 = (t << 9) + j;
-  uint32_t row = live ? (uint32_t)(g0 / J.G) : 0u;
-  uint32_t col = live ? (uint32_t)(g0 - (int64_t)row * J.G) : 0u;
-  const int k = J.k;
-
-  auto renorm = [&]() {
-    if (x < kL) {
-      x = (x << 16) | nw;
-      a2 += a2step;
-      nw = ring_word();
+  // ---- region starts: a prefix sum over the block's 32 region lengths
+  uint32_t rl, rstart;
+  int64_t ch0;
+  if (ILP == 1) {
+    const int64_t reg = blk0 * 32 + (lane >> 1);
+    rl = (reg < J.n_regions) ? (uint32_t)J.rlen[reg] : 0u;
+    uint32_t v = (lane & 1) ? 0u : rl;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t t = __shfl_up(v, d, 64);
+      if (lane >= d) v += t;
     }
-  };
-  auto step = [&](const uint32_t* tb) -> uint32_t {
-    uint32_t e = tb[x & (kM - 1)];
-    x = __umul24(e & 2047u, x >> 11) + ((e >> 11) & 2047u);
-    renorm();
-    return e;
-  };
-  auto bypass = [&](int nb) -> uint32_t {
-    uint32_t r = x & ((1u << nb) - 1u);
-    x >>= nb;
-    renorm();
-    return r;
-  };
-  // escape symbol (careful path): raw bits follow; returns the doubled coordinate
-  auto escape = [&](uint32_t e, int last, int pi) -> int32_t {
-    if (resident() < 11) top_up(11);
-    int c, neg, top2, er;
-    LY::esc_info(e, c, neg, top2, er);
-    int ex = k + er;
-    int nb = ex - 2 - last;
-    uint32_t raw = bypass(nb < 16 ? nb : 16);
-    if (nb > 16) raw |= bypass(nb - 16) << 16;
-    if (last) raw = (raw << 1) | (uint32_t)(c == 0 ? pi : (pi ^ neg));
-    uint32_t m = (1u << ex) | ((uint32_t)top2 << (ex - 2)) | raw;
-    int32_t uu = (int32_t)(2u * m + (uint32_t)c);
-    return neg ? -uu : uu;
-  };
+    rstart = J.ckpt[blk0] + v - rl;
+    ch0 = blk0 * 64 + lane;
+  } else {
+    const int64_t blk = blk0 + (lane >> 5);
+    const bool bok = blk < J.n_blocks;
+    const int64_t reg = blk * 32 + (lane & 31);
+    rl = (bok && reg < J.n_regions) ? (uint32_t)J.rlen[reg] : 0u;
+    uint32_t v = rl;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+      const uint32_t t = __shfl_up(v, d, 32);
+      if ((lane & 31) >= d) v += t;
+    }
+    rstart = (bok ? J.ckpt[blk] : 0u) + v - rl;
+    ch0 = 2 * reg;
+  }
 
   char* outp = (char*)J.out;
   constexpr int ESZ = (OUT == OUT_FP32 || OUT == OUT_COORDS) ? 4 : ((OUT == OUT_FP8 || OUT == OUT_INT8) ? 1 : 2);
-  char* optr = outp + (int64_t)(g0 * 8) * ESZ;      // C % 8 == 0: groups are contiguous
   const int64_t ostep = (int64_t)S * 8 * ESZ;
-  float h = ngr > 0 ? J.hr[row] : 0.f;
-  // a chunk load that is not needed reads the stream's first chunk: one line shared by
-  // every lane, always cached, always inside the stream allocation
-  const uint32_t safe_chunk = 0;
 
-  for (int kk = 0; kk < ngr; ++kk) {
-    // ---- ring service every second group (a fixed VMEM pattern: one chunk load)
+  Chain rd[ILP];
+  int ngr[ILP];
+  bool live[ILP];
+  uint32_t row[ILP], col[ILP];
+  float h[ILP];
+  char* optr[ILP];
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) {
+    const int64_t ch = ch0 + c;
+    const bool fwd = (ILP == 1) ? ((lane & 1) == 0) : (c == 0);
+    const uint32_t p0 = fwd ? rstart : rstart + rl - 1u;   // the chain's first word
+    live[c] = ch < J.n_chains && ch >= J.chain_lo && ch < J.chain_hi;
+    const int64_t t = ch >> J.log2S;
+    const int j = (int)(ch & (S - 1));
+    int64_t gt = J.n_groups - (t << 9);
+    if (gt > kTileGroups) gt = kTileGroups;
+    ngr[c] = (live[c] && gt > j) ? (int)((gt - j + S - 1) >> J.log2S) : 0;
+    Chain& r = rd[c];
+    r.x = (ch < J.n_chains) ? J.states[ch] : kL;
+    r.rb = (uint32_t)(kTabBytes + ((wave * 64 + lane) * ILP + c) * kChainRingBytes);
+    r.a2 = 2u * p0;
+    r.a2_0 = r.a2;
+    r.sgn = fwd ? 0u : ~0u;
+    r.a2step = fwd ? 2 : -2;
+    r.next = p0 & ~(uint32_t)(kChunkWords - 1);
+    r.F = fwd ? -(int32_t)(p0 & (kChunkWords - 1)) : (int32_t)(p0 & (kChunkWords - 1)) - (kChunkWords - 1);
+    r.Fmax = (int32_t)rl;
+    r.stepc = fwd ? kChunkWords : -kChunkWords;
+    r.pend = make_uint4(0u, 0u, 0u, 0u);
+    r.pend_c = 0;
+    r.have_pend = false;
+    if (live[c] && rl) ch_top_up(lds8, chunks, r, 17);
+    r.nw = ch_word(lds8, r);
+    const int64_t g0 = (t << 9) + j;
+    row[c] = live[c] ? (uint32_t)(g0 / J.G) : 0u;
+    col[c] = live[c] ? (uint32_t)(g0 - (int64_t)row[c] * J.G) : 0u;
+    h[c] = ngr[c] > 0 ? J.hr[row[c]] : 0.f;
+    optr[c] = outp + (live[c] ? g0 * 8 * ESZ : 0);   // C % 8 == 0: groups are contiguous
+  }
+  int nmax = ngr[0], nmin = ngr[0];
+#pragma unroll
+  for (int c = 1; c < ILP; ++c) {
+    nmax = ngr[c] > nmax ? ngr[c] : nmax;
+    nmin = ngr[c] < nmin ? ngr[c] : nmin;
+  }
+  const int k = J.k;
+
+  for (int kk = 0; kk < nmax; ++kk) {
     if ((kk & 1) == 0) {
-      flush_pend();
-      if (F - q_now() < 17) top_up(17);
-      const bool issue = F - q_now() <= kRingWords - kChunkWords && F < Fmax;
-      pend_c = next;
-      load(issue ? next : safe_chunk, pend);
-      if (issue) {
-        next += stepc;
-        F += kChunkWords;
-      }
-      have_pend = issue;
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) ch_service(lds8, chunks, rd[c]);
     }
     // ---- row scale of the next group, loaded one group ahead
-    uint32_t nrow = row + J.s_div_g, ncol = col + J.s_mod_g;
-    if (ncol >= (uint32_t)J.G) {
-      ncol -= (uint32_t)J.G;
-      ++nrow;
-    }
-    const float h_next = J.hr[nrow < J.R ? nrow : J.R - 1];
-
-    // ---- fast path: eight symbols, no escape handling
-    const uint32_t x_s = x, a2_s = a2, nw_s = nw;
-    uint32_t e[8];
-    e[0] = step(smem);
-    const int c = (int)((e[0] >> 22) & 1u);
-    const uint32_t* tf = smem + ((1 + c) << 11);
+    uint32_t nrow[ILP], ncol[ILP];
+    float h_next[ILP];
 #pragma unroll
-    for (int i = 1; i < 7; ++i) e[i] = step(tf);
-    const uint32_t par = e[0] ^ e[1] ^ e[2] ^ e[3] ^ e[4] ^ e[5] ^ e[6];
-    const int pi = (int)((par >> LY::kPar) & 1u);
-    e[7] = step(smem + ((3 + 2 * c + pi) << 11));
-    float w[8];
-    int32_t u[8];
-    bool slow = false;
-    if (ESC) {
-      const uint32_t any = (e[0] | e[1] | e[2]) | (e[3] | e[4] | e[5]) | (e[6] | e[7]);
-      slow = (any & LY::kEsc) != 0;
-    }
-    if (!slow) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (OUT == OUT_COORDS) u[i] = LY::u_of(e[i]);
-        else w[i] = LY::w_of(e[i], h, -128.f * h);
+    for (int c = 0; c < ILP; ++c) {
+      nrow[c] = row[c] + J.s_div_g;
+      ncol[c] = col[c] + J.s_mod_g;
+      if (ncol[c] >= (uint32_t)J.G) {
+        ncol[c] -= (uint32_t)J.G;
+        ++nrow[c];
       }
-    } else {
-      // ---- careful path: replay the group from its start with escape handling
-      x = x_s;
-      a2 = a2_s;
-      nw = nw_s;
-      uint32_t ee = step(smem);
-      const int cc = (int)((ee >> 22) & 1u);
-      u[0] = (ee & LY::kEsc) ? escape(ee, 0, 0) : LY::u_of(ee);
-      int pp = u[0] >> 1;
-      const uint32_t* tf2 = smem + ((1 + cc) << 11);
-      for (int i = 1; i < 7; ++i) {
-        ee = step(tf2);
-        u[i] = (ee & LY::kEsc) ? escape(ee, 0, 0) : LY::u_of(ee);
-        pp ^= u[i] >> 1;
-      }
-      const int pi2 = pp & 1;
-      ee = step(smem + ((3 + 2 * cc + pi2) << 11));
-      u[7] = (ee & LY::kEsc) ? escape(ee, 1, pi2) : LY::u_of(ee);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = h * (float)u[i];
-      top_up(17);
+      h_next[c] = J.hr[nrow[c] < J.R ? nrow[c] : J.R - 1];
     }
 
-    if (C8) {
-      store_group<OUT>(optr, 0, w, u, true, 8);
-    } else {
-      const int64_t c0 = (int64_t)col * 8;
-      store_group<OUT>(outp, (int64_t)row * J.C + c0, w, u, c0 + 8 <= J.C, J.C - c0);
+    // ---- fast path: eight symbols per chain, no escape handling
+    uint32_t xs[ILP], a2s[ILP], nws[ILP];
+    uint32_t e[ILP][8];
+    const uint32_t* tb[ILP];
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      xs[c] = rd[c].x;
+      a2s[c] = rd[c].a2;
+      nws[c] = rd[c].nw;
+      e[c][0] = ch_entry(smem, rd[c]);
     }
-    optr += ostep;
-    row = nrow;
-    col = ncol;
-    h = h_next;
+    // per step: every chain's table read, then every chain's state update, then the
+    // renormalisations (whose ring reads are conditional and so end the step's LDS batch)
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      ch_decode(rd[c], e[c][0]);
+      tb[c] = smem + ((1 + ((e[c][0] >> 22) & 1u)) << 11);
+    }
+    ch_renorm_all<ILP>(lds8, rd);
+#pragma unroll
+    for (int i = 1; i < 7; ++i) {
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) e[c][i] = ch_entry(tb[c], rd[c]);
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) ch_decode(rd[c], e[c][i]);
+      ch_renorm_all<ILP>(lds8, rd);
+    }
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      const uint32_t par = e[c][0] ^ e[c][1] ^ e[c][2] ^ e[c][3] ^ e[c][4] ^ e[c][5] ^ e[c][6];
+      const int pi = (int)((par >> LY::kPar) & 1u);
+      const int cs = (int)((e[c][0] >> 22) & 1u);
+      e[c][7] = ch_entry(smem + ((3 + 2 * cs + pi) << 11), rd[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) ch_decode(rd[c], e[c][7]);
+    ch_renorm_all<ILP>(lds8, rd);
+
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      const bool act = (ILP == 1) || kk < ngr[c];
+      float w[8];
+      int32_t u[8];
+      bool slow = false;
+      if (ESC) {
+        const uint32_t any = (e[c][0] | e[c][1] | e[c][2]) | (e[c][3] | e[c][4] | e[c][5]) | (e[c][6] | e[c][7]);
+        slow = act && (any & LY::kEsc) != 0;
+      }
+      if (!slow) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (OUT == OUT_COORDS) u[i] = LY::u_of(e[c][i]);
+          else w[i] = LY::w_of(e[c][i], h[c], -128.f * h[c]);
+        }
+      } else {
+        // replay the group from its start with escape handling
+        rd[c].x = xs[c];
+        rd[c].a2 = a2s[c];
+        rd[c].nw = nws[c];
+        ch_group_careful<LY>(smem, lds8, chunks, rd[c], k, u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = h[c] * (float)u[i];
+      }
+      if (act) {
+        if (C8) {
+          store_group<OUT>(optr[c], 0, w, u, true, 8);
+        } else {
+          const int64_t c0 = (int64_t)col[c] * 8;
+          store_group<OUT>(outp, (int64_t)row[c] * J.C + c0, w, u, c0 + 8 <= J.C, J.C - c0);
+        }
+      }
+    }
+    if (ILP > 1 && kk >= nmin) {
+      // a chain past its last group keeps its final state
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) {
+        if (kk >= ngr[c]) {
+          rd[c].x = xs[c];
+          rd[c].a2 = a2s[c];
+          rd[c].nw = nws[c];
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      optr[c] += ostep;
+      row[c] = nrow[c];
+      col[c] = ncol[c];
+      h[c] = h_next[c];
+    }
   }
-  if (live && x != kL) atomicAdd(J.err, 1u);
+#pragma unroll
+  for (int c = 0; c < ILP; ++c)
+    if (live[c] && rd[c].x != kL) atomicAdd(J.err, 1u);
 }
 
 // ---------------------------------------------------------------- launch helpers
@@ -476,10 +612,17 @@ int lds_max_bytes() {
   return v;
 }
 
-template <int OUT, bool ESC, bool C8, bool NARROW>
+// Launch shape: ILP chains per lane, `waves` waves per workgroup.
+struct Shape {
+  int ilp;
+  int waves;
+  int64_t blocks_per_wg() const { return (int64_t)ilp * waves; }
+};
+
+template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
 int launch_t(const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
-  auto kern = decode_kernel<OUT, ESC, C8, NARROW>;
-  size_t lds = (size_t)kTabBytes + (size_t)waves * kWaveRingBytes;
+  auto kern = decode_kernel<OUT, ESC, C8, NARROW, ILP>;
+  size_t lds = (size_t)kTabBytes + (size_t)waves * 64 * ILP * kChainRingBytes;
   static std::once_flag once;
   std::call_once(once, [&] {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max_bytes());
@@ -488,29 +631,33 @@ int launch_t(const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
   return hip_check(hipGetLastError(), "decode launch");
 }
 
-template <bool ESC, bool C8, bool NARROW>
+template <bool ESC, bool C8, bool NARROW, int ILP>
 int launch_out(int out, const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
   switch (out) {
-    case OUT_BF16: return launch_t<OUT_BF16, ESC, C8, NARROW>(B, n_wg, waves, st);
-    case OUT_BF16_SAT: return launch_t<OUT_BF16_SAT, ESC, C8, NARROW>(B, n_wg, waves, st);
-    case OUT_FP16: return launch_t<OUT_FP16, ESC, C8, NARROW>(B, n_wg, waves, st);
-    case OUT_FP32: return launch_t<OUT_FP32, ESC, C8, NARROW>(B, n_wg, waves, st);
-    case OUT_FP8: return launch_t<OUT_FP8, ESC, C8, NARROW>(B, n_wg, waves, st);
-    case OUT_INT8: return launch_t<OUT_INT8, ESC, C8, NARROW>(B, n_wg, waves, st);
-    default: return launch_t<OUT_COORDS, ESC, C8, NARROW>(B, n_wg, waves, st);
+    case OUT_BF16: return launch_t<OUT_BF16, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+    case OUT_BF16_SAT: return launch_t<OUT_BF16_SAT, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+    case OUT_FP16: return launch_t<OUT_FP16, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+    case OUT_FP32: return launch_t<OUT_FP32, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+    case OUT_FP8: return launch_t<OUT_FP8, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+    case OUT_INT8: return launch_t<OUT_INT8, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+    default: return launch_t<OUT_COORDS, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
   }
 }
 
-template <bool NARROW>
+template <bool NARROW, int ILP>
 int launch_n(int out, bool esc, bool c8, const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
-  if (c8) return esc ? launch_out<true, true, NARROW>(out, B, n_wg, waves, st)
-                     : launch_out<false, true, NARROW>(out, B, n_wg, waves, st);
-  return esc ? launch_out<true, false, NARROW>(out, B, n_wg, waves, st)
-             : launch_out<false, false, NARROW>(out, B, n_wg, waves, st);
+  if (c8) return esc ? launch_out<true, true, NARROW, ILP>(out, B, n_wg, waves, st)
+                     : launch_out<false, true, NARROW, ILP>(out, B, n_wg, waves, st);
+  return esc ? launch_out<true, false, NARROW, ILP>(out, B, n_wg, waves, st)
+             : launch_out<false, false, NARROW, ILP>(out, B, n_wg, waves, st);
 }
 
-int launch_any(int out, bool esc, bool c8, bool narrow, const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
-  return narrow ? launch_n<true>(out, esc, c8, B, n_wg, waves, st) : launch_n<false>(out, esc, c8, B, n_wg, waves, st);
+int launch_any(int out, bool esc, bool c8, bool narrow, Shape sh, const DecBatch& B, int64_t n_wg, hipStream_t st) {
+  if (sh.ilp == 2)
+    return narrow ? launch_n<true, 2>(out, esc, c8, B, n_wg, sh.waves, st)
+                  : launch_n<false, 2>(out, esc, c8, B, n_wg, sh.waves, st);
+  return narrow ? launch_n<true, 1>(out, esc, c8, B, n_wg, sh.waves, st)
+                : launch_n<false, 1>(out, esc, c8, B, n_wg, sh.waves, st);
 }
 
 int out_kind(const Blob& b) {
@@ -553,19 +700,40 @@ DecJob make_job(const Blob& b, void* out) {
   return j;
 }
 
-// Waves per workgroup.  One table copy (56 KB of LDS) serves the workgroup; each wave
-// adds a 4 KB ring.  Small launches use small workgroups so the blocks spread over all
-// 256 CUs; big launches use up to 16 waves (4 per SIMD) to hide the per-step latency.
-int pick_waves(int64_t n_blocks) {
+// Launch shape.  One table copy (56 KB of LDS) serves the workgroup and each chain adds
+// a 64-byte ring, so a workgroup holds at most 16 waves of one chain per lane or 13 of two.
+// The blocks of a launch are dealt to workgroups job by job; a CU holds one workgroup.
+// Cost model: workgroup rounds over the 256 CUs times the length of a round, which grows
+// with the chains per CU once they keep the VALU busy (about 12) and is flat below that.
+// Two chains per lane (EP_DECODE_ILP=2) double the lines a CU keeps open in L2 and thrash
+// it at full occupancy with the per-chain stream layout, so one chain per lane is the
+// default.  EP_DECODE_WAVES overrides the wave count.
+Shape pick_shape(const int64_t* n_blocks, int n) {
   const int cus = 256;
-  int w = (int)std::min<int64_t>(kMaxWaves, std::max<int64_t>(1, (n_blocks + cus - 1) / cus));
-  const int by_lds = (lds_max_bytes() - kTabBytes) / kWaveRingBytes;
-  w = std::min(w, by_lds);
-  if (const char* e = std::getenv("EP_DECODE_WAVES")) {
-    int v = std::atoi(e);
-    if (v >= 1 && v <= kMaxWaves) w = std::min(v, by_lds);
+  const int lds = lds_max_bytes() - kTabBytes;
+  const int max1 = std::max(1, std::min(kMaxWaves, lds / (64 * kChainRingBytes)));
+  const int max2 = std::min(kMaxWaves, lds / (2 * 64 * kChainRingBytes));
+  int ilp = 1;
+  if (const char* e = std::getenv("EP_DECODE_ILP"))
+    if (std::atoi(e) == 2 && max2 >= 1) ilp = 2;
+  const int wmax = ilp == 2 ? max2 : max1;
+  int best_w = 1;
+  int64_t best_cost = -1;
+  for (int w = 1; w <= wmax; w += (w == 1 ? 1 : 2)) {
+    int64_t wg = 0;
+    for (int i = 0; i < n; ++i) wg += (n_blocks[i] + (int64_t)ilp * w - 1) / ((int64_t)ilp * w);
+    const int64_t rounds = (wg + cus - 1) / cus;
+    const int64_t cost = rounds * std::max<int64_t>((int64_t)w * ilp, 12);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_w = w;
+    }
   }
-  return std::max(w, 1);
+  if (const char* e = std::getenv("EP_DECODE_WAVES")) {
+    const int v = std::atoi(e);
+    if (v >= 1 && v <= kMaxWaves) best_w = std::min(v, wmax);
+  }
+  return Shape{ilp, best_w};
 }
 
 int check_uploaded(const Blob& b) {
@@ -590,13 +758,13 @@ int decode_one(const Blob& b, void* dst, int64_t chain_lo, int64_t chain_hi, int
   if (bhi <= blo) return EP_OK;
   j.block_lo = blo;
   const int64_t nblk = bhi - blo;
-  const int waves = pick_waves(nblk);
-  const int64_t n_wg = (nblk + waves - 1) / waves;
+  const Shape sh = pick_shape(&nblk, 1);
+  const int64_t n_wg = (nblk + sh.blocks_per_wg() - 1) / sh.blocks_per_wg();
   j.n_blocks = bhi;   // blocks beyond the range are skipped
   DecBatch B{};
   B.j[0] = j;
   B.n = 1;
-  return launch_any(out, (b.flags & kFlagEsc) != 0, (b.C % 8) == 0, b.k <= 6, B, n_wg, waves, st);
+  return launch_any(out, (b.flags & kFlagEsc) != 0, (b.C % 8) == 0, b.k <= 6, sh, B, n_wg, st);
 }
 
 }  // namespace
@@ -699,7 +867,7 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
   // all blobs of one launch share the container kind and the escape path
   int out = -1;
   bool esc = false, c8 = true;
-  int64_t total_blocks = 0;
+  std::vector<int64_t> nblk(n);
   for (int i = 0; i < n; ++i) {
     if (!blobs[i] || !dsts[i]) return fail(EP_E_ARG, "null blob or destination");
     const Blob& b = blobs[i]->b;
@@ -714,9 +882,9 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
     else if (o != out) return fail(EP_E_ARG, "batch mixes container dtypes");
     esc |= (b.flags & kFlagEsc) != 0;
     c8 &= (b.C % 8) == 0;
-    total_blocks += b.n_blocks;
+    nblk[i] = b.n_blocks;
   }
-  const int waves = pick_waves(total_blocks);
+  const Shape sh = pick_shape(nblk.data(), n);
   // blobs whose tables use the narrow / wide entry layout go to separate launches,
   // each of up to kMaxBatch blobs
   for (int pass = 0; pass < 2; ++pass) {
@@ -731,9 +899,9 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
       for (int q = 0; q < B.n; ++q) {
         B.j[q] = make_job(blobs[idx[i0 + q]]->b, dsts[idx[i0 + q]]);
         B.j[q].wg_begin = wg;
-        wg += (B.j[q].n_blocks + waves - 1) / waves;
+        wg += (B.j[q].n_blocks + sh.blocks_per_wg() - 1) / sh.blocks_per_wg();
       }
-      int rc = launch_any(out, esc, c8, narrow, B, wg, waves, (hipStream_t)stream);
+      int rc = launch_any(out, esc, c8, narrow, sh, B, wg, (hipStream_t)stream);
       if (rc) return rc;
     }
   }

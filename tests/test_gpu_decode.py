@@ -83,6 +83,61 @@ def test_workgroup_sizes(waves):
     _check(f"waves={waves}", synth.rowscaled(257, 1024, 8), nx.DT_BF16, 4.0, S=8, env={"EP_DECODE_WAVES": waves})
 
 
+# Two chains per lane (the forward and backward chain of one region, interleaved): the
+# launch takes this shape by itself from 512 blocks on; here it is forced on small cases
+# that cover odd chain counts (a region with a forward chain only), chains that finish a
+# group earlier than their partner, several blocks per workgroup, escapes and containers.
+ILP2_CASES = [
+    ("ragged 37x13", lambda: synth.rowscaled(37, 13, 50), nx.DT_BF16, 4.0, None, "1"),
+    ("ragged 129x1000", lambda: synth.rowscaled(129, 1000, 51), nx.DT_BF16, 4.0, None, "3"),
+    ("S=8 odd tail", lambda: synth.rowscaled(257, 1024, 52), nx.DT_BF16, 4.0, 8, "2"),
+    ("S=2", lambda: synth.rowscaled(200, 536, 53), nx.DT_BF16, 3.0, 2, "13"),
+    ("S=64", lambda: synth.rowscaled(200, 536, 54), nx.DT_BF16, 3.0, 64, "5"),
+    ("S=1", lambda: synth.rowscaled(300, 520, 55), nx.DT_BF16, 4.0, 1, "4"),
+    ("escapes 8 bpp", lambda: synth.rowscaled(256, 512, 56), nx.DT_BF16, 8.0, 8, "2"),
+    ("escapes 11 bpp", lambda: synth.rowscaled(256, 512, 57), nx.DT_BF16, 11.0, 8, "1"),
+    ("outliers", lambda: synth.rowscaled(512, 1024, 58, 0.001), nx.DT_BF16, 4.0, 8, "13"),
+    ("low rate", lambda: synth.rowscaled(256, 512, 59), nx.DT_BF16, 0.001, 8, "2"),
+    ("fp8", lambda: synth.fp8_codes(512, 520, 60)[0], nx.DT_FP8, 5.0, 8, "3"),
+    ("int8", lambda: synth.int8_codes(512, 520, 61)[0], nx.DT_INT8, 4.0, 8, "3"),
+    ("fp32", lambda: synth.rowscaled_f32(256, 264, 62), nx.DT_FP32, 6.0, 8, "2"),
+]
+
+
+@pytest.mark.parametrize("case", ILP2_CASES, ids=[c[0] for c in ILP2_CASES])
+def test_two_chains_per_lane(case):
+    name, make, dt, t, S, waves = case
+    _check(f"ilp2 {name}", make(), dt, t, S=S, env={"EP_DECODE_ILP": "2", "EP_DECODE_WAVES": waves})
+
+
+def test_two_chains_per_lane_tiles():
+    src = synth.rowscaled(512, 1032, 63)
+    blob = oracle.compress(src, nx.DT_BF16, 4.0, chains_per_tile=8)
+    b = oracle.parse_blob(blob)
+    old = {k: os.environ.get(k) for k in ("EP_DECODE_ILP", "EP_DECODE_WAVES")}
+    os.environ["EP_DECODE_ILP"] = "2"
+    os.environ["EP_DECODE_WAVES"] = "2"
+    try:
+        db = DevBlob(blob)
+        full = db.decode()
+        G = -(-b.C // 8)
+        for (t0, t1) in [(0, 1), (1, 2), (3, 10), (b.n_tiles - 3, b.n_tiles)]:
+            say("ilp2 tiles", t0, t1)
+            part = db.decode_tiles(t0, t1, fill=0x5A)
+            gm = np.zeros(b.R * G, dtype=bool)
+            gm[512 * t0: 512 * t1] = True
+            cm = np.repeat(gm, 8).reshape(b.R, G * 8)[:, :b.C]
+            assert np.array_equal(part[cm], full[cm])
+            assert (part.view(np.uint8).reshape(b.R, -1)[np.repeat(~cm, 2, axis=1)] == 0x5A).all()
+        assert db.errors() == 0
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
 @pytest.mark.parametrize("dt", [nx.DT_FP16, nx.DT_FP32, nx.DT_FP8, nx.DT_INT8])
 def test_containers(dt):
     R, C = 512, 520
