@@ -1,9 +1,12 @@
-// Blob v1 parsing / validation and the host-only C ABI entry points.
+// Blob v2 parsing / validation and the host-only C ABI entry points.
 //
 // Layout (little-endian, packed; this project's format — the pages only say the
 // stream is tile-wise rANS and that actual_bpp counts metadata, [README] 快速开始):
-//   header 48 B | bf16 row scales[R] | model | u32 checkpoints[n_blocks] |
-//   u16 region lengths[ceil(n_chains/2)] | u32 states[n_chains] | u16 stream[n_words]
+//   header 48 B | bf16 row scales[R] | model | u32 block offsets[n_blocks] (chunks) |
+//   full chunks per chain (u8 if S >= 8, else u16)[n_chains] |
+//   tail lengths (4 bits per chain, chain 2i in the low nibble)[ceil(n_chains/2)] |
+//   u32 states[n_chains] | u16 stream[n_words]
+// A block area is [tile main areas (chunks in request order)][tails][pad to 8 words].
 #include <cmath>
 
 #include "ep_internal.h"
@@ -28,7 +31,7 @@ int parse_blob(std::vector<uint8_t>&& bytes, Blob* out) {
   const auto& by = b.bytes;
   if (by.size() < (size_t)kHeaderBytes) return fail(EP_E_CORRUPT, "blob truncated");
   if (std::memcmp(&by[0], "EPK1", 4) != 0) return fail(EP_E_CORRUPT, "bad magic");
-  if (rd<uint16_t>(by, 4) != 1) return fail(EP_E_CORRUPT, "unsupported version");
+  if (rd<uint16_t>(by, 4) != 2) return fail(EP_E_CORRUPT, "unsupported version");
   b.dtype = by[6];
   int P = by[7];
   b.S = by[8];
@@ -52,12 +55,14 @@ int parse_blob(std::vector<uint8_t>&& bytes, Blob* out) {
   if (b.n_tiles != std::max<int64_t>(1, (ng + kTileGroups - 1) / kTileGroups)) return fail(EP_E_CORRUPT, "bad tile count");
   b.n_chains = b.n_tiles * b.S;
   if (b.n_blocks != (b.n_chains + kBlockChains - 1) / kBlockChains) return fail(EP_E_CORRUPT, "bad block count");
-  b.n_regions = (b.n_chains + 1) / 2;
+  const size_t fw = b.S >= 8 ? 1 : 2;
+  const size_t n_nib = (size_t)((b.n_chains + 1) / 2);
   b.off_scales = kHeaderBytes;
   b.off_model = b.off_scales + 2 * (size_t)b.R;
-  b.off_ckpt = b.off_model + b.model_bytes;
-  b.off_rlen = b.off_ckpt + 4 * (size_t)b.n_blocks;
-  b.off_states = b.off_rlen + 2 * (size_t)b.n_regions;
+  b.off_boff = b.off_model + b.model_bytes;
+  b.off_full = b.off_boff + 4 * (size_t)b.n_blocks;
+  b.off_tail = b.off_full + fw * (size_t)b.n_chains;
+  b.off_states = b.off_tail + n_nib;
   b.off_stream = b.off_states + 4 * (size_t)b.n_chains;
   if (b.n_words > (uint64_t)1 << 40 || by.size() != b.off_stream + 2 * (size_t)b.n_words)
     return fail(EP_E_CORRUPT, "blob size mismatch");
@@ -67,23 +72,24 @@ int parse_blob(std::vector<uint8_t>&& bytes, Blob* out) {
   }
   std::string err;
   if (!Model::from_bytes(&by[b.off_model], b.model_bytes, b.k, &b.model, &err)) return fail(EP_E_CORRUPT, err);
-  uint64_t pos = 0;
-  b.max_span_words = 0;
-  uint64_t blk_start = 0;
-  for (int64_t r = 0; r < b.n_regions; ++r) {
-    if (r % (kBlockChains / 2) == 0) {
-      int64_t blk = r / (kBlockChains / 2);
-      if (rd<uint32_t>(by, b.off_ckpt + 4 * (size_t)blk) != pos) return fail(EP_E_CORRUPT, "checkpoint mismatch");
-      if (blk > 0) b.max_span_words = std::max<uint32_t>(b.max_span_words, (uint32_t)(pos - blk_start));
-      blk_start = pos;
-    }
-    uint16_t l = rd<uint16_t>(by, b.off_rlen + 2 * (size_t)r);
-    if (l & 1) return fail(EP_E_CORRUPT, "odd region length");
-    pos += l;
+  b.chain_len.assign((size_t)b.n_chains, 0);
+  for (int64_t c = 0; c < b.n_chains; ++c) {
+    const uint32_t full = fw == 1 ? by[b.off_full + (size_t)c] : rd<uint16_t>(by, b.off_full + 2 * (size_t)c);
+    const uint32_t tail = (by[b.off_tail + (size_t)(c / 2)] >> (4 * (c & 1))) & 15u;
+    if (tail >= 8) return fail(EP_E_CORRUPT, "bad tail length");
+    b.chain_len[c] = 8 * full + tail;
   }
-  b.max_span_words = std::max<uint32_t>(b.max_span_words, (uint32_t)(pos - blk_start));
-  if (pos != b.n_words) return fail(EP_E_CORRUPT, "region lengths do not cover the stream");
-  if (pos > 0xFFFFFFFFull) return fail(EP_E_CORRUPT, "stream too long");
+  if ((b.n_chains & 1) && (by[b.off_tail + n_nib - 1] >> 4)) return fail(EP_E_CORRUPT, "bad tail length");
+  uint64_t chunks = 0;
+  for (int64_t bk = 0; bk < b.n_blocks; ++bk) {
+    if (rd<uint32_t>(by, b.off_boff + 4 * (size_t)bk) != chunks) return fail(EP_E_CORRUPT, "block offset mismatch");
+    const int64_t c1 = std::min<int64_t>(b.n_chains, (bk + 1) * kBlockChains);
+    uint64_t words = 0;
+    for (int64_t c = bk * kBlockChains; c < c1; ++c) words += b.chain_len[c];
+    chunks += (words + 7) / 8;
+    if (chunks > 0xFFFFFFFFull) return fail(EP_E_CORRUPT, "stream too long");
+  }
+  if (8 * chunks != b.n_words) return fail(EP_E_CORRUPT, "chain lengths do not cover the stream");
   for (int64_t c = 0; c < b.n_chains; ++c)
     if (rd<uint32_t>(by, b.off_states + 4 * (size_t)c) < kL) return fail(EP_E_CORRUPT, "state below L");
   return EP_OK;

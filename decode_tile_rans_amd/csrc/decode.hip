@@ -46,14 +46,12 @@ constexpr int kValShift = 22;
 
 struct DecJob {
   const uint16_t* stream;
-  const uint32_t* states;
-  const uint16_t* rlen;
-  const uint32_t* ckpt;
+  const uint32_t* chain;     // per chain 4 x u32: state, tile main start, tail start, length
   const float* hr;
   const uint32_t* tab;
   uint32_t* err;
   void* out;
-  int64_t n_groups, G, C, n_chains, n_regions, n_blocks;
+  int64_t n_groups, G, C, n_chains, n_blocks;
   int64_t chain_lo, chain_hi;
   int64_t block_lo;          // first block decoded by workgroup 0 of this job
   int64_t wg_begin;          // batch: first workgroup of this job
@@ -226,53 +224,108 @@ struct EntryLayout {
 
 // ---- one rANS chain: its state and its stream reader
 //
-// Each chain owns a ring of 32 stream words in LDS; stream word w sits at ring byte
-// 2 (w mod 32).  Words are fetched in aligned 16-byte chunks.  q = words consumed,
-// F = words fetched from the chain's first word on in reading order (the chunk in
-// flight included), next = the next chunk.  Invariant: the chain only reads words
-// already written to its ring.  The ring is serviced every second group: at that point
-// >= 17 words are resident (two groups' symbols consume <= 16); an escape consumes <= 2
-// more and tops up to >= 11 first.  A chunk is written to the ring two groups after its
-// load was issued.
+// Stream layout: a block of 64 chains holds, per tile, the tile's 8-word chunks in the
+// order its chains request them (positions handed out by a ballot in chain order, the
+// tile's cursor advancing by 8 words per chunk), then every chain's last short piece
+// (tail).  Each chain keeps its words in a 32-word LDS ring: word i at ring byte
+// 2 (i mod 32), so chunk n fills ring bytes 16 (n mod 4) .. +15.  F = words fetched
+// (a chunk in flight included), q = words consumed (a2 = 2q).  Fetches happen only
+// at these sites, exactly as the encoder's schedule assumed:
+//   prime: until 17 ahead;  every even group: until 17 ahead, then one round for
+//   chains at most 24 ahead (a 16-byte load issued now, written to the ring two groups
+//   later);  a group with an escape (that chain): until 24 ahead before its careful
+//   decode, until 17 ahead after it.
+// Two escape-free groups consume <= 16 words and one group with escapes <= 24, so the
+// chain only reads words already in its ring; it never holds more than 32 words ahead.
 struct Chain {
-  uint32_t x;       // rANS state
-  uint32_t a2;      // 2 x (index of the next stream word); moves by a2step per word
-  uint32_t nw;      // that word, already read from the ring
-  uint32_t rb;      // LDS byte address of the ring (64-byte aligned)
-  uint32_t a2_0;    // a2 at the chain's first word
-  uint32_t sgn;     // 0 reading up, ~0 reading down: 2q = ((a2 - a2_0) ^ sgn) - sgn
-  int32_t a2step;   // +2 / -2
-  uint32_t next;    // first word of the next chunk
-  int32_t stepc;    // +8 / -8
-  int32_t F;
-  int32_t Fmax;     // words of the region in reading order
-  uint4 pend;       // chunk in flight
-  uint32_t pend_c;
+  uint32_t x;        // rANS state
+  uint32_t a2;       // 2 x words consumed
+  uint32_t nw;       // the next word, already read from the ring
+  uint32_t rb;       // LDS byte address of the ring (64-byte aligned)
+  int32_t F;         // words fetched
+  int32_t N;         // chain length in words
+  uint32_t cur;      // the tile's main-area cursor (word index; equal on the tile's lanes)
+  uint32_t tailp;    // word index of the chain's tail
+  uint32_t seg_lo;   // lanes of the chain's tile (ballot mask)
+  uint32_t seg_hi;
+  uint4 pend;        // chunk in flight
+  int32_t pend_F;    // its first word
   bool have_pend;
 };
 
-__device__ __forceinline__ int32_t ch_q(const Chain& r) {
-  return (int32_t)(((r.a2 - r.a2_0) ^ r.sgn) - r.sgn) >> 1;
-}
-__device__ __forceinline__ void ch_put(uint8_t* lds8, const Chain& r, uint32_t c, uint4 d) {
-  *(uint4*)(lds8 + r.rb + ((c & (kRingWords - 1)) << 1)) = d;
+struct StreamRef {
+  const uint16_t* w;
+  uint32_t last_chunk;   // highest word index a 16-byte load may start at: the stream's
+                         // length (the allocation has 256 bytes of slack after it)
+};
+
+__device__ __forceinline__ int32_t ch_q(const Chain& r) { return (int32_t)(r.a2 >> 1); }
+__device__ __forceinline__ void ch_put(uint8_t* lds8, const Chain& r, int32_t first_word, uint4 d) {
+  *(uint4*)(lds8 + r.rb + ((((uint32_t)first_word >> 3) & 3u) << 4)) = d;
 }
 __device__ __forceinline__ void ch_flush(uint8_t* lds8, Chain& r) {
   if (r.have_pend) {
-    ch_put(lds8, r, r.pend_c, r.pend);
+    ch_put(lds8, r, r.pend_F, r.pend);
     r.have_pend = false;
   }
 }
-// synchronous; rare after the prime
-__device__ __forceinline__ void ch_top_up(uint8_t* lds8, const uint4* chunks, Chain& r, int need) {
-  ch_flush(lds8, r);
-  const int32_t q = ch_q(r);
-  while (r.F - q < need && r.F < r.Fmax) {
-    const uint32_t c = r.next;
-    r.next += r.stepc;
-    r.F += kChunkWords;
-    ch_put(lds8, r, c, chunks[c >> 3]);
+// Positions for one round of requests: full chunks take the tile's next main-area
+// slots in lane (= chain) order, a tail sits at its own place.
+__device__ __forceinline__ uint32_t ch_claim(Chain& r, bool want, bool& full) {
+  full = want && (r.N - r.F >= kChunkWords);
+  const uint64_t m = __ballot(full);
+  const uint32_t mlo = (uint32_t)m & r.seg_lo, mhi = (uint32_t)(m >> 32) & r.seg_hi;
+  const uint32_t rank = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+  const uint32_t pos = full ? r.cur + kChunkWords * rank : r.tailp;
+  r.cur += kChunkWords * (uint32_t)(__builtin_popcount(mlo) + __builtin_popcount(mhi));
+  return pos;
+}
+__device__ __forceinline__ uint4 ld_chunk(const StreamRef& s, uint32_t pos) {
+  return *(const uint4*)(s.w + (pos < s.last_chunk ? pos : s.last_chunk));
+}
+__device__ __forceinline__ uint4 ld_tail(const StreamRef& s, uint32_t pos) {
+  const uint16_t* p = s.w + (pos < s.last_chunk ? pos : s.last_chunk);
+  uint4 d;
+  d.x = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
+  d.y = (uint32_t)p[2] | ((uint32_t)p[3] << 16);
+  d.z = (uint32_t)p[4] | ((uint32_t)p[5] << 16);
+  d.w = (uint32_t)p[6] | ((uint32_t)p[7] << 16);
+  return d;
+}
+// Sync site: rounds until no lane of the wave wants more (every active lane calls it).
+__device__ __forceinline__ void ch_sync(uint8_t* lds8, const StreamRef& s, Chain& r, bool cand, int32_t ahead) {
+  for (;;) {
+    const bool want = cand && r.F - ch_q(r) < ahead && r.F < r.N;
+    if (__ballot(want) == 0) return;
+    bool full;
+    const uint32_t pos = ch_claim(r, want, full);
+    if (want) {
+      ch_put(lds8, r, r.F, full ? ld_chunk(s, pos) : ld_tail(s, pos));
+      r.F = full ? r.F + kChunkWords : r.N;
+    }
   }
+}
+// Service at every even group: write the chunk in flight, top up to 17 ahead, then one
+// round for chains at most 24 ahead.  Full chunks load asynchronously with a fixed
+// pattern (one 16-byte load per lane; lanes without a chunk read the stream's first
+// one, a line every lane shares); tails, rare, are fetched at once.
+__device__ __forceinline__ void ch_service(uint8_t* lds8, const StreamRef& s, Chain& r, bool act) {
+  ch_flush(lds8, r);
+  ch_sync(lds8, s, r, act, 17);
+  const bool want = act && r.F - ch_q(r) <= kRingWords - kChunkWords && r.F < r.N;
+  bool full;
+  const uint32_t pos = ch_claim(r, want, full);
+  const bool tail = want && !full;
+  if (__ballot(tail) != 0) {
+    if (tail) {
+      ch_put(lds8, r, r.F, ld_tail(s, pos));
+      r.F = r.N;
+    }
+  }
+  r.pend_F = r.F;
+  r.pend = ld_chunk(s, full ? pos : 0u);
+  if (full) r.F += kChunkWords;
+  r.have_pend = full;
 }
 __device__ __forceinline__ uint32_t ch_word(const uint8_t* lds8, const Chain& r) {
   return *(const uint16_t*)(lds8 + (r.rb | (r.a2 & 62u)));
@@ -280,7 +333,7 @@ __device__ __forceinline__ uint32_t ch_word(const uint8_t* lds8, const Chain& r)
 __device__ __forceinline__ void ch_renorm_if(const uint8_t* lds8, Chain& r, bool need) {
   if (need) {
     r.x = (r.x << 16) | r.nw;
-    r.a2 += r.a2step;
+    r.a2 += 2u;
     r.nw = ch_word(lds8, r);
   }
 }
@@ -315,27 +368,9 @@ __device__ __forceinline__ uint32_t ch_bypass(const uint8_t* lds8, Chain& r, int
   ch_renorm(lds8, r);
   return v;
 }
-// ring service every second group: write the chunk in flight, top up if short, and
-// issue the next chunk load.  The load pattern is fixed (one 16-byte load per service);
-// a load that is not needed reads the stream's first chunk, one line shared by every
-// lane, always inside the allocation.
-__device__ __forceinline__ void ch_service(uint8_t* lds8, const uint4* chunks, Chain& r) {
-  ch_flush(lds8, r);
-  if (r.F - ch_q(r) < 17) ch_top_up(lds8, chunks, r, 17);
-  const bool issue = r.F - ch_q(r) <= kRingWords - kChunkWords && r.F < r.Fmax;
-  r.pend_c = r.next;
-  r.pend = chunks[issue ? (r.next >> 3) : 0u];
-  if (issue) {
-    r.next += r.stepc;
-    r.F += kChunkWords;
-  }
-  r.have_pend = issue;
-}
 // escape symbol: raw bits follow; returns the doubled coordinate
 template <class LY>
-__device__ __forceinline__ int32_t ch_escape(uint8_t* lds8, const uint4* chunks, Chain& r, uint32_t e, int k,
-                                             int last, int pi) {
-  if (r.F - ch_q(r) - (r.have_pend ? kChunkWords : 0) < 11) ch_top_up(lds8, chunks, r, 11);
+__device__ __forceinline__ int32_t ch_escape(const uint8_t* lds8, Chain& r, uint32_t e, int k, int last, int pi) {
   int c, neg, top2, er;
   LY::esc_info(e, c, neg, top2, er);
   const int ex = k + er;
@@ -347,34 +382,32 @@ __device__ __forceinline__ int32_t ch_escape(uint8_t* lds8, const uint4* chunks,
   const int32_t uu = (int32_t)(2u * m + (uint32_t)c);
   return neg ? -uu : uu;
 }
-// careful decode of one group (the chain's state is at the group's start): FIRST,
-// six FREE, LAST with escapes; tops the ring up again afterwards
+// careful decode of one group (the chain's state is at the group's start and 24 words
+// are in its ring): FIRST, six FREE, LAST, escapes with their raw bits
 template <class LY>
-__device__ __forceinline__ void ch_group_careful(const uint32_t* smem, uint8_t* lds8, const uint4* chunks, Chain& r,
-                                                 int k, int32_t* u) {
+__device__ __forceinline__ void ch_group_careful(const uint32_t* smem, const uint8_t* lds8, Chain& r, int k,
+                                                 int32_t* u) {
   uint32_t ee = ch_entry(smem, r);
   ch_advance(lds8, r, ee);
   const int cc = (int)((ee >> 22) & 1u);
-  u[0] = (ee & LY::kEsc) ? ch_escape<LY>(lds8, chunks, r, ee, k, 0, 0) : LY::u_of(ee);
+  u[0] = (ee & LY::kEsc) ? ch_escape<LY>(lds8, r, ee, k, 0, 0) : LY::u_of(ee);
   int pp = u[0] >> 1;
   const uint32_t* tf = smem + ((1 + cc) << 11);
   for (int i = 1; i < 7; ++i) {
     ee = ch_entry(tf, r);
     ch_advance(lds8, r, ee);
-    u[i] = (ee & LY::kEsc) ? ch_escape<LY>(lds8, chunks, r, ee, k, 0, 0) : LY::u_of(ee);
+    u[i] = (ee & LY::kEsc) ? ch_escape<LY>(lds8, r, ee, k, 0, 0) : LY::u_of(ee);
     pp ^= u[i] >> 1;
   }
   const int pi = pp & 1;
   ee = ch_entry(smem + ((3 + 2 * cc + pi) << 11), r);
   ch_advance(lds8, r, ee);
-  u[7] = (ee & LY::kEsc) ? ch_escape<LY>(lds8, chunks, r, ee, k, 1, pi) : LY::u_of(ee);
-  ch_top_up(lds8, chunks, r, 17);
+  u[7] = (ee & LY::kEsc) ? ch_escape<LY>(lds8, r, ee, k, 1, pi) : LY::u_of(ee);
 }
 
-// One wave decodes ILP blocks of 64 chains.  ILP = 1: lane l runs chain l of its block
-// (even lanes read their region up, odd lanes down).  ILP = 2: lane l runs both chains
-// of region l & 31 of block (l >> 5), the forward and the backward one, interleaved step
-// by step so that one chain's table read is in flight while the other one computes.
+// One wave decodes ILP blocks of 64 chains: lane l runs chain l of each, the ILP chains
+// interleaved step by step so that one chain's table read is in flight while another
+// computes.
 template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
 __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   using LY = EntryLayout<NARROW>;
@@ -401,37 +434,11 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   if (blk0 >= J.n_blocks) return;
 
   uint8_t* const lds8 = (uint8_t*)smem;
-  const uint4* chunks = (const uint4*)J.stream;
+  const StreamRef sref{J.stream, J.n_words};
   const int S = 1 << J.log2S;
-
-  // ---- region starts: a prefix sum over the block's 32 region lengths
-  uint32_t rl, rstart;
-  int64_t ch0;
-  if (ILP == 1) {
-    const int64_t reg = blk0 * 32 + (lane >> 1);
-    rl = (reg < J.n_regions) ? (uint32_t)J.rlen[reg] : 0u;
-    uint32_t v = (lane & 1) ? 0u : rl;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t t = __shfl_up(v, d, 64);
-      if (lane >= d) v += t;
-    }
-    rstart = J.ckpt[blk0] + v - rl;
-    ch0 = blk0 * 64 + lane;
-  } else {
-    const int64_t blk = blk0 + (lane >> 5);
-    const bool bok = blk < J.n_blocks;
-    const int64_t reg = blk * 32 + (lane & 31);
-    rl = (bok && reg < J.n_regions) ? (uint32_t)J.rlen[reg] : 0u;
-    uint32_t v = rl;
-#pragma unroll
-    for (int d = 1; d < 32; d <<= 1) {
-      const uint32_t t = __shfl_up(v, d, 32);
-      if ((lane & 31) >= d) v += t;
-    }
-    rstart = (bok ? J.ckpt[blk] : 0u) + v - rl;
-    ch0 = 2 * reg;
-  }
+  // lanes of this lane's tile (S consecutive lanes)
+  const int s0 = lane & ~(S - 1);
+  const uint64_t seg = (S == 64) ? ~0ull : (((1ull << S) - 1ull) << s0);
 
   char* outp = (char*)J.out;
   constexpr int ESZ = (OUT == OUT_FP32 || OUT == OUT_COORDS) ? 4 : ((OUT == OUT_FP8 || OUT == OUT_INT8) ? 1 : 2);
@@ -445,9 +452,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   char* optr[ILP];
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
-    const int64_t ch = ch0 + c;
-    const bool fwd = (ILP == 1) ? ((lane & 1) == 0) : (c == 0);
-    const uint32_t p0 = fwd ? rstart : rstart + rl - 1u;   // the chain's first word
+    const int64_t ch = (blk0 + c) * 64 + lane;
     live[c] = ch < J.n_chains && ch >= J.chain_lo && ch < J.chain_hi;
     const int64_t t = ch >> J.log2S;
     const int j = (int)(ch & (S - 1));
@@ -455,26 +460,30 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
     if (gt > kTileGroups) gt = kTileGroups;
     ngr[c] = (live[c] && gt > j) ? (int)((gt - j + S - 1) >> J.log2S) : 0;
     Chain& r = rd[c];
-    r.x = (ch < J.n_chains) ? J.states[ch] : kL;
+    uint4 meta = make_uint4(kL, 0u, 0u, 0u);
+    if (live[c]) meta = ((const uint4*)J.chain)[ch];
+    r.x = meta.x;
+    r.cur = meta.y;
+    r.tailp = meta.z;
+    r.N = (int32_t)meta.w;
+    r.F = 0;
+    r.a2 = 0;
     r.rb = (uint32_t)(kTabBytes + ((wave * 64 + lane) * ILP + c) * kChainRingBytes);
-    r.a2 = 2u * p0;
-    r.a2_0 = r.a2;
-    r.sgn = fwd ? 0u : ~0u;
-    r.a2step = fwd ? 2 : -2;
-    r.next = p0 & ~(uint32_t)(kChunkWords - 1);
-    r.F = fwd ? -(int32_t)(p0 & (kChunkWords - 1)) : (int32_t)(p0 & (kChunkWords - 1)) - (kChunkWords - 1);
-    r.Fmax = (int32_t)rl;
-    r.stepc = fwd ? kChunkWords : -kChunkWords;
+    r.seg_lo = (uint32_t)seg;
+    r.seg_hi = (uint32_t)(seg >> 32);
     r.pend = make_uint4(0u, 0u, 0u, 0u);
-    r.pend_c = 0;
+    r.pend_F = 0;
     r.have_pend = false;
-    if (live[c] && rl) ch_top_up(lds8, chunks, r, 17);
-    r.nw = ch_word(lds8, r);
     const int64_t g0 = (t << 9) + j;
     row[c] = live[c] ? (uint32_t)(g0 / J.G) : 0u;
     col[c] = live[c] ? (uint32_t)(g0 - (int64_t)row[c] * J.G) : 0u;
     h[c] = ngr[c] > 0 ? J.hr[row[c]] : 0.f;
     optr[c] = outp + (live[c] ? g0 * 8 * ESZ : 0);   // C % 8 == 0: groups are contiguous
+  }
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) {
+    ch_sync(lds8, sref, rd[c], live[c], 17);   // prime
+    rd[c].nw = ch_word(lds8, rd[c]);
   }
   int nmax = ngr[0], nmin = ngr[0];
 #pragma unroll
@@ -487,7 +496,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   for (int kk = 0; kk < nmax; ++kk) {
     if ((kk & 1) == 0) {
 #pragma unroll
-      for (int c = 0; c < ILP; ++c) ch_service(lds8, chunks, rd[c]);
+      for (int c = 0; c < ILP; ++c) ch_service(lds8, sref, rd[c], (ILP == 1) || kk < ngr[c]);
     }
     // ---- row scale of the next group, loaded one group ahead
     uint32_t nrow[ILP], ncol[ILP];
@@ -551,20 +560,29 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
         const uint32_t any = (e[c][0] | e[c][1] | e[c][2]) | (e[c][3] | e[c][4] | e[c][5]) | (e[c][6] | e[c][7]);
         slow = act && (any & LY::kEsc) != 0;
       }
+      if (ESC && __ballot(slow) != 0) {
+        // careful path for the chains whose group holds an escape: fetch to 24 ahead,
+        // replay the group from its start, fetch back to 17 ahead
+        if (slow) {
+          rd[c].x = xs[c];
+          rd[c].a2 = a2s[c];
+          ch_flush(lds8, rd[c]);
+        }
+        ch_sync(lds8, sref, rd[c], slow, 24);
+        if (slow) {
+          rd[c].nw = ch_word(lds8, rd[c]);
+          ch_group_careful<LY>(smem, lds8, rd[c], k, u);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i] = h[c] * (float)u[i];
+        }
+        ch_sync(lds8, sref, rd[c], slow, 17);
+      }
       if (!slow) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           if (OUT == OUT_COORDS) u[i] = LY::u_of(e[c][i]);
           else w[i] = LY::w_of(e[c][i], h[c], -128.f * h[c]);
         }
-      } else {
-        // replay the group from its start with escape handling
-        rd[c].x = xs[c];
-        rd[c].a2 = a2s[c];
-        rd[c].nw = nws[c];
-        ch_group_careful<LY>(smem, lds8, chunks, rd[c], k, u);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = h[c] * (float)u[i];
       }
       if (act) {
         if (C8) {
@@ -596,7 +614,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   }
 #pragma unroll
   for (int c = 0; c < ILP; ++c)
-    if (live[c] && rd[c].x != kL) atomicAdd(J.err, 1u);
+    if (live[c] && ngr[c] > 0 && rd[c].x != kL) atomicAdd(J.err, 1u);
 }
 
 // ---------------------------------------------------------------- launch helpers
@@ -673,9 +691,7 @@ int out_kind(const Blob& b) {
 DecJob make_job(const Blob& b, void* out) {
   DecJob j{};
   j.stream = b.d_stream;
-  j.states = b.d_states;
-  j.rlen = b.d_rlen;
-  j.ckpt = b.d_ckpt;
+  j.chain = b.d_chain;
   j.hr = b.d_hr;
   j.tab = b.d_tab;
   j.err = b.d_err;
@@ -684,7 +700,6 @@ DecJob make_job(const Blob& b, void* out) {
   j.G = (b.C + 7) / 8;
   j.C = b.C;
   j.n_chains = b.n_chains;
-  j.n_regions = b.n_regions;
   j.n_blocks = b.n_blocks;
   j.chain_lo = 0;
   j.chain_hi = b.n_chains;
@@ -794,10 +809,8 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
   auto al = [](size_t v) { return (v + 255) & ~size_t(255); };
   const size_t o_tab = 0;
   const size_t o_hr = o_tab + al(kTabBytes);
-  const size_t o_st = o_hr + al(4 * (size_t)b.R);
-  const size_t o_ck = o_st + al(4 * (size_t)b.n_chains);
-  const size_t o_rl = o_ck + al(4 * (size_t)(b.n_blocks + 1));
-  const size_t o_err = o_rl + al(2 * (size_t)b.n_regions);
+  const size_t o_ch = o_hr + al(4 * (size_t)b.R);
+  const size_t o_err = o_ch + al(16 * (size_t)b.n_chains);
   const size_t o_stream = o_err + 256;
   const size_t total = o_stream + al(2 * (size_t)b.n_words + 256);
   std::vector<uint8_t> host;
@@ -808,11 +821,35 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
   }
   build_slot_tables(b.model, (uint32_t*)&host[o_tab], b.k <= 6);
   half_scales(b, (float*)&host[o_hr]);
-  std::memcpy(&host[o_st], &b.bytes[b.off_states], 4 * (size_t)b.n_chains);
-  std::memcpy(&host[o_ck], &b.bytes[b.off_ckpt], 4 * (size_t)b.n_blocks);
-  uint32_t nw = (uint32_t)b.n_words;
-  std::memcpy(&host[o_ck + 4 * (size_t)b.n_blocks], &nw, 4);
-  std::memcpy(&host[o_rl], &b.bytes[b.off_rlen], 2 * (size_t)b.n_regions);
+  // per chain: state, word index of its tile's main area, of its tail, length
+  {
+    uint32_t* meta = (uint32_t*)&host[o_ch];
+    uint64_t block_start = 0;   // words
+    for (int64_t bk = 0; bk < b.n_blocks; ++bk) {
+      const int64_t c0 = bk * kBlockChains, c1 = std::min<int64_t>(b.n_chains, c0 + kBlockChains);
+      uint64_t main = block_start, words = 0;
+      for (int64_t c = c0; c < c1; ++c) words += b.chain_len[c];
+      uint64_t tails = block_start;
+      for (int64_t c = c0; c < c1; ++c) tails += 8 * (b.chain_len[c] / 8);
+      for (int64_t t0 = c0; t0 < c1; t0 += b.S) {
+        uint64_t tile_words = 0;
+        for (int64_t c = t0; c < t0 + b.S; ++c) tile_words += 8 * (b.chain_len[c] / 8);
+        for (int64_t c = t0; c < t0 + b.S; ++c) {
+          uint32_t st;
+          std::memcpy(&st, &b.bytes[b.off_states + 4 * (size_t)c], 4);
+          meta[4 * c + 0] = st;
+          meta[4 * c + 1] = (uint32_t)main;
+          meta[4 * c + 3] = b.chain_len[c];
+        }
+        main += tile_words;
+      }
+      for (int64_t c = c0; c < c1; ++c) {
+        meta[4 * c + 2] = (uint32_t)tails;
+        tails += b.chain_len[c] % 8;
+      }
+      block_start += 8 * ((words + 7) / 8);
+    }
+  }
   std::memcpy(&host[o_stream], &b.bytes[b.off_stream], 2 * (size_t)b.n_words);
   void* d = nullptr;
   if (hipMalloc(&d, total) != hipSuccess) {
@@ -830,9 +867,7 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
   uint8_t* p = (uint8_t*)d;
   b.d_tab = (const uint32_t*)(p + o_tab);
   b.d_hr = (const float*)(p + o_hr);
-  b.d_states = (const uint32_t*)(p + o_st);
-  b.d_ckpt = (const uint32_t*)(p + o_ck);
-  b.d_rlen = (const uint16_t*)(p + o_rl);
+  b.d_chain = (const uint32_t*)(p + o_ch);
   b.d_err = (uint32_t*)(p + o_err);
   b.d_stream = (const uint16_t*)(p + o_stream);
   return EP_OK;

@@ -306,6 +306,9 @@ Estimate estimate(const Matrix& mx, const std::vector<int64_t>& rows, float delt
 struct ChainOut {
   std::vector<uint16_t> words;   // decoding order
   uint32_t state;
+  std::vector<uint8_t> cons;     // words the decoder reads in each of the chain's groups
+  std::vector<uint8_t> slow;     // group holds a bucket (escape) symbol
+  std::vector<uint16_t> rank;    // main-area position of each full chunk in its tile
 };
 
 void encode_chain(const int32_t* u_all, const Model& m, int64_t t, int j, int S, int64_t n_groups,
@@ -325,9 +328,13 @@ void encode_chain(const int32_t* u_all, const Model& m, int64_t t, int j, int S,
   };
   Sym s[8];
   int ms[8];
+  out->cons.assign((size_t)ngr, 0);
+  out->slow.assign((size_t)ngr, 0);
   for (int kk = ngr - 1; kk >= 0; --kk) {
     int64_t g = (int64_t)kTileGroups * t + j + (int64_t)kk * S;
     symbolize(u_all + g * 8, m.k, s, ms);
+    const size_t w0 = w.size();
+    for (int i = 0; i < 8; ++i) out->slow[kk] |= ms[i] >= (1 << m.k);
     for (int i = 7; i >= 0; --i) {
       int rb = s[i].rawbits;
       if (rb > 16) bypass(s[i].rawval >> 16, rb - 16);
@@ -337,9 +344,67 @@ void encode_chain(const int32_t* u_all, const Model& m, int64_t t, int j, int S,
       if (x >= (f << 21)) emit();
       x = (x / f) * (uint64_t)kM + (x % f) + cum;
     }
+    out->cons[kk] = (uint8_t)(w.size() - w0);
   }
   std::reverse(w.begin(), w.end());
   out->state = (uint32_t)x;
+}
+
+// ------------------------------------------------------------------ stream layout
+// Request order of one tile's full chunks.  The decoder keeps a window of at most 32
+// fetched words per chain and fetches 8-word chunks only at these sites, chains taking
+// turns in chain order; a sync site repeats rounds until no chain wants more:
+//   prime: until 17 words ahead;  every even group: until 17 ahead, then one round for
+//   chains at most 24 ahead;  a group with an escape (that chain): until 24 ahead before
+//   it, until 17 ahead after it.  Only chains that decode the group take part; a chain's
+//   last short chunk (its tail) counts as a request but lives in the block's tail area.
+void schedule_tile(ChainOut* ch, int S) {
+  int32_t F[64], q[64], n[64], ngr[64];
+  uint16_t ctr = 0;
+  int gmax = 0;
+  for (int j = 0; j < S; ++j) {
+    F[j] = 0;
+    q[j] = 0;
+    n[j] = (int32_t)ch[j].words.size();
+    ngr[j] = (int32_t)ch[j].cons.size();
+    gmax = std::max(gmax, ngr[j]);
+    ch[j].rank.clear();
+  }
+  auto take = [&](int j) {
+    if (n[j] - F[j] >= 8) {
+      ch[j].rank.push_back(ctr++);
+      F[j] += 8;
+    } else {
+      F[j] = n[j];
+    }
+  };
+  auto sync = [&](auto cand, int32_t ahead) {
+    for (;;) {
+      bool any = false;
+      for (int j = 0; j < S; ++j)
+        if (cand(j) && F[j] - q[j] < ahead && F[j] < n[j]) {
+          take(j);
+          any = true;
+        }
+      if (!any) return;
+    }
+  };
+  sync([](int) { return true; }, 17);
+  for (int g = 0; g < gmax; ++g) {
+    auto act = [&](int j) { return g < ngr[j]; };
+    if ((g & 1) == 0) {
+      sync(act, 17);
+      for (int j = 0; j < S; ++j)
+        if (act(j) && F[j] - q[j] <= 24 && F[j] < n[j]) take(j);
+    }
+    auto slow = [&](int j) { return g < ngr[j] && ch[j].slow[g]; };
+    bool any_slow = false;
+    for (int j = 0; j < S; ++j) any_slow |= slow(j);
+    if (any_slow) sync(slow, 24);
+    for (int j = 0; j < S; ++j)
+      if (act(j)) q[j] += ch[j].cons[g];
+    if (any_slow) sync(slow, 17);
+  }
 }
 
 void put_u16(std::vector<uint8_t>& b, size_t off, uint16_t v) { std::memcpy(&b[off], &v, 2); }
@@ -527,6 +592,9 @@ int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_r
   parallel_for(n_chains, [&](int64_t b, int64_t e, int) {
     for (int64_t ch = b; ch < e; ++ch) encode_chain(u.data(), m, ch / S, (int)(ch % S), S, n_groups, &chains[ch]);
   }, 64);
+  parallel_for(n_tiles, [&](int64_t b, int64_t e, int) {
+    for (int64_t tt = b; tt < e; ++tt) schedule_tile(&chains[(size_t)(tt * S)], S);
+  }, 16);
 
   // ---- saturation flag
   std::atomic<bool> sat{false};
@@ -549,22 +617,30 @@ int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_r
     }, 16);
   }
 
-  // ---- regions, checkpoints, stream
-  const int64_t n_regions = (n_chains + 1) / 2;
+  // ---- block layout: per block of 64 chains [tile main areas][tails][pad to 8 words]
   const int64_t n_blocks = (n_chains + kBlockChains - 1) / kBlockChains;
-  std::vector<uint16_t> rlen((size_t)n_regions);
-  uint64_t n_words = 0;
-  for (int64_t r = 0; r < n_regions; ++r) {
-    size_t a = chains[2 * r].words.size();
-    size_t bsz = (2 * r + 1 < n_chains) ? chains[2 * r + 1].words.size() : 0;
-    size_t len = a + bsz + ((a + bsz) & 1);
-    if (len > 0xFFFF) return fail(EP_E_ARG, "region longer than 65535 words");
-    rlen[r] = (uint16_t)len;
-    n_words += len;
+  const size_t fw = S >= 8 ? 1 : 2;
+  const int64_t max_full = S >= 8 ? 0xFF : 0xFFFF;
+  std::vector<uint64_t> block_off((size_t)n_blocks + 1, 0);   // in chunks
+  for (int64_t bk = 0; bk < n_blocks; ++bk) {
+    const int64_t c0 = bk * kBlockChains, c1 = std::min(n_chains, c0 + kBlockChains);
+    uint64_t words = 0;
+    for (int64_t c = c0; c < c1; ++c) {
+      const uint64_t len = chains[c].words.size();
+      if ((int64_t)(len / 8) > max_full) return fail(EP_E_ARG, "chain longer than the chunk count field");
+      words += len;
+    }
+    uint64_t full_words = 0;
+    for (int64_t c = c0; c < c1; ++c) full_words += 8 * (chains[c].words.size() / 8);
+    uint64_t tail_words = words - full_words;
+    block_off[bk + 1] = block_off[bk] + (full_words + tail_words + 7) / 8;
   }
+  const uint64_t n_words = 8 * block_off[n_blocks];
+  if (block_off[n_blocks] > 0xFFFFFFFFull) return fail(EP_E_ARG, "stream too long for the block offsets");
   const std::vector<uint8_t> mbytes = m.to_bytes();
-  const size_t total = kHeaderBytes + 2 * (size_t)R + mbytes.size() + 4 * (size_t)n_blocks + 2 * (size_t)n_regions +
-                       4 * (size_t)n_chains + 2 * (size_t)n_words;
+  const size_t n_nib = (size_t)((n_chains + 1) / 2);
+  const size_t total = kHeaderBytes + 2 * (size_t)R + mbytes.size() + 4 * (size_t)n_blocks + fw * (size_t)n_chains +
+                       n_nib + 4 * (size_t)n_chains + 2 * (size_t)n_words;
   std::vector<uint8_t>& b = *out;
   try {
     b.assign(total, 0);
@@ -572,7 +648,7 @@ int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_r
     return fail(EP_E_NOMEM, "out of host memory");
   }
   std::memcpy(&b[0], "EPK1", 4);
-  put_u16(b, 4, 1);
+  put_u16(b, 4, 2);
   b[6] = (uint8_t)dtype;
   b[7] = (uint8_t)kP;
   b[8] = (uint8_t)S;
@@ -591,35 +667,48 @@ int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_r
   for (int64_t r = 0; r < R; ++r, off += 2) put_u16(b, off, mx.s_bits[r]);
   std::memcpy(&b[off], mbytes.data(), mbytes.size());
   off += mbytes.size();
-  const size_t off_ck = off;
+  const size_t off_bo = off;
   off += 4 * (size_t)n_blocks;
-  const size_t off_rl = off;
-  off += 2 * (size_t)n_regions;
+  const size_t off_full = off;
+  off += fw * (size_t)n_chains;
+  const size_t off_nib = off;
+  off += n_nib;
   const size_t off_st = off;
   off += 4 * (size_t)n_chains;
   const size_t off_stream = off;
-  uint64_t pos = 0;
-  for (int64_t r = 0; r < n_regions; ++r) {
-    if ((r % (kBlockChains / 2)) == 0) put_u32(b, off_ck + 4 * (size_t)(r / (kBlockChains / 2)), (uint32_t)pos);
-    put_u16(b, off_rl + 2 * (size_t)r, rlen[r]);
-    const auto& wa = chains[2 * r].words;
-    size_t q = off_stream + 2 * (size_t)pos;
-    for (uint16_t v : wa) {
-      std::memcpy(&b[q], &v, 2);
-      q += 2;
-    }
-    size_t nb = 0;
-    if (2 * r + 1 < n_chains) nb = chains[2 * r + 1].words.size();
-    if ((wa.size() + nb) & 1) q += 2;   // zero pad word
-    if (2 * r + 1 < n_chains) {
-      const auto& wb = chains[2 * r + 1].words;
-      for (size_t i = wb.size(); i-- > 0;) {
-        std::memcpy(&b[q], &wb[i], 2);
-        q += 2;
+  for (int64_t bk = 0; bk < n_blocks; ++bk) put_u32(b, off_bo + 4 * (size_t)bk, (uint32_t)block_off[bk]);
+  for (int64_t c = 0; c < n_chains; ++c) {
+    const size_t len = chains[c].words.size();
+    if (fw == 1) b[off_full + (size_t)c] = (uint8_t)(len / 8);
+    else put_u16(b, off_full + 2 * (size_t)c, (uint16_t)(len / 8));
+    b[off_nib + (size_t)(c / 2)] |= (uint8_t)((len % 8) << (4 * (c & 1)));
+  }
+  parallel_for(n_blocks, [&](int64_t bb, int64_t be, int) {
+    for (int64_t bk = bb; bk < be; ++bk) {
+      const int64_t c0 = bk * kBlockChains, c1 = std::min(n_chains, c0 + kBlockChains);
+      const size_t base = off_stream + 16 * (size_t)block_off[bk];
+      size_t tile_main = 0;   // words from the block start
+      size_t tails = 0;
+      for (int64_t c = c0; c < c1; ++c) tails += 8 * (chains[c].words.size() / 8);
+      for (int64_t t0 = c0; t0 < c1; t0 += S) {
+        size_t tile_words = 0;
+        for (int64_t c = t0; c < t0 + S; ++c) {
+          const auto& w = chains[c].words;
+          const size_t nf = w.size() / 8;
+          for (size_t nn = 0; nn < nf; ++nn)
+            std::memcpy(&b[base + 2 * (tile_main + 8 * (size_t)chains[c].rank[nn])], &w[8 * nn], 16);
+          tile_words += 8 * nf;
+        }
+        tile_main += tile_words;
+      }
+      for (int64_t c = c0; c < c1; ++c) {
+        const auto& w = chains[c].words;
+        const size_t nf = w.size() / 8, r = w.size() % 8;
+        if (r) std::memcpy(&b[base + 2 * tails], &w[8 * nf], 2 * r);
+        tails += r;
       }
     }
-    pos += rlen[r];
-  }
+  }, 1);
   for (int64_t ch = 0; ch < n_chains; ++ch) put_u32(b, off_st + 4 * (size_t)ch, chains[ch].state);
   return EP_OK;
 }

@@ -5,9 +5,10 @@
 // for the page keys):
 //   P = 11 (2048 slots per table), 32-bit rANS state in [2^16, 2^32), 16-bit words;
 //   tiles of 512 groups x 8 columns (4096 coordinates), S chains per tile, chain j
-//   decodes the tile's groups j, j+S, ...; chains 2i / 2i+1 share a region (forward
-//   / backward), one region length (u16, even) per pair, one checkpoint (u32 word
-//   offset) per 64 chains.
+//   decodes the tile's groups j, j+S, ...; a block of 64 chains stores its tiles'
+//   8-word chunks in the order the decoder requests them, then the chains' short
+//   tails; one u32 offset per block, one full-chunk count and one tail length per
+//   chain.
 #pragma once
 #include <cstdint>
 #include <cstring>
@@ -76,19 +77,18 @@ struct Blob {
   int dtype = 0, S = 0, k = 0, flags = 0;
   int64_t R = 0, C = 0;
   float delta = 0.f;
-  int64_t n_tiles = 0, n_blocks = 0, n_chains = 0, n_regions = 0;
+  int64_t n_tiles = 0, n_blocks = 0, n_chains = 0;
   uint64_t n_words = 0;
-  size_t off_scales = 0, off_model = 0, off_ckpt = 0, off_rlen = 0, off_states = 0, off_stream = 0;
+  size_t off_scales = 0, off_model = 0, off_boff = 0, off_full = 0, off_tail = 0, off_states = 0,
+         off_stream = 0;
   uint32_t model_bytes = 0;
   Model model;
-  uint32_t max_span_words = 0;         // largest block span (words)
+  std::vector<uint32_t> chain_len;     // words per chain
   // device mirror
   int device = -1;
   void* d_base = nullptr;              // one allocation
   const uint16_t* d_stream = nullptr;
-  const uint32_t* d_states = nullptr;
-  const uint16_t* d_rlen = nullptr;
-  const uint32_t* d_ckpt = nullptr;    // n_blocks + 1 entries
+  const uint32_t* d_chain = nullptr;   // per chain 4 x u32: state, tile main start, tail start, length
   const float* d_hr = nullptr;         // per-row half scales h_r
   const uint32_t* d_tab = nullptr;     // 7 x 2048 packed entries
   uint32_t* d_err = nullptr;

@@ -1,4 +1,4 @@
-"""Compress / decode and the blob v1 byte layout (oracle).
+"""Compress / decode and the blob v2 byte layout (oracle).
 
 [README] quick start: ``compress(tensor, config)`` / ``decompress`` restore
 shape and dtype; ``target_bpp`` is finite in [0.001, 11] and may be
@@ -6,25 +6,28 @@ non-integer; ``actual_bpp`` includes the metadata.  [NEWS]: lossy mode is for
 2-D floating and integer tensors only.  [ABS]/[SUM]: tiles are independently
 decodable and rANS-coded.
 
-Blob v1 (little-endian, packed, this project's format):
+Blob v2 (little-endian, packed, this project's format):
 
-  header (48 B)   'EPK1' | u16 version=1 | u8 dtype | u8 P=11 | u8 S | u8 k |
+  header (48 B)   'EPK1' | u16 version=2 | u8 dtype | u8 P=11 | u8 S | u8 k |
                   u8 flags (bit0: some escape, bit1: some value needs clamping)
                   | u8 tile_log2=12 | u32 R | u32 C | f32 delta | u32 n_tiles |
                   u32 n_blocks | u64 n_words | u32 model_bytes | u32 0
   row scales      bf16[R]
   model           model_bytes (bit-packed coset weight + magnitude frequencies)
-  checkpoints     u32[n_blocks]   word offset of each block of 64 chains
-  region lengths  u16[ceil(n_chains/2)]  (even; chains 2i / 2i+1 share a region)
+  block offsets   u32[n_blocks]  start of each block's area, in 8-word chunks
+  full chunks     u8[n_chains] if S >= 8 else u16[n_chains]: len // 8 per chain
+  tail lengths    u8[ceil(n_chains / 2)]: len % 8 of chain 2i (low nibble) and
+                  2i + 1 (high nibble)
   states          u32[n_chains]
-  stream          u16[n_words]
+  stream          u16[n_words]   the block areas, back to back (``layout``)
 
 Groups: row-major 8-wide column groups (columns padded with zeros to a
 multiple of 8; padded coordinates are coded and dropped).  Tile t holds
 groups [512 t, 512 t + 512) (4096 coordinates); chain j of tile t decodes
-its local groups j, j + S, j + 2S, ...  Chains are numbered t*S + j.  Chain
-2i reads its words forward from the region start, chain 2i+1 backward from
-the region end; one zero word separates them when their total is odd.
+its local groups j, j + S, j + 2S, ...  Chains are numbered t*S + j; a block
+is 64 consecutive chains (n_blocks = ceil(n_chains / 64)).  A tile's area
+holds its tiles' chains' words: 8-word chunks in the order a reader with a
+32-word window per chain requests them, then the short tails (``layout``).
 
 actual_bpp = 8 * len(blob) / (R * C).
 
@@ -41,11 +44,12 @@ import numpy as np
 
 from . import numerics as nx
 from .model import Model, group_symbols, count_symbols, build_model, n_msym
-from .rans import encode_chains, decode_chains, WordReader, L
+from .rans import encode_chains, ChainDecoder, L
+from .layout import CHUNK, TileSchedule, request_ranks, block_geometry, build_stream
 from .rate import row_scales_bf16, half_steps, quantize_rows, select_delta
 
 MAGIC = b"EPK1"
-VERSION = 1
+VERSION = 2
 HEADER = struct.Struct("<4sHBBBBBBIIfIIQII")
 assert HEADER.size == 48
 TILE_LOG2 = 12
@@ -107,8 +111,8 @@ class Blob:
     s_bits: np.ndarray
     model: Model
     model_bytes: bytes
-    checkpoints: np.ndarray
-    region_len: np.ndarray
+    block_offsets: np.ndarray
+    chain_lens: np.ndarray
     states: np.ndarray
     stream: np.ndarray
 
@@ -124,35 +128,26 @@ class Blob:
         hdr = HEADER.pack(MAGIC, VERSION, self.dtype, 11, self.S, self.k, self.flags, TILE_LOG2,
                           self.R, self.C, float(self.delta), self.n_tiles, self.n_blocks,
                           len(self.stream), len(self.model_bytes), 0)
+        lens = self.chain_lens.astype(np.int64)
+        full = (lens // CHUNK).astype("<u1" if self.S >= 8 else "<u2")
+        tails = np.zeros(2 * (-(-len(lens) // 2)), dtype=np.int64)
+        tails[:len(lens)] = lens % CHUNK
+        nib = (tails[0::2] | (tails[1::2] << 4)).astype("<u1")
         return b"".join([hdr, self.s_bits.astype("<u2").tobytes(), self.model_bytes,
-                         self.checkpoints.astype("<u4").tobytes(), self.region_len.astype("<u2").tobytes(),
+                         self.block_offsets.astype("<u4").tobytes(), full.tobytes(), nib.tobytes(),
                          self.states.astype("<u4").tobytes(), self.stream.astype("<u2").tobytes()])
 
 
-def _layout_regions(words, n_ch):
-    """Paired regions: returns (region_len u16[], stream u16[], checkpoints u32[])."""
-    n_reg = -(-n_ch // 2)
-    parts = []
-    rl = np.zeros(n_reg, dtype=np.int64)
-    for r in range(n_reg):
-        a = words[2 * r]
-        b = words[2 * r + 1] if 2 * r + 1 < n_ch else np.zeros(0, np.uint16)
-        pad = (len(a) + len(b)) & 1
-        parts.append(a)
-        if pad:
-            parts.append(np.zeros(1, np.uint16))
-        parts.append(b[::-1])
-        rl[r] = len(a) + len(b) + pad
-    assert (rl <= 0xFFFF).all()
-    stream = np.concatenate(parts) if parts else np.zeros(0, np.uint16)
-    starts = np.concatenate([[0], np.cumsum(rl)[:-1]]) if n_reg else np.zeros(0, np.int64)
-    n_blocks = -(-n_ch // BLOCK_CHAINS)
-    ck = starts[np.arange(n_blocks) * (BLOCK_CHAINS // 2)] if n_reg else np.zeros(n_blocks, np.int64)
-    return rl.astype(np.uint16), stream.astype(np.uint16), ck.astype(np.uint32)
+def chain_group_counts(n_groups: int, S: int, n_tiles: int):
+    """Groups decoded by each chain, shaped (n_tiles, S)."""
+    t = np.arange(n_tiles)[:, None]
+    j = np.arange(S)[None, :]
+    gt = np.minimum(n_groups - TILE_GROUPS * t, TILE_GROUPS)
+    return np.where(gt > j, (gt - j + S - 1) // S, 0)
 
 
 def compress(src, dtype: int, target_bpp: float, chains_per_tile=None, trace=None) -> bytes:
-    """Compress a 2-D container array (BF16/FP8 as bit patterns) to blob v1 bytes."""
+    """Compress a 2-D container array (BF16/FP8 as bit patterns) to blob v2 bytes."""
     src = np.asarray(src)
     validate(src.shape, dtype, target_bpp)
     R, C = src.shape
@@ -178,8 +173,16 @@ def compress(src, dtype: int, target_bpp: float, chains_per_tile=None, trace=Non
     S = chains_per_tile or default_chains_per_tile(R * C)
     assert S in (1, 2, 4, 8, 16, 32, 64)
     n_tiles, cg = chain_layout(n_groups, S)
-    states, words = encode_chains(sym, model, cg)
-    rl, stream, ck = _layout_regions(words, n_tiles * S)
+    states, words, cons = encode_chains(sym, model, cg)
+    lens = np.array([len(w) for w in words], dtype=np.int64).reshape(n_tiles, S)
+    assert (lens // CHUNK <= (0xFF if S >= 8 else 0xFFFF)).all()
+    # a group is decoded on the careful path when it holds a bucket symbol
+    esc_g = (sym["msym"] >= (1 << k)).any(axis=1)
+    slow = np.where(cg >= 0, esc_g[np.maximum(cg, 0)], False)
+    ngr = chain_group_counts(n_groups, S, n_tiles)
+    steps = cg.shape[1]
+    rank = request_ranks(lens, ngr, cons.reshape(n_tiles, S, steps), slow.reshape(n_tiles, S, steps))
+    offsets, stream = build_stream(words, lens.reshape(-1), rank, S)
     flags = 0
     if (sym["msym"] >= (1 << k)).any():
         flags |= FLAG_ESC
@@ -187,7 +190,7 @@ def compress(src, dtype: int, target_bpp: float, chains_per_tile=None, trace=Non
     if nx.needs_saturation(wh, dtype):
         flags |= FLAG_SAT
     blob = Blob(dtype, S, k, flags, R, C, np.float32(delta), n_tiles, s_bits, model, model.to_bytes(),
-                ck, rl, states, stream)
+                offsets, lens.reshape(-1).astype(np.uint16), states, stream)
     return blob.to_bytes()
 
 
@@ -208,9 +211,10 @@ def parse_blob(buf: bytes) -> Blob:
     n_ch = n_tiles * S
     if n_blocks != -(-n_ch // BLOCK_CHAINS):
         raise ValueError("bad block count")
-    n_reg = -(-n_ch // 2)
     off = HEADER.size
-    need = off + 2 * R + mb + 4 * n_blocks + 2 * n_reg + 4 * n_ch + 2 * n_words
+    fw = 1 if S >= 8 else 2
+    n_nib = -(-n_ch // 2)
+    need = off + 2 * R + mb + 4 * n_blocks + fw * n_ch + n_nib + 4 * n_ch + 2 * n_words
     if len(buf) != need:
         raise ValueError("blob size mismatch")
     s_bits = np.frombuffer(buf, "<u2", R, off).copy(); off += 2 * R
@@ -218,20 +222,24 @@ def parse_blob(buf: bytes) -> Blob:
         raise ValueError("bad row scale")
     mbytes = bytes(buf[off:off + mb]); off += mb
     model = Model.from_bytes(mbytes, k)
-    ck = np.frombuffer(buf, "<u4", n_blocks, off).copy(); off += 4 * n_blocks
-    rl = np.frombuffer(buf, "<u2", n_reg, off).copy(); off += 2 * n_reg
+    offs = np.frombuffer(buf, "<u4", n_blocks, off).copy(); off += 4 * n_blocks
+    full = np.frombuffer(buf, "<u1" if fw == 1 else "<u2", n_ch, off).astype(np.int64); off += fw * n_ch
+    nib = np.frombuffer(buf, "<u1", n_nib, off).astype(np.int64); off += n_nib
     st = np.frombuffer(buf, "<u4", n_ch, off).copy(); off += 4 * n_ch
     stream = np.frombuffer(buf, "<u2", n_words, off).copy()
-    if (rl & 1).any():
-        raise ValueError("odd region length")
-    starts = np.concatenate([[0], np.cumsum(rl.astype(np.int64))[:-1]])
-    if int(rl.astype(np.int64).sum()) != n_words:
-        raise ValueError("region lengths do not cover the stream")
-    if not np.array_equal(ck.astype(np.int64), starts[np.arange(n_blocks) * (BLOCK_CHAINS // 2)]):
-        raise ValueError("checkpoints inconsistent")
+    tails = np.stack([nib & 15, nib >> 4], axis=1).reshape(-1)[:n_ch]
+    if (tails >= CHUNK).any() or (n_ch % 2 and (nib[-1] >> 4) != 0):
+        raise ValueError("bad tail length")
+    lens = CHUNK * full + tails
+    size = block_geometry(lens, S)[3]
+    if n_words != CHUNK * int(size.sum()):
+        raise ValueError("chain lengths do not cover the stream")
+    if not np.array_equal(offs.astype(np.int64), np.concatenate([[0], np.cumsum(size)[:-1]])):
+        raise ValueError("block offsets inconsistent")
     if (st < L).any():
         raise ValueError("state below L")
-    return Blob(dtype, S, k, flags, R, C, np.float32(delta), n_tiles, s_bits, model, mbytes, ck, rl, st, stream)
+    return Blob(dtype, S, k, flags, R, C, np.float32(delta), n_tiles, s_bits, model, mbytes, offs,
+                lens.astype(np.uint16), st, stream)
 
 
 def reconstruct_f32(u: np.ndarray, h: np.ndarray) -> np.ndarray:
@@ -239,42 +247,96 @@ def reconstruct_f32(u: np.ndarray, h: np.ndarray) -> np.ndarray:
     return (h[:, None] * np.asarray(u).astype(np.float32)).astype(np.float32)
 
 
-def chain_readers(b: Blob):
-    n_ch = b.n_chains
-    rl = b.region_len.astype(np.int64)
-    starts = np.concatenate([[0], np.cumsum(rl)[:-1]])
-    ch = np.arange(n_ch)
-    r = ch // 2
-    fwd = (ch % 2) == 0
-    start = np.where(fwd, starts[r], starts[r] + rl[r] - 1)
-    step = np.where(fwd, 1, -1)
-    lo = starts[r]
-    hi = starts[r] + rl[r]
-    return WordReader(b.stream, start, step, lo, hi)
+class ChunkReader:
+    """Reads every chain's words from its tile area: full chunks where the
+    schedule placed them, the tail from the tile's tails.  A word is readable
+    only once the schedule has fetched its chunk."""
+
+    def __init__(self, b: Blob, sched: TileSchedule):
+        self.b = b
+        self.sched = sched
+        n_ch = b.n_tiles * b.S
+        self.nfull, self.main_start, self.tail_pos, _ = block_geometry(b.chain_lens, b.S)
+        self.base = CHUNK * b.block_offsets.astype(np.int64)[np.arange(n_ch) // BLOCK_CHAINS]
+        self.q = np.zeros(n_ch, dtype=np.int64)
+        self.overrun = np.zeros(n_ch, dtype=bool)
+
+    def _pos(self, c, i, checked):
+        S = self.b.S
+        t, j = c // S, c % S
+        n = i // CHUNK
+        full = n < self.nfull[c]
+        fetched = i < self.sched.F[t, j]
+        rk = self.sched.rank[t, j, np.minimum(n, self.sched.rank.shape[2] - 1)]
+        pos = np.where(full, self.base[c] + self.main_start[c] + CHUNK * rk + i % CHUNK,
+                       self.base[c] + self.tail_pos[c] + i - CHUNK * self.nfull[c])
+        ok = (i < self.b.chain_lens[c]) & (fetched | (not checked)) & ((~full) | (rk >= 0))
+        return np.where(ok, pos, -1), ok
+
+    def _read(self, pos):
+        w = np.zeros(len(pos), dtype=np.uint64)
+        good = pos >= 0
+        w[good] = self.b.stream[pos[good]]
+        return w
+
+    def peek(self, idx, n):
+        pos, _ = self._pos(idx, self.q[idx] + n, checked=False)
+        return self._read(pos)
+
+    def take(self, idx):
+        pos, ok = self._pos(idx, self.q[idx], checked=True)
+        self.overrun[idx[~ok]] = True
+        self.q[idx] += 1
+        return self._read(pos)
 
 
 def decode(buf, tiles=None):
     """Decode a blob.  Returns (u int32 (R, C) doubled coordinates, container array (R, C), info).
 
     ``tiles`` restricts decoding to an iterable of tile indices (other
-    outputs stay zero): the tile-independence property.
+    outputs stay zero): the tile-independence property.  Each tile runs the
+    request schedule of ``layout`` while it decodes, group by group.
     """
     b = parse_blob(buf) if not isinstance(buf, Blob) else buf
     R, C = b.R, b.C
     G = -(-C // 8)
     n_groups = R * G
     n_tiles, cg = chain_layout(n_groups, b.S)
-    reader = chain_readers(b)
+    S = b.S
+    ngr = chain_group_counts(n_groups, S, n_tiles)
     if tiles is not None:
         keep = np.zeros(n_tiles, dtype=bool)
         keep[np.asarray(list(tiles), dtype=np.int64)] = True
-        chain_keep = np.repeat(keep, b.S)
-        cg = np.where(chain_keep[:, None], cg, -1)
-    u, xend = decode_chains(b.model, b.states, cg, reader, n_groups)
-    active = (cg >= 0).any(axis=1)
-    ok_state = bool((xend[active] == L).all())
+    else:
+        keep = np.ones(n_tiles, dtype=bool)
+    ngr = np.where(keep[:, None], ngr, 0)
+    lens = np.where(keep[:, None], b.chain_lens.astype(np.int64).reshape(n_tiles, S), 0)
+    sched = TileSchedule(lens, ngr)
+    reader = ChunkReader(b, sched)
+    dec = ChainDecoder(b.model, b.states, n_groups)
+    sched.prime()
+    for g in range(cg.shape[1]):
+        act = (g < ngr).reshape(-1)
+        if g % 2 == 0:
+            sched.service(g)
+        idx = np.nonzero(act)[0]
+        if idx.size == 0:
+            continue
+        slow = np.zeros(n_tiles * S, dtype=bool)
+        if b.flags & FLAG_ESC:
+            slow[idx] = dec.escapes_ahead(idx, reader.peek)
+        sl = slow.reshape(n_tiles, S)
+        if sl.any():
+            sched.before_escapes(sl)
+        q0 = reader.q.copy()
+        dec.decode_group(idx, cg[idx, g], reader)
+        sched.consume(act.reshape(n_tiles, S), (reader.q - q0).reshape(n_tiles, S))
+        if sl.any():
+            sched.after_escapes(sl)
+    active = keep.repeat(S) & (ngr.reshape(-1) > 0)
+    ok_state = bool((dec.x[active] == L).all())
     ok_reads = not bool(reader.overrun.any())
-    u = u.reshape(R, G * 8)[:, :C]
+    u = dec.u.reshape(R, G * 8)[:, :C]
     h = half_steps(b.s_bits, b.delta)
     wh = reconstruct_f32(u, h)
     out = nx.cast_container(wh, b.dtype)

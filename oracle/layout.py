@@ -1,0 +1,171 @@
+"""Stream layout of blob v2: where every chain's words sit (oracle).
+
+[ABS] / [SUM] say only that the coordinates are rANS-coded in independently
+decodable tiles.  How the words sit in memory is this project's format,
+chosen so that a GPU wave fetches them with contiguous loads:
+
+* every chain's words (decoding order) are cut into chunks of 8 words; a
+  chain has nfull = len // 8 full chunks and a tail of len % 8 words;
+* a block (64 consecutive chains) stores [the main area of each of its tiles,
+  in tile order] [the tails of its chains, chain order, word after word]
+  [zeros up to a multiple of 8 words]; blocks follow each other;
+* a tile's main area holds its chains' full chunks in request order: the
+  order in which the reference reader below asks for them.  Chains take their
+  turn in chain order within a site; a sync site repeats rounds until no chain
+  wants more:
+
+      prime                      sync until ahead >= 17
+      group g (g even)           sync until ahead >= 17, then one round in which
+                                 a chain asks if ahead <= 24
+      group g holding an escape  that chain: sync until ahead >= 24 before the
+                                 group's words are consumed, sync until
+                                 ahead >= 17 after
+
+  where ahead = words fetched - words consumed (the tail counts as one
+  request).  A chain asks only while it has unfetched words and only at groups
+  it decodes (g < its group count).
+
+Why these numbers: a group consumes at most 8 words without escapes (one per
+symbol) and at most 24 with them (two more per escape for up to 28 raw bits),
+so every group's words are fetched before they are read; a chain never holds
+more than 32 words ahead (the reader's ring).
+
+Pins (tests): hand-worked schedules for small consumption patterns; every
+word fetched before it is read on random patterns; encoder/decoder round trips.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+CHUNK = 8            # words per chunk
+BLOCK = 64           # chains per block
+RING = 32            # words a chain may hold ahead
+AHEAD_GROUP = 17     # two escape-free groups consume <= 16
+AHEAD_ESC = 24       # one group with escapes consumes <= 24
+ASYNC_MAX = RING - CHUNK
+
+
+class TileSchedule:
+    """The reference reader for all tiles at once (arrays shaped (n_tiles, S)).
+
+    ``rank[t, j, n]`` receives the position (in chunks from the tile's start) of
+    chain j's full chunk n, in the order requested.
+    """
+
+    def __init__(self, lens: np.ndarray, ngr: np.ndarray):
+        self.n = np.asarray(lens, dtype=np.int64)
+        self.ngr = np.asarray(ngr, dtype=np.int64)
+        T, S = self.n.shape
+        self.F = np.zeros((T, S), dtype=np.int64)
+        self.q = np.zeros((T, S), dtype=np.int64)
+        self.ctr = np.zeros(T, dtype=np.int64)
+        nfull = int((self.n // CHUNK).max()) if self.n.size else 0
+        self.rank = np.full((T, S, max(nfull, 1)), -1, dtype=np.int64)
+
+    def _round(self, want):
+        """One round: every wanting chain takes its next chunk, in chain order."""
+        full = want & (self.n - self.F >= CHUNK)
+        order = np.cumsum(full, axis=1) - 1
+        t_idx, j_idx = np.nonzero(full)
+        self.rank[t_idx, j_idx, self.F[t_idx, j_idx] // CHUNK] = self.ctr[t_idx] + order[t_idx, j_idx]
+        self.ctr += full.sum(axis=1)
+        self.F = np.where(full, self.F + CHUNK, np.where(want, self.n, self.F))
+
+    def _sync(self, cand, ahead):
+        while True:
+            want = cand & (self.F - self.q < ahead) & (self.F < self.n)
+            if not want.any():
+                return
+            self._round(want)
+
+    def prime(self):
+        self._sync(np.ones_like(self.n, dtype=bool), AHEAD_GROUP)
+
+    def service(self, g: int):
+        act = g < self.ngr
+        self._sync(act, AHEAD_GROUP)
+        self._round(act & (self.F - self.q <= ASYNC_MAX) & (self.F < self.n))
+
+    def before_escapes(self, slow):
+        self._sync(slow, AHEAD_ESC)
+
+    def consume(self, act, words):
+        self.q = np.where(act, self.q + words, self.q)
+
+    def after_escapes(self, slow):
+        self._sync(slow, AHEAD_GROUP)
+
+
+def request_ranks(lens, ngr, cons, slow):
+    """Run the whole schedule for known per-group consumption.
+
+    lens, ngr: (T, S); cons, slow: (T, S, steps) words consumed by / escape in
+    each chain's group g.  Returns rank (T, S, max full chunks).
+    """
+    sch = TileSchedule(lens, ngr)
+    sch.prime()
+    steps = cons.shape[2]
+    for g in range(steps):
+        act = g < sch.ngr
+        if g % 2 == 0:
+            sch.service(g)
+        sl = act & slow[:, :, g]
+        if sl.any():
+            sch.before_escapes(sl)
+        sch.consume(act, cons[:, :, g])
+        if sl.any():
+            sch.after_escapes(sl)
+        assert (sch.q <= sch.F).all(), "a word was consumed before it was fetched"
+    assert (sch.F == sch.n).all()
+    return sch.rank
+
+
+def block_geometry(lens, S: int):
+    """Word positions of every chain's pieces, relative to its block's start.
+
+    lens: (n_chains,).  Returns (nfull, main_start, tail_pos, block_chunks):
+    main_start = start of the chain's tile main area, tail_pos = start of its
+    tail, both in words from the block start; block_chunks = size of each block
+    in chunks.
+    """
+    lens = np.asarray(lens, dtype=np.int64)
+    n_ch = len(lens)
+    nfull = lens // CHUNK
+    tail = lens % CHUNK
+    nb = -(-n_ch // BLOCK)
+    main_start = np.zeros(n_ch, dtype=np.int64)
+    tail_pos = np.zeros(n_ch, dtype=np.int64)
+    block_chunks = np.zeros(nb, dtype=np.int64)
+    for b in range(nb):
+        c0, c1 = BLOCK * b, min(BLOCK * (b + 1), n_ch)
+        tiles_main = CHUNK * nfull[c0:c1].reshape(-1, S).sum(axis=1)
+        tstart = np.concatenate([[0], np.cumsum(tiles_main)[:-1]])
+        main_start[c0:c1] = np.repeat(tstart, S)
+        tails0 = int(tiles_main.sum())
+        tail_pos[c0:c1] = tails0 + np.cumsum(tail[c0:c1]) - tail[c0:c1]
+        block_chunks[b] = -(-(tails0 + int(tail[c0:c1].sum())) // CHUNK)
+    return nfull, main_start, tail_pos, block_chunks
+
+
+def build_stream(words, lens, rank, S: int):
+    """Block areas from per-chain word arrays and the request ranks.
+
+    rank: (n_tiles, S, max full chunks) from the schedule.  Returns
+    (block offsets u32 in chunks, stream u16).
+    """
+    lens = np.asarray(lens, dtype=np.int64)
+    nfull, main_start, tail_pos, block_chunks = block_geometry(lens, S)
+    offsets = np.concatenate([[0], np.cumsum(block_chunks)[:-1]]).astype(np.int64)
+    stream = np.zeros(CHUNK * int(block_chunks.sum()), dtype=np.uint16)
+    for c in range(len(lens)):
+        base = CHUNK * offsets[c // BLOCK]
+        w = words[c]
+        t, j = c // S, c % S
+        for nn in range(nfull[c]):
+            p = base + main_start[c] + CHUNK * rank[t, j, nn]
+            stream[p:p + CHUNK] = w[CHUNK * nn:CHUNK * nn + CHUNK]
+        r = lens[c] % CHUNK
+        if r:
+            p = base + tail_pos[c]
+            stream[p:p + r] = w[CHUNK * nfull[c]:]
+    return offsets.astype(np.uint32), stream

@@ -50,20 +50,25 @@ def encode_chains(sym, model: Model, chain_groups):
 
     ``chain_groups`` is an (n_chains, steps) int64 array of global group
     indices in decoding order, -1 where a chain has no more groups.
-    Returns (states uint32[n_chains], list of uint16 word arrays in decoding order).
+    Returns (states uint32[n_chains], list of uint16 word arrays in decoding
+    order, words (n_chains, steps): how many words the decoder reads while
+    decoding each step's group -- the words emitted while encoding it).
     """
     n_ch, steps = chain_groups.shape
     x = np.full(n_ch, L, dtype=np.uint64)
     cap = steps * 8 * OPS_PER_COORD + 1
     buf = np.zeros((n_ch, cap), dtype=np.uint64)
     cnt = np.zeros(n_ch, dtype=np.int64)
+    per_step = np.zeros((n_ch, steps), dtype=np.int64)
     F, CUM = model.F, model.CUM
+    cur = [0]
 
     def emit(idx, mask):
         if mask.any():
             sel = idx[mask]
             buf[sel, cnt[sel]] = x[sel] & 0xFFFF
             cnt[sel] += 1
+            per_step[sel, cur[0]] += 1
             x[sel] >>= np.uint64(16)
 
     def bypass(idx, b, v):
@@ -81,6 +86,7 @@ def encode_chains(sym, model: Model, chain_groups):
         idx = np.nonzero(g >= 0)[0]
         if idx.size == 0:
             continue
+        cur[0] = s
         gg = g[idx]
         for i in range(7, -1, -1):
             ctx, ids, lo_b, lo_v, hi_b, hi_v = _ops_for_group(sym, gg, i)
@@ -95,62 +101,108 @@ def encode_chains(sym, model: Model, chain_groups):
     states = x.astype(np.uint32)
     assert (x < (1 << 32)).all() and (x >= L).all()
     words = [buf[c, :cnt[c]][::-1].astype(np.uint16) for c in range(n_ch)]
-    return states, words
+    return states, words, per_step
 
 
 class WordReader:
-    """Per-chain word cursors into the blob stream (forward or backward)."""
+    """Per-chain word cursors over chain-contiguous word arrays (the coder's own
+    tests; the blob layout has its own reader in ``codec``)."""
 
-    def __init__(self, stream: np.ndarray, start: np.ndarray, step: np.ndarray, lo: np.ndarray, hi: np.ndarray):
-        self.stream = stream
-        self.ptr = start.astype(np.int64).copy()
-        self.step = step.astype(np.int64)
-        self.lo, self.hi = lo, hi     # allowed [lo, hi) per chain
-        self.overrun = np.zeros(len(start), dtype=bool)
+    def __init__(self, words):
+        self.words = [np.asarray(w, dtype=np.uint16) for w in words]
+        self.q = np.zeros(len(words), dtype=np.int64)
+        self.overrun = np.zeros(len(words), dtype=bool)
+
+    def word_at(self, c: int, i: int) -> int:
+        w = self.words[c]
+        return int(w[i]) if 0 <= i < len(w) else -1
 
     def take(self, idx):
-        p = self.ptr[idx]
-        bad = (p < self.lo[idx]) | (p >= self.hi[idx])
-        self.overrun[idx[bad]] = True
-        pc = np.clip(p, 0, max(len(self.stream) - 1, 0))
-        w = self.stream[pc].astype(np.uint64) if len(self.stream) else np.zeros(len(idx), np.uint64)
-        w[bad] = 0
-        self.ptr[idx] = p + self.step[idx]
-        return w
+        out = np.zeros(len(idx), dtype=np.uint64)
+        for n, c in enumerate(idx):
+            v = self.word_at(c, self.q[c])
+            if v < 0:
+                self.overrun[c] = True
+                v = 0
+            out[n] = v
+            self.q[c] += 1
+        return out
 
 
-def decode_chains(model: Model, states, chain_groups, reader: WordReader, n_groups: int):
-    """Decode chains; returns (u int64 (n_groups, 8) filled at decoded groups, final x)."""
-    k = model.k
-    K = 1 << k
-    n_ch, steps = chain_groups.shape
-    x = np.asarray(states, dtype=np.uint64).copy()
-    u_out = np.zeros((n_groups, 8), dtype=np.int64)
-    F, CUM, S2I = model.F, model.CUM, model.SLOT2ID
+class ChainDecoder:
+    """Decodes chains group by group (all chains of a step together)."""
 
-    def renorm(idx):
-        low = x[idx] < L
-        if low.any():
-            sel = idx[low]
-            w = reader.take(sel)
-            x[sel] = (x[sel] << np.uint64(16)) | w
+    def __init__(self, model: Model, states, n_groups: int):
+        self.model = model
+        self.k = model.k
+        self.K = 1 << model.k
+        self.x = np.asarray(states, dtype=np.uint64).copy()
+        self.u = np.zeros((n_groups, 8), dtype=np.int64)
 
-    def bypass(idx, b):
-        r = np.zeros(len(idx), dtype=np.int64)
-        act = b > 0
-        if act.any():
-            sel = idx[act]
-            bb = b[act].astype(np.uint64)
-            r[act] = (x[sel] & ((np.uint64(1) << bb) - np.uint64(1))).astype(np.int64)
-            x[sel] = x[sel] >> bb
-            renorm(sel)
-        return r
+    def _symbol(self, x, ctx):
+        """One table step: returns (new x before renormalisation, symbol id)."""
+        F, CUM, S2I = self.model.F, self.model.CUM, self.model.SLOT2ID
+        slot = (x & np.uint64(M - 1)).astype(np.int64)
+        ids = S2I[ctx, slot]
+        f = F[ctx, ids].astype(np.uint64)
+        cum = CUM[ctx, ids].astype(np.uint64)
+        return f * (x >> np.uint64(P)) + slot.astype(np.uint64) - cum, ids
 
-    for s in range(steps):
-        g = chain_groups[:, s]
-        idx = np.nonzero(g >= 0)[0]
-        if idx.size == 0:
-            continue
+    def escapes_ahead(self, idx, peek):
+        """Whether each chain's next group holds a bucket (escape) symbol.
+
+        Decodes the group's symbols on a copy of the state without reading raw
+        bits: up to the first escape this is the true decode, so the first
+        escape is always seen; what follows it does not matter.  ``peek(idx, n)``
+        returns the n-th next word of each chain without consuming it.
+        """
+        x = self.x[idx].copy()
+        used = np.zeros(len(idx), dtype=np.int64)
+        c = np.zeros(len(idx), dtype=np.int64)
+        pi = np.zeros(len(idx), dtype=np.int64)
+        esc = np.zeros(len(idx), dtype=bool)
+        for i in range(8):
+            ctx = np.zeros(len(idx), np.int64) if i == 0 else (1 + c if i < 7 else 3 + 2 * c + pi)
+            x, ids = self._symbol(x, ctx)
+            low = x < L
+            if low.any():
+                w = peek(idx[low], used[low])
+                x[low] = (x[low] << np.uint64(16)) | w
+                used[low] += 1
+            if i == 0:
+                c = ids >> 9
+                sid = ids & 511
+            else:
+                sid = ids
+            msym = sid >> 1
+            esc |= msym >= self.K
+            if i < 7:
+                pi = pi ^ np.mod(msym + np.where(c == 0, 0, sid & 1), 2)
+        return esc
+
+    def decode_group(self, idx, groups, reader):
+        """Decode the next group of chains ``idx`` (global group ids ``groups``)."""
+        k, K = self.k, self.K
+        x = self.x
+
+        def renorm(sel):
+            low = x[sel] < L
+            if low.any():
+                s2 = sel[low]
+                w = reader.take(s2)
+                x[s2] = (x[s2] << np.uint64(16)) | w
+
+        def bypass(b):
+            r = np.zeros(len(idx), dtype=np.int64)
+            act = b > 0
+            if act.any():
+                sel = idx[act]
+                bb = b[act].astype(np.uint64)
+                r[act] = (x[sel] & ((np.uint64(1) << bb) - np.uint64(1))).astype(np.int64)
+                x[sel] = x[sel] >> bb
+                renorm(sel)
+            return r
+
         c = np.zeros(len(idx), dtype=np.int64)
         pi = np.zeros(len(idx), dtype=np.int64)
         urow = np.zeros((len(idx), 8), dtype=np.int64)
@@ -161,11 +213,7 @@ def decode_chains(model: Model, states, chain_groups, reader: WordReader, n_grou
                 ctx = 1 + c
             else:
                 ctx = 3 + 2 * c + pi
-            slot = (x[idx] & np.uint64(M - 1)).astype(np.int64)
-            ids = S2I[ctx, slot]
-            f = F[ctx, ids].astype(np.uint64)
-            cum = CUM[ctx, ids].astype(np.uint64)
-            x[idx] = f * (x[idx] >> np.uint64(P)) + slot.astype(np.uint64) - cum
+            x[idx], ids = self._symbol(x[idx], ctx)
             renorm(idx)
             if i == 0:
                 c = ids >> 9
@@ -178,8 +226,8 @@ def decode_chains(model: Model, states, chain_groups, reader: WordReader, n_grou
             e = k + (msym - K) // 4
             top2 = (msym - K) % 4
             nb = np.where(big, e - 2 - (1 if i == 7 else 0), 0)
-            lo = bypass(idx, np.minimum(nb, 16))
-            hi = bypass(idx, np.maximum(nb - 16, 0))
+            lo = bypass(np.minimum(nb, 16))
+            hi = bypass(np.maximum(nb - 16, 0))
             raw = lo | (hi << 16)
             if i == 7:
                 rho = np.where(c == 0, pi, pi ^ neg)
@@ -189,8 +237,18 @@ def decode_chains(model: Model, states, chain_groups, reader: WordReader, n_grou
             urow[:, i] = u
             if i < 7:
                 pi = pi ^ np.mod(u >> 1, 2)
-        u_out[g[idx]] = urow
-    return u_out, x
+        self.u[groups] = urow
+
+
+def decode_chains(model: Model, states, chain_groups, reader, n_groups: int):
+    """Decode chain-contiguous words; returns (u int64 (n_groups, 8), final x)."""
+    dec = ChainDecoder(model, states, n_groups)
+    for s in range(chain_groups.shape[1]):
+        g = chain_groups[:, s]
+        idx = np.nonzero(g >= 0)[0]
+        if idx.size:
+            dec.decode_group(idx, g[idx], reader)
+    return dec.u, dec.x
 
 
 def ideal_bits(sym, model: Model) -> float:

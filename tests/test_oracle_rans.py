@@ -5,7 +5,7 @@ import pytest
 
 from oracle import model as mdl
 from oracle import rans
-from oracle.codec import chain_layout, _layout_regions, Blob, chain_readers
+from oracle.codec import chain_layout
 from oracle.e8 import e8_nearest_doubled
 
 
@@ -32,15 +32,19 @@ def test_round_trip(S, n_groups, scale, k, heavy):
     sym = mdl.group_symbols(u, k)
     model = mdl.build_model(k, *mdl.count_symbols(sym, mdl.n_msym(k)))
     n_tiles, cg = chain_layout(n_groups, S)
-    states, words = rans.encode_chains(sym, model, cg)
-    rl, stream, ck = _layout_regions(words, n_tiles * S)
-    b = Blob(1, S, k, 0, 1, 8 * n_groups, np.float32(1), n_tiles, np.zeros(1, np.uint16), model,
-             model.to_bytes(), ck, rl, states, stream)
-    reader = chain_readers(b)
+    states, words, per_group = rans.encode_chains(sym, model, cg)
+    reader = rans.WordReader(words)
     u2, xend = rans.decode_chains(model, states, cg, reader, n_groups)
     assert np.array_equal(u2, u)
     assert (xend == rans.L).all()
     assert not reader.overrun.any()
+    # every word read, and the per-group counts add up to each chain's length
+    assert np.array_equal(reader.q, [len(w) for w in words])
+    assert np.array_equal(per_group.sum(axis=1), [len(w) for w in words])
+    # a group reads at most one word per symbol plus two per escape (raw bits <= 28)
+    esc = (sym["msym"] >= (1 << k)).any(axis=1)
+    g_esc = np.where(cg >= 0, esc[np.maximum(cg, 0)], False)
+    assert (per_group[~g_esc] <= 8).all() and (per_group <= 24).all()
     # code length: 16 W bits within the ideal plus a per-symbol slack of 0.06 bit
     # and one 16-bit flush per chain (the final state carries the rest)
     n_ops = sym["ctx"].size + int((sym["rawbits"] > 0).sum()) + int((sym["rawbits"] > 16).sum())
@@ -54,7 +58,7 @@ def test_state_range_and_word_counts():
     sym = mdl.group_symbols(u, k)
     model = mdl.build_model(k, *mdl.count_symbols(sym, mdl.n_msym(k)))
     _, cg = chain_layout(4096, 8)
-    states, words = rans.encode_chains(sym, model, cg)
+    states, words, _ = rans.encode_chains(sym, model, cg)
     assert (states >= rans.L).all()
     # on typical data the coder loses well under 0.01 bit per symbol
     n_sym = sym["ctx"].size
