@@ -180,12 +180,14 @@ constexpr int kRingWords = 32;                   // per-chain LDS ring (16-bit w
 constexpr int kChunkWords = 8;                   // one 16-byte stream load
 constexpr int kChainRingBytes = kRingWords * 2;  // 64 B per chain
 constexpr int kMaxWaves = 16;
+constexpr int kHrPad = 128;                      // zero row scales after the last row (prefetch slack)
 static_assert(kRingWords - kChunkWords >= 17, "ring too small for two groups plus a chunk");
 
 // Job descriptors travel by value in the kernel arguments (no per-launch copy).
 struct DecBatch {
   DecJob j[kMaxBatch];
   int n;
+  int64_t bpw;   // blocks per workgroup
 };
 
 // Entry layouts (chosen per blob when its tables are expanded):
@@ -228,9 +230,9 @@ struct EntryLayout {
 // order its chains request them (positions handed out by a ballot in chain order, the
 // tile's cursor advancing by 8 words per chunk), then every chain's last short piece
 // (tail).  Each chain keeps its words in a 32-word LDS ring: word i at ring byte
-// 2 (i mod 32), so chunk n fills ring bytes 16 (n mod 4) .. +15.  F = words fetched
-// (a chunk in flight included), q = words consumed (a2 = 2q).  Fetches happen only
-// at these sites, exactly as the encoder's schedule assumed:
+// 2 (i mod 32), so chunk n fills ring bytes 16 (n mod 4) .. +15.  Counters are kept in
+// bytes (2 per word): fb = fetched (a chunk in flight included), a2 = consumed.
+// Fetches happen only at these sites, exactly as the encoder's schedule assumed:
 //   prime: until 17 ahead;  every even group: until 17 ahead, then one round for
 //   chains at most 24 ahead (a 16-byte load issued now, written to the ring two groups
 //   later);  a group with an escape (that chain): until 24 ahead before its careful
@@ -242,14 +244,14 @@ struct Chain {
   uint32_t a2;       // 2 x words consumed
   uint32_t nw;       // the next word, already read from the ring
   uint32_t rb;       // LDS byte address of the ring (64-byte aligned)
-  int32_t F;         // words fetched
-  int32_t N;         // chain length in words
+  uint32_t fb;       // 2 x words fetched
+  int32_t rem;       // words not fetched yet
   uint32_t cur;      // the tile's main-area cursor (word index; equal on the tile's lanes)
   uint32_t tailp;    // word index of the chain's tail
   uint32_t seg_lo;   // lanes of the chain's tile (ballot mask)
   uint32_t seg_hi;
   uint4 pend;        // chunk in flight
-  int32_t pend_F;    // its first word
+  uint32_t pend_at;  // its ring address
   bool have_pend;
 };
 
@@ -259,20 +261,28 @@ struct StreamRef {
                          // length (the allocation has 256 bytes of slack after it)
 };
 
-__device__ __forceinline__ int32_t ch_q(const Chain& r) { return (int32_t)(r.a2 >> 1); }
-__device__ __forceinline__ void ch_put(uint8_t* lds8, const Chain& r, int32_t first_word, uint4 d) {
-  *(uint4*)(lds8 + r.rb + ((((uint32_t)first_word >> 3) & 3u) << 4)) = d;
+// three-input xor in one instruction (gfx950 v_bitop3, truth table 0x96)
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
 }
-__device__ __forceinline__ void ch_flush(uint8_t* lds8, Chain& r) {
-  if (r.have_pend) {
-    ch_put(lds8, r, r.pend_F, r.pend);
-    r.have_pend = false;
-  }
+
+// LDS is addressed with plain 32-bit local addresses (ring and table bases include the
+// dynamic LDS base), so a ring address is one and-or and a table address one shift-add.
+#define EP_LDS __attribute__((address_space(3)))
+__device__ __forceinline__ uint32_t lds_u16(uint32_t a) { return *(const EP_LDS uint16_t*)(uintptr_t)a; }
+__device__ __forceinline__ void lds_st128(uint32_t a, uint4 d) {
+  const u32x4 v = {d.x, d.y, d.z, d.w};
+  *(EP_LDS u32x4*)(uintptr_t)a = v;
 }
+
+__device__ __forceinline__ uint32_t ch_word(const Chain& r) { return lds_u16((r.a2 & 62u) | r.rb); }
+__device__ __forceinline__ void ch_put(const Chain& r, uint4 d) { lds_st128((r.fb & 48u) | r.rb, d); }
 // Positions for one round of requests: full chunks take the tile's next main-area
 // slots in lane (= chain) order, a tail sits at its own place.
 __device__ __forceinline__ uint32_t ch_claim(Chain& r, bool want, bool& full) {
-  full = want && (r.N - r.F >= kChunkWords);
+  full = want && r.rem >= kChunkWords;
   const uint64_t m = __ballot(full);
   const uint32_t mlo = (uint32_t)m & r.seg_lo, mhi = (uint32_t)(m >> 32) & r.seg_hi;
   const uint32_t rank = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
@@ -292,56 +302,64 @@ __device__ __forceinline__ uint4 ld_tail(const StreamRef& s, uint32_t pos) {
   d.w = (uint32_t)p[6] | ((uint32_t)p[7] << 16);
   return d;
 }
-// Sync site: rounds until no lane of the wave wants more (every active lane calls it).
-__device__ __forceinline__ void ch_sync(uint8_t* lds8, const StreamRef& s, Chain& r, bool cand, int32_t ahead) {
+// Sync site: rounds until no lane of the wave wants more (every active lane calls it);
+// ahead2 = the target in bytes.
+__device__ __forceinline__ void ch_sync(const StreamRef& s, Chain& r, bool cand, int32_t ahead2) {
   for (;;) {
-    const bool want = cand && r.F - ch_q(r) < ahead && r.F < r.N;
+    const bool want = cand && (int32_t)(r.fb - r.a2) < ahead2 && r.rem > 0;
     if (__ballot(want) == 0) return;
     bool full;
     const uint32_t pos = ch_claim(r, want, full);
     if (want) {
-      ch_put(lds8, r, r.F, full ? ld_chunk(s, pos) : ld_tail(s, pos));
-      r.F = full ? r.F + kChunkWords : r.N;
+      ch_put(r, full ? ld_chunk(s, pos) : ld_tail(s, pos));
+      const int32_t n = full ? kChunkWords : r.rem;
+      r.fb += 2u * (uint32_t)n;
+      r.rem -= n;
     }
   }
+}
+__device__ __forceinline__ void ch_flush(Chain& r) {
+  if (r.have_pend) lds_st128(r.pend_at, r.pend);
+  r.have_pend = false;
 }
 // Service at every even group: write the chunk in flight, top up to 17 ahead, then one
 // round for chains at most 24 ahead.  Full chunks load asynchronously with a fixed
 // pattern (one 16-byte load per lane; lanes without a chunk read the stream's first
 // one, a line every lane shares); tails, rare, are fetched at once.
-__device__ __forceinline__ void ch_service(uint8_t* lds8, const StreamRef& s, Chain& r, bool act) {
-  ch_flush(lds8, r);
-  ch_sync(lds8, s, r, act, 17);
-  const bool want = act && r.F - ch_q(r) <= kRingWords - kChunkWords && r.F < r.N;
+__device__ __forceinline__ void ch_service(const StreamRef& s, Chain& r, bool act) {
+  ch_flush(r);
+  ch_sync(s, r, act, 2 * 17);
+  const bool want = act && (int32_t)(r.fb - r.a2) <= 2 * (kRingWords - kChunkWords) && r.rem > 0;
   bool full;
   const uint32_t pos = ch_claim(r, want, full);
   const bool tail = want && !full;
   if (__ballot(tail) != 0) {
     if (tail) {
-      ch_put(lds8, r, r.F, ld_tail(s, pos));
-      r.F = r.N;
+      ch_put(r, ld_tail(s, pos));
+      r.fb += 2u * (uint32_t)r.rem;
+      r.rem = 0;
     }
   }
-  r.pend_F = r.F;
+  r.pend_at = (r.fb & 48u) | r.rb;
   r.pend = ld_chunk(s, full ? pos : 0u);
-  if (full) r.F += kChunkWords;
+  if (full) {
+    r.fb += 2u * kChunkWords;
+    r.rem -= kChunkWords;
+  }
   r.have_pend = full;
 }
-__device__ __forceinline__ uint32_t ch_word(const uint8_t* lds8, const Chain& r) {
-  return *(const uint16_t*)(lds8 + (r.rb | (r.a2 & 62u)));
-}
-__device__ __forceinline__ void ch_renorm_if(const uint8_t* lds8, Chain& r, bool need) {
+__device__ __forceinline__ void ch_renorm_if(Chain& r, bool need) {
   if (need) {
     r.x = (r.x << 16) | r.nw;
     r.a2 += 2u;
-    r.nw = ch_word(lds8, r);
+    r.nw = ch_word(r);
   }
 }
-__device__ __forceinline__ void ch_renorm(const uint8_t* lds8, Chain& r) { ch_renorm_if(lds8, r, r.x < kL); }
+__device__ __forceinline__ void ch_renorm(Chain& r) { ch_renorm_if(r, r.x < kL); }
 // Renormalise ILP chains: all conditions first, so that no chain's state update is
 // sunk below another chain's (conditional) ring read.
 template <int ILP>
-__device__ __forceinline__ void ch_renorm_all(const uint8_t* lds8, Chain* rd) {
+__device__ __forceinline__ void ch_renorm_all(Chain* rd) {
   bool need[ILP];
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
@@ -350,110 +368,247 @@ __device__ __forceinline__ void ch_renorm_all(const uint8_t* lds8, Chain* rd) {
     need[c] = rd[c].x < kL;
   }
 #pragma unroll
-  for (int c = 0; c < ILP; ++c) ch_renorm_if(lds8, rd[c], need[c]);
+  for (int c = 0; c < ILP; ++c) ch_renorm_if(rd[c], need[c]);
 }
-// table read of one symbol step (issued before the other chain's step finishes)
-__device__ __forceinline__ uint32_t ch_entry(const uint32_t* tb, const Chain& r) { return tb[r.x & (kM - 1)]; }
+// table entry of the chain's next symbol; `base` = byte offset of the table in LDS
+__device__ __forceinline__ uint32_t ch_entry(uint32_t base, const Chain& r) {
+  return ((const EP_LDS uint32_t*)(uintptr_t)base)[r.x & (kM - 1)];
+}
 // x = f (x >> P) + (slot - cum)
 __device__ __forceinline__ void ch_decode(Chain& r, uint32_t e) {
   r.x = __umul24(e & 2047u, r.x >> 11) + ((e >> 11) & 2047u);
 }
-__device__ __forceinline__ void ch_advance(const uint8_t* lds8, Chain& r, uint32_t e) {
+__device__ __forceinline__ void ch_advance(Chain& r, uint32_t e) {
   ch_decode(r, e);
-  ch_renorm(lds8, r);
+  ch_renorm(r);
 }
-__device__ __forceinline__ uint32_t ch_bypass(const uint8_t* lds8, Chain& r, int nb) {
+__device__ __forceinline__ uint32_t ch_bypass(Chain& r, int nb) {
   const uint32_t v = r.x & ((1u << nb) - 1u);
   r.x >>= nb;
-  ch_renorm(lds8, r);
+  ch_renorm(r);
   return v;
 }
 // escape symbol: raw bits follow; returns the doubled coordinate
 template <class LY>
-__device__ __forceinline__ int32_t ch_escape(const uint8_t* lds8, Chain& r, uint32_t e, int k, int last, int pi) {
+__device__ __forceinline__ int32_t ch_escape(Chain& r, uint32_t e, int k, int last, int pi) {
   int c, neg, top2, er;
   LY::esc_info(e, c, neg, top2, er);
   const int ex = k + er;
   const int nb = ex - 2 - last;
-  uint32_t raw = ch_bypass(lds8, r, nb < 16 ? nb : 16);
-  if (nb > 16) raw |= ch_bypass(lds8, r, nb - 16) << 16;
+  uint32_t raw = ch_bypass(r, nb < 16 ? nb : 16);
+  if (nb > 16) raw |= ch_bypass(r, nb - 16) << 16;
   if (last) raw = (raw << 1) | (uint32_t)(c == 0 ? pi : (pi ^ neg));
   const uint32_t m = (1u << ex) | ((uint32_t)top2 << (ex - 2)) | raw;
   const int32_t uu = (int32_t)(2u * m + (uint32_t)c);
   return neg ? -uu : uu;
 }
+// Byte offsets of the tables in LDS: FIRST at 0, FREE[c] at (1 + c) 8 KB, LAST[c][pi]
+// at (3 + 2c + pi) 8 KB.  The coset of a FIRST entry is bit 22 of every layout.
+__device__ __forceinline__ uint32_t free_base(uint32_t e_first) { return ((e_first >> 9) & 0x2000u) + 0x2000u; }
 // careful decode of one group (the chain's state is at the group's start and 24 words
 // are in its ring): FIRST, six FREE, LAST, escapes with their raw bits
 template <class LY>
-__device__ __forceinline__ void ch_group_careful(const uint32_t* smem, const uint8_t* lds8, Chain& r, int k,
-                                                 int32_t* u) {
-  uint32_t ee = ch_entry(smem, r);
-  ch_advance(lds8, r, ee);
-  const int cc = (int)((ee >> 22) & 1u);
-  u[0] = (ee & LY::kEsc) ? ch_escape<LY>(lds8, r, ee, k, 0, 0) : LY::u_of(ee);
+__device__ __forceinline__ void ch_group_careful(uint32_t lds0, Chain& r, int k, int32_t* u) {
+  uint32_t ee = ch_entry(lds0, r);
+  ch_advance(r, ee);
+  const uint32_t fb = free_base(ee);
+  u[0] = (ee & LY::kEsc) ? ch_escape<LY>(r, ee, k, 0, 0) : LY::u_of(ee);
   int pp = u[0] >> 1;
-  const uint32_t* tf = smem + ((1 + cc) << 11);
   for (int i = 1; i < 7; ++i) {
-    ee = ch_entry(tf, r);
-    ch_advance(lds8, r, ee);
-    u[i] = (ee & LY::kEsc) ? ch_escape<LY>(lds8, r, ee, k, 0, 0) : LY::u_of(ee);
+    ee = ch_entry(lds0 + fb, r);
+    ch_advance(r, ee);
+    u[i] = (ee & LY::kEsc) ? ch_escape<LY>(r, ee, k, 0, 0) : LY::u_of(ee);
     pp ^= u[i] >> 1;
   }
   const int pi = pp & 1;
-  ee = ch_entry(smem + ((3 + 2 * cc + pi) << 11), r);
-  ch_advance(lds8, r, ee);
-  u[7] = (ee & LY::kEsc) ? ch_escape<LY>(lds8, r, ee, k, 1, pi) : LY::u_of(ee);
+  ee = ch_entry(lds0 + 2u * fb + 0x2000u + ((uint32_t)pi << 13), r);
+  ch_advance(r, ee);
+  u[7] = (ee & LY::kEsc) ? ch_escape<LY>(r, ee, k, 1, pi) : LY::u_of(ee);
 }
 
-// One wave decodes ILP blocks of 64 chains: lane l runs chain l of each, the ILP chains
-// interleaved step by step so that one chain's table read is in flight while another
-// computes.
-template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
-__global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
-  using LY = EntryLayout<NARROW>;
-  extern __shared__ __align__(16) uint32_t smem[];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int nwaves = blockDim.x >> 6;
+// Row scale of a chain's groups.  A chain's groups are g0, g0 + S, g0 + 2S, ...  When
+// S <= G (the row length in groups) consecutive ones are at most one row apart, so the
+// scale changes only at precomputed group counts; otherwise every group is on a later row.
+// The scale of the row the chain moves to next is loaded at every group (the same
+// address until the row changes), so a group's memory pattern is fixed and a row change
+// only moves registers.
+struct RowScale {
+  float h, nh;          // h_r of the current group's row, and -128 h_r
+  float hn;             // the scale at pn (loaded one group ahead)
+  const float* pn;      // scale of the row the chain moves to next
+  uint32_t row;         // row of the current group
+  uint32_t kchg;        // group count at which the row changes next
+  uint32_t bnd;         // S <= G: first group of the row after the next one, - g0 + S - 1
+  uint32_t rown, coln;  // S > G: row and column group of the chain's next group
+};
 
-  // which job (uniform per workgroup)
-  int ji = 0;
-  for (int q = 1; q < B.n; ++q)
-    if (B.j[q].wg_begin <= (int64_t)blockIdx.x) ji = q;
-  const DecJob& J = B.j[ji];
-  const int64_t blk0 = J.block_lo + (((int64_t)blockIdx.x - J.wg_begin) * nwaves + wave) * ILP;
+struct GroupCtx {
+  const DecJob* J;
+  StreamRef sref;
+  uint32_t lds0;   // LDS address of the tables
+  uint32_t G;
+  int S;
+  bool rowwise;
+};
 
-  // stage the decode tables (shared by the workgroup's waves)
-  {
-    const uint4* src = (const uint4*)J.tab;
-    uint4* dst = (uint4*)smem;
-    for (int i = tid; i < kTabWords / 4; i += blockDim.x) dst[i] = src[i];
+// Row scale of group kk: move to the next row at a precomputed group count, then issue
+// the (usually repeated) load of the scale the chain moves to next.
+template <int ILP>
+__device__ __forceinline__ void row_scale(const GroupCtx& X, int kk, RowScale* rs, const int* ngr) {
+  const DecJob& J = *X.J;
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) {
+    RowScale& q = rs[c];
+    if ((uint32_t)kk == q.kchg && ((ILP == 1) || kk < ngr[c])) {
+      q.h = q.hn;
+      q.nh = -128.f * q.hn;
+      if (X.rowwise) {
+        ++q.row;
+        q.kchg = q.bnd >> J.log2S;
+        q.bnd += X.G;
+        q.pn += 1;
+      } else {
+        q.row = q.rown;
+        q.kchg = (uint32_t)kk + 1u;
+        q.coln += J.s_mod_g;
+        q.rown += J.s_div_g;
+        if (q.coln >= X.G) {
+          q.coln -= X.G;
+          ++q.rown;
+        }
+        q.pn = J.hr + q.rown;
+      }
+    }
+    q.hn = *q.pn;
   }
-  __syncthreads();
-  if (blk0 >= J.n_blocks) return;
 
-  uint8_t* const lds8 = (uint8_t*)smem;
-  const StreamRef sref{J.stream, J.n_words};
-  const int S = 1 << J.log2S;
+}
+
+// Decode group kk of ILP chains: fast path over eight symbols (escapes replayed on the
+// careful path), container store.
+template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
+__device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* rd, RowScale* rs, const int* ngr,
+                                             const uint32_t* g0, char** optr) {
+  using LY = EntryLayout<NARROW>;
+  const DecJob& J = *X.J;
+  // ---- fast path: eight symbols per chain, no escape handling
+  uint32_t xs[ILP], a2s[ILP], nws[ILP];
+  uint32_t e[ILP][8];
+  uint32_t fbs[ILP];
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) {
+    xs[c] = rd[c].x;
+    a2s[c] = rd[c].a2;
+    nws[c] = rd[c].nw;
+    e[c][0] = ch_entry(X.lds0, rd[c]);
+  }
+  // per step: every chain's table read, then every chain's state update, then the
+  // renormalisations (whose ring reads are conditional and so end the step's LDS batch)
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) {
+    ch_decode(rd[c], e[c][0]);
+    fbs[c] = X.lds0 + free_base(e[c][0]);
+  }
+  ch_renorm_all<ILP>(rd);
+#pragma unroll
+  for (int i = 1; i < 7; ++i) {
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) e[c][i] = ch_entry(fbs[c], rd[c]);
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) ch_decode(rd[c], e[c][i]);
+    ch_renorm_all<ILP>(rd);
+  }
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) {
+    // LAST[c][pi]: pi = parity of the seven floor(u/2), one bit of each entry
+    const uint32_t par = xor3(xor3(e[c][1], e[c][2], e[c][3]), xor3(e[c][4], e[c][5], e[c][6]), e[c][0]);
+    const uint32_t lb = 2u * fbs[c] - X.lds0 + 0x2000u + ((par >> (LY::kPar - 13)) & 0x2000u);
+    e[c][7] = ch_entry(lb, rd[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) ch_decode(rd[c], e[c][7]);
+  ch_renorm_all<ILP>(rd);
+
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) {
+    const bool act = (ILP == 1) || kk < ngr[c];
+    float w[8];
+    int32_t u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (OUT == OUT_COORDS) u[i] = LY::u_of(e[c][i]);
+      else w[i] = LY::w_of(e[c][i], rs[c].h, rs[c].nh);
+    }
+    if (ESC) {
+      const uint32_t any = (e[c][0] | e[c][1] | e[c][2]) | (e[c][3] | e[c][4] | e[c][5]) | (e[c][6] | e[c][7]);
+      const bool slow = act && (any & LY::kEsc) != 0;
+      if (__ballot(slow) != 0) {
+        // careful path for the chains whose group holds an escape: fetch to 24 ahead,
+        // replay the group from its start, fetch back to 17 ahead
+        if (slow) {
+          rd[c].x = xs[c];
+          rd[c].a2 = a2s[c];
+          ch_flush(rd[c]);
+        }
+        ch_sync(X.sref, rd[c], slow, 2 * 24);
+        if (slow) {
+          rd[c].nw = ch_word(rd[c]);
+          ch_group_careful<LY>(X.lds0, rd[c], J.k, u);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i] = rs[c].h * (float)u[i];
+        }
+        ch_sync(X.sref, rd[c], slow, 2 * 17);
+      }
+    }
+    if (act) {
+      if (C8) {
+        store_group<OUT>(optr[c], 0, w, u, true, 8);
+      } else {
+        const uint32_t gk = g0[c] + (uint32_t)kk * (uint32_t)X.S;
+        const int64_t c0 = (int64_t)(gk - rs[c].row * X.G) * 8;
+        store_group<OUT>(J.out, (int64_t)rs[c].row * J.C + c0, w, u, c0 + 8 <= J.C, J.C - c0);
+      }
+    }
+  }
+  if (ILP > 1) {
+    // a chain past its last group keeps its final state
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      if (kk >= ngr[c]) {
+        rd[c].x = xs[c];
+        rd[c].a2 = a2s[c];
+        rd[c].nw = nws[c];
+      }
+    }
+  }
+  constexpr int ESZ = (OUT == OUT_FP32 || OUT == OUT_COORDS) ? 4 : ((OUT == OUT_FP8 || OUT == OUT_INT8) ? 1 : 2);
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) optr[c] += (int64_t)X.S * 8 * ESZ;
+}
+
+// One wave decodes ILP blocks of 64 chains (blocks blk0 .. blk0 + ILP - 1, those below
+// blk_end): lane l runs chain l of each, the ILP chains interleaved step by step so
+// that one chain's table read is in flight while another computes.
+template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
+__device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, int64_t blk_end, int lane, int wave) {
+  const DecJob& J = *X.J;
+  const int S = X.S;
+  const uint32_t G = X.G;
   // lanes of this lane's tile (S consecutive lanes)
   const int s0 = lane & ~(S - 1);
   const uint64_t seg = (S == 64) ? ~0ull : (((1ull << S) - 1ull) << s0);
 
-  char* outp = (char*)J.out;
   constexpr int ESZ = (OUT == OUT_FP32 || OUT == OUT_COORDS) ? 4 : ((OUT == OUT_FP8 || OUT == OUT_INT8) ? 1 : 2);
-  const int64_t ostep = (int64_t)S * 8 * ESZ;
-
   Chain rd[ILP];
+  RowScale rs[ILP];
   int ngr[ILP];
   bool live[ILP];
-  uint32_t row[ILP], col[ILP];
-  float h[ILP];
+  uint32_t g0[ILP];
   char* optr[ILP];
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
     const int64_t ch = (blk0 + c) * 64 + lane;
-    live[c] = ch < J.n_chains && ch >= J.chain_lo && ch < J.chain_hi;
+    live[c] = blk0 + c < blk_end && ch < J.n_chains && ch >= J.chain_lo && ch < J.chain_hi;
     const int64_t t = ch >> J.log2S;
     const int j = (int)(ch & (S - 1));
     int64_t gt = J.n_groups - (t << 9);
@@ -465,156 +620,110 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
     r.x = meta.x;
     r.cur = meta.y;
     r.tailp = meta.z;
-    r.N = (int32_t)meta.w;
-    r.F = 0;
-    r.a2 = 0;
-    r.rb = (uint32_t)(kTabBytes + ((wave * 64 + lane) * ILP + c) * kChainRingBytes);
+    r.rem = (int32_t)meta.w;
+    // rotate each ring by a lane-dependent number of chunks (counters start there), so
+    // lanes whose rings share LDS banks touch different banks
+    r.fb = 16u * (uint32_t)(((lane >> 1) + (lane >> 3)) & 3);
+    r.a2 = r.fb;
+    uint32_t rb = X.lds0 + (uint32_t)(kTabBytes + ((wave * 64 + lane) * ILP + c) * kChainRingBytes);
+    asm volatile("" : "+v"(rb));   // keep the ring base opaque: ring addresses are one and-or
+    r.rb = rb;
     r.seg_lo = (uint32_t)seg;
     r.seg_hi = (uint32_t)(seg >> 32);
     r.pend = make_uint4(0u, 0u, 0u, 0u);
-    r.pend_F = 0;
+    r.pend_at = rb;
     r.have_pend = false;
-    const int64_t g0 = (t << 9) + j;
-    row[c] = live[c] ? (uint32_t)(g0 / J.G) : 0u;
-    col[c] = live[c] ? (uint32_t)(g0 - (int64_t)row[c] * J.G) : 0u;
-    h[c] = ngr[c] > 0 ? J.hr[row[c]] : 0.f;
-    optr[c] = outp + (live[c] ? g0 * 8 * ESZ : 0);   // C % 8 == 0: groups are contiguous
+    const bool any = ngr[c] > 0;
+    const int64_t gg = (t << 9) + j;
+    g0[c] = any ? (uint32_t)gg : 0u;
+    const uint32_t row0 = any ? (uint32_t)(gg / J.G) : 0u;
+    const uint32_t col0 = g0[c] - row0 * G;
+    RowScale& q = rs[c];
+    q.row = row0;
+    q.h = any ? J.hr[row0] : 0.f;
+    q.nh = -128.f * q.h;
+    if (X.rowwise) {
+      q.pn = J.hr + row0 + 1;                 // row scales are padded past the last row
+      q.kchg = any ? (((row0 + 1) * G - g0[c] + (uint32_t)S - 1u) >> J.log2S) : 0xFFFFFFFFu;
+      q.bnd = (row0 + 2) * G - g0[c] + (uint32_t)S - 1u;
+      q.rown = q.coln = 0;
+    } else {
+      q.coln = col0 + J.s_mod_g;
+      q.rown = row0 + J.s_div_g;
+      if (q.coln >= G) {
+        q.coln -= G;
+        ++q.rown;
+      }
+      q.pn = J.hr + (any ? q.rown : 0u);
+      q.kchg = any ? 1u : 0xFFFFFFFFu;
+      q.bnd = 0;
+    }
+    q.hn = *q.pn;
+    optr[c] = (char*)J.out + (live[c] ? gg * 8 * ESZ : 0);   // C % 8 == 0: groups are contiguous
   }
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
-    ch_sync(lds8, sref, rd[c], live[c], 17);   // prime
-    rd[c].nw = ch_word(lds8, rd[c]);
+    ch_sync(X.sref, rd[c], live[c], 2 * 17);   // prime
+    rd[c].nw = ch_word(rd[c]);
   }
-  int nmax = ngr[0], nmin = ngr[0];
+  int nmax = ngr[0];
 #pragma unroll
-  for (int c = 1; c < ILP; ++c) {
-    nmax = ngr[c] > nmax ? ngr[c] : nmax;
-    nmin = ngr[c] < nmin ? ngr[c] : nmin;
-  }
-  const int k = J.k;
+  for (int c = 1; c < ILP; ++c) nmax = ngr[c] > nmax ? ngr[c] : nmax;
 
-  for (int kk = 0; kk < nmax; ++kk) {
-    if ((kk & 1) == 0) {
+  // two groups per iteration: the stream service runs before every even group
+  // (the row scale of the even group is settled before the service, so that its load is
+  // followed by a fixed sequence of memory operations)
+  for (int kk = 0; kk < nmax; kk += 2) {
+    row_scale<ILP>(X, kk, rs, ngr);
 #pragma unroll
-      for (int c = 0; c < ILP; ++c) ch_service(lds8, sref, rd[c], (ILP == 1) || kk < ngr[c]);
-    }
-    // ---- row scale of the next group, loaded one group ahead
-    uint32_t nrow[ILP], ncol[ILP];
-    float h_next[ILP];
-#pragma unroll
-    for (int c = 0; c < ILP; ++c) {
-      nrow[c] = row[c] + J.s_div_g;
-      ncol[c] = col[c] + J.s_mod_g;
-      if (ncol[c] >= (uint32_t)J.G) {
-        ncol[c] -= (uint32_t)J.G;
-        ++nrow[c];
-      }
-      h_next[c] = J.hr[nrow[c] < J.R ? nrow[c] : J.R - 1];
-    }
-
-    // ---- fast path: eight symbols per chain, no escape handling
-    uint32_t xs[ILP], a2s[ILP], nws[ILP];
-    uint32_t e[ILP][8];
-    const uint32_t* tb[ILP];
-#pragma unroll
-    for (int c = 0; c < ILP; ++c) {
-      xs[c] = rd[c].x;
-      a2s[c] = rd[c].a2;
-      nws[c] = rd[c].nw;
-      e[c][0] = ch_entry(smem, rd[c]);
-    }
-    // per step: every chain's table read, then every chain's state update, then the
-    // renormalisations (whose ring reads are conditional and so end the step's LDS batch)
-#pragma unroll
-    for (int c = 0; c < ILP; ++c) {
-      ch_decode(rd[c], e[c][0]);
-      tb[c] = smem + ((1 + ((e[c][0] >> 22) & 1u)) << 11);
-    }
-    ch_renorm_all<ILP>(lds8, rd);
-#pragma unroll
-    for (int i = 1; i < 7; ++i) {
-#pragma unroll
-      for (int c = 0; c < ILP; ++c) e[c][i] = ch_entry(tb[c], rd[c]);
-#pragma unroll
-      for (int c = 0; c < ILP; ++c) ch_decode(rd[c], e[c][i]);
-      ch_renorm_all<ILP>(lds8, rd);
-    }
-#pragma unroll
-    for (int c = 0; c < ILP; ++c) {
-      const uint32_t par = e[c][0] ^ e[c][1] ^ e[c][2] ^ e[c][3] ^ e[c][4] ^ e[c][5] ^ e[c][6];
-      const int pi = (int)((par >> LY::kPar) & 1u);
-      const int cs = (int)((e[c][0] >> 22) & 1u);
-      e[c][7] = ch_entry(smem + ((3 + 2 * cs + pi) << 11), rd[c]);
-    }
-#pragma unroll
-    for (int c = 0; c < ILP; ++c) ch_decode(rd[c], e[c][7]);
-    ch_renorm_all<ILP>(lds8, rd);
-
-#pragma unroll
-    for (int c = 0; c < ILP; ++c) {
-      const bool act = (ILP == 1) || kk < ngr[c];
-      float w[8];
-      int32_t u[8];
-      bool slow = false;
-      if (ESC) {
-        const uint32_t any = (e[c][0] | e[c][1] | e[c][2]) | (e[c][3] | e[c][4] | e[c][5]) | (e[c][6] | e[c][7]);
-        slow = act && (any & LY::kEsc) != 0;
-      }
-      if (ESC && __ballot(slow) != 0) {
-        // careful path for the chains whose group holds an escape: fetch to 24 ahead,
-        // replay the group from its start, fetch back to 17 ahead
-        if (slow) {
-          rd[c].x = xs[c];
-          rd[c].a2 = a2s[c];
-          ch_flush(lds8, rd[c]);
-        }
-        ch_sync(lds8, sref, rd[c], slow, 24);
-        if (slow) {
-          rd[c].nw = ch_word(lds8, rd[c]);
-          ch_group_careful<LY>(smem, lds8, rd[c], k, u);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) w[i] = h[c] * (float)u[i];
-        }
-        ch_sync(lds8, sref, rd[c], slow, 17);
-      }
-      if (!slow) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (OUT == OUT_COORDS) u[i] = LY::u_of(e[c][i]);
-          else w[i] = LY::w_of(e[c][i], h[c], -128.f * h[c]);
-        }
-      }
-      if (act) {
-        if (C8) {
-          store_group<OUT>(optr[c], 0, w, u, true, 8);
-        } else {
-          const int64_t c0 = (int64_t)col[c] * 8;
-          store_group<OUT>(outp, (int64_t)row[c] * J.C + c0, w, u, c0 + 8 <= J.C, J.C - c0);
-        }
-      }
-    }
-    if (ILP > 1 && kk >= nmin) {
-      // a chain past its last group keeps its final state
-#pragma unroll
-      for (int c = 0; c < ILP; ++c) {
-        if (kk >= ngr[c]) {
-          rd[c].x = xs[c];
-          rd[c].a2 = a2s[c];
-          rd[c].nw = nws[c];
-        }
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < ILP; ++c) {
-      optr[c] += ostep;
-      row[c] = nrow[c];
-      col[c] = ncol[c];
-      h[c] = h_next[c];
+    for (int c = 0; c < ILP; ++c) ch_service(X.sref, rd[c], (ILP == 1) || kk < ngr[c]);
+    decode_group<OUT, ESC, C8, NARROW, ILP>(X, kk, rd, rs, ngr, g0, optr);
+    if (kk + 1 < nmax) {
+      row_scale<ILP>(X, kk + 1, rs, ngr);
+      decode_group<OUT, ESC, C8, NARROW, ILP>(X, kk + 1, rd, rs, ngr, g0, optr);
     }
   }
 #pragma unroll
   for (int c = 0; c < ILP; ++c)
     if (live[c] && ngr[c] > 0 && rd[c].x != kL) atomicAdd(J.err, 1u);
+}
+
+// A workgroup stages the decode tables of its job into LDS once, then its waves take
+// the workgroup's blocks in turn (wave w: blocks w ILP, (w + W) ILP, ...).  Each job
+// gives every workgroup `bpw` consecutive blocks (the last one fewer).
+template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
+__global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
+  extern __shared__ __align__(16) uint32_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nwaves = blockDim.x >> 6;
+
+  // which job (uniform per workgroup)
+  int ji = 0;
+  for (int q = 1; q < B.n; ++q)
+    if (B.j[q].wg_begin <= (int64_t)blockIdx.x) ji = q;
+  const DecJob& J = B.j[ji];
+  const int64_t wg_blk0 = J.block_lo + ((int64_t)blockIdx.x - J.wg_begin) * B.bpw;
+  const int64_t wg_blk1 = wg_blk0 + B.bpw < J.n_blocks ? wg_blk0 + B.bpw : J.n_blocks;
+
+  // stage the decode tables (shared by the workgroup's waves)
+  {
+    const uint4* src = (const uint4*)J.tab;
+    uint4* dst = (uint4*)smem;
+    for (int i = tid; i < kTabWords / 4; i += blockDim.x) dst[i] = src[i];
+  }
+  __syncthreads();
+
+  GroupCtx X;
+  X.J = &J;
+  X.lds0 = (uint32_t)(uintptr_t)(EP_LDS uint8_t*)smem;
+  X.sref = StreamRef{J.stream, J.n_words};
+  X.S = 1 << J.log2S;
+  X.G = (uint32_t)J.G;
+  X.rowwise = (uint32_t)X.S <= X.G;
+  for (int64_t b = wg_blk0 + (int64_t)wave * ILP; b < wg_blk1; b += (int64_t)nwaves * ILP)
+    decode_blocks<OUT, ESC, C8, NARROW, ILP>(X, b, wg_blk1, lane, wave);
 }
 
 // ---------------------------------------------------------------- launch helpers
@@ -630,11 +739,12 @@ int lds_max_bytes() {
   return v;
 }
 
-// Launch shape: ILP chains per lane, `waves` waves per workgroup.
+// Launch shape: ILP chains per lane, `waves` waves per workgroup, `bpw` blocks of 64
+// chains per workgroup (its waves loop over them).
 struct Shape {
   int ilp;
   int waves;
-  int64_t blocks_per_wg() const { return (int64_t)ilp * waves; }
+  int64_t bpw;
 };
 
 template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
@@ -715,40 +825,55 @@ DecJob make_job(const Blob& b, void* out) {
   return j;
 }
 
+int cu_count() {
+  static int v = -1;
+  if (v < 0) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    int x = 0;
+    if (hipDeviceGetAttribute(&x, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || x <= 0) x = 256;
+    v = x;
+  }
+  return v;
+}
+
 // Launch shape.  One table copy (56 KB of LDS) serves the workgroup and each chain adds
-// a 64-byte ring, so a workgroup holds at most 16 waves of one chain per lane or 13 of two.
-// The blocks of a launch are dealt to workgroups job by job; a CU holds one workgroup.
-// Cost model: workgroup rounds over the 256 CUs times the length of a round, which grows
-// with the chains per CU once they keep the VALU busy (about 12) and is flat below that.
-// Two chains per lane (EP_DECODE_ILP=2) double the lines a CU keeps open in L2 and thrash
-// it at full occupancy with the per-chain stream layout, so one chain per lane is the
-// default.  EP_DECODE_WAVES overrides the wave count.
+// a 64-byte ring, so a workgroup holds at most 16 waves of one chain per lane or 13 of
+// two.  A launch of at least one full round (every CU a workgroup of 16 waves) gives each
+// wave one block: all waves of a workgroup finish together, the 4 SIMDs carry equal
+// work, and a launch queued on another stream fills the CUs the last round leaves idle.
+// A smaller launch spreads its blocks evenly over at most one workgroup per CU (`bpw`
+// each, the fewest that fit), the waves looping over them.  Two chains per lane
+// (EP_DECODE_ILP=2) is an option; EP_DECODE_WAVES / EP_DECODE_BPW override the shape.
 Shape pick_shape(const int64_t* n_blocks, int n) {
-  const int cus = 256;
+  const int64_t cus = cu_count();
   const int lds = lds_max_bytes() - kTabBytes;
-  const int max1 = std::max(1, std::min(kMaxWaves, lds / (64 * kChainRingBytes)));
-  const int max2 = std::min(kMaxWaves, lds / (2 * 64 * kChainRingBytes));
   int ilp = 1;
   if (const char* e = std::getenv("EP_DECODE_ILP"))
-    if (std::atoi(e) == 2 && max2 >= 1) ilp = 2;
-  const int wmax = ilp == 2 ? max2 : max1;
-  int best_w = 1;
-  int64_t best_cost = -1;
-  for (int w = 1; w <= wmax; w += (w == 1 ? 1 : 2)) {
-    int64_t wg = 0;
-    for (int i = 0; i < n; ++i) wg += (n_blocks[i] + (int64_t)ilp * w - 1) / ((int64_t)ilp * w);
-    const int64_t rounds = (wg + cus - 1) / cus;
-    const int64_t cost = rounds * std::max<int64_t>((int64_t)w * ilp, 12);
-    if (best_cost < 0 || cost < best_cost) {
-      best_cost = cost;
-      best_w = w;
+    if (std::atoi(e) == 2) ilp = 2;
+  const int wmax = std::max(1, std::min(kMaxWaves, lds / (ilp * 64 * kChainRingBytes)));
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) total += n_blocks[i];
+  int64_t bpw;
+  if (total >= cus * wmax * ilp) {
+    bpw = (int64_t)wmax * ilp;
+  } else {
+    bpw = std::max<int64_t>(1, (total + cus - 1) / cus);
+    for (;;) {
+      int64_t wg = 0;
+      for (int i = 0; i < n; ++i) wg += (n_blocks[i] + bpw - 1) / bpw;
+      if (wg <= cus) break;
+      ++bpw;
     }
   }
+  if (const char* e = std::getenv("EP_DECODE_BPW"))
+    if (std::atoll(e) >= 1) bpw = std::atoll(e);
+  int waves = (int)std::min<int64_t>(wmax, (bpw + ilp - 1) / ilp);
   if (const char* e = std::getenv("EP_DECODE_WAVES")) {
     const int v = std::atoi(e);
-    if (v >= 1 && v <= kMaxWaves) best_w = std::min(v, wmax);
+    if (v >= 1 && v <= kMaxWaves) waves = std::min(v, wmax);
   }
-  return Shape{ilp, best_w};
+  return Shape{ilp, waves, bpw};
 }
 
 int check_uploaded(const Blob& b) {
@@ -774,11 +899,12 @@ int decode_one(const Blob& b, void* dst, int64_t chain_lo, int64_t chain_hi, int
   j.block_lo = blo;
   const int64_t nblk = bhi - blo;
   const Shape sh = pick_shape(&nblk, 1);
-  const int64_t n_wg = (nblk + sh.blocks_per_wg() - 1) / sh.blocks_per_wg();
+  const int64_t n_wg = (nblk + sh.bpw - 1) / sh.bpw;
   j.n_blocks = bhi;   // blocks beyond the range are skipped
   DecBatch B{};
   B.j[0] = j;
   B.n = 1;
+  B.bpw = sh.bpw;
   return launch_any(out, (b.flags & kFlagEsc) != 0, (b.C % 8) == 0, b.k <= 6, sh, B, n_wg, st);
 }
 
@@ -809,7 +935,7 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
   auto al = [](size_t v) { return (v + 255) & ~size_t(255); };
   const size_t o_tab = 0;
   const size_t o_hr = o_tab + al(kTabBytes);
-  const size_t o_ch = o_hr + al(4 * (size_t)b.R);
+  const size_t o_ch = o_hr + al(4 * ((size_t)b.R + kHrPad));
   const size_t o_err = o_ch + al(16 * (size_t)b.n_chains);
   const size_t o_stream = o_err + 256;
   const size_t total = o_stream + al(2 * (size_t)b.n_words + 256);
@@ -902,26 +1028,22 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
   // all blobs of one launch share the container kind and the escape path
   int out = -1;
   bool esc = false, c8 = true;
-  std::vector<int64_t> nblk(n);
   for (int i = 0; i < n; ++i) {
     if (!blobs[i] || !dsts[i]) return fail(EP_E_ARG, "null blob or destination");
     const Blob& b = blobs[i]->b;
     int rc = check_uploaded(b);
     if (rc) return rc;
     if (reinterpret_cast<uintptr_t>(dsts[i]) & 15) return fail(EP_E_ARG, "destination must be 16-byte aligned");
-    int o = out_kind(b);
-    if (o == OUT_BF16_SAT) o = OUT_BF16_SAT;
+    const int o = out_kind(b);
     if (out < 0) out = o;
     else if ((out == OUT_BF16 || out == OUT_BF16_SAT) && (o == OUT_BF16 || o == OUT_BF16_SAT))
       out = (out == OUT_BF16_SAT || o == OUT_BF16_SAT) ? OUT_BF16_SAT : OUT_BF16;
     else if (o != out) return fail(EP_E_ARG, "batch mixes container dtypes");
     esc |= (b.flags & kFlagEsc) != 0;
     c8 &= (b.C % 8) == 0;
-    nblk[i] = b.n_blocks;
   }
-  const Shape sh = pick_shape(nblk.data(), n);
   // blobs whose tables use the narrow / wide entry layout go to separate launches,
-  // each of up to kMaxBatch blobs
+  // each of up to kMaxBatch blobs with its own launch shape
   for (int pass = 0; pass < 2; ++pass) {
     const bool narrow = pass == 0;
     std::vector<int> idx;
@@ -930,11 +1052,15 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
     for (size_t i0 = 0; i0 < idx.size(); i0 += kMaxBatch) {
       DecBatch B{};
       B.n = (int)std::min<size_t>(kMaxBatch, idx.size() - i0);
+      int64_t nblk[kMaxBatch];
+      for (int q = 0; q < B.n; ++q) nblk[q] = blobs[idx[i0 + q]]->b.n_blocks;
+      const Shape sh = pick_shape(nblk, B.n);
+      B.bpw = sh.bpw;
       int64_t wg = 0;
       for (int q = 0; q < B.n; ++q) {
         B.j[q] = make_job(blobs[idx[i0 + q]]->b, dsts[idx[i0 + q]]);
         B.j[q].wg_begin = wg;
-        wg += (B.j[q].n_blocks + sh.blocks_per_wg() - 1) / sh.blocks_per_wg();
+        wg += (B.j[q].n_blocks + sh.bpw - 1) / sh.bpw;
       }
       int rc = launch_any(out, esc, c8, narrow, sh, B, wg, (hipStream_t)stream);
       if (rc) return rc;
