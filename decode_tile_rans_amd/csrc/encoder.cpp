@@ -260,7 +260,7 @@ Estimate estimate(const Matrix& mx, const std::vector<int64_t>& rows, float delt
   parallel_for((int64_t)rows.size(), [&](int64_t b, int64_t e, int) {
     for (int64_t i = b; i < e; ++i) quantize_row(mx, rows[i], delta, &u[(size_t)(i * G * 8)]);
   }, 8);
-  // choose k: smallest k with #(m >= 2^k) * 1024 <= #coords
+  // choose k: smallest k with #(m >= 2^k) * 2^20 <= #coords (escapes at most one in 2^20)
   int64_t ge[8] = {0};
   for (int64_t gi = 0; gi < ng; ++gi) {
     const int32_t* ug = &u[gi * 8];
@@ -273,7 +273,7 @@ Estimate estimate(const Matrix& mx, const std::vector<int64_t>& rows, float delt
   }
   int k = 7;
   for (int kk = 3; kk <= 7; ++kk)
-    if (ge[kk] * 1024 <= ng * 8) {
+    if (ge[kk] * (int64_t(1) << 20) <= ng * 8) {
       k = kk;
       break;
     }

@@ -317,10 +317,15 @@ def count_symbols(sym, nm: int):
 
 
 def choose_k(mags: np.ndarray) -> int:
-    """Smallest k in 3..7 with #(m >= 2^k) * 1024 <= #coordinates (else 7)."""
+    """Smallest k in 3..7 with #(m >= 2^k) * 2^20 <= #coordinates (else 7).
+
+    The pages leave the split between directly coded magnitudes and escape
+    buckets open; this reading keeps escapes (raw-bit symbols) at most one in
+    2^20 coordinates of the sample whenever K = 2^k <= 128 allows it.
+    """
     n = mags.size
     for k in range(3, 8):
-        if int((mags >= (1 << k)).sum()) * 1024 <= n:
+        if int((mags >= (1 << k)).sum()) * (1 << 20) <= n:
             return k
     return 7
 
