@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--no-linear", action="store_true")
     p.add_argument("--no-layer-mode", action="store_true")
     p.add_argument("--matrices", type=int, default=276, help="first N matrices of the stack (profiling runs)")
-    p.add_argument("--streams", type=int, default=2, help="HIP streams the block launches rotate over")
+    p.add_argument("--streams", type=int, default=3, help="HIP streams the block launches rotate over")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
     return p.parse_args()
