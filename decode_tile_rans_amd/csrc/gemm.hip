@@ -7,15 +7,18 @@
 // weight codes compressed by EntroPack and an FP8 GEMM at inference.
 //
 // Both kernels are "NT": X [T x K] and W [N x K] are K-contiguous, Y = X W^T is
-// [T x N] row-major BF16 with fp32 accumulation.  Workgroup tile 128 x 128, 4 waves
-// in a 2 x 2 arrangement, each wave 64 x 64 = 2 x 2 MFMA 32x32 tiles; K tiles of 128
-// bytes per row staged in LDS (double buffered through registers).
+// [T x N] row-major BF16 with fp32 accumulation.  The BF16 kernel (below, 256 x 256 or
+// 256 x 128 tiles, LDS filled by direct-to-LDS loads) serves the compressed linear layer
+// and its uncompressed baseline.  The FP8 kernel: workgroup tile 128 x 128, 4 waves in a
+// 2 x 2 arrangement, each wave 64 x 64 = 2 x 2 MFMA 32x32 tiles; K tiles of 128 bytes per
+// row staged in LDS (double buffered through registers).
 //   BF16: v_mfma_f32_32x32x16_bf16   (A/B: 8 bf16 per lane, lane -> row l%32,
 //                                      k = 8 (l/32) .. +8)
 //   FP8:  v_mfma_f32_32x32x64_f8f6f4 (A/B: 32 e4m3 per lane, k = 32 (l/32) .. +32)
 //   D:    lane l holds column l%32, rows 8 (r/4) + 4 (l/32) + r%4 for r = 0..15.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <mutex>
 
 #include "ep_internal.h"
@@ -154,6 +157,251 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(const uint8_t* __restrict_
     }
 }
 
+// ---------------------------------------------------------------- BF16 GEMM, 256 x BN tiles
+// Workgroup tile 256 x BN, waves 2 along M x W/2 along N (BN = 128: 4 waves of 128 x 64;
+// BN = 256: 8 waves of 128 x 64, two per SIMD), each wave 4 x 2 MFMA 32x32x16 blocks.
+// K tiles of BK elements go from HBM straight into one of NST LDS stages
+// (global_load_lds, 16 bytes per lane, lane l landing at base + 16 l), issued NST - 1
+// tiles ahead; one barrier per K tile.  LDS rows are 2 BK bytes; their 16-byte
+// chunks are XOR-swizzled by the row so that the eight lanes reading one fragment row
+// group touch all 32 banks once.  Chunks outside the matrix load a zero line.  The MFMA
+// takes the W fragment as its first operand, so each lane ends with four consecutive
+// outputs of one row (one 8-byte store).
+//   BN = 128: BK = 64, 3 stages (144 KB);  BN = 256: BK = 64, 2 stages (128 KB).
+constexpr int GBM = 256;
+__device__ __align__(16) uint4 g_zero_line[4];   // zero-initialised; the source of out-of-range chunks
+
+#define EP_LDS3 __attribute__((address_space(3)))
+
+// a per-wave value the compiler may keep in a scalar register
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int BN> struct GemmCfg;
+template <> struct GemmCfg<128> { static constexpr int BK = 64, NST = 3, WAVES = 4; };
+template <> struct GemmCfg<256> { static constexpr int BK = 64, NST = 2, WAVES = 8; };
+
+// chunk position of logical chunk c in row r (CPR chunks per row)
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+  return CPR == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 1) & 3));
+}
+
+template <int BN>
+__global__ void __launch_bounds__(64 * GemmCfg<BN>::WAVES, 1) gemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                                                           const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
+                                                           int64_t T, int64_t N, int64_t K, int ntm, int ntn) {
+  constexpr int BK = GemmCfg<BN>::BK, NST = GemmCfg<BN>::NST, NW = GemmCfg<BN>::WAVES;
+  constexpr int RB = 2 * BK, CPR = RB / 16, RPL = 64 / CPR;   // row bytes, chunks per row, rows per load
+  constexpr int A_BYTES = GBM * RB, B_BYTES = BN * RB, STAGE = A_BYTES + B_BYTES;
+  constexpr int WN = BN / (NW / 2), NJ = WN / 32, MI = 4;     // waves: 2 along M x NW/2 along N
+  constexpr int A_LD = GBM / RPL / NW, B_LD = BN / RPL / NW;  // load instructions per wave
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);   // uniform per wave
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
+
+  // tile of this workgroup: workgroups are dealt to the 8 XCDs in turn, so each XCD gets
+  // a contiguous range of tiles; tiles are ordered in groups of 4 M-tiles x all N-tiles,
+  // so the tiles resident on one XCD share X and W panels in its L2
+  const int ntiles = ntm * ntn;
+  int t = (int)blockIdx.x;
+  if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
+  constexpr int GM = 4;
+  const int gsz = GM * ntn, g = t / gsz, rem = t % gsz;
+  const int gm = ntm - g * GM < GM ? ntm - g * GM : GM;
+  const int64_t m0 = (int64_t)(g * GM + rem % gm) * GBM, n0 = (int64_t)(rem / gm) * BN;
+  const int64_t nkt = (K + BK - 1) / BK;
+
+  // this lane's part of each load instruction: row (within RPL) and the chunk it fetches.
+  // Rows past the matrix read its last row (their outputs are never stored); the byte
+  // offsets from the panel start are fixed, the panel base advances by one K tile.
+  const int lrow = lane / CPR, lpos = lane % CPR;
+  uint32_t offA[A_LD], offB[B_LD], kcA[A_LD], kcB[B_LD];   // byte offset, its K part
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int r = (wave * A_LD + i) * RPL + lrow;
+    const int64_t gr = m0 + r < T ? m0 + r : T - 1;
+    kcA[i] = (uint32_t)(swz<CPR>(r, lpos) * 16);
+    offA[i] = (uint32_t)((gr - m0) * K * 2) + kcA[i];
+  }
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int r = (wave * B_LD + i) * RPL + lrow;
+    const int64_t gr = n0 + r < N ? n0 + r : N - 1;
+    kcB[i] = (uint32_t)(swz<CPR>(r, lpos) * 16);
+    offB[i] = (uint32_t)((gr - n0) * K * 2) + kcB[i];
+  }
+  const char* xpan = (const char*)(X + m0 * K);
+  const char* wpan = (const char*)(W + n0 * K);
+  const char* pA[A_LD];
+  const char* pB[B_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) pA[i] = xpan + offA[i];
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) pB[i] = wpan + offB[i];
+  const bool ktail = (K % BK) != 0;
+  const char* zero = (const char*)g_zero_line;
+  auto issue = [&](int64_t kt, int st) {
+    EP_LDS3 uint8_t* sbase = (EP_LDS3 uint8_t*)lds + st * STAGE;
+    const int64_t kb = kt * BK * 2;
+    if (!ktail || kt + 1 < nkt) {
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(pA[i] + kb), (EP_LDS3 void*)(sbase + (wave * A_LD + i) * 1024), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < B_LD; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(pB[i] + kb), (EP_LDS3 void*)(sbase + A_BYTES + (wave * B_LD + i) * 1024), 16, 0, 0);
+    } else {
+      // last, partial K tile: chunks at or past K load the zero line
+      const int64_t kleft = 2 * K - kb;   // bytes of K left
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i) {
+        const bool in = (int64_t)kcA[i] < kleft;
+        __builtin_amdgcn_global_load_lds((const void*)(in ? pA[i] + kb : zero), (EP_LDS3 void*)(sbase + (wave * A_LD + i) * 1024), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < B_LD; ++i) {
+        const bool in = (int64_t)kcB[i] < kleft;
+        __builtin_amdgcn_global_load_lds((const void*)(in ? pB[i] + kb : zero), (EP_LDS3 void*)(sbase + A_BYTES + (wave * B_LD + i) * 1024), 16, 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // fragment addresses within a stage (the K16 step adds a swizzled chunk position)
+  const int lr = lane & 31, lh = lane >> 5;
+  auto frag_load = [&](const uint8_t* sA, const uint8_t* sB, int ks, bf16x8* fa, bf16x8* fb) {
+    const int c = 2 * ks + lh;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int r = wm * 128 + 32 * i + lr;
+      fa[i] = *(const bf16x8*)(sA + r * RB + (swz<CPR>(r, c) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int r = wn * WN + 32 * j + lr;
+      fb[j] = *(const bf16x8*)(sB + r * RB + (swz<CPR>(r, c) << 4));
+    }
+  };
+
+  // prologue: tiles 0 .. NST-2 in flight
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nkt) issue(s, s);
+  constexpr int LD = A_LD + B_LD;
+  auto tile = [&](int64_t kt, int st) {
+    // this wave's loads of tile kt are done once at most the later tiles' loads remain
+    const int64_t later = (nkt - 1 - kt) < (NST - 2) ? (nkt - 1 - kt) : (NST - 2);
+    if (NST >= 4 && later >= 2) __builtin_amdgcn_s_waitcnt((2 * LD & 15) | (((2 * LD) >> 4) << 14) | (7 << 4) | (15 << 8));
+    else if (later >= 1) __builtin_amdgcn_s_waitcnt((LD & 15) | ((LD >> 4) << 14) | (7 << 4) | (15 << 8));
+    else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    // every wave's part of tile kt is in LDS and stage (kt - 1) % NST is free once all
+    // waves pass; a plain s_barrier (no fence: the loads of later tiles stay in flight)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + NST - 1 < nkt) issue(kt + NST - 1, (st + NST - 1) % NST);
+    const uint8_t* sA = lds + st * STAGE;
+    const uint8_t* sB = sA + A_BYTES;
+    bf16x8 fa[2][MI], fb[2][NJ];
+    frag_load(sA, sB, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      // the next step's fragments are requested before this step's MFMAs
+      if (ks + 1 < BK / 16) frag_load(sA, sB, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int64_t kt = 0; kt < nkt; kt += NST) {
+#pragma unroll
+    for (int s = 0; s < NST; ++s)
+      if (kt + s < nkt) tile(kt + s, s);
+  }
+
+  // epilogue: lane holds row m = m0 + wm 128 + 32 i + lr and columns
+  // n = n0 + wn WN + 32 j + 8 (r / 4) + 4 lh + r % 4
+  const bool vec = (N % 4) == 0;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int64_t m = m0 + wm * 128 + 32 * i + lr;
+    if (m >= T) continue;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int64_t n = n0 + wn * WN + 32 * j + 8 * rq + 4 * lh;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[i][j][4 * rq + e];
+          if (bias && n + e < N) v[e] += bf16_to_float(bias[n + e]);
+        }
+        uint16_t* yp = Y + m * N + n;
+        if (vec && n + 3 < N) {
+          typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+          u32x2 pk;
+          pk.x = (uint32_t)float_to_bf16(v[0]) | ((uint32_t)float_to_bf16(v[1]) << 16);
+          pk.y = (uint32_t)float_to_bf16(v[2]) | ((uint32_t)float_to_bf16(v[3]) << 16);
+          *(u32x2*)yp = pk;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) yp[e] = float_to_bf16(v[e]);
+        }
+      }
+  }
+}
+
+template <int BN>
+int launch_bf16_bn(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K,
+                   hipStream_t st) {
+  constexpr int lds = GemmCfg<BN>::NST * (GBM + BN) * 2 * GemmCfg<BN>::BK;
+  auto kern = gemm_bf16_kernel<BN>;
+  static std::once_flag once;
+  std::call_once(once, [&] { (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); });
+  const int ntm = (int)((T + GBM - 1) / GBM), ntn = (int)((N + BN - 1) / BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(64 * GemmCfg<BN>::WAVES), lds, st, (const uint16_t*)x, (const uint16_t*)w,
+                     (const uint16_t*)bias, (uint16_t*)y, T, N, K, ntm, ntn);
+  return hip_check(hipGetLastError(), "gemm launch");
+}
+
+// BN = 256 unless 128-wide tiles fill the CUs' rounds much better (a 256 x 256 tile does
+// about 1.25x the work per cycle of a 256 x 128 one).
+int launch_bf16(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K,
+                hipStream_t st) {
+  if (!x || !w || !y) return fail(EP_E_ARG, "null pointer");
+  if (T < 1 || N < 1 || K < 1) return fail(EP_E_ARG, "GEMM sizes must be >= 1");
+  if (K % 8) return fail(EP_E_ARG, "K must be a multiple of 8 (BF16)");
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w)) & 15)
+    return fail(EP_E_ARG, "operands must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(y) & 7) && N % 4 == 0) return fail(EP_E_ARG, "output must be 8-byte aligned");
+  const int64_t ntm = (T + GBM - 1) / GBM;
+  auto eff = [&](int64_t bn) {
+    const int64_t tiles = ntm * ((N + bn - 1) / bn);
+    const int64_t rounds = (tiles + 255) / 256;
+    return (double)(T * N) / (double)(rounds * 256 * GBM * bn);
+  };
+  if (std::getenv("EP_GEMM_BN")) {
+    if (std::atoi(std::getenv("EP_GEMM_BN")) == 128) return launch_bf16_bn<128>(x, w, bias, y, T, N, K, st);
+    return launch_bf16_bn<256>(x, w, bias, y, T, N, K, st);
+  }
+  if (eff(128) > 1.25 * eff(256)) return launch_bf16_bn<128>(x, w, bias, y, T, N, K, st);
+  return launch_bf16_bn<256>(x, w, bias, y, T, N, K, st);
+}
+
 template <bool FP8>
 int launch_gemm(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K, float ax,
                 const float* aw, hipStream_t st) {
@@ -182,7 +430,7 @@ extern "C" {
 int ep_gemm_bf16_nt(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K,
                     ep_stream stream) {
   set_error("");
-  return launch_gemm<false>(x, w, bias, y, T, N, K, 1.f, nullptr, (hipStream_t)stream);
+  return launch_bf16(x, w, bias, y, T, N, K, (hipStream_t)stream);
 }
 
 int ep_gemm_fp8_nt(const void* xq, const void* wq, float a_x, const float* aw, void* y, int64_t T, int64_t N,
@@ -201,7 +449,7 @@ int ep_compressed_linear_forward(const ep_blob* w, const void* x, int64_t T, con
   void* wd = (void*)(((uintptr_t)ws + 255) & ~uintptr_t(255));
   int rc = ep_decompress(w, wd, stream);
   if (rc) return rc;
-  return launch_gemm<false>(x, wd, bias, y, T, b.R, b.C, 1.f, nullptr, (hipStream_t)stream);
+  return launch_bf16(x, wd, bias, y, T, b.R, b.C, (hipStream_t)stream);
 }
 
 }  // extern "C"
