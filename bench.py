@@ -223,6 +223,9 @@ def fused_linear(target_bpp, reps=10):
     t_gemm = timeit(lambda: L.ep_gemm_bf16_nt(x.data_ptr(), w.data_ptr(), None, y.data_ptr(), T, R, C, sp))
     t_torch = timeit(lambda: torch.matmul(x, w.t()))
     flops = 2.0 * T * R * C
+    # a sequence of layers (4 distinct weights, each twice): the next layer's decode on a
+    # second stream while this layer's GEMM runs, against the same GEMMs on plain weights
+    seq = linear_sequence(c, wbits, x, T, target_bpp, timeit)
     return {
         "workload": "CompressedLinear prefill 14336x4096 weight @%.1f bpp, 4096 tokens" % target_bpp,
         "actual_bpp": round(c.actual_bpp, 4),
@@ -232,7 +235,57 @@ def fused_linear(target_bpp, reps=10):
         "overhead_pct_vs_hipblaslt": round(100.0 * (t_fused / t_torch - 1.0), 2),
         "gemm_mfma_util": round(flops / (t_gemm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "gemm_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 1),
+        "sequence_overlapped": seq,
     }
+
+
+def linear_sequence(c0, wbits0, x, T, target_bpp, timeit, n_layers=8):
+    """n_layers compressed linears of the 14336x4096 shape (weights of seeds 5..8 in
+    turn): serial (decode then GEMM per layer, one stream), overlapped (decode of layer
+    i+1 on a side stream during the GEMM of layer i) and plain BF16 GEMMs."""
+    import torch
+    import synth
+    import decode_tile_rans_amd as ep
+    from decode_tile_rans_amd import _lib as L
+    R, C = wbits0.shape
+    comps, wts = [c0], [torch.from_numpy(wbits0).view(torch.bfloat16).cuda()]
+    os.environ["EP_NUM_THREADS"] = str(min(16, os.cpu_count() or 1))
+    for seed in (6, 7, 8):
+        wb = synth.rowscaled(R, C, seed)
+        c = ep.compress(wb, target_bpp, dtype=torch.bfloat16)
+        c.upload()
+        comps.append(c)
+        wts.append(torch.from_numpy(wb).view(torch.bfloat16).cuda())
+    os.environ.pop("EP_NUM_THREADS", None)
+    layers = [i % len(comps) for i in range(n_layers)]
+    hs = [comps[i].handle for i in layers]
+    ys = [torch.empty((T, R), dtype=torch.bfloat16, device="cuda") for _ in layers]
+    st = torch.cuda.current_stream()
+    sp = int(st.cuda_stream)
+    side = torch.cuda.Stream()
+    need = L.ep_linear_seq_workspace_bytes(hs)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    n1 = L.ep_linear_workspace_bytes(hs[0])
+    ws1 = torch.empty(n1, dtype=torch.uint8, device="cuda")
+
+    def plain():
+        for i, y in zip(layers, ys):
+            L.ep_gemm_bf16_nt(x.data_ptr(), wts[i].data_ptr(), None, y.data_ptr(), T, R, C, sp)
+
+    def serial():
+        for h, y in zip(hs, ys):
+            L.ep_compressed_linear_forward(h, x.data_ptr(), T, None, y.data_ptr(), ws1.data_ptr(), n1, sp)
+
+    def overlapped():
+        L.ep_compressed_linear_seq_forward(hs, [x.data_ptr()] * n_layers, T, None, [y.data_ptr() for y in ys],
+                                           ws.data_ptr(), need, sp, int(side.cuda_stream))
+
+    t_plain, t_serial, t_over = timeit(plain), timeit(serial), timeit(overlapped)
+    del ys, ws, ws1, wts
+    return {"layers": n_layers, "ms_plain_bf16_gemms": round(t_plain, 4), "ms_serial": round(t_serial, 4),
+            "ms_overlapped": round(t_over, 4),
+            "overhead_pct_serial": round(100.0 * (t_serial / t_plain - 1.0), 2),
+            "overhead_pct_overlapped": round(100.0 * (t_over / t_plain - 1.0), 2)}
 
 
 def main():

@@ -30,6 +30,9 @@ SIGNATURES = {
     "ep_blob_device_errors": (_i64, [_vp]),
     "ep_linear_workspace_bytes": (_sz, [_vp]),
     "ep_compressed_linear_forward": (_int, [_vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "ep_linear_seq_workspace_bytes": (_sz, [C.POINTER(_vp), _int]),
+    "ep_compressed_linear_seq_forward": (_int, [C.POINTER(_vp), _int, C.POINTER(_vp), _i64, C.POINTER(_vp),
+                                                C.POINTER(_vp), _vp, _sz, _vp, _vp]),
     "ep_gemm_bf16_nt": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "ep_gemm_fp8_nt": (_int, [_vp, _vp, _flt, _vp, _vp, _i64, _i64, _i64, _vp]),
     "ep_actual_bpp": (_dbl, [_vp]),
@@ -117,6 +120,21 @@ def ep_linear_workspace_bytes(blob: int) -> int:
 
 def ep_compressed_linear_forward(blob, dev_x, T, dev_bias, dev_y, dev_ws, ws_bytes, stream=0):
     check(lib().ep_compressed_linear_forward(blob, dev_x, T, dev_bias, dev_y, dev_ws, ws_bytes, stream))
+
+
+def _ptrs(seq):
+    return (_vp * len(seq))(*[p if p else None for p in seq])
+
+
+def ep_linear_seq_workspace_bytes(blobs) -> int:
+    return int(lib().ep_linear_seq_workspace_bytes(_ptrs(blobs), len(blobs)))
+
+
+def ep_compressed_linear_seq_forward(blobs, dev_xs, T, dev_biases, dev_ys, dev_ws, ws_bytes, main_stream, side_stream):
+    n = len(blobs)
+    bias = _ptrs(dev_biases) if dev_biases is not None else None
+    check(lib().ep_compressed_linear_seq_forward(_ptrs(blobs), n, _ptrs(dev_xs), T, bias, _ptrs(dev_ys), dev_ws,
+                                                 ws_bytes, main_stream, side_stream))
 
 
 def ep_gemm_bf16_nt(dev_x, dev_w, dev_bias, dev_y, T, N, K, stream=0):

@@ -18,6 +18,7 @@
 //   D:    lane l holds column l%32, rows 8 (r/4) + 4 (l/32) + r%4 for r = 0..15.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <mutex>
 
@@ -452,4 +453,69 @@ int ep_compressed_linear_forward(const ep_blob* w, const void* x, int64_t T, con
   return launch_bf16(x, wd, bias, y, T, b.R, b.C, (hipStream_t)stream);
 }
 
+size_t ep_linear_seq_workspace_bytes(const ep_blob* const* w, int n) {
+  if (!w || n < 1) return 0;
+  size_t mx = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!w[i]) return 0;
+    mx = std::max(mx, (size_t)w[i]->b.R * (size_t)w[i]->b.C * 2);
+  }
+  return 2 * ((mx + 255) & ~size_t(255)) + 256;
+}
+
+// Layers 0..n-1: decode i+1 on `side` while the GEMM of layer i runs on `main`.  Two
+// weight buffers alternate; decode i waits for the GEMM of layer i-2 (its buffer), the
+// GEMM of layer i for decode i.  The side stream starts after everything already queued
+// on main (inputs, earlier users of the workspace).
+int ep_compressed_linear_seq_forward(const ep_blob* const* w, int n, const void* const* x, int64_t T,
+                                     const void* const* bias, void* const* y, void* ws, size_t ws_bytes,
+                                     ep_stream main_s, ep_stream side_s) {
+  set_error("");
+  if (!w || !x || !y || !ws || n < 1) return fail(EP_E_ARG, "null pointer or empty sequence");
+  for (int i = 0; i < n; ++i) {
+    if (!w[i] || !x[i] || !y[i]) return fail(EP_E_ARG, "null blob, input or output");
+    if (w[i]->b.dtype != EP_BF16) return fail(EP_E_DTYPE, "compressed linear takes BF16 blobs");
+  }
+  const size_t need = ep_linear_seq_workspace_bytes(w, n);
+  if (ws_bytes < need) return fail(EP_E_WORKSPACE, "workspace too small");
+  const size_t half = (need - 256) / 2;
+  uint8_t* base = (uint8_t*)(((uintptr_t)ws + 255) & ~uintptr_t(255));
+  void* buf[2] = {base, base + half};
+  hipStream_t ms = (hipStream_t)main_s, ss = (hipStream_t)side_s;
+  hipEvent_t ev_start = nullptr, ev_dec[2] = {nullptr, nullptr}, ev_used[2] = {nullptr, nullptr};
+  int rc = EP_OK;
+  auto mk = [&](hipEvent_t* e) {
+    if (!rc) rc = hip_check(hipEventCreateWithFlags(e, hipEventDisableTiming), "event create");
+  };
+  mk(&ev_start);
+  for (int k = 0; k < 2; ++k) {
+    mk(&ev_dec[k]);
+    mk(&ev_used[k]);
+  }
+  if (!rc) rc = hip_check(hipEventRecord(ev_start, ms), "event record");
+  if (!rc) rc = hip_check(hipStreamWaitEvent(ss, ev_start, 0), "stream wait");
+  auto decode = [&](int i) {
+    const int k = i & 1;
+    if (i >= 2 && !rc) rc = hip_check(hipStreamWaitEvent(ss, ev_used[k], 0), "stream wait");
+    if (!rc) rc = ep_decompress(w[i], buf[k], side_s);
+    if (!rc) rc = hip_check(hipEventRecord(ev_dec[k], ss), "event record");
+  };
+  decode(0);
+  for (int i = 0; i < n && !rc; ++i) {
+    if (i + 1 < n) decode(i + 1);
+    const int k = i & 1;
+    if (!rc) rc = hip_check(hipStreamWaitEvent(ms, ev_dec[k], 0), "stream wait");
+    if (!rc) rc = launch_bf16(x[i], buf[k], bias ? bias[i] : nullptr, y[i], T, w[i]->b.R, w[i]->b.C, ms);
+    if (!rc) rc = hip_check(hipEventRecord(ev_used[k], ms), "event record");
+  }
+  // events may be destroyed while still pending; the runtime releases them when done
+  if (ev_start) (void)hipEventDestroy(ev_start);
+  for (int k = 0; k < 2; ++k) {
+    if (ev_dec[k]) (void)hipEventDestroy(ev_dec[k]);
+    if (ev_used[k]) (void)hipEventDestroy(ev_used[k]);
+  }
+  return rc;
+}
+
 }  // extern "C"
+

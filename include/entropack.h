@@ -123,6 +123,19 @@ int ep_compressed_linear_forward(const ep_blob* w, const void* dev_x, int64_t T,
                                  const void* dev_bias, void* dev_y,
                                  void* dev_ws, size_t ws_bytes, ep_stream stream);
 
+/* A sequence of compressed linear layers, y_i = x_i W_i^T (+ bias_i), i = 0..n-1
+ * ([README] 快速开始 layer(x), applied layer after layer as a model runs them; [ABS]:
+ * decoding cost grows with the weight count, so it should hide behind the GEMMs).
+ * The decode of layer i+1 runs on `side` while the GEMM of layer i runs on `main`; the
+ * two alternate between two weight buffers in dev_ws (>= ep_linear_seq_workspace_bytes
+ * bytes).  x[i] is T x cols_i, y[i] is T x rows_i, bias may be NULL or hold NULLs.
+ * The side stream first waits for the work already queued on `main`; all GEMMs run on
+ * `main`, so work queued on `main` afterwards sees every output.  Asynchronous. */
+size_t ep_linear_seq_workspace_bytes(const ep_blob* const* w, int n);
+int ep_compressed_linear_seq_forward(const ep_blob* const* w, int n, const void* const* dev_x, int64_t T,
+                                     const void* const* dev_bias, void* const* dev_y,
+                                     void* dev_ws, size_t ws_bytes, ep_stream main, ep_stream side);
+
 /* Plain BF16 "NT" GEMM on MFMA: y[T x N] = x[T x K] w[N x K]^T (+ bias[N]), fp32
  * accumulate, BF16 out.  The uncompressed baseline of the linear layer. */
 int ep_gemm_bf16_nt(const void* dev_x, const void* dev_w, const void* dev_bias,
@@ -142,7 +155,7 @@ int ep_blob_dtype(const ep_blob* blob);
 /* chains per tile, K_LOG2, flags (bit0 escapes present, bit1 clamping needed) */
 void ep_blob_params(const ep_blob* blob, int* chains_per_tile, int* k_log2, int* flags);
 
-/* Serialise (the blob v1 bytes; what a state_dict stores, [NEWS]) / deserialise
+/* Serialise (the blob v2 bytes; what a state_dict stores, [NEWS]) / deserialise
  * with full validation (EP_E_CORRUPT on any inconsistency). */
 size_t ep_serialized_size(const ep_blob* blob);
 int ep_serialize(const ep_blob* blob, void* host_dst, size_t capacity);

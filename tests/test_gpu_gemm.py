@@ -118,3 +118,51 @@ def test_python_api_module_and_state_dict():
     assert c.to_bytes() == blob_w
     _, ref_w, _ = oracle.decode(blob_w)
     assert np.array_equal(r.cpu().view(torch.int16).numpy().view(np.uint16), ref_w)
+
+
+def test_compressed_linear_sequence_overlapped():
+    """Layers run with the next layer's decode on a second stream: every output is
+    bit-identical to the one-layer path and within tolerance of the oracle GEMM."""
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    shapes = [(512, 768), (768, 512), (1024, 768), (768, 1024), (512, 768)]   # (rows = out, cols = in)
+    T = 200
+    dbs, xs, ys, refs, bs = [], [], [], [], []
+    for i, (R, C) in enumerate(shapes):
+        blob = oracle.compress(synth.rowscaled(R, C, 40 + i), nx.DT_BF16, 3.0 + 0.5 * i)
+        _, w_hat, _ = oracle.decode(blob)
+        x = synth.activations(T, C, 60 + i)
+        b = synth.f32_to_bf16_bits(np.linspace(-0.25, 0.25, R).astype(np.float32)) if i % 2 == 0 else None
+        dbs.append(DevBlob(blob))
+        xs.append(_t(x, torch.bfloat16))
+        bs.append(_t(b, torch.bfloat16) if b is not None else None)
+        ys.append(torch.empty((T, R), dtype=torch.bfloat16, device="cuda"))
+        refs.append(linear_ref(nx.bf16_to_f64(x), nx.bf16_to_f64(w_hat), nx.bf16_to_f64(b) if b is not None else None))
+    hs = [d.h for d in dbs]
+    need = L.ep_linear_seq_workspace_bytes(hs)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    say("linear sequence", len(shapes), T)
+    with pytest.raises(L.EPError):
+        L.ep_compressed_linear_seq_forward(hs, [x.data_ptr() for x in xs], T, [b.data_ptr() if b is not None else 0 for b in bs],
+                                           [y.data_ptr() for y in ys], ws.data_ptr(), need - 1, stream_ptr(),
+                                           int(side.cuda_stream))
+    for rep in range(2):
+        for y in ys:
+            y.zero_()
+        L.ep_compressed_linear_seq_forward(hs, [x.data_ptr() for x in xs], T, [b.data_ptr() if b is not None else 0 for b in bs],
+                                           [y.data_ptr() for y in ys], ws.data_ptr(), need, stream_ptr(),
+                                           int(side.cuda_stream))
+        torch.cuda.synchronize()
+        for i, (db, x, b, y, ref) in enumerate(zip(dbs, xs, bs, ys, refs)):
+            one = torch.empty_like(y)
+            n1 = L.ep_linear_workspace_bytes(db.h)
+            w1 = torch.empty(n1, dtype=torch.uint8, device="cuda")
+            L.ep_compressed_linear_forward(db.h, x.data_ptr(), T, b.data_ptr() if b is not None else 0, one.data_ptr(),
+                                           w1.data_ptr(), n1, stream_ptr())
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), one.view(torch.int16)), f"layer {i} differs from the one-layer path"
+            got = nx.bf16_to_f64(y.cpu().view(torch.int16).numpy().view(np.uint16))
+            assert rel_l2(got, ref) <= TOL
+    for db in dbs:
+        assert db.errors() == 0
