@@ -35,6 +35,8 @@ SIGNATURES = {
                                                 C.POINTER(_vp), _vp, _sz, _vp, _vp]),
     "ep_gemm_bf16_nt": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "ep_gemm_fp8_nt": (_int, [_vp, _vp, _flt, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "ep_plan_bitrates": (_int, [_int, _int, C.POINTER(_dbl), C.POINTER(_dbl), _dbl, C.POINTER(_int)]),
+    "ep_blob_distortion": (_int, [_vp, C.POINTER(_dbl), C.POINTER(_dbl)]),
     "ep_actual_bpp": (_dbl, [_vp]),
     "ep_blob_shape": (None, [_vp, C.POINTER(_i64), C.POINTER(_i64)]),
     "ep_blob_dtype": (_int, [_vp]),
@@ -143,6 +145,22 @@ def ep_gemm_bf16_nt(dev_x, dev_w, dev_bias, dev_y, T, N, K, stream=0):
 
 def ep_gemm_fp8_nt(dev_xq, dev_wq, a_x, dev_aw, dev_y, T, N, K, stream=0):
     check(lib().ep_gemm_fp8_nt(dev_xq, dev_wq, a_x, dev_aw, dev_y, T, N, K, stream))
+
+
+def ep_plan_bitrates(bits, cost, budget_bits):
+    """bits, cost: n x n_cand nested sequences. Returns the chosen candidate per matrix."""
+    n, m = len(bits), len(bits[0])
+    fb = (_dbl * (n * m))(*[float(v) for row in bits for v in row])
+    fc = (_dbl * (n * m))(*[float(v) for row in cost for v in row])
+    out = (_int * n)()
+    check(lib().ep_plan_bitrates(n, m, fb, fc, float(budget_bits), out))
+    return list(out)
+
+
+def ep_blob_distortion(blob: int):
+    e, r = _dbl(), _dbl()
+    check(lib().ep_blob_distortion(blob, C.byref(e), C.byref(r)))
+    return e.value, r.value
 
 
 def ep_actual_bpp(blob: int) -> float:

@@ -42,6 +42,12 @@ class Compressed:
         return L.ep_actual_bpp(self._h)
 
     @property
+    def distortion(self):
+        """(sum (w - h_r u)^2, sum w^2) of the lattice reconstruction, float64; known
+        only for blobs compressed in this process (EPError otherwise)."""
+        return L.ep_blob_distortion(self._h)
+
+    @property
     def nbytes(self) -> int:
         return L.ep_serialized_size(self._h)
 
@@ -88,6 +94,38 @@ def compress(x, target_bpp: float, dtype=None, chains_per_tile: int = 0) -> Comp
         raise EPError(-4, "lossy compression takes 2-D tensors only")
     h = L.ep_compress(ptr, ep_dt, host.shape[0], host.shape[1], float(target_bpp), chains_per_tile)
     return Compressed(h)
+
+
+def plan_bitrates(mats, budget_bpp: float, candidates=(2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0), weights=None,
+                  dtype=None, chains_per_tile: int = 0):
+    """Compress every matrix at one of ``candidates`` so that all of them together take
+    at most ``budget_bpp`` x (total parameters) stored bits and the summed cost
+    weight_i x squared reconstruction error is small (ep_plan_bitrates).
+
+    The default weights (all 1) minimise the stack's overall relative L2 error
+    sqrt(sum err / sum |W|^2).  Each matrix is compressed once per candidate to
+    measure (bits, error) and once more at its chosen target (the encoder is
+    deterministic, so the bits match).  Returns (list of Compressed, chosen targets).
+    """
+    mats = list(mats)
+    cands = [float(t) for t in candidates]
+    if weights is None:
+        weights = [1.0] * len(mats)
+    bits, cost, numel = [], [], 0
+    for x, wgt in zip(mats, weights):
+        row_b, row_c = [], []
+        for t in cands:
+            c = compress(x, t, dtype=dtype, chains_per_tile=chains_per_tile)
+            n = c.shape[0] * c.shape[1]
+            row_b.append(c.actual_bpp * n)
+            row_c.append(float(wgt) * c.distortion[0])
+            del c
+        bits.append(row_b)
+        cost.append(row_c)
+        numel += n
+    choice = L.ep_plan_bitrates(bits, cost, float(budget_bpp) * numel)
+    out = [compress(x, cands[j], dtype=dtype, chains_per_tile=chains_per_tile) for x, j in zip(mats, choice)]
+    return out, [cands[j] for j in choice]
 
 
 def decompress(c: Compressed, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

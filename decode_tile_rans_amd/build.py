@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libentropack_hip.so")
 BUILD = os.path.join(ROOT, "_build")
 
-HOST_SRCS = ["model.cpp", "encoder.cpp", "blob.cpp"]
+HOST_SRCS = ["model.cpp", "encoder.cpp", "blob.cpp", "plan.cpp"]
 HIP_SRCS = ["decode.hip", "gemm.hip"]
 ARCH = os.environ.get("EP_OFFLOAD_ARCH", "gfx950")
 

@@ -14,7 +14,6 @@
 namespace ep {
 
 const char* last_error_cstr();
-int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_req, std::vector<uint8_t>* out);
 
 namespace {
 template <class T>
@@ -117,7 +116,8 @@ int ep_compress_ex(const void* src, int dtype, int64_t rows, int64_t cols, doubl
   if (!out) return fail(EP_E_ARG, "null output pointer");
   *out = nullptr;
   std::vector<uint8_t> bytes;
-  int rc = ep::compress(src, dtype, rows, cols, target_bpp, S, &bytes);
+  Distortion dist;
+  int rc = ep::compress(src, dtype, rows, cols, target_bpp, S, &bytes, &dist);
   if (rc) return rc;
   ep_blob* blob = new (std::nothrow) ep_blob();
   if (!blob) return fail(EP_E_NOMEM, "out of host memory");
@@ -126,6 +126,7 @@ int ep_compress_ex(const void* src, int dtype, int64_t rows, int64_t cols, doubl
     delete blob;
     return rc;
   }
+  blob->b.dist = dist;
   *out = blob;
   return EP_OK;
 }

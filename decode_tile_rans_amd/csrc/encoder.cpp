@@ -414,7 +414,7 @@ void put_u64(std::vector<uint8_t>& b, size_t off, uint64_t v) { std::memcpy(&b[o
 }  // namespace
 
 int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_req,
-             std::vector<uint8_t>* out) {
+             std::vector<uint8_t>* out, Distortion* dist) {
   if (!src || !out) return fail(EP_E_ARG, "null pointer");
   if (dtype < EP_BF16 || dtype > EP_INT8) return fail(EP_E_DTYPE, "unsupported dtype");
   if (R < 1 || C < 1) return fail(EP_E_ARG, "rows and cols must be >= 1");
@@ -595,6 +595,32 @@ int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_r
   parallel_for(n_tiles, [&](int64_t b, int64_t e, int) {
     for (int64_t tt = b; tt < e; ++tt) schedule_tile(&chains[(size_t)(tt * S)], S);
   }, 16);
+
+  // ---- distortion of the lattice reconstruction fl32(h_r u) (before the container
+  // cast): per-row sums left to right, rows added in order
+  if (dist) {
+    std::vector<double> re((size_t)R, 0.0), rw((size_t)R, 0.0);
+    parallel_for(R, [&](int64_t b, int64_t e, int) {
+      for (int64_t r = b; r < e; ++r) {
+        const float h = mx.s[r] * delta;
+        double se = 0.0, sw = 0.0;
+        for (int64_t c = 0; c < C; ++c) {
+          const double w = mx.w[(size_t)(r * C + c)];
+          const double d = w - (double)(h * (float)u[(size_t)(r * mx.G * 8 + c)]);
+          se += d * d;
+          sw += w * w;
+        }
+        re[(size_t)r] = se;
+        rw[(size_t)r] = sw;
+      }
+    }, 16);
+    dist->sq_err = 0.0;
+    dist->sq_ref = 0.0;
+    for (int64_t r = 0; r < R; ++r) {
+      dist->sq_err += re[(size_t)r];
+      dist->sq_ref += rw[(size_t)r];
+    }
+  }
 
   // ---- saturation flag
   std::atomic<bool> sat{false};

@@ -71,6 +71,14 @@ extern const int32_t* log2q_table();   // floor(2^16 log2 f + 1/2), f in [0, 204
 //     neg | top2<<1 | (e-k)<<3 (escape)
 void build_slot_tables(const Model& m, uint32_t* out /* 7*2048 */, bool narrow);
 
+// Squared error of the lattice reconstruction fl32(h_r u) against the input, and the
+// input's squared norm (both over all rows x cols entries).
+struct Distortion {
+  double sq_err = -1.0, sq_ref = -1.0;
+};
+int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_req, std::vector<uint8_t>* out,
+             Distortion* dist);
+
 // Parsed blob (host side) + device mirror.
 struct Blob {
   std::vector<uint8_t> bytes;          // serialized form
@@ -84,6 +92,7 @@ struct Blob {
   uint32_t model_bytes = 0;
   Model model;
   std::vector<uint32_t> chain_len;     // words per chain
+  Distortion dist;                     // known for blobs made by ep_compress in this process
   // device mirror
   int device = -1;
   void* d_base = nullptr;              // one allocation

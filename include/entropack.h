@@ -147,6 +147,26 @@ int ep_gemm_bf16_nt(const void* dev_x, const void* dev_w, const void* dev_bias,
 int ep_gemm_fp8_nt(const void* dev_xq, const void* dev_wq, float a_x, const float* dev_aw,
                    void* dev_y, int64_t T, int64_t N, int64_t K, ep_stream stream);
 
+/* ---------------------------------------------------------------- budgeted bitrates
+ * [ABS] arbitrary target rates from sampled storage estimates; [README] 性能 / [NEWS]:
+ * whole-model packs at a fixed average rate.  ep_plan_bitrates spends a total bit
+ * budget over n matrices, each with n_cand measured candidates: bits[i*n_cand + j] =
+ * stored bits of matrix i at candidate j, cost[...] = the caller's weight x its squared
+ * reconstruction error (both finite, >= 0).  Lagrangian pick (per matrix the candidate
+ * minimising cost + lambda bits; ties: fewer bits, lower index; lambda = 0 or the
+ * smallest pick-changing value that fits, else every matrix at its fewest bits), then
+ * greedy upgrades by cost saved per extra bit while the budget allows (ties: lower
+ * matrix, lower candidate).  choice[i] (caller-owned, n ints) receives the candidate
+ * index of matrix i.  EP_E_ARG for null/empty/negative/non-finite input, EP_E_RANGE if
+ * even the smallest candidates exceed the budget.  Host only, deterministic. */
+int ep_plan_bitrates(int n, int n_cand, const double* bits, const double* cost, double budget_bits, int* choice);
+
+/* Squared error of the lattice reconstruction fl32(h_r u) (before the container cast)
+ * against the compressed input, and the input's squared norm, summed over all entries
+ * in double (row by row, left to right).  Known for blobs made by ep_compress in this
+ * process (EP_E_STATE otherwise). */
+int ep_blob_distortion(const ep_blob* blob, double* sq_err, double* sq_ref);
+
 /* ---------------------------------------------------------------- blob accessors
  * actual_bpp = 8 * serialized bytes / (rows * cols)  ([README]: includes metadata). */
 double ep_actual_bpp(const ep_blob* blob);

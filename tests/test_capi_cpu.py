@@ -148,3 +148,80 @@ def test_serialize_deserialize_and_corruption():
         assert e.value.name == "EP_E_CORRUPT"
         with pytest.raises(ValueError):
             oracle.parse_blob(bb)
+
+
+DIST_CASES = [c for c in CASES if c[0] in ("odd_37x13", "r512_8", "r512_2.3", "S8", "fp16", "fp32", "fp8", "int8",
+                                           "zeros", "low", "1x1")]
+
+
+@pytest.mark.parametrize("name,gen,dt,t,S", DIST_CASES, ids=[c[0] for c in DIST_CASES])
+def test_encoder_distortion_matches_oracle(name, gen, dt, t, S):
+    from oracle import plan
+    src = np.ascontiguousarray(gen())
+    h = L.ep_compress(src.ctypes.data, dt, src.shape[0], src.shape[1], t, S)
+    try:
+        e, r = L.ep_blob_distortion(h)
+        blob = L.ep_serialize(h)
+    finally:
+        L.ep_blob_free(h)
+    we, wr = plan.distortion(src, dt, blob)
+    assert e == pytest.approx(we, rel=1e-12, abs=1e-300) and r == pytest.approx(wr, rel=1e-12, abs=1e-300)
+    # a blob read back from bytes carries no source: the accessor says so
+    h2 = L.ep_deserialize(blob)
+    try:
+        with pytest.raises(L.EPError) as ei:
+            L.ep_blob_distortion(h2)
+        assert ei.value.name == "EP_E_STATE"
+    finally:
+        L.ep_blob_free(h2)
+
+
+def test_plan_bitrates_matches_oracle():
+    from oracle import plan
+    rng = np.random.default_rng(77)
+    for it in range(60):
+        n, m = int(rng.integers(1, 9)), int(rng.integers(1, 6))
+        bits = np.sort(rng.uniform(1.0, 10.0, size=(n, m)), axis=1) * rng.integers(100, 10 ** 6, size=(n, 1))
+        cost = np.sort(rng.uniform(0.0, 5.0, size=(n, m)), axis=1)[:, ::-1].copy()
+        cost[rng.random((n, m)) < 0.15] *= 3.0
+        if it % 5 == 0:                      # exact ties in bits and in cost
+            bits = np.round(bits / 1000.0) * 1000.0
+            cost = np.round(cost)
+        lo = sum(float(v) for v in bits.min(axis=1))        # in matrix order, as both sides add
+        hi = sum(float(v) for v in bits.max(axis=1))
+        for budget in np.linspace(lo, hi * 1.05, 7):
+            want = plan.plan(bits, cost, float(budget))
+            assert L.ep_plan_bitrates(bits.tolist(), cost.tolist(), float(budget)) == want, (it, budget)
+        with pytest.raises(L.EPError) as ei:
+            L.ep_plan_bitrates(bits.tolist(), cost.tolist(), lo * 0.999 - 1.0)
+        assert ei.value.name == "EP_E_RANGE"
+    with pytest.raises(L.EPError) as ei:
+        L.ep_plan_bitrates([[1.0, -2.0]], [[1.0, 0.5]], 10.0)
+    assert ei.value.name == "EP_E_ARG"
+
+
+def test_plan_bitrates_api_matches_oracle_pipeline():
+    # the whole pipeline (compress at every candidate, measure, plan, recompress) against
+    # the same steps done with the oracle encoder, bpp and distortion
+    import torch
+    from oracle import plan
+    import decode_tile_rans_amd as ep
+    from oracle.codec import actual_bpp
+    mats = [synth.rowscaled(96, 256, 41), synth.rowscaled(64, 320, 42, outlier_frac=0.01),
+            synth.rowscaled(128, 128, 43), synth.rowscaled(40, 200, 44)]
+    # matrices of different norms (exact power-of-two scalings): the squared error of the
+    # larger ones falls by more per bit, so they should get more bits
+    mats = [synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(m) * np.float32(f)) for m, f in zip(mats, (1, 8, 0.125, 1))]
+    cands = (2.0, 3.0, 4.0, 5.0)
+    budget = 3.2
+    got, targets = ep.plan_bitrates(mats, budget, cands, dtype=torch.bfloat16)
+    bits = [[actual_bpp(oracle.compress(m, nx.DT_BF16, t)) * m.size for t in cands] for m in mats]
+    cost = [[plan.distortion(m, nx.DT_BF16, oracle.compress(m, nx.DT_BF16, t))[0] for t in cands] for m in mats]
+    want = plan.plan(np.array(bits), np.array(cost), budget * sum(m.size for m in mats))
+    assert targets == [cands[j] for j in want]
+    assert sum(c.actual_bpp * m.size for c, m in zip(got, mats)) <= budget * sum(m.size for m in mats)
+    for c, m, j in zip(got, mats, want):
+        assert c.to_bytes() == oracle.compress(m, nx.DT_BF16, cands[j])
+    assert len(set(targets)) > 1            # the matrices differ enough to get different rates
+    # uniform 3.0 fits the same budget; the plan does better on the summed error
+    assert sum(cost[i][j] for i, j in enumerate(want)) < sum(cost[i][1] for i in range(len(mats)))
