@@ -178,7 +178,8 @@ __device__ inline void store_group(void* out, int64_t base, const float* vin, co
 constexpr int kMaxBatch = 12;
 constexpr int kRingWords = 32;                   // per-chain LDS ring (16-bit words)
 constexpr int kChunkWords = 8;                   // one 16-byte stream load
-constexpr int kChainRingBytes = kRingWords * 2;  // 64 B per chain
+constexpr int kMirrorBytes = 32;                 // copy of ring bytes 0..31 after the ring
+constexpr int kChainRingBytes = kRingWords * 2 + kMirrorBytes;  // 96 B per chain
 constexpr int kMaxWaves = 16;
 constexpr int kHrPad = 128;                      // zero row scales after the last row (prefetch slack)
 static_assert(kRingWords - kChunkWords >= 17, "ring too small for two groups plus a chunk");
@@ -230,8 +231,12 @@ struct EntryLayout {
 // order its chains request them (positions handed out by a ballot in chain order, the
 // tile's cursor advancing by 8 words per chunk), then every chain's last short piece
 // (tail).  Each chain keeps its words in a 32-word LDS ring: word i at ring byte
-// 2 (i mod 32), so chunk n fills ring bytes 16 (n mod 4) .. +15.  Counters are kept in
-// bytes (2 per word): fb = fetched (a chunk in flight included), a2 = consumed.
+// 2 (i mod 32), so chunk n fills ring bytes 16 (n mod 4) .. +15; chunks 0 and 1 of the
+// ring are also written to bytes 64..95 (a mirror), so that a reader may run up to 16
+// words past the ring's end without wrapping.  Counters are kept in bytes (2 per word):
+// fb = fetched (a chunk in flight included), a2 = consumed.  The escape-free groups of a
+// pair read through a linear pointer ra (set from a2 at the pair's start, a2 brought
+// up to date at its end); escape replays and fetches work on a2.
 // Fetches happen only at these sites, exactly as the encoder's schedule assumed:
 //   prime: until 17 ahead;  every even group: until 17 ahead, then one round for
 //   chains at most 24 ahead (a 16-byte load issued now, written to the ring two groups
@@ -241,9 +246,11 @@ struct EntryLayout {
 // chain only reads words already in its ring; it never holds more than 32 words ahead.
 struct Chain {
   uint32_t x;        // rANS state
-  uint32_t a2;       // 2 x words consumed
+  uint32_t a2;       // 2 x words consumed (behind by the pair's reads until its end)
+  uint32_t ra;       // LDS byte address of the next word within a group pair (unwrapped)
+  uint32_t d;        // a2 - ra at the pair's start
   uint32_t nw;       // the next word, already read from the ring
-  uint32_t rb;       // LDS byte address of the ring (64-byte aligned)
+  uint32_t rb;       // LDS byte address of the ring (16-byte aligned)
   uint32_t fb;       // 2 x words fetched
   int32_t rem;       // words not fetched yet
   uint32_t cur;      // the tile's main-area cursor (word index; equal on the tile's lanes)
@@ -253,6 +260,7 @@ struct Chain {
   uint4 pend;        // chunk in flight
   uint32_t pend_at;  // its ring address
   bool have_pend;
+  bool pend_mirror;  // it also goes to the mirror
 };
 
 struct StreamRef {
@@ -277,8 +285,19 @@ __device__ __forceinline__ void lds_st128(uint32_t a, uint4 d) {
   *(EP_LDS u32x4*)(uintptr_t)a = v;
 }
 
-__device__ __forceinline__ uint32_t ch_word(const Chain& r) { return lds_u16((r.a2 & 62u) | r.rb); }
-__device__ __forceinline__ void ch_put(const Chain& r, uint4 d) { lds_st128((r.fb & 48u) | r.rb, d); }
+__device__ __forceinline__ uint32_t ch_word(const Chain& r) { return lds_u16((r.a2 & 62u) + r.rb); }
+__device__ __forceinline__ void ch_put(const Chain& r, uint4 d) {
+  const uint32_t o = r.fb & 48u;
+  lds_st128(r.rb + o, d);
+  if (o < (uint32_t)kMirrorBytes) lds_st128(r.rb + o + 2u * kRingWords, d);
+}
+// start of a group pair: the linear read pointer from the consumed count
+__device__ __forceinline__ void ch_linear(Chain& r) {
+  r.ra = r.rb + (r.a2 & 62u);
+  r.d = r.a2 - r.ra;
+}
+// end of a group pair: the consumed count from the linear read pointer
+__device__ __forceinline__ void ch_settle(Chain& r) { r.a2 = r.ra + r.d; }
 // Positions for one round of requests: full chunks take the tile's next main-area
 // slots in lane (= chain) order, a tail sits at its own place.
 __device__ __forceinline__ uint32_t ch_claim(Chain& r, bool want, bool& full) {
@@ -318,9 +337,71 @@ __device__ __forceinline__ void ch_sync(const StreamRef& s, Chain& r, bool cand,
     }
   }
 }
+// Prime: the rounds of a sync site to 17 ahead from an empty ring.  Three rounds always
+// suffice (each request adds 8 words, or the tail, after which the chain wants no more),
+// and request positions do not depend on the data, so all loads are issued before the
+// first is written: one memory latency instead of three.
+// (Full chunks load unconditionally, lanes without one reading the stream's first
+// chunk, so that no loaded value is merged before its wait; a tail, at most one per
+// chain and rare, is fetched after the rounds.)
+struct PrimeLoads {
+  uint4 dat[3];
+  uint32_t at[3];
+  bool put[3], mir[3];
+  uint32_t t_at, t_pos;
+  bool t_has, t_mir;
+};
+__device__ __forceinline__ void ch_prime_issue(const StreamRef& s, Chain& r, bool cand, PrimeLoads& P) {
+  uint4* dat = P.dat;
+  uint32_t* at = P.at;
+  bool* put = P.put;
+  bool* mir = P.mir;
+  uint32_t t_at = 0u, t_pos = 0u;
+  bool t_has = false, t_mir = false;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const bool want = cand && (int32_t)(r.fb - r.a2) < 2 * 17 && r.rem > 0;
+    bool full;
+    const uint32_t pos = ch_claim(r, want, full);
+    const uint32_t o = r.fb & 48u;
+    at[k] = r.rb + o;
+    put[k] = full;
+    mir[k] = full && o < (uint32_t)kMirrorBytes;
+    dat[k] = ld_chunk(s, full ? pos : 0u);
+    if (want && !full) {
+      t_has = true;
+      t_at = r.rb + o;
+      t_pos = pos;
+      t_mir = o < (uint32_t)kMirrorBytes;
+    }
+    if (want) {
+      const int32_t n = full ? kChunkWords : r.rem;
+      r.fb += 2u * (uint32_t)n;
+      r.rem -= n;
+    }
+  }
+  P.t_at = t_at;
+  P.t_pos = t_pos;
+  P.t_has = t_has;
+  P.t_mir = t_mir;
+}
+__device__ __forceinline__ void ch_prime_finish(const StreamRef& s, const PrimeLoads& P) {
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    if (P.put[k]) lds_st128(P.at[k], P.dat[k]);
+    if (P.mir[k]) lds_st128(P.at[k] + 2u * kRingWords, P.dat[k]);
+  }
+  if (P.t_has) {
+    const uint4 d = ld_tail(s, P.t_pos);
+    lds_st128(P.t_at, d);
+    if (P.t_mir) lds_st128(P.t_at + 2u * kRingWords, d);
+  }
+}
 __device__ __forceinline__ void ch_flush(Chain& r) {
   if (r.have_pend) lds_st128(r.pend_at, r.pend);
+  if (r.pend_mirror) lds_st128(r.pend_at + 2u * kRingWords, r.pend);
   r.have_pend = false;
+  r.pend_mirror = false;
 }
 // Service at every even group: write the chunk in flight, top up to 17 ahead, then one
 // round for chains at most 24 ahead.  Full chunks load asynchronously with a fixed
@@ -340,7 +421,8 @@ __device__ __forceinline__ void ch_service(const StreamRef& s, Chain& r, bool ac
       r.rem = 0;
     }
   }
-  r.pend_at = (r.fb & 48u) | r.rb;
+  r.pend_at = (r.fb & 48u) + r.rb;
+  r.pend_mirror = full && (r.fb & 32u) == 0u;
   r.pend = ld_chunk(s, full ? pos : 0u);
   if (full) {
     r.fb += 2u * kChunkWords;
@@ -356,6 +438,14 @@ __device__ __forceinline__ void ch_renorm_if(Chain& r, bool need) {
   }
 }
 __device__ __forceinline__ void ch_renorm(Chain& r) { ch_renorm_if(r, r.x < kL); }
+// the same within a group pair's escape-free groups, through the linear pointer
+__device__ __forceinline__ void ch_renorm_lin_if(Chain& r, bool need) {
+  if (need) {
+    r.x = (r.x << 16) | r.nw;
+    r.ra += 2u;
+    r.nw = lds_u16(r.ra);
+  }
+}
 // Renormalise ILP chains: all conditions first, so that no chain's state update is
 // sunk below another chain's (conditional) ring read.
 template <int ILP>
@@ -368,7 +458,7 @@ __device__ __forceinline__ void ch_renorm_all(Chain* rd) {
     need[c] = rd[c].x < kL;
   }
 #pragma unroll
-  for (int c = 0; c < ILP; ++c) ch_renorm_if(rd[c], need[c]);
+  for (int c = 0; c < ILP; ++c) ch_renorm_lin_if(rd[c], need[c]);
 }
 // table entry of the chain's next symbol; `base` = byte offset of the table in LDS
 __device__ __forceinline__ uint32_t ch_entry(uint32_t base, const Chain& r) {
@@ -402,14 +492,20 @@ __device__ __forceinline__ int32_t ch_escape(Chain& r, uint32_t e, int k, int la
   const int32_t uu = (int32_t)(2u * m + (uint32_t)c);
   return neg ? -uu : uu;
 }
-// Byte offsets of the tables in LDS: FIRST at 0, FREE[c] at (1 + c) 8 KB, LAST[c][pi]
-// at (3 + 2c + pi) 8 KB.  The coset of a FIRST entry is bit 22 of every layout.
-__device__ __forceinline__ uint32_t free_base(uint32_t e_first) { return ((e_first >> 9) & 0x2000u) + 0x2000u; }
+// Byte offsets of the tables in LDS (8 KB each): FREE[0] at 0, FIRST at 8 KB, FREE[1] at
+// 16 KB, LAST[c][pi] at (3 + 2c + pi) 8 KB = FREE[c] + 24 KB + pi 8 KB, so the LAST
+// address is the FREE address of the same state plus a constant and the parity bit.
+// The coset of a FIRST entry is bit 22 of every layout.
+constexpr uint32_t kFirstOff = 0x2000u;
+constexpr uint32_t kLastOff = 0x6000u;
+__device__ __forceinline__ uint32_t free_base(uint32_t e_first) { return (e_first >> 8) & 0x4000u; }
+// LDS table slot of stored table t (stored order FIRST, FREE[0], FREE[1], LAST...)
+__host__ __device__ constexpr int lds_table_slot(int t) { return t == 0 ? 1 : (t == 1 ? 0 : t); }
 // careful decode of one group (the chain's state is at the group's start and 24 words
 // are in its ring): FIRST, six FREE, LAST, escapes with their raw bits
 template <class LY>
 __device__ __forceinline__ void ch_group_careful(uint32_t lds0, Chain& r, int k, int32_t* u) {
-  uint32_t ee = ch_entry(lds0, r);
+  uint32_t ee = ch_entry(lds0 + kFirstOff, r);
   ch_advance(r, ee);
   const uint32_t fb = free_base(ee);
   u[0] = (ee & LY::kEsc) ? ch_escape<LY>(r, ee, k, 0, 0) : LY::u_of(ee);
@@ -421,10 +517,44 @@ __device__ __forceinline__ void ch_group_careful(uint32_t lds0, Chain& r, int k,
     pp ^= u[i] >> 1;
   }
   const int pi = pp & 1;
-  ee = ch_entry(lds0 + 2u * fb + 0x2000u + ((uint32_t)pi << 13), r);
+  ee = ch_entry(lds0 + fb + kLastOff + ((uint32_t)pi << 13), r);
   ch_advance(r, ee);
   u[7] = (ee & LY::kEsc) ? ch_escape<LY>(r, ee, k, 1, pi) : LY::u_of(ee);
 }
+
+// Stages a job's decode tables into LDS (stored order FIRST, FREE[0], ...; in LDS the
+// first two swap places).  issue() starts four 16-byte loads per thread, commit()
+// stores them (and does the rest on small workgroups), then waits at the workgroup
+// barrier; the first block's stream loads go out in between, so a starting workgroup
+// waits about one memory latency for both.
+struct TabStager {
+  static constexpr int kQ = kM / 4;   // uint4 per table
+  static constexpr int kN = kTabWords / 4;
+  const uint4* src;
+  uint4* dst;
+  int tid, nt;
+  uint4 v[4];
+  // (indices past the end are clamped to the last element, which then is loaded and
+  // stored by several threads with the same value: no conditional stores, so the
+  // loads stay where they are issued)
+  __device__ void issue() {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = k * nt + tid;
+      v[k] = src[i < kN ? i : kN - 1];
+    }
+  }
+  __device__ void put(int i, uint4 d) { dst[i < 2 * kQ ? (i ^ kQ) : i] = d; }
+  __device__ void commit() {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = k * nt + tid;
+      put(i < kN ? i : kN - 1, v[k]);
+    }
+    for (int i = 4 * nt + tid; i < kN; i += nt) put(i, src[i]);
+    __syncthreads();
+  }
+};
 
 // Row scale of a chain's groups.  A chain's groups are g0, g0 + S, g0 + 2S, ...  When
 // S <= G (the row length in groups) consecutive ones are at most one row apart, so the
@@ -492,15 +622,15 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
   using LY = EntryLayout<NARROW>;
   const DecJob& J = *X.J;
   // ---- fast path: eight symbols per chain, no escape handling
-  uint32_t xs[ILP], a2s[ILP], nws[ILP];
+  uint32_t xs[ILP], ras[ILP], nws[ILP];
   uint32_t e[ILP][8];
   uint32_t fbs[ILP];
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
     xs[c] = rd[c].x;
-    a2s[c] = rd[c].a2;
+    ras[c] = rd[c].ra;
     nws[c] = rd[c].nw;
-    e[c][0] = ch_entry(X.lds0, rd[c]);
+    e[c][0] = ch_entry(X.lds0 + kFirstOff, rd[c]);
   }
   // per step: every chain's table read, then every chain's state update, then the
   // renormalisations (whose ring reads are conditional and so end the step's LDS batch)
@@ -522,7 +652,7 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
   for (int c = 0; c < ILP; ++c) {
     // LAST[c][pi]: pi = parity of the seven floor(u/2), one bit of each entry
     const uint32_t par = xor3(xor3(e[c][1], e[c][2], e[c][3]), xor3(e[c][4], e[c][5], e[c][6]), e[c][0]);
-    const uint32_t lb = 2u * fbs[c] - X.lds0 + 0x2000u + ((par >> (LY::kPar - 13)) & 0x2000u);
+    const uint32_t lb = fbs[c] + kLastOff + (((par >> LY::kPar) & 1u) << 13);
     e[c][7] = ch_entry(lb, rd[c]);
   }
 #pragma unroll
@@ -547,7 +677,7 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
         // replay the group from its start, fetch back to 17 ahead
         if (slow) {
           rd[c].x = xs[c];
-          rd[c].a2 = a2s[c];
+          rd[c].a2 = ras[c] + rd[c].d;
           ch_flush(rd[c]);
         }
         ch_sync(X.sref, rd[c], slow, 2 * 24);
@@ -558,6 +688,7 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
           for (int i = 0; i < 8; ++i) w[i] = rs[c].h * (float)u[i];
         }
         ch_sync(X.sref, rd[c], slow, 2 * 17);
+        if (slow) ch_linear(rd[c]);
       }
     }
     if (act) {
@@ -576,7 +707,7 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
     for (int c = 0; c < ILP; ++c) {
       if (kk >= ngr[c]) {
         rd[c].x = xs[c];
-        rd[c].a2 = a2s[c];
+        rd[c].ra = ras[c];
         rd[c].nw = nws[c];
       }
     }
@@ -590,7 +721,8 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
 // blk_end): lane l runs chain l of each, the ILP chains interleaved step by step so
 // that one chain's table read is in flight while another computes.
 template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
-__device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, int64_t blk_end, int lane, int wave) {
+__device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, int64_t blk_end, int lane, int wave,
+                                              TabStager& st, bool stage) {
   const DecJob& J = *X.J;
   const int S = X.S;
   const uint32_t G = X.G;
@@ -633,6 +765,9 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
     r.pend = make_uint4(0u, 0u, 0u, 0u);
     r.pend_at = rb;
     r.have_pend = false;
+    r.pend_mirror = false;
+    r.ra = rb;
+    r.d = 0u;
     const bool any = ngr[c] > 0;
     const int64_t gg = (t << 9) + j;
     g0[c] = any ? (uint32_t)gg : 0u;
@@ -661,9 +796,23 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
     q.hn = *q.pn;
     optr[c] = (char*)J.out + (live[c] ? gg * 8 * ESZ : 0);   // C % 8 == 0: groups are contiguous
   }
+  // (the workgroup's first blocks: table loads, then stream loads, then table stores
+  // and the barrier, then ring stores)
+  // (both branches leave the same loads in flight, the stream loads, so that the wait
+  // counts after them need not assume the table loads outstanding)
+  PrimeLoads pl[ILP];
+  if (stage) {
+    st.issue();
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) ch_prime_issue(X.sref, rd[c], live[c], pl[c]);
+    st.commit();
+  } else {
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) ch_prime_issue(X.sref, rd[c], live[c], pl[c]);
+  }
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
-    ch_sync(X.sref, rd[c], live[c], 2 * 17);   // prime
+    ch_prime_finish(X.sref, pl[c]);
     rd[c].nw = ch_word(rd[c]);
   }
   int nmax = ngr[0];
@@ -676,12 +825,17 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
   for (int kk = 0; kk < nmax; kk += 2) {
     row_scale<ILP>(X, kk, rs, ngr);
 #pragma unroll
-    for (int c = 0; c < ILP; ++c) ch_service(X.sref, rd[c], (ILP == 1) || kk < ngr[c]);
+    for (int c = 0; c < ILP; ++c) {
+      ch_service(X.sref, rd[c], (ILP == 1) || kk < ngr[c]);
+      ch_linear(rd[c]);
+    }
     decode_group<OUT, ESC, C8, NARROW, ILP>(X, kk, rd, rs, ngr, g0, optr);
     if (kk + 1 < nmax) {
       row_scale<ILP>(X, kk + 1, rs, ngr);
       decode_group<OUT, ESC, C8, NARROW, ILP>(X, kk + 1, rd, rs, ngr, g0, optr);
     }
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) ch_settle(rd[c]);
   }
 #pragma unroll
   for (int c = 0; c < ILP; ++c)
@@ -707,13 +861,14 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   const int64_t wg_blk0 = J.block_lo + ((int64_t)blockIdx.x - J.wg_begin) * B.bpw;
   const int64_t wg_blk1 = wg_blk0 + B.bpw < J.n_blocks ? wg_blk0 + B.bpw : J.n_blocks;
 
-  // stage the decode tables (shared by the workgroup's waves)
-  {
-    const uint4* src = (const uint4*)J.tab;
-    uint4* dst = (uint4*)smem;
-    for (int i = tid; i < kTabWords / 4; i += blockDim.x) dst[i] = src[i];
-  }
-  __syncthreads();
+  // the decode tables, shared by the workgroup's waves: staged during each wave's
+  // first block (every wave passes the stager's barrier exactly once)
+  static_assert(lds_table_slot(0) == 1 && lds_table_slot(1) == 0 && lds_table_slot(2) == 2, "");
+  TabStager st;
+  st.src = (const uint4*)J.tab;
+  st.dst = (uint4*)smem;
+  st.tid = tid;
+  st.nt = (int)blockDim.x;
 
   GroupCtx X;
   X.J = &J;
@@ -722,8 +877,14 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   X.S = 1 << J.log2S;
   X.G = (uint32_t)J.G;
   X.rowwise = (uint32_t)X.S <= X.G;
-  for (int64_t b = wg_blk0 + (int64_t)wave * ILP; b < wg_blk1; b += (int64_t)nwaves * ILP)
-    decode_blocks<OUT, ESC, C8, NARROW, ILP>(X, b, wg_blk1, lane, wave);
+  int64_t b = wg_blk0 + (int64_t)wave * ILP;
+  if (b >= wg_blk1) {   // a wave without blocks still stages its share
+    st.issue();
+    st.commit();
+    return;
+  }
+  for (bool first = true; b < wg_blk1; b += (int64_t)nwaves * ILP, first = false)
+    decode_blocks<OUT, ESC, C8, NARROW, ILP>(X, b, wg_blk1, lane, wave, st, first);
 }
 
 // ---------------------------------------------------------------- launch helpers
@@ -838,8 +999,8 @@ int cu_count() {
 }
 
 // Launch shape.  One table copy (56 KB of LDS) serves the workgroup and each chain adds
-// a 64-byte ring, so a workgroup holds at most 16 waves of one chain per lane or 13 of
-// two.  A launch of at least one full round (every CU a workgroup of 16 waves) gives each
+// a 96-byte ring (with its mirror), so a workgroup holds at most 16 waves of one chain
+// per lane or 8 of two.  A launch of at least one full round (every CU a workgroup of 16 waves) gives each
 // wave one block: all waves of a workgroup finish together, the 4 SIMDs carry equal
 // work, and a launch queued on another stream fills the CUs the last round leaves idle.
 // A smaller launch spreads its blocks evenly over at most one workgroup per CU (`bpw`
@@ -982,20 +1143,25 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
     (void)hipGetLastError();
     return fail(EP_E_NOMEM, "device allocation failed");
   }
-  int rc = hip_check(hipMemcpyAsync(d, host.data(), total, hipMemcpyHostToDevice, (hipStream_t)stream), "upload");
-  if (!rc) rc = hip_check(hipStreamSynchronize((hipStream_t)stream), "upload sync");
-  if (rc) {
-    (void)hipFree(d);
-    return rc;
-  }
-  (void)hipGetDevice(&b.device);
-  b.d_base = d;
   uint8_t* p = (uint8_t*)d;
   b.d_tab = (const uint32_t*)(p + o_tab);
   b.d_hr = (const float*)(p + o_hr);
   b.d_chain = (const uint32_t*)(p + o_ch);
   b.d_err = (uint32_t*)(p + o_err);
   b.d_stream = (const uint16_t*)(p + o_stream);
+  int rc = hip_check(hipMemcpyAsync(d, host.data(), total, hipMemcpyHostToDevice, (hipStream_t)stream), "upload");
+  if (!rc) rc = hip_check(hipStreamSynchronize((hipStream_t)stream), "upload sync");
+  if (rc) {
+    (void)hipFree(d);
+    b.d_tab = nullptr;
+    b.d_hr = nullptr;
+    b.d_chain = nullptr;
+    b.d_err = nullptr;
+    b.d_stream = nullptr;
+    return rc;
+  }
+  (void)hipGetDevice(&b.device);
+  b.d_base = d;
   return EP_OK;
 }
 
@@ -1025,9 +1191,8 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
   set_error("");
   if (n < 0 || (n > 0 && (!blobs || !dsts))) return fail(EP_E_ARG, "null pointer");
   if (n == 0) return EP_OK;
-  // all blobs of one launch share the container kind and the escape path
+  // all blobs of one call share the container kind
   int out = -1;
-  bool esc = false, c8 = true;
   for (int i = 0; i < n; ++i) {
     if (!blobs[i] || !dsts[i]) return fail(EP_E_ARG, "null blob or destination");
     const Blob& b = blobs[i]->b;
@@ -1039,16 +1204,22 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
     else if ((out == OUT_BF16 || out == OUT_BF16_SAT) && (o == OUT_BF16 || o == OUT_BF16_SAT))
       out = (out == OUT_BF16_SAT || o == OUT_BF16_SAT) ? OUT_BF16_SAT : OUT_BF16;
     else if (o != out) return fail(EP_E_ARG, "batch mixes container dtypes");
-    esc |= (b.flags & kFlagEsc) != 0;
-    c8 &= (b.C % 8) == 0;
   }
-  // blobs whose tables use the narrow / wide entry layout go to separate launches,
-  // each of up to kMaxBatch blobs with its own launch shape
-  for (int pass = 0; pass < 2; ++pass) {
-    const bool narrow = pass == 0;
+  // Blobs go to separate launches by table layout (narrow / wide entries) and by
+  // whether they hold escapes (the kernel without the escape path is faster), each of
+  // up to kMaxBatch blobs with its own launch shape.
+  for (int pass = 0; pass < 4; ++pass) {
+    const bool narrow = pass < 2;
+    const bool pesc = (pass & 1) != 0;
     std::vector<int> idx;
-    for (int i = 0; i < n; ++i)
-      if ((blobs[i]->b.k <= 6) == narrow) idx.push_back(i);
+    bool pc8 = true;
+    for (int i = 0; i < n; ++i) {
+      const Blob& b = blobs[i]->b;
+      if ((b.k <= 6) == narrow && ((b.flags & kFlagEsc) != 0) == pesc) {
+        idx.push_back(i);
+        pc8 &= (b.C % 8) == 0;
+      }
+    }
     for (size_t i0 = 0; i0 < idx.size(); i0 += kMaxBatch) {
       DecBatch B{};
       B.n = (int)std::min<size_t>(kMaxBatch, idx.size() - i0);
@@ -1062,7 +1233,7 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
         B.j[q].wg_begin = wg;
         wg += (B.j[q].n_blocks + sh.bpw - 1) / sh.bpw;
       }
-      int rc = launch_any(out, esc, c8, narrow, sh, B, wg, (hipStream_t)stream);
+      int rc = launch_any(out, pesc, pc8, narrow, sh, B, wg, (hipStream_t)stream);
       if (rc) return rc;
     }
   }

@@ -205,6 +205,106 @@ def test_batch_matches_single():
         assert d.errors() == 0
 
 
+def _batch_parity(cases, env, label):
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    from gpu_util import stream_ptr
+    dbs, refs = [], []
+    for (src, dt, t, S) in cases:
+        blob = oracle.compress(src, dt, t, chains_per_tile=S)
+        dbs.append(DevBlob(blob))
+        refs.append(oracle.decode(blob)[1])
+    outs = [d.empty_out(0x5A) for d in dbs]
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update(env)
+    try:
+        say(label, "batch of", len(dbs), "blocks", sum(oracle.parse_blob(d.data).n_blocks for d in dbs))
+        L.ep_decompress_batch([d.h for d in dbs], [o.data_ptr() for o in outs], stream_ptr())
+        torch.cuda.synchronize()
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    for i, (d, o, r) in enumerate(zip(dbs, outs, refs)):
+        assert np.array_equal(to_np(o, d.dt).view(np.uint8), r.view(np.uint8)), (label, i)
+        assert d.errors() == 0, (label, i)
+
+
+# Batches: blobs with and without escapes and with narrow and wide tables go to separate
+# launches of at most 12 blobs; small and ragged blobs, containers, more blobs than
+# one launch holds.
+def test_batch_small_and_ragged():
+    cases = [(synth.rowscaled(R, C, 800 + i), nx.DT_BF16, t, S)
+             for i, (R, C, t, S) in enumerate([(37, 13, 4.0, None), (256, 512, 3.0, 8), (1, 8, 4.0, 1),
+                                               (129, 1000, 4.5, 8), (64, 64, 1.0, 1), (300, 300, 2.3, 8)])]
+    _batch_parity(cases, {}, "batch small")
+
+
+def test_batch_many_shapes():
+    rng = np.random.default_rng(7)
+    cases = []
+    for i in range(24):
+        R, C = int(rng.integers(64, 700)), int(rng.choice([256, 520, 1024, 1032]))
+        cases.append((synth.rowscaled(R, C, 820 + i), nx.DT_BF16, float(rng.choice([2.3, 3.0, 4.0, 5.0])),
+                      int(rng.choice([1, 2, 4, 8]))))
+    _batch_parity(cases, {}, "batch shapes")
+
+
+def test_batch_escapes_and_wide_tables():
+    cases = [(synth.rowscaled(256, 512, 840), nx.DT_BF16, 8.0, 8), (synth.rowscaled(512, 1024, 841, 0.001),
+             nx.DT_BF16, 4.0, 8), (synth.rowscaled(256, 512, 842), nx.DT_BF16, 11.0, 8),
+             (synth.rowscaled(200, 536, 843), nx.DT_BF16, 3.0, 2), (synth.rowscaled(128, 1024, 844), nx.DT_BF16, 9.0, 4)]
+    _batch_parity(cases, {}, "batch escapes")
+
+
+@pytest.mark.parametrize("dt", [nx.DT_FP16, nx.DT_FP32, nx.DT_FP8, nx.DT_INT8])
+def test_batch_containers(dt):
+    if dt == nx.DT_FP8:
+        mk = lambda i: synth.fp8_codes(256, 520, 850 + i)[0]
+    elif dt == nx.DT_INT8:
+        mk = lambda i: synth.int8_codes(256, 520, 850 + i)[0]
+    elif dt == nx.DT_FP16:
+        mk = lambda i: synth.rowscaled_f32(256, 520, 850 + i).astype(np.float16).view(np.uint16)
+    else:
+        mk = lambda i: synth.rowscaled_f32(256, 264, 850 + i)
+    cases = [(mk(i), dt, 4.0 + i, 8) for i in range(3)]
+    _batch_parity(cases, {}, f"batch dt {dt}")
+
+
+def test_batch_more_blobs_than_one_launch():
+    cases = [(synth.rowscaled(16 + i % 5, 64 + 8 * (i % 7), 900 + i), nx.DT_BF16, 4.0, 1) for i in range(170)]
+    _batch_parity(cases, {}, "batch 170 blobs")
+
+
+def test_budgeted_mixed_rate_stack():
+    # a stack planned under one bit budget (matrices of different norms get different
+    # targets) decodes in one batch launch, every matrix bit-exact with the oracle
+    import torch
+    import decode_tile_rans_amd as ep
+    from decode_tile_rans_amd import _lib as L
+    from gpu_util import stream_ptr
+    shapes = [(256, 512, 1.0), (128, 1024, 8.0), (300, 200, 0.125), (64, 2048, 2.0), (512, 256, 0.5),
+              (96, 640, 4.0), (200, 384, 0.25), (128, 128, 16.0)]
+    mats = [synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(synth.rowscaled(R, C, 900 + i)) * np.float32(f))
+            for i, (R, C, f) in enumerate(shapes)]
+    cs, targets = ep.plan_bitrates(mats, 3.0, (2.0, 2.5, 3.0, 3.5, 4.0, 5.0), dtype=torch.bfloat16)
+    say("mixed-rate stack, targets", targets)
+    assert len(set(targets)) >= 3
+    assert sum(c.actual_bpp * m.size for c, m in zip(cs, mats)) <= 3.0 * sum(m.size for m in mats)
+    refs = []
+    for m, t, c in zip(mats, targets, cs):
+        blob = oracle.compress(m, nx.DT_BF16, t)
+        assert c.to_bytes() == blob
+        refs.append(oracle.decode(blob)[1])
+    outs = ep.decompress_batch(cs)
+    torch.cuda.synchronize()
+    for c, o, r in zip(cs, outs, refs):
+        assert np.array_equal(to_np(o, nx.DT_BF16), r)
+        assert c.device_errors() == 0
+
+
 def test_corrupt_stream_flags_error():
     src = synth.rowscaled(256, 1024, 13)
     blob = bytearray(oracle.compress(src, nx.DT_BF16, 4.0, chains_per_tile=8))
