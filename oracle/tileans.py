@@ -14,7 +14,8 @@ rANS machinery as the lossy blob (``codec``, ``rans``, ``layout``):
   tiles of 512 groups (4096 bytes), S chains per tile (8 when the tensor has
   at least 2^22 bytes, else 1), chain j of a tile decoding its groups j, j+S,
   ... exactly as for the lossy coordinates;
-* a byte's context is its position inside its element (byte index mod E); each
+* a byte's context is its position inside its element, at most 4 contexts
+  (byte index mod min(E, 4): an 8-byte element shares them), each
   context has a table over the 256 byte values: Q(counts, 2048) of ``model``
   over all of the context's bytes (padding included), unless the coded size
   estimated with LOG2Q plus the 4096 bits of the stored table is not below the
@@ -58,6 +59,10 @@ TILE_LOG2 = 12
 ELEM_SIZES = (1, 2, 4, 8)
 
 
+def n_contexts(E: int) -> int:
+    return min(E, 4)
+
+
 class TileAnsError(ValueError):
     pass
 
@@ -79,11 +84,12 @@ def default_chains_per_tile(n_bytes: int) -> int:
 
 
 def context_tables(padded: np.ndarray, E: int):
-    """(F (E, 256), uniform mask): Q-quantised counts or uniform per context."""
-    F = np.zeros((E, 256), dtype=np.int64)
+    """(F (contexts, 256), uniform mask): Q-quantised counts or uniform per context."""
+    nc = n_contexts(E)
+    F = np.zeros((nc, 256), dtype=np.int64)
     mask = 0
-    for p in range(E):
-        counts = np.bincount(padded[p::E], minlength=256).astype(np.int64)
+    for p in range(nc):
+        counts = np.bincount(padded[p::nc], minlength=256).astype(np.int64)
         f = quantize_freqs(counts, np.arange(256), M)
         used = counts > 0
         # (the stored table, 256 x 16 bits, counts against the coded side)
@@ -114,7 +120,7 @@ def compress(raw, E: int, dims, dtype_tag: int = 0, chains_per_tile=None) -> byt
     F, mask = context_tables(padded, E)
     tabs = Tables(F)
     by = padded.reshape(n_groups, 8).astype(np.int64)
-    ctx = np.broadcast_to(np.arange(8) % E, (n_groups, 8))
+    ctx = np.broadcast_to(np.arange(8) % n_contexts(E), (n_groups, 8))
     sym = {"ctx": ctx, "id": by, "rawval": np.zeros_like(by), "rawbits": np.zeros_like(by)}
     S = chains_per_tile or default_chains_per_tile(n_bytes)
     assert S in (1, 2, 4, 8, 16, 32, 64)
@@ -136,7 +142,7 @@ def compress(raw, E: int, dims, dtype_tag: int = 0, chains_per_tile=None) -> byt
     tails = np.zeros(2 * (-(-n_ch // 2)), dtype=np.int64)
     tails[:n_ch] = flat % CHUNK
     nib = (tails[0::2] | (tails[1::2] << 4)).astype("<u1")
-    tables = b"".join(F[p].astype("<u2").tobytes() for p in range(E) if not (mask >> p) & 1)
+    tables = b"".join(F[p].astype("<u2").tobytes() for p in range(len(F)) if not (mask >> p) & 1)
     return b"".join([hdr, np.array(dims, dtype="<u8").tobytes(), tables, offsets.astype("<u4").tobytes(),
                      full.tobytes(), nib.tobytes(), states.astype("<u4").tobytes(), stream.astype("<u2").tobytes()])
 
@@ -152,7 +158,7 @@ def parse(buf: bytes) -> Blob:
     (magic, ver, tag, E, p, S, ndim, mask, tl, n_bytes, n_tiles, n_blocks, n_words, z) = HEADER.unpack_from(buf, 0)
     if magic != MAGIC or ver != VERSION or p != P or tl != TILE_LOG2 or z != 0:
         raise TileAnsError("bad header")
-    if E not in ELEM_SIZES or S not in (1, 2, 4, 8, 16, 32, 64) or not (1 <= ndim <= 8) or mask >> E:
+    if E not in ELEM_SIZES or S not in (1, 2, 4, 8, 16, 32, 64) or not (1 <= ndim <= 8) or mask >> n_contexts(E):
         raise TileAnsError("bad header fields")
     off = HEADER.size
     if len(buf) < off + 8 * ndim:
@@ -167,14 +173,15 @@ def parse(buf: bytes) -> Blob:
     n_ch = n_tiles * S
     if n_blocks != -(-n_ch // BLOCK_CHAINS):
         raise TileAnsError("bad block count")
-    n_coded = sum(1 for q in range(E) if not (mask >> q) & 1)
+    nc = n_contexts(E)
+    n_coded = sum(1 for q in range(nc) if not (mask >> q) & 1)
     fw = 1 if S >= 8 else 2
     n_nib = -(-n_ch // 2)
     need = off + 512 * n_coded + 4 * n_blocks + fw * n_ch + n_nib + 4 * n_ch + 2 * n_words
     if len(buf) != need:
         raise TileAnsError("blob size mismatch")
-    F = np.zeros((E, 256), dtype=np.int64)
-    for q in range(E):
+    F = np.zeros((nc, 256), dtype=np.int64)
+    for q in range(nc):
         if (mask >> q) & 1:
             F[q] = M // 256
         else:
@@ -231,7 +238,7 @@ def decode(buf, tiles=None):
             continue
         q0 = reader.q.copy()
         for i in range(8):
-            ctx = i % b.E
+            ctx = i % n_contexts(b.E)
             slot = (x[idx] & np.uint64(M - 1)).astype(np.int64)
             v = S2I[ctx, slot]
             f = F[ctx, v].astype(np.uint64)

@@ -48,7 +48,7 @@ def test_coded_size_within_entropy_bound():
     a = synth.rowscaled(128, 512, 11)
     blob, b = _check(a, 2, 8)
     raw = _bytes_of(a)
-    ctx = np.arange(len(raw)) % 2
+    ctx = np.arange(len(raw)) % ta.n_contexts(2)
     f = b.tables.F[ctx, raw].astype(np.float64)
     ideal = float(np.sum(P - np.log2(f)))
     n_ch = b.n_tiles * b.S
