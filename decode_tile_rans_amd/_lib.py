@@ -38,6 +38,10 @@ SIGNATURES = {
     "ep_plan_bitrates": (_int, [_int, _int, C.POINTER(_dbl), C.POINTER(_dbl), _dbl, C.POINTER(_int)]),
     "ep_blob_distortion": (_int, [_vp, C.POINTER(_dbl), C.POINTER(_dbl)]),
     "ep_actual_bpp": (_dbl, [_vp]),
+    "ep_compress_lossless": (_int, [_vp, _i64, _int, C.POINTER(_i64), _int, _int, _int, C.POINTER(_vp)]),
+    "ep_blob_kind": (_int, [_vp]),
+    "ep_blob_dims": (_int, [_vp, C.POINTER(_i64), _int]),
+    "ep_blob_elem_bytes": (_int, [_vp]),
     "ep_blob_shape": (None, [_vp, C.POINTER(_i64), C.POINTER(_i64)]),
     "ep_blob_dtype": (_int, [_vp]),
     "ep_blob_params": (None, [_vp, C.POINTER(_int), C.POINTER(_int), C.POINTER(_int)]),
@@ -161,6 +165,29 @@ def ep_blob_distortion(blob: int):
     e, r = _dbl(), _dbl()
     check(lib().ep_blob_distortion(blob, C.byref(e), C.byref(r)))
     return e.value, r.value
+
+
+def ep_compress_lossless(src_ptr: int, n_bytes: int, elem_bytes: int, dims, dtype_tag: int = 0,
+                         chains_per_tile: int = 0) -> int:
+    d = (_i64 * len(dims))(*[int(v) for v in dims])
+    out = _vp()
+    check(lib().ep_compress_lossless(src_ptr, n_bytes, elem_bytes, d, len(dims), dtype_tag, chains_per_tile,
+                                     C.byref(out)))
+    return out.value
+
+
+def ep_blob_kind(blob: int) -> int:
+    return int(lib().ep_blob_kind(blob))
+
+
+def ep_blob_dims(blob: int):
+    d = (_i64 * 8)()
+    n = lib().ep_blob_dims(blob, d, 8)
+    return tuple(int(d[i]) for i in range(n))
+
+
+def ep_blob_elem_bytes(blob: int) -> int:
+    return int(lib().ep_blob_elem_bytes(blob))
 
 
 def ep_actual_bpp(blob: int) -> float:

@@ -15,6 +15,10 @@ from ._lib import EPError
 _TORCH_TO_EP = {torch.bfloat16: L.EP_BF16, torch.float16: L.EP_FP16, torch.float32: L.EP_FP32,
                 torch.float8_e4m3fn: L.EP_FP8_E4M3FN, torch.int8: L.EP_INT8}
 _EP_TO_TORCH = {v: k for k, v in _TORCH_TO_EP.items()}
+# TileANS blobs carry the tensor's dtype as a tag (an index into this list)
+_LOSSLESS_DTYPES = [torch.bfloat16, torch.float16, torch.float32, torch.float64, torch.float8_e4m3fn,
+                    torch.float8_e5m2, torch.int8, torch.uint8, torch.int16, torch.int32, torch.int64, torch.bool,
+                    torch.uint16, torch.uint32, torch.uint64, torch.complex64]
 
 
 def _stream_ptr(stream=None) -> int:
@@ -27,9 +31,15 @@ class Compressed:
 
     def __init__(self, handle: int):
         self._h = handle
-        self.shape = L.ep_blob_shape(handle)
-        self.ep_dtype = L.ep_blob_dtype(handle)
-        self.dtype = _EP_TO_TORCH[self.ep_dtype]
+        self.lossless = L.ep_blob_kind(handle) == 1
+        if self.lossless:
+            self.shape = L.ep_blob_dims(handle)
+            self.ep_dtype = None
+            self.dtype = _LOSSLESS_DTYPES[L.ep_blob_dtype(handle)]
+        else:
+            self.shape = L.ep_blob_shape(handle)
+            self.ep_dtype = L.ep_blob_dtype(handle)
+            self.dtype = _EP_TO_TORCH[self.ep_dtype]
         self.chains_per_tile, self.k_log2, self.flags = L.ep_blob_params(handle)
 
     @property
@@ -96,6 +106,19 @@ def compress(x, target_bpp: float, dtype=None, chains_per_tile: int = 0) -> Comp
     return Compressed(h)
 
 
+def compress_lossless(x: torch.Tensor, chains_per_tile: int = 0) -> Compressed:
+    """TileANS: a bit-exact compressed copy of a tensor of any shape and of the dtypes in
+    ``_LOSSLESS_DTYPES`` ([README] Config：压缩配置 TileANSConfig)."""
+    if x.dtype not in _LOSSLESS_DTYPES:
+        raise EPError(-3, f"unsupported dtype {x.dtype}")
+    host = x.detach().to("cpu").contiguous()
+    shape = tuple(host.shape) if host.dim() > 0 else (1,)
+    raw = host.reshape(-1).view(torch.uint8)
+    h = L.ep_compress_lossless(raw.data_ptr(), raw.numel(), host.element_size(), shape,
+                               _LOSSLESS_DTYPES.index(host.dtype), chains_per_tile)
+    return Compressed(h)
+
+
 def plan_bitrates(mats, budget_bpp: float, candidates=(2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0), weights=None,
                   dtype=None, chains_per_tile: int = 0):
     """Compress every matrix at one of ``candidates`` so that all of them together take
@@ -129,7 +152,8 @@ def plan_bitrates(mats, budget_bpp: float, candidates=(2.0, 2.5, 3.0, 3.5, 4.0, 
 
 
 def decompress(c: Compressed, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Decode on the current GPU into a new (or given) tensor of the original shape/dtype."""
+    """Decode on the current GPU into a new (or given) tensor of the original shape/dtype
+    (both blob kinds)."""
     c.upload(stream)
     if out is None:
         out = torch.empty(c.shape, dtype=c.dtype, device="cuda")

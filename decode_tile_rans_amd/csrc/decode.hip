@@ -36,7 +36,12 @@ int hip_check(int err, const char* what) {
 
 namespace {
 
-enum OutKind { OUT_BF16 = 0, OUT_BF16_SAT = 1, OUT_FP16 = 2, OUT_FP32 = 3, OUT_FP8 = 4, OUT_INT8 = 5, OUT_COORDS = 6 };
+enum OutKind { OUT_BF16 = 0, OUT_BF16_SAT = 1, OUT_FP16 = 2, OUT_FP32 = 3, OUT_FP8 = 4, OUT_INT8 = 5, OUT_COORDS = 6,
+               OUT_BYTES = 7 /* TileANS: the decoded symbols are the tensor's bytes */ };
+template <int OUT>
+constexpr int out_elem_bytes() {
+  return (OUT == OUT_FP32 || OUT == OUT_COORDS) ? 4 : ((OUT == OUT_FP8 || OUT == OUT_INT8 || OUT == OUT_BYTES) ? 1 : 2);
+}
 
 constexpr int kTabWords = kNumCtx * kM;          // 14336 u32
 constexpr int kTabBytes = kTabWords * 4;         // 57344 B
@@ -59,6 +64,7 @@ struct DecJob {
   int log2S, k, c8;
   uint32_t s_div_g, s_mod_g;   // S = s_div_g * G + s_mod_g (group stride in rows / columns)
   uint32_t R;
+  uint32_t ctx_mask;           // TileANS: byte contexts - 1 (symbol i of a group uses i & ctx_mask)
 };
 
 // ---------------------------------------------------------------- container stores
@@ -109,9 +115,11 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 template <int OUT>
 __device__ inline void store_group(void* out, int64_t base, const float* vin, const int32_t* u, bool full,
                                    int64_t nvalid) {
-  float v[8];
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if constexpr (OUT != OUT_BYTES && OUT != OUT_COORDS) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = vin[i];
+    for (int i = 0; i < 8; ++i) v[i] = vin[i];
+  }
   if (OUT == OUT_BF16_SAT) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = fminf(fmaxf(v[i], -3.38953139e38f), 3.38953139e38f);
@@ -155,6 +163,20 @@ __device__ inline void store_group(void* out, int64_t base, const float* vin, co
       lo |= a << (8 * i);
       hi |= b << (8 * i);
     }
+    uint8_t* o = (uint8_t*)out + base;
+    if (full) {
+      typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+      u32x2 pv = {lo, hi};
+      __builtin_nontemporal_store(pv, (u32x2*)o);
+    } else {
+      for (int i = 0; i < nvalid; ++i) o[i] = (uint8_t)((i < 4 ? lo : hi) >> (8 * (i & 3)));
+    }
+  } else if (OUT == OUT_BYTES) {
+    // (u holds the eight bytes, one per entry's top byte)
+    const uint32_t lo = ((uint32_t)u[0] >> 24) | (((uint32_t)u[1] >> 24) << 8) | (((uint32_t)u[2] >> 24) << 16) |
+                        ((uint32_t)u[3] & 0xFF000000u);
+    const uint32_t hi = ((uint32_t)u[4] >> 24) | (((uint32_t)u[5] >> 24) << 8) | (((uint32_t)u[6] >> 24) << 16) |
+                        ((uint32_t)u[7] & 0xFF000000u);
     uint8_t* o = (uint8_t*)out + base;
     if (full) {
       typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
@@ -533,6 +555,7 @@ struct TabStager {
   const uint4* src;
   uint4* dst;
   int tid, nt;
+  bool swap;    // the lossy layout: stored FIRST, FREE[0] change places (TileANS: as stored)
   uint4 v[4];
   // (indices past the end are clamped to the last element, which then is loaded and
   // stored by several threads with the same value: no conditional stores, so the
@@ -544,7 +567,7 @@ struct TabStager {
       v[k] = src[i < kN ? i : kN - 1];
     }
   }
-  __device__ void put(int i, uint4 d) { dst[i < 2 * kQ ? (i ^ kQ) : i] = d; }
+  __device__ void put(int i, uint4 d) { dst[swap && i < 2 * kQ ? (i ^ kQ) : i] = d; }
   __device__ void commit() {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -576,6 +599,7 @@ struct GroupCtx {
   const DecJob* J;
   StreamRef sref;
   uint32_t lds0;   // LDS address of the tables
+  uint32_t ctx_mask;
   uint32_t G;
   int S;
   bool rowwise;
@@ -621,6 +645,45 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
                                              const uint32_t* g0, char** optr) {
   using LY = EntryLayout<NARROW>;
   const DecJob& J = *X.J;
+  if constexpr (OUT == OUT_BYTES) {
+    // TileANS: eight byte symbols, symbol i from the table of context i & ctx_mask
+    uint32_t xs[ILP], ras[ILP], nws[ILP];
+    int32_t e[ILP][8];
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      xs[c] = rd[c].x;
+      ras[c] = rd[c].ra;
+      nws[c] = rd[c].nw;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t tb = X.lds0 + ((i & X.ctx_mask) << 13);
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) e[c][i] = (int32_t)ch_entry(tb, rd[c]);
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) ch_decode(rd[c], (uint32_t)e[c][i]);
+      ch_renorm_all<ILP>(rd);
+    }
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      const bool act = (ILP == 1) || kk < ngr[c];
+      if (act) {
+        if (C8) {
+          store_group<OUT>(optr[c], 0, nullptr, e[c], true, 8);
+        } else {
+          const int64_t c0 = (int64_t)(g0[c] + (uint32_t)kk * (uint32_t)X.S) * 8;
+          store_group<OUT>(J.out, c0, nullptr, e[c], c0 + 8 <= J.C, J.C - c0);
+        }
+      }
+      if (ILP > 1 && kk >= ngr[c]) {
+        rd[c].x = xs[c];
+        rd[c].ra = ras[c];
+        rd[c].nw = nws[c];
+      }
+      optr[c] += (int64_t)X.S * 8;
+    }
+    return;
+  }
   // ---- fast path: eight symbols per chain, no escape handling
   uint32_t xs[ILP], ras[ILP], nws[ILP];
   uint32_t e[ILP][8];
@@ -712,7 +775,7 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
       }
     }
   }
-  constexpr int ESZ = (OUT == OUT_FP32 || OUT == OUT_COORDS) ? 4 : ((OUT == OUT_FP8 || OUT == OUT_INT8) ? 1 : 2);
+  constexpr int ESZ = out_elem_bytes<OUT>();
 #pragma unroll
   for (int c = 0; c < ILP; ++c) optr[c] += (int64_t)X.S * 8 * ESZ;
 }
@@ -730,7 +793,7 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
   const int s0 = lane & ~(S - 1);
   const uint64_t seg = (S == 64) ? ~0ull : (((1ull << S) - 1ull) << s0);
 
-  constexpr int ESZ = (OUT == OUT_FP32 || OUT == OUT_COORDS) ? 4 : ((OUT == OUT_FP8 || OUT == OUT_INT8) ? 1 : 2);
+  constexpr int ESZ = out_elem_bytes<OUT>();
   Chain rd[ILP];
   RowScale rs[ILP];
   int ngr[ILP];
@@ -775,6 +838,14 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
     const uint32_t col0 = g0[c] - row0 * G;
     RowScale& q = rs[c];
     q.row = row0;
+    if constexpr (OUT == OUT_BYTES) {   // no row scales
+      q.h = q.nh = q.hn = 0.f;
+      q.pn = nullptr;
+      q.kchg = 0xFFFFFFFFu;
+      q.bnd = q.rown = q.coln = 0;
+      optr[c] = (char*)J.out + (live[c] ? gg * 8 : 0);
+      continue;
+    }
     q.h = any ? J.hr[row0] : 0.f;
     q.nh = -128.f * q.h;
     if (X.rowwise) {
@@ -823,7 +894,7 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
   // (the row scale of the even group is settled before the service, so that its load is
   // followed by a fixed sequence of memory operations)
   for (int kk = 0; kk < nmax; kk += 2) {
-    row_scale<ILP>(X, kk, rs, ngr);
+    if constexpr (OUT != OUT_BYTES) row_scale<ILP>(X, kk, rs, ngr);
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       ch_service(X.sref, rd[c], (ILP == 1) || kk < ngr[c]);
@@ -831,7 +902,7 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
     }
     decode_group<OUT, ESC, C8, NARROW, ILP>(X, kk, rd, rs, ngr, g0, optr);
     if (kk + 1 < nmax) {
-      row_scale<ILP>(X, kk + 1, rs, ngr);
+      if constexpr (OUT != OUT_BYTES) row_scale<ILP>(X, kk + 1, rs, ngr);
       decode_group<OUT, ESC, C8, NARROW, ILP>(X, kk + 1, rd, rs, ngr, g0, optr);
     }
 #pragma unroll
@@ -869,6 +940,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   st.dst = (uint4*)smem;
   st.tid = tid;
   st.nt = (int)blockDim.x;
+  st.swap = OUT != OUT_BYTES;
 
   GroupCtx X;
   X.J = &J;
@@ -877,6 +949,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   X.S = 1 << J.log2S;
   X.G = (uint32_t)J.G;
   X.rowwise = (uint32_t)X.S <= X.G;
+  X.ctx_mask = J.ctx_mask;
   int64_t b = wg_blk0 + (int64_t)wave * ILP;
   if (b >= wg_blk1) {   // a wave without blocks still stages its share
     st.issue();
@@ -929,6 +1002,9 @@ int launch_out(int out, const DecBatch& B, int64_t n_wg, int waves, hipStream_t 
     case OUT_FP32: return launch_t<OUT_FP32, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
     case OUT_FP8: return launch_t<OUT_FP8, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
     case OUT_INT8: return launch_t<OUT_INT8, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+    case OUT_BYTES:
+      if constexpr (!ESC && NARROW) return launch_t<OUT_BYTES, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+      return fail(EP_E_ARG, "byte output takes the escape-free narrow kernel");
     default: return launch_t<OUT_COORDS, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
   }
 }
@@ -950,6 +1026,7 @@ int launch_any(int out, bool esc, bool c8, bool narrow, Shape sh, const DecBatch
 }
 
 int out_kind(const Blob& b) {
+  if (b.kind == kKindTileAns) return OUT_BYTES;
   switch (b.dtype) {
     case EP_BF16: return (b.flags & kFlagSat) ? OUT_BF16_SAT : OUT_BF16;
     case EP_FP16: return OUT_FP16;
@@ -983,6 +1060,7 @@ DecJob make_job(const Blob& b, void* out) {
   j.s_div_g = (uint32_t)(b.S / j.G);
   j.s_mod_g = (uint32_t)(b.S % j.G);
   j.R = (uint32_t)b.R;
+  j.ctx_mask = b.kind == kKindTileAns ? (uint32_t)(b.n_ctx - 1) : 0u;
   return j;
 }
 
@@ -1106,8 +1184,12 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
   } catch (...) {
     return fail(EP_E_NOMEM, "out of host memory");
   }
-  build_slot_tables(b.model, (uint32_t*)&host[o_tab], b.k <= 6);
-  half_scales(b, (float*)&host[o_hr]);
+  if (b.kind == kKindTileAns) {
+    build_byte_tables(b.LF, b.n_ctx, (uint32_t*)&host[o_tab]);   // (no row scales: zeros)
+  } else {
+    build_slot_tables(b.model, (uint32_t*)&host[o_tab], b.k <= 6);
+    half_scales(b, (float*)&host[o_hr]);
+  }
   // per chain: state, word index of its tile's main area, of its tail, length
   {
     uint32_t* meta = (uint32_t*)&host[o_ch];
@@ -1184,6 +1266,7 @@ int ep_test_decode_coords(const ep_blob* blob, int32_t* dev_u, ep_stream stream)
   set_error("");
   if (!blob) return fail(EP_E_ARG, "null blob");
   const Blob& b = blob->b;
+  if (b.kind != kKindLossy) return fail(EP_E_ARG, "lattice coordinates exist for lossy blobs only");
   return decode_one(b, dev_u, 0, b.n_chains, OUT_COORDS, (hipStream_t)stream);
 }
 

@@ -411,6 +411,114 @@ void put_u16(std::vector<uint8_t>& b, size_t off, uint16_t v) { std::memcpy(&b[o
 void put_u32(std::vector<uint8_t>& b, size_t off, uint32_t v) { std::memcpy(&b[off], &v, 4); }
 void put_u64(std::vector<uint8_t>& b, size_t off, uint64_t v) { std::memcpy(&b[off], &v, 8); }
 
+// The chain area shared by both blob kinds: u32 block offsets | full chunks per chain
+// (u8 if S >= 8, else u16) | tail nibbles | u32 states | u16 stream; a block of 64
+// chains holds [tile main areas (chunks in request order)][tails][pad to 8 words].
+struct Area {
+  std::vector<uint64_t> block_off;   // in chunks, n_blocks + 1 entries
+  int64_t n_blocks = 0;
+  uint64_t n_words = 0;
+  size_t bytes = 0;                  // size of the whole area
+};
+
+int plan_area(const std::vector<ChainOut>& chains, int S, Area* a) {
+  const int64_t n_chains = (int64_t)chains.size();
+  a->n_blocks = (n_chains + kBlockChains - 1) / kBlockChains;
+  const int64_t max_full = S >= 8 ? 0xFF : 0xFFFF;
+  a->block_off.assign((size_t)a->n_blocks + 1, 0);
+  for (int64_t bk = 0; bk < a->n_blocks; ++bk) {
+    const int64_t c0 = bk * kBlockChains, c1 = std::min(n_chains, c0 + kBlockChains);
+    uint64_t words = 0;
+    for (int64_t c = c0; c < c1; ++c) {
+      const uint64_t len = chains[c].words.size();
+      if ((int64_t)(len / 8) > max_full) return fail(EP_E_ARG, "chain longer than the chunk count field");
+      words += len;
+    }
+    a->block_off[bk + 1] = a->block_off[bk] + (words + 7) / 8;
+  }
+  a->n_words = 8 * a->block_off[a->n_blocks];
+  if (a->block_off[a->n_blocks] > 0xFFFFFFFFull) return fail(EP_E_ARG, "stream too long for the block offsets");
+  const size_t fw = S >= 8 ? 1 : 2;
+  a->bytes = 4 * (size_t)a->n_blocks + fw * (size_t)n_chains + (size_t)((n_chains + 1) / 2) +
+             4 * (size_t)n_chains + 2 * (size_t)a->n_words;
+  return EP_OK;
+}
+
+// b[off ..) must be zeroed
+void write_area(const std::vector<ChainOut>& chains, int S, const Area& a, std::vector<uint8_t>& b, size_t off) {
+  const int64_t n_chains = (int64_t)chains.size();
+  const size_t fw = S >= 8 ? 1 : 2;
+  const size_t off_bo = off;
+  const size_t off_full = off_bo + 4 * (size_t)a.n_blocks;
+  const size_t off_nib = off_full + fw * (size_t)n_chains;
+  const size_t off_st = off_nib + (size_t)((n_chains + 1) / 2);
+  const size_t off_stream = off_st + 4 * (size_t)n_chains;
+  for (int64_t bk = 0; bk < a.n_blocks; ++bk) put_u32(b, off_bo + 4 * (size_t)bk, (uint32_t)a.block_off[bk]);
+  for (int64_t c = 0; c < n_chains; ++c) {
+    const size_t len = chains[c].words.size();
+    if (fw == 1) b[off_full + (size_t)c] = (uint8_t)(len / 8);
+    else put_u16(b, off_full + 2 * (size_t)c, (uint16_t)(len / 8));
+    b[off_nib + (size_t)(c / 2)] |= (uint8_t)((len % 8) << (4 * (c & 1)));
+  }
+  parallel_for(a.n_blocks, [&](int64_t bb, int64_t be, int) {
+    for (int64_t bk = bb; bk < be; ++bk) {
+      const int64_t c0 = bk * kBlockChains, c1 = std::min(n_chains, c0 + kBlockChains);
+      const size_t base = off_stream + 16 * (size_t)a.block_off[bk];
+      size_t tile_main = 0;   // words from the block start
+      size_t tails = 0;
+      for (int64_t c = c0; c < c1; ++c) tails += 8 * (chains[c].words.size() / 8);
+      for (int64_t t0 = c0; t0 < c1; t0 += S) {
+        size_t tile_words = 0;
+        for (int64_t c = t0; c < t0 + S; ++c) {
+          const auto& w = chains[c].words;
+          const size_t nf = w.size() / 8;
+          for (size_t nn = 0; nn < nf; ++nn)
+            std::memcpy(&b[base + 2 * (tile_main + 8 * (size_t)chains[c].rank[nn])], &w[8 * nn], 16);
+          tile_words += 8 * nf;
+        }
+        tile_main += tile_words;
+      }
+      for (int64_t c = c0; c < c1; ++c) {
+        const auto& w = chains[c].words;
+        const size_t nf = w.size() / 8, r = w.size() % 8;
+        if (r) std::memcpy(&b[base + 2 * tails], &w[8 * nf], 2 * r);
+        tails += r;
+      }
+    }
+  }, 1);
+  for (int64_t ch = 0; ch < n_chains; ++ch) put_u32(b, off_st + 4 * (size_t)ch, chains[ch].state);
+}
+
+// TileANS: chain j of tile t codes the bytes of its groups, context = byte position
+// within the group modulo the context count
+void encode_chain_bytes(const uint8_t* by, const int32_t (*F)[256], const int32_t (*CUM)[256], int n_ctx,
+                        int64_t t, int j, int S, int64_t n_groups, ChainOut* out) {
+  int64_t gt = std::min<int64_t>(kTileGroups, n_groups - (int64_t)kTileGroups * t);
+  int ngr = gt > j ? (int)((gt - j + S - 1) / S) : 0;
+  uint64_t x = kL;
+  std::vector<uint16_t>& w = out->words;
+  w.clear();
+  out->cons.assign((size_t)ngr, 0);
+  out->slow.assign((size_t)ngr, 0);
+  for (int kk = ngr - 1; kk >= 0; --kk) {
+    const int64_t g = (int64_t)kTileGroups * t + j + (int64_t)kk * S;
+    const size_t w0 = w.size();
+    for (int i = 7; i >= 0; --i) {
+      const int ctx = i % n_ctx;
+      const uint8_t v = by[g * 8 + i];
+      const uint64_t f = (uint64_t)F[ctx][v], cum = (uint64_t)CUM[ctx][v];
+      if (x >= (f << 21)) {
+        w.push_back((uint16_t)(x & 0xFFFFu));
+        x >>= 16;
+      }
+      x = (x / f) * (uint64_t)kM + (x % f) + cum;
+    }
+    out->cons[kk] = (uint8_t)(w.size() - w0);
+  }
+  std::reverse(w.begin(), w.end());
+  out->state = (uint32_t)x;
+}
+
 }  // namespace
 
 int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_req,
@@ -643,30 +751,12 @@ int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_r
     }, 16);
   }
 
-  // ---- block layout: per block of 64 chains [tile main areas][tails][pad to 8 words]
-  const int64_t n_blocks = (n_chains + kBlockChains - 1) / kBlockChains;
-  const size_t fw = S >= 8 ? 1 : 2;
-  const int64_t max_full = S >= 8 ? 0xFF : 0xFFFF;
-  std::vector<uint64_t> block_off((size_t)n_blocks + 1, 0);   // in chunks
-  for (int64_t bk = 0; bk < n_blocks; ++bk) {
-    const int64_t c0 = bk * kBlockChains, c1 = std::min(n_chains, c0 + kBlockChains);
-    uint64_t words = 0;
-    for (int64_t c = c0; c < c1; ++c) {
-      const uint64_t len = chains[c].words.size();
-      if ((int64_t)(len / 8) > max_full) return fail(EP_E_ARG, "chain longer than the chunk count field");
-      words += len;
-    }
-    uint64_t full_words = 0;
-    for (int64_t c = c0; c < c1; ++c) full_words += 8 * (chains[c].words.size() / 8);
-    uint64_t tail_words = words - full_words;
-    block_off[bk + 1] = block_off[bk] + (full_words + tail_words + 7) / 8;
-  }
-  const uint64_t n_words = 8 * block_off[n_blocks];
-  if (block_off[n_blocks] > 0xFFFFFFFFull) return fail(EP_E_ARG, "stream too long for the block offsets");
+  // ---- blob: header | row scales | model | chain area
+  Area area;
+  int rc = plan_area(chains, S, &area);
+  if (rc) return rc;
   const std::vector<uint8_t> mbytes = m.to_bytes();
-  const size_t n_nib = (size_t)((n_chains + 1) / 2);
-  const size_t total = kHeaderBytes + 2 * (size_t)R + mbytes.size() + 4 * (size_t)n_blocks + fw * (size_t)n_chains +
-                       n_nib + 4 * (size_t)n_chains + 2 * (size_t)n_words;
+  const size_t total = kHeaderBytes + 2 * (size_t)R + mbytes.size() + area.bytes;
   std::vector<uint8_t>& b = *out;
   try {
     b.assign(total, 0);
@@ -685,57 +775,130 @@ int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_r
   put_u32(b, 16, (uint32_t)C);
   put_u32(b, 20, dbits);
   put_u32(b, 24, (uint32_t)n_tiles);
-  put_u32(b, 28, (uint32_t)n_blocks);
-  put_u64(b, 32, n_words);
+  put_u32(b, 28, (uint32_t)area.n_blocks);
+  put_u64(b, 32, area.n_words);
   put_u32(b, 40, (uint32_t)mbytes.size());
   put_u32(b, 44, 0);
   size_t off = kHeaderBytes;
   for (int64_t r = 0; r < R; ++r, off += 2) put_u16(b, off, mx.s_bits[r]);
   std::memcpy(&b[off], mbytes.data(), mbytes.size());
   off += mbytes.size();
-  const size_t off_bo = off;
-  off += 4 * (size_t)n_blocks;
-  const size_t off_full = off;
-  off += fw * (size_t)n_chains;
-  const size_t off_nib = off;
-  off += n_nib;
-  const size_t off_st = off;
-  off += 4 * (size_t)n_chains;
-  const size_t off_stream = off;
-  for (int64_t bk = 0; bk < n_blocks; ++bk) put_u32(b, off_bo + 4 * (size_t)bk, (uint32_t)block_off[bk]);
-  for (int64_t c = 0; c < n_chains; ++c) {
-    const size_t len = chains[c].words.size();
-    if (fw == 1) b[off_full + (size_t)c] = (uint8_t)(len / 8);
-    else put_u16(b, off_full + 2 * (size_t)c, (uint16_t)(len / 8));
-    b[off_nib + (size_t)(c / 2)] |= (uint8_t)((len % 8) << (4 * (c & 1)));
+  write_area(chains, S, area, b, off);
+  return EP_OK;
+}
+
+// TileANS (lossless): the tensor's raw bytes, per-byte-position tables (or uniform),
+// the lossy blob's chains and chain area.
+int compress_lossless(const void* src, int64_t n_bytes, int E, const int64_t* dims, int ndim, int tag, int S_req,
+                      std::vector<uint8_t>* out) {
+  if (!src || !out || (ndim > 0 && !dims)) return fail(EP_E_ARG, "null pointer");
+  if (E != 1 && E != 2 && E != 4 && E != 8) return fail(EP_E_ARG, "element size must be 1, 2, 4 or 8 bytes");
+  if (ndim < 1 || ndim > 8) return fail(EP_E_SHAPE, "rank must be 1..8");
+  if (tag < 0 || tag > 255) return fail(EP_E_ARG, "dtype tag must be 0..255");
+  __int128 prod = E;
+  for (int d = 0; d < ndim; ++d) {
+    if (dims[d] < 1) return fail(EP_E_SHAPE, "every extent must be >= 1");
+    prod *= dims[d];
+    if (prod > ((__int128)1 << 40)) return fail(EP_E_SHAPE, "tensor too large");
   }
-  parallel_for(n_blocks, [&](int64_t bb, int64_t be, int) {
-    for (int64_t bk = bb; bk < be; ++bk) {
-      const int64_t c0 = bk * kBlockChains, c1 = std::min(n_chains, c0 + kBlockChains);
-      const size_t base = off_stream + 16 * (size_t)block_off[bk];
-      size_t tile_main = 0;   // words from the block start
-      size_t tails = 0;
-      for (int64_t c = c0; c < c1; ++c) tails += 8 * (chains[c].words.size() / 8);
-      for (int64_t t0 = c0; t0 < c1; t0 += S) {
-        size_t tile_words = 0;
-        for (int64_t c = t0; c < t0 + S; ++c) {
-          const auto& w = chains[c].words;
-          const size_t nf = w.size() / 8;
-          for (size_t nn = 0; nn < nf; ++nn)
-            std::memcpy(&b[base + 2 * (tile_main + 8 * (size_t)chains[c].rank[nn])], &w[8 * nn], 16);
-          tile_words += 8 * nf;
-        }
-        tile_main += tile_words;
-      }
-      for (int64_t c = c0; c < c1; ++c) {
-        const auto& w = chains[c].words;
-        const size_t nf = w.size() / 8, r = w.size() % 8;
-        if (r) std::memcpy(&b[base + 2 * tails], &w[8 * nf], 2 * r);
-        tails += r;
-      }
+  if (n_bytes != (int64_t)prod) return fail(EP_E_SHAPE, "byte count does not match the shape");
+  if (S_req != 0 && S_req != 1 && S_req != 2 && S_req != 4 && S_req != 8 && S_req != 16 &&
+      S_req != 32 && S_req != 64)
+    return fail(EP_E_ARG, "chains_per_tile must be 0 or a power of two <= 64");
+  const int n_ctx = E < 4 ? E : 4;
+  const int64_t n_groups = (n_bytes + 7) / 8;
+  std::vector<uint8_t> by;
+  try {
+    by.assign((size_t)(8 * n_groups), 0);
+  } catch (...) {
+    return fail(EP_E_NOMEM, "out of host memory");
+  }
+  std::memcpy(by.data(), src, (size_t)n_bytes);
+
+  // ---- per-context tables
+  const int nt = num_threads();
+  std::vector<std::vector<int64_t>> part((size_t)nt, std::vector<int64_t>(4 * 256, 0));
+  parallel_for(8 * n_groups, [&](int64_t b0, int64_t e0, int tid) {
+    auto& p = part[tid];
+    for (int64_t q = b0; q < e0; ++q) p[(size_t)((q % n_ctx) * 256 + by[q])]++;
+  }, 1 << 16);
+  int32_t F[4][256], CUM[4][256];
+  int umask = 0;
+  const int32_t* lq = log2q_table();
+  for (int c = 0; c < n_ctx; ++c) {
+    int64_t cnt[256];
+    for (int v = 0; v < 256; ++v) {
+      cnt[v] = 0;
+      for (auto& p : part) cnt[v] += p[(size_t)(c * 256 + v)];
     }
-  }, 1);
-  for (int64_t ch = 0; ch < n_chains; ++ch) put_u32(b, off_st + 4 * (size_t)ch, chains[ch].state);
+    int32_t f[256];
+    quantize_freqs(cnt, 256, kM, f);
+    // coded estimate (plus the stored table's 4096 bits) against 8 raw bits a byte
+    __int128 coded = (__int128)256 * 16 * 65536, raw = 0;
+    for (int v = 0; v < 256; ++v) {
+      if (cnt[v] > 0) coded += (__int128)cnt[v] * (kP * 65536 - lq[f[v]]);
+      raw += (__int128)cnt[v] * 8 * 65536;
+    }
+    if (coded >= raw) {
+      umask |= 1 << c;
+      for (int v = 0; v < 256; ++v) F[c][v] = kM / 256;
+    } else {
+      for (int v = 0; v < 256; ++v) F[c][v] = f[v];
+    }
+    int32_t acc = 0;
+    for (int v = 0; v < 256; ++v) {
+      CUM[c][v] = acc;
+      acc += F[c][v];
+    }
+  }
+
+  // ---- chains
+  const int S = S_req ? S_req : (n_bytes >= (1ll << 22) ? 8 : 1);
+  const int64_t n_tiles = std::max<int64_t>(1, (n_groups + kTileGroups - 1) / kTileGroups);
+  const int64_t n_chains = n_tiles * S;
+  std::vector<ChainOut> chains((size_t)n_chains);
+  parallel_for(n_chains, [&](int64_t b0, int64_t e0, int) {
+    for (int64_t ch = b0; ch < e0; ++ch)
+      encode_chain_bytes(by.data(), F, CUM, n_ctx, ch / S, (int)(ch % S), S, n_groups, &chains[ch]);
+  }, 64);
+  parallel_for(n_tiles, [&](int64_t b0, int64_t e0, int) {
+    for (int64_t tt = b0; tt < e0; ++tt) schedule_tile(&chains[(size_t)(tt * S)], S);
+  }, 16);
+
+  // ---- blob: header | dims | tables | chain area
+  Area area;
+  int rc = plan_area(chains, S, &area);
+  if (rc) return rc;
+  int n_coded = 0;
+  for (int c = 0; c < n_ctx; ++c) n_coded += !((umask >> c) & 1);
+  const size_t total = kHeaderBytes + 8 * (size_t)ndim + 512 * (size_t)n_coded + area.bytes;
+  std::vector<uint8_t>& b = *out;
+  try {
+    b.assign(total, 0);
+  } catch (...) {
+    return fail(EP_E_NOMEM, "out of host memory");
+  }
+  std::memcpy(&b[0], "EPT1", 4);
+  put_u16(b, 4, 1);
+  b[6] = (uint8_t)tag;
+  b[7] = (uint8_t)E;
+  b[8] = (uint8_t)kP;
+  b[9] = (uint8_t)S;
+  b[10] = (uint8_t)ndim;
+  b[11] = (uint8_t)umask;
+  b[12] = 12;
+  put_u64(b, 16, (uint64_t)n_bytes);
+  put_u32(b, 24, (uint32_t)n_tiles);
+  put_u32(b, 28, (uint32_t)area.n_blocks);
+  put_u64(b, 32, area.n_words);
+  put_u64(b, 40, 0);
+  size_t off = kHeaderBytes;
+  for (int d = 0; d < ndim; ++d, off += 8) put_u64(b, off, (uint64_t)dims[d]);
+  for (int c = 0; c < n_ctx; ++c) {
+    if ((umask >> c) & 1) continue;
+    for (int v = 0; v < 256; ++v, off += 2) put_u16(b, off, (uint16_t)F[c][v]);
+  }
+  write_area(chains, S, area, b, off);
   return EP_OK;
 }
 

@@ -70,6 +70,8 @@ extern const int32_t* log2q_table();   // floor(2^16 log2 f + 1/2), f in [0, 204
 //     bit 22 coset, bit 23 escape, bits 24..31 u + 128 (direct) or
 //     neg | top2<<1 | (e-k)<<3 (escape)
 void build_slot_tables(const Model& m, uint32_t* out /* 7*2048 */, bool narrow);
+// TileANS entries: f | bias << 11 | byte << 24, one 2048-slot table per context
+void build_byte_tables(const int32_t (*F)[256], int n_ctx, uint32_t* out /* n_ctx*2048 */);
 
 // Squared error of the lattice reconstruction fl32(h_r u) against the input, and the
 // input's squared norm (both over all rows x cols entries).
@@ -78,12 +80,24 @@ struct Distortion {
 };
 int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_req, std::vector<uint8_t>* out,
              Distortion* dist);
+// TileANS (lossless) blob of a tensor's raw bytes.
+int compress_lossless(const void* src, int64_t n_bytes, int E, const int64_t* dims, int ndim, int tag, int S_req,
+                      std::vector<uint8_t>* out);
+constexpr int kKindLossy = 0;
+constexpr int kKindTileAns = 1;
 
-// Parsed blob (host side) + device mirror.
+// Parsed blob (host side) + device mirror.  A TileANS blob is held as one row of
+// n_bytes "columns" (R = 1, C = n_bytes: the same groups, tiles and chains as a
+// lossy blob of that shape); `dtype` is then the caller's opaque tag.
 struct Blob {
   std::vector<uint8_t> bytes;          // serialized form
+  int kind = kKindLossy;
   int dtype = 0, S = 0, k = 0, flags = 0;
   int64_t R = 0, C = 0;
+  // TileANS only
+  int E = 0, n_ctx = 0, umask = 0;
+  std::vector<int64_t> dims;
+  int32_t LF[4][256];                  // per-context byte frequencies (sum 2048)
   float delta = 0.f;
   int64_t n_tiles = 0, n_blocks = 0, n_chains = 0;
   uint64_t n_words = 0;

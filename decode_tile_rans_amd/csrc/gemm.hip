@@ -445,7 +445,7 @@ int ep_compressed_linear_forward(const ep_blob* w, const void* x, int64_t T, con
   set_error("");
   if (!w || !x || !y || !ws) return fail(EP_E_ARG, "null pointer");
   const Blob& b = w->b;
-  if (b.dtype != EP_BF16) return fail(EP_E_DTYPE, "compressed linear takes a BF16 blob");
+  if (b.kind != kKindLossy || b.dtype != EP_BF16) return fail(EP_E_DTYPE, "compressed linear takes a lossy BF16 blob");
   if (ws_bytes < ep_linear_workspace_bytes(w)) return fail(EP_E_WORKSPACE, "workspace too small");
   void* wd = (void*)(((uintptr_t)ws + 255) & ~uintptr_t(255));
   int rc = ep_decompress(w, wd, stream);
@@ -474,7 +474,8 @@ int ep_compressed_linear_seq_forward(const ep_blob* const* w, int n, const void*
   if (!w || !x || !y || !ws || n < 1) return fail(EP_E_ARG, "null pointer or empty sequence");
   for (int i = 0; i < n; ++i) {
     if (!w[i] || !x[i] || !y[i]) return fail(EP_E_ARG, "null blob, input or output");
-    if (w[i]->b.dtype != EP_BF16) return fail(EP_E_DTYPE, "compressed linear takes BF16 blobs");
+    if (w[i]->b.kind != kKindLossy || w[i]->b.dtype != EP_BF16)
+      return fail(EP_E_DTYPE, "compressed linear takes lossy BF16 blobs");
   }
   const size_t need = ep_linear_seq_workspace_bytes(w, n);
   if (ws_bytes < need) return fail(EP_E_WORKSPACE, "workspace too small");

@@ -295,4 +295,15 @@ void build_slot_tables(const Model& m, uint32_t* out, bool narrow) {
   }
 }
 
+void build_byte_tables(const int32_t (*F)[256], int n_ctx, uint32_t* out) {
+  for (int c = 0; c < n_ctx; ++c) {
+    int32_t cum = 0;
+    for (int v = 0; v < 256; ++v) {
+      for (int32_t q = 0; q < F[c][v]; ++q)
+        out[c * kM + cum + q] = uint32_t(F[c][v]) | (uint32_t(q) << 11) | (uint32_t(v) << 24);
+      cum += F[c][v];
+    }
+  }
+}
+
 }  // namespace ep

@@ -136,6 +136,7 @@ int ep_plan_bitrates(int n, int n_cand, const double* bits, const double* cost, 
 int ep_blob_distortion(const ep_blob* blob, double* sq_err, double* sq_ref) {
   set_error("");
   if (!blob || !sq_err || !sq_ref) return fail(EP_E_ARG, "null pointer");
+  if (blob->b.kind != kKindLossy) return fail(EP_E_ARG, "a lossless blob has no reconstruction error");
   if (blob->b.dist.sq_err < 0.0) return fail(EP_E_STATE, "distortion is known only for blobs compressed in this process");
   *sq_err = blob->b.dist.sq_err;
   *sq_ref = blob->b.dist.sq_ref;

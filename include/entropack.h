@@ -82,6 +82,20 @@ int ep_compress(const void* host_src, int dtype, int64_t rows, int64_t cols,
 int ep_compress_ex(const void* host_src, int dtype, int64_t rows, int64_t cols,
                    double target_bpp, int chains_per_tile, ep_blob** out);
 
+/* TileANS lossless compression ([README] Config：压缩配置: a lossless codec for BF16, FP16,
+ * FP32, FP8, INT8 and other dtypes whose ratio depends on the data; [NEWS]: tensors
+ * that are not 2-D take the lossless way).  host_src: the tensor's n_bytes raw bytes
+ * (C order, little-endian elements of elem_bytes = 1, 2, 4 or 8 bytes), dims[ndim]
+ * its shape (ndim 1..8, n_bytes = elem_bytes x prod(dims)), dtype_tag an opaque
+ * 0..255 label returned by ep_blob_dtype.  Bytes are coded with per-byte-position
+ * tables (byte index mod min(elem_bytes, 4)) or raw, in the lossy blob's tiles,
+ * chains and stream layout.  chains_per_tile 0 = default (8 from 4 MiB on, else 1).
+ * Decoded with ep_decompress / ep_decompress_tiles (tiles of 4096 bytes) /
+ * ep_decompress_batch into n_bytes (16-byte aligned).  Errors: EP_E_ARG, EP_E_SHAPE,
+ * EP_E_NOMEM. */
+int ep_compress_lossless(const void* host_src, int64_t n_bytes, int elem_bytes, const int64_t* dims, int ndim,
+                         int dtype_tag, int chains_per_tile, ep_blob** out);
+
 /* Copy the blob's stream, tile tables, row scales and the 7 expanded 2048-slot decode
  * tables to the current device (one H2D copy, enqueued on `stream`; the host side
  * waits for it).  Idempotent.  The device copy lives until ep_blob_free(). */
@@ -168,10 +182,18 @@ int ep_plan_bitrates(int n, int n_cand, const double* bits, const double* cost, 
 int ep_blob_distortion(const ep_blob* blob, double* sq_err, double* sq_ref);
 
 /* ---------------------------------------------------------------- blob accessors
- * actual_bpp = 8 * serialized bytes / (rows * cols)  ([README]: includes metadata). */
+ * actual_bpp = 8 * serialized bytes / elements  ([README]: includes metadata).
+ * ep_blob_shape: rows x cols of a lossy blob; 1 x elements of a TileANS blob.
+ * ep_blob_dtype: EP_* container of a lossy blob; the caller's tag of a TileANS blob. */
 double ep_actual_bpp(const ep_blob* blob);
 void ep_blob_shape(const ep_blob* blob, int64_t* rows, int64_t* cols);
 int ep_blob_dtype(const ep_blob* blob);
+/* 0 = lossy (E8 lattice), 1 = TileANS (lossless); -1 for NULL */
+int ep_blob_kind(const ep_blob* blob);
+/* the tensor's shape: writes up to max_dims extents, returns the rank (lossy: 2) */
+int ep_blob_dims(const ep_blob* blob, int64_t* dims, int max_dims);
+/* bytes per element of the decoded tensor */
+int ep_blob_elem_bytes(const ep_blob* blob);
 /* chains per tile, K_LOG2, flags (bit0 escapes present, bit1 clamping needed) */
 void ep_blob_params(const ep_blob* blob, int* chains_per_tile, int* k_log2, int* flags);
 

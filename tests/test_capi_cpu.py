@@ -225,3 +225,73 @@ def test_plan_bitrates_api_matches_oracle_pipeline():
     assert len(set(targets)) > 1            # the matrices differ enough to get different rates
     # uniform 3.0 fits the same budget; the plan does better on the summed error
     assert sum(cost[i][j] for i, j in enumerate(want)) < sum(cost[i][1] for i in range(len(mats)))
+
+
+# ---------------------------------------------------------------- TileANS (lossless)
+def _lossless_blob(a, E, S=0, tag=7):
+    raw = np.frombuffer(np.ascontiguousarray(a).tobytes(), dtype=np.uint8).copy()
+    h = L.ep_compress_lossless(raw.ctypes.data, len(raw), E, a.shape, tag, S)
+    try:
+        return L.ep_serialize(h), L.ep_actual_bpp(h), L.ep_blob_kind(h), L.ep_blob_dims(h), L.ep_blob_dtype(h), \
+            L.ep_blob_elem_bytes(h), L.ep_blob_shape(h)
+    finally:
+        L.ep_blob_free(h)
+
+
+TA_CASES = [
+    ("bf16", lambda: synth.rowscaled(96, 200, 1), 2, 0),
+    ("bf16 S8", lambda: synth.rowscaled(64, 1024, 2), 2, 8),
+    ("fp32 3-d", lambda: synth.rowscaled_f32(8, 24, 3).reshape(2, 4, 24), 4, 2),
+    ("fp16 1-d ragged", lambda: synth.rowscaled_f32(1, 1001, 4).astype(np.float16).reshape(-1), 2, 1),
+    ("fp8", lambda: synth.fp8_codes(64, 136, 5)[0], 1, 4),
+    ("int8 S64", lambda: synth.int8_codes(32, 520, 6)[0], 1, 64),
+    ("int64 4-d", lambda: np.random.default_rng(7).integers(-5, 5, size=(2, 3, 5, 7)), 8, 0),
+    ("one byte", lambda: np.array([200], dtype=np.uint8), 1, 0),
+    ("zeros", lambda: np.zeros((33, 17), dtype=np.uint16), 2, 0),
+    ("random", lambda: np.random.default_rng(8).integers(0, 256, size=5000, dtype=np.uint8), 1, 0),
+    ("bf16 4 MiB", lambda: synth.rowscaled(1024, 2048, 9), 2, 0),
+]
+
+
+@pytest.mark.parametrize("name,gen,E,S", TA_CASES, ids=[c[0] for c in TA_CASES])
+def test_tileans_byte_parity(name, gen, E, S):
+    from oracle import tileans
+    a = gen()
+    got, bpp, kind, dims, tag, eb, shape = _lossless_blob(a, E, S)
+    raw = np.frombuffer(np.ascontiguousarray(a).tobytes(), dtype=np.uint8)
+    want = tileans.compress(raw, E, a.shape, 7, chains_per_tile=S or None)
+    assert got == want
+    assert kind == 1 and dims == tuple(a.shape) and tag == 7 and eb == E and shape == (1, a.size)
+    assert abs(bpp - 8.0 * len(want) / a.size) < 1e-12
+    h = L.ep_deserialize(got)          # read back: same accessors
+    try:
+        assert L.ep_blob_kind(h) == 1 and L.ep_blob_dims(h) == tuple(a.shape)
+    finally:
+        L.ep_blob_free(h)
+
+
+def test_tileans_validation():
+    from oracle import tileans
+    raw = np.zeros(64, np.uint8)
+    for args, code in [((raw.ctypes.data, 64, 3, (64,)), "EP_E_ARG"), ((raw.ctypes.data, 60, 2, (32,)), "EP_E_SHAPE"),
+                       ((raw.ctypes.data, 64, 1, (0, 64)), "EP_E_SHAPE"), ((raw.ctypes.data, 64, 1, (64,), 300), "EP_E_ARG")]:
+        with pytest.raises(L.EPError) as ei:
+            L.ep_compress_lossless(*args)
+        assert ei.value.name == code, args
+    blob = bytearray(tileans.compress(np.arange(4096, dtype=np.uint16), 2, (4096,)))
+    for cut in (len(blob) - 2, 40, 60):
+        with pytest.raises(L.EPError) as ei:
+            L.ep_deserialize(bytes(blob[:cut]))
+        assert ei.value.name == "EP_E_CORRUPT"
+    bad = bytearray(blob)
+    bad[48 + 8 + 5] ^= 0x40            # a table entry: the table no longer sums to 2048
+    with pytest.raises(L.EPError) as ei:
+        L.ep_deserialize(bytes(bad))
+    assert ei.value.name == "EP_E_CORRUPT"
+    # lossy-only calls refuse a lossless blob
+    h = L.ep_deserialize(bytes(blob))
+    try:
+        with pytest.raises(L.EPError):
+            L.ep_blob_distortion(h)
+    finally:
+        L.ep_blob_free(h)
