@@ -18,8 +18,10 @@
 #include <atomic>
 #include <cmath>
 #include <cstdlib>
+#include <functional>
 #include <thread>
 
+#include "codec_math.h"
 #include "ep_internal.h"
 
 namespace ep {
@@ -53,52 +55,8 @@ void parallel_for(int64_t n, Fn fn, int64_t min_chunk = 1) {
 }
 
 // ------------------------------------------------------------------ containers
-double fp8_e4m3fn_value(uint8_t b) {
-  int e = (b >> 3) & 15, m = b & 7;
-  double v;
-  if (e == 0) v = std::ldexp(m / 8.0, -6);
-  else v = std::ldexp(1.0 + m / 8.0, e - 7);
-  if (e == 15 && m == 7) v = NAN;
-  return (b & 0x80) ? -v : v;
-}
-
-double fp16_value(uint16_t h) {
-  int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
-  double v;
-  if (e == 0) v = std::ldexp((double)m, -24);
-  else if (e == 31) v = m ? NAN : INFINITY;
-  else v = std::ldexp(1.0 + m / 1024.0, e - 15);
-  return s ? -v : v;
-}
-
 void widen(const void* src, int dtype, int64_t n, double* out) {
-  switch (dtype) {
-    case EP_BF16: {
-      auto p = (const uint16_t*)src;
-      for (int64_t i = 0; i < n; ++i) out[i] = (double)bf16_to_f32(p[i]);
-      break;
-    }
-    case EP_FP16: {
-      auto p = (const uint16_t*)src;
-      for (int64_t i = 0; i < n; ++i) out[i] = fp16_value(p[i]);
-      break;
-    }
-    case EP_FP32: {
-      auto p = (const float*)src;
-      for (int64_t i = 0; i < n; ++i) out[i] = (double)p[i];
-      break;
-    }
-    case EP_FP8_E4M3FN: {
-      auto p = (const uint8_t*)src;
-      for (int64_t i = 0; i < n; ++i) out[i] = fp8_e4m3fn_value(p[i]);
-      break;
-    }
-    case EP_INT8: {
-      auto p = (const int8_t*)src;
-      for (int64_t i = 0; i < n; ++i) out[i] = (double)p[i];
-      break;
-    }
-  }
+  for (int64_t i = 0; i < n; ++i) out[i] = cm::widen_one(src, dtype, i);
 }
 
 double container_max(int dtype) {
@@ -111,95 +69,9 @@ double container_max(int dtype) {
   }
 }
 
-// ------------------------------------------------------------------ E8
-inline void d8_nearest(const double* v, double* f) {
-  double s = 0.0;
-  for (int i = 0; i < 8; ++i) {
-    f[i] = std::nearbyint(v[i]);
-    s += f[i];
-  }
-  if (std::fmod(s, 2.0) != 0.0) {
-    int best = 0;
-    double be = std::fabs(v[0] - f[0]);
-    for (int i = 1; i < 8; ++i) {
-      double e = std::fabs(v[i] - f[i]);
-      if (e > be) {
-        be = e;
-        best = i;
-      }
-    }
-    f[best] += (v[best] - f[best] >= 0.0) ? 1.0 : -1.0;
-  }
-}
-
-inline void e8_doubled(const double* y, int32_t* u) {
-  double p0[8], p1[8], ym[8];
-  d8_nearest(y, p0);
-  for (int i = 0; i < 8; ++i) ym[i] = y[i] - 0.5;
-  d8_nearest(ym, p1);
-  for (int i = 0; i < 8; ++i) p1[i] += 0.5;
-  double t = y[0] - p0[0];
-  double d0 = t * t;
-  for (int i = 1; i < 8; ++i) {
-    t = y[i] - p0[i];
-    d0 = d0 + t * t;
-  }
-  t = y[0] - p1[0];
-  double d1 = t * t;
-  for (int i = 1; i < 8; ++i) {
-    t = y[i] - p1[i];
-    d1 = d1 + t * t;
-  }
-  const double* p = (d1 < d0) ? p1 : p0;
-  for (int i = 0; i < 8; ++i) u[i] = (int32_t)(2.0 * p[i]);
-}
-
-// ------------------------------------------------------------------ symbols
-struct Sym {
-  int ctx, id, rawbits;
-  uint32_t rawval;
-};
-
-inline int ilog2(uint32_t v) { return 31 - __builtin_clz(v); }
-
-// u -> 8 coded symbols in decoding order; returns coset; msym[] for counting.
-inline int symbolize(const int32_t* u, int k, Sym* s, int* msym) {
-  const int K = 1 << k;
-  int c = u[0] & 1;
-  int q_sum = 0;
-  int neg[8], raw_rb[8];
-  uint32_t raw[8];
-  for (int i = 0; i < 8; ++i) {
-    int a = u[i] < 0 ? -u[i] : u[i];
-    uint32_t m = (uint32_t)((a - c) >> 1);
-    neg[i] = u[i] < 0;
-    if ((int64_t)m < K) {
-      msym[i] = (int)m;
-      raw[i] = 0;
-      raw_rb[i] = 0;
-    } else {
-      int e = ilog2(m);
-      int top2 = (m >> (e - 2)) & 3;
-      msym[i] = K + 4 * (e - k) + top2;
-      raw[i] = m & ((1u << (e - 2)) - 1u);
-      raw_rb[i] = e - 2;
-    }
-    if (i < 7) q_sum += (u[i] >> 1);
-  }
-  int pi = q_sum & 1;
-  for (int i = 0; i < 8; ++i) {
-    int sid = 2 * msym[i] + neg[i];
-    s[i].ctx = i == 0 ? 0 : (i < 7 ? 1 + c : 3 + 2 * c + pi);
-    s[i].id = i == 0 ? 512 * c + sid : sid;
-    s[i].rawval = raw[i];
-    s[i].rawbits = raw_rb[i];
-  }
-  if (msym[7] >= K) {           // the low raw bit of the last coordinate is implied
-    s[7].rawval >>= 1;
-    s[7].rawbits -= 1;
-  }
-  return c;
-}
+using cm::Sym;
+using cm::e8_doubled;
+using cm::symbolize;
 
 // ------------------------------------------------------------------ row geometry
 struct Matrix {
@@ -237,20 +109,7 @@ void quantize_row(const Matrix& mx, int64_t r, float delta, int32_t* u_out) {
   }
 }
 
-bool admissible(const Matrix& mx, float delta) {
-  for (int64_t r = 0; r < mx.R; ++r) {
-    if (!(mx.s[r] > 0.f)) continue;
-    float h = mx.s[r] * delta;
-    if (!(h > 0.f) || !std::isfinite(h)) return false;
-    if (!(mx.amax[r] / (2.0 * (double)h) < 536870912.0)) return false;
-  }
-  return true;
-}
-
-struct Estimate {
-  int64_t est;
-  int k;
-};
+bool admissible(const Matrix& mx, float delta) { return resolution_admissible(mx.s.data(), mx.amax.data(), mx.R, delta); }
 
 // est(delta) over the sample rows.
 Estimate estimate(const Matrix& mx, const std::vector<int64_t>& rows, float delta) {
@@ -521,6 +380,80 @@ void encode_chain_bytes(const uint8_t* by, const int32_t (*F)[256], const int32_
 
 }  // namespace
 
+bool resolution_admissible(const float* s, const double* amax, int64_t R, float delta) {
+  for (int64_t r = 0; r < R; ++r) {
+    if (!(s[r] > 0.f)) continue;
+    float h = s[r] * delta;
+    if (!(h > 0.f) || !std::isfinite(h)) return false;
+    if (!(amax[r] / (2.0 * (double)h) < 536870912.0)) return false;
+  }
+  return true;
+}
+
+// The resolution search over float32 bit patterns: bracket between powers of two from
+// 2^floor(1 - t) (within [2^jmin, 2^4]), then bisect to adjacent patterns, keeping the
+// largest delta whose sampled estimate reaches T; the finest admissible delta if the
+// target is out of reach.  Estimates are computed once per pattern.
+void select_resolution(double t, int64_t T, int jmin, const std::function<Estimate(uint32_t)>& estimate_at,
+                       uint32_t* dbits_out, int* k_out) {
+  struct Probe {
+    uint32_t bits;
+    Estimate e;
+  };
+  std::vector<Probe> cache;
+  auto est_at = [&](uint32_t bits) -> Estimate {
+    for (auto& p : cache)
+      if (p.bits == bits) return p.e;
+    Estimate e = estimate_at(bits);
+    cache.push_back({bits, e});
+    return e;
+  };
+  auto ok = [&](uint32_t bits) { return est_at(bits).est >= T; };
+  auto pow2bits = [](int j) {
+    float f = std::ldexp(1.0f, j);
+    uint32_t b;
+    std::memcpy(&b, &f, 4);
+    return b;
+  };
+  const int jmax = 4;
+  int j0 = (int)std::floor(1.0 - t);
+  j0 = std::min(std::max(j0, jmin), jmax);
+  uint32_t dbits = 0;
+  bool done = false;
+  uint32_t lo = 0, hi = 0;
+  if (ok(pow2bits(j0))) {
+    int j = j0;
+    while (j < jmax && ok(pow2bits(j + 1))) ++j;
+    if (j == jmax) {
+      dbits = pow2bits(j);
+      done = true;
+    } else {
+      lo = pow2bits(j);
+      hi = pow2bits(j + 1);
+    }
+  } else {
+    int j = j0 - 1;
+    while (j >= jmin && !ok(pow2bits(j))) --j;
+    if (j < jmin) {
+      dbits = pow2bits(jmin);
+      done = true;
+    } else {
+      lo = pow2bits(j);
+      hi = pow2bits(j + 1);
+    }
+  }
+  if (!done) {
+    while (hi - lo > 1) {
+      uint32_t mid = lo + ((hi - lo) >> 1);
+      if (ok(mid)) lo = mid;
+      else hi = mid;
+    }
+    dbits = lo;
+  }
+  *dbits_out = dbits;
+  *k_out = est_at(dbits).k;
+}
+
 int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_req,
              std::vector<uint8_t>* out, Distortion* dist) {
   if (!src || !out) return fail(EP_E_ARG, "null pointer");
@@ -591,64 +524,17 @@ int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_r
   const int64_t T = (int64_t)std::ceil(t * 65536.0 * (double)n_sample);
 
   // ---- resolution search
-  struct Probe {
-    uint32_t bits;
-    Estimate e;
-  };
-  std::vector<Probe> cache;
-  auto est_at = [&](uint32_t bits) -> Estimate {
-    for (auto& p : cache)
-      if (p.bits == bits) return p.e;
-    Estimate e = estimate(mx, rows, f32_from_bits(bits));
-    cache.push_back({bits, e});
-    return e;
-  };
-  auto ok = [&](uint32_t bits) { return est_at(bits).est >= T; };
-  auto pow2bits = [](int j) { return f32_bits(std::ldexp(1.0f, j)); };
-  const int jmax = 4;
   int jmin = 999;
-  for (int j = -126; j <= jmax; ++j)
+  for (int j = -126; j <= 4; ++j)
     if (admissible(mx, std::ldexp(1.0f, j))) {
       jmin = j;
       break;
     }
   if (jmin == 999) return fail(EP_E_RANGE, "no admissible resolution");
-  int j0 = (int)std::floor(1.0 - t);
-  j0 = std::min(std::max(j0, jmin), jmax);
   uint32_t dbits;
-  bool done = false;
-  uint32_t lo = 0, hi = 0;
-  if (ok(pow2bits(j0))) {
-    int j = j0;
-    while (j < jmax && ok(pow2bits(j + 1))) ++j;
-    if (j == jmax) {
-      dbits = pow2bits(j);
-      done = true;
-    } else {
-      lo = pow2bits(j);
-      hi = pow2bits(j + 1);
-    }
-  } else {
-    int j = j0 - 1;
-    while (j >= jmin && !ok(pow2bits(j))) --j;
-    if (j < jmin) {
-      dbits = pow2bits(jmin);
-      done = true;
-    } else {
-      lo = pow2bits(j);
-      hi = pow2bits(j + 1);
-    }
-  }
-  if (!done) {
-    while (hi - lo > 1) {
-      uint32_t mid = lo + ((hi - lo) >> 1);
-      if (ok(mid)) lo = mid;
-      else hi = mid;
-    }
-    dbits = lo;
-  }
+  int k;
+  select_resolution(t, T, jmin, [&](uint32_t bits) { return estimate(mx, rows, f32_from_bits(bits)); }, &dbits, &k);
   const float delta = f32_from_bits(dbits);
-  const int k = est_at(dbits).k;
 
   // ---- full quantisation
   const int64_t n_groups = R * mx.G;

@@ -12,6 +12,7 @@
 #pragma once
 #include <cstdint>
 #include <cstring>
+#include <functional>
 #include <string>
 #include <vector>
 
@@ -80,6 +81,14 @@ struct Distortion {
 };
 int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_req, std::vector<uint8_t>* out,
              Distortion* dist);
+// Sampled storage estimate (2^-16 bits) at one resolution, and the k it chose.
+struct Estimate {
+  int64_t est;
+  int k;
+};
+bool resolution_admissible(const float* s, const double* amax, int64_t R, float delta);
+void select_resolution(double t, int64_t T, int jmin, const std::function<Estimate(uint32_t)>& estimate_at,
+                       uint32_t* dbits, int* k);
 // TileANS (lossless) blob of a tensor's raw bytes.
 int compress_lossless(const void* src, int64_t n_bytes, int E, const int64_t* dims, int ndim, int tag, int S_req,
                       std::vector<uint8_t>* out);
