@@ -38,6 +38,7 @@ SIGNATURES = {
     "ep_plan_bitrates": (_int, [_int, _int, C.POINTER(_dbl), C.POINTER(_dbl), _dbl, C.POINTER(_int)]),
     "ep_blob_distortion": (_int, [_vp, C.POINTER(_dbl), C.POINTER(_dbl)]),
     "ep_actual_bpp": (_dbl, [_vp]),
+    "ep_compress_device": (_int, [_vp, _int, _i64, _i64, _dbl, _int, _vp, C.POINTER(_vp)]),
     "ep_compress_lossless": (_int, [_vp, _i64, _int, C.POINTER(_i64), _int, _int, _int, C.POINTER(_vp)]),
     "ep_blob_kind": (_int, [_vp]),
     "ep_blob_dims": (_int, [_vp, C.POINTER(_i64), _int]),
@@ -165,6 +166,14 @@ def ep_blob_distortion(blob: int):
     e, r = _dbl(), _dbl()
     check(lib().ep_blob_distortion(blob, C.byref(e), C.byref(r)))
     return e.value, r.value
+
+
+def ep_compress_device(dev_ptr: int, dtype: int, rows: int, cols: int, target_bpp: float,
+                       chains_per_tile: int = 0, stream: int = 0) -> int:
+    out = _vp()
+    check(lib().ep_compress_device(dev_ptr, dtype, rows, cols, float(target_bpp), chains_per_tile, stream,
+                                   C.byref(out)))
+    return out.value
 
 
 def ep_compress_lossless(src_ptr: int, n_bytes: int, elem_bytes: int, dims, dtype_tag: int = 0,

@@ -17,7 +17,7 @@ OUT = os.path.join(HERE, "libentropack_hip.so")
 BUILD = os.path.join(ROOT, "_build")
 
 HOST_SRCS = ["model.cpp", "encoder.cpp", "blob.cpp", "plan.cpp"]
-HIP_SRCS = ["decode.hip", "gemm.hip"]
+HIP_SRCS = ["decode.hip", "gemm.hip", "encode_gpu.hip"]
 ARCH = os.environ.get("EP_OFFLOAD_ARCH", "gfx950")
 
 

@@ -82,6 +82,18 @@ int ep_compress(const void* host_src, int dtype, int64_t rows, int64_t cols,
 int ep_compress_ex(const void* host_src, int dtype, int64_t rows, int64_t cols,
                    double target_bpp, int chains_per_tile, ep_blob** out);
 
+/* The same compression on the GPU ([README] 快速开始 / [NEWS]: GPU encode and decode;
+ * [README] 性能: 276 layers compressed in seconds): dev_src is a device array of rows x
+ * cols container values; row statistics, the E8 quantisation of every resolution probe,
+ * the symbol counts, the rANS chains, the fetch schedule and the stream layout run on
+ * the device (on `stream`; the call returns when the blob is complete), the search
+ * and model construction on the host.  The blob is byte-identical to ep_compress_ex's
+ * with the same arguments.  Uses temporary device memory of about 36 bytes per
+ * coordinate plus 50 bytes per group of 8 at one chain per tile.  Errors as
+ * ep_compress_ex, plus EP_E_NOMEM / EP_E_DEVICE. */
+int ep_compress_device(const void* dev_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
+                       int chains_per_tile, ep_stream stream, ep_blob** out);
+
 /* TileANS lossless compression ([README] Config：压缩配置: a lossless codec for BF16, FP16,
  * FP32, FP8, INT8 and other dtypes whose ratio depends on the data; [NEWS]: tensors
  * that are not 2-D take the lossless way).  host_src: the tensor's n_bytes raw bytes
