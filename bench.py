@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--no-linear", action="store_true")
     p.add_argument("--no-layer-mode", action="store_true")
     p.add_argument("--no-lossless", action="store_true")
+    p.add_argument("--no-gpu-encode", action="store_true")
     p.add_argument("--matrices", type=int, default=276, help="first N matrices of the stack (profiling runs)")
     p.add_argument("--streams", type=int, default=3, help="HIP streams the block launches rotate over")
     p.add_argument("--copy-calibration", action="store_true",
@@ -334,6 +335,39 @@ def lossless_block(reps=10):
             "host_encode_s": round(t_enc, 2), "bit_exact": ok}
 
 
+def gpu_encode_stack(n, target_bpp):
+    """The GPU encoder over the stack: every matrix already in HBM (BF16), compressed in
+    turn on one stream; wall time of the whole pass against the host encoder's rate on a
+    few matrices (all host cores)."""
+    import torch
+    import synth
+    from decode_tile_rans_amd import _lib as L
+    ws = [synth.dit_stack_torch(i) for i in range(n)]
+    torch.cuda.synchronize()
+    sp = int(torch.cuda.current_stream().cuda_stream)
+    h = L.ep_compress_device(ws[0].data_ptr(), L.EP_BF16, ws[0].shape[0], ws[0].shape[1], target_bpp, 0, sp)
+    L.ep_blob_free(h)
+    t0 = time.time()
+    nbytes = 0
+    for w in ws:
+        h = L.ep_compress_device(w.data_ptr(), L.EP_BF16, w.shape[0], w.shape[1], target_bpp, 0, sp)
+        nbytes += L.ep_serialized_size(h)
+        L.ep_blob_free(h)
+    dt = time.time() - t0
+    params = sum(w.numel() for w in ws)
+    # host encoder on the first 9 matrices (one transformer block)
+    hs = [w.cpu() for w in ws[:9]]
+    t1 = time.time()
+    for w in hs:
+        h = L.ep_compress(w.data_ptr(), L.EP_BF16, w.shape[0], w.shape[1], target_bpp, 0)
+        L.ep_blob_free(h)
+    dh = time.time() - t1
+    hp = sum(w.numel() for w in hs)
+    return {"workload": f"GPU encoder, {n} stack matrices (BF16, resident in HBM), target {target_bpp} bpp",
+            "seconds": round(dt, 3), "params_per_s": round(params / dt, 1), "actual_bpp": round(8.0 * nbytes / params, 4),
+            "host_encoder_params_per_s": round(hp / dh, 1), "host_threads": os.cpu_count()}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -393,6 +427,8 @@ def main():
         result["fused_linear"] = fused_linear(a.target_bpp)
     if not a.no_lossless:
         result["lossless"] = lossless_block()
+    if not a.no_gpu_encode:
+        result["gpu_encode"] = gpu_encode_stack(a.matrices, a.target_bpp)
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(a.target_bpp)
     print(json.dumps(result))
