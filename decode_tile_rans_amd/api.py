@@ -84,8 +84,20 @@ class Compressed:
                 pass
 
 
-def compress(x, target_bpp: float, dtype=None, chains_per_tile: int = 0) -> Compressed:
-    """Compress a 2-D tensor (torch on any device, or numpy with ``dtype`` = torch dtype)."""
+def compress(x, target_bpp: float, dtype=None, chains_per_tile: int = 0, stream=None) -> Compressed:
+    """Compress a 2-D tensor (torch on any device, or numpy with ``dtype`` = torch dtype).
+
+    A tensor on the GPU is compressed there (ep_compress_device); the blob is the same,
+    byte for byte, as the host encoder's."""
+    if isinstance(x, torch.Tensor) and x.is_cuda:
+        if x.dim() != 2:
+            raise EPError(-4, "lossy compression takes 2-D tensors only")
+        if x.dtype not in _TORCH_TO_EP:
+            raise EPError(-3, f"unsupported dtype {x.dtype}")
+        xc = x.detach().contiguous()
+        h = L.ep_compress_device(xc.data_ptr(), _TORCH_TO_EP[xc.dtype], xc.shape[0], xc.shape[1], float(target_bpp),
+                                 chains_per_tile, _stream_ptr(stream))
+        return Compressed(h)
     if isinstance(x, np.ndarray):
         if dtype is None:
             raise ValueError("numpy input needs dtype= (a torch dtype)")

@@ -65,6 +65,7 @@ struct DecJob {
   uint32_t s_div_g, s_mod_g;   // S = s_div_g * G + s_mod_g (group stride in rows / columns)
   uint32_t R;
   uint32_t ctx_mask;           // TileANS: byte contexts - 1 (symbol i of a group uses i & ctx_mask)
+  uint32_t tab_words;          // table words to stage
 };
 
 // ---------------------------------------------------------------- container stores
@@ -551,7 +552,7 @@ __device__ __forceinline__ void ch_group_careful(uint32_t lds0, Chain& r, int k,
 // waits about one memory latency for both.
 struct TabStager {
   static constexpr int kQ = kM / 4;   // uint4 per table
-  static constexpr int kN = kTabWords / 4;
+  int kN;                             // uint4 to stage (at most kTabWords / 4)
   const uint4* src;
   uint4* dst;
   int tid, nt;
@@ -941,6 +942,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   st.tid = tid;
   st.nt = (int)blockDim.x;
   st.swap = OUT != OUT_BYTES;
+  st.kN = (int)(J.tab_words / 4);
 
   GroupCtx X;
   X.J = &J;
@@ -1061,6 +1063,8 @@ DecJob make_job(const Blob& b, void* out) {
   j.s_mod_g = (uint32_t)(b.S % j.G);
   j.R = (uint32_t)b.R;
   j.ctx_mask = b.kind == kKindTileAns ? (uint32_t)(b.n_ctx - 1) : 0u;
+  // TileANS stages only its contexts' tables
+  j.tab_words = b.kind == kKindTileAns ? (uint32_t)(b.n_ctx * kM) : (uint32_t)kTabWords;
   return j;
 }
 

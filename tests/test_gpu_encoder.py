@@ -102,3 +102,17 @@ def test_gpu_encoder_errors():
     with pytest.raises(L.EPError) as ei:
         _gpu_blob(synth.rowscaled(8, 16, 1), nx.DT_BF16, 12.0)
     assert ei.value.name == "EP_E_RANGE"
+
+
+def test_api_compress_on_gpu_tensor():
+    # ep.compress of a CUDA tensor goes through the GPU encoder and gives the same bytes
+    # as compressing the host copy
+    import torch
+    import decode_tile_rans_amd as ep
+    w = torch.from_numpy(synth.rowscaled(256, 1024, 77)).view(torch.bfloat16)
+    c_gpu = ep.compress(w.cuda(), 3.5)
+    c_cpu = ep.compress(w, 3.5)
+    assert c_gpu.to_bytes() == c_cpu.to_bytes()
+    y = ep.decompress(c_gpu)
+    torch.cuda.synchronize()
+    assert y.shape == w.shape and y.dtype == torch.bfloat16
