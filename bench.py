@@ -94,6 +94,9 @@ def build_stack(n, target_bpp):
     return comps, [blocks[b] for b in sorted(blocks)]
 
 
+_SIDE_STREAMS = []
+
+
 def time_stack(comps, blocks, outs, steps, warmup, per_layer=False, n_streams=1):
     """Time `steps` passes over the stack.  Consecutive launches rotate over n_streams
     streams (default priority) so one launch's tail overlaps the next one's start; every
@@ -101,7 +104,12 @@ def time_stack(comps, blocks, outs, steps, warmup, per_layer=False, n_streams=1)
     import torch
     from decode_tile_rans_amd import _lib as L
     main = torch.cuda.current_stream()
-    streams = [main] + [torch.cuda.Stream() for _ in range(n_streams - 1)]
+    # side streams are created once per process and reused: each new HIP stream is bound
+    # to one of the runtime's few hardware queues in turn, and a side stream that shares
+    # the main stream's queue would serialise with it
+    while len(_SIDE_STREAMS) < n_streams - 1:
+        _SIDE_STREAMS.append(torch.cuda.Stream())
+    streams = [main] + _SIDE_STREAMS[:n_streams - 1]
     handles = [c.handle for c in comps]
     ptrs = [o.data_ptr() for o in outs]
     units = [[i] for i in range(len(comps))] if per_layer else blocks
