@@ -272,7 +272,9 @@ def linear_sequence(c0, wbits0, x, T, target_bpp, timeit, n_layers=8):
     ys = [torch.empty((T, R), dtype=torch.bfloat16, device="cuda") for _ in layers]
     st = torch.cuda.current_stream()
     sp = int(st.cuda_stream)
-    side = torch.cuda.Stream()
+    if not _SIDE_STREAMS:
+        _SIDE_STREAMS.append(torch.cuda.Stream())
+    side = _SIDE_STREAMS[0]      # (the first side stream: not on the main stream's queue)
     need = L.ep_linear_seq_workspace_bytes(hs)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     n1 = L.ep_linear_workspace_bytes(hs[0])
