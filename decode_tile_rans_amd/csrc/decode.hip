@@ -1119,6 +1119,21 @@ Shape pick_shape(const int64_t* n_blocks, int n) {
   return Shape{ilp, waves, bpw};
 }
 
+}  // namespace
+
+// A pointer the GPU may dereference: device or managed memory, or pinned host memory.
+// (A pageable host pointer would fault the kernel; HIP does not know it.)
+int check_gpu_pointer(const void* p, const char* what) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess || a.type == hipMemoryTypeUnregistered) {
+    (void)hipGetLastError();
+    return fail(EP_E_ARG, std::string(what) + " is not memory the GPU can access");
+  }
+  return EP_OK;
+}
+
+namespace {
+
 int check_uploaded(const Blob& b) {
   if (!b.d_base) return fail(EP_E_STATE, "blob not uploaded (call ep_blob_upload)");
   int dev = -1;
@@ -1131,6 +1146,7 @@ int decode_one(const Blob& b, void* dst, int64_t chain_lo, int64_t chain_hi, int
   int rc = check_uploaded(b);
   if (rc) return rc;
   if (!dst) return fail(EP_E_ARG, "null destination");
+  if ((rc = check_gpu_pointer(dst, "destination"))) return rc;
   if (out != OUT_COORDS && (reinterpret_cast<uintptr_t>(dst) & 15)) return fail(EP_E_ARG, "destination must be 16-byte aligned");
   if (out == OUT_COORDS && (reinterpret_cast<uintptr_t>(dst) & 15)) return fail(EP_E_ARG, "destination must be 16-byte aligned");
   DecJob j = make_job(b, dst);
@@ -1286,6 +1302,7 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
     int rc = check_uploaded(b);
     if (rc) return rc;
     if (reinterpret_cast<uintptr_t>(dsts[i]) & 15) return fail(EP_E_ARG, "destination must be 16-byte aligned");
+    if ((rc = check_gpu_pointer(dsts[i], "destination"))) return rc;
     const int o = out_kind(b);
     if (out < 0) out = o;
     else if ((out == OUT_BF16 || out == OUT_BF16_SAT) && (o == OUT_BF16 || o == OUT_BF16_SAT))

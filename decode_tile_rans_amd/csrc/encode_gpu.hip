@@ -354,6 +354,7 @@ int compress_device(const void* dsrc, int dtype, int64_t R, int64_t C, double t,
   const int64_t N = R * C;
   const int64_t n_groups = R * G;
   int rc;
+  if ((rc = check_gpu_pointer(dsrc, "source"))) return rc;
   auto hc = [&](hipError_t e, const char* what) { return hip_check((int)e, what); };
 
   // ---- row statistics

@@ -147,6 +147,8 @@ inline uint16_t f32_to_bf16_rne(float f) {
 }
 
 int hip_check(int err, const char* what);
+// EP_E_ARG unless the GPU can dereference p (device, managed or pinned host memory)
+int check_gpu_pointer(const void* p, const char* what);
 
 }  // namespace ep
 

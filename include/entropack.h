@@ -116,7 +116,9 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream);
 /* ---------------------------------------------------------------- decode
  * ep_decompress — [SUM]: fused symbol decode + algebraic inverse lattice + row rescale.
  * Writes rows*cols elements of the blob's container dtype, row-major, to dev_dst.
- * No intermediate symbol or coordinate tensor is written. */
+ * No intermediate symbol or coordinate tensor is written.  Every decode entry point
+ * refuses (EP_E_ARG, before any launch) a destination the GPU cannot dereference
+ * (pageable host memory); device, managed and pinned host memory are accepted. */
 int ep_decompress(const ep_blob* blob, void* dev_dst, ep_stream stream);
 
 /* Decode only tiles [tile_begin, tile_end) (each 4096 coordinates = 512 groups of

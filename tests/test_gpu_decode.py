@@ -320,3 +320,18 @@ def test_corrupt_stream_flags_error():
     db = DevBlob(blob)
     db.decode()
     assert db.errors() > 0
+
+
+def test_host_pointer_destination_refused():
+    # a pageable host buffer as the destination is refused before any launch
+    from decode_tile_rans_amd import _lib as L
+    blob = oracle.compress(synth.rowscaled(64, 64, 3), nx.DT_BF16, 4.0)
+    db = DevBlob(blob)
+    host = np.zeros(64 * 64 + 64, dtype=np.uint16)
+    p = host.ctypes.data + ((16 - host.ctypes.data % 16) % 16)
+    with pytest.raises(L.EPError) as ei:
+        L.ep_decompress(db.h, p, 0)
+    assert ei.value.name == "EP_E_ARG"
+    with pytest.raises(L.EPError) as ei:
+        L.ep_decompress_batch([db.h], [p], 0)
+    assert ei.value.name == "EP_E_ARG"

@@ -116,3 +116,11 @@ def test_api_compress_on_gpu_tensor():
     y = ep.decompress(c_gpu)
     torch.cuda.synchronize()
     assert y.shape == w.shape and y.dtype == torch.bfloat16
+
+
+def test_host_pointer_source_refused():
+    from decode_tile_rans_amd import _lib as L
+    src = np.ascontiguousarray(synth.rowscaled(16, 64, 1))
+    with pytest.raises(L.EPError) as ei:
+        L.ep_compress_device(src.ctypes.data, nx.DT_BF16, 16, 64, 4.0, 0, 0)
+    assert ei.value.name == "EP_E_ARG"
