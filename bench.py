@@ -345,6 +345,52 @@ def lossless_block(reps=10):
             "host_encode_s": round(t_enc, 2), "bit_exact": ok}
 
 
+def fp8_linear(reps=10):
+    """FP8@5 ([README]/[NEWS]: FP8 W8A8 weight codes compressed at 5 bpp, FP8 GEMM): decode
+    the 14336x4096 code tensor to FP8, then the FP8 MFMA GEMM with 4096 FP8 activations."""
+    import torch
+    import synth
+    import decode_tile_rans_amd as ep
+    from decode_tile_rans_amd import _lib as L
+    R, C, T = 14336, 4096, 4096
+    wq, aw = synth.fp8_codes(R, C, 5)
+    xq, ax_rows = synth.fp8_codes(T, C, 50)
+    c = ep.compress(wq, 5.0, dtype=torch.float8_e4m3fn)
+    c.upload()
+    wd = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+    xt = torch.from_numpy(xq).cuda()
+    awt = torch.from_numpy(aw).cuda()
+    y = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
+    a_x = float(ax_rows.max())
+    st = torch.cuda.current_stream()
+    sp = int(st.cuda_stream)
+
+    def timeit(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def gemm():
+        L.ep_gemm_fp8_nt(xt.data_ptr(), wd.data_ptr(), a_x, awt.data_ptr(), y.data_ptr(), T, R, C, sp)
+
+    t_dec = timeit(lambda: L.ep_decompress(c.handle, wd.data_ptr(), sp))
+    t_gemm = timeit(gemm)
+    t_both = timeit(lambda: (L.ep_decompress(c.handle, wd.data_ptr(), sp), gemm()))
+    flops = 2.0 * T * R * C
+    return {"workload": "FP8@5: 14336x4096 E4M3FN weight codes @5.0 bpp, FP8 GEMM with 4096 FP8 tokens",
+            "actual_bpp": round(c.actual_bpp, 4), "ms_decode": round(t_dec, 4), "ms_fp8_gemm": round(t_gemm, 4),
+            "ms_decode_plus_gemm": round(t_both, 4), "fp8_gemm_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 1),
+            "fp8_mfma_util": round(flops / (t_gemm * 1e-3) / 1e12 / 5000.0, 4),
+            "overhead_pct": round(100.0 * (t_both / t_gemm - 1.0), 2)}
+
+
 def gpu_encode_stack(n, target_bpp):
     """The GPU encoder over the stack: every matrix already in HBM (BF16), compressed in
     turn on one stream; wall time of the whole pass against the host encoder's rate on a
@@ -435,6 +481,7 @@ def main():
     torch.cuda.empty_cache()
     if not a.no_linear:
         result["fused_linear"] = fused_linear(a.target_bpp)
+        result["fp8_linear"] = fp8_linear()
     if not a.no_lossless:
         result["lossless"] = lossless_block()
     if not a.no_gpu_encode:
