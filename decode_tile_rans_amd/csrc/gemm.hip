@@ -6,12 +6,11 @@
 // transformer prefill) where the GEMM dominates.  [NEWS] / [README] "FP8@5": FP8 W8A8
 // weight codes compressed by EntroPack and an FP8 GEMM at inference.
 //
-// Both kernels are "NT": X [T x K] and W [N x K] are K-contiguous, Y = X W^T is
-// [T x N] row-major BF16 with fp32 accumulation.  The BF16 kernel (below, 256 x 256 or
-// 256 x 128 tiles, LDS filled by direct-to-LDS loads) serves the compressed linear layer
-// and its uncompressed baseline.  The FP8 kernel: workgroup tile 128 x 128, 4 waves in a
-// 2 x 2 arrangement, each wave 64 x 64 = 2 x 2 MFMA 32x32 tiles; K tiles of 128 bytes per
-// row staged in LDS (double buffered through registers).
+// Both GEMMs are "NT": X [T x K] and W [N x K] are K-contiguous, Y = X W^T is [T x N]
+// row-major BF16 with fp32 accumulation.  One kernel (below, 256 x 256 or 256 x 128
+// tiles, LDS filled by direct-to-LDS loads, 128 bytes of K per row and stage) serves
+// both element types: BF16 (the compressed linear layer and its uncompressed baseline)
+// and FP8 E4M3 codes (y = acc * a_x * a_w[n]).
 //   BF16: v_mfma_f32_32x32x16_bf16   (A/B: 8 bf16 per lane, lane -> row l%32,
 //                                      k = 8 (l/32) .. +8)
 //   FP8:  v_mfma_f32_32x32x64_f8f6f4 (A/B: 32 e4m3 per lane, k = 32 (l/32) .. +32)
@@ -21,6 +20,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <mutex>
+#include <type_traits>
 
 #include "ep_internal.h"
 
@@ -31,145 +31,26 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
-constexpr int BM = 128, BN = 128;
-constexpr int ROWB = 128;            // bytes of K per row per tile
-constexpr int LDSROW = ROWB + 16;    // padded LDS row (bytes)
-constexpr int TILE_BYTES = BM * LDSROW;
-constexpr int GEMM_LDS = 2 * 2 * TILE_BYTES;   // A + B, double buffered
+// ---------------------------------------------------------------- GEMM, 256 x BN tiles
+// Workgroup tile 256 x BN, waves 2 along M x W/2 along N (BN = 128: 4 waves of 128 x 64;
+// BN = 256: 8 waves of 128 x 64, two per SIMD), each wave 4 x 2 MFMA 32x32x16 blocks.
+// K tiles of 128 bytes go from HBM straight into one of NST LDS stages
+// (global_load_lds, 16 bytes per lane, lane l landing at base + 16 l), issued NST - 1
+// tiles ahead; one barrier per K tile.  LDS rows are 128 bytes; their 16-byte
+// chunks are XOR-swizzled by the row so that the eight lanes reading one fragment row
+// group touch all 32 banks once.  Chunks outside the matrix load a zero line.  The MFMA
+// takes the W fragment as its first operand, so each lane ends with four consecutive
+// outputs of one row (one 8-byte store).
+//   BN = 128: 3 stages (144 KB);  BN = 256: 2 stages (128 KB).  A stage holds 128 bytes of
+//   K per row: 64 BF16 (four MFMA 32x32x16 steps) or 128 FP8 (two 32x32x64 steps, a lane's
+//   32-byte operand read as two swizzled 16-byte chunks).
+constexpr int GBM = 256;
 
 __device__ inline float bf16_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ inline uint16_t float_to_bf16(float f) {
   __bf16 x = (__bf16)f;
   return __builtin_bit_cast(uint16_t, x);
 }
-
-// Load one K tile (128 bytes per row) of a [rows x kbytes] K-contiguous matrix into
-// registers: 1024 16-byte chunks per operand, 4 per thread; zero outside the matrix.
-__device__ inline void load_tile(const uint8_t* __restrict__ M, int64_t rows, int64_t kbytes, int64_t r0, int64_t kb0,
-                                 int tid, uint4 (&reg)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int c = tid + 256 * i;
-    int r = c >> 3, ch = c & 7;
-    int64_t gr = r0 + r, gk = kb0 + ch * 16;
-    if (gr < rows && gk < kbytes) reg[i] = *(const uint4*)(M + gr * kbytes + gk);
-    else reg[i] = make_uint4(0, 0, 0, 0);
-  }
-}
-
-__device__ inline void store_tile(uint8_t* s, int tid, const uint4 (&reg)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int c = tid + 256 * i;
-    int r = c >> 3, ch = c & 7;
-    *(uint4*)(s + r * LDSROW + ch * 16) = reg[i];
-  }
-}
-
-template <bool FP8>
-__global__ void __launch_bounds__(256) gemm_nt_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
-                                                      const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
-                                                      int64_t T, int64_t N, int64_t K, float ax,
-                                                      const float* __restrict__ aw) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-  const int64_t kbytes = FP8 ? K : 2 * K;
-  const int64_t nkt = (kbytes + ROWB - 1) / ROWB;
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-
-  uint4 ra[4], rb[4];
-  load_tile(X, T, kbytes, m0, 0, tid, ra);
-  load_tile(W, N, kbytes, n0, 0, tid, rb);
-  store_tile(lds, tid, ra);
-  store_tile(lds + TILE_BYTES, tid, rb);
-  __syncthreads();
-
-  const int lr = lane & 31, lh = lane >> 5;
-  for (int64_t kt = 0; kt < nkt; ++kt) {
-    const int buf = (int)(kt & 1);
-    if (kt + 1 < nkt) {
-      load_tile(X, T, kbytes, m0, (kt + 1) * ROWB, tid, ra);
-      load_tile(W, N, kbytes, n0, (kt + 1) * ROWB, tid, rb);
-    }
-    const uint8_t* sA = lds + buf * 2 * TILE_BYTES;
-    const uint8_t* sB = sA + TILE_BYTES;
-    if (!FP8) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {       // 4 x K16 per 64-element tile
-        bf16x8 fa[2], fb[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          fa[t] = *(const bf16x8*)(sA + (wm * 64 + t * 32 + lr) * LDSROW + ks * 32 + lh * 16);
-          fb[t] = *(const bf16x8*)(sB + (wn * 64 + t * 32 + lr) * LDSROW + ks * 32 + lh * 16);
-        }
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {       // 2 x K64 per 128-byte tile
-        i32x8 fa[2], fb[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          fa[t] = *(const i32x8*)(sA + (wm * 64 + t * 32 + lr) * LDSROW + ks * 64 + lh * 32);
-          fb[t] = *(const i32x8*)(sB + (wn * 64 + t * 32 + lr) * LDSROW + ks * 64 + lh * 32);
-        }
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[a], fb[b], acc[a][b], 0, 0, 0, 0, 0, 0);
-      }
-    }
-    if (kt + 1 < nkt) {
-      uint8_t* dA = lds + (buf ^ 1) * 2 * TILE_BYTES;
-      store_tile(dA, tid, ra);
-      store_tile(dA + TILE_BYTES, tid, rb);
-    }
-    __syncthreads();
-  }
-
-  // epilogue
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t col = n0 + wn * 64 + b * 32 + lr;
-      if (col >= N) continue;
-      float bv = 0.f, sc = 1.f;
-      if (FP8) sc = ax * aw[col];
-      else if (bias) bv = bf16_to_float(bias[col]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + a * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (row < T) Y[row * N + col] = float_to_bf16(FP8 ? acc[a][b][r] * sc : acc[a][b][r] + bv);
-      }
-    }
-}
-
-// ---------------------------------------------------------------- BF16 GEMM, 256 x BN tiles
-// Workgroup tile 256 x BN, waves 2 along M x W/2 along N (BN = 128: 4 waves of 128 x 64;
-// BN = 256: 8 waves of 128 x 64, two per SIMD), each wave 4 x 2 MFMA 32x32x16 blocks.
-// K tiles of BK elements go from HBM straight into one of NST LDS stages
-// (global_load_lds, 16 bytes per lane, lane l landing at base + 16 l), issued NST - 1
-// tiles ahead; one barrier per K tile.  LDS rows are 2 BK bytes; their 16-byte
-// chunks are XOR-swizzled by the row so that the eight lanes reading one fragment row
-// group touch all 32 banks once.  Chunks outside the matrix load a zero line.  The MFMA
-// takes the W fragment as its first operand, so each lane ends with four consecutive
-// outputs of one row (one 8-byte store).
-//   BN = 128: BK = 64, 3 stages (144 KB);  BN = 256: BK = 64, 2 stages (128 KB).
-constexpr int GBM = 256;
 __device__ __align__(16) uint4 g_zero_line[4];   // zero-initialised; the source of out-of-range chunks
 
 #define EP_LDS3 __attribute__((address_space(3)))
@@ -178,8 +59,8 @@ __device__ __align__(16) uint4 g_zero_line[4];   // zero-initialised; the source
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 template <int BN> struct GemmCfg;
-template <> struct GemmCfg<128> { static constexpr int BK = 64, NST = 3, WAVES = 4; };
-template <> struct GemmCfg<256> { static constexpr int BK = 64, NST = 2, WAVES = 8; };
+template <> struct GemmCfg<128> { static constexpr int NST = 3, WAVES = 4; };
+template <> struct GemmCfg<256> { static constexpr int NST = 2, WAVES = 8; };
 
 // chunk position of logical chunk c in row r (CPR chunks per row)
 template <int CPR>
@@ -187,12 +68,16 @@ __device__ __forceinline__ int swz(int r, int c) {
   return CPR == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 1) & 3));
 }
 
-template <int BN>
-__global__ void __launch_bounds__(64 * GemmCfg<BN>::WAVES, 1) gemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+template <int BN, bool FP8>
+__global__ void __launch_bounds__(64 * GemmCfg<BN>::WAVES, 1) gemm_tile_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
                                                            const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
-                                                           int64_t T, int64_t N, int64_t K, int ntm, int ntn) {
-  constexpr int BK = GemmCfg<BN>::BK, NST = GemmCfg<BN>::NST, NW = GemmCfg<BN>::WAVES;
-  constexpr int RB = 2 * BK, CPR = RB / 16, RPL = 64 / CPR;   // row bytes, chunks per row, rows per load
+                                                           int64_t T, int64_t N, int64_t K, int ntm, int ntn, float ax,
+                                                           const float* __restrict__ aw) {
+  constexpr int NST = GemmCfg<BN>::NST, NW = GemmCfg<BN>::WAVES;
+  constexpr int RB = 128, CPR = RB / 16, RPL = 64 / CPR;      // row bytes, chunks per row, rows per load
+  constexpr int NKS = FP8 ? 2 : 4;                            // MFMA K steps per stage
+  constexpr bool kDoubleFrag = !(FP8 && BN == 256);           // fragments double-buffered
+  const int64_t KB = FP8 ? K : 2 * K;                         // bytes of K per matrix row
   constexpr int A_BYTES = GBM * RB, B_BYTES = BN * RB, STAGE = A_BYTES + B_BYTES;
   constexpr int WN = BN / (NW / 2), NJ = WN / 32, MI = 4;     // waves: 2 along M x NW/2 along N
   constexpr int A_LD = GBM / RPL / NW, B_LD = BN / RPL / NW;  // load instructions per wave
@@ -211,7 +96,7 @@ __global__ void __launch_bounds__(64 * GemmCfg<BN>::WAVES, 1) gemm_bf16_kernel(c
   const int gsz = GM * ntn, g = t / gsz, rem = t % gsz;
   const int gm = ntm - g * GM < GM ? ntm - g * GM : GM;
   const int64_t m0 = (int64_t)(g * GM + rem % gm) * GBM, n0 = (int64_t)(rem / gm) * BN;
-  const int64_t nkt = (K + BK - 1) / BK;
+  const int64_t nkt = (KB + RB - 1) / RB;
 
   // this lane's part of each load instruction: row (within RPL) and the chunk it fetches.
   // Rows past the matrix read its last row (their outputs are never stored); the byte
@@ -223,28 +108,28 @@ __global__ void __launch_bounds__(64 * GemmCfg<BN>::WAVES, 1) gemm_bf16_kernel(c
     const int r = (wave * A_LD + i) * RPL + lrow;
     const int64_t gr = m0 + r < T ? m0 + r : T - 1;
     kcA[i] = (uint32_t)(swz<CPR>(r, lpos) * 16);
-    offA[i] = (uint32_t)((gr - m0) * K * 2) + kcA[i];
+    offA[i] = (uint32_t)((gr - m0) * KB) + kcA[i];
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
     const int r = (wave * B_LD + i) * RPL + lrow;
     const int64_t gr = n0 + r < N ? n0 + r : N - 1;
     kcB[i] = (uint32_t)(swz<CPR>(r, lpos) * 16);
-    offB[i] = (uint32_t)((gr - n0) * K * 2) + kcB[i];
+    offB[i] = (uint32_t)((gr - n0) * KB) + kcB[i];
   }
-  const char* xpan = (const char*)(X + m0 * K);
-  const char* wpan = (const char*)(W + n0 * K);
+  const char* xpan = (const char*)(X + m0 * KB);
+  const char* wpan = (const char*)(W + n0 * KB);
   const char* pA[A_LD];
   const char* pB[B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) pA[i] = xpan + offA[i];
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) pB[i] = wpan + offB[i];
-  const bool ktail = (K % BK) != 0;
+  const bool ktail = (KB % RB) != 0;
   const char* zero = (const char*)g_zero_line;
   auto issue = [&](int64_t kt, int st) {
     EP_LDS3 uint8_t* sbase = (EP_LDS3 uint8_t*)lds + st * STAGE;
-    const int64_t kb = kt * BK * 2;
+    const int64_t kb = kt * RB;
     if (!ktail || kt + 1 < nkt) {
 #pragma unroll
       for (int i = 0; i < A_LD; ++i)
@@ -254,7 +139,7 @@ __global__ void __launch_bounds__(64 * GemmCfg<BN>::WAVES, 1) gemm_bf16_kernel(c
         __builtin_amdgcn_global_load_lds((const void*)(pB[i] + kb), (EP_LDS3 void*)(sbase + A_BYTES + (wave * B_LD + i) * 1024), 16, 0, 0);
     } else {
       // last, partial K tile: chunks at or past K load the zero line
-      const int64_t kleft = 2 * K - kb;   // bytes of K left
+      const int64_t kleft = KB - kb;   // bytes of K left
 #pragma unroll
       for (int i = 0; i < A_LD; ++i) {
         const bool in = (int64_t)kcA[i] < kleft;
@@ -278,18 +163,25 @@ __global__ void __launch_bounds__(64 * GemmCfg<BN>::WAVES, 1) gemm_bf16_kernel(c
 
   // fragment addresses within a stage (the K16 step adds a swizzled chunk position)
   const int lr = lane & 31, lh = lane >> 5;
-  auto frag_load = [&](const uint8_t* sA, const uint8_t* sB, int ks, bf16x8* fa, bf16x8* fb) {
-    const int c = 2 * ks + lh;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int r = wm * 128 + 32 * i + lr;
-      fa[i] = *(const bf16x8*)(sA + r * RB + (swz<CPR>(r, c) << 4));
+  typedef typename std::conditional<FP8, i32x8, bf16x8>::type frag_t;
+  // a lane's operand: BF16 chunk 2 ks + lh (8 elements); FP8 chunks 4 ks + 2 lh and the
+  // next one (32 codes)
+  auto frag_at = [&](const uint8_t* s, int r, int ks) -> frag_t {
+    if constexpr (FP8) {
+      const int c = 4 * ks + 2 * lh;
+      const uint4 lo = *(const uint4*)(s + r * RB + (swz<CPR>(r, c) << 4));
+      const uint4 hi = *(const uint4*)(s + r * RB + (swz<CPR>(r, c + 1) << 4));
+      const i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      return v;
+    } else {
+      return *(const bf16x8*)(s + r * RB + (swz<CPR>(r, 2 * ks + lh) << 4));
     }
+  };
+  auto frag_load = [&](const uint8_t* sA, const uint8_t* sB, int ks, frag_t* fa, frag_t* fb) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int r = wn * WN + 32 * j + lr;
-      fb[j] = *(const bf16x8*)(sB + r * RB + (swz<CPR>(r, c) << 4));
-    }
+    for (int i = 0; i < MI; ++i) fa[i] = frag_at(sA, wm * 128 + 32 * i + lr, ks);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) fb[j] = frag_at(sB, wn * WN + 32 * j + lr, ks);
   };
 
   // prologue: tiles 0 .. NST-2 in flight
@@ -311,18 +203,38 @@ __global__ void __launch_bounds__(64 * GemmCfg<BN>::WAVES, 1) gemm_bf16_kernel(c
     if (kt + NST - 1 < nkt) issue(kt + NST - 1, (st + NST - 1) % NST);
     const uint8_t* sA = lds + st * STAGE;
     const uint8_t* sB = sA + A_BYTES;
-    bf16x8 fa[2][MI], fb[2][NJ];
+    if constexpr (!kDoubleFrag) {
+      // one set of fragments at a time (the wider FP8 operands of the 256-wide tile
+      // would not fit twice beside the accumulators)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        frag_t fa[MI], fb[NJ];
+        frag_load(sA, sB, ks, fa, fb);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+      }
+      return;
+    }
+    frag_t fa[2][MI], fb[2][NJ];
     frag_load(sA, sB, 0, fa[0], fb[0]);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
       // the next step's fragments are requested before this step's MFMAs
-      if (ks + 1 < BK / 16) frag_load(sA, sB, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      if (ks + 1 < NKS) frag_load(sA, sB, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NJ; ++j) {
+          if constexpr (FP8)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0,
+                                                                      0, 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
+        }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -348,7 +260,8 @@ __global__ void __launch_bounds__(64 * GemmCfg<BN>::WAVES, 1) gemm_bf16_kernel(c
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           v[e] = acc[i][j][4 * rq + e];
-          if (bias && n + e < N) v[e] += bf16_to_float(bias[n + e]);
+          if (FP8) v[e] *= n + e < N ? ax * aw[n + e] : 0.f;
+          else if (bias && n + e < N) v[e] += bf16_to_float(bias[n + e]);
         }
         uint16_t* yp = Y + m * N + n;
         if (vec && n + 3 < N) {
@@ -366,26 +279,27 @@ __global__ void __launch_bounds__(64 * GemmCfg<BN>::WAVES, 1) gemm_bf16_kernel(c
   }
 }
 
-template <int BN>
-int launch_bf16_bn(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K,
-                   hipStream_t st) {
-  constexpr int lds = GemmCfg<BN>::NST * (GBM + BN) * 2 * GemmCfg<BN>::BK;
-  auto kern = gemm_bf16_kernel<BN>;
+template <int BN, bool FP8>
+int launch_tile(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K, float ax,
+                const float* aw, hipStream_t st) {
+  constexpr int lds = GemmCfg<BN>::NST * (GBM + BN) * 128;
+  auto kern = gemm_tile_kernel<BN, FP8>;
   static std::once_flag once;
   std::call_once(once, [&] { (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); });
   const int ntm = (int)((T + GBM - 1) / GBM), ntn = (int)((N + BN - 1) / BN);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(64 * GemmCfg<BN>::WAVES), lds, st, (const uint16_t*)x, (const uint16_t*)w,
-                     (const uint16_t*)bias, (uint16_t*)y, T, N, K, ntm, ntn);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(64 * GemmCfg<BN>::WAVES), lds, st, (const uint8_t*)x,
+                     (const uint8_t*)w, (const uint16_t*)bias, (uint16_t*)y, T, N, K, ntm, ntn, ax, aw);
   return hip_check(hipGetLastError(), "gemm launch");
 }
 
 // BN = 256 unless 128-wide tiles fill the CUs' rounds much better (a 256 x 256 tile does
 // about 1.25x the work per cycle of a 256 x 128 one).
-int launch_bf16(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K,
-                hipStream_t st) {
-  if (!x || !w || !y) return fail(EP_E_ARG, "null pointer");
+template <bool FP8>
+int launch_gemm(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K, float ax,
+                const float* aw, hipStream_t st) {
+  if (!x || !w || !y || (FP8 && !aw)) return fail(EP_E_ARG, "null pointer");
   if (T < 1 || N < 1 || K < 1) return fail(EP_E_ARG, "GEMM sizes must be >= 1");
-  if (K % 8) return fail(EP_E_ARG, "K must be a multiple of 8 (BF16)");
+  if ((FP8 ? K : 2 * K) % 16) return fail(EP_E_ARG, "K must be a multiple of 8 (BF16) or 16 (FP8)");
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w)) & 15)
     return fail(EP_E_ARG, "operands must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(y) & 7) && N % 4 == 0) return fail(EP_E_ARG, "output must be 8-byte aligned");
@@ -395,31 +309,18 @@ int launch_bf16(const void* x, const void* w, const void* bias, void* y, int64_t
     const int64_t rounds = (tiles + 255) / 256;
     return (double)(T * N) / (double)(rounds * 256 * GBM * bn);
   };
-  if (std::getenv("EP_GEMM_BN")) {
-    if (std::atoi(std::getenv("EP_GEMM_BN")) == 128) return launch_bf16_bn<128>(x, w, bias, y, T, N, K, st);
-    return launch_bf16_bn<256>(x, w, bias, y, T, N, K, st);
-  }
-  if (eff(128) > 1.25 * eff(256)) return launch_bf16_bn<128>(x, w, bias, y, T, N, K, st);
-  return launch_bf16_bn<256>(x, w, bias, y, T, N, K, st);
+  bool narrow = eff(128) > 1.25 * eff(256);
+  if (const char* e = std::getenv("EP_GEMM_BN")) narrow = std::atoi(e) == 128;
+  if (narrow) return launch_tile<128, FP8>(x, w, bias, y, T, N, K, ax, aw, st);
+  return launch_tile<256, FP8>(x, w, bias, y, T, N, K, ax, aw, st);
 }
 
-template <bool FP8>
-int launch_gemm(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K, float ax,
-                const float* aw, hipStream_t st) {
-  if (!x || !w || !y || (FP8 && !aw)) return fail(EP_E_ARG, "null pointer");
-  if (T < 1 || N < 1 || K < 1) return fail(EP_E_ARG, "GEMM sizes must be >= 1");
-  const int64_t kb = FP8 ? K : 2 * K;
-  if (kb % 16) return fail(EP_E_ARG, "K must be a multiple of 8 (BF16) or 16 (FP8)");
-  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w)) & 15)
-    return fail(EP_E_ARG, "operands must be 16-byte aligned");
-  auto kern = gemm_nt_kernel<FP8>;
-  static std::once_flag once;
-  std::call_once(once, [&] { (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS); });
-  dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((T + BM - 1) / BM));
-  hipLaunchKernelGGL(kern, grid, dim3(256), GEMM_LDS, st, (const uint8_t*)x, (const uint8_t*)w,
-                     (const uint16_t*)bias, (uint16_t*)y, T, N, K, ax, aw);
-  return hip_check(hipGetLastError(), "gemm launch");
+int launch_bf16(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K,
+                hipStream_t st) {
+  return launch_gemm<false>(x, w, bias, y, T, N, K, 1.f, nullptr, st);
 }
+
+
 
 }  // namespace
 }  // namespace ep
