@@ -236,6 +236,7 @@ def fused_linear(target_bpp, reps=10):
     # a sequence of layers (4 distinct weights, each twice): the next layer's decode on a
     # second stream while this layer's GEMM runs, against the same GEMMs on plain weights
     seq = linear_sequence(c, wbits, x, T, target_bpp, timeit)
+    small = small_batch(c, w, x, ws, need, wd, sp, timeit)
     return {
         "workload": "CompressedLinear prefill 14336x4096 weight @%.1f bpp, 4096 tokens" % target_bpp,
         "actual_bpp": round(c.actual_bpp, 4),
@@ -246,7 +247,33 @@ def fused_linear(target_bpp, reps=10):
         "gemm_mfma_util": round(flops / (t_gemm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "gemm_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 1),
         "sequence_overlapped": seq,
+        "small_batch": small,
     }
+
+
+def small_batch(c, w, x, ws, need, wd, sp, timeit):
+    """The same layer on 1..8 tokens (decode-time inference): the fused decode-and-product
+    kernel against decode then our GEMM and against hipBLASLt on the plain BF16 weight.
+    Rate = blob bytes / fused time (the weights are read once, compressed)."""
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    R, C = c.shape
+    out = []
+    for T in (1, 2, 4, 8):
+        xs = x[:T].contiguous()
+        y = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
+        nmv = L.ep_matvec_workspace_bytes(c.handle, T)
+        t_mv = timeit(lambda: L.ep_compressed_matvec(c.handle, xs.data_ptr(), T, None, y.data_ptr(), ws.data_ptr(),
+                                                     nmv, sp))
+        t_two = timeit(lambda: (L.ep_decompress(c.handle, wd, sp),
+                                L.ep_gemm_bf16_nt(xs.data_ptr(), wd, None, y.data_ptr(), T, R, C, sp)))
+        t_plain = timeit(lambda: torch.matmul(xs, w.t()))
+        out.append({"tokens": T, "ms_fused": round(t_mv, 4), "ms_decode_then_gemm": round(t_two, 4),
+                    "ms_hipblaslt_plain_bf16": round(t_plain, 4),
+                    "fused_speedup_vs_decode_then_gemm": round(t_two / t_mv, 3),
+                    "fused_blob_gbs": round(c.nbytes / (t_mv * 1e-3) / 1e9, 1),
+                    "plain_weight_gbs": round(2.0 * R * C / (t_plain * 1e-3) / 1e9, 1)})
+    return out
 
 
 def linear_sequence(c0, wbits0, x, T, target_bpp, timeit, n_layers=8):

@@ -31,6 +31,8 @@ SIGNATURES = {
     "ep_linear_workspace_bytes": (_sz, [_vp]),
     "ep_compressed_linear_forward": (_int, [_vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "ep_linear_seq_workspace_bytes": (_sz, [C.POINTER(_vp), _int]),
+    "ep_matvec_workspace_bytes": (_sz, [_vp, _i64]),
+    "ep_compressed_matvec": (_int, [_vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "ep_compressed_linear_seq_forward": (_int, [C.POINTER(_vp), _int, C.POINTER(_vp), _i64, C.POINTER(_vp),
                                                 C.POINTER(_vp), _vp, _sz, _vp, _vp]),
     "ep_gemm_bf16_nt": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -127,6 +129,14 @@ def ep_linear_workspace_bytes(blob: int) -> int:
 
 def ep_compressed_linear_forward(blob, dev_x, T, dev_bias, dev_y, dev_ws, ws_bytes, stream=0):
     check(lib().ep_compressed_linear_forward(blob, dev_x, T, dev_bias, dev_y, dev_ws, ws_bytes, stream))
+
+
+def ep_matvec_workspace_bytes(blob: int, T: int) -> int:
+    return int(lib().ep_matvec_workspace_bytes(blob, T))
+
+
+def ep_compressed_matvec(blob, dev_x, T, dev_bias, dev_y, dev_ws, ws_bytes, stream=0):
+    check(lib().ep_compressed_matvec(blob, dev_x, T, dev_bias, dev_y, dev_ws, ws_bytes, stream))
 
 
 def _ptrs(seq):

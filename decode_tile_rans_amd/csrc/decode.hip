@@ -37,7 +37,14 @@ int hip_check(int err, const char* what) {
 namespace {
 
 enum OutKind { OUT_BF16 = 0, OUT_BF16_SAT = 1, OUT_FP16 = 2, OUT_FP32 = 3, OUT_FP8 = 4, OUT_INT8 = 5, OUT_COORDS = 6,
-               OUT_BYTES = 7 /* TileANS: the decoded symbols are the tensor's bytes */ };
+               OUT_BYTES = 7 /* TileANS: the decoded symbols are the tensor's bytes */,
+               // fused matrix-vector product with 1, 2, 4 or 8 activation rows: the BF16
+               // weights are multiplied into per-chain partial sums and never stored
+               OUT_MV1 = 8, OUT_MV2 = 9, OUT_MV4 = 10, OUT_MV8 = 11 };
+template <int OUT>
+constexpr int mv_tokens() {
+  return OUT >= OUT_MV1 ? 1 << (OUT - OUT_MV1) : 0;
+}
 template <int OUT>
 constexpr int out_elem_bytes() {
   return (OUT == OUT_FP32 || OUT == OUT_COORDS) ? 4 : ((OUT == OUT_FP8 || OUT == OUT_INT8 || OUT == OUT_BYTES) ? 1 : 2);
@@ -66,6 +73,10 @@ struct DecJob {
   uint32_t R;
   uint32_t ctx_mask;           // TileANS: byte contexts - 1 (symbol i of a group uses i & ctx_mask)
   uint32_t tab_words;          // table words to stage
+  // fused matrix-vector product (OUT_MV*): activations X (mv_T rows of C BF16), partial
+  // sums out[(chain * mv_slots + row - first row of the chain) * tokens + t]
+  const uint16_t* mv_x;
+  uint32_t mv_T, mv_slots, mv_sat;
 };
 
 // ---------------------------------------------------------------- container stores
@@ -606,6 +617,31 @@ struct GroupCtx {
   bool rowwise;
 };
 
+// Fused matrix-vector product: a chain's running dot products of its weights in the
+// current row with the NT activation rows, written to the chain's partial-sum slot of
+// that row when the chain moves on (a chain's groups run through the rows in order).
+struct MvAcc {
+  float a[8];
+  uint32_t row, rlo;   // row being summed, the chain's first row
+  int64_t slot0;       // partial-sum slot of (chain, rlo)
+};
+
+template <int NT>
+__device__ __forceinline__ void mv_flush(const DecJob& J, MvAcc& m) {
+  float* o = (float*)J.out + (m.slot0 + (int64_t)(m.row - m.rlo)) * NT;
+  typedef __attribute__((ext_vector_type(4))) float f32x4;
+  if constexpr (NT >= 4) {
+#pragma unroll
+    for (int t = 0; t < NT; t += 4) *(f32x4*)(o + t) = f32x4{m.a[t], m.a[t + 1], m.a[t + 2], m.a[t + 3]};
+  } else if constexpr (NT == 2) {
+    *(f32x2*)o = f32x2{m.a[0], m.a[1]};
+  } else {
+    o[0] = m.a[0];
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) m.a[t] = 0.f;
+}
+
 // Row scale of group kk: move to the next row at a precomputed group count, then issue
 // the (usually repeated) load of the scale the chain moves to next.
 template <int ILP>
@@ -643,9 +679,28 @@ __device__ __forceinline__ void row_scale(const GroupCtx& X, int kk, RowScale* r
 // careful path), container store.
 template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
 __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* rd, RowScale* rs, const int* ngr,
-                                             const uint32_t* g0, char** optr) {
+                                             const uint32_t* g0, char** optr, MvAcc* mv) {
   using LY = EntryLayout<NARROW>;
   const DecJob& J = *X.J;
+  constexpr int NT = mv_tokens<OUT>();
+  // fused product: this group's activation chunks are requested before its symbols are
+  // decoded (row and column of the group are known; idle chains read column 0)
+  uint4 xv[ILP][NT > 0 ? NT : 1];
+  uint32_t mrow[ILP];
+  if constexpr (NT > 0) {
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      const bool act = kk < ngr[c];
+      mrow[c] = rs[c].row;
+      const uint32_t gk = g0[c] + (uint32_t)kk * (uint32_t)X.S;
+      const int64_t c0 = act ? (int64_t)(gk - mrow[c] * X.G) * 8 : 0;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int64_t tt = (uint32_t)t < J.mv_T ? t : (int64_t)J.mv_T - 1;
+        xv[c][t] = *(const uint4*)(J.mv_x + tt * J.C + c0);
+      }
+    }
+  }
   if constexpr (OUT == OUT_BYTES) {
     // TileANS: eight byte symbols, symbol i from the table of context i & ctx_mask
     uint32_t xs[ILP], ras[ILP], nws[ILP];
@@ -755,7 +810,35 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
         if (slow) ch_linear(rd[c]);
       }
     }
-    if (act) {
+    if constexpr (NT > 0) {
+      if (act) {
+        // the weights as the BF16 container holds them, then two products per dot step
+        uint32_t p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float a = w[2 * i], b = w[2 * i + 1];
+          if (J.mv_sat) {
+            a = fminf(fmaxf(a, -3.38953139e38f), 3.38953139e38f);
+            b = fminf(fmaxf(b, -3.38953139e38f), 3.38953139e38f);
+          }
+          f32x2 fv = {a, b};
+          p[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(fv, bf16x2));
+        }
+        if (mrow[c] != mv[c].row) {
+          mv_flush<NT>(J, mv[c]);
+          mv[c].row = mrow[c];
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float acc = mv[c].a[t];
+          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[0]), __builtin_bit_cast(bf16x2, xv[c][t].x), acc, false);
+          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[1]), __builtin_bit_cast(bf16x2, xv[c][t].y), acc, false);
+          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[2]), __builtin_bit_cast(bf16x2, xv[c][t].z), acc, false);
+          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[3]), __builtin_bit_cast(bf16x2, xv[c][t].w), acc, false);
+          mv[c].a[t] = acc;
+        }
+      }
+    } else if (act) {
       if (C8) {
         store_group<OUT>(optr[c], 0, w, u, true, 8);
       } else {
@@ -801,6 +884,8 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
   bool live[ILP];
   uint32_t g0[ILP];
   char* optr[ILP];
+  MvAcc mv[ILP];
+  constexpr int NT = mv_tokens<OUT>();
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
     const int64_t ch = (blk0 + c) * 64 + lane;
@@ -839,6 +924,12 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
     const uint32_t col0 = g0[c] - row0 * G;
     RowScale& q = rs[c];
     q.row = row0;
+    if constexpr (NT > 0) {
+      mv[c].row = mv[c].rlo = row0;
+      mv[c].slot0 = ch * (int64_t)J.mv_slots;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) mv[c].a[t] = 0.f;
+    }
     if constexpr (OUT == OUT_BYTES) {   // no row scales
       q.h = q.nh = q.hn = 0.f;
       q.pn = nullptr;
@@ -901,13 +992,18 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
       ch_service(X.sref, rd[c], (ILP == 1) || kk < ngr[c]);
       ch_linear(rd[c]);
     }
-    decode_group<OUT, ESC, C8, NARROW, ILP>(X, kk, rd, rs, ngr, g0, optr);
+    decode_group<OUT, ESC, C8, NARROW, ILP>(X, kk, rd, rs, ngr, g0, optr, mv);
     if (kk + 1 < nmax) {
       if constexpr (OUT != OUT_BYTES) row_scale<ILP>(X, kk + 1, rs, ngr);
-      decode_group<OUT, ESC, C8, NARROW, ILP>(X, kk + 1, rd, rs, ngr, g0, optr);
+      decode_group<OUT, ESC, C8, NARROW, ILP>(X, kk + 1, rd, rs, ngr, g0, optr, mv);
     }
 #pragma unroll
     for (int c = 0; c < ILP; ++c) ch_settle(rd[c]);
+  }
+  if constexpr (NT > 0) {
+#pragma unroll
+    for (int c = 0; c < ILP; ++c)
+      if (live[c] && ngr[c] > 0) mv_flush<NT>(J, mv[c]);
   }
 #pragma unroll
   for (int c = 0; c < ILP; ++c)
@@ -1007,6 +1103,17 @@ int launch_out(int out, const DecBatch& B, int64_t n_wg, int waves, hipStream_t 
     case OUT_BYTES:
       if constexpr (!ESC && NARROW) return launch_t<OUT_BYTES, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
       return fail(EP_E_ARG, "byte output takes the escape-free narrow kernel");
+    case OUT_MV1:
+    case OUT_MV2:
+    case OUT_MV4:
+    case OUT_MV8:
+      if constexpr (C8 && ILP == 1) {
+        if (out == OUT_MV1) return launch_t<OUT_MV1, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+        if (out == OUT_MV2) return launch_t<OUT_MV2, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+        if (out == OUT_MV4) return launch_t<OUT_MV4, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+        return launch_t<OUT_MV8, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+      }
+      return fail(EP_E_ARG, "the fused product takes whole groups per row and one chain per lane");
     default: return launch_t<OUT_COORDS, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
   }
 }
@@ -1167,7 +1274,95 @@ int decode_one(const Blob& b, void* dst, int64_t chain_lo, int64_t chain_hi, int
   return launch_any(out, (b.flags & kFlagEsc) != 0, (b.C % 8) == 0, b.k <= 6, sh, B, n_wg, st);
 }
 
+// Sum of the fused product's partial sums of row r for activation row t, in a fixed
+// order (tiles, then chains of a tile, ascending), plus the bias; rounded to BF16 as the
+// GEMM's epilogue rounds.  Thread i: t = i / R, r = i % R.
+__global__ void matvec_finish_kernel(const float* __restrict__ part, const uint16_t* __restrict__ bias,
+                                     uint16_t* __restrict__ y, int64_t T, int64_t R, int64_t G, int log2S,
+                                     int64_t n_groups, int slots, int NT) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * R) return;
+  const int64_t t = i / R, r = i % R;
+  const int64_t S = 1 << log2S;
+  const int64_t g_lo = r * G, g_hi = (r + 1) * G;   // the row's groups
+  float sum = 0.f;
+  for (int64_t tile = g_lo >> 9; tile <= (g_hi - 1) >> 9; ++tile) {
+    int64_t gt = n_groups - (tile << 9);
+    if (gt > kTileGroups) gt = kTileGroups;
+    for (int64_t j = 0; j < S; ++j) {
+      const int64_t g0 = (tile << 9) + j;
+      const int64_t ngr = gt > j ? (gt - j + S - 1) >> log2S : 0;
+      const int64_t k = g_lo > g0 ? (g_lo - g0 + S - 1) >> log2S : 0;   // first group at or past the row
+      if (k >= ngr || g0 + (k << log2S) >= g_hi) continue;
+      const int64_t ch = (tile << log2S) + j;
+      sum += part[(ch * slots + (r - g0 / G)) * NT + t];
+    }
+  }
+  if (bias) sum += __uint_as_float((uint32_t)bias[r] << 16);
+  const __bf16 o = (__bf16)sum;
+  y[t * R + r] = __builtin_bit_cast(uint16_t, o);
+}
+
 }  // namespace
+
+// Rows a chain's groups can touch: the chain's groups lie within its tile's 512
+// consecutive groups, so at most 511 / G + 2 rows.
+int matvec_slots(const Blob& b) { return (int)(511 / ((b.C + 7) / 8)) + 2; }
+
+size_t matvec_workspace_bytes(const Blob& b, int64_t T) {
+  const int nt = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
+  return (size_t)b.n_chains * (size_t)matvec_slots(b) * (size_t)nt * 4 + 256;
+}
+
+bool matvec_supported(const Blob& b, int64_t T) {
+  return b.kind == kKindLossy && b.dtype == EP_BF16 && T >= 1 && T <= kMatvecMaxT && b.C % 8 == 0 &&
+         b.S <= (b.C + 7) / 8;
+}
+
+// Y[T x R] = X[T x C] W^T (+ bias) with W decoded inside the product (never stored);
+// `part` (256-byte aligned, matvec_workspace_bytes - 256 bytes) holds the partial sums.
+int matvec_launch(const Blob& b, const void* x, int64_t T, const void* bias, void* y, float* part, ep_stream stream) {
+  hipStream_t st = (hipStream_t)stream;
+  int rc = check_uploaded(b);
+  if (rc) return rc;
+  if (!matvec_supported(b, T))
+    return fail(EP_E_ARG, "the fused product takes lossy BF16 blobs, 1..8 activation rows, C % 8 == 0 and at least S groups per row");
+  if ((reinterpret_cast<uintptr_t>(x) & 15)) return fail(EP_E_ARG, "activations must be 16-byte aligned");
+  if ((rc = check_gpu_pointer(x, "activations")) || (rc = check_gpu_pointer(y, "output")) ||
+      (rc = check_gpu_pointer(part, "workspace")))
+    return rc;
+  if (bias && (rc = check_gpu_pointer(bias, "bias"))) return rc;
+  const int nt = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
+  const int out = nt == 1 ? OUT_MV1 : nt == 2 ? OUT_MV2 : nt == 4 ? OUT_MV4 : OUT_MV8;
+  DecJob j = make_job(b, part);
+  j.mv_x = (const uint16_t*)x;
+  j.mv_T = (uint32_t)T;
+  j.mv_slots = (uint32_t)matvec_slots(b);
+  j.mv_sat = (b.flags & kFlagSat) ? 1u : 0u;
+  const int64_t nblk = b.n_blocks;
+  Shape sh = pick_shape(&nblk, 1);
+  sh.ilp = 1;
+  const int64_t n_wg = (nblk + sh.bpw - 1) / sh.bpw;
+  DecBatch B{};
+  B.j[0] = j;
+  B.n = 1;
+  B.bpw = sh.bpw;
+  rc = launch_any(out, (b.flags & kFlagEsc) != 0, true, b.k <= 6, sh, B, n_wg, st);
+  if (rc) return rc;
+  const int64_t n = T * b.R;
+  hipLaunchKernelGGL(matvec_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part,
+                     (const uint16_t*)bias, (uint16_t*)y, T, b.R, (int64_t)((b.C + 7) / 8), j.log2S, b.n_groups(),
+                     (int)j.mv_slots, nt);
+  return hip_check(hipGetLastError(), "fused product finish launch");
+}
+
+int matvec_forward(const Blob& b, const void* x, int64_t T, const void* bias, void* y, void* ws, size_t ws_bytes,
+                   ep_stream stream) {
+  if (!ws) return fail(EP_E_ARG, "null workspace");
+  if (ws_bytes < matvec_workspace_bytes(b, T)) return fail(EP_E_WORKSPACE, "workspace too small");
+  return matvec_launch(b, x, T, bias, y, (float*)(((uintptr_t)ws + 255) & ~uintptr_t(255)), stream);
+}
+
 }  // namespace ep
 
 using namespace ep;

@@ -150,6 +150,15 @@ int hip_check(int err, const char* what);
 // EP_E_ARG unless the GPU can dereference p (device, managed or pinned host memory)
 int check_gpu_pointer(const void* p, const char* what);
 
+// Fused matrix-vector product of a lossy BF16 blob (decode.hip): up to kMatvecMaxT
+// activation rows; the weights are decoded and multiplied in one kernel.
+constexpr int64_t kMatvecMaxT = 8;
+bool matvec_supported(const Blob& b, int64_t T);
+size_t matvec_workspace_bytes(const Blob& b, int64_t T);
+int matvec_launch(const Blob& b, const void* x, int64_t T, const void* bias, void* y, float* part, ep_stream st);
+int matvec_forward(const Blob& b, const void* x, int64_t T, const void* bias, void* y, void* ws, size_t ws_bytes,
+                   ep_stream st);
+
 }  // namespace ep
 
 struct ep_blob {

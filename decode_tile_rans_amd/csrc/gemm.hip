@@ -341,6 +341,10 @@ int ep_gemm_fp8_nt(const void* xq, const void* wq, float a_x, const float* aw, v
   return launch_gemm<true>(xq, wq, nullptr, y, T, N, K, a_x, aw, (hipStream_t)stream);
 }
 
+static bool use_matvec(const ep_blob* w, int64_t T) {
+  return matvec_supported(w->b, T) && matvec_workspace_bytes(w->b, T) <= ep_linear_workspace_bytes(w);
+}
+
 int ep_compressed_linear_forward(const ep_blob* w, const void* x, int64_t T, const void* bias, void* y, void* ws,
                                  size_t ws_bytes, ep_stream stream) {
   set_error("");
@@ -348,10 +352,25 @@ int ep_compressed_linear_forward(const ep_blob* w, const void* x, int64_t T, con
   const Blob& b = w->b;
   if (b.kind != kKindLossy || b.dtype != EP_BF16) return fail(EP_E_DTYPE, "compressed linear takes a lossy BF16 blob");
   if (ws_bytes < ep_linear_workspace_bytes(w)) return fail(EP_E_WORKSPACE, "workspace too small");
+  // a few activation rows: the product runs inside the decode kernel (no BF16 weights
+  // written and read back), when its partial sums fit the same workspace
+  if (use_matvec(w, T)) return matvec_forward(b, x, T, bias, y, ws, ws_bytes, stream);
   void* wd = (void*)(((uintptr_t)ws + 255) & ~uintptr_t(255));
   int rc = ep_decompress(w, wd, stream);
   if (rc) return rc;
   return launch_bf16(x, wd, bias, y, T, b.R, b.C, (hipStream_t)stream);
+}
+
+size_t ep_matvec_workspace_bytes(const ep_blob* w, int64_t T) {
+  if (!w || !matvec_supported(w->b, T)) return 0;
+  return matvec_workspace_bytes(w->b, T);
+}
+
+int ep_compressed_matvec(const ep_blob* w, const void* x, int64_t T, const void* bias, void* y, void* ws,
+                         size_t ws_bytes, ep_stream stream) {
+  set_error("");
+  if (!w || !x || !y || !ws) return fail(EP_E_ARG, "null pointer");
+  return matvec_forward(w->b, x, T, bias, y, ws, ws_bytes, stream);
 }
 
 size_t ep_linear_seq_workspace_bytes(const ep_blob* const* w, int n) {
@@ -396,8 +415,13 @@ int ep_compressed_linear_seq_forward(const ep_blob* const* w, int n, const void*
   }
   if (!rc) rc = hip_check(hipEventRecord(ev_start, ms), "event record");
   if (!rc) rc = hip_check(hipStreamWaitEvent(ss, ev_start, 0), "stream wait");
+  // layers with few activation rows take the fused product (as the one-layer entry does),
+  // with their buffer as its partial-sum space, and need no decode
+  std::vector<char> mv(n);
+  for (int i = 0; i < n; ++i) mv[i] = use_matvec(w[i], T);
   auto decode = [&](int i) {
     const int k = i & 1;
+    if (mv[i]) return;
     if (i >= 2 && !rc) rc = hip_check(hipStreamWaitEvent(ss, ev_used[k], 0), "stream wait");
     if (!rc) rc = ep_decompress(w[i], buf[k], side_s);
     if (!rc) rc = hip_check(hipEventRecord(ev_dec[k], ss), "event record");
@@ -406,8 +430,12 @@ int ep_compressed_linear_seq_forward(const ep_blob* const* w, int n, const void*
   for (int i = 0; i < n && !rc; ++i) {
     if (i + 1 < n) decode(i + 1);
     const int k = i & 1;
-    if (!rc) rc = hip_check(hipStreamWaitEvent(ms, ev_dec[k], 0), "stream wait");
-    if (!rc) rc = launch_bf16(x[i], buf[k], bias ? bias[i] : nullptr, y[i], T, w[i]->b.R, w[i]->b.C, ms);
+    if (mv[i]) {
+      if (!rc) rc = matvec_launch(w[i]->b, x[i], T, bias ? bias[i] : nullptr, y[i], (float*)buf[k], ms);
+    } else {
+      if (!rc) rc = hip_check(hipStreamWaitEvent(ms, ev_dec[k], 0), "stream wait");
+      if (!rc) rc = launch_bf16(x[i], buf[k], bias ? bias[i] : nullptr, y[i], T, w[i]->b.R, w[i]->b.C, ms);
+    }
     if (!rc) rc = hip_check(hipEventRecord(ev_used[k], ms), "event record");
   }
   // events may be destroyed while still pending; the runtime releases them when done

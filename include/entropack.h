@@ -145,7 +145,9 @@ int64_t ep_blob_device_errors(const ep_blob* blob);
  * W is the decoded BF16 blob (rows = out features, cols = in features); x is T x cols
  * BF16, y is T x rows BF16, bias is rows BF16 or NULL.  The decode goes to dev_ws
  * (>= ep_linear_workspace_bytes bytes), then an MFMA BF16 GEMM with fp32
- * accumulation runs on the same stream. */
+ * accumulation runs on the same stream.  With T <= 8, when ep_compressed_matvec takes
+ * the blob and its partial sums fit ep_linear_workspace_bytes, that fused product runs
+ * instead (same result up to fp32 summation order). */
 size_t ep_linear_workspace_bytes(const ep_blob* blob);
 int ep_compressed_linear_forward(const ep_blob* w, const void* dev_x, int64_t T,
                                  const void* dev_bias, void* dev_y,
@@ -163,6 +165,21 @@ size_t ep_linear_seq_workspace_bytes(const ep_blob* const* w, int n);
 int ep_compressed_linear_seq_forward(const ep_blob* const* w, int n, const void* const* dev_x, int64_t T,
                                      const void* const* dev_bias, void* const* dev_y,
                                      void* dev_ws, size_t ws_bytes, ep_stream main, ep_stream side);
+
+/* Fused decode and product for few activation rows (decode-time inference: [ABS] and
+ * [README] 快速开始 decode weights on the spot inside the layer; [ABS]: decoding cost
+ * grows with the weight count, which for T <= 8 rows dominates the product):
+ * y = x W^T (+ bias) with the BF16 weights of W decoded and multiplied inside the decode
+ * kernel, never written to memory.  x is T x cols BF16 (16-byte aligned), y is T x rows
+ * BF16, bias rows BF16 or NULL, 1 <= T <= 8.  Takes lossy BF16 blobs with cols % 8 == 0
+ * and at least S groups of 8 per row (cols >= 8 S); EP_E_ARG otherwise.  Each chain sums
+ * w * x over its groups of one row in fp32 (two-term BF16 dot steps) into a partial sum
+ * in dev_ws (>= ep_matvec_workspace_bytes(w, T) bytes, which returns 0 when the blob or
+ * T is not taken); a second kernel adds a row's partial sums in a fixed order, adds the
+ * bias and rounds to BF16, so repeated calls give identical bits.  Asynchronous. */
+size_t ep_matvec_workspace_bytes(const ep_blob* w, int64_t T);
+int ep_compressed_matvec(const ep_blob* w, const void* dev_x, int64_t T, const void* dev_bias,
+                         void* dev_y, void* dev_ws, size_t ws_bytes, ep_stream stream);
 
 /* Plain BF16 "NT" GEMM on MFMA: y[T x N] = x[T x K] w[N x K]^T (+ bias[N]), fp32
  * accumulate, BF16 out.  The uncompressed baseline of the linear layer. */
