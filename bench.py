@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+VALU_LANE_OPS_PER_S = 256 * 64 * 2.4e9   # 256 CUs, 4 SIMDs x 16 lanes each, 2.4 GHz
 
 
 def log(*a):
@@ -157,9 +158,9 @@ def time_stack(comps, blocks, outs, steps, warmup, per_layer=False, n_streams=1)
     return wall / steps * 1e3, launch_ms, units
 
 
-def traffic_per_launch(coords_per_launch):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
-    or None when the decode kernel source changed since those counters were taken."""
+def decode_counters():
+    """The committed rocprofv3 counter summary of the decode kernel (HBM bytes and VALU
+    instructions per parameter), or None when the kernel source changed since then."""
     import hashlib
     try:
         info = json.load(open(os.path.join(ROOT, "profiles", "decode_traffic.json")))
@@ -168,7 +169,29 @@ def traffic_per_launch(coords_per_launch):
         return None
     if hashlib.sha1(src).hexdigest() != info.get("decode_source_sha1"):
         return None
+    return info
+
+
+def traffic_per_launch(coords_per_launch):
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE, or None (see decode_counters)."""
+    info = decode_counters()
+    if info is None:
+        return None
     return (info["fetch_bytes_per_param"] + info["write_bytes_per_param"]) * coords_per_launch
+
+
+def valu_issue(params_per_s):
+    """The decode against the chip's VALU issue rate (256 CUs x 64 lanes x 2.4 GHz lane
+    operations per second) at the measured SQ_INSTS_VALU x 64 lane operations per
+    parameter; None without a current counter summary."""
+    info = decode_counters()
+    if info is None or "valu_lane_ops_per_param" not in info:
+        return None
+    ops = info["valu_lane_ops_per_param"]
+    ceiling = VALU_LANE_OPS_PER_S / ops
+    return {"lane_ops_per_param": ops, "peak_lane_ops_per_s": VALU_LANE_OPS_PER_S,
+            "ceiling_params_per_s": round(ceiling), "achieved_params_per_s": round(params_per_s),
+            "frac": round(params_per_s / ceiling, 4)}
 
 
 def cpu_baseline(target_bpp):
@@ -495,7 +518,9 @@ def main():
                      "traffic": (lambda t: round(t) if t else None)(traffic_per_launch(n_params / len(units))),
                      "kernel": "decode_kernel (BF16 out)", "avg_launch_ms": round(kern_ms / len(units), 5),
                      "algorithmic_bytes_per_launch": round(alg_bytes / len(units)),
-                     "step_effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1)},
+                     "step_effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+                     "valu_issue_per_launch": valu_issue(n_params / (kern_ms * 1e-3)),
+                     "valu_issue_step": valu_issue(n_params / (ms * 1e-3))},
     }
     if not a.no_layer_mode:
         ms_l, lms, units_l = time_stack(comps, blocks, outs, max(2, a.steps // 2), 1, per_layer=True,
