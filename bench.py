@@ -296,6 +296,35 @@ def small_batch(c, w, x, ws, need, wd, sp, timeit):
                     "fused_speedup_vs_decode_then_gemm": round(t_two / t_mv, 3),
                     "fused_blob_gbs": round(c.nbytes / (t_mv * 1e-3) / 1e9, 1),
                     "plain_weight_gbs": round(2.0 * R * C / (t_plain * 1e-3) / 1e9, 1)})
+    return {"layer_14336x4096": out, "qkv_3840": qkv_batch(timeit, sp)}
+
+
+def qkv_batch(timeit, sp):
+    """Query, key and value projections of one 3840-wide layer (three 3840 x 3840 weights
+    @4.0 bpp, seeds 900..902) on one token: three fused calls against one batched call."""
+    import torch
+    import synth
+    import decode_tile_rans_amd as ep
+    from decode_tile_rans_amd import _lib as L
+    os.environ["EP_NUM_THREADS"] = str(min(16, os.cpu_count() or 1))
+    cs = [ep.compress(synth.rowscaled(3840, 3840, 900 + i), 4.0, dtype=torch.bfloat16) for i in range(3)]
+    os.environ.pop("EP_NUM_THREADS", None)
+    for c in cs:
+        c.upload()
+    hs = [c.handle for c in cs]
+    out = {}
+    for T in (1, 8):
+        x = torch.randn(T, 3840, dtype=torch.bfloat16, device="cuda")
+        ys = [torch.empty((T, 3840), dtype=torch.bfloat16, device="cuda") for _ in cs]
+        n1 = L.ep_matvec_workspace_bytes(hs[0], T)
+        nb = L.ep_matvec_batch_workspace_bytes(hs, T)
+        ws = torch.empty(max(n1, nb), dtype=torch.uint8, device="cuda")
+        t_sep = timeit(lambda: [L.ep_compressed_matvec(h, x.data_ptr(), T, None, y.data_ptr(), ws.data_ptr(), n1, sp)
+                                for h, y in zip(hs, ys)])
+        t_bat = timeit(lambda: L.ep_compressed_matvec_batch(hs, x.data_ptr(), T, None, [y.data_ptr() for y in ys],
+                                                            ws.data_ptr(), nb, sp))
+        out[f"tokens_{T}"] = {"ms_three_calls": round(t_sep, 4), "ms_batched": round(t_bat, 4),
+                              "speedup": round(t_sep / t_bat, 3)}
     return out
 
 

@@ -33,6 +33,9 @@ SIGNATURES = {
     "ep_linear_seq_workspace_bytes": (_sz, [C.POINTER(_vp), _int]),
     "ep_matvec_workspace_bytes": (_sz, [_vp, _i64]),
     "ep_compressed_matvec": (_int, [_vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "ep_matvec_batch_workspace_bytes": (_sz, [C.POINTER(_vp), _int, _i64]),
+    "ep_compressed_matvec_batch": (_int, [C.POINTER(_vp), _int, _vp, _i64, C.POINTER(_vp), C.POINTER(_vp), _vp, _sz,
+                                          _vp]),
     "ep_compressed_linear_seq_forward": (_int, [C.POINTER(_vp), _int, C.POINTER(_vp), _i64, C.POINTER(_vp),
                                                 C.POINTER(_vp), _vp, _sz, _vp, _vp]),
     "ep_gemm_bf16_nt": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -141,6 +144,16 @@ def ep_compressed_matvec(blob, dev_x, T, dev_bias, dev_y, dev_ws, ws_bytes, stre
 
 def _ptrs(seq):
     return (_vp * len(seq))(*[p if p else None for p in seq])
+
+
+def ep_matvec_batch_workspace_bytes(blobs, T) -> int:
+    return int(lib().ep_matvec_batch_workspace_bytes(_ptrs(blobs), len(blobs), T))
+
+
+def ep_compressed_matvec_batch(blobs, dev_x, T, dev_biases, dev_ys, dev_ws, ws_bytes, stream=0):
+    biases = _ptrs(dev_biases) if dev_biases is not None else None
+    check(lib().ep_compressed_matvec_batch(_ptrs(blobs), len(blobs), dev_x, T, biases, _ptrs(dev_ys), dev_ws,
+                                           ws_bytes, stream))
 
 
 def ep_linear_seq_workspace_bytes(blobs) -> int:

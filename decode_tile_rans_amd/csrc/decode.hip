@@ -1319,41 +1319,75 @@ bool matvec_supported(const Blob& b, int64_t T) {
          b.S <= (b.C + 7) / 8;
 }
 
-// Y[T x R] = X[T x C] W^T (+ bias) with W decoded inside the product (never stored);
-// `part` (256-byte aligned, matvec_workspace_bytes - 256 bytes) holds the partial sums.
-int matvec_launch(const Blob& b, const void* x, int64_t T, const void* bias, void* y, float* part, ep_stream stream) {
+// Y_i[T x R_i] = X[T x C] W_i^T (+ bias_i) for blobs i < n sharing the activations, with
+// each W_i decoded inside the product (never stored); part[i] (256-byte aligned,
+// matvec_workspace_bytes - 256 bytes) holds blob i's partial sums.  The blobs' blocks
+// share launches (by table layout and escape variant, up to kMaxBatch blobs each).
+int matvec_batch_launch(const Blob* const* bs, int n, const void* x, int64_t T, const void* const* bias,
+                        void* const* y, float* const* part, ep_stream stream) {
   hipStream_t st = (hipStream_t)stream;
-  int rc = check_uploaded(b);
+  if (n < 1) return fail(EP_E_ARG, "empty batch");
+  if (!x || (reinterpret_cast<uintptr_t>(x) & 15)) return fail(EP_E_ARG, "activations must be 16-byte aligned");
+  int rc = check_gpu_pointer(x, "activations");
   if (rc) return rc;
-  if (!matvec_supported(b, T))
-    return fail(EP_E_ARG, "the fused product takes lossy BF16 blobs, 1..8 activation rows, C % 8 == 0 and at least S groups per row");
-  if ((reinterpret_cast<uintptr_t>(x) & 15)) return fail(EP_E_ARG, "activations must be 16-byte aligned");
-  if ((rc = check_gpu_pointer(x, "activations")) || (rc = check_gpu_pointer(y, "output")) ||
-      (rc = check_gpu_pointer(part, "workspace")))
-    return rc;
-  if (bias && (rc = check_gpu_pointer(bias, "bias"))) return rc;
+  for (int i = 0; i < n; ++i) {
+    const Blob& b = *bs[i];
+    if ((rc = check_uploaded(b))) return rc;
+    if (!matvec_supported(b, T))
+      return fail(EP_E_ARG, "the fused product takes lossy BF16 blobs, 1..8 activation rows, C % 8 == 0 and at least S groups per row");
+    if (b.C != bs[0]->C) return fail(EP_E_ARG, "blobs sharing activations need the same number of columns");
+    if (!y[i] || !part[i]) return fail(EP_E_ARG, "null output or workspace");
+    if ((rc = check_gpu_pointer(y[i], "output")) || (rc = check_gpu_pointer(part[i], "workspace"))) return rc;
+    if (bias && bias[i] && (rc = check_gpu_pointer(bias[i], "bias"))) return rc;
+  }
   const int nt = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
   const int out = nt == 1 ? OUT_MV1 : nt == 2 ? OUT_MV2 : nt == 4 ? OUT_MV4 : OUT_MV8;
-  DecJob j = make_job(b, part);
-  j.mv_x = (const uint16_t*)x;
-  j.mv_T = (uint32_t)T;
-  j.mv_slots = (uint32_t)matvec_slots(b);
-  j.mv_sat = (b.flags & kFlagSat) ? 1u : 0u;
-  const int64_t nblk = b.n_blocks;
-  Shape sh = pick_shape(&nblk, 1);
-  sh.ilp = 1;
-  const int64_t n_wg = (nblk + sh.bpw - 1) / sh.bpw;
-  DecBatch B{};
-  B.j[0] = j;
-  B.n = 1;
-  B.bpw = sh.bpw;
-  rc = launch_any(out, (b.flags & kFlagEsc) != 0, true, b.k <= 6, sh, B, n_wg, st);
-  if (rc) return rc;
-  const int64_t n = T * b.R;
-  hipLaunchKernelGGL(matvec_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part,
-                     (const uint16_t*)bias, (uint16_t*)y, T, b.R, (int64_t)((b.C + 7) / 8), j.log2S, b.n_groups(),
-                     (int)j.mv_slots, nt);
-  return hip_check(hipGetLastError(), "fused product finish launch");
+  for (int pass = 0; pass < 4; ++pass) {
+    const bool narrow = pass < 2, pesc = (pass & 1) != 0;
+    std::vector<int> idx;
+    for (int i = 0; i < n; ++i)
+      if ((bs[i]->k <= 6) == narrow && ((bs[i]->flags & kFlagEsc) != 0) == pesc) idx.push_back(i);
+    for (size_t i0 = 0; i0 < idx.size(); i0 += kMaxBatch) {
+      DecBatch B{};
+      B.n = (int)std::min<size_t>(kMaxBatch, idx.size() - i0);
+      int64_t nblk[kMaxBatch];
+      for (int q = 0; q < B.n; ++q) nblk[q] = bs[idx[i0 + q]]->n_blocks;
+      Shape sh = pick_shape(nblk, B.n);
+      sh.ilp = 1;
+      B.bpw = sh.bpw;
+      int64_t wg = 0;
+      for (int q = 0; q < B.n; ++q) {
+        const int i = idx[i0 + q];
+        const Blob& b = *bs[i];
+        DecJob j = make_job(b, part[i]);
+        j.mv_x = (const uint16_t*)x;
+        j.mv_T = (uint32_t)T;
+        j.mv_slots = (uint32_t)matvec_slots(b);
+        j.mv_sat = (b.flags & kFlagSat) ? 1u : 0u;
+        j.wg_begin = wg;
+        wg += (j.n_blocks + sh.bpw - 1) / sh.bpw;
+        B.j[q] = j;
+      }
+      if ((rc = launch_any(out, pesc, true, narrow, sh, B, wg, st))) return rc;
+    }
+  }
+  for (int i = 0; i < n; ++i) {
+    const Blob& b = *bs[i];
+    const int64_t cnt = T * b.R;
+    hipLaunchKernelGGL(matvec_finish_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st, part[i],
+                       (const uint16_t*)(bias ? bias[i] : nullptr), (uint16_t*)y[i], T, b.R, (int64_t)((b.C + 7) / 8),
+                       (int)__builtin_ctz((unsigned)b.S), b.n_groups(), matvec_slots(b), nt);
+    if ((rc = hip_check(hipGetLastError(), "fused product finish launch"))) return rc;
+  }
+  return EP_OK;
+}
+
+int matvec_launch(const Blob& b, const void* x, int64_t T, const void* bias, void* y, float* part, ep_stream stream) {
+  const Blob* bs[1] = {&b};
+  const void* bi[1] = {bias};
+  void* ys[1] = {y};
+  float* ps[1] = {part};
+  return matvec_batch_launch(bs, 1, x, T, bi, ys, ps, stream);
 }
 
 int matvec_forward(const Blob& b, const void* x, int64_t T, const void* bias, void* y, void* ws, size_t ws_bytes,

@@ -155,6 +155,8 @@ int check_gpu_pointer(const void* p, const char* what);
 constexpr int64_t kMatvecMaxT = 8;
 bool matvec_supported(const Blob& b, int64_t T);
 size_t matvec_workspace_bytes(const Blob& b, int64_t T);
+int matvec_batch_launch(const Blob* const* bs, int n, const void* x, int64_t T, const void* const* bias,
+                        void* const* y, float* const* part, ep_stream st);
 int matvec_launch(const Blob& b, const void* x, int64_t T, const void* bias, void* y, float* part, ep_stream st);
 int matvec_forward(const Blob& b, const void* x, int64_t T, const void* bias, void* y, void* ws, size_t ws_bytes,
                    ep_stream st);

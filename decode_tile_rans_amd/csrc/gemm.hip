@@ -373,6 +373,37 @@ int ep_compressed_matvec(const ep_blob* w, const void* x, int64_t T, const void*
   return matvec_forward(w->b, x, T, bias, y, ws, ws_bytes, stream);
 }
 
+size_t ep_matvec_batch_workspace_bytes(const ep_blob* const* w, int n, int64_t T) {
+  if (!w || n < 1) return 0;
+  size_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!w[i] || !matvec_supported(w[i]->b, T)) return 0;
+    total += (matvec_workspace_bytes(w[i]->b, T) - 256 + 255) & ~size_t(255);
+  }
+  return total + 256;
+}
+
+int ep_compressed_matvec_batch(const ep_blob* const* w, int n, const void* x, int64_t T, const void* const* bias,
+                               void* const* y, void* ws, size_t ws_bytes, ep_stream stream) {
+  set_error("");
+  if (!w || !x || !y || !ws || n < 1) return fail(EP_E_ARG, "null pointer or empty batch");
+  for (int i = 0; i < n; ++i)
+    if (!w[i] || !y[i]) return fail(EP_E_ARG, "null blob or output");
+  const size_t need = ep_matvec_batch_workspace_bytes(w, n, T);
+  if (need == 0)
+    return fail(EP_E_ARG, "the fused product takes lossy BF16 blobs, 1..8 activation rows, C % 8 == 0 and at least S groups per row");
+  if (ws_bytes < need) return fail(EP_E_WORKSPACE, "workspace too small");
+  std::vector<const Blob*> bs(n);
+  std::vector<float*> part(n);
+  uintptr_t p = ((uintptr_t)ws + 255) & ~uintptr_t(255);
+  for (int i = 0; i < n; ++i) {
+    bs[i] = &w[i]->b;
+    part[i] = (float*)p;
+    p += (matvec_workspace_bytes(w[i]->b, T) - 256 + 255) & ~size_t(255);
+  }
+  return matvec_batch_launch(bs.data(), n, x, T, bias, y, part.data(), stream);
+}
+
 size_t ep_linear_seq_workspace_bytes(const ep_blob* const* w, int n) {
   if (!w || n < 1) return 0;
   size_t mx = 0;

@@ -181,6 +181,19 @@ size_t ep_matvec_workspace_bytes(const ep_blob* w, int64_t T);
 int ep_compressed_matvec(const ep_blob* w, const void* dev_x, int64_t T, const void* dev_bias,
                          void* dev_y, void* dev_ws, size_t ws_bytes, ep_stream stream);
 
+/* The fused product for n blobs that take the same activations (e.g. the query, key
+ * and value projections of one layer): y[i] = x W_i^T (+ bias[i]), all W_i with the same
+ * cols; bias may be NULL or hold NULLs.  The blobs' blocks share decode launches, which
+ * fills the GPU better than n separate calls (one matrix of a few thousand rows leaves
+ * most wave slots idle).  dev_ws >= ep_matvec_batch_workspace_bytes(w, n, T) (0 when a
+ * blob or T is not taken).  Each y[i] equals ep_compressed_matvec's result for blob i,
+ * bit for bit.  Same requirements and errors as ep_compressed_matvec, and EP_E_ARG when
+ * the blobs' cols differ.  Asynchronous. */
+size_t ep_matvec_batch_workspace_bytes(const ep_blob* const* w, int n, int64_t T);
+int ep_compressed_matvec_batch(const ep_blob* const* w, int n, const void* dev_x, int64_t T,
+                               const void* const* dev_bias, void* const* dev_y, void* dev_ws,
+                               size_t ws_bytes, ep_stream stream);
+
 /* Plain BF16 "NT" GEMM on MFMA: y[T x N] = x[T x K] w[N x K]^T (+ bias[N]), fp32
  * accumulate, BF16 out.  The uncompressed baseline of the linear layer. */
 int ep_gemm_bf16_nt(const void* dev_x, const void* dev_w, const void* dev_bias,

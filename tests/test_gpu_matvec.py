@@ -186,3 +186,74 @@ def test_matvec_refusals():
         with pytest.raises(L.EPError):
             L.ep_compressed_matvec(d.h, x.data_ptr(), 4, 0, y.data_ptr(), ws.data_ptr(), need, stream_ptr())
     torch.cuda.synchronize()
+
+
+def _single(L, db, x, T, bias):
+    import torch
+    need = L.ep_matvec_workspace_bytes(db.h, T)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, db.R), dtype=torch.bfloat16, device="cuda")
+    L.ep_compressed_matvec(db.h, x.data_ptr(), T, bias.data_ptr() if bias is not None else 0, y.data_ptr(),
+                           ws.data_ptr(), need, stream_ptr())
+    return y
+
+
+@pytest.mark.parametrize("specs,T", [
+    # (rows, target bpp, chains per tile) sharing 768 columns: narrow and wide tables,
+    # with and without escapes, several chain counts, in one call
+    ([(384, 4.0, 8), (640, 8.0, 8), (200, 2.3, 1), (1000, 5.0, 4)], 3),
+    # more blobs than one launch takes
+    ([(64 + 8 * i, 3.0 + 0.25 * (i % 4), 8) for i in range(14)], 1),
+])
+def test_matvec_batch_equals_single_calls(specs, T):
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    C = 768
+    say("matvec batch", len(specs), T)
+    dbs, biases, blobs = [], [], []
+    for i, (R, bpp, S) in enumerate(specs):
+        blob = oracle.compress(synth.rowscaled(R, C, 200 + i), nx.DT_BF16, bpp, chains_per_tile=S)
+        blobs.append(blob)
+        dbs.append(DevBlob(blob))
+        b = synth.f32_to_bf16_bits(np.linspace(-0.3, 0.3, R).astype(np.float32)) if i % 3 != 1 else None
+        biases.append(_t(b, torch.bfloat16) if b is not None else None)
+    x_bits = synth.activations(T, C, 300)
+    x = _t(x_bits, torch.bfloat16)
+    hs = [d.h for d in dbs]
+    need = L.ep_matvec_batch_workspace_bytes(hs, T)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ys = [torch.empty((T, d.R), dtype=torch.bfloat16, device="cuda") for d in dbs]
+    bp = [b.data_ptr() if b is not None else 0 for b in biases]
+    with pytest.raises(L.EPError):
+        L.ep_compressed_matvec_batch(hs, x.data_ptr(), T, bp, [y.data_ptr() for y in ys], ws.data_ptr(), need - 1,
+                                     stream_ptr())
+    L.ep_compressed_matvec_batch(hs, x.data_ptr(), T, bp, [y.data_ptr() for y in ys], ws.data_ptr(), need,
+                                 stream_ptr())
+    torch.cuda.synchronize()
+    for i, (db, y, b) in enumerate(zip(dbs, ys, biases)):
+        one = _single(L, db, x, T, b)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), one.view(torch.int16)), f"blob {i} differs from its single call"
+    # one of them against the oracle product
+    _, w_hat, _ = oracle.decode(blobs[1])
+    _check(_bits(ys[1]), x_bits, w_hat, None if biases[1] is None else _bits(biases[1]))
+    for db in dbs:
+        assert db.errors() == 0
+
+
+def test_matvec_batch_refuses_mixed_widths():
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    say("matvec batch refusals")
+    a = DevBlob(oracle.compress(synth.rowscaled(64, 256, 1), nx.DT_BF16, 4.0))
+    b = DevBlob(oracle.compress(synth.rowscaled(64, 512, 2), nx.DT_BF16, 4.0))
+    x = torch.zeros((2, 512), dtype=torch.bfloat16, device="cuda")
+    ys = [torch.empty((2, 64), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    need = L.ep_matvec_batch_workspace_bytes([a.h, b.h], 2)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    with pytest.raises(L.EPError):
+        L.ep_compressed_matvec_batch([a.h, b.h], x.data_ptr(), 2, None, [y.data_ptr() for y in ys], ws.data_ptr(),
+                                     need, stream_ptr())
+    assert L.ep_matvec_batch_workspace_bytes([a.h, b.h], 9) == 0
+    torch.cuda.synchronize()
