@@ -68,6 +68,33 @@ def copy_calibration(reps=5):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": reps}))
 
 
+def practical_ceilings(reps=10):
+    """Achievable HBM rates on this GPU as context for the decode's byte rate: a plain
+    1 GiB device copy (read + write) and a 1 GiB fill (write only), torch's own kernels."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    st = torch.cuda.current_stream()
+
+    def rate(fn, bytes_moved):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return round(bytes_moved / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+
+    out = {"copy_GBps": rate(lambda: b.copy_(a), 2 * n), "write_only_GBps": rate(lambda: b.fill_(2), n)}
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def build_stack(n, target_bpp):
     """Draw the stack on the GPU, compress on the host (all cores), upload blobs."""
     import torch
@@ -549,14 +576,17 @@ def main():
                      "algorithmic_bytes_per_launch": round(alg_bytes / len(units)),
                      "step_effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
                      "valu_issue_per_launch": valu_issue(n_params / (kern_ms * 1e-3)),
-                     "valu_issue_step": valu_issue(n_params / (ms * 1e-3))},
+                     "valu_issue_step": valu_issue(n_params / (ms * 1e-3)),
+                     "practical_ceilings": practical_ceilings()},
     }
     if not a.no_layer_mode:
         ms_l, lms, units_l = time_stack(comps, blocks, outs, max(2, a.steps // 2), 1, per_layer=True,
                                         n_streams=max(a.streams, 4))
         result["per_layer_mode"] = {"ms_per_step": round(ms_l, 4),
                                     "bf16_out_GBps": round(out_bytes / (ms_l * 1e-3) / 1e9, 2),
-                                    "hbm_frac": round(alg_bytes / (sum(lms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                    # the step's algorithmic bytes over its wall time (the launches
+                                    # overlap across streams, so their durations do not add up)
+                                    "hbm_frac": round(alg_bytes / (ms_l * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                     "launches_per_step": len(units_l), "streams": max(a.streams, 4)}
     del outs
     torch.cuda.empty_cache()

@@ -58,9 +58,8 @@ __device__ __align__(16) uint4 g_zero_line[4];   // zero-initialised; the source
 // a per-wave value the compiler may keep in a scalar register
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <int BN> struct GemmCfg;
-template <> struct GemmCfg<128> { static constexpr int NST = 3, WAVES = 4; };
-template <> struct GemmCfg<256> { static constexpr int NST = 2, WAVES = 8; };
+// waves per workgroup by tile width
+constexpr int gemm_waves(int BN) { return BN == 256 ? 8 : 4; }
 
 // chunk position of logical chunk c in row r (CPR chunks per row)
 template <int CPR>
@@ -68,14 +67,14 @@ __device__ __forceinline__ int swz(int r, int c) {
   return CPR == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 1) & 3));
 }
 
-template <int BN, bool FP8>
-__global__ void __launch_bounds__(64 * GemmCfg<BN>::WAVES, 1) gemm_tile_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
+template <int BN, int NST, int RB, bool FP8>
+__global__ void __launch_bounds__(64 * gemm_waves(BN), 1) gemm_tile_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
                                                            const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
                                                            int64_t T, int64_t N, int64_t K, int ntm, int ntn, float ax,
                                                            const float* __restrict__ aw) {
-  constexpr int NST = GemmCfg<BN>::NST, NW = GemmCfg<BN>::WAVES;
-  constexpr int RB = 128, CPR = RB / 16, RPL = 64 / CPR;      // row bytes, chunks per row, rows per load
-  constexpr int NKS = FP8 ? 2 : 4;                            // MFMA K steps per stage
+  constexpr int NW = gemm_waves(BN);
+  constexpr int CPR = RB / 16, RPL = 64 / CPR;                // chunks per row, rows per load
+  constexpr int NKS = RB / (FP8 ? 64 : 32);                   // MFMA K steps per stage
   constexpr bool kDoubleFrag = !(FP8 && BN == 256);           // fragments double-buffered
   const int64_t KB = FP8 ? K : 2 * K;                         // bytes of K per matrix row
   constexpr int A_BYTES = GBM * RB, B_BYTES = BN * RB, STAGE = A_BYTES + B_BYTES;
@@ -192,7 +191,8 @@ __global__ void __launch_bounds__(64 * GemmCfg<BN>::WAVES, 1) gemm_tile_kernel(c
   auto tile = [&](int64_t kt, int st) {
     // this wave's loads of tile kt are done once at most the later tiles' loads remain
     const int64_t later = (nkt - 1 - kt) < (NST - 2) ? (nkt - 1 - kt) : (NST - 2);
-    if (NST >= 4 && later >= 2) __builtin_amdgcn_s_waitcnt((2 * LD & 15) | (((2 * LD) >> 4) << 14) | (7 << 4) | (15 << 8));
+    if (NST >= 5 && later >= 3) __builtin_amdgcn_s_waitcnt((3 * LD & 15) | (((3 * LD) >> 4) << 14) | (7 << 4) | (15 << 8));
+    else if (NST >= 4 && later >= 2) __builtin_amdgcn_s_waitcnt((2 * LD & 15) | (((2 * LD) >> 4) << 14) | (7 << 4) | (15 << 8));
     else if (later >= 1) __builtin_amdgcn_s_waitcnt((LD & 15) | ((LD >> 4) << 14) | (7 << 4) | (15 << 8));
     else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
     // every wave's part of tile kt is in LDS and stage (kt - 1) % NST is free once all
@@ -279,15 +279,15 @@ __global__ void __launch_bounds__(64 * GemmCfg<BN>::WAVES, 1) gemm_tile_kernel(c
   }
 }
 
-template <int BN, bool FP8>
+template <int BN, int NST, int RB, bool FP8>
 int launch_tile(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K, float ax,
                 const float* aw, hipStream_t st) {
-  constexpr int lds = GemmCfg<BN>::NST * (GBM + BN) * 128;
-  auto kern = gemm_tile_kernel<BN, FP8>;
+  constexpr int lds = NST * (GBM + BN) * RB;
+  auto kern = gemm_tile_kernel<BN, NST, RB, FP8>;
   static std::once_flag once;
   std::call_once(once, [&] { (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); });
   const int ntm = (int)((T + GBM - 1) / GBM), ntn = (int)((N + BN - 1) / BN);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(64 * GemmCfg<BN>::WAVES), lds, st, (const uint8_t*)x,
+  hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(64 * gemm_waves(BN)), lds, st, (const uint8_t*)x,
                      (const uint8_t*)w, (const uint16_t*)bias, (uint16_t*)y, T, N, K, ntm, ntn, ax, aw);
   return hip_check(hipGetLastError(), "gemm launch");
 }
@@ -311,8 +311,8 @@ int launch_gemm(const void* x, const void* w, const void* bias, void* y, int64_t
   };
   bool narrow = eff(128) > 1.25 * eff(256);
   if (const char* e = std::getenv("EP_GEMM_BN")) narrow = std::atoi(e) == 128;
-  if (narrow) return launch_tile<128, FP8>(x, w, bias, y, T, N, K, ax, aw, st);
-  return launch_tile<256, FP8>(x, w, bias, y, T, N, K, ax, aw, st);
+  if (narrow) return launch_tile<128, 3, 128, FP8>(x, w, bias, y, T, N, K, ax, aw, st);
+  return launch_tile<256, 2, 128, FP8>(x, w, bias, y, T, N, K, ax, aw, st);
 }
 
 int launch_bf16(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K,
