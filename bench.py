@@ -47,6 +47,7 @@ def parse():
     p.add_argument("--no-layer-mode", action="store_true")
     p.add_argument("--no-lossless", action="store_true")
     p.add_argument("--no-gpu-encode", action="store_true")
+    p.add_argument("--no-sweep", action="store_true", help="skip the 8192^2 container and chains-per-tile sweep")
     p.add_argument("--matrices", type=int, default=276, help="first N matrices of the stack (profiling runs)")
     p.add_argument("--streams", type=int, default=3, help="HIP streams the block launches rotate over")
     p.add_argument("--copy-calibration", action="store_true",
@@ -91,6 +92,74 @@ def practical_ceilings(reps=10):
 
     out = {"copy_GBps": rate(lambda: b.copy_(a), 2 * n), "write_only_GBps": rate(lambda: b.fill_(2), n)}
     del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def container_sweep(reps=10):
+    """One 8192 x 8192 matrix (log-normal row scales, seed 4; FP8 / INT8 per-row absmax
+    codes of it): decode time per container and target bitrate, warm (back to back) and
+    cold (a 512 MB write between launches evicts the 256 MB last-level cache); then the
+    chains-per-tile sweep at BF16 4.0 bpp (state bits per tile against parallelism)."""
+    import torch
+    import synth
+    import decode_tile_rans_amd as ep
+    from decode_tile_rans_amd import _lib as L
+    n = 8192
+    st = torch.cuda.current_stream()
+    sp = int(st.cuda_stream)
+    junk = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def times(c, out_t):
+        dst = torch.empty((n, n), dtype=out_t, device="cuda")
+        for _ in range(3):
+            L.ep_decompress(c.handle, dst.data_ptr(), sp)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            L.ep_decompress(c.handle, dst.data_ptr(), sp)
+        b.record(st)
+        torch.cuda.synchronize()
+        warm = a.elapsed_time(b) / reps
+        cold = 0.0
+        for _ in range(reps):
+            junk.fill_(1)
+            a.record(st)
+            L.ep_decompress(c.handle, dst.data_ptr(), sp)
+            b.record(st)
+            torch.cuda.synchronize()
+            cold += a.elapsed_time(b) / reps
+        return warm, cold
+
+    def entry(c, out_t, esz, **kw):
+        warm, cold = times(c, out_t)
+        alg = c.nbytes + esz * n * n
+        return dict(kw, actual_bpp=round(c.actual_bpp, 4), ms_warm=round(warm, 4), ms_cold=round(cold, 4),
+                    out_GBps_warm=round(esz * n * n / (warm * 1e-3) / 1e9, 1),
+                    hbm_frac_warm=round(alg / (warm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    hbm_frac_cold=round(alg / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+
+    os.environ["EP_NUM_THREADS"] = str(min(16, os.cpu_count() or 1))
+    out = {"containers": [], "chains_per_tile": []}
+    bf = synth.rowscaled(n, n, 4)
+    for kind, t in (("bf16", 2.3), ("bf16", 3.0), ("bf16", 5.0), ("bf16", 8.0), ("fp8", 5.0), ("int8", 4.0)):
+        if kind == "bf16":
+            c, out_t, esz = ep.compress(bf, t, dtype=torch.bfloat16), torch.bfloat16, 2
+        elif kind == "fp8":
+            c, out_t, esz = ep.compress(synth.fp8_codes(n, n, 4)[0], t, dtype=torch.float8_e4m3fn), torch.float8_e4m3fn, 1
+        else:
+            c, out_t, esz = ep.compress(synth.int8_codes(n, n, 4)[0], t, dtype=torch.int8), torch.int8, 1
+        c.upload()
+        out["containers"].append(entry(c, out_t, esz, container=kind, target_bpp=t))
+        del c
+    for S in (1, 2, 4, 8):
+        c = ep.compress(bf, 4.0, dtype=torch.bfloat16, chains_per_tile=S)
+        c.upload()
+        out["chains_per_tile"].append(entry(c, torch.bfloat16, 2, S=S))
+        del c
+    os.environ.pop("EP_NUM_THREADS", None)
+    del junk
     torch.cuda.empty_cache()
     return out
 
@@ -597,6 +666,8 @@ def main():
         result["lossless"] = lossless_block()
     if not a.no_gpu_encode:
         result["gpu_encode"] = gpu_encode_stack(a.matrices, a.target_bpp)
+    if not a.no_sweep:
+        result["sweep_8192"] = container_sweep()
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(a.target_bpp)
     print(json.dumps(result))

@@ -33,6 +33,7 @@ SIGNATURES = {
     "ep_linear_seq_workspace_bytes": (_sz, [C.POINTER(_vp), _int]),
     "ep_matvec_workspace_bytes": (_sz, [_vp, _i64]),
     "ep_compressed_matvec": (_int, [_vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "ep_test_cast": (_int, [_int, _vp, _vp, _i64, _int, _vp]),
     "ep_matvec_batch_workspace_bytes": (_sz, [C.POINTER(_vp), _int, _i64]),
     "ep_compressed_matvec_batch": (_int, [C.POINTER(_vp), _int, _vp, _i64, C.POINTER(_vp), C.POINTER(_vp), _vp, _sz,
                                           _vp]),
@@ -132,6 +133,10 @@ def ep_linear_workspace_bytes(blob: int) -> int:
 
 def ep_compressed_linear_forward(blob, dev_x, T, dev_bias, dev_y, dev_ws, ws_bytes, stream=0):
     check(lib().ep_compressed_linear_forward(blob, dev_x, T, dev_bias, dev_y, dev_ws, ws_bytes, stream))
+
+
+def ep_test_cast(dtype, dev_in, dev_out, n, hw=0, stream=0):
+    check(lib().ep_test_cast(dtype, dev_in, dev_out, n, hw, stream))
 
 
 def ep_matvec_workspace_bytes(blob: int, T: int) -> int:

@@ -114,6 +114,25 @@ __device__ inline uint32_t f32_to_e4m3fn(float v) {
   return code | sign;
 }
 
+// Four values to E4M3FN bytes (value i in byte i).  HW: clamp to +-448 (v_med3), then
+// the conversion instruction (round to nearest even, OCP E4M3FN on gfx950), two values
+// per instruction; otherwise the bit manipulation above, one value at a time.
+template <bool HW>
+__device__ inline uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  if constexpr (HW) {
+    a = __builtin_amdgcn_fmed3f(a, -448.f, 448.f);
+    b = __builtin_amdgcn_fmed3f(b, -448.f, 448.f);
+    c = __builtin_amdgcn_fmed3f(c, -448.f, 448.f);
+    d = __builtin_amdgcn_fmed3f(d, -448.f, 448.f);
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    return (uint32_t)r;
+  } else {
+    return f32_to_e4m3fn(a) | (f32_to_e4m3fn(b) << 8) | (f32_to_e4m3fn(c) << 16) | (f32_to_e4m3fn(d) << 24);
+  }
+}
+constexpr bool kFp8Hw = true;    // the decoder's FP8 cast
+
 __device__ inline uint32_t f32_to_i8(float v) {
   float r = fminf(fmaxf(rintf(v), -128.f), 127.f);
   return (uint32_t)((int32_t)r) & 0xFFu;
@@ -168,12 +187,15 @@ __device__ inline void store_group(void* out, int64_t base, const float* vin, co
     }
   } else if (OUT == OUT_FP8 || OUT == OUT_INT8) {
     uint32_t lo = 0, hi = 0;
+    if constexpr (OUT == OUT_FP8) {
+      lo = pack_fp8x4<kFp8Hw>(v[0], v[1], v[2], v[3]);
+      hi = pack_fp8x4<kFp8Hw>(v[4], v[5], v[6], v[7]);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t a = (OUT == OUT_FP8) ? f32_to_e4m3fn(v[i]) : f32_to_i8(v[i]);
-      uint32_t b = (OUT == OUT_FP8) ? f32_to_e4m3fn(v[i + 4]) : f32_to_i8(v[i + 4]);
-      lo |= a << (8 * i);
-      hi |= b << (8 * i);
+      for (int i = 0; i < 4; ++i) {
+        lo |= f32_to_i8(v[i]) << (8 * i);
+        hi |= f32_to_i8(v[i + 4]) << (8 * i);
+      }
     }
     uint8_t* o = (uint8_t*)out + base;
     if (full) {
@@ -1303,7 +1325,46 @@ __global__ void matvec_finish_kernel(const float* __restrict__ part, const uint1
   y[t * R + r] = __builtin_bit_cast(uint16_t, o);
 }
 
+// Test hook: the container casts of the decoder applied to plain float inputs, one
+// group of eight per thread (FP8 through the instruction or the bit manipulation).
+template <int OUT, bool HW>
+__global__ void cast_test_kernel(const float* __restrict__ in, uint8_t* __restrict__ out, int64_t n) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t base = g * 8;
+  if (base >= n) return;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = base + i < n ? in[base + i] : 0.f;
+  if constexpr (OUT == OUT_FP8) {
+    const uint32_t lo = pack_fp8x4<HW>(v[0], v[1], v[2], v[3]), hi = pack_fp8x4<HW>(v[4], v[5], v[6], v[7]);
+    for (int i = 0; i < 8 && base + i < n; ++i) out[base + i] = (uint8_t)((i < 4 ? lo : hi) >> (8 * (i & 3)));
+  } else {
+    store_group<OUT>(out, base, v, nullptr, base + 8 <= n, n - base);
+  }
+}
+
 }  // namespace
+
+int test_cast(int dtype, const float* in, void* out, int64_t n, int hw, ep_stream stream) {
+  hipStream_t st = (hipStream_t)stream;
+  if (n < 0 || (n > 0 && (!in || !out))) return fail(EP_E_ARG, "null pointer or negative size");
+  if (n == 0) return EP_OK;
+  int rc;
+  if ((rc = check_gpu_pointer(in, "input")) || (rc = check_gpu_pointer(out, "output"))) return rc;
+  const dim3 grid((unsigned)((n + 8 * 256 - 1) / (8 * 256))), block(256);
+  uint8_t* o = (uint8_t*)out;
+  switch (dtype) {
+    case EP_BF16: hipLaunchKernelGGL((cast_test_kernel<OUT_BF16_SAT, false>), grid, block, 0, st, in, o, n); break;
+    case EP_FP16: hipLaunchKernelGGL((cast_test_kernel<OUT_FP16, false>), grid, block, 0, st, in, o, n); break;
+    case EP_INT8: hipLaunchKernelGGL((cast_test_kernel<OUT_INT8, false>), grid, block, 0, st, in, o, n); break;
+    case EP_FP8_E4M3FN:
+      if (hw) hipLaunchKernelGGL((cast_test_kernel<OUT_FP8, true>), grid, block, 0, st, in, o, n);
+      else hipLaunchKernelGGL((cast_test_kernel<OUT_FP8, false>), grid, block, 0, st, in, o, n);
+      break;
+    default: return fail(EP_E_DTYPE, "cast test takes BF16, FP16, FP8 or INT8");
+  }
+  return hip_check(hipGetLastError(), "cast test launch");
+}
 
 // Rows a chain's groups can touch: the chain's groups lie within its tile's 512
 // consecutive groups, so at most 511 / G + 2 rows.
@@ -1509,6 +1570,11 @@ int ep_decompress_tiles(const ep_blob* blob, int64_t tile_begin, int64_t tile_en
   const Blob& b = blob->b;
   if (tile_begin < 0 || tile_end > b.n_tiles || tile_begin > tile_end) return fail(EP_E_ARG, "tile range out of bounds");
   return decode_one(b, dev_dst, tile_begin * b.S, tile_end * b.S, out_kind(b), (hipStream_t)stream);
+}
+
+int ep_test_cast(int dtype, const float* dev_in, void* dev_out, int64_t n, int hw, ep_stream stream) {
+  set_error("");
+  return test_cast(dtype, dev_in, dev_out, n, hw, stream);
 }
 
 int ep_test_decode_coords(const ep_blob* blob, int32_t* dev_u, ep_stream stream) {

@@ -150,6 +150,8 @@ int hip_check(int err, const char* what);
 // EP_E_ARG unless the GPU can dereference p (device, managed or pinned host memory)
 int check_gpu_pointer(const void* p, const char* what);
 
+int test_cast(int dtype, const float* in, void* out, int64_t n, int hw, ep_stream stream);
+
 // Fused matrix-vector product of a lossy BF16 blob (decode.hip): up to kMatvecMaxT
 // activation rows; the weights are decoded and multiplied in one kernel.
 constexpr int64_t kMatvecMaxT = 8;

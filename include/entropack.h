@@ -136,6 +136,14 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dev_dsts, int 
  * the E8 point p) instead of weights.  Same kernel, coordinate-emitting variant. */
 int ep_test_decode_coords(const ep_blob* blob, int32_t* dev_u, ep_stream stream);
 
+/* Test hook: the decoder's container casts of float32 values ([NEWS]: the stored dtype
+ * is restored; BF16 and FP16 round to nearest even and saturate, FP8-E4M3FN rounds to
+ * nearest even and saturates at 448, INT8 rounds half to even and clamps to [-128, 127])
+ * applied to n device floats, writing n container elements to dev_out.  For FP8, hw = 1
+ * uses the conversion instruction (after clamping), hw = 0 the bit manipulation; other
+ * dtypes ignore hw.  EP_E_DTYPE for FP32 or unknown dtypes.  Asynchronous. */
+int ep_test_cast(int dtype, const float* dev_in, void* dev_out, int64_t n, int hw, ep_stream stream);
+
 /* Device-side error count of the blob (decodes whose rANS chains did not end in the
  * initial state).  Synchronises the device. */
 int64_t ep_blob_device_errors(const ep_blob* blob);
