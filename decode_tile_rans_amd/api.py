@@ -206,7 +206,8 @@ class CompressedLinear(torch.nn.Module):
     """Drop-in replacement of a BF16 ``torch.nn.Linear`` whose weight is stored compressed.
 
     forward(x) decodes the weight into a workspace and runs the MFMA GEMM
-    (ep_compressed_linear_forward).  The compressed bytes live in the
+    (ep_compressed_linear_forward); with at most 8 input rows the decode kernel forms
+    the product itself and no weights are written.  The compressed bytes live in the
     ``packed`` buffer so they travel with ``state_dict``.
     """
 
@@ -253,3 +254,28 @@ class CompressedLinear(torch.nn.Module):
         L.ep_compressed_linear_forward(self._c.handle, x2.data_ptr(), x2.shape[0], b, y.data_ptr(),
                                        self._ws.data_ptr(), need, _stream_ptr())
         return y.reshape(*lead, self.out_features)
+
+
+def linear_batch(layers, x: torch.Tensor):
+    """Several CompressedLinear layers applied to the same input (e.g. a block's query,
+    key and value projections): [layer(x) for layer in layers], bit for bit.  With at most
+    8 input rows the layers' decodes share launches (ep_compressed_matvec_batch)."""
+    layers = list(layers)
+    if not layers:
+        return []
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, layers[0].in_features).to(torch.bfloat16).contiguous()
+    T = x2.shape[0]
+    for m in layers:
+        m._c.upload()
+    hs = [m._c.handle for m in layers]
+    need = L.ep_matvec_batch_workspace_bytes(hs, T) if all(m.in_features == layers[0].in_features for m in layers) else 0
+    fused = need > 0 and all(L.ep_matvec_workspace_bytes(h, T) <= L.ep_linear_workspace_bytes(h) for h in hs)
+    if not fused:
+        return [m(x) for m in layers]
+    ws = torch.empty(need, dtype=torch.uint8, device=x2.device)
+    ys = [torch.empty((T, m.out_features), dtype=torch.bfloat16, device=x2.device) for m in layers]
+    biases = [m.bias.data_ptr() if m.bias is not None else None for m in layers]
+    L.ep_compressed_matvec_batch(hs, x2.data_ptr(), T, biases, [y.data_ptr() for y in ys], ws.data_ptr(), need,
+                                 _stream_ptr())
+    return [y.reshape(*lead, m.out_features) for y, m in zip(ys, layers)]

@@ -257,3 +257,21 @@ def test_matvec_batch_refuses_mixed_widths():
                                      need, stream_ptr())
     assert L.ep_matvec_batch_workspace_bytes([a.h, b.h], 9) == 0
     torch.cuda.synchronize()
+
+
+def test_python_linear_batch_equals_layers():
+    """ep.linear_batch over three layers sharing an input: the same bits as calling each
+    layer, for 2 tokens (fused, one batched call) and for 20 (decode then GEMM)."""
+    import torch
+    import decode_tile_rans_amd as ep
+    say("python linear_batch")
+    torch.manual_seed(3)
+    layers = [ep.CompressedLinear.from_linear(torch.nn.Linear(512, r, dtype=torch.bfloat16, device="cuda"),
+                                              target_bpp=4.0) for r in (256, 384, 128)]
+    for T in (2, 20):
+        x = torch.randn(T, 512, dtype=torch.bfloat16, device="cuda")
+        with torch.inference_mode():
+            got = ep.linear_batch(layers, x)
+            want = [m(x) for m in layers]
+        for g, w in zip(got, want):
+            assert g.shape == w.shape and torch.equal(g.view(torch.int16), w.view(torch.int16))
