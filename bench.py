@@ -346,11 +346,23 @@ def fused_linear(target_bpp, reps=10):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    t_fused = timeit(lambda: L.ep_compressed_linear_forward(c.handle, x.data_ptr(), T, None, y.data_ptr(),
-                                                            ws.data_ptr(), need, sp))
-    t_dec = timeit(lambda: L.ep_decompress(c.handle, wd, sp))
-    t_gemm = timeit(lambda: L.ep_gemm_bf16_nt(x.data_ptr(), w.data_ptr(), None, y.data_ptr(), T, R, C, sp))
-    t_torch = timeit(lambda: torch.matmul(x, w.t()))
+    fns = {
+        "fused": lambda: L.ep_compressed_linear_forward(c.handle, x.data_ptr(), T, None, y.data_ptr(), ws.data_ptr(),
+                                                        need, sp),
+        "dec": lambda: L.ep_decompress(c.handle, wd, sp),
+        "gemm": lambda: L.ep_gemm_bf16_nt(x.data_ptr(), w.data_ptr(), None, y.data_ptr(), T, R, C, sp),
+        "torch": lambda: torch.matmul(x, w.t()),
+    }
+    # the GPU's clocks settle over the first few hundred milliseconds of MFMA load: run the
+    # GEMM until then, and take each variant's best of three rounds measured in turn
+    for _ in range(40):
+        fns["gemm"]()
+    torch.cuda.synchronize()
+    best = {k: min(timeit(f) for _ in range(3)) for k, f in fns.items()}
+    for _ in range(2):
+        for k, f in fns.items():
+            best[k] = min(best[k], timeit(f))
+    t_fused, t_dec, t_gemm, t_torch = best["fused"], best["dec"], best["gemm"], best["torch"]
     flops = 2.0 * T * R * C
     # a sequence of layers (4 distinct weights, each twice): the next layer's decode on a
     # second stream while this layer's GEMM runs, against the same GEMMs on plain weights
@@ -378,15 +390,19 @@ def small_batch(c, w, x, ws, need, wd, sp, timeit):
     from decode_tile_rans_amd import _lib as L
     R, C = c.shape
     out = []
+
+    def best(fn):
+        return min(timeit(fn) for _ in range(3))
+
     for T in (1, 2, 4, 8):
         xs = x[:T].contiguous()
         y = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
         nmv = L.ep_matvec_workspace_bytes(c.handle, T)
-        t_mv = timeit(lambda: L.ep_compressed_matvec(c.handle, xs.data_ptr(), T, None, y.data_ptr(), ws.data_ptr(),
+        t_mv = best(lambda: L.ep_compressed_matvec(c.handle, xs.data_ptr(), T, None, y.data_ptr(), ws.data_ptr(),
                                                      nmv, sp))
-        t_two = timeit(lambda: (L.ep_decompress(c.handle, wd, sp),
+        t_two = best(lambda: (L.ep_decompress(c.handle, wd, sp),
                                 L.ep_gemm_bf16_nt(xs.data_ptr(), wd, None, y.data_ptr(), T, R, C, sp)))
-        t_plain = timeit(lambda: torch.matmul(xs, w.t()))
+        t_plain = best(lambda: torch.matmul(xs, w.t()))
         out.append({"tokens": T, "ms_fused": round(t_mv, 4), "ms_decode_then_gemm": round(t_two, 4),
                     "ms_hipblaslt_plain_bf16": round(t_plain, 4),
                     "fused_speedup_vs_decode_then_gemm": round(t_two / t_mv, 3),
@@ -415,10 +431,10 @@ def qkv_batch(timeit, sp):
         n1 = L.ep_matvec_workspace_bytes(hs[0], T)
         nb = L.ep_matvec_batch_workspace_bytes(hs, T)
         ws = torch.empty(max(n1, nb), dtype=torch.uint8, device="cuda")
-        t_sep = timeit(lambda: [L.ep_compressed_matvec(h, x.data_ptr(), T, None, y.data_ptr(), ws.data_ptr(), n1, sp)
-                                for h, y in zip(hs, ys)])
-        t_bat = timeit(lambda: L.ep_compressed_matvec_batch(hs, x.data_ptr(), T, None, [y.data_ptr() for y in ys],
-                                                            ws.data_ptr(), nb, sp))
+        t_sep = min(timeit(lambda: [L.ep_compressed_matvec(h, x.data_ptr(), T, None, y.data_ptr(), ws.data_ptr(), n1, sp)
+                                for h, y in zip(hs, ys)]) for _ in range(3))
+        t_bat = min(timeit(lambda: L.ep_compressed_matvec_batch(hs, x.data_ptr(), T, None, [y.data_ptr() for y in ys],
+                                                            ws.data_ptr(), nb, sp)) for _ in range(3))
         out[f"tokens_{T}"] = {"ms_three_calls": round(t_sep, 4), "ms_batched": round(t_bat, 4),
                               "speedup": round(t_sep / t_bat, 3)}
     return out
@@ -467,7 +483,11 @@ def linear_sequence(c0, wbits0, x, T, target_bpp, timeit, n_layers=8):
         L.ep_compressed_linear_seq_forward(hs, [x.data_ptr()] * n_layers, T, None, [y.data_ptr() for y in ys],
                                            ws.data_ptr(), need, sp, int(side.cuda_stream))
 
+    # best of three rounds measured in turn (clocks drift over a run)
     t_plain, t_serial, t_over = timeit(plain), timeit(serial), timeit(overlapped)
+    for _ in range(2):
+        t_plain, t_serial, t_over = min(t_plain, timeit(plain)), min(t_serial, timeit(serial)), \
+            min(t_over, timeit(overlapped))
     del ys, ws, ws1, wts
     return {"layers": n_layers, "ms_plain_bf16_gemms": round(t_plain, 4), "ms_serial": round(t_serial, 4),
             "ms_overlapped": round(t_over, 4),
@@ -555,9 +575,12 @@ def fp8_linear(reps=10):
     def gemm():
         L.ep_gemm_fp8_nt(xt.data_ptr(), wd.data_ptr(), a_x, awt.data_ptr(), y.data_ptr(), T, R, C, sp)
 
-    t_dec = timeit(lambda: L.ep_decompress(c.handle, wd.data_ptr(), sp))
-    t_gemm = timeit(gemm)
-    t_both = timeit(lambda: (L.ep_decompress(c.handle, wd.data_ptr(), sp), gemm()))
+    for _ in range(40):   # settle the clocks under MFMA load
+        gemm()
+    torch.cuda.synchronize()
+    fns = [lambda: L.ep_decompress(c.handle, wd.data_ptr(), sp), gemm,
+           lambda: (L.ep_decompress(c.handle, wd.data_ptr(), sp), gemm())]
+    t_dec, t_gemm, t_both = [min(timeit(f) for _ in range(3)) for f in fns]
     flops = 2.0 * T * R * C
     return {"workload": "FP8@5: 14336x4096 E4M3FN weight codes @5.0 bpp, FP8 GEMM with 4096 FP8 tokens",
             "actual_bpp": round(c.actual_bpp, 4), "ms_decode": round(t_dec, 4), "ms_fp8_gemm": round(t_gemm, 4),

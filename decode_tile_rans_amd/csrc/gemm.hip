@@ -70,7 +70,7 @@ __device__ __forceinline__ int swz(int r, int c) {
 template <int BN, int NST, int RB, bool FP8>
 __global__ void __launch_bounds__(64 * gemm_waves(BN), 1) gemm_tile_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
                                                            const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
-                                                           int64_t T, int64_t N, int64_t K, int ntm, int ntn, float ax,
+                                                           int64_t T, int64_t N, int64_t K, int ntm, int ntn, int GM, float ax,
                                                            const float* __restrict__ aw) {
   constexpr int NW = gemm_waves(BN);
   constexpr int CPR = RB / 16, RPL = 64 / CPR;                // chunks per row, rows per load
@@ -91,7 +91,6 @@ __global__ void __launch_bounds__(64 * gemm_waves(BN), 1) gemm_tile_kernel(const
   const int ntiles = ntm * ntn;
   int t = (int)blockIdx.x;
   if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
-  constexpr int GM = 4;
   const int gsz = GM * ntn, g = t / gsz, rem = t % gsz;
   const int gm = ntm - g * GM < GM ? ntm - g * GM : GM;
   const int64_t m0 = (int64_t)(g * GM + rem % gm) * GBM, n0 = (int64_t)(rem / gm) * BN;
@@ -287,8 +286,9 @@ int launch_tile(const void* x, const void* w, const void* bias, void* y, int64_t
   static std::once_flag once;
   std::call_once(once, [&] { (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); });
   const int ntm = (int)((T + GBM - 1) / GBM), ntn = (int)((N + BN - 1) / BN);
+  const int gm = 4;   // tile groups of 4 M-tiles (measured: 2, 8 or all M-tiles are no faster)
   hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(64 * gemm_waves(BN)), lds, st, (const uint8_t*)x,
-                     (const uint8_t*)w, (const uint16_t*)bias, (uint16_t*)y, T, N, K, ntm, ntn, ax, aw);
+                     (const uint8_t*)w, (const uint16_t*)bias, (uint16_t*)y, T, N, K, ntm, ntn, gm, ax, aw);
   return hip_check(hipGetLastError(), "gemm launch");
 }
 
