@@ -6,8 +6,9 @@
 // estimates, a conditional model, tile-wise rANS.
 //
 // Steps (device unless noted):
-//   row statistics   one thread per row: RMS summed left to right in float64, BF16 row
-//                    scale, the row's largest |w|, non-finite / too-small rows
+//   row statistics   per row (one lane per row, rows staged through LDS in 32-column
+//                    slices): RMS summed left to right in float64, BF16 row scale, the
+//                    row's largest |w|, non-finite / too-small rows
 //   search (host)    the host encoder's resolution search; each probe quantises the
 //                    sample rows on the device (E8 per group of 8, counts of large
 //                    magnitudes for k), then counts symbols per context; the host builds
@@ -150,6 +151,109 @@ __global__ void row_error_kernel(const void* src, int dtype, int64_t R, int64_t 
   sw[r] = q;
   if (out) atomicOr(sat, 1u);
 }
+
+// ---------------------------------------------------------------- tiled row passes
+// The same per-row sums with one wave per 64 rows: the wave stages 32-column slices of
+// its rows (and of the lattice coordinates) in LDS with coalesced 16-byte loads, then
+// every lane walks its own row's slice left to right, so each row's float64 sums keep
+// the one-thread-per-row order exactly.  Needs rows of a multiple of 16 bytes and a
+// 16-byte aligned source.
+constexpr int kTileRowBytes = 144;   // 128-byte slice + 16 bytes against bank conflicts
+
+template <int DT>
+__device__ __forceinline__ double tile_value(const uint8_t* row, int k) {
+  return cm::widen_one(row, DT, k);
+}
+
+// stage rows r0 .. r0 + 63, columns c0 .. c0 + 31 of a row-major array with `rowb`
+// bytes per row (element size esz) into ts (row rr at rr * kTileRowBytes); pieces past
+// the rows' end or past R read as zero
+__device__ __forceinline__ void stage_slice(const uint8_t* base, int64_t R, int64_t rowb, int esz, int64_t r0,
+                                            int64_t c0, uint8_t* ts, int lane) {
+  const int spr = 2 * esz;   // 16-byte pieces per row of a 32-column slice
+  for (int p = lane; p < 64 * spr; p += 64) {
+    const int rr = p / spr, pp = p % spr;
+    const int64_t gr = r0 + rr;
+    const int64_t cb = c0 * esz + pp * 16;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (gr < R && cb < rowb) v = *(const uint4*)(base + gr * rowb + cb);
+    *(uint4*)(ts + rr * kTileRowBytes + pp * 16) = v;
+  }
+}
+
+template <int DT>
+__global__ void __launch_bounds__(64) row_stats_tiled_kernel(const void* src, int64_t R, int64_t C, uint16_t* s_bits,
+                                                             float* s, double* amax, uint32_t* flags) {
+  __shared__ __align__(16) uint8_t ts[64 * kTileRowBytes];
+  constexpr int esz = DT == EP_FP32 ? 4 : (DT == EP_FP8_E4M3FN || DT == EP_INT8 ? 1 : 2);
+  const int lane = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 64, r = r0 + lane;
+  double acc = 0.0, am = 0.0;
+  bool live = false, bad = false;
+  for (int64_t c0 = 0; c0 < C; c0 += 32) {
+    stage_slice((const uint8_t*)src, R, C * esz, esz, r0, c0, ts, lane);
+    __syncthreads();
+    const int n = C - c0 < 32 ? (int)(C - c0) : 32;
+    const uint8_t* row = ts + lane * kTileRowBytes;
+    for (int k = 0; k < n; ++k) {
+      const double v = tile_value<DT>(row, k);
+      if (!isfinite(v)) bad = true;
+      acc = acc + v * v;
+      const double a = fabs(v);
+      if (a > am) am = a;
+      live |= v != 0.0;
+    }
+    __syncthreads();
+  }
+  if (r >= R) return;
+  const double rms = sqrt(acc / (double)C);
+  const uint16_t sb = dev_f32_to_bf16_rne((float)rms);
+  s_bits[r] = sb;
+  s[r] = __uint_as_float((uint32_t)sb << 16);
+  amax[r] = am;
+  if (bad) atomicOr(flags, 1u);
+  if (live && ((sb >> 7) & 0xFF) == 0) atomicOr(flags, 2u);
+}
+
+template <int DT>
+__global__ void __launch_bounds__(64) row_error_tiled_kernel(const void* src, int64_t R, int64_t C, int64_t G,
+                                                             const float* s, float delta, const int32_t* u,
+                                                             double cmax, double* se, double* sw, uint32_t* sat) {
+  __shared__ __align__(16) uint8_t ts[64 * kTileRowBytes];
+  __shared__ __align__(16) uint8_t tu[64 * kTileRowBytes];
+  constexpr int esz = DT == EP_FP32 ? 4 : (DT == EP_FP8_E4M3FN || DT == EP_INT8 ? 1 : 2);
+  const int lane = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 64, r = r0 + lane;
+  const float h = r < R ? s[r] * delta : 0.f;
+  double e = 0.0, q = 0.0;
+  bool out = false;
+  for (int64_t c0 = 0; c0 < C; c0 += 32) {
+    stage_slice((const uint8_t*)src, R, C * esz, esz, r0, c0, ts, lane);
+    stage_slice((const uint8_t*)u, R, G * 8 * 4, 4, r0, c0, tu, lane);
+    __syncthreads();
+    const int n = C - c0 < 32 ? (int)(C - c0) : 32;
+    const uint8_t* row = ts + lane * kTileRowBytes;
+    const int32_t* urow = (const int32_t*)(tu + lane * kTileRowBytes);
+    for (int k = 0; k < n; ++k) {
+      const double w = tile_value<DT>(row, k);
+      const float v = h * (float)urow[k];
+      const double d = w - (double)v;
+      e += d * d;
+      q += w * w;
+      const double dv = (double)v;
+      if (DT != EP_FP32) {
+        if (DT == EP_INT8) out |= nearbyint(dv) > 127.0 || nearbyint(dv) < -128.0;
+        else out |= fabs(dv) > cmax;
+      }
+    }
+    __syncthreads();
+  }
+  if (r >= R) return;
+  se[r] = e;
+  sw[r] = q;
+  if (out) atomicOr(sat, 1u);
+}
+
 
 // ---------------------------------------------------------------- rANS chains
 // One thread per chain: groups j, j+S, ... of its tile, encoded last to first (the
@@ -363,8 +467,25 @@ int compress_device(const void* dsrc, int dtype, int64_t R, int64_t C, double t,
       (rc = dalloc(d_flags, 16)))
     return rc;
   if ((rc = hc(hipMemsetAsync(d_flags.p, 0, 4, st), "memset"))) return rc;
-  hipLaunchKernelGGL(row_stats_kernel, dim3((unsigned)((R + 127) / 128)), dim3(128), 0, st, dsrc, dtype, R, C,
-                     d_sb.as<uint16_t>(), d_s.as<float>(), d_am.as<double>(), d_flags.as<uint32_t>());
+  const int esz = dtype == EP_FP32 ? 4 : (dtype == EP_FP8_E4M3FN || dtype == EP_INT8 ? 1 : 2);
+  const bool tiled = (C * esz) % 16 == 0 && (reinterpret_cast<uintptr_t>(dsrc) & 15) == 0;
+  const dim3 tgrid((unsigned)((R + 63) / 64)), tblock(64);
+  if (tiled) {
+    auto launch_stats = [&](auto kern) {
+      hipLaunchKernelGGL(kern, tgrid, tblock, 0, st, dsrc, R, C, d_sb.as<uint16_t>(), d_s.as<float>(),
+                         d_am.as<double>(), d_flags.as<uint32_t>());
+    };
+    switch (dtype) {
+      case EP_BF16: launch_stats(row_stats_tiled_kernel<EP_BF16>); break;
+      case EP_FP16: launch_stats(row_stats_tiled_kernel<EP_FP16>); break;
+      case EP_FP32: launch_stats(row_stats_tiled_kernel<EP_FP32>); break;
+      case EP_FP8_E4M3FN: launch_stats(row_stats_tiled_kernel<EP_FP8_E4M3FN>); break;
+      default: launch_stats(row_stats_tiled_kernel<EP_INT8>); break;
+    }
+  } else {
+    hipLaunchKernelGGL(row_stats_kernel, dim3((unsigned)((R + 127) / 128)), dim3(128), 0, st, dsrc, dtype, R, C,
+                       d_sb.as<uint16_t>(), d_s.as<float>(), d_am.as<double>(), d_flags.as<uint32_t>());
+  }
   std::vector<uint16_t> s_bits((size_t)R);
   std::vector<float> s((size_t)R);
   std::vector<double> amax((size_t)R);
@@ -488,9 +609,23 @@ int compress_device(const void* dsrc, int dtype, int64_t R, int64_t C, double t,
   if ((rc = hc(hipMemsetAsync(d_flags.p, 0, 4, st), "memset"))) return rc;
   const double cmax = dtype == EP_BF16 ? (double)__builtin_bit_cast(float, 0x7F7F0000u)
                                        : (dtype == EP_FP16 ? 65504.0 : (dtype == EP_FP8_E4M3FN ? 448.0 : 127.0));
-  hipLaunchKernelGGL(row_error_kernel, dim3((unsigned)((R + 127) / 128)), dim3(128), 0, st, dsrc, dtype, R, C, G,
-                     d_s.as<float>(), delta, d_u.as<int32_t>(), cmax, d_se.as<double>(), d_sw.as<double>(),
-                     d_flags.as<uint32_t>());
+  if (tiled) {
+    auto launch_err = [&](auto kern) {
+      hipLaunchKernelGGL(kern, tgrid, tblock, 0, st, dsrc, R, C, G, d_s.as<float>(), delta, d_u.as<int32_t>(), cmax,
+                         d_se.as<double>(), d_sw.as<double>(), d_flags.as<uint32_t>());
+    };
+    switch (dtype) {
+      case EP_BF16: launch_err(row_error_tiled_kernel<EP_BF16>); break;
+      case EP_FP16: launch_err(row_error_tiled_kernel<EP_FP16>); break;
+      case EP_FP32: launch_err(row_error_tiled_kernel<EP_FP32>); break;
+      case EP_FP8_E4M3FN: launch_err(row_error_tiled_kernel<EP_FP8_E4M3FN>); break;
+      default: launch_err(row_error_tiled_kernel<EP_INT8>); break;
+    }
+  } else {
+    hipLaunchKernelGGL(row_error_kernel, dim3((unsigned)((R + 127) / 128)), dim3(128), 0, st, dsrc, dtype, R, C, G,
+                       d_s.as<float>(), delta, d_u.as<int32_t>(), cmax, d_se.as<double>(), d_sw.as<double>(),
+                       d_flags.as<uint32_t>());
+  }
   std::vector<double> se((size_t)R), sw((size_t)R);
   uint32_t sat = 0;
   if ((rc = hc(hipMemcpyAsync(se.data(), d_se.p, 8 * R, hipMemcpyDeviceToHost, st), "copy")) ||
