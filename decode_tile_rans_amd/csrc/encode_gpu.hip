@@ -103,9 +103,21 @@ __global__ void quantize_kernel(const void* src, int dtype, int64_t C, int64_t G
 }
 
 // Symbol counts per (context, id) and the raw bits, for a chosen k.
-__global__ void histogram_kernel(const int32_t* u, int64_t n_groups, int k, unsigned long long* hist,
-                                 unsigned long long* rawbits) {
+// k < 0: the escape bucket k is picked here from the quantiser's counts ge of
+// magnitudes >= 2^k (the smallest k in 3..7 whose count is at most 2^-20 of the
+// coordinates, else 7) and written to k_out, so the host needs no round trip for it
+__global__ void histogram_kernel(const int32_t* u, int64_t n_groups, int k, const unsigned long long* ge,
+                                 unsigned long long* hist, unsigned long long* rawbits, unsigned long long* k_out) {
   __shared__ uint32_t lh[kHistBins];
+  if (k < 0) {
+    k = 7;
+    for (int kk = 3; kk <= 7; ++kk)
+      if ((int64_t)ge[kk - 3] * (int64_t(1) << 20) <= n_groups * 8) {
+        k = kk;
+        break;
+      }
+    if (blockIdx.x == 0 && threadIdx.x == 0) *k_out = (unsigned long long)k;
+  }
   for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = 0;
   __syncthreads();
   uint32_t rb = 0;
@@ -160,9 +172,31 @@ __global__ void row_error_kernel(const void* src, int dtype, int64_t R, int64_t 
 // 16-byte aligned source.
 constexpr int kTileRowBytes = 144;   // 128-byte slice + 16 bytes against bank conflicts
 
+// element k of a 32-column slice held in registers (w: 2 esz dwords per 16 bytes)
 template <int DT>
-__device__ __forceinline__ double tile_value(const uint8_t* row, int k) {
-  return cm::widen_one(row, DT, k);
+__device__ __forceinline__ double slice_value(const uint32_t* w, int k) {
+  if constexpr (DT == EP_FP32) {
+    return (double)__uint_as_float(w[k]);
+  } else if constexpr (DT == EP_BF16 || DT == EP_FP16) {
+    const uint16_t b = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+    return DT == EP_BF16 ? cm::bf16_value(b) : cm::fp16_value(b);
+  } else {
+    const uint8_t b = (uint8_t)(w[k >> 2] >> (8 * (k & 3)));
+    return DT == EP_FP8_E4M3FN ? cm::fp8_e4m3fn_value(b) : (double)(int8_t)b;
+  }
+}
+
+// the lane's row of a staged slice, into registers (nd dwords)
+template <int ND>
+__device__ __forceinline__ void slice_regs(const uint8_t* ts, int lane, uint32_t* w) {
+#pragma unroll
+  for (int i = 0; i < ND / 4; ++i) {
+    const uint4 v = *(const uint4*)(ts + lane * kTileRowBytes + 16 * i);
+    w[4 * i] = v.x;
+    w[4 * i + 1] = v.y;
+    w[4 * i + 2] = v.z;
+    w[4 * i + 3] = v.w;
+  }
 }
 
 // stage rows r0 .. r0 + 63, columns c0 .. c0 + 31 of a row-major array with `rowb`
@@ -194,9 +228,12 @@ __global__ void __launch_bounds__(64) row_stats_tiled_kernel(const void* src, in
     stage_slice((const uint8_t*)src, R, C * esz, esz, r0, c0, ts, lane);
     __syncthreads();
     const int n = C - c0 < 32 ? (int)(C - c0) : 32;
-    const uint8_t* row = ts + lane * kTileRowBytes;
-    for (int k = 0; k < n; ++k) {
-      const double v = tile_value<DT>(row, k);
+    uint32_t wr[8 * esz];
+    slice_regs<8 * esz>(ts, lane, wr);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      if (k >= n) break;
+      const double v = slice_value<DT>(wr, k);
       if (!isfinite(v)) bad = true;
       acc = acc + v * v;
       const double a = fabs(v);
@@ -232,11 +269,14 @@ __global__ void __launch_bounds__(64) row_error_tiled_kernel(const void* src, in
     stage_slice((const uint8_t*)u, R, G * 8 * 4, 4, r0, c0, tu, lane);
     __syncthreads();
     const int n = C - c0 < 32 ? (int)(C - c0) : 32;
-    const uint8_t* row = ts + lane * kTileRowBytes;
-    const int32_t* urow = (const int32_t*)(tu + lane * kTileRowBytes);
-    for (int k = 0; k < n; ++k) {
-      const double w = tile_value<DT>(row, k);
-      const float v = h * (float)urow[k];
+    uint32_t wr[8 * esz], ur[32];
+    slice_regs<8 * esz>(ts, lane, wr);
+    slice_regs<32>(tu, lane, ur);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      if (k >= n) break;
+      const double w = slice_value<DT>(wr, k);
+      const float v = h * (float)(int32_t)ur[k];
       const double d = w - (double)v;
       e += d * d;
       q += w * w;
@@ -416,6 +456,23 @@ int dalloc(DevBuf& b, size_t bytes) {
   return EP_OK;
 }
 
+// pinned host memory (allocated here, never registered after the fact)
+struct HostBuf {
+  void* p = nullptr;
+  ~HostBuf() {
+    if (p) (void)hipHostFree(p);
+  }
+};
+
+int halloc(HostBuf& b, size_t bytes) {
+  if (hipHostMalloc(&b.p, std::max<size_t>(bytes, 16), hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    b.p = nullptr;
+    return fail(EP_E_NOMEM, "pinned host allocation failed");
+  }
+  return EP_OK;
+}
+
 void put16(std::vector<uint8_t>& b, size_t off, uint16_t v) { std::memcpy(&b[off], &v, 2); }
 void put32(std::vector<uint8_t>& b, size_t off, uint32_t v) { std::memcpy(&b[off], &v, 4); }
 void put64(std::vector<uint8_t>& b, size_t off, uint64_t v) { std::memcpy(&b[off], &v, 8); }
@@ -527,6 +584,8 @@ int compress_device(const void* dsrc, int dtype, int64_t R, int64_t C, double t,
   unsigned long long* d_hist = d_ge + 8;
   unsigned long long* d_raw = d_hist + kHistBins;
   std::vector<unsigned long long> hist((size_t)kHistBins + 1);
+  HostBuf cnt_host;   // pinned: the probes' counts come back by DMA
+  if ((rc = halloc(cnt_host, 8 * (size_t)(8 + kHistBins + 1)))) return rc;
   const int32_t* lq = log2q_table();
   int err = EP_OK;
 
@@ -537,22 +596,16 @@ int compress_device(const void* dsrc, int dtype, int64_t R, int64_t C, double t,
     const int64_t ng = nrows * G;
     hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, st, dsrc, dtype, C, G,
                        drows, nrows, d_s.as<float>(), delta, du, d_ge);
-    unsigned long long ge[5];
-    if ((e = hc(hipMemcpyAsync(ge, d_ge, sizeof(ge), hipMemcpyDeviceToHost, st), "copy")) ||
-        (e = hc(hipStreamSynchronize(st), "sync")))
-      return e;
-    int k = 7;
-    for (int kk = 3; kk <= 7; ++kk)
-      if ((int64_t)ge[kk - 3] * (int64_t(1) << 20) <= ng * 8) {
-        k = kk;
-        break;
-      }
+    // the bucket k is picked on the device; one copy back per probe (counts, k, histogram)
     const unsigned nb = (unsigned)std::min<int64_t>(1024, (ng + 255) / 256);
-    hipLaunchKernelGGL(histogram_kernel, dim3(nb), dim3(256), 0, st, du, ng, k, d_hist, d_raw);
-    if ((e = hc(hipMemcpyAsync(hist.data(), d_hist, 8 * hist.size(), hipMemcpyDeviceToHost, st), "copy")) ||
+    hipLaunchKernelGGL(histogram_kernel, dim3(nb), dim3(256), 0, st, du, ng, -1, d_ge, d_hist, d_raw, d_ge + 7);
+    if ((e = hc(hipMemcpyAsync(cnt_host.p, d_cnt.p, 8 * (size_t)(8 + kHistBins + 1), hipMemcpyDeviceToHost, st),
+                "copy")) ||
         (e = hc(hipStreamSynchronize(st), "sync")))
       return e;
-    *k_out = k;
+    const unsigned long long* ch = (const unsigned long long*)cnt_host.p;
+    std::copy(ch + 8, ch + 8 + kHistBins + 1, hist.begin());
+    *k_out = (int)ch[7];
     return EP_OK;
   };
   auto estimate_at = [&](uint32_t bits) -> Estimate {
@@ -591,13 +644,13 @@ int compress_device(const void* dsrc, int dtype, int64_t R, int64_t C, double t,
   if (k_all != k) {
     const unsigned nb = (unsigned)std::min<int64_t>(1024, (n_groups + 255) / 256);
     if ((rc = hc(hipMemsetAsync(d_hist, 0, 8 * (size_t)(kHistBins + 1), st), "memset"))) return rc;
-    hipLaunchKernelGGL(histogram_kernel, dim3(nb), dim3(256), 0, st, d_u.as<int32_t>(), n_groups, k, d_hist, d_raw);
+    hipLaunchKernelGGL(histogram_kernel, dim3(nb), dim3(256), 0, st, d_u.as<int32_t>(), n_groups, k, d_ge, d_hist,
+                       d_raw, d_ge + 7);
     if ((rc = hc(hipMemcpyAsync(hist.data(), d_hist, 8 * hist.size(), hipMemcpyDeviceToHost, st), "copy")) ||
         (rc = hc(hipStreamSynchronize(st), "sync")))
       return rc;
   }
-  unsigned long long ge_all[5];
-  if ((rc = hc(hipMemcpy(ge_all, d_ge, sizeof(ge_all), hipMemcpyDeviceToHost), "copy"))) return rc;
+  const unsigned long long* ge_all = (const unsigned long long*)cnt_host.p;   // the full pass's counts
   const bool any_esc = ge_all[k - 3] > 0;
   int64_t cc[2];
   std::vector<int64_t> mag0, mag1;
