@@ -1214,8 +1214,11 @@ int cu_count() {
 // per lane or 8 of two.  A launch of at least one full round (every CU a workgroup of 16 waves) gives each
 // wave one block: all waves of a workgroup finish together, the 4 SIMDs carry equal
 // work, and a launch queued on another stream fills the CUs the last round leaves idle.
-// A smaller launch spreads its blocks evenly over at most one workgroup per CU (`bpw`
-// each, the fewest that fit), the waves looping over them.  Two chains per lane
+// A smaller launch gives each workgroup at least 8 blocks (more when one workgroup per
+// CU would not hold them all): every block is resident at once either way, so a lone
+// launch takes one block's time, while the tables (56 KB of LDS per workgroup) serve
+// more waves, so launches running side by side on other streams fit more waves on the
+// chip (per-layer decode of the 276-matrix stack on four streams: 8.3 -> 6.0 ms).  Two chains per lane
 // (EP_DECODE_ILP=2) is an option; EP_DECODE_WAVES / EP_DECODE_BPW override the shape.
 Shape pick_shape(const int64_t* n_blocks, int n) {
   const int64_t cus = cu_count();
@@ -1230,7 +1233,7 @@ Shape pick_shape(const int64_t* n_blocks, int n) {
   if (total >= cus * wmax * ilp) {
     bpw = (int64_t)wmax * ilp;
   } else {
-    bpw = std::max<int64_t>(1, (total + cus - 1) / cus);
+    bpw = std::max<int64_t>(std::min<int64_t>(8, (int64_t)wmax * ilp), (total + cus - 1) / cus);
     for (;;) {
       int64_t wg = 0;
       for (int i = 0; i < n; ++i) wg += (n_blocks[i] + bpw - 1) / bpw;
