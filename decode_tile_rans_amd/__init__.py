@@ -11,5 +11,6 @@ in the library (host C++ encoder, gfx950 HIP decode and MFMA GEMM kernels).
     y = layer(x)
 """
 from .api import (Compressed, compress, decompress, decompress_batch, CompressedLinear,  # noqa: F401
-                  gemm_bf16_nt, gemm_fp8_nt, plan_bitrates, compress_lossless, linear_batch, EPError)
+                  gemm_bf16_nt, gemm_fp8_nt, plan_bitrates, compress_lossless, compress_many, linear_batch,
+                  EPError)
 from . import _lib  # noqa: F401

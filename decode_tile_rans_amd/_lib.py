@@ -45,6 +45,8 @@ SIGNATURES = {
     "ep_blob_distortion": (_int, [_vp, C.POINTER(_dbl), C.POINTER(_dbl)]),
     "ep_actual_bpp": (_dbl, [_vp]),
     "ep_compress_device": (_int, [_vp, _int, _i64, _i64, _dbl, _int, _vp, C.POINTER(_vp)]),
+    "ep_compress_device_batch": (_int, [C.POINTER(_vp), C.POINTER(_i64), C.POINTER(_i64), _int, _int, _dbl, _int,
+                                        _vp, C.POINTER(_vp)]),
     "ep_compress_lossless": (_int, [_vp, _i64, _int, C.POINTER(_i64), _int, _int, _int, C.POINTER(_vp)]),
     "ep_blob_kind": (_int, [_vp]),
     "ep_blob_dims": (_int, [_vp, C.POINTER(_i64), _int]),
@@ -202,6 +204,17 @@ def ep_compress_device(dev_ptr: int, dtype: int, rows: int, cols: int, target_bp
     check(lib().ep_compress_device(dev_ptr, dtype, rows, cols, float(target_bpp), chains_per_tile, stream,
                                    C.byref(out)))
     return out.value
+
+
+def ep_compress_device_batch(dev_ptrs, shapes, dtype: int, target_bpp: float, chains_per_tile: int = 0,
+                             stream: int = 0):
+    n = len(dev_ptrs)
+    src = (_vp * n)(*dev_ptrs)
+    rows = (_i64 * n)(*[int(r) for r, _ in shapes])
+    cols = (_i64 * n)(*[int(c) for _, c in shapes])
+    out = (_vp * n)()
+    check(lib().ep_compress_device_batch(src, rows, cols, n, dtype, float(target_bpp), chains_per_tile, stream, out))
+    return [out[i] for i in range(n)]
 
 
 def ep_compress_lossless(src_ptr: int, n_bytes: int, elem_bytes: int, dims, dtype_tag: int = 0,

@@ -118,6 +118,20 @@ def compress(x, target_bpp: float, dtype=None, chains_per_tile: int = 0, stream=
     return Compressed(h)
 
 
+def compress_many(tensors, target_bpp: float, chains_per_tile: int = 0, stream=None):
+    """compress() over several 2-D tensors at one target; CUDA tensors of one dtype go
+    through the GPU encoder's batch entry (several matrices in flight at once)."""
+    tensors = list(tensors)
+    if tensors and all(isinstance(t, torch.Tensor) and t.is_cuda and t.dim() == 2 for t in tensors) and \
+            len({t.dtype for t in tensors}) == 1 and tensors[0].dtype in _TORCH_TO_EP:
+        xs = [t.detach().contiguous() for t in tensors]
+        hs = L.ep_compress_device_batch([x.data_ptr() for x in xs], [tuple(x.shape) for x in xs],
+                                        _TORCH_TO_EP[xs[0].dtype], float(target_bpp), chains_per_tile,
+                                        _stream_ptr(stream))
+        return [Compressed(h) for h in hs]
+    return [compress(t, target_bpp, chains_per_tile=chains_per_tile, stream=stream) for t in tensors]
+
+
 def compress_lossless(x: torch.Tensor, chains_per_tile: int = 0) -> Compressed:
     """TileANS: a bit-exact compressed copy of a tensor of any shape and of the dtypes in
     ``_LOSSLESS_DTYPES`` ([README] Config：压缩配置 TileANSConfig)."""

@@ -22,7 +22,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <string>
+#include <thread>
 #include <vector>
 
 #include "codec_math.h"
@@ -436,10 +439,20 @@ __global__ void layout_kernel(const uint16_t* words, int max_words, const uint32
 }
 
 // ---------------------------------------------------------------- host side
+// Device buffers of one encode.  A batch worker turns on a per-thread cache, so the
+// buffers of one matrix are reused by the next instead of freed (a free waits for the
+// whole device and would serialise the workers); a matrix's work on its stream is done
+// before its buffers go back (the encode ends with a stream synchronisation).
+thread_local bool t_cache_on = false;
+thread_local std::vector<std::pair<void*, size_t>> t_cache;   // free blocks and their sizes
+
 struct DevBuf {
   void* p = nullptr;
+  size_t cap = 0;
   ~DevBuf() {
-    if (p) (void)hipFree(p);
+    if (!p) return;
+    if (t_cache_on) t_cache.emplace_back(p, cap);
+    else (void)hipFree(p);
   }
   template <class T>
   T* as() const {
@@ -448,12 +461,31 @@ struct DevBuf {
 };
 
 int dalloc(DevBuf& b, size_t bytes) {
-  if (hipMalloc(&b.p, std::max<size_t>(bytes, 16)) != hipSuccess) {
+  bytes = std::max<size_t>(bytes, 16);
+  if (t_cache_on) {   // the smallest cached block that fits
+    size_t best = t_cache.size();
+    for (size_t i = 0; i < t_cache.size(); ++i)
+      if (t_cache[i].second >= bytes && (best == t_cache.size() || t_cache[i].second < t_cache[best].second)) best = i;
+    if (best < t_cache.size()) {
+      b.p = t_cache[best].first;
+      b.cap = t_cache[best].second;
+      t_cache.erase(t_cache.begin() + (ptrdiff_t)best);
+      return EP_OK;
+    }
+  }
+  if (hipMalloc(&b.p, bytes) != hipSuccess) {
     (void)hipGetLastError();
     b.p = nullptr;
     return fail(EP_E_NOMEM, "device allocation failed");
   }
+  b.cap = bytes;
   return EP_OK;
+}
+
+void cache_release() {
+  for (auto& e : t_cache) (void)hipFree(e.first);
+  t_cache.clear();
+  t_cache_on = false;
 }
 
 // pinned host memory (allocated here, never registered after the fact)
@@ -846,6 +878,65 @@ int ep_compress_device(const void* dev_src, int dtype, int64_t rows, int64_t col
   }
   blob->b.dist = dist;
   *out = blob;
+  return EP_OK;
+}
+
+// n matrices on up to four host threads, each with a stream of its own (the encoder's
+// host steps and its small per-probe round trips overlap across matrices).  Every blob
+// equals ep_compress_device's for that matrix.
+int ep_compress_device_batch(const void* const* dev_src, const int64_t* rows, const int64_t* cols, int n, int dtype,
+                             double target_bpp, int chains_per_tile, ep_stream stream, ep_blob** out) {
+  set_error("");
+  if (n < 0 || (n > 0 && (!dev_src || !rows || !cols || !out))) return fail(EP_E_ARG, "null pointer or negative count");
+  for (int i = 0; i < n; ++i) out[i] = nullptr;
+  if (n == 0) return EP_OK;
+  int dev = 0;
+  int rc = hip_check((int)hipGetDevice(&dev), "get device");
+  if (rc) return rc;
+  // the inputs are ready once the work already queued on `stream` is done
+  if ((rc = hip_check((int)hipStreamSynchronize((hipStream_t)stream), "stream sync"))) return rc;
+  const int nw = std::min(n, 4);
+  std::vector<int> codes(n, EP_OK);
+  std::vector<std::string> msgs(n);
+  std::atomic<int> next{0};
+  auto work = [&]() {
+    if (hipSetDevice(dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return;
+    }
+    hipStream_t st = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) {
+      (void)hipGetLastError();
+      st = nullptr;
+    }
+    t_cache_on = true;
+    for (int i = next++; i < n; i = next++) {
+      if (!st) {
+        codes[i] = EP_E_DEVICE;
+        msgs[i] = "stream creation failed";
+        continue;
+      }
+      codes[i] = ep_compress_device(dev_src[i], dtype, rows[i], cols[i], target_bpp, chains_per_tile, (ep_stream)st,
+                                    &out[i]);
+      if (codes[i]) msgs[i] = ep_last_error();
+    }
+    cache_release();
+    if (st) (void)hipStreamDestroy(st);
+  };
+  std::vector<std::thread> pool;
+  for (int w = 1; w < nw; ++w) pool.emplace_back(work);
+  work();
+  for (auto& t : pool) t.join();
+  for (int i = 0; i < n; ++i)
+    if (codes[i] != EP_OK || !out[i]) {
+      const int code = codes[i] != EP_OK ? codes[i] : EP_E_DEVICE;
+      const std::string msg = "matrix " + std::to_string(i) + ": " + (msgs[i].empty() ? "not compressed" : msgs[i]);
+      for (int k = 0; k < n; ++k) {
+        ep_blob_free(out[k]);
+        out[k] = nullptr;
+      }
+      return fail(code, msg);
+    }
   return EP_OK;
 }
 

@@ -94,6 +94,17 @@ int ep_compress_ex(const void* host_src, int dtype, int64_t rows, int64_t cols,
 int ep_compress_device(const void* dev_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
                        int chains_per_tile, ep_stream stream, ep_blob** out);
 
+/* The GPU encoder over n matrices of one dtype and target (a whole model's layers,
+ * [README] 性能: the 276 layers compressed in seconds): dev_src[i] is rows[i] x cols[i],
+ * out[i] (caller-owned array of n) receives blob i, equal byte for byte to
+ * ep_compress_device's.  Work already queued on `stream` completes first; the matrices
+ * are then encoded by up to four host threads on streams of their own, and the call
+ * returns when all are done.  On an error no blob is returned (every out[i] NULL) and
+ * the message names the first failing matrix. */
+int ep_compress_device_batch(const void* const* dev_src, const int64_t* rows, const int64_t* cols, int n,
+                             int dtype, double target_bpp, int chains_per_tile, ep_stream stream,
+                             ep_blob** out);
+
 /* TileANS lossless compression ([README] Config：压缩配置: a lossless codec for BF16, FP16,
  * FP32, FP8, INT8 and other dtypes whose ratio depends on the data; [NEWS]: tensors
  * that are not 2-D take the lossless way).  host_src: the tensor's n_bytes raw bytes

@@ -124,3 +124,40 @@ def test_host_pointer_source_refused():
     with pytest.raises(L.EPError) as ei:
         L.ep_compress_device(src.ctypes.data, nx.DT_BF16, 16, 64, 4.0, 0, 0)
     assert ei.value.name == "EP_E_ARG"
+
+
+def test_batch_entry_equals_single_calls():
+    """ep_compress_device_batch over matrices of several shapes: every blob equals the
+    single-matrix entry's, byte for byte; a bad matrix fails the call and names it."""
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    say("gpu encoder batch")
+    shapes = [(256, 512), (37, 13), (300, 1000), (1024, 4096), (129, 777), (64, 256), (8, 16)]
+    ws = [torch.from_numpy(synth.rowscaled(r, c, 500 + i)).view(torch.bfloat16).cuda() for i, (r, c) in enumerate(shapes)]
+    sp = stream_ptr()
+    torch.cuda.synchronize()
+    hs = L.ep_compress_device_batch([w.data_ptr() for w in ws], shapes, L.EP_BF16, 3.5, 0, sp)
+    try:
+        for w, h, shp in zip(ws, hs, shapes):
+            one = L.ep_compress_device(w.data_ptr(), L.EP_BF16, shp[0], shp[1], 3.5, 0, sp)
+            try:
+                assert L.ep_serialize(h) == L.ep_serialize(one), f"shape {shp}"
+            finally:
+                L.ep_blob_free(one)
+    finally:
+        for h in hs:
+            L.ep_blob_free(h)
+    bad = torch.full((16, 16), float("nan"), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(L.EPError, match="matrix 1"):
+        L.ep_compress_device_batch([ws[0].data_ptr(), bad.data_ptr()], [shapes[0], (16, 16)], L.EP_BF16, 3.5, 0, sp)
+
+
+def test_python_compress_many():
+    import torch
+    import decode_tile_rans_amd as ep
+    say("compress_many")
+    ws = [torch.from_numpy(synth.rowscaled(r, c, 600 + r)).view(torch.bfloat16).cuda() for r, c in ((64, 256), (96, 512), (40, 48))]
+    many = ep.compress_many(ws, 3.0)
+    for w, c in zip(ws, many):
+        assert c.to_bytes() == ep.compress(w, 3.0).to_bytes()
+        assert c.shape == tuple(w.shape) and c.dtype == torch.bfloat16
