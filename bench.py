@@ -22,7 +22,6 @@ import math
 import os
 import sys
 import time
-from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -165,26 +164,23 @@ def container_sweep(reps=10):
 
 
 def build_stack(n, target_bpp):
-    """Draw the stack on the GPU, compress on the host (all cores), upload blobs."""
+    """Draw the stack on the GPU and compress it there (the GPU encoder's batch entry,
+    whose blobs equal the host encoder's byte for byte), upload the blobs."""
     import torch
     import synth
     import decode_tile_rans_amd as ep
     shapes = synth.dit_stack_shapes()[:n]
-    ncpu = max(1, min(16, os.cpu_count() or 1))
-    os.environ["EP_NUM_THREADS"] = "1"
     t0 = time.time()
-
-    def job(i):
-        w = synth.dit_stack_torch(i).cpu()
-        return ep.compress(w, target_bpp)
-
-    with ThreadPoolExecutor(ncpu) as pool:
-        comps = list(pool.map(job, range(n)))
-    os.environ.pop("EP_NUM_THREADS", None)
+    comps = []
+    for i0 in range(0, n, 32):
+        ws = [synth.dit_stack_torch(i) for i in range(i0, min(n, i0 + 32))]
+        comps += ep.compress_many(ws, target_bpp)
+        del ws
     for c in comps:
         c.upload()
     torch.cuda.synchronize()
-    log(f"compressed {n} matrices in {time.time() - t0:.1f}s on {ncpu} threads")
+    torch.cuda.empty_cache()
+    log(f"compressed {n} matrices in {time.time() - t0:.1f}s on the GPU")
     blocks = {}
     for i, (_, _, _, b) in enumerate(shapes):
         blocks.setdefault(b, []).append(i)
