@@ -364,6 +364,7 @@ def fused_linear(target_bpp, reps=10):
     # second stream while this layer's GEMM runs, against the same GEMMs on plain weights
     seq = linear_sequence(c, wbits, x, T, target_bpp, timeit)
     small = small_batch(c, w, x, ws, need, wd, sp, timeit)
+    sweep = token_sweep(c, w, ws, need, sp, timeit)
     return {
         "workload": "CompressedLinear prefill 14336x4096 weight @%.1f bpp, 4096 tokens" % target_bpp,
         "actual_bpp": round(c.actual_bpp, 4),
@@ -375,7 +376,32 @@ def fused_linear(target_bpp, reps=10):
         "gemm_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 1),
         "sequence_overlapped": seq,
         "small_batch": small,
+        "token_sweep": sweep,
     }
+
+
+def token_sweep(c, w, ws, need, sp, timeit):
+    """The compressed linear (decode, then our GEMM) against our plain GEMM on the same
+    weight for 512 .. 16384 tokens (X N(0,1), seed 51): the decode's share shrinks as the
+    product grows."""
+    import torch
+    import synth
+    from decode_tile_rans_amd import _lib as L
+    R, C = c.shape
+    out = []
+    for T in (512, 1024, 2048, 4096, 8192, 16384):
+        x = torch.from_numpy(synth.activations(T, C, 51)).view(torch.bfloat16).cuda()
+        y = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
+        fused = lambda: L.ep_compressed_linear_forward(c.handle, x.data_ptr(), T, None, y.data_ptr(), ws.data_ptr(),
+                                                       need, sp)
+        plain = lambda: L.ep_gemm_bf16_nt(x.data_ptr(), w.data_ptr(), None, y.data_ptr(), T, R, C, sp)
+        t_f, t_p = timeit(fused), timeit(plain)
+        for _ in range(2):
+            t_f, t_p = min(t_f, timeit(fused)), min(t_p, timeit(plain))
+        out.append({"tokens": T, "ms_decode_plus_gemm": round(t_f, 4), "ms_gemm": round(t_p, 4),
+                    "overhead_pct": round(100.0 * (t_f / t_p - 1.0), 2)})
+        del x, y
+    return out
 
 
 def small_batch(c, w, x, ws, need, wd, sp, timeit):
