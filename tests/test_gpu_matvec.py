@@ -177,8 +177,10 @@ def test_matvec_refusals():
     with pytest.raises(L.EPError):   # activations in pageable host memory
         xh = np.zeros((8, 256), np.uint16)
         L.ep_compressed_matvec(db.h, xh.ctypes.data, 8, 0, y.data_ptr(), ws.data_ptr(), need, stream_ptr())
-    # rows of a width that is not a multiple of 8, FP16 blobs, lossless blobs: not taken
+    # rows of a width that is not a multiple of 8, rows of fewer groups than chains per
+    # tile (16 columns = 2 groups at S = 8), FP16 blobs: not taken
     for b in (oracle.compress(synth.rowscaled(64, 100, 9), nx.DT_BF16, 4.0),
+              oracle.compress(synth.rowscaled(64, 16, 9), nx.DT_BF16, 4.0, chains_per_tile=8),
               oracle.compress((np.random.default_rng(9).standard_normal((64, 256)) * 0.02).astype(np.float16)
                               .view(np.uint16), nx.DT_FP16, 4.0)):
         d = DevBlob(b)
@@ -275,3 +277,23 @@ def test_python_linear_batch_equals_layers():
             want = [m(x) for m in layers]
         for g, w in zip(got, want):
             assert g.shape == w.shape and torch.equal(g.view(torch.int16), w.view(torch.int16))
+
+
+def test_linear_falls_back_when_product_not_taken():
+    """Rows shorter than S groups: the linear entry decodes and runs the GEMM instead."""
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    say("matvec fallback")
+    R, C, T = 200, 16, 3
+    blob = oracle.compress(synth.rowscaled(R, C, 11), nx.DT_BF16, 4.0, chains_per_tile=8)
+    _, w_hat, _ = oracle.decode(blob)
+    db = DevBlob(blob)
+    assert L.ep_matvec_workspace_bytes(db.h, T) == 0
+    x = synth.activations(T, C, 12)
+    xt = _t(x, torch.bfloat16)
+    y = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
+    need = L.ep_linear_workspace_bytes(db.h)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    L.ep_compressed_linear_forward(db.h, xt.data_ptr(), T, 0, y.data_ptr(), ws.data_ptr(), need, stream_ptr())
+    torch.cuda.synchronize()
+    _check(_bits(y), x, w_hat, None)
