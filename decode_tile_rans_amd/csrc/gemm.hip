@@ -70,7 +70,7 @@ __device__ __forceinline__ int swz(int r, int c) {
 template <int BN, int NST, int RB, bool FP8>
 __global__ void __launch_bounds__(64 * gemm_waves(BN), 1) gemm_tile_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
                                                            const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
-                                                           int64_t T, int64_t N, int64_t K, int ntm, int ntn, int GM, float ax,
+                                                           int64_t T, int64_t N, int64_t ldy, int64_t K, int ntm, int ntn, int GM, float ax,
                                                            const float* __restrict__ aw) {
   constexpr int NW = gemm_waves(BN);
   constexpr int CPR = RB / 16, RPL = 64 / CPR;                // chunks per row, rows per load
@@ -245,7 +245,7 @@ __global__ void __launch_bounds__(64 * gemm_waves(BN), 1) gemm_tile_kernel(const
 
   // epilogue: lane holds row m = m0 + wm 128 + 32 i + lr and columns
   // n = n0 + wn WN + 32 j + 8 (r / 4) + 4 lh + r % 4
-  const bool vec = (N % 4) == 0;
+  const bool vec = (N % 4) == 0 && (ldy % 4) == 0;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int64_t m = m0 + wm * 128 + 32 * i + lr;
@@ -262,7 +262,7 @@ __global__ void __launch_bounds__(64 * gemm_waves(BN), 1) gemm_tile_kernel(const
           if (FP8) v[e] *= n + e < N ? ax * aw[n + e] : 0.f;
           else if (bias && n + e < N) v[e] += bf16_to_float(bias[n + e]);
         }
-        uint16_t* yp = Y + m * N + n;
+        uint16_t* yp = Y + m * ldy + n;
         if (vec && n + 3 < N) {
           typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
           u32x2 pk;
@@ -279,8 +279,8 @@ __global__ void __launch_bounds__(64 * gemm_waves(BN), 1) gemm_tile_kernel(const
 }
 
 template <int BN, int NST, int RB, bool FP8>
-int launch_tile(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K, float ax,
-                const float* aw, hipStream_t st) {
+int launch_tile(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t ldy, int64_t K,
+                float ax, const float* aw, hipStream_t st) {
   constexpr int lds = NST * (GBM + BN) * RB;
   auto kern = gemm_tile_kernel<BN, NST, RB, FP8>;
   static std::once_flag once;
@@ -288,12 +288,23 @@ int launch_tile(const void* x, const void* w, const void* bias, void* y, int64_t
   const int ntm = (int)((T + GBM - 1) / GBM), ntn = (int)((N + BN - 1) / BN);
   const int gm = 4;   // tile groups of 4 M-tiles (measured: 2, 8 or all M-tiles are no faster)
   hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(64 * gemm_waves(BN)), lds, st, (const uint8_t*)x,
-                     (const uint8_t*)w, (const uint16_t*)bias, (uint16_t*)y, T, N, K, ntm, ntn, gm, ax, aw);
+                     (const uint8_t*)w, (const uint16_t*)bias, (uint16_t*)y, T, N, ldy, K, ntm, ntn, gm, ax, aw);
   return hip_check(hipGetLastError(), "gemm launch");
 }
 
 // BN = 256 unless 128-wide tiles fill the CUs' rounds much better (a 256 x 256 tile does
 // about 1.25x the work per cycle of a 256 x 128 one).
+int gemm_cu_count() {
+  static int v = -1;
+  if (v < 0) {
+    int dev = 0, x = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&x, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || x <= 0) x = 256;
+    v = x;
+  }
+  return v;
+}
+
 template <bool FP8>
 int launch_gemm(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K, float ax,
                 const float* aw, hipStream_t st) {
@@ -311,8 +322,26 @@ int launch_gemm(const void* x, const void* w, const void* bias, void* y, int64_t
   };
   bool narrow = eff(128) > 1.25 * eff(256);
   if (const char* e = std::getenv("EP_GEMM_BN")) narrow = std::atoi(e) == 128;
-  if (narrow) return launch_tile<128, 3, 128, FP8>(x, w, bias, y, T, N, K, ax, aw, st);
-  return launch_tile<256, 2, 128, FP8>(x, w, bias, y, T, N, K, ax, aw, st);
+  if (narrow) return launch_tile<128, 3, 128, FP8>(x, w, bias, y, T, N, N, K, ax, aw, st);
+  // When the 256-wide tiles leave the last round of the CUs partly idle, the columns of
+  // the whole rounds take 256-wide tiles and the rest 128-wide ones (a second launch of
+  // about one round at roughly 0.6 of a 256-wide tile's time), e.g. 4096 x 14336: 768 +
+  // 256 tiles in 3.6 round-times instead of 896 in 4.
+  const int64_t cus = gemm_cu_count();
+  const int64_t tiles = ntm * ((N + 255) / 256);
+  const int64_t n1 = (tiles / cus) * cus / ntm;   // 256-wide column tiles of the whole rounds
+  if (tiles % cus != 0 && n1 >= 1 && n1 * 256 < N) {
+    const int64_t rem = N - n1 * 256, tiles2 = ntm * ((rem + 127) / 128);
+    const double split = (double)((ntm * n1 + cus - 1) / cus) + 0.625 * (double)((tiles2 + cus - 1) / cus);
+    if (split < (double)((tiles + cus - 1) / cus) - 0.2) {
+      const int64_t c0 = n1 * 256, kb = FP8 ? K : 2 * K;
+      int rc = launch_tile<256, 2, 128, FP8>(x, w, bias, y, T, c0, N, K, ax, aw, st);
+      if (rc) return rc;
+      return launch_tile<128, 3, 128, FP8>(x, (const uint8_t*)w + c0 * kb, bias ? (const uint16_t*)bias + c0 : nullptr,
+                                           (uint16_t*)y + c0, T, rem, N, K, ax, aw ? aw + c0 : nullptr, st);
+    }
+  }
+  return launch_tile<256, 2, 128, FP8>(x, w, bias, y, T, N, N, K, ax, aw, st);
 }
 
 int launch_bf16(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K,

@@ -20,8 +20,10 @@ def _t(a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a)).view(dtype).cuda()
 
 
+# (2048, 9000, 256): 288 tiles of 256 x 256, more than one round of the CUs, so the
+# columns of the whole round take 256-wide tiles and the ragged rest 128-wide ones
 @pytest.mark.parametrize("T,N,K", [(128, 128, 64), (256, 384, 512), (100, 200, 72), (1, 1, 8), (300, 129, 1032),
-                                   (1024, 1024, 4096)])
+                                   (1024, 1024, 4096), (2048, 9000, 256)])
 def test_gemm_bf16(T, N, K):
     import torch
     from decode_tile_rans_amd import _lib as L
@@ -38,7 +40,7 @@ def test_gemm_bf16(T, N, K):
     assert rel_l2(got, ref) <= TOL
 
 
-@pytest.mark.parametrize("T,N,K", [(128, 128, 128), (256, 384, 512), (100, 200, 144), (512, 1024, 2048)])
+@pytest.mark.parametrize("T,N,K", [(128, 128, 128), (256, 384, 512), (100, 200, 144), (512, 1024, 2048), (2048, 9000, 256)])
 def test_gemm_fp8(T, N, K):
     import torch
     from decode_tile_rans_amd import _lib as L
