@@ -502,9 +502,19 @@ __device__ __forceinline__ void ch_renorm_lin_if(Chain& r, bool need) {
     r.nw = lds_u16(r.ra);
   }
 }
+// the same without a branch: selects, and the next word read every symbol (the same
+// word again when the state did not renormalise).  Shorter per-symbol latency (no
+// exec-mask switch) for more ring reads: faster for launches of few waves per CU,
+// slower when LDS is busy.
+__device__ __forceinline__ void ch_renorm_lin_sel(Chain& r, bool need) {
+  const uint32_t xs = (r.x << 16) | r.nw;
+  r.x = need ? xs : r.x;
+  r.ra += need ? 2u : 0u;
+  r.nw = lds_u16(r.ra);
+}
 // Renormalise ILP chains: all conditions first, so that no chain's state update is
 // sunk below another chain's (conditional) ring read.
-template <int ILP>
+template <int ILP, bool SEL>
 __device__ __forceinline__ void ch_renorm_all(Chain* rd) {
   bool need[ILP];
 #pragma unroll
@@ -514,7 +524,10 @@ __device__ __forceinline__ void ch_renorm_all(Chain* rd) {
     need[c] = rd[c].x < kL;
   }
 #pragma unroll
-  for (int c = 0; c < ILP; ++c) ch_renorm_lin_if(rd[c], need[c]);
+  for (int c = 0; c < ILP; ++c) {
+    if constexpr (SEL) ch_renorm_lin_sel(rd[c], need[c]);
+    else ch_renorm_lin_if(rd[c], need[c]);
+  }
 }
 // table entry of the chain's next symbol; `base` = byte offset of the table in LDS
 __device__ __forceinline__ uint32_t ch_entry(uint32_t base, const Chain& r) {
@@ -699,7 +712,7 @@ __device__ __forceinline__ void row_scale(const GroupCtx& X, int kk, RowScale* r
 
 // Decode group kk of ILP chains: fast path over eight symbols (escapes replayed on the
 // careful path), container store.
-template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
+template <int OUT, bool ESC, bool C8, bool NARROW, int ILP, bool SEL>
 __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* rd, RowScale* rs, const int* ngr,
                                              const uint32_t* g0, char** optr, MvAcc* mv) {
   using LY = EntryLayout<NARROW>;
@@ -740,7 +753,7 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
       for (int c = 0; c < ILP; ++c) e[c][i] = (int32_t)ch_entry(tb, rd[c]);
 #pragma unroll
       for (int c = 0; c < ILP; ++c) ch_decode(rd[c], (uint32_t)e[c][i]);
-      ch_renorm_all<ILP>(rd);
+      ch_renorm_all<ILP, SEL>(rd);
     }
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
@@ -780,14 +793,14 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
     ch_decode(rd[c], e[c][0]);
     fbs[c] = X.lds0 + free_base(e[c][0]);
   }
-  ch_renorm_all<ILP>(rd);
+  ch_renorm_all<ILP, SEL>(rd);
 #pragma unroll
   for (int i = 1; i < 7; ++i) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c) e[c][i] = ch_entry(fbs[c], rd[c]);
 #pragma unroll
     for (int c = 0; c < ILP; ++c) ch_decode(rd[c], e[c][i]);
-    ch_renorm_all<ILP>(rd);
+    ch_renorm_all<ILP, SEL>(rd);
   }
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
@@ -798,7 +811,7 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
   }
 #pragma unroll
   for (int c = 0; c < ILP; ++c) ch_decode(rd[c], e[c][7]);
-  ch_renorm_all<ILP>(rd);
+  ch_renorm_all<ILP, SEL>(rd);
 
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
@@ -889,7 +902,7 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
 // One wave decodes ILP blocks of 64 chains (blocks blk0 .. blk0 + ILP - 1, those below
 // blk_end): lane l runs chain l of each, the ILP chains interleaved step by step so
 // that one chain's table read is in flight while another computes.
-template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
+template <int OUT, bool ESC, bool C8, bool NARROW, int ILP, bool SEL>
 __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, int64_t blk_end, int lane, int wave,
                                               TabStager& st, bool stage) {
   const DecJob& J = *X.J;
@@ -1014,10 +1027,10 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
       ch_service(X.sref, rd[c], (ILP == 1) || kk < ngr[c]);
       ch_linear(rd[c]);
     }
-    decode_group<OUT, ESC, C8, NARROW, ILP>(X, kk, rd, rs, ngr, g0, optr, mv);
+    decode_group<OUT, ESC, C8, NARROW, ILP, SEL>(X, kk, rd, rs, ngr, g0, optr, mv);
     if (kk + 1 < nmax) {
       if constexpr (OUT != OUT_BYTES) row_scale<ILP>(X, kk + 1, rs, ngr);
-      decode_group<OUT, ESC, C8, NARROW, ILP>(X, kk + 1, rd, rs, ngr, g0, optr, mv);
+      decode_group<OUT, ESC, C8, NARROW, ILP, SEL>(X, kk + 1, rd, rs, ngr, g0, optr, mv);
     }
 #pragma unroll
     for (int c = 0; c < ILP; ++c) ch_settle(rd[c]);
@@ -1035,7 +1048,7 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
 // A workgroup stages the decode tables of its job into LDS once, then its waves take
 // the workgroup's blocks in turn (wave w: blocks w ILP, (w + W) ILP, ...).  Each job
 // gives every workgroup `bpw` consecutive blocks (the last one fewer).
-template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
+template <int OUT, bool ESC, bool C8, bool NARROW, int ILP, bool SEL>
 __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   extern __shared__ __align__(16) uint32_t smem[];
   const int tid = threadIdx.x;
@@ -1077,7 +1090,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
     return;
   }
   for (bool first = true; b < wg_blk1; b += (int64_t)nwaves * ILP, first = false)
-    decode_blocks<OUT, ESC, C8, NARROW, ILP>(X, b, wg_blk1, lane, wave, st, first);
+    decode_blocks<OUT, ESC, C8, NARROW, ILP, SEL>(X, b, wg_blk1, lane, wave, st, first);
 }
 
 // ---------------------------------------------------------------- launch helpers
@@ -1099,11 +1112,12 @@ struct Shape {
   int ilp;
   int waves;
   int64_t bpw;
+  bool partial;   // less than one full round: every block resident at once
 };
 
-template <int OUT, bool ESC, bool C8, bool NARROW, int ILP>
+template <int OUT, bool ESC, bool C8, bool NARROW, int ILP, bool SEL>
 int launch_t(const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
-  auto kern = decode_kernel<OUT, ESC, C8, NARROW, ILP>;
+  auto kern = decode_kernel<OUT, ESC, C8, NARROW, ILP, SEL>;
   size_t lds = (size_t)kTabBytes + (size_t)waves * 64 * ILP * kChainRingBytes;
   static std::once_flag once;
   std::call_once(once, [&] {
@@ -1113,47 +1127,51 @@ int launch_t(const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
   return hip_check(hipGetLastError(), "decode launch");
 }
 
-template <bool ESC, bool C8, bool NARROW, int ILP>
+template <bool ESC, bool C8, bool NARROW, int ILP, bool SEL>
 int launch_out(int out, const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
   switch (out) {
-    case OUT_BF16: return launch_t<OUT_BF16, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
-    case OUT_BF16_SAT: return launch_t<OUT_BF16_SAT, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
-    case OUT_FP16: return launch_t<OUT_FP16, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
-    case OUT_FP32: return launch_t<OUT_FP32, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
-    case OUT_FP8: return launch_t<OUT_FP8, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
-    case OUT_INT8: return launch_t<OUT_INT8, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+    case OUT_BF16: return launch_t<OUT_BF16, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
+    case OUT_BF16_SAT: return launch_t<OUT_BF16_SAT, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
+    case OUT_FP16: return launch_t<OUT_FP16, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
+    case OUT_FP32: return launch_t<OUT_FP32, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
+    case OUT_FP8: return launch_t<OUT_FP8, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
+    case OUT_INT8: return launch_t<OUT_INT8, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
     case OUT_BYTES:
-      if constexpr (!ESC && NARROW) return launch_t<OUT_BYTES, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+      if constexpr (!ESC && NARROW) return launch_t<OUT_BYTES, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
       return fail(EP_E_ARG, "byte output takes the escape-free narrow kernel");
     case OUT_MV1:
     case OUT_MV2:
     case OUT_MV4:
     case OUT_MV8:
       if constexpr (C8 && ILP == 1) {
-        if (out == OUT_MV1) return launch_t<OUT_MV1, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
-        if (out == OUT_MV2) return launch_t<OUT_MV2, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
-        if (out == OUT_MV4) return launch_t<OUT_MV4, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
-        return launch_t<OUT_MV8, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+        if (out == OUT_MV1) return launch_t<OUT_MV1, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
+        if (out == OUT_MV2) return launch_t<OUT_MV2, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
+        if (out == OUT_MV4) return launch_t<OUT_MV4, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
+        return launch_t<OUT_MV8, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
       }
       return fail(EP_E_ARG, "the fused product takes whole groups per row and one chain per lane");
-    default: return launch_t<OUT_COORDS, ESC, C8, NARROW, ILP>(B, n_wg, waves, st);
+    default: return launch_t<OUT_COORDS, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
   }
 }
 
-template <bool NARROW, int ILP>
+template <bool NARROW, int ILP, bool SEL>
 int launch_n(int out, bool esc, bool c8, const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
-  if (c8) return esc ? launch_out<true, true, NARROW, ILP>(out, B, n_wg, waves, st)
-                     : launch_out<false, true, NARROW, ILP>(out, B, n_wg, waves, st);
-  return esc ? launch_out<true, false, NARROW, ILP>(out, B, n_wg, waves, st)
-             : launch_out<false, false, NARROW, ILP>(out, B, n_wg, waves, st);
+  if (c8) return esc ? launch_out<true, true, NARROW, ILP, SEL>(out, B, n_wg, waves, st)
+                     : launch_out<false, true, NARROW, ILP, SEL>(out, B, n_wg, waves, st);
+  return esc ? launch_out<true, false, NARROW, ILP, SEL>(out, B, n_wg, waves, st)
+             : launch_out<false, false, NARROW, ILP, SEL>(out, B, n_wg, waves, st);
 }
 
 int launch_any(int out, bool esc, bool c8, bool narrow, Shape sh, const DecBatch& B, int64_t n_wg, hipStream_t st) {
   if (sh.ilp == 2)
-    return narrow ? launch_n<true, 2>(out, esc, c8, B, n_wg, sh.waves, st)
-                  : launch_n<false, 2>(out, esc, c8, B, n_wg, sh.waves, st);
-  return narrow ? launch_n<true, 1>(out, esc, c8, B, n_wg, sh.waves, st)
-                : launch_n<false, 1>(out, esc, c8, B, n_wg, sh.waves, st);
+    return narrow ? launch_n<true, 2, false>(out, esc, c8, B, n_wg, sh.waves, st)
+                  : launch_n<false, 2, false>(out, esc, c8, B, n_wg, sh.waves, st);
+  // launches of less than a full round: the branch-free renormalisation (latency-bound)
+  if (sh.partial)
+    return narrow ? launch_n<true, 1, true>(out, esc, c8, B, n_wg, sh.waves, st)
+                  : launch_n<false, 1, true>(out, esc, c8, B, n_wg, sh.waves, st);
+  return narrow ? launch_n<true, 1, false>(out, esc, c8, B, n_wg, sh.waves, st)
+                : launch_n<false, 1, false>(out, esc, c8, B, n_wg, sh.waves, st);
 }
 
 int out_kind(const Blob& b) {
@@ -1248,7 +1266,7 @@ Shape pick_shape(const int64_t* n_blocks, int n) {
     const int v = std::atoi(e);
     if (v >= 1 && v <= kMaxWaves) waves = std::min(v, wmax);
   }
-  return Shape{ilp, waves, bpw};
+  return Shape{ilp, waves, bpw, total < cus * wmax * ilp};
 }
 
 }  // namespace
