@@ -1112,7 +1112,7 @@ struct Shape {
   int ilp;
   int waves;
   int64_t bpw;
-  bool partial;   // less than one full round: every block resident at once
+  bool partial;   // less than one full round at <= 8 waves per CU: latency-bound
 };
 
 template <int OUT, bool ESC, bool C8, bool NARROW, int ILP, bool SEL>
@@ -1166,7 +1166,7 @@ int launch_any(int out, bool esc, bool c8, bool narrow, Shape sh, const DecBatch
   if (sh.ilp == 2)
     return narrow ? launch_n<true, 2, false>(out, esc, c8, B, n_wg, sh.waves, st)
                   : launch_n<false, 2, false>(out, esc, c8, B, n_wg, sh.waves, st);
-  // launches of less than a full round: the branch-free renormalisation (latency-bound)
+  // few waves per CU: the branch-free renormalisation (latency-bound)
   if (sh.partial)
     return narrow ? launch_n<true, 1, true>(out, esc, c8, B, n_wg, sh.waves, st)
                   : launch_n<false, 1, true>(out, esc, c8, B, n_wg, sh.waves, st);
@@ -1266,7 +1266,10 @@ Shape pick_shape(const int64_t* n_blocks, int n) {
     const int v = std::atoi(e);
     if (v >= 1 && v <= kMaxWaves) waves = std::min(v, wmax);
   }
-  return Shape{ilp, waves, bpw, total < cus * wmax * ilp};
+  // (the branch-free variant only where a CU holds at most 8 of these waves: with more,
+  // its extra ring reads cost more than the branch, e.g. 2700 blocks at 11 waves per CU
+  // took 83 us against 77)
+  return Shape{ilp, waves, bpw, total < cus * wmax * ilp && waves <= 8};
 }
 
 }  // namespace
