@@ -657,7 +657,7 @@ def gpu_encode_stack(n, target_bpp):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); multi-GPU decode is not part of this build.",
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
     import torch
