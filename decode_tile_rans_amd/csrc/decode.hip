@@ -1322,26 +1322,30 @@ int decode_one(const Blob& b, void* dst, int64_t chain_lo, int64_t chain_hi, int
 
 // Sum of the fused product's partial sums of row r for activation row t, in a fixed
 // order (tiles, then chains of a tile, ascending), plus the bias; rounded to BF16 as the
-// GEMM's epilogue rounds.  Thread i: t = i / R, r = i % R.
+// GEMM's epilogue rounds.
 __global__ void matvec_finish_kernel(const float* __restrict__ part, const uint16_t* __restrict__ bias,
                                      uint16_t* __restrict__ y, int64_t T, int64_t R, int64_t G, int log2S,
                                      int64_t n_groups, int slots, int NT) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T * R) return;
-  const int64_t t = i / R, r = i % R;
+  // thread (x, y): row r, activation row t (no division for either)
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, t = blockIdx.y;
+  if (r >= R) return;
   const int64_t S = 1 << log2S;
   const int64_t g_lo = r * G, g_hi = (r + 1) * G;   // the row's groups
   float sum = 0.f;
   for (int64_t tile = g_lo >> 9; tile <= (g_hi - 1) >> 9; ++tile) {
     int64_t gt = n_groups - (tile << 9);
     if (gt > kTileGroups) gt = kTileGroups;
+    // the row of the tile's first group; chain j starts S > j groups later, at most
+    // one row further (G >= S)
+    const int64_t rt = (tile << 9) / G, rem = (tile << 9) - rt * G;
     for (int64_t j = 0; j < S; ++j) {
       const int64_t g0 = (tile << 9) + j;
       const int64_t ngr = gt > j ? (gt - j + S - 1) >> log2S : 0;
       const int64_t k = g_lo > g0 ? (g_lo - g0 + S - 1) >> log2S : 0;   // first group at or past the row
       if (k >= ngr || g0 + (k << log2S) >= g_hi) continue;
       const int64_t ch = (tile << log2S) + j;
-      sum += part[(ch * slots + (r - g0 / G)) * NT + t];
+      const int64_t r0 = rt + (rem + j >= G ? 1 : 0);   // = g0 / G
+      sum += part[(ch * slots + (r - r0)) * NT + t];
     }
   }
   if (bias) sum += __uint_as_float((uint32_t)bias[r] << 16);
@@ -1458,8 +1462,7 @@ int matvec_batch_launch(const Blob* const* bs, int n, const void* x, int64_t T, 
   }
   for (int i = 0; i < n; ++i) {
     const Blob& b = *bs[i];
-    const int64_t cnt = T * b.R;
-    hipLaunchKernelGGL(matvec_finish_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st, part[i],
+    hipLaunchKernelGGL(matvec_finish_kernel, dim3((unsigned)((b.R + 255) / 256), (unsigned)T), dim3(256), 0, st, part[i],
                        (const uint16_t*)(bias ? bias[i] : nullptr), (uint16_t*)y[i], T, b.R, (int64_t)((b.C + 7) / 8),
                        (int)__builtin_ctz((unsigned)b.S), b.n_groups(), matvec_slots(b), nt);
     if ((rc = hip_check(hipGetLastError(), "fused product finish launch"))) return rc;
