@@ -38,8 +38,8 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--target-bpp", type=float, default=4.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-linear", action="store_true")
