@@ -8,8 +8,10 @@ FP8 variant: Y = (X_q W_q^T) * a_x * a_r with per-tensor activation scale a_x
 and per-row weight scales a_r ([README] "FP8@5": FP8 W8A8 weight codes, FP8
 GEMM at inference).
 
-Pins (tests): agreement with an independent pure-Python dot product on small
-shapes.
+Pins (tests/test_oracle_gemm.py): every output of both functions equals an
+exactly rounded pure-Python dot product (math.fsum over the float64 products) on
+shapes whose three sizes all differ, with a bias and a non-uniform per-row scale,
+bit for bit where the inputs make every partial sum exact.
 """
 from __future__ import annotations
 

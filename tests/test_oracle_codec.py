@@ -82,6 +82,27 @@ def test_config2_bar_and_estimate():
     assert abs(data_bpp - est_bpp) < 0.02 + 24.0 * b.n_chains / src.size
 
 
+def test_outliers_take_the_escape_path():
+    """The outlier recipe (log-normal rows, 0.1 % of entries at +-10 s_r) at 6 bpp: the
+    outliers land beyond the largest direct magnitude (K = 128), so they are coded as
+    escape buckets with raw bits.  Every decoded coordinate must equal the E8 point of
+    the encoder's lattice input, and most outliers must be among the escaped ones."""
+    R = C = 768
+    src = synth.rowscaled(R, C, 2, 0.001)
+    blob = oracle.compress(src, nx.DT_BF16, 6.0)
+    b = codec.parse_blob(blob)
+    assert b.k == 7 and (b.flags & codec.FLAG_ESC)
+    assert 6.0 <= codec.actual_bpp(blob) <= 6.1
+    u, out, info = oracle.decode(blob)
+    assert info["final_state_ok"] and info["reads_in_bounds"]
+    h = rate.half_steps(b.s_bits, b.delta)
+    w = nx.bf16_to_f64(src)
+    assert np.array_equal(u, rate.quantize_rows(w, h).reshape(R, C))
+    big = np.abs(u) >> 1 >= 128
+    outl = np.abs(w) >= 9.0 * np.sqrt((w * w).mean(axis=1, keepdims=True))
+    assert (big & outl).sum() >= 0.5 * outl.sum() > 0      # most outliers take escapes
+
+
 @pytest.mark.parametrize("t", [1.0, 2.3, 3.0, 5.0, 8.0, 11.0])
 def test_rate_bar_sweep(t):
     src = synth.rowscaled(512, 512, 40 + int(t * 10))

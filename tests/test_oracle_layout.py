@@ -70,3 +70,95 @@ def test_block_geometry():
     tails = lens % 8
     assert tail_pos[0] == 8 * 72 and tail_pos[1] == 8 * 72 + 1 and tail_pos[3] == 8 * 72 + 1
     assert chunks.tolist() == [72 + -(-int(tails[:64].sum()) // 8), 7 + -(-int(tails[64:].sum()) // 8)]
+
+
+# ---- the stream layout inverts: every chain's words come back from the blob
+
+INVERT_CASES = [
+    # (rows, cols, target bpp, chains per tile, seed): ragged last tiles, escapes at
+    # 8 and 11 bpp, one chain per tile, all 64 chains of a block in one tile
+    (256, 256, 3.5, 1, 0),
+    (300, 520, 4.0, 8, 1),
+    (200, 512, 8.0, 8, 2),
+    (120, 512, 11.0, 4, 3),
+    (200, 512, 3.0, 64, 4),
+    (37, 13, 2.3, 2, 5),
+]
+
+
+@pytest.mark.parametrize("R,C,t,S,seed", INVERT_CASES)
+def test_stream_gives_back_every_chains_words(monkeypatch, R, C, t, S, seed):
+    """compress() places each chain's words (as encode_chains emitted them, in decoding
+    order) at the positions the request schedule assigns; reading the blob by hand --
+    blocks from their offsets, tiles' main areas in tile order, full chunk n of chain j
+    at 8 * rank[t, j, n], then the tails in chain order, then zero padding -- must give
+    every chain's words back exactly."""
+    import synth
+    import oracle
+    from oracle import codec, numerics as nx
+
+    seen = {}
+    enc, place = codec.encode_chains, codec.build_stream
+
+    def spy_encode(sym, model, cg):
+        states, words, cons = enc(sym, model, cg)
+        seen["words"] = [np.array(w, dtype=np.uint16) for w in words]
+        seen["cons"] = np.array(cons)
+        seen["cg"] = np.array(cg)
+        return states, words, cons
+
+    def spy_place(words, lens, rank, S_):
+        seen["rank"] = np.array(rank)
+        return place(words, lens, rank, S_)
+
+    monkeypatch.setattr(codec, "encode_chains", spy_encode)
+    monkeypatch.setattr(codec, "build_stream", spy_place)
+    blob = oracle.compress(synth.rowscaled(R, C, seed), nx.DT_BF16, t, chains_per_tile=S)
+    b = oracle.parse_blob(blob)
+    words, rank = seen["words"], seen["rank"]
+    n_ch = b.n_tiles * S
+    lens = b.chain_lens.astype(np.int64)
+    assert len(words) == n_ch
+    assert [len(w) for w in words] == lens.tolist()
+
+    # the ranks are the schedule's for the consumption the encoder recorded
+    T_, steps = b.n_tiles, seen["cg"].shape[1]
+    ngr = (seen["cg"] >= 0).sum(axis=1).reshape(T_, S)
+    esc_any = np.zeros((T_, S, steps), dtype=bool)
+    if b.flags & 1:
+        # a group takes the careful path when one of its magnitudes reaches the escape
+        # threshold 2^k: recomputed from the decoded coordinates, not the encoder's symbols
+        u, _, _ = oracle.decode(blob)
+        G = -(-C // 8)
+        up = np.zeros((R, G * 8), dtype=np.int64)
+        up[:, :C] = u
+        mags = np.abs(up.reshape(-1, 8)) >> 1
+        gesc = (mags >= (1 << b.k)).any(axis=1)
+        cg = seen["cg"]
+        esc_any = np.where(cg >= 0, gesc[np.maximum(cg, 0)], False).reshape(T_, S, steps)
+    assert np.array_equal(layout.request_ranks(lens.reshape(T_, S), ngr, seen["cons"].reshape(T_, S, steps), esc_any),
+                          rank)
+
+    stream = b.stream
+    offs = [int(o) * 8 for o in b.block_offsets] + [len(stream)]
+    for blk in range(b.n_blocks):
+        c0, c1 = 64 * blk, min(64 * blk + 64, n_ch)
+        pos = offs[blk]
+        for tile in range(c0 // S, -(-c1 // S)):
+            chunks = 0
+            for j in range(S):
+                c = tile * S + j
+                for n in range(int(lens[c]) // 8):
+                    p = pos + 8 * int(rank[tile, j, n])
+                    assert np.array_equal(stream[p:p + 8], words[c][8 * n:8 * n + 8]), (c, n)
+                    chunks += 1
+            # the tile's ranks are exactly 0 .. chunks - 1
+            got = sorted(int(rank[tile, j, n]) for j in range(S) for n in range(int(lens[tile * S + j]) // 8))
+            assert got == list(range(chunks))
+            pos += 8 * chunks
+        for c in range(c0, c1):
+            r = int(lens[c]) % 8
+            assert np.array_equal(stream[pos:pos + r], words[c][len(words[c]) - r:]), c
+            pos += r
+        assert 0 <= offs[blk + 1] - pos < 8
+        assert not stream[pos:offs[blk + 1]].any()
