@@ -85,3 +85,25 @@ class DevBlob:
             self.L.ep_blob_free(self.h)
         except Exception:
             pass
+
+
+def linear_bound(ref, mag, K, scale_roundings=0):
+    """Per-element error bound of a BF16-out product with fp32 accumulation.
+
+    ref: exact (float64) outputs; mag: the same product of the absolute values (times
+    any scales); K: terms per output.  Products of BF16 (or FP8) inputs are exact in
+    fp32, so the fp32 sum of K terms (plus bias) is within (K + 1) 2^-24 mag of the exact
+    one in any order (Higham's gamma_n bound), each fp32 scaling adds 2^-24 |ref|, and the
+    final rounding to BF16 half an ulp, at most 2^-8 of the value."""
+    u = 2.0 ** -24
+    acc = (K + 1) * u * mag + scale_roundings * u * np.abs(ref)
+    return 2.0 ** -8 * (np.abs(ref) + acc) + acc * 1.000001 + 1e-30
+
+
+def check_linear(got, ref, mag, K, scale_roundings=0):
+    """Every output within linear_bound; names the first offending element."""
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    bound = linear_bound(ref, mag, K, scale_roundings)
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, (f"{len(bad)} of {err.size} outputs off, first {tuple(bad[0])}: "
+                           f"got {got[tuple(bad[0])]} ref {ref[tuple(bad[0])]} bound {bound[tuple(bad[0])]}")
