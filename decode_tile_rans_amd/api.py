@@ -249,10 +249,19 @@ class CompressedLinear(torch.nn.Module):
         return self._c.actual_bpp
 
     def _load_from_state_dict(self, state_dict, prefix, *args, **kwargs):
-        super()._load_from_state_dict(state_dict, prefix, *args, **kwargs)
+        # The stored blob's length depends on the weight and its target rate, so the
+        # ``packed`` buffer takes the incoming length before the copy; the blob is parsed
+        # (and a corrupt one refused) before anything of the module changes, and the
+        # handle is rebuilt from the bytes that actually landed in ``packed``.
         key = prefix + "packed"
         if key in state_dict:
-            self._c = Compressed.from_bytes(state_dict[key].cpu().numpy().tobytes())
+            incoming = state_dict[key]
+            Compressed.from_bytes(incoming.detach().cpu().contiguous().numpy().tobytes())
+            if incoming.shape != self.packed.shape:
+                self.packed = torch.empty(incoming.shape, dtype=torch.uint8, device=self.packed.device)
+        super()._load_from_state_dict(state_dict, prefix, *args, **kwargs)
+        if key in state_dict:
+            self._c = Compressed.from_bytes(self.packed.detach().cpu().numpy().tobytes())
             self.out_features, self.in_features = self._c.shape
             self._ws = None
 

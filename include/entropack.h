@@ -166,7 +166,9 @@ int64_t ep_blob_device_errors(const ep_blob* blob);
  * (>= ep_linear_workspace_bytes bytes), then an MFMA BF16 GEMM with fp32
  * accumulation runs on the same stream.  With T <= 8, when ep_compressed_matvec takes
  * the blob and its partial sums fit ep_linear_workspace_bytes, that fused product runs
- * instead (same result up to fp32 summation order). */
+ * instead (same result up to fp32 summation order).  x, y, bias and dev_ws must be
+ * device, managed or pinned memory (EP_E_ARG otherwise, for every T, before any
+ * launch).  Asynchronous. */
 size_t ep_linear_workspace_bytes(const ep_blob* blob);
 int ep_compressed_linear_forward(const ep_blob* w, const void* dev_x, int64_t T,
                                  const void* dev_bias, void* dev_y,
@@ -175,11 +177,17 @@ int ep_compressed_linear_forward(const ep_blob* w, const void* dev_x, int64_t T,
 /* A sequence of compressed linear layers, y_i = x_i W_i^T (+ bias_i), i = 0..n-1
  * ([README] 快速开始 layer(x), applied layer after layer as a model runs them; [ABS]:
  * decoding cost grows with the weight count, so it should hide behind the GEMMs).
- * The decode of layer i+1 runs on `side` while the GEMM of layer i runs on `main`; the
- * two alternate between two weight buffers in dev_ws (>= ep_linear_seq_workspace_bytes
- * bytes).  x[i] is T x cols_i, y[i] is T x rows_i, bias may be NULL or hold NULLs.
- * The side stream first waits for the work already queued on `main`; all GEMMs run on
- * `main`, so work queued on `main` afterwards sees every output.  Asynchronous. */
+ * Each layer is decoded, then multiplied.  The decode of layer i+1 runs on `side`, beside
+ * the GEMM of layer i on `main`, when that GEMM has fewer 256 x 256 output tiles than the
+ * GPU has CUs (its workgroups leave CUs idle); otherwise it runs on `main` before its
+ * GEMM (a decode workgroup cannot share a CU with a GEMM workgroup: their LDS needs add
+ * up to more than a CU holds, so a side-stream decode could only take CUs away from a
+ * GEMM that fills them).  Two weight buffers in dev_ws (>= ep_linear_seq_workspace_bytes
+ * bytes) alternate.  x[i] is T x cols_i, y[i] is T x rows_i, bias may be NULL or hold
+ * NULLs; every pointer must be device, managed or pinned memory (EP_E_ARG otherwise,
+ * before any launch).  The side stream first waits for the work already queued on
+ * `main`; all GEMMs run on `main`, so work queued on `main` afterwards sees every
+ * output.  Asynchronous. */
 size_t ep_linear_seq_workspace_bytes(const ep_blob* const* w, int n);
 int ep_compressed_linear_seq_forward(const ep_blob* const* w, int n, const void* const* dev_x, int64_t T,
                                      const void* const* dev_bias, void* const* dev_y,
@@ -214,13 +222,16 @@ int ep_compressed_matvec_batch(const ep_blob* const* w, int n, const void* dev_x
                                size_t ws_bytes, ep_stream stream);
 
 /* Plain BF16 "NT" GEMM on MFMA: y[T x N] = x[T x K] w[N x K]^T (+ bias[N]), fp32
- * accumulate, BF16 out.  The uncompressed baseline of the linear layer. */
+ * accumulate, BF16 out.  The uncompressed baseline of the linear layer.  x and w
+ * 16-byte aligned, K % 8 == 0; every pointer must be device, managed or pinned memory
+ * (EP_E_ARG otherwise, checked before any launch).  Asynchronous. */
 int ep_gemm_bf16_nt(const void* dev_x, const void* dev_w, const void* dev_bias,
                     void* dev_y, int64_t T, int64_t N, int64_t K, ep_stream stream);
 
 /* FP8 (E4M3FN) "NT" GEMM on MFMA ([NEWS]/[README] FP8@5: FP8 W8A8 codes, FP8 GEMM):
  * y[T x N] (BF16) = (xq[T x K] wq[N x K]^T) * a_x * a_w[N], fp32 accumulate.
- * a_w is a device float array (per output row), a_x a host float. */
+ * a_w is a device float array (per output row), a_x a host float.  K % 16 == 0; the
+ * same alignment and pointer rules as ep_gemm_bf16_nt. */
 int ep_gemm_fp8_nt(const void* dev_xq, const void* dev_wq, float a_x, const float* dev_aw,
                    void* dev_y, int64_t T, int64_t N, int64_t K, ep_stream stream);
 

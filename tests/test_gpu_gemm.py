@@ -1,5 +1,7 @@
 """GPU tests of the MFMA GEMMs and the compressed linear layer against the
-float64 oracle GEMM (relative L2 <= 1e-2, the bound BF16 outputs allow)."""
+float64 oracle GEMM: every output within the per-element bound of an fp32-accumulated
+BF16-out product (gpu_util.linear_bound), which a wrong tile, row or K-slice exceeds by
+far; the layer outputs also within 1e-2 relative L2 (the pages' bar)."""
 import numpy as np
 import pytest
 
@@ -10,7 +12,7 @@ from oracle.gemm import linear_ref, linear_fp8_ref, rel_l2
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import DevBlob, say, stream_ptr  # noqa: E402
+from gpu_util import DevBlob, check_linear, say, stream_ptr  # noqa: E402
 
 TOL = 1e-2
 
@@ -35,8 +37,11 @@ def test_gemm_bf16(T, N, K):
     y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
     L.ep_gemm_bf16_nt(xt.data_ptr(), wt.data_ptr(), bt.data_ptr(), y.data_ptr(), T, N, K, stream_ptr())
     torch.cuda.synchronize()
-    ref = linear_ref(nx.bf16_to_f64(x), nx.bf16_to_f64(w), nx.bf16_to_f64(bias))
+    xf, wf, bf = nx.bf16_to_f64(x), nx.bf16_to_f64(w), nx.bf16_to_f64(bias)
+    ref = linear_ref(xf, wf, bf)
+    mag = linear_ref(np.abs(xf), np.abs(wf), np.abs(bf))
     got = nx.bf16_to_f64(y.cpu().view(torch.int16).numpy().view(np.uint16))
+    check_linear(got, ref, mag, K)
     assert rel_l2(got, ref) <= TOL
 
 
@@ -53,8 +58,11 @@ def test_gemm_fp8(T, N, K):
     y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
     L.ep_gemm_fp8_nt(xt.data_ptr(), wt.data_ptr(), a_x, awt.data_ptr(), y.data_ptr(), T, N, K, stream_ptr())
     torch.cuda.synchronize()
-    ref = linear_fp8_ref(nx.fp8_e4m3fn_to_f64(xq), nx.fp8_e4m3fn_to_f64(wq), a_x, aw)
+    xf, wf = nx.fp8_e4m3fn_to_f64(xq), nx.fp8_e4m3fn_to_f64(wq)
+    ref = linear_fp8_ref(xf, wf, a_x, aw)
+    mag = linear_fp8_ref(np.abs(xf), np.abs(wf), a_x, aw)
     got = nx.bf16_to_f64(y.cpu().view(torch.int16).numpy().view(np.uint16))
+    check_linear(got, ref, mag, K, scale_roundings=2)
     assert rel_l2(got, ref) <= TOL
 
 
@@ -79,9 +87,50 @@ def test_compressed_linear_forward():
     L.ep_compressed_linear_forward(db.h, xt.data_ptr(), T, bt.data_ptr(), y.data_ptr(), ws.data_ptr(), need,
                                    stream_ptr())
     torch.cuda.synchronize()
-    ref = linear_ref(nx.bf16_to_f64(x), nx.bf16_to_f64(w_hat), nx.bf16_to_f64(bias))
+    xf, wf, bf = nx.bf16_to_f64(x), nx.bf16_to_f64(w_hat), nx.bf16_to_f64(bias)
+    ref = linear_ref(xf, wf, bf)
     got = nx.bf16_to_f64(y.cpu().view(torch.int16).numpy().view(np.uint16))
+    check_linear(got, ref, linear_ref(np.abs(xf), np.abs(wf), np.abs(bf)), C)
     assert rel_l2(got, ref) <= TOL
+    assert db.errors() == 0
+
+
+def test_linear_and_gemm_refuse_host_memory():
+    """Pageable host pointers are refused before any launch, for every token count."""
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    say("host-memory refusals")
+    R, C = 256, 512
+    db = DevBlob(oracle.compress(synth.rowscaled(R, C, 23), nx.DT_BF16, 4.0))
+    need = L.ep_linear_workspace_bytes(db.h)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for T in (4, 64):
+        xd = torch.zeros((T, C), dtype=torch.bfloat16, device="cuda")
+        yd = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
+        xh = np.zeros((T, C), np.uint16)
+        yh = np.zeros((T, R), np.uint16)
+        bh = np.zeros(R, np.uint16)
+        wsh = np.zeros(need, np.uint8)
+        for args in ((xh.ctypes.data, 0, yd.data_ptr(), ws.data_ptr()),
+                     (xd.data_ptr(), 0, yh.ctypes.data, ws.data_ptr()),
+                     (xd.data_ptr(), bh.ctypes.data, yd.data_ptr(), ws.data_ptr()),
+                     (xd.data_ptr(), 0, yd.data_ptr(), wsh.ctypes.data)):
+            x_, b_, y_, w_ = args
+            with pytest.raises(L.EPError):
+                L.ep_compressed_linear_forward(db.h, x_, T, b_, y_, w_, need, stream_ptr())
+    T, N, K = 64, 128, 256
+    xd = torch.zeros((T, K), dtype=torch.bfloat16, device="cuda")
+    wd = torch.zeros((N, K), dtype=torch.bfloat16, device="cuda")
+    yd = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    host = np.zeros((N, K), np.uint16)
+    with pytest.raises(L.EPError):
+        L.ep_gemm_bf16_nt(xd.data_ptr(), host.ctypes.data, None, yd.data_ptr(), T, N, K, stream_ptr())
+    with pytest.raises(L.EPError):
+        L.ep_gemm_bf16_nt(host.ctypes.data, wd.data_ptr(), None, yd.data_ptr(), T, N, K, stream_ptr())
+    aw = np.ones(N, np.float32)
+    with pytest.raises(L.EPError):
+        L.ep_gemm_fp8_nt(xd.data_ptr(), wd.data_ptr(), 1.0, aw.ctypes.data, yd.data_ptr(), T, N, K, stream_ptr())
+    torch.cuda.synchronize()
     assert db.errors() == 0
 
 
@@ -102,9 +151,12 @@ def test_python_api_module_and_state_dict():
     blob = oracle.compress(w_bits, nx.DT_BF16, 4.0)
     assert layer._c.to_bytes() == blob
     _, w_hat, _ = oracle.decode(blob)
-    ref = linear_ref(x.float().cpu().numpy().astype(np.float64), nx.bf16_to_f64(w_hat),
-                     lin.bias.detach().float().cpu().numpy())
-    assert rel_l2(y.float().cpu().numpy(), ref) <= TOL
+    xf, wf = x.float().cpu().numpy().astype(np.float64), nx.bf16_to_f64(w_hat)
+    bf = lin.bias.detach().float().cpu().numpy().astype(np.float64)
+    ref = linear_ref(xf, wf, bf)
+    got = y.float().cpu().numpy().astype(np.float64)
+    check_linear(got, ref, linear_ref(np.abs(xf), np.abs(wf), np.abs(bf)), 512)
+    assert rel_l2(got, ref) <= TOL
     sd = layer.state_dict()
     layer2 = ep.CompressedLinear(ep.Compressed.from_bytes(blob), torch.zeros(384, dtype=torch.bfloat16, device="cuda"))
     layer2.load_state_dict(sd)
@@ -122,14 +174,23 @@ def test_python_api_module_and_state_dict():
     assert np.array_equal(r.cpu().view(torch.int16).numpy().view(np.uint16), ref_w)
 
 
-def test_compressed_linear_sequence_overlapped():
-    """Layers run with the next layer's decode on a second stream: every output is
-    bit-identical to the one-layer path and within tolerance of the oracle GEMM."""
+# (T, [(rows = out, cols = in), ...]): at 200 tokens every GEMM leaves CUs idle, so every
+# decode after the first runs on the side stream; at 4096 tokens the 4096-row layers'
+# GEMMs take 256 tiles (one per CU) and the next decode runs in order on the main stream,
+# while the 512-row layer's 32-tile GEMM lets the decode after it go to the side stream
+SEQ_CASES = [
+    (200, [(512, 768), (768, 512), (1024, 768), (768, 1024), (512, 768)]),
+    (4096, [(4096, 256), (512, 256), (4096, 256), (4096, 256)]),
+]
+
+
+@pytest.mark.parametrize("T,shapes", SEQ_CASES, ids=["side", "mixed"])
+def test_compressed_linear_sequence(T, shapes):
+    """A sequence of layers: every output is bit-identical to the one-layer path and
+    every element within the per-element bound of the oracle GEMM."""
     import torch
     from decode_tile_rans_amd import _lib as L
-    shapes = [(512, 768), (768, 512), (1024, 768), (768, 1024), (512, 768)]   # (rows = out, cols = in)
-    T = 200
-    dbs, xs, ys, refs, bs = [], [], [], [], []
+    dbs, xs, ys, refs, mags, bs = [], [], [], [], [], []
     for i, (R, C) in enumerate(shapes):
         blob = oracle.compress(synth.rowscaled(R, C, 40 + i), nx.DT_BF16, 3.0 + 0.5 * i)
         _, w_hat, _ = oracle.decode(blob)
@@ -139,7 +200,10 @@ def test_compressed_linear_sequence_overlapped():
         xs.append(_t(x, torch.bfloat16))
         bs.append(_t(b, torch.bfloat16) if b is not None else None)
         ys.append(torch.empty((T, R), dtype=torch.bfloat16, device="cuda"))
-        refs.append(linear_ref(nx.bf16_to_f64(x), nx.bf16_to_f64(w_hat), nx.bf16_to_f64(b) if b is not None else None))
+        xf, wf = nx.bf16_to_f64(x), nx.bf16_to_f64(w_hat)
+        bf = nx.bf16_to_f64(b) if b is not None else None
+        refs.append(linear_ref(xf, wf, bf))
+        mags.append(linear_ref(np.abs(xf), np.abs(wf), np.abs(bf) if bf is not None else None))
     hs = [d.h for d in dbs]
     need = L.ep_linear_seq_workspace_bytes(hs)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
@@ -165,6 +229,7 @@ def test_compressed_linear_sequence_overlapped():
             torch.cuda.synchronize()
             assert torch.equal(y.view(torch.int16), one.view(torch.int16)), f"layer {i} differs from the one-layer path"
             got = nx.bf16_to_f64(y.cpu().view(torch.int16).numpy().view(np.uint16))
+            check_linear(got, ref, mags[i], shapes[i][1])
             assert rel_l2(got, ref) <= TOL
     for db in dbs:
         assert db.errors() == 0
