@@ -286,26 +286,56 @@ def valu_issue(params_per_s):
             "frac": round(params_per_s / ceiling, 4)}
 
 
-def cpu_baseline(target_bpp):
-    """The oracle decoder (NumPy, single process) on one 3840 x 3840 stack matrix."""
+def _oracle_decode_worker(args):
+    """One host process of the oracle baseline: decode the blob repeatedly for about
+    `seconds`; returns (coordinates decoded, seconds)."""
+    blob, n_coords, seconds = args
+    import oracle
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.decode(blob)
+        n += n_coords
+        if time.perf_counter() - t0 >= seconds:
+            return n, time.perf_counter() - t0
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(target_bpp, seconds=10.0):
+    """The oracle decoder (NumPy) on one 3840 x 3840 stack matrix: one process, then one
+    process per host core (at most 16, the host share of one GPU) each decoding the
+    blob for the same time; the all-cores rate is the reported value."""
+    import multiprocessing as mp
     import numpy as np
     import oracle
     import synth
     from oracle import numerics as nx
     w = synth.dit_stack_torch(0).cpu().view(__import__("torch").int16).numpy().view(np.uint16)
     blob = oracle.compress(w, nx.DT_BF16, target_bpp)
-    n = 0
-    t0 = time.perf_counter()
-    reps = 0
-    while time.perf_counter() - t0 < 10.0 or reps < 1:
-        oracle.decode(blob)
-        n += w.size
-        reps += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(2.0 * n / dt / 1e9, 4), "unit": "GB/s (BF16 out)", "cores": 1, "kind": "oracle",
-            "sample": f"oracle.decode of one 3840x3840 stack matrix (14.7M params, {reps} repetitions, "
-                      f"{dt:.1f}s), NumPy single process",
-            "coords_per_s": round(n / dt, 1)}
+    n1, dt1 = _oracle_decode_worker((blob, w.size, seconds))
+    nproc = os.cpu_count() or 1
+    workers = max(1, min(16, nproc))
+    with mp.get_context("spawn").Pool(workers) as pool:
+        pool.map(_oracle_decode_worker, [(blob, w.size, 0.0)] * workers)     # start-up and imports
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_decode_worker, [(blob, w.size, seconds)] * workers)
+        wall = time.perf_counter() - t0
+    n_all = sum(n for n, _ in res)
+    return {"value": round(2.0 * n_all / wall / 1e9, 4), "unit": "GB/s (BF16 out)", "cores": workers, "kind": "oracle",
+            "sample": f"oracle.decode of one 3840x3840 stack matrix (14.7M params) in {workers} processes for "
+                      f"{wall:.1f}s ({n_all // w.size} decodes), NumPy",
+            "coords_per_s": round(n_all / wall, 1), "nproc": nproc, "cpu_model": _cpu_model(),
+            "single_process": {"value": round(2.0 * n1 / dt1 / 1e9, 4), "coords_per_s": round(n1 / dt1, 1),
+                               "seconds": round(dt1, 1), "cores": 1}}
 
 
 def fused_linear(target_bpp, reps=10):
@@ -685,7 +715,7 @@ def main():
         "value": round(out_bytes / (ms * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; trained weights unavailable)",
         "config": {"workload": f"{len(comps)}-matrix DiT-shaped BF16 stack (30 blocks x q,k,v,o 3840^2, w1,w3 "
                                f"10240x3840, w2 3840x10240, mod1,mod2 3840^2 + 6 x 3840^2), target "
