@@ -1413,7 +1413,7 @@ bool matvec_supported(const Blob& b, int64_t T) {
 // matvec_workspace_bytes - 256 bytes) holds blob i's partial sums.  The blobs' blocks
 // share launches (by table layout and escape variant, up to kMaxBatch blobs each).
 int matvec_batch_launch(const Blob* const* bs, int n, const void* x, int64_t T, const void* const* bias,
-                        void* const* y, float* const* part, ep_stream stream) {
+                        void* const* y, float* const* part, ep_stream stream, bool check_part) {
   hipStream_t st = (hipStream_t)stream;
   if (n < 1) return fail(EP_E_ARG, "empty batch");
   if (!x || (reinterpret_cast<uintptr_t>(x) & 15)) return fail(EP_E_ARG, "activations must be 16-byte aligned");
@@ -1426,27 +1426,32 @@ int matvec_batch_launch(const Blob* const* bs, int n, const void* x, int64_t T, 
       return fail(EP_E_ARG, "the fused product takes lossy BF16 blobs, 1..8 activation rows, C % 8 == 0 and at least S groups per row");
     if (b.C != bs[0]->C) return fail(EP_E_ARG, "blobs sharing activations need the same number of columns");
     if (!y[i] || !part[i]) return fail(EP_E_ARG, "null output or workspace");
-    if ((rc = check_gpu_pointer(y[i], "output")) || (rc = check_gpu_pointer(part[i], "workspace"))) return rc;
+    if ((rc = check_gpu_pointer(y[i], "output")) || (check_part && (rc = check_gpu_pointer(part[i], "workspace"))))
+      return rc;
     if (bias && bias[i] && (rc = check_gpu_pointer(bias[i], "bias"))) return rc;
   }
   const int nt = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
   const int out = nt == 1 ? OUT_MV1 : nt == 2 ? OUT_MV2 : nt == 4 ? OUT_MV4 : OUT_MV8;
+  // (no host allocation here: the launches' blob lists are fixed-size arrays, filled
+  // in blob order per table layout and escape variant)
   for (int pass = 0; pass < 4; ++pass) {
     const bool narrow = pass < 2, pesc = (pass & 1) != 0;
-    std::vector<int> idx;
-    for (int i = 0; i < n; ++i)
-      if ((bs[i]->k <= 6) == narrow && ((bs[i]->flags & kFlagEsc) != 0) == pesc) idx.push_back(i);
-    for (size_t i0 = 0; i0 < idx.size(); i0 += kMaxBatch) {
+    int idx[kMaxBatch];
+    int m = 0;
+    for (int i = 0; i <= n; ++i) {
+      if (i < n && (bs[i]->k <= 6) == narrow && ((bs[i]->flags & kFlagEsc) != 0) == pesc) idx[m++] = i;
+      if (m == 0 || (m < kMaxBatch && i < n)) continue;
       DecBatch B{};
-      B.n = (int)std::min<size_t>(kMaxBatch, idx.size() - i0);
+      B.n = m;
+      m = 0;
       int64_t nblk[kMaxBatch];
-      for (int q = 0; q < B.n; ++q) nblk[q] = bs[idx[i0 + q]]->n_blocks;
+      for (int q = 0; q < B.n; ++q) nblk[q] = bs[idx[q]]->n_blocks;
       Shape sh = pick_shape(nblk, B.n);
       sh.ilp = 1;
       B.bpw = sh.bpw;
       int64_t wg = 0;
       for (int q = 0; q < B.n; ++q) {
-        const int i = idx[i0 + q];
+        const int i = idx[q];
         const Blob& b = *bs[i];
         DecJob j = make_job(b, part[i]);
         j.mv_x = (const uint16_t*)x;
@@ -1483,6 +1488,39 @@ int matvec_forward(const Blob& b, const void* x, int64_t T, const void* bias, vo
   if (!ws) return fail(EP_E_ARG, "null workspace");
   if (ws_bytes < matvec_workspace_bytes(b, T)) return fail(EP_E_WORKSPACE, "workspace too small");
   return matvec_launch(b, x, T, bias, y, (float*)(((uintptr_t)ws + 255) & ~uintptr_t(255)), stream);
+}
+
+// ---------------------------------------------------------------- the fused product without a workspace
+// Partial sums of ep_compressed_matvec_noalloc: one file-scope device array (every GPU the
+// library runs on holds its own copy until the process ends).  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is kept per device.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+static int scratch_address(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+    (void)hipGetLastError();
+    return fail(EP_E_DEVICE, "no current device for the scratch array");
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(EP_E_DEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (float*)g_scratch_ptr[dev];
+  return EP_OK;
 }
 
 }  // namespace ep
@@ -1677,6 +1715,30 @@ int64_t ep_blob_device_errors(const ep_blob* blob) {
 size_t ep_linear_workspace_bytes(const ep_blob* blob) {
   if (!blob) return 0;
   return (size_t)blob->b.R * (size_t)blob->b.C * 2 + 256;
+}
+
+// The fused product with its partial sums in the library's scratch array (no allocation,
+// no workspace argument).  Every slot the finishing kernel reads is written by the
+// decode kernel of the same call, so nothing needs clearing between calls.
+int ep_compressed_matvec_noalloc(const ep_blob* w, const void* x, int64_t T, const void* bias, void* y,
+                                 ep_stream stream) {
+  set_error("");
+  if (!w || !x || !y) return fail(EP_E_ARG, "null pointer");
+  const Blob& b = w->b;
+  if (!matvec_supported(b, T))
+    return fail(EP_E_ARG, "the fused product takes lossy BF16 blobs, 1..8 activation rows, C % 8 == 0 and at least S groups per row");
+  const size_t need = matvec_workspace_bytes(b, T) - 256;
+  if (need > kScratchBytes)
+    return fail(EP_E_WORKSPACE, "partial sums of " + std::to_string(need) + " bytes exceed the 16 MiB scratch array "
+                "(use ep_compressed_matvec with a workspace)");
+  float* part = nullptr;
+  int rc = scratch_address(&part);
+  if (rc) return rc;
+  const Blob* bs[1] = {&b};
+  const void* bi[1] = {bias};
+  void* ys[1] = {y};
+  float* ps[1] = {part};
+  return matvec_batch_launch(bs, 1, x, T, bi, ys, ps, stream, false);
 }
 
 }  // extern "C"

@@ -157,8 +157,10 @@ int test_cast(int dtype, const float* in, void* out, int64_t n, int hw, ep_strea
 constexpr int64_t kMatvecMaxT = 8;
 bool matvec_supported(const Blob& b, int64_t T);
 size_t matvec_workspace_bytes(const Blob& b, int64_t T);
+// (check_part = false only for the library's own scratch array, which the runtime's
+// pointer query does not describe as an allocation)
 int matvec_batch_launch(const Blob* const* bs, int n, const void* x, int64_t T, const void* const* bias,
-                        void* const* y, float* const* part, ep_stream st);
+                        void* const* y, float* const* part, ep_stream st, bool check_part = true);
 int matvec_launch(const Blob& b, const void* x, int64_t T, const void* bias, void* y, float* part, ep_stream st);
 int matvec_forward(const Blob& b, const void* x, int64_t T, const void* bias, void* y, void* ws, size_t ws_bytes,
                    ep_stream st);

@@ -208,6 +208,20 @@ size_t ep_matvec_workspace_bytes(const ep_blob* w, int64_t T);
 int ep_compressed_matvec(const ep_blob* w, const void* dev_x, int64_t T, const void* dev_bias,
                          void* dev_y, void* dev_ws, size_t ws_bytes, ep_stream stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): ep_compressed_matvec with its partial sums in the
+ * library's own scratch array instead of a caller workspace.  Same arguments, rules,
+ * errors and bits as ep_compressed_matvec minus dev_ws / ws_bytes.  The array is one
+ * file-scope device array of 16 MiB per GPU, held until the process ends; a blob whose
+ * partial sums (ep_matvec_workspace_bytes(w, T) - 256 bytes) exceed it is refused with
+ * EP_E_WORKSPACE before any launch (14336 x 4096 at S = 8 and T = 8 needs 11 MB).  No
+ * hipMalloc, hipFree or other allocation is made.  Every call on one GPU shares that
+ * array: calls that overlap on one GPU (other streams, other host threads) race and must
+ * be ordered by the caller.  Nothing needs clearing between calls (each call writes
+ * every partial sum it reads).  Asynchronous. */
+int ep_compressed_matvec_noalloc(const ep_blob* w, const void* dev_x, int64_t T, const void* dev_bias,
+                                 void* dev_y, ep_stream stream);
+
 /* The fused product for n blobs that take the same activations (e.g. the query, key
  * and value projections of one layer): y[i] = x W_i^T (+ bias[i]), all W_i with the same
  * cols; bias may be NULL or hold NULLs.  The blobs' blocks share decode launches, which
