@@ -23,6 +23,7 @@ SIGNATURES = {
     "ep_compress": (_int, [_vp, _int, _i64, _i64, _dbl, C.POINTER(_vp)]),
     "ep_compress_ex": (_int, [_vp, _int, _i64, _i64, _dbl, _int, C.POINTER(_vp)]),
     "ep_blob_upload": (_int, [_vp, _vp]),
+    "ep_device_bytes": (_sz, [_vp]),
     "ep_decompress": (_int, [_vp, _vp, _vp]),
     "ep_decompress_tiles": (_int, [_vp, _i64, _i64, _vp, _vp]),
     "ep_decompress_batch": (_int, [C.POINTER(_vp), C.POINTER(_vp), _int, _vp]),
@@ -140,6 +141,10 @@ def ep_compressed_linear_forward(blob, dev_x, T, dev_bias, dev_y, dev_ws, ws_byt
 
 def ep_test_cast(dtype, dev_in, dev_out, n, hw=0, stream=0):
     check(lib().ep_test_cast(dtype, dev_in, dev_out, n, hw, stream))
+
+
+def ep_device_bytes(blob: int) -> int:
+    return int(lib().ep_device_bytes(blob))
 
 
 def ep_matvec_workspace_bytes(blob: int, T: int) -> int:

@@ -61,6 +61,11 @@ class Compressed:
     def nbytes(self) -> int:
         return L.ep_serialized_size(self._h)
 
+    @property
+    def device_bytes(self) -> int:
+        """Bytes of GPU memory the uploaded blob holds (0 before upload)."""
+        return L.ep_device_bytes(self._h)
+
     def to_bytes(self) -> bytes:
         return L.ep_serialize(self._h)
 

@@ -58,7 +58,13 @@ constexpr int kValShift = 22;
 
 struct DecJob {
   const uint16_t* stream;
-  const uint32_t* chain;     // per chain 4 x u32: state, tile main start, tail start, length
+  // the blob's chain area as stored: per block the start of its area (in 8-word chunks),
+  // per chain its full chunks (u8 at S >= 8, else u16), its tail words (4 bits) and the
+  // initial decoder state
+  const uint32_t* boff;
+  const void* full;
+  const uint8_t* nib;
+  const uint32_t* states;
   const float* hr;
   const uint32_t* tab;
   uint32_t* err;
@@ -899,6 +905,38 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
   for (int c = 0; c < ILP; ++c) optr[c] += (int64_t)X.S * 8 * ESZ;
 }
 
+// Where chain `lane` of block blk starts: its initial state, the word index of its tile's
+// main area, the word index of its tail and its length in words, from the stored chunk
+// counts and tail lengths.  Chains store their full chunks tile after tile and then all
+// tails in chain order, so a wave-wide exclusive prefix sum over the block's 64 chains of
+// (full chunks | tail words << 22) gives every offset: a tile's main area starts at the
+// chunk sum of the chains before its first lane, the tails after the block's chunk total.
+// (Full chunks of one block stay below 2^22 and tail words below 2^10.)  Every lane of the
+// wave takes part; blk is uniform per wave.
+__device__ __forceinline__ uint4 chain_meta(const DecJob& J, int64_t blk, int lane, int s0) {
+  if (blk >= J.n_blocks) return make_uint4(kL, 0u, 0u, 0u);
+  const int64_t ch = blk * 64 + lane;
+  uint32_t nf = 0u, tl = 0u, st = kL;
+  if (ch < J.n_chains) {
+    nf = J.log2S >= 3 ? (uint32_t)((const uint8_t*)J.full)[ch] : (uint32_t)((const uint16_t*)J.full)[ch];
+    tl = (uint32_t)(J.nib[ch >> 1] >> (4 * (ch & 1))) & 15u;
+    st = J.states[ch];
+  }
+  const uint32_t v = nf | (tl << 22);
+  uint32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = (uint32_t)__shfl_up((int)inc, (unsigned)o, 64);
+    inc += lane >= o ? t : 0u;
+  }
+  const uint32_t exc = inc - v;
+  const uint32_t tot = (uint32_t)__shfl((int)inc, 63, 64);
+  const uint32_t tile = (uint32_t)__shfl((int)exc, s0, 64);
+  const uint32_t base = 8u * J.boff[blk];   // the block's first word
+  constexpr uint32_t kLo = (1u << 22) - 1u;
+  return make_uint4(st, base + 8u * (tile & kLo), base + 8u * (tot & kLo) + (exc >> 22), 8u * nf + tl);
+}
+
 // One wave decodes ILP blocks of 64 chains (blocks blk0 .. blk0 + ILP - 1, those below
 // blk_end): lane l runs chain l of each, the ILP chains interleaved step by step so
 // that one chain's table read is in flight while another computes.
@@ -931,8 +969,8 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
     if (gt > kTileGroups) gt = kTileGroups;
     ngr[c] = (live[c] && gt > j) ? (int)((gt - j + S - 1) >> J.log2S) : 0;
     Chain& r = rd[c];
-    uint4 meta = make_uint4(kL, 0u, 0u, 0u);
-    if (live[c]) meta = ((const uint4*)J.chain)[ch];
+    uint4 meta = chain_meta(J, blk0 + c, lane, s0);
+    if (!live[c]) meta = make_uint4(kL, 0u, 0u, 0u);
     r.x = meta.x;
     r.cur = meta.y;
     r.tailp = meta.z;
@@ -1188,7 +1226,10 @@ int out_kind(const Blob& b) {
 DecJob make_job(const Blob& b, void* out) {
   DecJob j{};
   j.stream = b.d_stream;
-  j.chain = b.d_chain;
+  j.boff = b.d_boff;
+  j.full = b.d_full;
+  j.nib = b.d_nib;
+  j.states = b.d_states;
   j.hr = b.d_hr;
   j.tab = b.d_tab;
   j.err = b.d_err;
@@ -1546,11 +1587,19 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
   if (!blob) return fail(EP_E_ARG, "null blob");
   Blob& b = blob->b;
   if (b.d_base) return EP_OK;
+  // the decoder addresses stream words with 32-bit indices
+  if (b.n_words >= ((uint64_t)1 << 31)) return fail(EP_E_ARG, "stream too long for the device decoder (2^31 words)");
   auto al = [](size_t v) { return (v + 255) & ~size_t(255); };
   const size_t o_tab = 0;
   const size_t o_hr = o_tab + al(kTabBytes);
-  const size_t o_ch = o_hr + al(4 * ((size_t)b.R + kHrPad));
-  const size_t o_err = o_ch + al(16 * (size_t)b.n_chains);
+  // the chain area as stored (block offsets, chunk counts, tail nibbles, states), each
+  // section 256-byte aligned; the kernel derives every chain's offsets from it
+  const size_t fw = b.S >= 8 ? 1 : 2, n_nib = ((size_t)b.n_chains + 1) / 2;
+  const size_t o_boff = o_hr + al(4 * ((size_t)b.R + kHrPad));
+  const size_t o_full = o_boff + al(4 * (size_t)b.n_blocks);
+  const size_t o_nib = o_full + al(fw * (size_t)b.n_chains);
+  const size_t o_states = o_nib + al(n_nib);
+  const size_t o_err = o_states + al(4 * (size_t)b.n_chains);
   const size_t o_stream = o_err + 256;
   const size_t total = o_stream + al(2 * (size_t)b.n_words + 256);
   std::vector<uint8_t> host;
@@ -1565,35 +1614,10 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
     build_slot_tables(b.model, (uint32_t*)&host[o_tab], b.k <= 6);
     half_scales(b, (float*)&host[o_hr]);
   }
-  // per chain: state, word index of its tile's main area, of its tail, length
-  {
-    uint32_t* meta = (uint32_t*)&host[o_ch];
-    uint64_t block_start = 0;   // words
-    for (int64_t bk = 0; bk < b.n_blocks; ++bk) {
-      const int64_t c0 = bk * kBlockChains, c1 = std::min<int64_t>(b.n_chains, c0 + kBlockChains);
-      uint64_t main = block_start, words = 0;
-      for (int64_t c = c0; c < c1; ++c) words += b.chain_len[c];
-      uint64_t tails = block_start;
-      for (int64_t c = c0; c < c1; ++c) tails += 8 * (b.chain_len[c] / 8);
-      for (int64_t t0 = c0; t0 < c1; t0 += b.S) {
-        uint64_t tile_words = 0;
-        for (int64_t c = t0; c < t0 + b.S; ++c) tile_words += 8 * (b.chain_len[c] / 8);
-        for (int64_t c = t0; c < t0 + b.S; ++c) {
-          uint32_t st;
-          std::memcpy(&st, &b.bytes[b.off_states + 4 * (size_t)c], 4);
-          meta[4 * c + 0] = st;
-          meta[4 * c + 1] = (uint32_t)main;
-          meta[4 * c + 3] = b.chain_len[c];
-        }
-        main += tile_words;
-      }
-      for (int64_t c = c0; c < c1; ++c) {
-        meta[4 * c + 2] = (uint32_t)tails;
-        tails += b.chain_len[c] % 8;
-      }
-      block_start += 8 * ((words + 7) / 8);
-    }
-  }
+  std::memcpy(&host[o_boff], &b.bytes[b.off_boff], 4 * (size_t)b.n_blocks);
+  std::memcpy(&host[o_full], &b.bytes[b.off_full], fw * (size_t)b.n_chains);
+  std::memcpy(&host[o_nib], &b.bytes[b.off_tail], n_nib);
+  std::memcpy(&host[o_states], &b.bytes[b.off_states], 4 * (size_t)b.n_chains);
   std::memcpy(&host[o_stream], &b.bytes[b.off_stream], 2 * (size_t)b.n_words);
   void* d = nullptr;
   if (hipMalloc(&d, total) != hipSuccess) {
@@ -1603,7 +1627,10 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
   uint8_t* p = (uint8_t*)d;
   b.d_tab = (const uint32_t*)(p + o_tab);
   b.d_hr = (const float*)(p + o_hr);
-  b.d_chain = (const uint32_t*)(p + o_ch);
+  b.d_boff = (const uint32_t*)(p + o_boff);
+  b.d_full = (const void*)(p + o_full);
+  b.d_nib = (const uint8_t*)(p + o_nib);
+  b.d_states = (const uint32_t*)(p + o_states);
   b.d_err = (uint32_t*)(p + o_err);
   b.d_stream = (const uint16_t*)(p + o_stream);
   int rc = hip_check(hipMemcpyAsync(d, host.data(), total, hipMemcpyHostToDevice, (hipStream_t)stream), "upload");
@@ -1612,15 +1639,21 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
     (void)hipFree(d);
     b.d_tab = nullptr;
     b.d_hr = nullptr;
-    b.d_chain = nullptr;
+    b.d_boff = nullptr;
+    b.d_full = nullptr;
+    b.d_nib = nullptr;
+    b.d_states = nullptr;
     b.d_err = nullptr;
     b.d_stream = nullptr;
     return rc;
   }
   (void)hipGetDevice(&b.device);
   b.d_base = d;
+  b.d_bytes = total;
   return EP_OK;
 }
+
+size_t ep_device_bytes(const ep_blob* blob) { return blob ? blob->b.d_bytes : 0; }
 
 int ep_decompress(const ep_blob* blob, void* dev_dst, ep_stream stream) {
   set_error("");

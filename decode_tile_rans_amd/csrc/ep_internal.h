@@ -120,7 +120,11 @@ struct Blob {
   int device = -1;
   void* d_base = nullptr;              // one allocation
   const uint16_t* d_stream = nullptr;
-  const uint32_t* d_chain = nullptr;   // per chain 4 x u32: state, tile main start, tail start, length
+  size_t d_bytes = 0;                  // size of the device allocation
+  const uint32_t* d_boff = nullptr;    // the stored chain area: block offsets (u32),
+  const void* d_full = nullptr;        //   full chunks per chain (u8 at S >= 8, else u16),
+  const uint8_t* d_nib = nullptr;      //   tail nibbles,
+  const uint32_t* d_states = nullptr;  //   initial states
   const float* d_hr = nullptr;         // per-row half scales h_r
   const uint32_t* d_tab = nullptr;     // 7 x 2048 packed entries
   uint32_t* d_err = nullptr;

@@ -119,10 +119,18 @@ int ep_compress_device_batch(const void* const* dev_src, const int64_t* rows, co
 int ep_compress_lossless(const void* host_src, int64_t n_bytes, int elem_bytes, const int64_t* dims, int ndim,
                          int dtype_tag, int chains_per_tile, ep_blob** out);
 
-/* Copy the blob's stream, tile tables, row scales and the 7 expanded 2048-slot decode
- * tables to the current device (one H2D copy, enqueued on `stream`; the host side
- * waits for it).  Idempotent.  The device copy lives until ep_blob_free(). */
+/* Copy the blob's stream and chain area (block offsets, chunk counts, tail lengths and
+ * states, as stored), its row half-scales (float32) and the 7 expanded 2048-slot decode
+ * tables to the current device (one allocation, one H2D copy enqueued on `stream`; the
+ * host side waits for it).  The decoder derives each chain's stream offsets on the
+ * device (one wave prefix sum per 64 chains), so nothing per chain is expanded.
+ * Idempotent.  The device copy lives until ep_blob_free().  EP_E_ARG for streams of
+ * 2^31 words or more, EP_E_NOMEM when an allocation fails. */
 int ep_blob_upload(ep_blob* blob, ep_stream stream);
+
+/* Bytes of device memory the blob holds (0 before ep_blob_upload): the resident cost
+ * of a compressed weight, to set against its serialized size (actual_bpp). */
+size_t ep_device_bytes(const ep_blob* blob);
 
 /* ---------------------------------------------------------------- decode
  * ep_decompress — [SUM]: fused symbol decode + algebraic inverse lattice + row rescale.

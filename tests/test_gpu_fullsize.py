@@ -117,6 +117,21 @@ def test_dit_block_rate(dit_block):
         assert 4.0 <= L.ep_actual_bpp(h) <= 4.1
 
 
+def test_dit_block_device_residency(dit_block):
+    """What a compressed weight costs in HBM: the stored bytes, plus the 56 KB of
+    expanded decode tables, float32 row half-scales and section alignment -- within
+    0.03 bpp of actual_bpp over the block (nothing is expanded per chain)."""
+    from decode_tile_rans_amd import _lib as L
+    srcs, handles, _ = dit_block
+    params = sum(s.size for s in srcs)
+    stored = sum(L.ep_serialized_size(h) for h in handles)
+    dev = sum(L.ep_device_bytes(h) for h in handles)
+    for s, h in zip(srcs, handles):
+        extra = L.ep_device_bytes(h) - L.ep_serialized_size(h)
+        assert 0 < extra <= 57344 + 4 * (s.shape[0] + 128) + 7 * 256 + 512
+    assert 8.0 * dev / params <= 8.0 * stored / params + 0.03
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("index", list(range(9)))     # q, k, v, o, w1, w3, w2, mod1, mod2
 def test_dit_block_parity_full(dit_block, index):
