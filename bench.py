@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true", help="skip the 8192^2 container and chains-per-tile sweep")
     p.add_argument("--matrices", type=int, default=276, help="first N matrices of the stack (profiling runs)")
     p.add_argument("--streams", type=int, default=3, help="HIP streams the block launches rotate over")
+    p.add_argument("--gemm-only", action="store_true",
+                   help="only run the BF16 and FP8 GEMMs at 4096 x 14336 x 4096 and hipBLASLt (counter runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
     return p.parse_args()
@@ -66,6 +68,30 @@ def copy_calibration(reps=5):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_per_launch": n, "launches": reps}))
+
+
+def gemm_only(reps=5):
+    """Counter runs: our BF16 GEMM, our FP8 GEMM and hipBLASLt (torch.matmul) on the prefill
+    shape, T x N x K = 4096 x 14336 x 4096, `reps` calls each, one after the other."""
+    import torch
+    import synth
+    from decode_tile_rans_amd import _lib as L
+    T, N, K = 4096, 14336, 4096
+    x = torch.from_numpy(synth.activations(T, K, 50)).view(torch.bfloat16).cuda()
+    w = torch.from_numpy(synth.rowscaled(N, K, 5)).view(torch.bfloat16).cuda()
+    wq, aw = synth.fp8_codes(N, K, 5)
+    xq, axr = synth.fp8_codes(T, K, 50)
+    wqt, xqt, awt = torch.from_numpy(wq).cuda(), torch.from_numpy(xq).cuda(), torch.from_numpy(aw).cuda()
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    sp = int(torch.cuda.current_stream().cuda_stream)
+    for _ in range(reps):
+        L.ep_gemm_bf16_nt(x.data_ptr(), w.data_ptr(), None, y.data_ptr(), T, N, K, sp)
+    for _ in range(reps):
+        L.ep_gemm_fp8_nt(xqt.data_ptr(), wqt.data_ptr(), float(axr.max()), awt.data_ptr(), y.data_ptr(), T, N, K, sp)
+    for _ in range(reps):
+        torch.matmul(x, w.t())
+    torch.cuda.synchronize()
+    print(json.dumps({"gemm_only": [T, N, K], "reps": reps}))
 
 
 def practical_ceilings(reps=10):
@@ -392,7 +418,7 @@ def fused_linear(target_bpp, reps=10):
     flops = 2.0 * T * R * C
     # a sequence of layers (4 distinct weights, each twice): the next layer's decode on a
     # second stream while this layer's GEMM runs, against the same GEMMs on plain weights
-    seq = linear_sequence(c, wbits, x, T, target_bpp, timeit)
+    seq = linear_sequence(c, wbits, target_bpp, timeit)
     small = small_batch(c, w, x, ws, need, wd, sp, timeit)
     sweep = token_sweep(c, w, ws, need, sp, timeit)
     return {
@@ -492,10 +518,13 @@ def qkv_batch(timeit, sp):
     return out
 
 
-def linear_sequence(c0, wbits0, x, T, target_bpp, timeit, n_layers=8):
+def linear_sequence(c0, wbits0, target_bpp, timeit, n_layers=8):
     """n_layers compressed linears of the 14336x4096 shape (weights of seeds 5..8 in
-    turn): serial (decode then GEMM per layer, one stream), overlapped (decode of layer
-    i+1 on a side stream during the GEMM of layer i) and plain BF16 GEMMs."""
+    turn) at 4096 and at 256 tokens (X N(0,1), seed 52): serial (decode then GEMM per
+    layer, one stream), the sequence entry (which puts the decode of layer i+1 on a side
+    stream beside the GEMM of layer i when that GEMM leaves CUs idle: at 256 tokens its
+    56 tiles use 56 of the 256 CUs; at 4096 tokens it fills them and the entry runs in
+    order) and plain BF16 GEMMs."""
     import torch
     import synth
     import decode_tile_rans_amd as ep
@@ -512,6 +541,16 @@ def linear_sequence(c0, wbits0, x, T, target_bpp, timeit, n_layers=8):
     os.environ.pop("EP_NUM_THREADS", None)
     layers = [i % len(comps) for i in range(n_layers)]
     hs = [comps[i].handle for i in layers]
+    out = {}
+    for T in (4096, 256):
+        x = torch.from_numpy(synth.activations(T, C, 52)).view(torch.bfloat16).cuda()
+        out[f"tokens_{T}"] = _sequence_times(L, hs, wts, layers, x, T, R, C, n_layers, timeit)
+    del wts
+    return out
+
+
+def _sequence_times(L, hs, wts, layers, x, T, R, C, n_layers, timeit):
+    import torch
     ys = [torch.empty((T, R), dtype=torch.bfloat16, device="cuda") for _ in layers]
     st = torch.cuda.current_stream()
     sp = int(st.cuda_stream)
@@ -540,11 +579,11 @@ def linear_sequence(c0, wbits0, x, T, target_bpp, timeit, n_layers=8):
     for _ in range(2):
         t_plain, t_serial, t_over = min(t_plain, timeit(plain)), min(t_serial, timeit(serial)), \
             min(t_over, timeit(overlapped))
-    del ys, ws, ws1, wts
-    return {"layers": n_layers, "ms_plain_bf16_gemms": round(t_plain, 4), "ms_serial": round(t_serial, 4),
-            "ms_overlapped": round(t_over, 4),
+    del ys, ws, ws1
+    return {"layers": n_layers, "tokens": T, "ms_plain_bf16_gemms": round(t_plain, 4), "ms_serial": round(t_serial, 4),
+            "ms_sequence_entry": round(t_over, 4), "side_stream_used": (T + 255) // 256 * ((R + 255) // 256) < 256,
             "overhead_pct_serial": round(100.0 * (t_serial / t_plain - 1.0), 2),
-            "overhead_pct_overlapped": round(100.0 * (t_over / t_plain - 1.0), 2)}
+            "overhead_pct_sequence_entry": round(100.0 * (t_over / t_plain - 1.0), 2)}
 
 
 def lossless_block(reps=10):
@@ -695,6 +734,9 @@ def main():
     if a.copy_calibration:
         copy_calibration()
         return
+    if a.gemm_only:
+        gemm_only()
+        return
     comps, blocks = build_stack(a.matrices, a.target_bpp)
     outs = [torch.empty(c.shape, dtype=torch.bfloat16, device="cuda") for c in comps]
     n_params = sum(c.shape[0] * c.shape[1] for c in comps)
@@ -702,8 +744,14 @@ def main():
     out_bytes = 2 * n_params
 
     ms, _, units = time_stack(comps, blocks, outs, a.steps, a.warmup, n_streams=a.streams)
-    # per-launch kernel time for the roofline: one stream, launches back to back
+    # per-launch kernel time for the roofline: one stream, launches back to back, each
+    # launch alone on the GPU (so its blocks are spread evenly over the CUs, one
+    # workgroup per CU: EP_DECODE_SPREAD=1); the same launches with the timed step's
+    # shape (one block per wave, made for overlapping streams) reported beside it
+    _, launch_ms_std, _ = time_stack(comps, blocks, outs, 2, 1, n_streams=1)
+    os.environ["EP_DECODE_SPREAD"] = "1"
     _, launch_ms, _ = time_stack(comps, blocks, outs, 2, 1, n_streams=1)
+    os.environ.pop("EP_DECODE_SPREAD", None)
     errs = sum(c.device_errors() for c in comps)
     if errs:
         raise SystemExit(f"decode reported {errs} failed chains")
@@ -721,14 +769,20 @@ def main():
                                f"10240x3840, w2 3840x10240, mod1,mod2 3840^2 + 6 x 3840^2), target "
                                f"{a.target_bpp} bpp, decoded block by block (one launch per 9-matrix block)",
                    "params": n_params, "compressed_bytes": blob_bytes,
-                   "actual_bpp": round(8.0 * blob_bytes / n_params, 4), "launches_per_step": len(units),
+                   "actual_bpp": round(8.0 * blob_bytes / n_params, 4),
+                   "resident_bpp": round(8.0 * sum(c.device_bytes for c in comps) / n_params, 4),
+                   "launches_per_step": len(units),
                    "streams": a.streams},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (lambda t: round(t) if t else None)(traffic_per_launch(n_params / len(units))),
                      "kernel": "decode_kernel (BF16 out)", "avg_launch_ms": round(kern_ms / len(units), 5),
+                     "launch_shape": "one stream, blocks spread evenly over the CUs (EP_DECODE_SPREAD=1)",
+                     "frac_one_block_per_wave": round(alg_bytes / (sum(launch_ms_std) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "avg_launch_ms_one_block_per_wave": round(sum(launch_ms_std) / len(units), 5),
                      "algorithmic_bytes_per_launch": round(alg_bytes / len(units)),
                      "step_effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+                     "step_effective_frac": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "valu_issue_per_launch": valu_issue(n_params / (kern_ms * 1e-3)),
                      "valu_issue_step": valu_issue(n_params / (ms * 1e-3)),
                      "practical_ceilings": practical_ceilings()},

@@ -1279,8 +1279,20 @@ int cu_count() {
 // more waves, so launches running side by side on other streams fit more waves on the
 // chip (per-layer decode of the 276-matrix stack on four streams: 8.3 -> 6.0 ms).  Two chains per lane
 // (EP_DECODE_ILP=2) is an option; EP_DECODE_WAVES / EP_DECODE_BPW override the shape.
-Shape pick_shape(const int64_t* n_blocks, int n) {
-  const int64_t cus = cu_count();
+// Launch shape for launches of at least one full round.  By default every wave takes one
+// block, so a workgroup's LDS frees as its 16 waves end and launches queued on other
+// streams overlap the last round (the fastest way through a model's worth of matrices).
+// EP_DECODE_SPREAD=1 (read at every launch) spreads the blocks evenly instead, one
+// workgroup per CU whose waves loop over their share: a launch that runs alone ends with
+// every CU busy to its last round rather than a last round on part of the CUs.
+bool spread_mode() {
+  const char* e = std::getenv("EP_DECODE_SPREAD");
+  return e && std::atoi(e) == 1;
+}
+
+Shape pick_shape(const int64_t* n_blocks, int n, int64_t max_wg = 0) {
+  // (max_wg > 0: a launch meant to run beside other work, on at most max_wg CUs)
+  const int64_t cus = max_wg > 0 ? std::min<int64_t>(max_wg, cu_count()) : cu_count();
   const int lds = lds_max_bytes() - kTabBytes;
   int ilp = 1;
   if (const char* e = std::getenv("EP_DECODE_ILP"))
@@ -1289,7 +1301,18 @@ Shape pick_shape(const int64_t* n_blocks, int n) {
   int64_t total = 0;
   for (int i = 0; i < n; ++i) total += n_blocks[i];
   int64_t bpw;
-  if (total >= cus * wmax * ilp) {
+  if (total >= cus * wmax * ilp && spread_mode()) {
+    // one workgroup per CU, its waves looping over an even share of the blocks: a lone
+    // launch ends with every CU busy to its last round instead of a last round that
+    // holds only part of the CUs (it leaves no room for a launch on another stream)
+    bpw = (total + cus - 1) / cus;
+    for (;;) {
+      int64_t wg = 0;
+      for (int i = 0; i < n; ++i) wg += (n_blocks[i] + bpw - 1) / bpw;
+      if (wg <= cus) break;
+      ++bpw;
+    }
+  } else if (total >= cus * wmax * ilp) {
     bpw = (int64_t)wmax * ilp;
   } else {
     bpw = std::max<int64_t>(std::min<int64_t>(8, (int64_t)wmax * ilp), (total + cus - 1) / cus);
@@ -1336,7 +1359,8 @@ int check_uploaded(const Blob& b) {
   return EP_OK;
 }
 
-int decode_one(const Blob& b, void* dst, int64_t chain_lo, int64_t chain_hi, int out, hipStream_t st) {
+int decode_one(const Blob& b, void* dst, int64_t chain_lo, int64_t chain_hi, int out, hipStream_t st,
+               int64_t max_wg = 0) {
   int rc = check_uploaded(b);
   if (rc) return rc;
   if (!dst) return fail(EP_E_ARG, "null destination");
@@ -1351,7 +1375,7 @@ int decode_one(const Blob& b, void* dst, int64_t chain_lo, int64_t chain_hi, int
   if (bhi <= blo) return EP_OK;
   j.block_lo = blo;
   const int64_t nblk = bhi - blo;
-  const Shape sh = pick_shape(&nblk, 1);
+  const Shape sh = pick_shape(&nblk, 1, max_wg);
   const int64_t n_wg = (nblk + sh.bpw - 1) / sh.bpw;
   j.n_blocks = bhi;   // blocks beyond the range are skipped
   DecBatch B{};
@@ -1529,6 +1553,10 @@ int matvec_forward(const Blob& b, const void* x, int64_t T, const void* bias, vo
   if (!ws) return fail(EP_E_ARG, "null workspace");
   if (ws_bytes < matvec_workspace_bytes(b, T)) return fail(EP_E_WORKSPACE, "workspace too small");
   return matvec_launch(b, x, T, bias, y, (float*)(((uintptr_t)ws + 255) & ~uintptr_t(255)), stream);
+}
+
+int decompress_beside(const Blob& b, void* dst, ep_stream st, int64_t max_wg) {
+  return decode_one(b, dst, 0, b.n_chains, out_kind(b), (hipStream_t)st, max_wg);
 }
 
 // ---------------------------------------------------------------- the fused product without a workspace

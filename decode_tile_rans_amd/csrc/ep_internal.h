@@ -168,6 +168,9 @@ int matvec_batch_launch(const Blob* const* bs, int n, const void* x, int64_t T, 
 int matvec_launch(const Blob& b, const void* x, int64_t T, const void* bias, void* y, float* part, ep_stream st);
 int matvec_forward(const Blob& b, const void* x, int64_t T, const void* bias, void* y, void* ws, size_t ws_bytes,
                    ep_stream st);
+// Decode the whole blob with at most max_wg workgroups (one per CU): a launch that runs
+// beside another kernel which holds the other CUs.
+int decompress_beside(const Blob& b, void* dst, ep_stream st, int64_t max_wg);
 
 }  // namespace ep
 

@@ -305,6 +305,26 @@ int gemm_cu_count() {
   return v;
 }
 
+// Whether launch_gemm takes the 128-wide tiles for T x N (they fill the CUs' rounds much
+// better than 256-wide ones)
+bool gemm_narrow(int64_t T, int64_t N) {
+  const int64_t ntm = (T + GBM - 1) / GBM;
+  auto eff = [&](int64_t bn) {
+    const int64_t tiles = ntm * ((N + bn - 1) / bn);
+    const int64_t rounds = (tiles + 255) / 256;
+    return (double)(T * N) / (double)(rounds * 256 * GBM * bn);
+  };
+  bool narrow = eff(128) > 1.25 * eff(256);
+  if (const char* e = std::getenv("EP_GEMM_BN")) narrow = std::atoi(e) == 128;
+  return narrow;
+}
+
+// Workgroups (one per CU) of the BF16 GEMM for T x N when it takes one launch
+int64_t gemm_tiles(int64_t T, int64_t N) {
+  const int64_t ntm = (T + GBM - 1) / GBM;
+  return gemm_narrow(T, N) ? ntm * ((N + 127) / 128) : ntm * ((N + 255) / 256);
+}
+
 template <bool FP8>
 int launch_gemm(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K, float ax,
                 const float* aw, hipStream_t st) {
@@ -321,14 +341,7 @@ int launch_gemm(const void* x, const void* w, const void* bias, void* y, int64_t
       (aw && (rc = check_gpu_pointer(aw, "weight scales"))))
     return rc;
   const int64_t ntm = (T + GBM - 1) / GBM;
-  auto eff = [&](int64_t bn) {
-    const int64_t tiles = ntm * ((N + bn - 1) / bn);
-    const int64_t rounds = (tiles + 255) / 256;
-    return (double)(T * N) / (double)(rounds * 256 * GBM * bn);
-  };
-  bool narrow = eff(128) > 1.25 * eff(256);
-  if (const char* e = std::getenv("EP_GEMM_BN")) narrow = std::atoi(e) == 128;
-  if (narrow) return launch_tile<128, 3, 128, FP8>(x, w, bias, y, T, N, N, K, ax, aw, st);
+  if (gemm_narrow(T, N)) return launch_tile<128, 3, 128, FP8>(x, w, bias, y, T, N, N, K, ax, aw, st);
   // When the 256-wide tiles leave the last round of the CUs partly idle, the columns of
   // the whole rounds take 256-wide tiles and the rest 128-wide ones (a second launch of
   // about one round at roughly 0.6 of a 256-wide tile's time), e.g. 4096 x 14336: 768 +
@@ -455,11 +468,11 @@ size_t ep_linear_seq_workspace_bytes(const ep_blob* const* w, int n) {
 
 // Layers 0..n-1, each decode then GEMM.  The decode of layer i+1 runs on `side`, beside
 // the GEMM of layer i, only when that GEMM's tiles leave CUs idle for its whole run
-// (fewer tiles than CUs): a decode workgroup holds 56 KB of tables plus its chains'
-// rings and a GEMM workgroup 128-144 KB of LDS, so the two never share a CU, and when
-// the GEMM fills every CU a side-stream decode only takes CUs away from it (measured:
-// eight 4096-token layers 7 % slower than in order).  Otherwise the decode runs on
-// `main` right before its GEMM.  Two weight buffers alternate; a side-stream decode
+// (fewer tiles than CUs), and then on at most as many workgroups as there are idle CUs:
+// a decode workgroup holds 56 KB of tables plus its chains' rings and a GEMM workgroup
+// 128-144 KB of LDS, so the two never share a CU, and when the GEMM fills every CU a
+// side-stream decode only takes CUs away from it (measured: eight 4096-token layers 7 %
+// slower than in order).  Otherwise the decode runs on `main` right before its GEMM.  Two weight buffers alternate; a side-stream decode
 // into a buffer waits for the GEMM that last read it, a GEMM for its side-stream
 // decode.  The side stream starts after everything already queued on main.
 int ep_compressed_linear_seq_forward(const ep_blob* const* w, int n, const void* const* x, int64_t T,
@@ -489,9 +502,11 @@ int ep_compressed_linear_seq_forward(const ep_blob* const* w, int n, const void*
   for (int i = 0; i < n; ++i) mv[i] = use_matvec(w[i], T);
   const int64_t cus = gemm_cu_count();
   bool any_side = false;
+  std::vector<int64_t> free_cus(n, 0);
   for (int i = 1; i < n; ++i) {
-    const int64_t tiles = ((T + GBM - 1) / GBM) * ((w[i - 1]->b.R + 255) / 256);
+    const int64_t tiles = gemm_tiles(T, w[i - 1]->b.R);
     on_side[i] = !mv[i] && !mv[i - 1] && tiles < cus;
+    free_cus[i] = cus - tiles;
     any_side = any_side || on_side[i];
   }
   hipEvent_t ev_start = nullptr, ev_dec[2] = {nullptr, nullptr}, ev_used[2] = {nullptr, nullptr};
@@ -510,7 +525,9 @@ int ep_compressed_linear_seq_forward(const ep_blob* const* w, int n, const void*
   auto decode_side = [&](int i) {
     const int k = i & 1;
     if (i >= 2 && !rc) rc = hip_check(hipStreamWaitEvent(ss, ev_used[k], 0), "stream wait");
-    if (!rc) rc = ep_decompress(w[i], buf[k], side_s);
+    // on the CUs the GEMM leaves free (a decode workgroup queued behind a GEMM workgroup
+    // would only start when that GEMM ends)
+    if (!rc) rc = decompress_beside(w[i]->b, buf[k], side_s, free_cus[i]);
     if (!rc) rc = hip_check(hipEventRecord(ev_dec[k], ss), "event record");
   };
   for (int i = 0; i < n && !rc; ++i) {

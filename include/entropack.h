@@ -186,9 +186,9 @@ int ep_compressed_linear_forward(const ep_blob* w, const void* dev_x, int64_t T,
  * ([README] 快速开始 layer(x), applied layer after layer as a model runs them; [ABS]:
  * decoding cost grows with the weight count, so it should hide behind the GEMMs).
  * Each layer is decoded, then multiplied.  The decode of layer i+1 runs on `side`, beside
- * the GEMM of layer i on `main`, when that GEMM has fewer 256 x 256 output tiles than the
- * GPU has CUs (its workgroups leave CUs idle); otherwise it runs on `main` before its
- * GEMM (a decode workgroup cannot share a CU with a GEMM workgroup: their LDS needs add
+ * the GEMM of layer i on `main`, when that GEMM has fewer output tiles than the GPU has
+ * CUs (its workgroups leave CUs idle), on at most as many workgroups as there are idle
+ * CUs; otherwise it runs on `main` before its GEMM (a decode workgroup cannot share a CU with a GEMM workgroup: their LDS needs add
  * up to more than a CU holds, so a side-stream decode could only take CUs away from a
  * GEMM that fills them).  Two weight buffers in dev_ws (>= ep_linear_seq_workspace_bytes
  * bytes) alternate.  x[i] is T x cols_i, y[i] is T x rows_i, bias may be NULL or hold

@@ -139,6 +139,28 @@ def test_dit_block_parity_full(dit_block, index):
     _full_parity(handles[index], to_np(outs[index], nx.DT_BF16), nx.DT_BF16, f"stack matrix {index}")
 
 
+def test_dit_block_spread_launch_equal(dit_block):
+    """The block's launch (6300 blocks: more than one round of 256 CUs x 16 waves) with
+    its blocks spread evenly over the CUs (EP_DECODE_SPREAD=1, waves looping over their
+    share) writes the same bits as the default launch shape, which the parity tests
+    above compare with the oracle."""
+    import os
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    srcs, handles, outs = dit_block
+    outs2 = [torch.full(s.shape, 7.0, dtype=torch.bfloat16, device="cuda") for s in srcs]
+    os.environ["EP_DECODE_SPREAD"] = "1"
+    try:
+        L.ep_decompress_batch(handles, [o.data_ptr() for o in outs2], stream_ptr())
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("EP_DECODE_SPREAD", None)
+    for a, b in zip(outs, outs2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for h in handles:
+        assert L.ep_blob_device_errors(h) == 0
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("index", list(range(6)))
 def test_dit_extras_parity_full(dit_extras, index):
