@@ -78,7 +78,7 @@ int parse_tileans(Blob& b) {
   b.S = by[9];
   const int ndim = by[10];
   b.umask = by[11];
-  if (P != kP || by[12] != 12 || by[13] || by[14] || by[15] || rd<uint64_t>(by, 40) != 0)
+  if (P != kPBytes || by[12] != 12 || by[13] || by[14] || by[15] || rd<uint64_t>(by, 40) != 0)
     return fail(EP_E_CORRUPT, "bad header constants");
   if (b.E != 1 && b.E != 2 && b.E != 4 && b.E != 8) return fail(EP_E_CORRUPT, "bad element size");
   b.n_ctx = b.E < 4 ? b.E : 4;
@@ -105,7 +105,7 @@ int parse_tileans(Blob& b) {
   for (int c = 0; c < b.n_ctx; ++c) {
     int32_t sum = 0;
     if ((b.umask >> c) & 1) {
-      for (int v = 0; v < 256; ++v) b.LF[c][v] = kM / 256;
+      for (int v = 0; v < 256; ++v) b.LF[c][v] = kMBytes / 256;
       continue;
     }
     if (by.size() < off + 512) return fail(EP_E_CORRUPT, "blob truncated");
@@ -113,7 +113,7 @@ int parse_tileans(Blob& b) {
       b.LF[c][v] = rd<uint16_t>(by, off);
       sum += b.LF[c][v];
     }
-    if (sum != kM) return fail(EP_E_CORRUPT, "table does not sum to 2048");
+    if (sum != kMBytes) return fail(EP_E_CORRUPT, "table does not sum to 2048");
   }
   return parse_area(b, off);
 }
@@ -126,7 +126,7 @@ int parse_blob(std::vector<uint8_t>&& bytes, Blob* out) {
   if (by.size() < (size_t)kHeaderBytes) return fail(EP_E_CORRUPT, "blob truncated");
   if (std::memcmp(&by[0], "EPT1", 4) == 0) return parse_tileans(b);
   if (std::memcmp(&by[0], "EPK1", 4) != 0) return fail(EP_E_CORRUPT, "bad magic");
-  if (rd<uint16_t>(by, 4) != 2) return fail(EP_E_CORRUPT, "unsupported version");
+  if (rd<uint16_t>(by, 4) != 3) return fail(EP_E_CORRUPT, "unsupported version");
   b.dtype = by[6];
   int P = by[7];
   b.S = by[8];
@@ -140,10 +140,11 @@ int parse_blob(std::vector<uint8_t>&& bytes, Blob* out) {
   b.n_blocks = rd<uint32_t>(by, 28);
   b.n_words = rd<uint64_t>(by, 32);
   b.model_bytes = rd<uint32_t>(by, 40);
-  if (P != kP || tl != 12 || rd<uint32_t>(by, 44) != 0) return fail(EP_E_CORRUPT, "bad header constants");
+  if (tl != 12 || rd<uint32_t>(by, 44) != 0) return fail(EP_E_CORRUPT, "bad header constants");
   if (b.dtype < EP_BF16 || b.dtype > EP_INT8) return fail(EP_E_CORRUPT, "bad dtype");
   if (b.S < 1 || b.S > 64 || (b.S & (b.S - 1))) return fail(EP_E_CORRUPT, "bad chains per tile");
   if (b.k < 3 || b.k > 7 || b.flags > 3) return fail(EP_E_CORRUPT, "bad header fields");
+  if (P != precision(b.k)) return fail(EP_E_CORRUPT, "table precision does not match the escape threshold");
   if (b.R < 1 || b.C < 1) return fail(EP_E_CORRUPT, "bad shape");
   if (!(std::isfinite(b.delta) && b.delta > 0.f)) return fail(EP_E_CORRUPT, "bad resolution");
   b.off_scales = kHeaderBytes;

@@ -12,7 +12,7 @@
 //   * a workgroup of W waves stages the 7 decode tables (7 x 2048 packed u32 = 56 KB)
 //     into LDS once; every chain keeps a 64-byte ring of stream words in LDS, fed by
 //     16-byte loads issued two groups ahead of use;
-//   * per coordinate: one LDS table read, x = f (x >> 11) + bias (24-bit mad), a
+//   * per coordinate: one LDS table read, x = f (x >> P) + bias (24-bit mad), a
 //     16-bit renormalisation from a prefetched ring word, the doubled coordinate taken
 //     straight from the table entry (escapes: bypass bits, replayed on a careful path),
 //     h_r * u in fp32, container cast, one 16-byte store per 8-coordinate group (BF16);
@@ -24,6 +24,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
 
 #include "ep_internal.h"
 
@@ -50,8 +51,7 @@ constexpr int out_elem_bytes() {
   return (OUT == OUT_FP32 || OUT == OUT_COORDS) ? 4 : ((OUT == OUT_FP8 || OUT == OUT_INT8 || OUT == OUT_BYTES) ? 1 : 2);
 }
 
-constexpr int kTabWords = kNumCtx * kM;          // 14336 u32
-constexpr int kTabBytes = kTabWords * 4;         // 57344 B
+constexpr int kTabBytes = kNumCtx * kMMax * 4;   // 57344 B: LDS region of any table layout
 // packed table entry: f (bits 0..10) | bias (11..21) | value (22..30) | escape (31);
 // value = doubled coordinate u (signed 9 bit) or, for escapes, c | neg<<1 | top2<<2 | (e-k)<<4
 constexpr int kValShift = 22;
@@ -254,8 +254,8 @@ struct DecBatch {
 };
 
 // Entry layouts (chosen per blob when its tables are expanded):
-//   wide   (K = 128): f 0..10 | bias 11..21 | u or escape info 22..30 (9 bit) | escape 31
-//   narrow (K <= 64): f 0..10 | bias 11..21 | c 22 | escape 23 | u + 128 or escape info 24..31
+//   wide   (K >= 64): f 0..10 | bias 11..21 | u or escape info 22..30 (9 bit) | escape 31
+//   narrow (K <= 32): f 0..10 | bias 11..21 | c 22 | escape 23 | u + 128 or escape info 24..31
 // In both, bit 22 is the coset of a FIRST symbol.  The parity of floor(u/2) (bit 1 of u)
 // sits at bit 23 (wide) or 25 (narrow).
 template <bool NARROW>
@@ -284,6 +284,38 @@ struct EntryLayout {
       top2 = (int)((i >> 2) & 3u);
       er = (int)(i >> 4);
     }
+  }
+};
+
+// ---- table geometry of a kernel variant
+// Lossy blobs with escape threshold K <= 32 (narrow entries) use M = 1024 slots per table,
+// K >= 64 (wide entries) and TileANS byte tables 2048.  Narrow blobs without escapes get
+// split entries, two words per slot (build_split_tables); the others one packed word.
+// In LDS the 7 tables sit in the order FREE[0], FIRST, FREE[1], LAST[0][0..1],
+// LAST[1][0..1], one table every kTable bytes, so a LAST table is the FREE table of the
+// same coset plus 3 kTable plus kTable for parity 1.
+typedef __attribute__((ext_vector_type(2))) uint32_t EntPair;   // a split entry: value word, bias
+
+template <int OUT, bool ESC, bool NARROW>
+struct Geo {
+  static constexpr bool kSplit = NARROW && !ESC && OUT != OUT_BYTES;
+  static constexpr int kP = (NARROW && OUT != OUT_BYTES) ? 10 : 11;
+  static constexpr uint32_t kMask = (1u << kP) - 1u;
+  static constexpr int kTableLog2 = kP + (kSplit ? 3 : 2);          // bytes per table, log2
+  static constexpr uint32_t kTable = 1u << kTableLog2;
+  static constexpr uint32_t kFirstOff = kTable;
+  static constexpr uint32_t kLastOff = 3u * kTable;
+  using Ent = typename std::conditional<kSplit, EntPair, uint32_t>::type;
+  // the entry word holding the value (coset, parity and u + 128 or the wide value)
+  __device__ static uint32_t lo(Ent e) {
+    if constexpr (kSplit) return e.x;
+    else return e;
+  }
+  // FREE table of a FIRST entry's coset: 2 kTable c, the coset being bit 24 of a split
+  // entry and bit 22 of a packed one
+  __device__ static uint32_t free_base(uint32_t e_first) {
+    constexpr int cbit = kSplit ? 24 : 22;
+    return (e_first >> (cbit - (kTableLog2 + 1))) & (2u * kTable);
   }
 };
 
@@ -536,15 +568,22 @@ __device__ __forceinline__ void ch_renorm_all(Chain* rd) {
   }
 }
 // table entry of the chain's next symbol; `base` = byte offset of the table in LDS
-__device__ __forceinline__ uint32_t ch_entry(uint32_t base, const Chain& r) {
-  return ((const EP_LDS uint32_t*)(uintptr_t)base)[r.x & (kM - 1)];
+template <class G>
+__device__ __forceinline__ typename G::Ent ch_entry(uint32_t base, const Chain& r) {
+  if constexpr (G::kSplit) return ((const EP_LDS EntPair*)(uintptr_t)base)[r.x & G::kMask];
+  else return ((const EP_LDS uint32_t*)(uintptr_t)base)[r.x & G::kMask];
 }
 // x = f (x >> P) + (slot - cum)
-__device__ __forceinline__ void ch_decode(Chain& r, uint32_t e) {
-  r.x = __umul24(e & 2047u, r.x >> 11) + ((e >> 11) & 2047u);
+// (split entries: f alone in the low 24 bits of the first word, the bias alone in the
+// second, so the 24-bit multiply-add takes them as they are)
+template <class G>
+__device__ __forceinline__ void ch_decode(Chain& r, typename G::Ent e) {
+  if constexpr (G::kSplit) r.x = __umul24(e.x, r.x >> G::kP) + e.y;
+  else r.x = __umul24(e & 2047u, r.x >> G::kP) + ((e >> 11) & 2047u);
 }
-__device__ __forceinline__ void ch_advance(Chain& r, uint32_t e) {
-  ch_decode(r, e);
+template <class G>
+__device__ __forceinline__ void ch_advance(Chain& r, typename G::Ent e) {
+  ch_decode<G>(r, e);
   ch_renorm(r);
 }
 __device__ __forceinline__ uint32_t ch_bypass(Chain& r, int nb) {
@@ -567,33 +606,28 @@ __device__ __forceinline__ int32_t ch_escape(Chain& r, uint32_t e, int k, int la
   const int32_t uu = (int32_t)(2u * m + (uint32_t)c);
   return neg ? -uu : uu;
 }
-// Byte offsets of the tables in LDS (8 KB each): FREE[0] at 0, FIRST at 8 KB, FREE[1] at
-// 16 KB, LAST[c][pi] at (3 + 2c + pi) 8 KB = FREE[c] + 24 KB + pi 8 KB, so the LAST
-// address is the FREE address of the same state plus a constant and the parity bit.
-// The coset of a FIRST entry is bit 22 of every layout.
-constexpr uint32_t kFirstOff = 0x2000u;
-constexpr uint32_t kLastOff = 0x6000u;
-__device__ __forceinline__ uint32_t free_base(uint32_t e_first) { return (e_first >> 8) & 0x4000u; }
 // LDS table slot of stored table t (stored order FIRST, FREE[0], FREE[1], LAST...)
 __host__ __device__ constexpr int lds_table_slot(int t) { return t == 0 ? 1 : (t == 1 ? 0 : t); }
 // careful decode of one group (the chain's state is at the group's start and 24 words
 // are in its ring): FIRST, six FREE, LAST, escapes with their raw bits
-template <class LY>
+// (kernels for blobs with escapes: one packed word per slot)
+template <class LY, class G>
 __device__ __forceinline__ void ch_group_careful(uint32_t lds0, Chain& r, int k, int32_t* u) {
-  uint32_t ee = ch_entry(lds0 + kFirstOff, r);
-  ch_advance(r, ee);
-  const uint32_t fb = free_base(ee);
+  static_assert(!G::kSplit, "escapes take packed entries");
+  uint32_t ee = ch_entry<G>(lds0 + G::kFirstOff, r);
+  ch_advance<G>(r, ee);
+  const uint32_t fb = G::free_base(ee);
   u[0] = (ee & LY::kEsc) ? ch_escape<LY>(r, ee, k, 0, 0) : LY::u_of(ee);
   int pp = u[0] >> 1;
   for (int i = 1; i < 7; ++i) {
-    ee = ch_entry(lds0 + fb, r);
-    ch_advance(r, ee);
+    ee = ch_entry<G>(lds0 + fb, r);
+    ch_advance<G>(r, ee);
     u[i] = (ee & LY::kEsc) ? ch_escape<LY>(r, ee, k, 0, 0) : LY::u_of(ee);
     pp ^= u[i] >> 1;
   }
   const int pi = pp & 1;
-  ee = ch_entry(lds0 + fb + kLastOff + ((uint32_t)pi << 13), r);
-  ch_advance(r, ee);
+  ee = ch_entry<G>(lds0 + fb + G::kLastOff + ((uint32_t)pi << G::kTableLog2), r);
+  ch_advance<G>(r, ee);
   u[7] = (ee & LY::kEsc) ? ch_escape<LY>(r, ee, k, 1, pi) : LY::u_of(ee);
 }
 
@@ -603,8 +637,8 @@ __device__ __forceinline__ void ch_group_careful(uint32_t lds0, Chain& r, int k,
 // barrier; the first block's stream loads go out in between, so a starting workgroup
 // waits about one memory latency for both.
 struct TabStager {
-  static constexpr int kQ = kM / 4;   // uint4 per table
-  int kN;                             // uint4 to stage (at most kTabWords / 4)
+  int q;                              // uint4 per table
+  int kN;                             // uint4 to stage (at most kTabBytes / 16)
   const uint4* src;
   uint4* dst;
   int tid, nt;
@@ -620,7 +654,7 @@ struct TabStager {
       v[k] = src[i < kN ? i : kN - 1];
     }
   }
-  __device__ void put(int i, uint4 d) { dst[swap && i < 2 * kQ ? (i ^ kQ) : i] = d; }
+  __device__ void put(int i, uint4 d) { dst[swap && i < 2 * q ? (i ^ q) : i] = d; }
   __device__ void commit() {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -722,6 +756,7 @@ template <int OUT, bool ESC, bool C8, bool NARROW, int ILP, bool SEL>
 __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* rd, RowScale* rs, const int* ngr,
                                              const uint32_t* g0, char** optr, MvAcc* mv) {
   using LY = EntryLayout<NARROW>;
+  using G = Geo<OUT, ESC, NARROW>;
   const DecJob& J = *X.J;
   constexpr int NT = mv_tokens<OUT>();
   // fused product: this group's activation chunks are requested before its symbols are
@@ -754,11 +789,11 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t tb = X.lds0 + ((i & X.ctx_mask) << 13);
+      const uint32_t tb = X.lds0 + ((i & X.ctx_mask) << G::kTableLog2);
 #pragma unroll
-      for (int c = 0; c < ILP; ++c) e[c][i] = (int32_t)ch_entry(tb, rd[c]);
+      for (int c = 0; c < ILP; ++c) e[c][i] = (int32_t)ch_entry<G>(tb, rd[c]);
 #pragma unroll
-      for (int c = 0; c < ILP; ++c) ch_decode(rd[c], (uint32_t)e[c][i]);
+      for (int c = 0; c < ILP; ++c) ch_decode<G>(rd[c], (uint32_t)e[c][i]);
       ch_renorm_all<ILP, SEL>(rd);
     }
 #pragma unroll
@@ -782,41 +817,51 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
     return;
   }
   // ---- fast path: eight symbols per chain, no escape handling
+  // (e holds each entry's value word; a split entry's bias word is used by its decode
+  // step only)
   uint32_t xs[ILP], ras[ILP], nws[ILP];
   uint32_t e[ILP][8];
   uint32_t fbs[ILP];
+  typename G::Ent en[ILP];
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
     xs[c] = rd[c].x;
     ras[c] = rd[c].ra;
     nws[c] = rd[c].nw;
-    e[c][0] = ch_entry(X.lds0 + kFirstOff, rd[c]);
+    en[c] = ch_entry<G>(X.lds0 + G::kFirstOff, rd[c]);
   }
   // per step: every chain's table read, then every chain's state update, then the
   // renormalisations (whose ring reads are conditional and so end the step's LDS batch)
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
-    ch_decode(rd[c], e[c][0]);
-    fbs[c] = X.lds0 + free_base(e[c][0]);
+    ch_decode<G>(rd[c], en[c]);
+    e[c][0] = G::lo(en[c]);
+    fbs[c] = X.lds0 + G::free_base(e[c][0]);
   }
   ch_renorm_all<ILP, SEL>(rd);
 #pragma unroll
   for (int i = 1; i < 7; ++i) {
 #pragma unroll
-    for (int c = 0; c < ILP; ++c) e[c][i] = ch_entry(fbs[c], rd[c]);
+    for (int c = 0; c < ILP; ++c) en[c] = ch_entry<G>(fbs[c], rd[c]);
 #pragma unroll
-    for (int c = 0; c < ILP; ++c) ch_decode(rd[c], e[c][i]);
+    for (int c = 0; c < ILP; ++c) {
+      ch_decode<G>(rd[c], en[c]);
+      e[c][i] = G::lo(en[c]);
+    }
     ch_renorm_all<ILP, SEL>(rd);
   }
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
     // LAST[c][pi]: pi = parity of the seven floor(u/2), one bit of each entry
     const uint32_t par = xor3(xor3(e[c][1], e[c][2], e[c][3]), xor3(e[c][4], e[c][5], e[c][6]), e[c][0]);
-    const uint32_t lb = fbs[c] + kLastOff + (((par >> LY::kPar) & 1u) << 13);
-    e[c][7] = ch_entry(lb, rd[c]);
+    const uint32_t lb = fbs[c] + G::kLastOff + (((par >> LY::kPar) & 1u) << G::kTableLog2);
+    en[c] = ch_entry<G>(lb, rd[c]);
   }
 #pragma unroll
-  for (int c = 0; c < ILP; ++c) ch_decode(rd[c], e[c][7]);
+  for (int c = 0; c < ILP; ++c) {
+    ch_decode<G>(rd[c], en[c]);
+    e[c][7] = G::lo(en[c]);
+  }
   ch_renorm_all<ILP, SEL>(rd);
 
 #pragma unroll
@@ -829,7 +874,7 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
       if (OUT == OUT_COORDS) u[i] = LY::u_of(e[c][i]);
       else w[i] = LY::w_of(e[c][i], rs[c].h, rs[c].nh);
     }
-    if (ESC) {
+    if constexpr (ESC) {
       const uint32_t any = (e[c][0] | e[c][1] | e[c][2]) | (e[c][3] | e[c][4] | e[c][5]) | (e[c][6] | e[c][7]);
       const bool slow = act && (any & LY::kEsc) != 0;
       if (__ballot(slow) != 0) {
@@ -843,7 +888,7 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
         ch_sync(X.sref, rd[c], slow, 2 * 24);
         if (slow) {
           rd[c].nw = ch_word(rd[c]);
-          ch_group_careful<LY>(X.lds0, rd[c], J.k, u);
+          ch_group_careful<LY, G>(X.lds0, rd[c], J.k, u);
 #pragma unroll
           for (int i = 0; i < 8; ++i) w[i] = rs[c].h * (float)u[i];
         }
@@ -1111,6 +1156,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   st.tid = tid;
   st.nt = (int)blockDim.x;
   st.swap = OUT != OUT_BYTES;
+  st.q = (int)(Geo<OUT, ESC, NARROW>::kTable / 16);
   st.kN = (int)(J.tab_words / 4);
 
   GroupCtx X;
@@ -1252,7 +1298,7 @@ DecJob make_job(const Blob& b, void* out) {
   j.R = (uint32_t)b.R;
   j.ctx_mask = b.kind == kKindTileAns ? (uint32_t)(b.n_ctx - 1) : 0u;
   // TileANS stages only its contexts' tables
-  j.tab_words = b.kind == kKindTileAns ? (uint32_t)(b.n_ctx * kM) : (uint32_t)kTabWords;
+  j.tab_words = b.d_tab_words;
   return j;
 }
 
@@ -1382,7 +1428,7 @@ int decode_one(const Blob& b, void* dst, int64_t chain_lo, int64_t chain_hi, int
   B.j[0] = j;
   B.n = 1;
   B.bpw = sh.bpw;
-  return launch_any(out, (b.flags & kFlagEsc) != 0, (b.C % 8) == 0, b.k <= 6, sh, B, n_wg, st);
+  return launch_any(out, (b.flags & kFlagEsc) != 0, (b.C % 8) == 0, b.k <= 5, sh, B, n_wg, st);
 }
 
 // Sum of the fused product's partial sums of row r for activation row t, in a fixed
@@ -1504,7 +1550,7 @@ int matvec_batch_launch(const Blob* const* bs, int n, const void* x, int64_t T, 
     int idx[kMaxBatch];
     int m = 0;
     for (int i = 0; i <= n; ++i) {
-      if (i < n && (bs[i]->k <= 6) == narrow && ((bs[i]->flags & kFlagEsc) != 0) == pesc) idx[m++] = i;
+      if (i < n && (bs[i]->k <= 5) == narrow && ((bs[i]->flags & kFlagEsc) != 0) == pesc) idx[m++] = i;
       if (m == 0 || (m < kMaxBatch && i < n)) continue;
       DecBatch B{};
       B.n = m;
@@ -1618,8 +1664,14 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
   // the decoder addresses stream words with 32-bit indices
   if (b.n_words >= ((uint64_t)1 << 31)) return fail(EP_E_ARG, "stream too long for the device decoder (2^31 words)");
   auto al = [](size_t v) { return (v + 255) & ~size_t(255); };
+  // decode tables: TileANS byte tables; split entries (two words a slot) for lossy blobs
+  // with escape threshold <= 64 and no escape; packed entries otherwise (M slots a table)
+  const bool split = b.kind != kKindTileAns && b.k <= 5 && !(b.flags & kFlagEsc);
+  const int M = 1 << precision(b.k);
+  const size_t tab_words = b.kind == kKindTileAns ? (size_t)b.n_ctx * kMBytes
+                                                  : (size_t)kNumCtx * M * (split ? 2 : 1);
   const size_t o_tab = 0;
-  const size_t o_hr = o_tab + al(kTabBytes);
+  const size_t o_hr = o_tab + al(4 * tab_words);
   // the chain area as stored (block offsets, chunk counts, tail nibbles, states), each
   // section 256-byte aligned; the kernel derives every chain's offsets from it
   const size_t fw = b.S >= 8 ? 1 : 2, n_nib = ((size_t)b.n_chains + 1) / 2;
@@ -1639,7 +1691,8 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
   if (b.kind == kKindTileAns) {
     build_byte_tables(b.LF, b.n_ctx, (uint32_t*)&host[o_tab]);   // (no row scales: zeros)
   } else {
-    build_slot_tables(b.model, (uint32_t*)&host[o_tab], b.k <= 6);
+    if (split) build_split_tables(b.model, (uint32_t*)&host[o_tab]);
+    else build_slot_tables(b.model, (uint32_t*)&host[o_tab], b.k <= 5);
     half_scales(b, (float*)&host[o_hr]);
   }
   std::memcpy(&host[o_boff], &b.bytes[b.off_boff], 4 * (size_t)b.n_blocks);
@@ -1678,6 +1731,7 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
   (void)hipGetDevice(&b.device);
   b.d_base = d;
   b.d_bytes = total;
+  b.d_tab_words = (uint32_t)tab_words;
   return EP_OK;
 }
 
@@ -1740,7 +1794,7 @@ int ep_decompress_batch(const ep_blob* const* blobs, void* const* dsts, int n, e
     bool pc8 = true;
     for (int i = 0; i < n; ++i) {
       const Blob& b = blobs[i]->b;
-      if ((b.k <= 6) == narrow && ((b.flags & kFlagEsc) != 0) == pesc) {
+      if ((b.k <= 5) == narrow && ((b.flags & kFlagEsc) != 0) == pesc) {
         idx.push_back(i);
         pc8 &= (b.C % 8) == 0;
       }

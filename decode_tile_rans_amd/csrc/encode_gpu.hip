@@ -315,6 +315,7 @@ __global__ void encode_chains_kernel(const int32_t* u, int64_t n_groups, int S, 
   uint32_t x = kL;
   int n = 0;
   const int K = 1 << k;
+  const int P = k >= 6 ? 11 : 10;   // the table precision of escape threshold K (precision())
   for (int kk = ngr - 1; kk >= 0; --kk) {
     const int64_t g = (int64_t)kTileGroups * t + j + (int64_t)kk * S;
     cm::Sym sy[8];
@@ -343,11 +344,11 @@ __global__ void encode_chains_kernel(const int32_t* u, int64_t n_groups, int S, 
       }
       const uint32_t f = (uint32_t)F[sy[i].ctx * kHistIds + sy[i].id];
       const uint32_t cum = (uint32_t)CUM[sy[i].ctx * kHistIds + sy[i].id];
-      if ((uint64_t)x >= ((uint64_t)f << 21)) {
+      if ((uint64_t)x >= ((uint64_t)f << (32 - P))) {
         w[n++] = (uint16_t)(x & 0xFFFFu);
         x >>= 16;
       }
-      x = (x / f) * (uint32_t)kM + (x % f) + cum;
+      x = (x / f) * (1u << P) + (x % f) + cum;
     }
     cons[ch * steps + kk] = (uint8_t)(n - n0);
     slow[ch * steps + kk] = esc ? 1 : 0;
@@ -657,7 +658,7 @@ int compress_device(const void* dsrc, int dtype, int64_t R, int64_t C, double t,
     for (int ctx = 0; ctx < kNumCtx; ++ctx)
       for (int id = 0; id < kHistIds; ++id) {
         const int64_t c = (int64_t)hist[(size_t)(ctx * kHistIds + id)];
-        if (c) est += c * ((int64_t)kP * 65536 - lq[m.F[ctx][id]]);
+        if (c) est += c * ((int64_t)m.P * 65536 - lq[m.F[ctx][id]]);
       }
     return {est, k};
   };
@@ -823,9 +824,9 @@ int compress_device(const void* dsrc, int dtype, int64_t R, int64_t C, double t,
   if ((rc = hc(hipMemcpyAsync(&b[off_stream], d_stream.p, 2 * (size_t)n_words, hipMemcpyDeviceToHost, st), "copy")))
     return rc;
   std::memcpy(&b[0], "EPK1", 4);
-  put16(b, 4, 2);
+  put16(b, 4, 3);
   b[6] = (uint8_t)dtype;
-  b[7] = (uint8_t)kP;
+  b[7] = (uint8_t)precision(k);
   b[8] = (uint8_t)S;
   b[9] = (uint8_t)k;
   b[10] = (uint8_t)((any_esc ? kFlagEsc : 0) | (sat ? kFlagSat : 0));

@@ -154,7 +154,7 @@ Estimate estimate(const Matrix& mx, const std::vector<int64_t>& rows, float delt
     symbolize(&u[gi * 8], k, s, ms);
     for (int i = 0; i < 8; ++i) {
       int32_t f = m.F[s[i].ctx][s[i].id];
-      est += (int64_t)kP * 65536 - lq[f];
+      est += (int64_t)m.P * 65536 - lq[f];
       est += (int64_t)65536 * s[i].rawbits;
     }
   }
@@ -200,8 +200,9 @@ void encode_chain(const int32_t* u_all, const Model& m, int64_t t, int j, int S,
       if (rb > 0) bypass(s[i].rawval & 0xFFFFu, std::min(rb, 16));
       uint64_t f = (uint64_t)m.F[s[i].ctx][s[i].id];
       uint64_t cum = (uint64_t)m.CUM[s[i].ctx][s[i].id];
-      if (x >= (f << 21)) emit();
-      x = (x / f) * (uint64_t)kM + (x % f) + cum;
+      // before a step x stays below f (L / M) 2^16 = f << (32 - P)
+      if (x >= (f << (32 - m.P))) emit();
+      x = (x / f) * (uint64_t)m.M + (x % f) + cum;
     }
     out->cons[kk] = (uint8_t)(w.size() - w0);
   }
@@ -366,11 +367,11 @@ void encode_chain_bytes(const uint8_t* by, const int32_t (*F)[256], const int32_
       const int ctx = i % n_ctx;
       const uint8_t v = by[g * 8 + i];
       const uint64_t f = (uint64_t)F[ctx][v], cum = (uint64_t)CUM[ctx][v];
-      if (x >= (f << 21)) {
+      if (x >= (f << (32 - kPBytes))) {
         w.push_back((uint16_t)(x & 0xFFFFu));
         x >>= 16;
       }
-      x = (x / f) * (uint64_t)kM + (x % f) + cum;
+      x = (x / f) * (uint64_t)kMBytes + (x % f) + cum;
     }
     out->cons[kk] = (uint8_t)(w.size() - w0);
   }
@@ -650,9 +651,9 @@ int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_r
     return fail(EP_E_NOMEM, "out of host memory");
   }
   std::memcpy(&b[0], "EPK1", 4);
-  put_u16(b, 4, 2);
+  put_u16(b, 4, 3);
   b[6] = (uint8_t)dtype;
-  b[7] = (uint8_t)kP;
+  b[7] = (uint8_t)precision(k);
   b[8] = (uint8_t)S;
   b[9] = (uint8_t)k;
   b[10] = (uint8_t)((any_esc ? kFlagEsc : 0) | (sat ? kFlagSat : 0));
@@ -718,16 +719,16 @@ int compress_lossless(const void* src, int64_t n_bytes, int E, const int64_t* di
       for (auto& p : part) cnt[v] += p[(size_t)(c * 256 + v)];
     }
     int32_t f[256];
-    quantize_freqs(cnt, 256, kM, f);
+    quantize_freqs(cnt, 256, kMBytes, f);
     // coded estimate (plus the stored table's 4096 bits) against 8 raw bits a byte
     __int128 coded = (__int128)256 * 16 * 65536, raw = 0;
     for (int v = 0; v < 256; ++v) {
-      if (cnt[v] > 0) coded += (__int128)cnt[v] * (kP * 65536 - lq[f[v]]);
+      if (cnt[v] > 0) coded += (__int128)cnt[v] * (kPBytes * 65536 - lq[f[v]]);
       raw += (__int128)cnt[v] * 8 * 65536;
     }
     if (coded >= raw) {
       umask |= 1 << c;
-      for (int v = 0; v < 256; ++v) F[c][v] = kM / 256;
+      for (int v = 0; v < 256; ++v) F[c][v] = kMBytes / 256;
     } else {
       for (int v = 0; v < 256; ++v) F[c][v] = f[v];
     }
@@ -768,7 +769,7 @@ int compress_lossless(const void* src, int64_t n_bytes, int E, const int64_t* di
   put_u16(b, 4, 1);
   b[6] = (uint8_t)tag;
   b[7] = (uint8_t)E;
-  b[8] = (uint8_t)kP;
+  b[8] = (uint8_t)kPBytes;
   b[9] = (uint8_t)S;
   b[10] = (uint8_t)ndim;
   b[11] = (uint8_t)umask;

@@ -3,7 +3,8 @@
 //
 // Format constants (this project's reading of the pages; see include/entropack.h
 // for the page keys):
-//   P = 11 (2048 slots per table), 32-bit rANS state in [2^16, 2^32), 16-bit words;
+//   M = 2^P slots per table, P = 10 when the escape threshold K = 2^k is at most 32 and
+//   P = 11 when K >= 64; 32-bit rANS state in [2^16, 2^32), 16-bit words;
 //   tiles of 512 groups x 8 columns (4096 coordinates), S chains per tile, chain j
 //   decodes the tile's groups j, j+S, ...; a block of 64 chains stores its tiles'
 //   8-word chunks in the order the decoder requests them, then the chains' short
@@ -20,9 +21,13 @@
 
 namespace ep {
 
-constexpr int kP = 11;
-constexpr int kM = 1 << kP;          // 2048
-constexpr int kHalf = kM >> 1;       // 1024
+constexpr int kPMax = 11;
+constexpr int kMMax = 1 << kPMax;    // the largest tables: 2048 slots
+// table precision of a lossy blob with escape threshold 2^k
+inline int precision(int k) { return k >= 6 ? 11 : 10; }
+// TileANS byte tables: P = 11
+constexpr int kPBytes = 11;
+constexpr int kMBytes = 1 << kPBytes;
 constexpr int kNumCtx = 7;
 constexpr int kIdSpace = 1024;
 constexpr int kMaxE = 28;
@@ -46,8 +51,9 @@ void quantize_freqs(const int64_t* w, int n, int total, int32_t* f_out);
 struct Model {
   int k = 3;
   int nm = 0;
+  int P = 10, M = 1024;                // table precision and slots (precision(k))
   int w[2] = {0, 0};
-  std::vector<int32_t> g[2];           // magnitude frequencies (sum 1024)
+  std::vector<int32_t> g[2];           // magnitude frequencies (sum M / 2)
   int32_t F[kNumCtx][kIdSpace];        // frequency per symbol id
   int32_t CUM[kNumCtx][kIdSpace];      // first slot per symbol id
   bool last_ok(int c, int pi, int sid) const;
@@ -58,21 +64,26 @@ struct Model {
 
 Model build_model(int k, const int64_t coset_counts[2], const int64_t* mag0, const int64_t* mag1);
 
-extern const int32_t* log2q_table();   // floor(2^16 log2 f + 1/2), f in [0, 2048]
+extern const int32_t* log2q_table();   // floor(2^16 log2 f + 1/2), f in [0, 2048] (any precision)
 
-// Packed decode-table entry (device tables, one u32 per slot):
-//   bits  0..10  f      (1..2047)
+// Packed decode-table entry (device tables, one u32 per slot, M slots per table):
+//   bits  0..10  f      (1..M-1)
 //   bits 11..21  bias   (slot - cum)
-//   wide layout (K = 128):
+//   wide layout (K >= 64):
 //     bits 22..30  direct symbol: doubled coordinate u (signed 9 bit; bit 22 = coset,
 //                  bit 23 = parity of floor(u/2)); escape: c | neg<<1 | top2<<2 | (e-k)<<4
 //     bit  31      escape (bucket symbol: raw bits follow)
-//   narrow layout (K <= 64, |u| <= 127):
+//   narrow layout (K <= 32, |u| <= 127):
 //     bit 22 coset, bit 23 escape, bits 24..31 u + 128 (direct) or
 //     neg | top2<<1 | (e-k)<<3 (escape)
-void build_slot_tables(const Model& m, uint32_t* out /* 7*2048 */, bool narrow);
+void build_slot_tables(const Model& m, uint32_t* out /* 7*M */, bool narrow);
+// Split entries for narrow blobs without escapes (two u32 per slot, 7*M pairs): the
+// first holds f in bits 0..9 (bits 10..23 zero, so a 24-bit multiply takes it as is)
+// and u + 128 in bits 24..31 (bit 24 = coset, bit 25 = parity of floor(u/2)), the
+// second the bias alone, so that x' = f (x >> P) + bias needs no field extraction.
+void build_split_tables(const Model& m, uint32_t* out /* 2*7*M */);
 // TileANS entries: f | bias << 11 | byte << 24, one 2048-slot table per context
-void build_byte_tables(const int32_t (*F)[256], int n_ctx, uint32_t* out /* n_ctx*2048 */);
+void build_byte_tables(const int32_t (*F)[256], int n_ctx, uint32_t* out /* n_ctx*kMBytes */);
 
 // Squared error of the lattice reconstruction fl32(h_r u) against the input, and the
 // input's squared norm (both over all rows x cols entries).
@@ -106,7 +117,7 @@ struct Blob {
   // TileANS only
   int E = 0, n_ctx = 0, umask = 0;
   std::vector<int64_t> dims;
-  int32_t LF[4][256];                  // per-context byte frequencies (sum 2048)
+  int32_t LF[4][256];                  // per-context byte frequencies (sum kMBytes)
   float delta = 0.f;
   int64_t n_tiles = 0, n_blocks = 0, n_chains = 0;
   uint64_t n_words = 0;
@@ -121,12 +132,13 @@ struct Blob {
   void* d_base = nullptr;              // one allocation
   const uint16_t* d_stream = nullptr;
   size_t d_bytes = 0;                  // size of the device allocation
+  uint32_t d_tab_words = 0;            // u32 words of its decode tables
   const uint32_t* d_boff = nullptr;    // the stored chain area: block offsets (u32),
   const void* d_full = nullptr;        //   full chunks per chain (u8 at S >= 8, else u16),
   const uint8_t* d_nib = nullptr;      //   tail nibbles,
   const uint32_t* d_states = nullptr;  //   initial states
   const float* d_hr = nullptr;         // per-row half scales h_r
-  const uint32_t* d_tab = nullptr;     // 7 x 2048 packed entries
+  const uint32_t* d_tab = nullptr;     // decode tables (build_slot_tables / build_split_tables)
   uint32_t* d_err = nullptr;
   int64_t n_groups() const { return R * ((C + 7) / 8); }
 };

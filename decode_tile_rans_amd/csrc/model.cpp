@@ -6,13 +6,13 @@
 // m = (|u| - c)/2 and a sign.  Magnitudes below K = 2^k are direct symbols; larger ones
 // are log-buckets (4 per octave) with e-2 raw bits.  Signed symbol sid = 2 msym + neg.
 //
-// Seven tables of 2048 slots:
+// Seven tables of M = 2^P slots (P = precision(k)):
 //   FIRST        coordinate 0, joint (c, sid), id = 512 c + sid
 //   FREE[c]      coordinates 1..6 (signs share a magnitude's probability evenly)
 //   LAST[c][pi]  coordinate 7, pi = parity of sum_{i<7} floor(u_i / 2); E8 fixes the
 //                parity of floor(u_7 / 2), so only agreeing direct symbols remain and
 //                buckets send one raw bit fewer.
-// Stored: coset weights (sum 2048) and per-coset magnitude frequencies (sum 1024);
+// Stored: coset weights (sum M) and per-coset magnitude frequencies (sum M / 2);
 // FIRST and LAST are derived with the quantiser Q below.
 #include <algorithm>
 #include <cmath>
@@ -124,7 +124,7 @@ void Model::derive() {
         wts.push_back(int64_t(w[c]) * freeF[c][s]);
       }
     std::vector<int32_t> f(ids.size());
-    quantize_freqs(wts.data(), (int)ids.size(), kM, f.data());
+    quantize_freqs(wts.data(), (int)ids.size(), M, f.data());
     for (size_t i = 0; i < ids.size(); ++i) F[0][ids[i]] = f[i];
   }
   for (int c = 0; c < 2; ++c)
@@ -137,7 +137,7 @@ void Model::derive() {
           wts.push_back(freeF[c][s]);
         }
       std::vector<int32_t> f(ids.size());
-      quantize_freqs(wts.data(), (int)ids.size(), kM, f.data());
+      quantize_freqs(wts.data(), (int)ids.size(), M, f.data());
       for (size_t i = 0; i < ids.size(); ++i) F[3 + 2 * c + pi][ids[i]] = f[i];
     }
   for (int t = 0; t < kNumCtx; ++t) {
@@ -200,6 +200,8 @@ bool Model::from_bytes(const uint8_t* p, size_t n, int k, Model* out, std::strin
   Model m;
   m.k = k;
   m.nm = n_msym(k);
+  m.P = precision(k);
+  m.M = 1 << m.P;
   uint32_t w1 = br.get(11);
   for (int c = 0; c < 2; ++c) {
     uint32_t n_mag = br.get(8);
@@ -215,12 +217,12 @@ bool Model::from_bytes(const uint8_t* p, size_t n, int k, Model* out, std::strin
       s += m.g[c][i];
       npres += m.g[c][i] > 0;
     }
-    if (!br.ok || s != kHalf || npres < 2) {
+    if (!br.ok || s != m.M / 2 || npres < 2) {
       *err = "bad magnitude frequencies";
       return false;
     }
   }
-  if (w1 < 1 || w1 > uint32_t(kM - 1)) {
+  if (w1 < 1 || w1 > uint32_t(m.M - 1)) {
     *err = "bad coset weight";
     return false;
   }
@@ -228,7 +230,7 @@ bool Model::from_bytes(const uint8_t* p, size_t n, int k, Model* out, std::strin
     *err = "model has trailing bytes";
     return false;
   }
-  m.w[0] = kM - (int)w1;
+  m.w[0] = m.M - (int)w1;
   m.w[1] = (int)w1;
   m.derive();
   *out = m;
@@ -239,23 +241,25 @@ Model build_model(int k, const int64_t cc[2], const int64_t* mag0, const int64_t
   Model m;
   m.k = k;
   m.nm = n_msym(k);
+  m.P = precision(k);
+  m.M = 1 << m.P;
   int32_t wq[2];
-  quantize_freqs(cc, 2, kM, wq);
+  quantize_freqs(cc, 2, m.M, wq);
   m.w[0] = wq[0];
   m.w[1] = wq[1];
   for (int c = 0; c < 2; ++c) {
     m.g[c].assign(m.nm, 0);
-    quantize_freqs(c == 0 ? mag0 : mag1, m.nm, kHalf, m.g[c].data());
+    quantize_freqs(c == 0 ? mag0 : mag1, m.nm, m.M / 2, m.g[c].data());
   }
   m.derive();
   return m;
 }
 
 const int32_t* log2q_table() {
-  static int32_t t[kM + 1] = {0};
+  static int32_t t[kMMax + 1] = {0};
   static bool init = false;
   if (!init) {
-    for (int f = 1; f <= kM; ++f) t[f] = (int32_t)std::floor(65536.0 * std::log2((double)f) + 0.5);
+    for (int f = 1; f <= kMMax; ++f) t[f] = (int32_t)std::floor(65536.0 * std::log2((double)f) + 0.5);
     init = true;
   }
   return t;
@@ -289,7 +293,28 @@ void build_slot_tables(const Model& m, uint32_t* out, bool narrow) {
       int32_t cum = m.CUM[t][id];
       for (int s = cum; s < cum + f; ++s) {
         uint32_t bias = uint32_t(s - cum);
-        out[t * kM + s] = uint32_t(f) | (bias << 11) | (hi << 22);
+        out[t * m.M + s] = uint32_t(f) | (bias << 11) | (hi << 22);
+      }
+    }
+  }
+}
+
+void build_split_tables(const Model& m, uint32_t* out) {
+  const int K = 1 << m.k;
+  for (int t = 0; t < kNumCtx; ++t) {
+    for (int id = 0; id < kIdSpace; ++id) {
+      const int32_t f = m.F[t][id];
+      if (f <= 0) continue;
+      const int c = t == 0 ? id >> 9 : ((t == 1 || t == 3 || t == 4) ? 0 : 1);
+      const int sid = t == 0 ? id & 511 : id;
+      const int msym = sid >> 1, neg = sid & 1;
+      // (blobs without escapes: every symbol is direct, msym < K)
+      int u = msym < K ? 2 * msym + c : 0;
+      if (neg) u = -u;
+      const int32_t cum = m.CUM[t][id];
+      for (int s = cum; s < cum + f; ++s) {
+        out[2 * (t * m.M + s)] = uint32_t(f) | (uint32_t(u + 128) << 24);
+        out[2 * (t * m.M + s) + 1] = uint32_t(s - cum);
       }
     }
   }
@@ -300,7 +325,7 @@ void build_byte_tables(const int32_t (*F)[256], int n_ctx, uint32_t* out) {
     int32_t cum = 0;
     for (int v = 0; v < 256; ++v) {
       for (int32_t q = 0; q < F[c][v]; ++q)
-        out[c * kM + cum + q] = uint32_t(F[c][v]) | (uint32_t(q) << 11) | (uint32_t(v) << 24);
+        out[c * kMBytes + cum + q] = uint32_t(F[c][v]) | (uint32_t(q) << 11) | (uint32_t(v) << 24);
       cum += F[c][v];
     }
   }

@@ -1,4 +1,4 @@
-"""Compress / decode and the blob v2 byte layout (oracle).
+"""Compress / decode and the blob v3 byte layout (oracle).
 
 [README] quick start: ``compress(tensor, config)`` / ``decompress`` restore
 shape and dtype; ``target_bpp`` is finite in [0.001, 11] and may be
@@ -6,9 +6,9 @@ non-integer; ``actual_bpp`` includes the metadata.  [NEWS]: lossy mode is for
 2-D floating and integer tensors only.  [ABS]/[SUM]: tiles are independently
 decodable and rANS-coded.
 
-Blob v2 (little-endian, packed, this project's format):
+Blob v3 (little-endian, packed, this project's format):
 
-  header (48 B)   'EPK1' | u16 version=2 | u8 dtype | u8 P=11 | u8 S | u8 k |
+  header (48 B)   'EPK1' | u16 version=3 | u8 dtype | u8 P | u8 S | u8 k |
                   u8 flags (bit0: some escape, bit1: some value needs clamping)
                   | u8 tile_log2=12 | u32 R | u32 C | f32 delta | u32 n_tiles |
                   u32 n_blocks | u64 n_words | u32 model_bytes | u32 0
@@ -43,13 +43,13 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import numerics as nx
-from .model import Model, group_symbols, count_symbols, build_model, n_msym
+from .model import Model, group_symbols, count_symbols, build_model, n_msym, precision
 from .rans import encode_chains, ChainDecoder, L
 from .layout import CHUNK, TileSchedule, request_ranks, block_geometry, build_stream
 from .rate import row_scales_bf16, half_steps, quantize_rows, select_delta
 
 MAGIC = b"EPK1"
-VERSION = 2
+VERSION = 3
 HEADER = struct.Struct("<4sHBBBBBBIIfIIQII")
 assert HEADER.size == 48
 TILE_LOG2 = 12
@@ -125,7 +125,7 @@ class Blob:
         return -(-self.n_chains // BLOCK_CHAINS)
 
     def to_bytes(self) -> bytes:
-        hdr = HEADER.pack(MAGIC, VERSION, self.dtype, 11, self.S, self.k, self.flags, TILE_LOG2,
+        hdr = HEADER.pack(MAGIC, VERSION, self.dtype, precision(self.k), self.S, self.k, self.flags, TILE_LOG2,
                           self.R, self.C, float(self.delta), self.n_tiles, self.n_blocks,
                           len(self.stream), len(self.model_bytes), 0)
         lens = self.chain_lens.astype(np.int64)
@@ -147,7 +147,7 @@ def chain_group_counts(n_groups: int, S: int, n_tiles: int):
 
 
 def compress(src, dtype: int, target_bpp: float, chains_per_tile=None, trace=None) -> bytes:
-    """Compress a 2-D container array (BF16/FP8 as bit patterns) to blob v2 bytes."""
+    """Compress a 2-D container array (BF16/FP8 as bit patterns) to blob v3 bytes."""
     src = np.asarray(src)
     validate(src.shape, dtype, target_bpp)
     R, C = src.shape
@@ -199,10 +199,12 @@ def parse_blob(buf: bytes) -> Blob:
         raise ValueError("blob truncated")
     (magic, ver, dtype, p, S, k, flags, tl, R, C, delta, n_tiles, n_blocks, n_words, mb, z) = \
         HEADER.unpack_from(buf, 0)
-    if magic != MAGIC or ver != VERSION or p != 11 or tl != TILE_LOG2 or z != 0:
+    if magic != MAGIC or ver != VERSION or tl != TILE_LOG2 or z != 0:
         raise ValueError("bad header")
     if dtype not in nx.DTYPES or S not in (1, 2, 4, 8, 16, 32, 64) or not (3 <= k <= 7) or flags > 3:
         raise ValueError("bad header fields")
+    if p != precision(k):
+        raise ValueError("table precision does not match the escape threshold")
     if R < 1 or C < 1:
         raise ValueError("bad shape")
     n_groups = R * (-(-C // 8))

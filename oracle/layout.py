@@ -1,4 +1,4 @@
-"""Stream layout of blob v2: where every chain's words sit (oracle).
+"""Stream layout of blob v3 (unchanged since v2): where every chain's words sit (oracle).
 
 [ABS] / [SUM] say only that the coordinates are rANS-coded in independently
 decodable tiles.  How the words sit in memory is this project's format,

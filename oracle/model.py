@@ -13,7 +13,7 @@ msym = K + 4 (e - k) + ((m >> (e-2)) & 3) with e = floor(log2 m), and the
 remaining e - 2 low bits of m travel raw (bypass-coded).  The signed symbol is
 sid = 2 msym + neg (c = 0, m = 0 has no sign: sid = 0).
 
-Contexts (7 tables of 2^P = 2048 slots):
+Contexts (7 tables of M = 2^P slots; P = 10 when K <= 32, P = 11 when K >= 64):
   0          FIRST      coordinate 0, joint over (c, sid): id = 512 c + sid
   1 + c      FREE[c]    coordinates 1..6
   3 + 2c + pi  LAST[c][pi] coordinate 7, where pi = parity of sum_{i<7} floor(u_i/2).
@@ -22,8 +22,8 @@ floor(u_7/2) has parity pi: LAST only holds the direct symbols that agree with
 it, and for bucket symbols one raw bit fewer is sent (its low bit is implied:
 rho = pi for c = 0, rho = pi xor neg for c = 1).
 
-Stored model: coset weights w = Q([n(0), n(1)], 2048) and per-coset magnitude
-frequencies g_c = Q(n_c(msym), 1024).  FREE[c] gives each sign half of the
+Stored model: coset weights w = Q([n(0), n(1)], M) and per-coset magnitude
+frequencies g_c = Q(n_c(msym), M / 2).  FREE[c] gives each sign half of the
 magnitude's probability (the zero of coset 0 gets 2 g_0(0)), so signs cost
 exactly one bit.  FIRST and LAST are derived from the stored model with Q.
 
@@ -36,12 +36,21 @@ from __future__ import annotations
 import math
 import numpy as np
 
-P = 11
-M = 1 << P            # 2048 slots per table
-HALF = M >> 1         # magnitude-frequency total
+P_MAX = 11
+M_MAX = 1 << P_MAX    # the largest table: 2048 slots
 N_CTX = 7
 ID_SPACE = 1024       # ids per table (FIRST uses 512 c + sid)
 MAX_E = 28            # |u| < 2^30  ->  m < 2^29  ->  e <= 28
+
+
+def precision(k: int) -> int:
+    """Table precision P (M = 2^P slots) for escape threshold K = 2^k: 10 for K <= 32,
+    11 for K >= 64.  (This project's reading -- the pages fix no table size.  On
+    row-scaled Gaussian weights, 1024 slots cost, counting both the longer code and
+    the coarser resolution the rate search then settles on, about 0.005 bit a
+    coordinate at K = 16, 0.01 at K = 32, 0.02-0.03 at K = 64 and 0.1 at K = 128;
+    the two larger alphabets keep 2048 slots.)"""
+    return 11 if k >= 6 else 10
 
 
 def n_msym(k: int) -> int:
@@ -147,7 +156,9 @@ class Model:
         self.k = k
         self.K = 1 << k
         self.nm = n_msym(k)
-        self.w = np.array([M - w1, w1], dtype=np.int64)
+        self.P = precision(k)
+        self.M = 1 << self.P
+        self.w = np.array([self.M - w1, w1], dtype=np.int64)
         self.g = [np.zeros(self.nm, dtype=np.int64), np.zeros(self.nm, dtype=np.int64)]
         self.g[0][:len(g0)] = g0
         self.g[1][:len(g1)] = g1
@@ -190,17 +201,17 @@ class Model:
                     continue
                 ids.append(512 * c + sid)
                 wts.append(int(self.w[c]) * int(free[c][sid]))
-        F[0, ids] = quantize_freqs(wts, ids, M)
+        F[0, ids] = quantize_freqs(wts, ids, self.M)
         # LAST[c][pi]
         for c in (0, 1):
             for pi in (0, 1):
                 alph = self.last_alphabet(c, pi)
-                F[3 + 2 * c + pi, alph] = quantize_freqs(free[c][alph], alph, M)
+                F[3 + 2 * c + pi, alph] = quantize_freqs(free[c][alph], alph, self.M)
         self.F = F
         self.CUM = np.zeros_like(F)
         self.CUM[:, 1:] = np.cumsum(F, axis=1)[:, :-1]
         # slot -> id (the plain definition of the rANS symbol lookup)
-        self.SLOT2ID = np.zeros((N_CTX, M), dtype=np.int64)
+        self.SLOT2ID = np.zeros((N_CTX, self.M), dtype=np.int64)
         for t in range(N_CTX):
             self.SLOT2ID[t] = np.repeat(np.arange(ID_SPACE), F[t])
 
@@ -248,10 +259,11 @@ class Model:
             if n_mag > n_msym(k) or n_mag < 1:
                 raise ValueError("bad magnitude alphabet size")
             gs.append(np.array([get(10) for _ in range(n_mag)], dtype=np.int64))
+        M = 1 << precision(k)
         if not (1 <= w1 <= M - 1):
             raise ValueError("bad coset weight")
         for g in gs:
-            if int(g.sum()) != HALF or (g > 0).sum() < 2:
+            if int(g.sum()) != M // 2 or (g > 0).sum() < 2:
                 raise ValueError("bad magnitude frequencies")
         if (len(buf) * 8 - pos[0]) >= 8:
             raise ValueError("model has trailing bytes")
@@ -260,9 +272,10 @@ class Model:
 
 def build_model(k: int, coset_counts, mag_counts0, mag_counts1) -> Model:
     nm = n_msym(k)
+    M = 1 << precision(k)
     w = quantize_freqs(coset_counts, [0, 1], M)
-    g0 = quantize_freqs(mag_counts0[:nm], np.arange(nm), HALF)
-    g1 = quantize_freqs(mag_counts1[:nm], np.arange(nm), HALF)
+    g0 = quantize_freqs(mag_counts0[:nm], np.arange(nm), M // 2)
+    g1 = quantize_freqs(mag_counts1[:nm], np.arange(nm), M // 2)
     return Model(k, int(w[1]), g0, g1)
 
 
@@ -333,8 +346,8 @@ def choose_k(mags: np.ndarray) -> int:
 # ---------------------------------------------------------------- cost table
 def log2q_table() -> np.ndarray:
     """LOG2Q[f] = floor(2^16 log2 f + 1/2) for f in [1, 2048] (index 0 unused)."""
-    t = np.zeros(M + 1, dtype=np.int64)
-    for f in range(1, M + 1):
+    t = np.zeros(M_MAX + 1, dtype=np.int64)
+    for f in range(1, M_MAX + 1):
         t[f] = int(math.floor(65536.0 * math.log2(f) + 0.5))
     return t
 
@@ -346,4 +359,4 @@ def est_bits_q16(sym, model: Model) -> int:
     """Estimated code length in units of 2^-16 bit: sum of (P - log2 f) + raw bits."""
     f = model.F[sym["ctx"], sym["id"]]
     assert (f > 0).all()
-    return int((P * 65536 - LOG2Q[f]).sum()) + 65536 * int(sym["rawbits"].sum())
+    return int((model.P * 65536 - LOG2Q[f]).sum()) + 65536 * int(sym["rawbits"].sum())

@@ -3,7 +3,7 @@
 [SUM]: the final coordinates are coded with rANS in independently decodable
 tiles; [ABS]: "entropy-coded in independently decodable tiles".  Parameters
 (pages silent; ours): 32-bit state x in [L, 2^32) with L = 2^16, 16-bit
-words, P = 11 (M = 2048 slots).  Reference: J. Duda, "Asymmetric numeral
+words, M = 2^P slots per table (P = 10 or 11, ``model.precision``).  Reference: J. Duda, "Asymmetric numeral
 systems" (arXiv 1311.2540), range variant.
 
 Decoding one symbol of table T:
@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .model import P, M, Model
+from .model import Model
 
 L = 1 << 16
 WORD = 16
@@ -95,9 +95,10 @@ def encode_chains(sym, model: Model, chain_groups):
             f = F[ctx, ids].astype(np.uint64)
             cum = CUM[ctx, ids].astype(np.uint64)
             assert (f > 0).all()
-            emit(idx, x[idx] >= np.left_shift(f, np.uint64(21)))
+            # the encoder keeps x below f * (L / M) * 2^16 = f << (32 - P) before a step
+            emit(idx, x[idx] >= np.left_shift(f, np.uint64(32 - model.P)))
             xs = x[idx]
-            x[idx] = (xs // f) * np.uint64(M) + (xs % f) + cum
+            x[idx] = (xs // f) * np.uint64(model.M) + (xs % f) + cum
     states = x.astype(np.uint32)
     assert (x < (1 << 32)).all() and (x >= L).all()
     words = [buf[c, :cnt[c]][::-1].astype(np.uint16) for c in range(n_ch)]
@@ -142,11 +143,11 @@ class ChainDecoder:
     def _symbol(self, x, ctx):
         """One table step: returns (new x before renormalisation, symbol id)."""
         F, CUM, S2I = self.model.F, self.model.CUM, self.model.SLOT2ID
-        slot = (x & np.uint64(M - 1)).astype(np.int64)
+        slot = (x & np.uint64(self.model.M - 1)).astype(np.int64)
         ids = S2I[ctx, slot]
         f = F[ctx, ids].astype(np.uint64)
         cum = CUM[ctx, ids].astype(np.uint64)
-        return f * (x >> np.uint64(P)) + slot.astype(np.uint64) - cum, ids
+        return f * (x >> np.uint64(self.model.P)) + slot.astype(np.uint64) - cum, ids
 
     def escapes_ahead(self, idx, peek):
         """Whether each chain's next group holds a bucket (escape) symbol.
@@ -253,4 +254,4 @@ def decode_chains(model: Model, states, chain_groups, reader, n_groups: int):
 
 def ideal_bits(sym, model: Model) -> float:
     f = model.F[sym["ctx"], sym["id"]].astype(np.float64)
-    return float(np.sum(P - np.log2(f)) + sym["rawbits"].sum())
+    return float(np.sum(model.P - np.log2(f)) + sym["rawbits"].sum())

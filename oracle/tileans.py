@@ -21,8 +21,9 @@ rANS machinery as the lossy blob (``codec``, ``rans``, ``layout``):
   estimated with LOG2Q plus the 4096 bits of the stored table is not below the
   raw 8 bits per byte, in which case the table is uniform and not stored
   (f = 8 for every value: exactly 8 bits a byte);
-* the rANS coder, its 32-bit state, 16-bit words, P = 11, the final state L and
-  the request-order stream layout are those of the lossy blob (no escapes).
+* the rANS coder (32-bit state, 16-bit words, the final state L) and the
+  request-order stream layout are those of the lossy blob (no escapes); the
+  byte tables keep P = 11 (2048 slots).
 
 Blob (little-endian, packed):
 
@@ -48,8 +49,11 @@ import numpy as np
 
 from .codec import chain_layout, chain_group_counts, ChunkReader, BLOCK_CHAINS, TILE_GROUPS
 from .layout import CHUNK, TileSchedule, request_ranks, build_stream, block_geometry
-from .model import quantize_freqs, LOG2Q, P, M
+from .model import quantize_freqs, LOG2Q
 from .rans import encode_chains, L
+
+P = 11                # table precision of the byte tables (2048 slots)
+M = 1 << P
 
 MAGIC = b"EPT1"
 VERSION = 1
@@ -69,7 +73,11 @@ class TileAnsError(ValueError):
 
 class Tables:
     """Per-context frequencies over the 256 byte values (the ``rans`` model
-    interface: F, CUM indexed [context, value]; SLOT2ID for decoding)."""
+    interface: F, CUM indexed [context, value]; SLOT2ID for decoding; the
+    precision P and slot count M)."""
+
+    P = P
+    M = M
 
     def __init__(self, F):
         self.F = np.asarray(F, dtype=np.int64)

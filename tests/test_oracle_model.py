@@ -71,14 +71,15 @@ def test_last_restriction_matches_e8_parity(scale):
         assert (m.F[sym["ctx"], sym["id"]] > 0).all()
 
 
-def test_tables_sum_and_roundtrip():
+@pytest.mark.parametrize("k,P", [(4, 10), (5, 10), (6, 11), (7, 11)])
+def test_tables_sum_and_roundtrip(k, P):
     rng = np.random.default_rng(9)
-    u = e8_nearest_doubled(rng.standard_normal((5000, 8)) * 5.0)
-    k = 4
+    u = e8_nearest_doubled(rng.standard_normal((5000, 8)) * 5.0 * (1 << (k - 4)))
     sym = mdl.group_symbols(u, k)
     m = mdl.build_model(k, *mdl.count_symbols(sym, mdl.n_msym(k)))
-    assert (m.F.sum(axis=1) == mdl.M).all()
-    assert m.F.max() <= mdl.M - 1
+    assert m.P == P == mdl.precision(k) and m.M == 1 << P
+    assert (m.F.sum(axis=1) == m.M).all()
+    assert m.F.max() <= m.M - 1
     # FREE: signs split a magnitude's probability evenly
     for c in (0, 1):
         f = m.F[1 + c, :2 * m.nm]
@@ -89,7 +90,7 @@ def test_tables_sum_and_roundtrip():
 
 def test_log2q_clear_of_ties():
     t = mdl.LOG2Q
-    for f in range(1, mdl.M + 1):
+    for f in range(1, mdl.M_MAX + 1):
         x = 65536.0 * math.log2(f)
         assert abs((x - math.floor(x)) - 0.5) > 1e-6
     for j in range(12):

@@ -5,7 +5,7 @@ import pytest
 
 import synth
 from oracle import tileans as ta
-from oracle.model import P, M
+from oracle.tileans import P, M
 
 
 def _bytes_of(a):
