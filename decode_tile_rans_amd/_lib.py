@@ -10,7 +10,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libentropack_hip.so")
+# EP_LIB_PATH selects another build of the same C ABI (the host-only sanitizer build,
+# which exports the host entry points alone)
+LIB_PATH = os.environ.get("EP_LIB_PATH") or os.path.join(HERE, "libentropack_hip.so")
 
 EP_BF16, EP_FP16, EP_FP32, EP_FP8_E4M3FN, EP_INT8 = 1, 2, 3, 4, 5
 ERRORS = {0: "EP_OK", -1: "EP_E_ARG", -2: "EP_E_RANGE", -3: "EP_E_DTYPE", -4: "EP_E_SHAPE",
@@ -82,6 +84,8 @@ def lib():
             raise ImportError(f"{LIB_PATH} is missing: build it with `python -m decode_tile_rans_amd.build`")
         L = C.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
+            if os.environ.get("EP_LIB_PATH") and not hasattr(L, name):
+                continue
             f = getattr(L, name)
             f.restype = res
             f.argtypes = args

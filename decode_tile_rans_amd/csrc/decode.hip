@@ -6,12 +6,14 @@
 //
 // Work mapping (MI355X-first, not the pages' H20 design):
 //   * one wavefront = one block of 64 rANS chains, one chain per lane (64/S tiles), or two
-//     blocks with two chains per lane; the wave's prefix sum over the block's 32 region
-//     lengths gives every chain its stream start, so only one u32 checkpoint per 64
-//     chains is stored;
-//   * a workgroup of W waves stages the 7 decode tables (7 x 2048 packed u32 = 56 KB)
-//     into LDS once; every chain keeps a 64-byte ring of stream words in LDS, fed by
-//     16-byte loads issued two groups ahead of use;
+//     blocks with two chains per lane; a wave-wide prefix sum over the block's stored
+//     chunk counts and tail lengths gives every chain its stream positions, so the stored
+//     per-chain metadata stays at one byte of chunk count and half a byte of tail length
+//     (plus the chain's initial state) and one u32 offset per block;
+//   * a workgroup of W waves stages the 7 decode tables into LDS once (56 KB: 1024 slots
+//     of two-word entries, or 1024 / 2048 slots of packed words, by table precision and
+//     escapes); every chain keeps a 32-word ring of stream words in LDS, fed by 16-byte
+//     loads in the order the stream stores them, issued two groups ahead of use;
 //   * per coordinate: one LDS table read, x = f (x >> P) + bias (24-bit mad), a
 //     16-bit renormalisation from a prefetched ring word, the doubled coordinate taken
 //     straight from the table entry (escapes: bypass bits, replayed on a careful path),

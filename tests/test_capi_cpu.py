@@ -137,7 +137,7 @@ def test_serialize_deserialize_and_corruption():
     bad.append(bytes(b2))
     b3 = bytearray(blob)
     off = 48 + 2 * 256 + ob.model_bytes.__len__()
-    b3[off] ^= 2                            # checkpoint 0 no longer 0
+    b3[off] ^= 2                            # block 0's offset no longer 0
     bad.append(bytes(b3))
     b4 = bytearray(blob)
     b4[48 + 1] |= 0x80                      # negative row scale
@@ -148,6 +148,51 @@ def test_serialize_deserialize_and_corruption():
         assert e.value.name == "EP_E_CORRUPT"
         with pytest.raises(ValueError):
             oracle.parse_blob(bb)
+
+
+def _mutations(blob, rng, n):
+    """n corrupted copies of blob: 1-4 random bytes changed, cut short or lengthened."""
+    out = []
+    for i in range(n):
+        b = bytearray(blob)
+        kind = i % 4
+        if kind == 0:
+            b = b[:int(rng.integers(0, len(b)))]
+        elif kind == 1:
+            b += bytes(rng.integers(0, 256, int(rng.integers(1, 64)), dtype=np.uint8))
+        else:
+            for _ in range(int(rng.integers(1, 5))):
+                # bias toward the header and the model, where the parser makes most checks
+                hi = len(b) if rng.random() < 0.3 else min(len(b), 48 + 4 * 256 + 1024)
+                b[int(rng.integers(0, hi))] = int(rng.integers(0, 256))
+        out.append(bytes(b))
+    return out
+
+
+def test_deserialize_random_corruptions():
+    """The parser of untrusted bytes on corrupted blobs (lossy with and without escapes,
+    TileANS): every copy is either refused as EP_E_CORRUPT or accepted, and an accepted
+    copy serializes back to exactly its bytes.  (Run under ASan/UBSan by
+    test_host_sanitizers.)"""
+    rng = np.random.default_rng(11)
+    blobs = [lib_blob(synth.small_gauss(), nx.DT_BF16, 3.5)[0],
+             lib_blob(synth.rowscaled(64, 256, 31), nx.DT_BF16, 11.0)[0]]
+    blobs.append(_lossless_blob(synth.rowscaled(64, 256, 5), 2)[0])
+    accepted = 0
+    for blob in blobs:
+        for bb in _mutations(blob, rng, 400):
+            try:
+                h = L.ep_deserialize(bb)
+            except L.EPError as e:
+                assert e.name == "EP_E_CORRUPT", e
+                continue
+            try:
+                assert L.ep_serialize(h) == bb
+                assert np.isfinite(L.ep_actual_bpp(h))
+                accepted += 1
+            finally:
+                L.ep_blob_free(h)
+    assert accepted < 3 * 400
 
 
 DIST_CASES = [c for c in CASES if c[0] in ("odd_37x13", "r512_8", "r512_2.3", "S8", "fp16", "fp32", "fp8", "int8",
