@@ -447,7 +447,8 @@ struct PrimeLoads {
   uint32_t t_at, t_pos;
   bool t_has, t_mir;
 };
-__device__ __forceinline__ void ch_prime_issue(const StreamRef& s, Chain& r, bool cand, PrimeLoads& P) {
+__device__ __forceinline__ void ch_prime_issue(const StreamRef& s, Chain& r, bool cand, int32_t ahead2,
+                                               PrimeLoads& P) {
   uint4* dat = P.dat;
   uint32_t* at = P.at;
   bool* put = P.put;
@@ -456,7 +457,7 @@ __device__ __forceinline__ void ch_prime_issue(const StreamRef& s, Chain& r, boo
   bool t_has = false, t_mir = false;
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
-    const bool want = cand && (int32_t)(r.fb - r.a2) < 2 * 17 && r.rem > 0;
+    const bool want = cand && (int32_t)(r.fb - r.a2) < ahead2 && r.rem > 0;
     bool full;
     const uint32_t pos = ch_claim(r, want, full);
     const uint32_t o = r.fb & 48u;
@@ -499,13 +500,14 @@ __device__ __forceinline__ void ch_flush(Chain& r) {
   r.have_pend = false;
   r.pend_mirror = false;
 }
-// Service at every even group: write the chunk in flight, top up to 17 ahead, then one
-// round for chains at most 24 ahead.  Full chunks load asynchronously with a fixed
-// pattern (one 16-byte load per lane; lanes without a chunk read the stream's first
-// one, a line every lane shares); tails, rare, are fetched at once.
-__device__ __forceinline__ void ch_service(const StreamRef& s, Chain& r, bool act) {
+// Service (every even group; every group of a blob with escapes): write the chunk in
+// flight, top up to ahead2 / 2 words ahead (17, or 24 with escapes), then one round for
+// chains at most 24 ahead.  Full chunks load asynchronously with a fixed pattern (one
+// 16-byte load per lane; lanes without a chunk read the stream's first one, a line
+// every lane shares); tails, rare, are fetched at once.
+__device__ __forceinline__ void ch_service(const StreamRef& s, Chain& r, bool act, int32_t ahead2) {
   ch_flush(r);
-  ch_sync(s, r, act, 2 * 17);
+  ch_sync(s, r, act, ahead2);
   const bool want = act && (int32_t)(r.fb - r.a2) <= 2 * (kRingWords - kChunkWords) && r.rem > 0;
   bool full;
   const uint32_t pos = ch_claim(r, want, full);
@@ -880,22 +882,18 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
       const uint32_t any = (e[c][0] | e[c][1] | e[c][2]) | (e[c][3] | e[c][4] | e[c][5]) | (e[c][6] | e[c][7]);
       const bool slow = act && (any & LY::kEsc) != 0;
       if (__ballot(slow) != 0) {
-        // careful path for the chains whose group holds an escape: fetch to 24 ahead,
-        // replay the group from its start, fetch back to 17 ahead
+        // careful path for the chains whose group holds an escape: replay the group from
+        // its start (the group's service left 24 words in the ring, as many as a group
+        // can consume)
         if (slow) {
           rd[c].x = xs[c];
           rd[c].a2 = ras[c] + rd[c].d;
-          ch_flush(rd[c]);
-        }
-        ch_sync(X.sref, rd[c], slow, 2 * 24);
-        if (slow) {
           rd[c].nw = ch_word(rd[c]);
           ch_group_careful<LY, G>(X.lds0, rd[c], J.k, u);
 #pragma unroll
           for (int i = 0; i < 8; ++i) w[i] = rs[c].h * (float)u[i];
+          ch_linear(rd[c]);
         }
-        ch_sync(X.sref, rd[c], slow, 2 * 17);
-        if (slow) ch_linear(rd[c]);
       }
     }
     if constexpr (NT > 0) {
@@ -998,6 +996,8 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
   const uint64_t seg = (S == 64) ? ~0ull : (((1ull << S) - 1ull) << s0);
 
   constexpr int ESZ = out_elem_bytes<OUT>();
+  // words kept ahead by a service (in bytes): two escape-free groups, or one group with escapes
+  constexpr int32_t kAhead2 = ESC ? 2 * 24 : 2 * 17;
   Chain rd[ILP];
   RowScale rs[ILP];
   int ngr[ILP];
@@ -1087,11 +1087,11 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
   if (stage) {
     st.issue();
 #pragma unroll
-    for (int c = 0; c < ILP; ++c) ch_prime_issue(X.sref, rd[c], live[c], pl[c]);
+    for (int c = 0; c < ILP; ++c) ch_prime_issue(X.sref, rd[c], live[c], kAhead2, pl[c]);
     st.commit();
   } else {
 #pragma unroll
-    for (int c = 0; c < ILP; ++c) ch_prime_issue(X.sref, rd[c], live[c], pl[c]);
+    for (int c = 0; c < ILP; ++c) ch_prime_issue(X.sref, rd[c], live[c], kAhead2, pl[c]);
   }
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
@@ -1102,19 +1102,28 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
 #pragma unroll
   for (int c = 1; c < ILP; ++c) nmax = ngr[c] > nmax ? ngr[c] : nmax;
 
-  // two groups per iteration: the stream service runs before every even group
-  // (the row scale of the even group is settled before the service, so that its load is
+  // two groups per iteration: the stream service runs before every even group, and
+  // (blobs with escapes) before every odd one too
+  // (the row scale of a group is settled before its service, so that its load is
   // followed by a fixed sequence of memory operations)
   for (int kk = 0; kk < nmax; kk += 2) {
     if constexpr (OUT != OUT_BYTES) row_scale<ILP>(X, kk, rs, ngr);
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
-      ch_service(X.sref, rd[c], (ILP == 1) || kk < ngr[c]);
+      ch_service(X.sref, rd[c], (ILP == 1) || kk < ngr[c], kAhead2);
       ch_linear(rd[c]);
     }
     decode_group<OUT, ESC, C8, NARROW, ILP, SEL>(X, kk, rd, rs, ngr, g0, optr, mv);
     if (kk + 1 < nmax) {
       if constexpr (OUT != OUT_BYTES) row_scale<ILP>(X, kk + 1, rs, ngr);
+      if constexpr (ESC) {
+#pragma unroll
+        for (int c = 0; c < ILP; ++c) {
+          ch_settle(rd[c]);
+          ch_service(X.sref, rd[c], (ILP == 1) || kk + 1 < ngr[c], kAhead2);
+          ch_linear(rd[c]);
+        }
+      }
       decode_group<OUT, ESC, C8, NARROW, ILP, SEL>(X, kk + 1, rd, rs, ngr, g0, optr, mv);
     }
 #pragma unroll

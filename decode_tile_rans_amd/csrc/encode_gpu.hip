@@ -301,10 +301,10 @@ __global__ void __launch_bounds__(64) row_error_tiled_kernel(const void* src, in
 // ---------------------------------------------------------------- rANS chains
 // One thread per chain: groups j, j+S, ... of its tile, encoded last to first (the
 // decoder reads them first to last).  Words are stored in emission order (the reverse
-// of decoding order); cons / slow per group feed the schedule.
+// of decoding order); cons (words per group) feeds the schedule.
 __global__ void encode_chains_kernel(const int32_t* u, int64_t n_groups, int S, int log2S, int64_t n_chains, int k,
                                      const int32_t* F, const int32_t* CUM, int max_words, int steps, uint16_t* words,
-                                     uint8_t* cons, uint8_t* slow, uint32_t* len, uint32_t* state) {
+                                     uint8_t* cons, uint32_t* len, uint32_t* state) {
   const int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (ch >= n_chains) return;
   const int64_t t = ch >> log2S;
@@ -314,16 +314,13 @@ __global__ void encode_chains_kernel(const int32_t* u, int64_t n_groups, int S, 
   uint16_t* w = words + ch * (int64_t)max_words;
   uint32_t x = kL;
   int n = 0;
-  const int K = 1 << k;
-  const int P = k >= 6 ? 11 : 10;   // the table precision of escape threshold K (precision())
+  const int P = k >= 6 ? 11 : 10;   // the table precision of escape threshold 2^k (precision())
   for (int kk = ngr - 1; kk >= 0; --kk) {
     const int64_t g = (int64_t)kTileGroups * t + j + (int64_t)kk * S;
     cm::Sym sy[8];
     int ms[8];
     cm::symbolize(u + g * 8, k, sy, ms);
     const int n0 = n;
-    bool esc = false;
-    for (int i = 0; i < 8; ++i) esc |= ms[i] >= K;
     for (int i = 7; i >= 0; --i) {
       const int rb = sy[i].rawbits;
       if (rb > 16) {
@@ -351,18 +348,17 @@ __global__ void encode_chains_kernel(const int32_t* u, int64_t n_groups, int S, 
       x = (x / f) * (1u << P) + (x % f) + cum;
     }
     cons[ch * steps + kk] = (uint8_t)(n - n0);
-    slow[ch * steps + kk] = esc ? 1 : 0;
   }
   len[ch] = (uint32_t)n;
   state[ch] = x;
 }
 
-// One thread per tile: the decoder's fetch schedule (prime to 17 words ahead; before
-// every even group to 17 ahead plus one round for chains at most 24 ahead; around a
-// group with an escape, that chain to 24 ahead before and 17 after), handing out the
-// tile's main-area positions in request order.
-__global__ void schedule_kernel(const uint32_t* len, const uint8_t* cons, const uint8_t* slow, int64_t n_groups,
-                                int S, int64_t n_tiles, int steps, int max_full, uint16_t* rank) {
+// One thread per tile: the decoder's fetch schedule, handing out the tile's main-area
+// positions in request order.  Blobs without escapes: prime to 17 words ahead, before
+// every even group to 17 ahead plus one round for chains at most 24 ahead; blobs with
+// escapes: prime to 24 ahead, before every group to 24 ahead plus the same round.
+__global__ void schedule_kernel(const uint32_t* len, const uint8_t* cons, int64_t n_groups, int S, int64_t n_tiles,
+                                int steps, int max_full, bool esc, uint16_t* rank) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= n_tiles) return;
   int32_t Fw[64], q[64], n[64], ngr[64], nf[64];
@@ -385,15 +381,12 @@ __global__ void schedule_kernel(const uint32_t* len, const uint8_t* cons, const 
       Fw[j] = n[j];
     }
   };
-  // sync: rounds until no candidate wants more (mode 0: all chains, 1: chains decoding
-  // group g, 2: chains whose group g holds an escape)
-  auto sync = [&](int mode, int g, int32_t ahead) {
+  // sync: rounds until no candidate wants more (all chains, or those decoding group g)
+  auto sync = [&](bool all, int g, int32_t ahead) {
     for (;;) {
       bool any = false;
       for (int j = 0; j < S; ++j) {
-        const bool cand = mode == 0 ? true
-                                    : (mode == 1 ? g < ngr[j] : (g < ngr[j] && slow[(t * S + j) * steps + g] != 0));
-        if (cand && Fw[j] - q[j] < ahead && Fw[j] < n[j]) {
+        if ((all || g < ngr[j]) && Fw[j] - q[j] < ahead && Fw[j] < n[j]) {
           take(j);
           any = true;
         }
@@ -401,19 +394,16 @@ __global__ void schedule_kernel(const uint32_t* len, const uint8_t* cons, const 
       if (!any) return;
     }
   };
-  sync(0, 0, 17);
+  const int32_t ahead = esc ? 24 : 17;
+  sync(true, 0, ahead);
   for (int g = 0; g < gmax; ++g) {
-    if ((g & 1) == 0) {
-      sync(1, g, 17);
+    if (esc || (g & 1) == 0) {
+      sync(false, g, ahead);
       for (int j = 0; j < S; ++j)
         if (g < ngr[j] && Fw[j] - q[j] <= 24 && Fw[j] < n[j]) take(j);
     }
-    bool any_slow = false;
-    for (int j = 0; j < S; ++j) any_slow |= g < ngr[j] && slow[(t * S + j) * steps + g] != 0;
-    if (any_slow) sync(2, g, 24);
     for (int j = 0; j < S; ++j)
       if (g < ngr[j]) q[j] += cons[(t * S + j) * steps + g];
-    if (any_slow) sync(2, g, 17);
   }
 }
 
@@ -736,9 +726,9 @@ int compress_device(const void* dsrc, int dtype, int64_t R, int64_t C, double t,
   const int steps = kTileGroups / S;
   const int max_words = 24 * steps + 2;
   const int max_full = max_words / 8 + 1;
-  DevBuf d_tab, d_words, d_cons, d_slow, d_len, d_state, d_rank, d_dst, d_stream;
+  DevBuf d_tab, d_words, d_cons, d_len, d_state, d_rank, d_dst, d_stream;
   if ((rc = dalloc(d_tab, 8 * (size_t)kHistBins)) || (rc = dalloc(d_words, 2 * (size_t)n_chains * max_words)) ||
-      (rc = dalloc(d_cons, (size_t)n_chains * steps)) || (rc = dalloc(d_slow, (size_t)n_chains * steps)) ||
+      (rc = dalloc(d_cons, (size_t)n_chains * steps)) ||
       (rc = dalloc(d_len, 4 * (size_t)n_chains)) || (rc = dalloc(d_state, 4 * (size_t)n_chains)) ||
       (rc = dalloc(d_rank, 2 * (size_t)n_chains * max_full)) || (rc = dalloc(d_dst, 16 * (size_t)n_chains)))
     return rc;
@@ -756,10 +746,9 @@ int compress_device(const void* dsrc, int dtype, int64_t R, int64_t C, double t,
   hipLaunchKernelGGL(encode_chains_kernel, dim3((unsigned)((n_chains + 127) / 128)), dim3(128), 0, st,
                      d_u.as<int32_t>(), n_groups, S, log2S, n_chains, k, d_tab.as<int32_t>(),
                      d_tab.as<int32_t>() + kHistBins, max_words, steps, d_words.as<uint16_t>(), d_cons.as<uint8_t>(),
-                     d_slow.as<uint8_t>(), d_len.as<uint32_t>(), d_state.as<uint32_t>());
+                     d_len.as<uint32_t>(), d_state.as<uint32_t>());
   hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)((n_tiles + 63) / 64)), dim3(64), 0, st, d_len.as<uint32_t>(),
-                     d_cons.as<uint8_t>(), d_slow.as<uint8_t>(), n_groups, S, n_tiles, steps, max_full,
-                     d_rank.as<uint16_t>());
+                     d_cons.as<uint8_t>(), n_groups, S, n_tiles, steps, max_full, any_esc, d_rank.as<uint16_t>());
   std::vector<uint32_t> lens((size_t)n_chains), states((size_t)n_chains);
   if ((rc = hc(hipMemcpyAsync(lens.data(), d_len.p, 4 * (size_t)n_chains, hipMemcpyDeviceToHost, st), "copy")) ||
       (rc = hc(hipMemcpyAsync(states.data(), d_state.p, 4 * (size_t)n_chains, hipMemcpyDeviceToHost, st), "copy")) ||

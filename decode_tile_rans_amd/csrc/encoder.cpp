@@ -166,7 +166,6 @@ struct ChainOut {
   std::vector<uint16_t> words;   // decoding order
   uint32_t state;
   std::vector<uint8_t> cons;     // words the decoder reads in each of the chain's groups
-  std::vector<uint8_t> slow;     // group holds a bucket (escape) symbol
   std::vector<uint16_t> rank;    // main-area position of each full chunk in its tile
 };
 
@@ -188,12 +187,10 @@ void encode_chain(const int32_t* u_all, const Model& m, int64_t t, int j, int S,
   Sym s[8];
   int ms[8];
   out->cons.assign((size_t)ngr, 0);
-  out->slow.assign((size_t)ngr, 0);
   for (int kk = ngr - 1; kk >= 0; --kk) {
     int64_t g = (int64_t)kTileGroups * t + j + (int64_t)kk * S;
     symbolize(u_all + g * 8, m.k, s, ms);
     const size_t w0 = w.size();
-    for (int i = 0; i < 8; ++i) out->slow[kk] |= ms[i] >= (1 << m.k);
     for (int i = 7; i >= 0; --i) {
       int rb = s[i].rawbits;
       if (rb > 16) bypass(s[i].rawval >> 16, rb - 16);
@@ -214,11 +211,13 @@ void encode_chain(const int32_t* u_all, const Model& m, int64_t t, int j, int S,
 // Request order of one tile's full chunks.  The decoder keeps a window of at most 32
 // fetched words per chain and fetches 8-word chunks only at these sites, chains taking
 // turns in chain order; a sync site repeats rounds until no chain wants more:
-//   prime: until 17 words ahead;  every even group: until 17 ahead, then one round for
-//   chains at most 24 ahead;  a group with an escape (that chain): until 24 ahead before
-//   it, until 17 ahead after it.  Only chains that decode the group take part; a chain's
-//   last short chunk (its tail) counts as a request but lives in the block's tail area.
-void schedule_tile(ChainOut* ch, int S) {
+//   no escapes in the blob: prime until 17 words ahead; every even group: until 17
+//   ahead, then one round for chains at most 24 ahead;
+//   escapes in the blob: prime until 24 ahead; every group: until 24 ahead, then one
+//   round for chains at most 24 ahead.
+// Only chains that decode the group take part; a chain's last short chunk (its tail)
+// counts as a request but lives in the block's tail area.
+void schedule_tile(ChainOut* ch, int S, bool esc) {
   int32_t F[64], q[64], n[64], ngr[64];
   uint16_t ctr = 0;
   int gmax = 0;
@@ -249,21 +248,17 @@ void schedule_tile(ChainOut* ch, int S) {
       if (!any) return;
     }
   };
-  sync([](int) { return true; }, 17);
+  const int32_t ahead = esc ? 24 : 17;
+  sync([](int) { return true; }, ahead);
   for (int g = 0; g < gmax; ++g) {
     auto act = [&](int j) { return g < ngr[j]; };
-    if ((g & 1) == 0) {
-      sync(act, 17);
+    if (esc || (g & 1) == 0) {
+      sync(act, ahead);
       for (int j = 0; j < S; ++j)
         if (act(j) && F[j] - q[j] <= 24 && F[j] < n[j]) take(j);
     }
-    auto slow = [&](int j) { return g < ngr[j] && ch[j].slow[g]; };
-    bool any_slow = false;
-    for (int j = 0; j < S; ++j) any_slow |= slow(j);
-    if (any_slow) sync(slow, 24);
     for (int j = 0; j < S; ++j)
       if (act(j)) q[j] += ch[j].cons[g];
-    if (any_slow) sync(slow, 17);
   }
 }
 
@@ -359,7 +354,6 @@ void encode_chain_bytes(const uint8_t* by, const int32_t (*F)[256], const int32_
   std::vector<uint16_t>& w = out->words;
   w.clear();
   out->cons.assign((size_t)ngr, 0);
-  out->slow.assign((size_t)ngr, 0);
   for (int kk = ngr - 1; kk >= 0; --kk) {
     const int64_t g = (int64_t)kTileGroups * t + j + (int64_t)kk * S;
     const size_t w0 = w.size();
@@ -588,7 +582,7 @@ int compress(const void* src, int dtype, int64_t R, int64_t C, double t, int S_r
     for (int64_t ch = b; ch < e; ++ch) encode_chain(u.data(), m, ch / S, (int)(ch % S), S, n_groups, &chains[ch]);
   }, 64);
   parallel_for(n_tiles, [&](int64_t b, int64_t e, int) {
-    for (int64_t tt = b; tt < e; ++tt) schedule_tile(&chains[(size_t)(tt * S)], S);
+    for (int64_t tt = b; tt < e; ++tt) schedule_tile(&chains[(size_t)(tt * S)], S, any_esc);
   }, 16);
 
   // ---- distortion of the lattice reconstruction fl32(h_r u) (before the container
@@ -749,7 +743,7 @@ int compress_lossless(const void* src, int64_t n_bytes, int E, const int64_t* di
       encode_chain_bytes(by.data(), F, CUM, n_ctx, ch / S, (int)(ch % S), S, n_groups, &chains[ch]);
   }, 64);
   parallel_for(n_tiles, [&](int64_t b0, int64_t e0, int) {
-    for (int64_t tt = b0; tt < e0; ++tt) schedule_tile(&chains[(size_t)(tt * S)], S);
+    for (int64_t tt = b0; tt < e0; ++tt) schedule_tile(&chains[(size_t)(tt * S)], S, false);
   }, 16);
 
   // ---- blob: header | dims | tables | chain area

@@ -176,16 +176,13 @@ def compress(src, dtype: int, target_bpp: float, chains_per_tile=None, trace=Non
     states, words, cons = encode_chains(sym, model, cg)
     lens = np.array([len(w) for w in words], dtype=np.int64).reshape(n_tiles, S)
     assert (lens // CHUNK <= (0xFF if S >= 8 else 0xFFFF)).all()
-    # a group is decoded on the careful path when it holds a bucket symbol
-    esc_g = (sym["msym"] >= (1 << k)).any(axis=1)
-    slow = np.where(cg >= 0, esc_g[np.maximum(cg, 0)], False)
-    ngr = chain_group_counts(n_groups, S, n_tiles)
-    steps = cg.shape[1]
-    rank = request_ranks(lens, ngr, cons.reshape(n_tiles, S, steps), slow.reshape(n_tiles, S, steps))
-    offsets, stream = build_stream(words, lens.reshape(-1), rank, S)
     flags = 0
     if (sym["msym"] >= (1 << k)).any():
         flags |= FLAG_ESC
+    ngr = chain_group_counts(n_groups, S, n_tiles)
+    steps = cg.shape[1]
+    rank = request_ranks(lens, ngr, cons.reshape(n_tiles, S, steps), esc=bool(flags & FLAG_ESC))
+    offsets, stream = build_stream(words, lens.reshape(-1), rank, S)
     wh = reconstruct_f32(u.reshape(R, G * 8)[:, :C], h)
     if nx.needs_saturation(wh, dtype):
         flags |= FLAG_SAT
@@ -252,7 +249,8 @@ def reconstruct_f32(u: np.ndarray, h: np.ndarray) -> np.ndarray:
 class ChunkReader:
     """Reads every chain's words from its tile area: full chunks where the
     schedule placed them, the tail from the tile's tails.  A word is readable
-    only once the schedule has fetched its chunk."""
+    only once a sync round of the schedule has fetched its chunk (a site's
+    last, asynchronous round lands at the next site)."""
 
     def __init__(self, b: Blob, sched: TileSchedule):
         self.b = b
@@ -268,7 +266,7 @@ class ChunkReader:
         t, j = c // S, c % S
         n = i // CHUNK
         full = n < self.nfull[c]
-        fetched = i < self.sched.F[t, j]
+        fetched = i < self.sched.landed[t, j]
         rk = self.sched.rank[t, j, np.minimum(n, self.sched.rank.shape[2] - 1)]
         pos = np.where(full, self.base[c] + self.main_start[c] + CHUNK * rk + i % CHUNK,
                        self.base[c] + self.tail_pos[c] + i - CHUNK * self.nfull[c])
@@ -280,10 +278,6 @@ class ChunkReader:
         good = pos >= 0
         w[good] = self.b.stream[pos[good]]
         return w
-
-    def peek(self, idx, n):
-        pos, _ = self._pos(idx, self.q[idx] + n, checked=False)
-        return self._read(pos)
 
     def take(self, idx):
         pos, ok = self._pos(idx, self.q[idx], checked=True)
@@ -313,28 +307,20 @@ def decode(buf, tiles=None):
         keep = np.ones(n_tiles, dtype=bool)
     ngr = np.where(keep[:, None], ngr, 0)
     lens = np.where(keep[:, None], b.chain_lens.astype(np.int64).reshape(n_tiles, S), 0)
-    sched = TileSchedule(lens, ngr)
+    sched = TileSchedule(lens, ngr, esc=bool(b.flags & FLAG_ESC))
     reader = ChunkReader(b, sched)
     dec = ChainDecoder(b.model, b.states, n_groups)
     sched.prime()
     for g in range(cg.shape[1]):
         act = (g < ngr).reshape(-1)
-        if g % 2 == 0:
+        if sched.serves(g):
             sched.service(g)
         idx = np.nonzero(act)[0]
         if idx.size == 0:
             continue
-        slow = np.zeros(n_tiles * S, dtype=bool)
-        if b.flags & FLAG_ESC:
-            slow[idx] = dec.escapes_ahead(idx, reader.peek)
-        sl = slow.reshape(n_tiles, S)
-        if sl.any():
-            sched.before_escapes(sl)
         q0 = reader.q.copy()
         dec.decode_group(idx, cg[idx, g], reader)
         sched.consume(act.reshape(n_tiles, S), (reader.q - q0).reshape(n_tiles, S))
-        if sl.any():
-            sched.after_escapes(sl)
     active = keep.repeat(S) & (ngr.reshape(-1) > 0)
     ok_state = bool((dec.x[active] == L).all())
     ok_reads = not bool(reader.overrun.any())

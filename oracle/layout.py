@@ -1,4 +1,4 @@
-"""Stream layout of blob v3 (unchanged since v2): where every chain's words sit (oracle).
+"""Stream layout of blob v3: where every chain's words sit (oracle).
 
 [ABS] / [SUM] say only that the coordinates are rANS-coded in independently
 decodable tiles.  How the words sit in memory is this project's format,
@@ -12,26 +12,32 @@ chosen so that a GPU wave fetches them with contiguous loads:
 * a tile's main area holds its chains' full chunks in request order: the
   order in which the reference reader below asks for them.  Chains take their
   turn in chain order within a site; a sync site repeats rounds until no chain
-  wants more:
+  wants more.  Blobs without escape symbols:
 
       prime                      sync until ahead >= 17
       group g (g even)           sync until ahead >= 17, then one round in which
                                  a chain asks if ahead <= 24
-      group g holding an escape  that chain: sync until ahead >= 24 before the
-                                 group's words are consumed, sync until
-                                 ahead >= 17 after
+
+  blobs with escape symbols (header flag), every group served:
+
+      prime                      sync until ahead >= 24
+      group g (every g)          sync until ahead >= 24, then one round in which
+                                 a chain asks if ahead <= 24
 
   where ahead = words fetched - words consumed (the tail counts as one
   request).  A chain asks only while it has unfetched words and only at groups
   it decodes (g < its group count).
 
 Why these numbers: a group consumes at most 8 words without escapes (one per
-symbol) and at most 24 with them (two more per escape for up to 28 raw bits),
-so every group's words are fetched before they are read; a chain never holds
-more than 32 words ahead (the reader's ring).
+symbol) and at most 24 with them (two more per escape for up to 28 raw bits).
+The reader's words from a site's last round arrive only at the next site, so
+a chain may read only what the sync rounds fetched: 17 covers the two
+escape-free groups until the next site, 24 the one group of a blob with
+escapes.  A chain never holds more than 32 words ahead (the reader's ring).
 
 Pins (tests): hand-worked schedules for small consumption patterns; every
-word fetched before it is read on random patterns; encoder/decoder round trips.
+word fetched by a sync round before it is read, and never more than 32 words
+ahead, on random patterns; encoder/decoder round trips.
 """
 from __future__ import annotations
 
@@ -49,14 +55,19 @@ class TileSchedule:
     """The reference reader for all tiles at once (arrays shaped (n_tiles, S)).
 
     ``rank[t, j, n]`` receives the position (in chunks from the tile's start) of
-    chain j's full chunk n, in the order requested.
+    chain j's full chunk n, in the order requested.  ``esc`` selects the
+    schedule of blobs with escape symbols.  ``landed`` counts the words of the
+    sync rounds (and of earlier sites): the words a chain may read.
     """
 
-    def __init__(self, lens: np.ndarray, ngr: np.ndarray):
+    def __init__(self, lens: np.ndarray, ngr: np.ndarray, esc: bool = False):
         self.n = np.asarray(lens, dtype=np.int64)
         self.ngr = np.asarray(ngr, dtype=np.int64)
+        self.esc = bool(esc)
+        self.ahead = AHEAD_ESC if esc else AHEAD_GROUP
         T, S = self.n.shape
         self.F = np.zeros((T, S), dtype=np.int64)
+        self.landed = np.zeros((T, S), dtype=np.int64)
         self.q = np.zeros((T, S), dtype=np.int64)
         self.ctr = np.zeros(T, dtype=np.int64)
         nfull = int((self.n // CHUNK).max()) if self.n.size else 0
@@ -70,52 +81,47 @@ class TileSchedule:
         self.rank[t_idx, j_idx, self.F[t_idx, j_idx] // CHUNK] = self.ctr[t_idx] + order[t_idx, j_idx]
         self.ctr += full.sum(axis=1)
         self.F = np.where(full, self.F + CHUNK, np.where(want, self.n, self.F))
+        assert (self.F - self.q <= RING).all(), "a chain would hold more than the ring"
 
     def _sync(self, cand, ahead):
         while True:
             want = cand & (self.F - self.q < ahead) & (self.F < self.n)
             if not want.any():
-                return
+                break
             self._round(want)
+        self.landed = self.F.copy()
 
     def prime(self):
-        self._sync(np.ones_like(self.n, dtype=bool), AHEAD_GROUP)
+        self._sync(np.ones_like(self.n, dtype=bool), self.ahead)
+
+    def serves(self, g: int) -> bool:
+        """Whether group g begins with a service site."""
+        return self.esc or g % 2 == 0
 
     def service(self, g: int):
         act = g < self.ngr
-        self._sync(act, AHEAD_GROUP)
+        self._sync(act, self.ahead)
         self._round(act & (self.F - self.q <= ASYNC_MAX) & (self.F < self.n))
-
-    def before_escapes(self, slow):
-        self._sync(slow, AHEAD_ESC)
 
     def consume(self, act, words):
         self.q = np.where(act, self.q + words, self.q)
 
-    def after_escapes(self, slow):
-        self._sync(slow, AHEAD_GROUP)
 
-
-def request_ranks(lens, ngr, cons, slow):
+def request_ranks(lens, ngr, cons, esc=False):
     """Run the whole schedule for known per-group consumption.
 
-    lens, ngr: (T, S); cons, slow: (T, S, steps) words consumed by / escape in
-    each chain's group g.  Returns rank (T, S, max full chunks).
+    lens, ngr: (T, S); cons: (T, S, steps) words consumed by each chain's group g;
+    esc: the blob holds escape symbols.  Returns rank (T, S, max full chunks).
     """
-    sch = TileSchedule(lens, ngr)
+    sch = TileSchedule(lens, ngr, esc)
     sch.prime()
     steps = cons.shape[2]
     for g in range(steps):
         act = g < sch.ngr
-        if g % 2 == 0:
+        if sch.serves(g):
             sch.service(g)
-        sl = act & slow[:, :, g]
-        if sl.any():
-            sch.before_escapes(sl)
         sch.consume(act, cons[:, :, g])
-        if sl.any():
-            sch.after_escapes(sl)
-        assert (sch.q <= sch.F).all(), "a word was consumed before it was fetched"
+        assert (sch.q <= sch.landed).all(), "a word was read before a sync round fetched it"
     assert (sch.F == sch.n).all()
     return sch.rank
 

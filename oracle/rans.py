@@ -149,38 +149,6 @@ class ChainDecoder:
         cum = CUM[ctx, ids].astype(np.uint64)
         return f * (x >> np.uint64(self.model.P)) + slot.astype(np.uint64) - cum, ids
 
-    def escapes_ahead(self, idx, peek):
-        """Whether each chain's next group holds a bucket (escape) symbol.
-
-        Decodes the group's symbols on a copy of the state without reading raw
-        bits: up to the first escape this is the true decode, so the first
-        escape is always seen; what follows it does not matter.  ``peek(idx, n)``
-        returns the n-th next word of each chain without consuming it.
-        """
-        x = self.x[idx].copy()
-        used = np.zeros(len(idx), dtype=np.int64)
-        c = np.zeros(len(idx), dtype=np.int64)
-        pi = np.zeros(len(idx), dtype=np.int64)
-        esc = np.zeros(len(idx), dtype=bool)
-        for i in range(8):
-            ctx = np.zeros(len(idx), np.int64) if i == 0 else (1 + c if i < 7 else 3 + 2 * c + pi)
-            x, ids = self._symbol(x, ctx)
-            low = x < L
-            if low.any():
-                w = peek(idx[low], used[low])
-                x[low] = (x[low] << np.uint64(16)) | w
-                used[low] += 1
-            if i == 0:
-                c = ids >> 9
-                sid = ids & 511
-            else:
-                sid = ids
-            msym = sid >> 1
-            esc |= msym >= self.K
-            if i < 7:
-                pi = pi ^ np.mod(msym + np.where(c == 0, 0, sid & 1), 2)
-        return esc
-
     def decode_group(self, idx, groups, reader):
         """Decode the next group of chains ``idx`` (global group ids ``groups``)."""
         k, K = self.k, self.K

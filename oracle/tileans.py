@@ -139,7 +139,7 @@ def compress(raw, E: int, dims, dtype_tag: int = 0, chains_per_tile=None) -> byt
         raise TileAnsError("chain longer than the chunk count field")
     ngr = chain_group_counts(n_groups, S, n_tiles)
     steps = cg.shape[1]
-    rank = request_ranks(lens, ngr, cons.reshape(n_tiles, S, steps), np.zeros((n_tiles, S, steps), dtype=bool))
+    rank = request_ranks(lens, ngr, cons.reshape(n_tiles, S, steps))
     offsets, stream = build_stream(words, lens.reshape(-1), rank, S)
     n_ch = n_tiles * S
     n_blocks = -(-n_ch // BLOCK_CHAINS)
@@ -239,7 +239,7 @@ def decode(buf, tiles=None):
     sched.prime()
     for g in range(cg.shape[1]):
         act = (g < ngr).reshape(-1)
-        if g % 2 == 0:
+        if sched.serves(g):
             sched.service(g)
         idx = np.nonzero(act)[0]
         if idx.size == 0:

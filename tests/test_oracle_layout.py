@@ -8,23 +8,36 @@ from oracle import layout
 
 
 def test_hand_worked_two_chains():
-    # Chain 0: 40 words, five groups of 8, no escapes.
-    # Chain 1: 64 words, groups of 20, 20, 8, 8, 8; groups 0 and 1 hold escapes.
-    # prime:  rounds (0:r0 1:r1) (0:r2 1:r3) (0:r4 1:r5): both 24 ahead
-    # g0:     service: no sync; async 0:r6 1:r7 (both had 24 <= 24 ahead)
-    #         chain 1 escapes: 32 ahead >= 24, nothing; consumes 20 -> 12 ahead
-    #         after: 1:r8 (20 ahead)
-    # g1:     chain 1 escapes: 20 < 24 -> 1:r9 (28); consumes 20 -> 8 ahead
-    #         after: 1:r10 (16), 1:r11 (24, all fetched)
-    # g2:     service: chain 0 has 32 - 16 = 16 < 17 ahead -> 0:r12 (all fetched)
+    # No escapes.  Chain 0: 40 words, groups of 8; chain 1: 24 words, groups 8, 8, 8, 0, 0.
+    # prime:  rounds (0:r0 1:r1) (0:r2 1:r3) (0:r4 1:r5): 24 ahead each, chain 1 complete
+    # g0:     sync to 17: nothing; async: 0:r6 (24 <= 24 ahead)
+    # g1:     no site (chain 0 reads words 8..15 of what it fetched by g0's sync)
+    # g2:     sync to 17: chain 0 has 32 - 16 = 16 < 17 ahead -> 0:r7 (all fetched)
+    lens = np.array([[40, 24]])
+    ngr = np.array([[5, 3]])
+    cons = np.array([[[8, 8, 8, 8, 8], [8, 8, 8, 0, 0]]])
+    rank = layout.request_ranks(lens, ngr, cons)
+    assert rank[0, 0, :5].tolist() == [0, 2, 4, 6, 7]
+    assert rank[0, 1, :3].tolist() == [1, 3, 5]
+
+
+def test_hand_worked_escape_schedule():
+    # A blob with escapes: every group is served, to 24 ahead.
+    # Chain 0: 40 words, five groups of 8; chain 1: 64 words, groups of 20, 20, 8, 8, 8.
+    # prime:  (0:r0 1:r1) (0:r2 1:r3) (0:r4 1:r5): both 24 ahead
+    # g0:     sync: nothing; async 0:r6 1:r7 (both 24 <= 24 ahead); consume 8, 20
+    # g1:     sync: chain 1 has 32 - 20 = 12 -> 1:r8 (20) -> 1:r9 (28); async: chain 0
+    #         (32 - 8 = 24 ahead) 0:r10 (all fetched); consume 8, 20
+    # g2:     sync: chain 1 has 48 - 40 = 8 -> 1:r11 (16) -> 1:r12 (24, all fetched)
     lens = np.array([[40, 64]])
     ngr = np.array([[5, 5]])
     cons = np.array([[[8, 8, 8, 8, 8], [20, 20, 8, 8, 8]]])
-    slow = np.zeros((1, 2, 5), dtype=bool)
-    slow[0, 1, :2] = True
-    rank = layout.request_ranks(lens, ngr, cons, slow)
-    assert rank[0, 0, :5].tolist() == [0, 2, 4, 6, 12]
-    assert rank[0, 1, :8].tolist() == [1, 3, 5, 7, 8, 9, 10, 11]
+    rank = layout.request_ranks(lens, ngr, cons, esc=True)
+    assert rank[0, 0, :5].tolist() == [0, 2, 4, 6, 10]
+    assert rank[0, 1, :8].tolist() == [1, 3, 5, 7, 8, 9, 11, 12]
+    # the same pattern under the escape-free schedule would read words before they land
+    with pytest.raises(AssertionError):
+        layout.request_ranks(lens, ngr, cons)
 
 
 def test_hand_worked_tail_and_short_chain():
@@ -34,29 +47,48 @@ def test_hand_worked_tail_and_short_chain():
     lens = np.array([[32, 20]])
     ngr = np.array([[4, 4]])
     cons = np.array([[[8, 8, 8, 8], [5, 5, 5, 5]]])
-    rank = layout.request_ranks(lens, ngr, cons, np.zeros((1, 2, 4), dtype=bool))
+    rank = layout.request_ranks(lens, ngr, cons)
     assert rank[0, 0, :4].tolist() == [0, 2, 4, 5]
     assert rank[0, 1, :2].tolist() == [1, 3]
 
 
-@pytest.mark.parametrize("S,seed", [(1, 0), (2, 1), (8, 2), (8, 3), (64, 4)])
-def test_random_patterns_fetch_before_read(S, seed):
+@pytest.mark.parametrize("S,seed,esc", [(1, 0, False), (2, 1, False), (8, 2, False), (64, 4, False),
+                                        (1, 5, True), (2, 6, True), (8, 7, True), (8, 3, True), (64, 8, True)])
+def test_random_patterns_fetch_before_read(S, seed, esc):
     rng = np.random.default_rng(seed)
     T = 50
     steps = 512 // S
     ngr = np.full((T, S), steps)
     ngr[-1] = rng.integers(0, steps + 1, S)           # a ragged last tile
-    slow = (rng.random((T, S, steps)) < 0.05) & (np.arange(steps) < ngr[..., None])
-    cons = np.where(slow, rng.integers(0, 25, (T, S, steps)), rng.integers(0, 9, (T, S, steps)))
-    cons = np.where(np.arange(steps) < ngr[..., None], cons, 0)
+    live = np.arange(steps) < ngr[..., None]
+    cons = rng.integers(0, 9, (T, S, steps))
+    if esc:
+        # groups with escapes consume up to 24 words; some chains escape in runs
+        slow = (rng.random((T, S, steps)) < 0.05) | ((rng.random((T, S, 1)) < 0.1) & (rng.random((T, S, steps)) < 0.7))
+        cons = np.where(slow, rng.integers(0, 25, (T, S, steps)), cons)
+    cons = np.where(live, cons, 0)
     lens = cons.sum(axis=2)
-    rank = layout.request_ranks(lens, ngr, cons, slow)    # asserts fetched-before-read
+    # asserts every word read was landed by a sync round and the ring never overfills
+    rank = layout.request_ranks(lens, ngr, cons, esc=esc)
     nfull = lens // layout.CHUNK
     for t in range(T):
         got = np.concatenate([rank[t, j, :nfull[t, j]] for j in range(S)])
         assert np.array_equal(np.sort(got), np.arange(nfull[t].sum()))   # a permutation
         for j in range(S):
             assert (np.diff(rank[t, j, :nfull[t, j]]) > 0).all()          # in chain order
+
+
+def test_schedule_catches_a_planted_overread():
+    # the invariant check itself: a 25-word group is more than any group may consume
+    # (24 with escapes); the first group's 25th word comes from g0's asynchronous round,
+    # which lands only at the next site, so both schedules must refuse the pattern
+    lens = np.array([[25]])
+    ngr = np.array([[1]])
+    cons = np.array([[[25]]])
+    for esc in (False, True):
+        with pytest.raises(AssertionError):
+            layout.request_ranks(lens, ngr, cons, esc=esc)
+    layout.request_ranks(np.array([[24]]), ngr, np.array([[[24]]]), esc=True)
 
 
 def test_block_geometry():
@@ -124,20 +156,8 @@ def test_stream_gives_back_every_chains_words(monkeypatch, R, C, t, S, seed):
     # the ranks are the schedule's for the consumption the encoder recorded
     T_, steps = b.n_tiles, seen["cg"].shape[1]
     ngr = (seen["cg"] >= 0).sum(axis=1).reshape(T_, S)
-    esc_any = np.zeros((T_, S, steps), dtype=bool)
-    if b.flags & 1:
-        # a group takes the careful path when one of its magnitudes reaches the escape
-        # threshold 2^k: recomputed from the decoded coordinates, not the encoder's symbols
-        u, _, _ = oracle.decode(blob)
-        G = -(-C // 8)
-        up = np.zeros((R, G * 8), dtype=np.int64)
-        up[:, :C] = u
-        mags = np.abs(up.reshape(-1, 8)) >> 1
-        gesc = (mags >= (1 << b.k)).any(axis=1)
-        cg = seen["cg"]
-        esc_any = np.where(cg >= 0, gesc[np.maximum(cg, 0)], False).reshape(T_, S, steps)
-    assert np.array_equal(layout.request_ranks(lens.reshape(T_, S), ngr, seen["cons"].reshape(T_, S, steps), esc_any),
-                          rank)
+    assert np.array_equal(layout.request_ranks(lens.reshape(T_, S), ngr, seen["cons"].reshape(T_, S, steps),
+                                               esc=bool(b.flags & 1)), rank)
 
     stream = b.stream
     offs = [int(o) * 8 for o in b.block_offsets] + [len(stream)]
