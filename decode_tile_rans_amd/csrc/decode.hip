@@ -258,6 +258,8 @@ struct DecBatch {
 // Entry layouts (chosen per blob when its tables are expanded):
 //   wide   (K >= 64): f 0..10 | bias 11..21 | u or escape info 22..30 (9 bit) | escape 31
 //   narrow (K <= 32): f 0..10 | bias 11..21 | c 22 | escape 23 | u + 128 or escape info 24..31
+// Escape info: the coset c, the sign, the bucket's top two bits below the leading one and
+// n2 = e - 2, the number of magnitude bits below those three (e = floor(log2 m)).
 // In both, bit 22 is the coset of a FIRST symbol.  The parity of floor(u/2) (bit 1 of u)
 // sits at bit 23 (wide) or 25 (narrow).
 template <bool NARROW>
@@ -271,20 +273,17 @@ struct EntryLayout {
   __device__ static float w_of(uint32_t e, float h, float nh128) {
     return NARROW ? __builtin_fmaf((float)(e >> 24), h, nh128) : h * (float)u_of(e);
   }
-  // escape info: c, neg, top2, e - k
-  __device__ static void esc_info(uint32_t e, int& c, int& neg, int& top2, int& er) {
+  // escape info: c, neg, the leading three magnitude bits 4 + top2, n2 = e - 2
+  __device__ static void esc_info(uint32_t e, uint32_t& c, uint32_t& neg, uint32_t& lead3, uint32_t& n2) {
+    c = (e >> 22) & 1u;
     if (NARROW) {
-      uint32_t b = e >> 24;
-      c = (int)((e >> 22) & 1u);
-      neg = (int)(b & 1u);
-      top2 = (int)((b >> 1) & 3u);
-      er = (int)(b >> 3);
+      neg = (e >> 24) & 1u;
+      lead3 = ((e >> 25) & 3u) | 4u;
+      n2 = e >> 27;
     } else {
-      uint32_t i = (e >> 22) & 0x1FFu;
-      c = (int)(i & 1u);
-      neg = (int)((i >> 1) & 1u);
-      top2 = (int)((i >> 2) & 3u);
-      er = (int)(i >> 4);
+      neg = (e >> 23) & 1u;
+      lead3 = ((e >> 24) & 3u) | 4u;
+      n2 = (e >> 26) & 31u;
     }
   }
 };
@@ -585,55 +584,29 @@ __device__ __forceinline__ void ch_decode(Chain& r, typename G::Ent e) {
   if constexpr (G::kSplit) r.x = __umul24(e.x, r.x >> G::kP) + e.y;
   else r.x = __umul24(e & 2047u, r.x >> G::kP) + ((e >> 11) & 2047u);
 }
-template <class G>
-__device__ __forceinline__ void ch_advance(Chain& r, typename G::Ent e) {
-  ch_decode<G>(r, e);
-  ch_renorm(r);
-}
-__device__ __forceinline__ uint32_t ch_bypass(Chain& r, int nb) {
-  const uint32_t v = r.x & ((1u << nb) - 1u);
+// Bypass field of nb <= 16 raw bits (the state's low bits), through the linear pointer
+__device__ __forceinline__ uint32_t ch_bypass_lin(Chain& r, uint32_t nb) {
+  const uint32_t v = __builtin_amdgcn_ubfe(r.x, 0u, nb);
   r.x >>= nb;
-  ch_renorm(r);
+  ch_renorm_lin_if(r, r.x < kL);
   return v;
 }
-// escape symbol: raw bits follow; returns the doubled coordinate
+// Doubled coordinate of an escape symbol: its raw bits follow the table step (low 16
+// first, then the rest), the last coordinate's lowest bit implied by the E8 parity pi.
 template <class LY>
-__device__ __forceinline__ int32_t ch_escape(Chain& r, uint32_t e, int k, int last, int pi) {
-  int c, neg, top2, er;
-  LY::esc_info(e, c, neg, top2, er);
-  const int ex = k + er;
-  const int nb = ex - 2 - last;
-  uint32_t raw = ch_bypass(r, nb < 16 ? nb : 16);
-  if (nb > 16) raw |= ch_bypass(r, nb - 16) << 16;
-  if (last) raw = (raw << 1) | (uint32_t)(c == 0 ? pi : (pi ^ neg));
-  const uint32_t m = (1u << ex) | ((uint32_t)top2 << (ex - 2)) | raw;
-  const int32_t uu = (int32_t)(2u * m + (uint32_t)c);
+__device__ __forceinline__ int32_t ch_escape_lin(Chain& r, uint32_t e, bool last, uint32_t pi) {
+  uint32_t c, neg, lead3, n2;
+  LY::esc_info(e, c, neg, lead3, n2);
+  const uint32_t nb = last ? n2 - 1u : n2;
+  uint32_t raw = ch_bypass_lin(r, nb < 16u ? nb : 16u);
+  if (nb > 16u) raw |= ch_bypass_lin(r, nb - 16u) << 16;
+  if (last) raw = (raw << 1) | (pi ^ (neg & c));
+  const uint32_t m = (lead3 << n2) | raw;
+  const int32_t uu = (int32_t)(2u * m + c);
   return neg ? -uu : uu;
 }
 // LDS table slot of stored table t (stored order FIRST, FREE[0], FREE[1], LAST...)
 __host__ __device__ constexpr int lds_table_slot(int t) { return t == 0 ? 1 : (t == 1 ? 0 : t); }
-// careful decode of one group (the chain's state is at the group's start and 24 words
-// are in its ring): FIRST, six FREE, LAST, escapes with their raw bits
-// (kernels for blobs with escapes: one packed word per slot)
-template <class LY, class G>
-__device__ __forceinline__ void ch_group_careful(uint32_t lds0, Chain& r, int k, int32_t* u) {
-  static_assert(!G::kSplit, "escapes take packed entries");
-  uint32_t ee = ch_entry<G>(lds0 + G::kFirstOff, r);
-  ch_advance<G>(r, ee);
-  const uint32_t fb = G::free_base(ee);
-  u[0] = (ee & LY::kEsc) ? ch_escape<LY>(r, ee, k, 0, 0) : LY::u_of(ee);
-  int pp = u[0] >> 1;
-  for (int i = 1; i < 7; ++i) {
-    ee = ch_entry<G>(lds0 + fb, r);
-    ch_advance<G>(r, ee);
-    u[i] = (ee & LY::kEsc) ? ch_escape<LY>(r, ee, k, 0, 0) : LY::u_of(ee);
-    pp ^= u[i] >> 1;
-  }
-  const int pi = pp & 1;
-  ee = ch_entry<G>(lds0 + fb + G::kLastOff + ((uint32_t)pi << G::kTableLog2), r);
-  ch_advance<G>(r, ee);
-  u[7] = (ee & LY::kEsc) ? ch_escape<LY>(r, ee, k, 1, pi) : LY::u_of(ee);
-}
 
 // Stages a job's decode tables into LDS (stored order FIRST, FREE[0], ...; in LDS the
 // first two swap places).  issue() starts four 16-byte loads per thread, commit()
@@ -820,20 +793,63 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
     }
     return;
   }
-  // ---- fast path: eight symbols per chain, no escape handling
-  // (e holds each entry's value word; a split entry's bias word is used by its decode
-  // step only)
-  uint32_t xs[ILP], ras[ILP], nws[ILP];
+  uint32_t xs[ILP], ras[ILP], nws[ILP], ds[ILP];
   uint32_t e[ILP][8];
-  uint32_t fbs[ILP];
-  typename G::Ent en[ILP];
+  int32_t uu[ILP][8];
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
     xs[c] = rd[c].x;
     ras[c] = rd[c].ra;
     nws[c] = rd[c].nw;
-    en[c] = ch_entry<G>(X.lds0 + G::kFirstOff, rd[c]);
+    ds[c] = rd[c].d;
   }
+  if constexpr (ESC) {
+    // ---- blobs with escapes: one pass, each escape symbol's raw bits read where it
+    // stands.  A symbol reads at most three words (a renormalisation and two bypass
+    // fields), so four symbols stay within the 16 words the linear pointer may run past
+    // the ring's end: it is re-derived from the consumed count after the fourth.
+    static_assert(!G::kSplit, "escapes take packed entries");
+    uint32_t fbs[ILP], pp[ILP];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i == 4) {
+#pragma unroll
+        for (int c = 0; c < ILP; ++c) {
+          ch_settle(rd[c]);
+          ch_linear(rd[c]);
+        }
+      }
+      uint32_t ee[ILP];
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) {
+        uint32_t tb;
+        if (i == 0) tb = X.lds0 + G::kFirstOff;
+        else if (i < 7) tb = fbs[c];
+        else tb = fbs[c] + G::kLastOff + ((pp[c] & 1u) << G::kTableLog2);
+        ee[c] = ch_entry<G>(tb, rd[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) ch_decode<G>(rd[c], ee[c]);
+      ch_renorm_all<ILP, SEL>(rd);
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) {
+        if (i == 0) fbs[c] = X.lds0 + G::free_base(ee[c]);
+        int32_t v = LY::u_of(ee[c]);
+        if (ee[c] & LY::kEsc) v = ch_escape_lin<LY>(rd[c], ee[c], i == 7, pp[c] & 1u);
+        uu[c][i] = v;
+        // parity of the first seven floor(u / 2): bit 1 of their xor
+        if (i == 0) pp[c] = (uint32_t)v >> 1;
+        else if (i < 7) pp[c] ^= (uint32_t)v >> 1;
+      }
+    }
+  } else {
+  // ---- escape-free blobs: eight symbols per chain, the coordinate straight from the
+  // entry (e holds each entry's value word; a split entry's bias word is used by its
+  // decode step only)
+  uint32_t fbs[ILP];
+  typename G::Ent en[ILP];
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) en[c] = ch_entry<G>(X.lds0 + G::kFirstOff, rd[c]);
   // per step: every chain's table read, then every chain's state update, then the
   // renormalisations (whose ring reads are conditional and so end the step's LDS batch)
 #pragma unroll
@@ -867,6 +883,7 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
     e[c][7] = G::lo(en[c]);
   }
   ch_renorm_all<ILP, SEL>(rd);
+  }
 
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
@@ -875,25 +892,12 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
     int32_t u[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (OUT == OUT_COORDS) u[i] = LY::u_of(e[c][i]);
-      else w[i] = LY::w_of(e[c][i], rs[c].h, rs[c].nh);
-    }
-    if constexpr (ESC) {
-      const uint32_t any = (e[c][0] | e[c][1] | e[c][2]) | (e[c][3] | e[c][4] | e[c][5]) | (e[c][6] | e[c][7]);
-      const bool slow = act && (any & LY::kEsc) != 0;
-      if (__ballot(slow) != 0) {
-        // careful path for the chains whose group holds an escape: replay the group from
-        // its start (the group's service left 24 words in the ring, as many as a group
-        // can consume)
-        if (slow) {
-          rd[c].x = xs[c];
-          rd[c].a2 = ras[c] + rd[c].d;
-          rd[c].nw = ch_word(rd[c]);
-          ch_group_careful<LY, G>(X.lds0, rd[c], J.k, u);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) w[i] = rs[c].h * (float)u[i];
-          ch_linear(rd[c]);
-        }
+      if constexpr (ESC) {
+        if (OUT == OUT_COORDS) u[i] = uu[c][i];
+        else w[i] = rs[c].h * (float)uu[c][i];
+      } else {
+        if (OUT == OUT_COORDS) u[i] = LY::u_of(e[c][i]);
+        else w[i] = LY::w_of(e[c][i], rs[c].h, rs[c].nh);
       }
     }
     if constexpr (NT > 0) {
@@ -942,6 +946,7 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
         rd[c].x = xs[c];
         rd[c].ra = ras[c];
         rd[c].nw = nws[c];
+        if constexpr (ESC) rd[c].d = ds[c];   // (the escape pass re-derives the pointer)
       }
     }
   }
