@@ -256,10 +256,13 @@ struct DecBatch {
 };
 
 // Entry layouts (chosen per blob when its tables are expanded):
-//   wide   (K >= 64): f 0..10 | bias 11..21 | u or escape info 22..30 (9 bit) | escape 31
-//   narrow (K <= 32): f 0..10 | bias 11..21 | c 22 | escape 23 | u + 128 or escape info 24..31
-// Escape info: the coset c, the sign, the bucket's top two bits below the leading one and
-// n2 = e - 2, the number of magnitude bits below those three (e = floor(log2 m)).
+//   wide   (K >= 64): f 0..10 | bias 11..21 | u (9 bit) 22..30 | escape 31
+//   narrow (K <= 32): f 0..10 | bias 11..21 | c 22 | escape 23 | u + 128 24..31
+// An escape (bucket) symbol holds instead the coset c, the sign, n2 = e - 2 (the number of
+// magnitude bits below the leading three; e = floor(log2 m)) and the two bits top2 after
+// the leading one:  wide  c 22 | neg 23 | n2 24..28 | top2 29..30 | 1 31  (so that bits
+//                               29..31 are the leading three bits 1 top2 themselves)
+//                   narrow c 22 | 1 23 | n2 24..28 | top2 29..30 | neg 31
 // In both, bit 22 is the coset of a FIRST symbol.  The parity of floor(u/2) (bit 1 of u)
 // sits at bit 23 (wide) or 25 (narrow).
 template <bool NARROW>
@@ -273,17 +276,16 @@ struct EntryLayout {
   __device__ static float w_of(uint32_t e, float h, float nh128) {
     return NARROW ? __builtin_fmaf((float)(e >> 24), h, nh128) : h * (float)u_of(e);
   }
-  // escape info: c, neg, the leading three magnitude bits 4 + top2, n2 = e - 2
-  __device__ static void esc_info(uint32_t e, uint32_t& c, uint32_t& neg, uint32_t& lead3, uint32_t& n2) {
+  // escape info: c, the sign as 0 / -1, the leading three magnitude bits 4 + top2, n2
+  __device__ static void esc_info(uint32_t e, uint32_t& c, int32_t& sgn, uint32_t& lead3, uint32_t& n2) {
     c = (e >> 22) & 1u;
+    n2 = (e >> 24) & 31u;
     if (NARROW) {
-      neg = (e >> 24) & 1u;
-      lead3 = ((e >> 25) & 3u) | 4u;
-      n2 = e >> 27;
+      sgn = (int32_t)e >> 31;
+      lead3 = ((e >> 29) & 3u) | 4u;
     } else {
-      neg = (e >> 23) & 1u;
-      lead3 = ((e >> 24) & 3u) | 4u;
-      n2 = (e >> 26) & 31u;
+      sgn = __builtin_amdgcn_sbfe((int32_t)e, 23, 1);
+      lead3 = e >> 29;
     }
   }
 };
@@ -595,15 +597,21 @@ __device__ __forceinline__ uint32_t ch_bypass_lin(Chain& r, uint32_t nb) {
 // first, then the rest), the last coordinate's lowest bit implied by the E8 parity pi.
 template <class LY>
 __device__ __forceinline__ int32_t ch_escape_lin(Chain& r, uint32_t e, bool last, uint32_t pi) {
-  uint32_t c, neg, lead3, n2;
-  LY::esc_info(e, c, neg, lead3, n2);
+  uint32_t c, lead3, n2;
+  int32_t sgn;
+  LY::esc_info(e, c, sgn, lead3, n2);
   const uint32_t nb = last ? n2 - 1u : n2;
-  uint32_t raw = ch_bypass_lin(r, nb < 16u ? nb : 16u);
-  if (nb > 16u) raw |= ch_bypass_lin(r, nb - 16u) << 16;
-  if (last) raw = (raw << 1) | (pi ^ (neg & c));
+  uint32_t raw;
+  if (nb <= 16u) {
+    raw = ch_bypass_lin(r, nb);
+  } else {   // (magnitudes of 2^19 and more)
+    raw = ch_bypass_lin(r, 16u);
+    raw |= ch_bypass_lin(r, nb - 16u) << 16;
+  }
+  if (last) raw = (raw << 1) | (pi ^ ((uint32_t)sgn & c));
   const uint32_t m = (lead3 << n2) | raw;
-  const int32_t uu = (int32_t)(2u * m + c);
-  return neg ? -uu : uu;
+  const uint32_t a = (m << 1) | c;
+  return (int32_t)((a ^ (uint32_t)sgn) - (uint32_t)sgn);   // -a for a negative coordinate
 }
 // LDS table slot of stored table t (stored order FIRST, FREE[0], FREE[1], LAST...)
 __host__ __device__ constexpr int lds_table_slot(int t) { return t == 0 ? 1 : (t == 1 ? 0 : t); }

@@ -71,11 +71,11 @@ extern const int32_t* log2q_table();   // floor(2^16 log2 f + 1/2), f in [0, 204
 //   bits 11..21  bias   (slot - cum)
 //   wide layout (K >= 64):
 //     bits 22..30  direct symbol: doubled coordinate u (signed 9 bit; bit 22 = coset,
-//                  bit 23 = parity of floor(u/2)); escape: c | neg<<1 | top2<<2 | (e-2)<<4
+//                  bit 23 = parity of floor(u/2)); escape: c | neg<<1 | (e-2)<<2 | top2<<7
 //     bit  31      escape (bucket symbol: raw bits follow)
 //   narrow layout (K <= 32, |u| <= 127):
 //     bit 22 coset, bit 23 escape, bits 24..31 u + 128 (direct) or
-//     neg | top2<<1 | (e-2)<<3 (escape)
+//     (e-2) | top2<<5 | neg<<7 (escape)
 void build_slot_tables(const Model& m, uint32_t* out /* 7*M */, bool narrow);
 // Split entries for narrow blobs without escapes (two u32 per slot, 7*M pairs): the
 // first holds f in bits 0..9 (bits 10..23 zero, so a 24-bit multiply takes it as is)

@@ -288,8 +288,8 @@ void build_slot_tables(const Model& m, uint32_t* out, bool narrow) {
       } else {
         // bucket: n2 = e - 2 magnitude bits below the leading three (1, top2)
         int n2 = ((msym - K) >> 2) + m.k - 2, top2 = (msym - K) & 3;
-        hi = narrow ? (uint32_t(c) | (1u << 1) | (uint32_t(neg | (top2 << 1) | (n2 << 3)) << 2))
-                    : (uint32_t(c | (neg << 1) | (top2 << 2) | (n2 << 4)) | (1u << 9));
+        hi = narrow ? (uint32_t(c) | (1u << 1) | (uint32_t(n2) << 2) | (uint32_t(top2) << 7) | (uint32_t(neg) << 9))
+                    : (uint32_t(c) | (uint32_t(neg) << 1) | (uint32_t(n2) << 2) | (uint32_t(top2) << 7) | (1u << 9));
       }
       int32_t cum = m.CUM[t][id];
       for (int s = cum; s < cum + f; ++s) {
