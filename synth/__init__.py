@@ -68,6 +68,19 @@ def rowscaled_f32(rows: int, cols: int, seed: int, outlier_frac: float = 0.0) ->
     return w.astype(np.float32)
 
 
+def rowscaled_row_outliers(rows: int, cols: int, seed: int, every: int = 4, first: int = 1,
+                           mult: float = 12.0) -> np.ndarray:
+    """BF16 bit patterns of :func:`rowscaled_f32` with one +-mult x s_r entry in each of
+    rows first, first + every, ... (random column and sign; s_r the row's scale)."""
+    w = rowscaled_f32(rows, cols, seed)
+    rng = np.random.default_rng(seed + 7919)
+    r = np.arange(first, rows, every)
+    c = rng.integers(0, cols, r.size)
+    rms = np.sqrt((w[r].astype(np.float64) ** 2).mean(axis=1))
+    w[r, c] = (mult * rms * np.where(rng.random(r.size) < 0.5, -1.0, 1.0)).astype(np.float32)
+    return f32_to_bf16_bits(w)
+
+
 def rowscaled(rows: int, cols: int, seed: int, outlier_frac: float = 0.0) -> np.ndarray:
     """BF16 bit patterns of :func:`rowscaled_f32`."""
     return f32_to_bf16_bits(rowscaled_f32(rows, cols, seed, outlier_frac))

@@ -57,6 +57,17 @@ def test_small_gauss_config():
     _check("small_gauss 256x256 @3.5", synth.small_gauss(), nx.DT_BF16, 3.5)
 
 
+@pytest.mark.parametrize("t,S", [(2.3, None), (3.0, 8), (4.0, None), (4.0, 2)])
+def test_escapes_outside_the_rate_sample(t, S):
+    # 1024 x 1024: the rate search samples every fourth row from row 0, so outliers in rows
+    # 1, 5, 9, ... stay out of its escape count: a small escape threshold (K <= 32, the
+    # narrow one-word tables of 1024 slots) with escape symbols in the blob
+    src = synth.rowscaled_row_outliers(1024, 1024, 91)
+    blob, _, _ = _check(f"outliers outside the sample 1024^2 @{t} S={S}", src, nx.DT_BF16, t, S)
+    b = oracle.parse_blob(blob)
+    assert b.k <= 5 and (b.flags & 1), (b.k, b.flags)
+
+
 def test_rowscaled_outliers_3072():
     _check("rowscaled+outliers 3072x3072 @4.0", synth.rowscaled(3072, 3072, 2, 0.001), nx.DT_BF16, 4.0)
 

@@ -100,6 +100,30 @@ def test_matvec_matches_oracle(R, C, T, bpp, S, seed):
     assert db.errors() == 0
 
 
+@pytest.mark.parametrize("T,t", [(1, 3.0), (5, 4.0)])
+def test_matvec_narrow_escapes(T, t):
+    # the fused product on a blob with escape symbols and a small escape threshold (the
+    # outliers sit in rows the rate search does not sample)
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    say("matvec narrow escapes", T, t)
+    src = synth.rowscaled_row_outliers(1024, 1024, 91)
+    blob = oracle.compress(src, nx.DT_BF16, t)
+    b = oracle.parse_blob(blob)
+    assert b.k <= 5 and (b.flags & 1), (b.k, b.flags)
+    _, w_hat, _ = oracle.decode(blob)
+    x = synth.activations(T, 1024, 77)
+    db = DevBlob(blob)
+    xt = _t(x, torch.bfloat16)
+    need = L.ep_matvec_workspace_bytes(db.h, T)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, 1024), dtype=torch.bfloat16, device="cuda")
+    L.ep_compressed_matvec(db.h, xt.data_ptr(), T, 0, y.data_ptr(), ws.data_ptr(), need, stream_ptr())
+    torch.cuda.synchronize()
+    _check(_bits(y), x, w_hat, None)
+    assert db.errors() == 0
+
+
 def test_matvec_python_layer_small_batch():
     """CompressedLinear on 1..8 tokens goes through the fused path; result against the
     oracle product of the oracle's decode of the layer's own blob."""
