@@ -68,6 +68,18 @@ def test_escapes_outside_the_rate_sample(t, S):
     assert b.k <= 5 and (b.flags & 1), (b.k, b.flags)
 
 
+@pytest.mark.parametrize("t", [9.0, 11.0])
+def test_huge_magnitudes_two_bypass_fields(t):
+    # one entry per row 1e4 times the others: magnitudes of 2^19 and more, whose raw bits
+    # (more than 16) are read as two bypass fields
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((4, 65536)) * 0.01).astype(np.float32)
+    w[:, 5] = 100.0
+    w[2, 70000 % 65536] = -100.0
+    blob, u_o, _ = _check(f"huge magnitudes 4x65536 @{t}", synth.f32_to_bf16_bits(w), nx.DT_BF16, t)
+    assert (np.abs(u_o) >> 1).max() >= 1 << 19
+
+
 def test_rowscaled_outliers_3072():
     _check("rowscaled+outliers 3072x3072 @4.0", synth.rowscaled(3072, 3072, 2, 0.001), nx.DT_BF16, 4.0)
 
