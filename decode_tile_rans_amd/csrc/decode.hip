@@ -735,8 +735,8 @@ __device__ __forceinline__ void row_scale(const GroupCtx& X, int kk, RowScale* r
 
 }
 
-// Decode group kk of ILP chains: fast path over eight symbols (escapes replayed on the
-// careful path), container store.
+// Decode group kk of ILP chains: eight symbols per chain (escape symbols' raw bits read
+// in place), container store or fused product.
 template <int OUT, bool ESC, bool C8, bool NARROW, int ILP, bool SEL>
 __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* rd, RowScale* rs, const int* ngr,
                                              const uint32_t* g0, char** optr, MvAcc* mv) {
