@@ -199,16 +199,19 @@ __global__ void __launch_bounds__(64 * gemm_waves(BN), 1) gemm_tile_kernel(const
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + NST - 1 < nkt) issue(kt + NST - 1, (st + NST - 1) % NST);
     const uint8_t* sA = lds + st * STAGE;
     const uint8_t* sB = sA + A_BYTES;
     if constexpr (!kDoubleFrag) {
       // one set of fragments at a time (the wider FP8 operands of the 256-wide tile
-      // would not fit twice beside the accumulators)
+      // would not fit twice beside the accumulators).  The next tile's loads go out after
+      // this tile's last fragment reads: an LDS read issued while a direct-to-LDS load is
+      // in flight makes the compiler wait for that load first, which would expose its
+      // whole latency at every tile
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         frag_t fa[MI], fb[NJ];
         frag_load(sA, sB, ks, fa, fb);
+        if (ks == NKS - 1 && kt + NST - 1 < nkt) issue(kt + NST - 1, (st + NST - 1) % NST);
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -217,6 +220,7 @@ __global__ void __launch_bounds__(64 * gemm_waves(BN), 1) gemm_tile_kernel(const
       }
       return;
     }
+    if (kt + NST - 1 < nkt) issue(kt + NST - 1, (st + NST - 1) % NST);
     frag_t fa[2][MI], fb[2][NJ];
     frag_load(sA, sB, 0, fa[0], fb[0]);
 #pragma unroll
