@@ -331,14 +331,15 @@ struct Geo {
 // 2 (i mod 32), so chunk n fills ring bytes 16 (n mod 4) .. +15; chunks 0 and 1 of the
 // ring are also written to bytes 64..95 (a mirror), so that a reader may run up to 16
 // words past the ring's end without wrapping.  Counters are kept in bytes (2 per word):
-// fb = fetched (a chunk in flight included), a2 = consumed.  The escape-free groups of a
-// pair read through a linear pointer ra (set from a2 at the pair's start, a2 brought
-// up to date at its end); escape replays and fetches work on a2.
+// fb = fetched (a chunk in flight included), a2 = consumed.  Between services a chain
+// reads through a linear pointer ra (set from a2 at the service, a2 brought up to date
+// at the next one; blobs with escapes re-derive it within a group); fetches work on a2.
 // Fetches happen only at these sites, exactly as the encoder's schedule assumed:
-//   prime: until 17 ahead;  every even group: until 17 ahead, then one round for
-//   chains at most 24 ahead (a 16-byte load issued now, written to the ring two groups
-//   later);  a group with an escape (that chain): until 24 ahead before its careful
-//   decode, until 17 ahead after it.
+//   blobs without escapes: prime until 17 ahead; every even group: until 17 ahead,
+//   then one round for chains at most 24 ahead (a 16-byte load issued now, written to
+//   the ring at the next service);
+//   blobs with escapes: prime until 24 ahead; every group: until 24 ahead, then the
+//   same round.
 // Two escape-free groups consume <= 16 words and one group with escapes <= 24, so the
 // chain only reads words already in its ring; it never holds more than 32 words ahead.
 struct Chain {
@@ -529,15 +530,8 @@ __device__ __forceinline__ void ch_service(const StreamRef& s, Chain& r, bool ac
   }
   r.have_pend = full;
 }
-__device__ __forceinline__ void ch_renorm_if(Chain& r, bool need) {
-  if (need) {
-    r.x = (r.x << 16) | r.nw;
-    r.a2 += 2u;
-    r.nw = ch_word(r);
-  }
-}
-__device__ __forceinline__ void ch_renorm(Chain& r) { ch_renorm_if(r, r.x < kL); }
-// the same within a group pair's escape-free groups, through the linear pointer
+// 16-bit renormalisation from the word already read, through the linear pointer (the
+// next word is read at once, for the next renormalisation)
 __device__ __forceinline__ void ch_renorm_lin_if(Chain& r, bool need) {
   if (need) {
     r.x = (r.x << 16) | r.nw;
