@@ -43,10 +43,12 @@ enum OutKind { OUT_BF16 = 0, OUT_BF16_SAT = 1, OUT_FP16 = 2, OUT_FP32 = 3, OUT_F
                OUT_BYTES = 7 /* TileANS: the decoded symbols are the tensor's bytes */,
                // fused matrix-vector product with 1, 2, 4 or 8 activation rows: the BF16
                // weights are multiplied into per-chain partial sums and never stored
-               OUT_MV1 = 8, OUT_MV2 = 9, OUT_MV4 = 10, OUT_MV8 = 11 };
+               OUT_MV1 = 8, OUT_MV2 = 9, OUT_MV4 = 10, OUT_MV8 = 11,
+               // BF16 stored through the caches (a GEMM reads the weights right after)
+               OUT_BF16_L2 = 12 };
 template <int OUT>
 constexpr int mv_tokens() {
-  return OUT >= OUT_MV1 ? 1 << (OUT - OUT_MV1) : 0;
+  return (OUT >= OUT_MV1 && OUT <= OUT_MV8) ? 1 << (OUT - OUT_MV1) : 0;
 }
 template <int OUT>
 constexpr int out_elem_bytes() {
@@ -163,7 +165,7 @@ __device__ inline void store_group(void* out, int64_t base, const float* vin, co
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = fminf(fmaxf(v[i], -3.38953139e38f), 3.38953139e38f);
   }
-  if (OUT == OUT_BF16 || OUT == OUT_BF16_SAT || OUT == OUT_FP16) {
+  if (OUT == OUT_BF16 || OUT == OUT_BF16_L2 || OUT == OUT_BF16_SAT || OUT == OUT_FP16) {
     uint32_t p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -177,9 +179,11 @@ __device__ inline void store_group(void* out, int64_t base, const float* vin, co
     uint16_t* o = (uint16_t*)out + base;
     if (full) {
       // streaming store: the weights are written once, so they should not evict the
-      // compressed stream's lines from L2 (the lanes re-read those lines chunk by chunk)
+      // compressed stream's lines from L2 (the lanes re-read those lines chunk by chunk);
+      // weights a GEMM reads next are stored through the caches, where it finds them
       u32x4 pv = {p[0], p[1], p[2], p[3]};
-      __builtin_nontemporal_store(pv, (u32x4*)o);
+      if constexpr (OUT == OUT_BF16_L2) *(u32x4*)o = pv;
+      else __builtin_nontemporal_store(pv, (u32x4*)o);
     } else {
       for (int i = 0; i < nvalid; ++i) o[i] = (uint16_t)(p[i >> 1] >> ((i & 1) * 16));
     }
@@ -1233,6 +1237,7 @@ template <bool ESC, bool C8, bool NARROW, int ILP, bool SEL>
 int launch_out(int out, const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
   switch (out) {
     case OUT_BF16: return launch_t<OUT_BF16, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
+    case OUT_BF16_L2: return launch_t<OUT_BF16_L2, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
     case OUT_BF16_SAT: return launch_t<OUT_BF16_SAT, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
     case OUT_FP16: return launch_t<OUT_FP16, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
     case OUT_FP32: return launch_t<OUT_FP32, ESC, C8, NARROW, ILP, SEL>(B, n_wg, waves, st);
@@ -1619,8 +1624,16 @@ int matvec_forward(const Blob& b, const void* x, int64_t T, const void* bias, vo
   return matvec_launch(b, x, T, bias, y, (float*)(((uintptr_t)ws + 255) & ~uintptr_t(255)), stream);
 }
 
+// Decode for a GEMM that reads the weights next: BF16 stored through the caches
+int gemm_out_kind(const Blob& b) {
+  const int o = out_kind(b);
+  return o == OUT_BF16 ? OUT_BF16_L2 : o;
+}
+int decompress_for_gemm(const Blob& b, void* dst, ep_stream st) {
+  return decode_one(b, dst, 0, b.n_chains, gemm_out_kind(b), (hipStream_t)st);
+}
 int decompress_beside(const Blob& b, void* dst, ep_stream st, int64_t max_wg) {
-  return decode_one(b, dst, 0, b.n_chains, out_kind(b), (hipStream_t)st, max_wg);
+  return decode_one(b, dst, 0, b.n_chains, gemm_out_kind(b), (hipStream_t)st, max_wg);
 }
 
 // ---------------------------------------------------------------- the fused product without a workspace

@@ -183,6 +183,8 @@ int matvec_forward(const Blob& b, const void* x, int64_t T, const void* bias, vo
 // Decode the whole blob with at most max_wg workgroups (one per CU): a launch that runs
 // beside another kernel which holds the other CUs.
 int decompress_beside(const Blob& b, void* dst, ep_stream st, int64_t max_wg);
+// the whole blob for a GEMM that reads the weights next (stores kept in the caches)
+int decompress_for_gemm(const Blob& b, void* dst, ep_stream st);
 
 }  // namespace ep
 

@@ -420,7 +420,7 @@ int ep_compressed_linear_forward(const ep_blob* w, const void* x, int64_t T, con
   // written and read back), when its partial sums fit the same workspace
   if (use_matvec(w, T)) return matvec_forward(b, x, T, bias, y, ws, ws_bytes, stream);
   void* wd = (void*)(((uintptr_t)ws + 255) & ~uintptr_t(255));
-  rc = ep_decompress(w, wd, stream);
+  rc = decompress_for_gemm(b, wd, stream);
   if (rc) return rc;
   return launch_bf16(x, wd, bias, y, T, b.R, b.C, (hipStream_t)stream);
 }
@@ -551,7 +551,7 @@ int ep_compressed_linear_seq_forward(const ep_blob* const* w, int n, const void*
       if (on_side[i]) {
         if (!rc) rc = hip_check(hipStreamWaitEvent(ms, ev_dec[k], 0), "stream wait");
       } else if (!rc) {
-        rc = ep_decompress(w[i], buf[k], main_s);
+        rc = decompress_for_gemm(w[i]->b, buf[k], main_s);
       }
       if (!rc) rc = launch_bf16(x[i], buf[k], bias ? bias[i] : nullptr, y[i], T, w[i]->b.R, w[i]->b.C, ms);
     }
