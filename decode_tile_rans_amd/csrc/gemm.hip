@@ -30,6 +30,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 // ---------------------------------------------------------------- GEMM, 256 x BN tiles
 // Workgroup tile 256 x BN, waves 2 along M x W/2 along N (BN = 128: 4 waves of 128 x 64;
@@ -65,6 +66,54 @@ constexpr int gemm_waves(int BN) { return BN == 256 ? 8 : 4; }
 template <int CPR>
 __device__ __forceinline__ int swz(int r, int c) {
   return CPR == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 1) & 3));
+}
+
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// The epilogue's per-column terms for four consecutive output columns n .. n + 3: the BF16
+// bias (added) or the FP8 scale a_x a_w[n] (multiplied; 0 past the matrix), read once for
+// all the rows a lane stores, as one 8- or 16-byte load where the four columns lie inside
+// the matrix and the vector is aligned.
+template <bool FP8>
+__device__ __forceinline__ void column_terms(const uint16_t* __restrict__ bias, const float* __restrict__ aw, float ax,
+                                             int64_t n, int64_t N, bool vec, float* c) {
+  if constexpr (FP8) {
+    if (vec && n + 3 < N) {
+      const float4 s = *(const float4*)(aw + n);
+      c[0] = ax * s.x; c[1] = ax * s.y; c[2] = ax * s.z; c[3] = ax * s.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = n + e < N ? ax * aw[n + e] : 0.f;
+    }
+  } else {
+    if (!bias) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = 0.f;
+    } else if (vec && n + 3 < N) {
+      const u32x2 b = *(const u32x2*)(bias + n);
+      c[0] = __uint_as_float(b.x << 16); c[1] = __uint_as_float(b.x & 0xffff0000u);
+      c[2] = __uint_as_float(b.y << 16); c[3] = __uint_as_float(b.y & 0xffff0000u);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = n + e < N ? bf16_to_float(bias[n + e]) : 0.f;
+    }
+  }
+}
+
+// Stores a lane's four outputs of row m, columns n .. n + 3 (BF16, round to nearest even)
+__device__ __forceinline__ void store4(uint16_t* __restrict__ Y, int64_t m, int64_t ldy, int64_t n, int64_t N, bool vec,
+                                       const float* v) {
+  uint16_t* yp = Y + m * ldy + n;
+  if (vec && n + 3 < N) {
+    u32x2 pk;
+    pk.x = (uint32_t)float_to_bf16(v[0]) | ((uint32_t)float_to_bf16(v[1]) << 16);
+    pk.y = (uint32_t)float_to_bf16(v[2]) | ((uint32_t)float_to_bf16(v[3]) << 16);
+    *(u32x2*)yp = pk;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < N) yp[e] = float_to_bf16(v[e]);
+  }
 }
 
 template <int BN, int NST, int RB, bool FP8>
@@ -258,6 +307,13 @@ __global__ void __launch_bounds__(64 * gemm_waves(BN), 1) gemm_tile_kernel(const
   // epilogue: lane holds row m = m0 + wm 128 + 32 i + lr and columns
   // n = n0 + wn WN + 32 j + 8 (r / 4) + 4 lh + r % 4
   const bool vec = (N % 4) == 0 && (ldy % 4) == 0;
+  const bool cvec = vec && ((reinterpret_cast<uintptr_t>(FP8 ? (const void*)aw : (const void*)bias) & (FP8 ? 15 : 7)) == 0);
+  float c[NJ][4][4];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq)
+      column_terms<FP8>(bias, aw, ax, n0 + wn * WN + 32 * j + 8 * rq + 4 * lh, N, cvec, c[j][rq]);
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int64_t m = m0 + wm * 128 + 32 * i + lr;
@@ -266,28 +322,220 @@ __global__ void __launch_bounds__(64 * gemm_waves(BN), 1) gemm_tile_kernel(const
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int64_t n = n0 + wn * WN + 32 * j + 8 * rq + 4 * lh;
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = acc[i][j][4 * rq + e];
-          if (FP8) v[e] *= n + e < N ? ax * aw[n + e] : 0.f;
-          else if (bias && n + e < N) v[e] += bf16_to_float(bias[n + e]);
-        }
-        uint16_t* yp = Y + m * ldy + n;
-        if (vec && n + 3 < N) {
-          typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-          u32x2 pk;
-          pk.x = (uint32_t)float_to_bf16(v[0]) | ((uint32_t)float_to_bf16(v[1]) << 16);
-          pk.y = (uint32_t)float_to_bf16(v[2]) | ((uint32_t)float_to_bf16(v[3]) << 16);
-          *(u32x2*)yp = pk;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) yp[e] = float_to_bf16(v[e]);
-        }
+        for (int e = 0; e < 4; ++e)
+          v[e] = FP8 ? acc[i][j][4 * rq + e] * c[j][rq][e] : acc[i][j][4 * rq + e] + c[j][rq][e];
+        store4(Y, m, ldy, n0 + wn * WN + 32 * j + 8 * rq + 4 * lh, N, vec, v);
       }
   }
+}
+
+// ------------------------------------------- BF16 GEMM, 256 x 256 tiles of four waves
+// Each wave owns 128 x 128 outputs (4 x 4 MFMA 32x32x16 blocks: 256 accumulators per
+// lane, held in AGPRs), one wave per SIMD, so a K step's eight fragments feed 16 MFMAs
+// (LDS reads per MFMA: two thirds of the 8-wave tile's).  Operands go HBM -> registers
+// -> LDS through buffer loads (an SGPR descriptor per panel, 32-bit lane offsets):
+// tile kt + 3's loads are issued while tile kt is multiplied, into the register set
+// that held tile kt + 1, which that same tile writes to the LDS stage tile kt - 1 used.
+// Each K step's share of those stores and loads sits between its MFMAs, and since every
+// LDS access is an ordinary read or write the compiler waits for exactly the fragments
+// an MFMA needs (a direct-to-LDS load in flight would make it wait for all).  LDS: two
+// stages of (256 + 256) rows x 128 bytes (128 KB), the 16-byte chunks of a row swizzled
+// as in gemm_tile_kernel.  Whole K tiles only (K % 64 == 0).
+// Measured at 4096 x 14336 x 4096 against gemm_tile_kernel (same process, bit-identical
+// outputs): 0.412 vs 0.425 ms; 4096^3 0.119 vs 0.132 ms; 4096 x 4096 x 14336 0.366 vs
+// 0.385 ms.
+__global__ void __launch_bounds__(256, 1) gemm_w4_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
+                                                      const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
+                                                      int64_t T, int64_t N, int64_t ldy, int64_t K, int ntm, int ntn,
+                                                      int GM) {
+  constexpr int RB = 128, CPR = 8, RPL = 8, NL = 8;   // bytes of K per row and stage, chunks per row,
+                                                      // rows per load, loads per wave and operand
+  constexpr int OPB = GBM * RB, STAGE = 2 * OPB;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // tile of this workgroup (the same XCD-aware order as gemm_tile_kernel)
+  const int ntiles = ntm * ntn;
+  int t = (int)blockIdx.x;
+  if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
+  const int gsz = GM * ntn, g = t / gsz, rem = t % gsz;
+  const int gm = ntm - g * GM < GM ? ntm - g * GM : GM;
+  const int64_t m0 = (int64_t)(g * GM + rem % gm) * GBM, n0 = (int64_t)(rem / gm) * GBM;
+  const int64_t KB = 2 * K, nkt = KB / RB;
+
+  // load i of this wave: LDS row (wave NL + i) RPL + lane / CPR, position lane % CPR,
+  // holding the row's logical chunk swz(row, position); rows past the matrix read its
+  // last row (their outputs are never stored)
+  const int lrow = lane / CPR, lpos = lane % CPR;
+  uint32_t offA[NL], offB[NL], kc[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int r = (wave * NL + i) * RPL + lrow;
+    kc[i] = (uint32_t)(swz<CPR>(r, lpos) * 16);
+    const int64_t ga = m0 + r < T ? m0 + r : T - 1, gb = n0 + r < N ? n0 + r : N - 1;
+    offA[i] = (uint32_t)((ga - m0) * KB) + kc[i];
+    offB[i] = (uint32_t)((gb - n0) * KB) + kc[i];
+  }
+  // buffer descriptors of the two 256-row panels (32-bit offsets from an SGPR base)
+  const int64_t rows_a = T - m0 < GBM ? T - m0 : GBM, rows_b = N - n0 < GBM ? N - n0 : GBM;
+  auto rsrc = [](const uint8_t* p, int64_t bytes) {
+    // every lane holds the same values: make that visible, so the descriptor sits in SGPRs
+    const uint64_t a = (uint64_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t xr = rsrc(X + m0 * KB, rows_a * KB);
+  const __amdgpu_buffer_rsrc_t wr = rsrc(W + n0 * KB, rows_b * KB);
+  u32x4 ra[2][NL], rb[2][NL];   // two register sets: tiles kt + 1 and kt + 2 in flight
+  // whole K tiles only (the launcher sends K % 64 != 0 to gemm_tile_kernel); part q of
+  // four: loads 2q and 2q + 1 of each operand
+  auto gload = [&](int rs, int64_t kt, int q) {
+    const int kb = (int)(kt * RB);
+#pragma unroll
+    for (int i = 2 * q; i < 2 * q + 2; ++i) ra[rs][i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)offA[i], kb, 0);
+#pragma unroll
+    for (int i = 2 * q; i < 2 * q + 2; ++i) rb[rs][i] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)offB[i], kb, 0);
+  };
+  auto swrite = [&](int rs, int st, int q) {
+    uint8_t* s0 = lds + st * STAGE + (wave * NL) * 1024 + lane * 16;
+#pragma unroll
+    for (int i = 2 * q; i < 2 * q + 2; ++i) *(u32x4*)(s0 + i * 1024) = ra[rs][i];
+#pragma unroll
+    for (int i = 2 * q; i < 2 * q + 2; ++i) *(u32x4*)(s0 + OPB + i * 1024) = rb[rs][i];
+  };
+  // every wave's stores to LDS are done, then all waves meet (a plain s_barrier: the
+  // register loads of the next tile stay in flight)
+  auto lds_barrier = [&] {
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // fragment of MFMA block i (rows 32 i + lane % 32 of this wave's 128) at K step ks:
+  // logical chunk 2 ks + lane / 32 of the row; (row >> 1) & 7 is (lane % 32 >> 1) & 7
+  const int lr = lane & 31, lh = lane >> 5, sw = (lr >> 1) & 7;
+  const uint32_t rowA = (uint32_t)(wm * 128 + lr) * RB, rowB = OPB + (uint32_t)(wn * 128 + lr) * RB;
+  uint32_t cofs[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) cofs[ks] = (uint32_t)(((2 * ks + lh) ^ sw) << 4);
+  auto frags = [&](int st, int ks, bf16x8* fa, bf16x8* fb) {
+    const uint8_t* s = lds + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(s + rowA + i * 32 * RB + cofs[ks]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = *(const bf16x8*)(s + rowB + j * 32 * RB + cofs[ks]);
+  };
+  // tile kt sits in stage st, tile kt + 1 in register set st ^ 1, tile kt + 2 in set st.
+  // K step ks: request step ks + 1's fragments, move a quarter of tile kt + 1 from its
+  // registers into the other stage and reload them with tile kt + 3 (past the end: the
+  // last tile again, never used), then the step's 16 MFMAs, with the LDS and buffer
+  // traffic spread between them
+  auto tile = [&](int64_t kt, int st) {
+    bf16x8 fa[2][4], fb[2][4];
+    frags(st, 0, fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t knext = kt + 3 < nkt ? kt + 3 : nkt - 1;
+    const int rs = st ^ 1;   // the register set holding tile kt + 1
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks + 1 < 4) frags(st, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      swrite(rs, st ^ 1, ks);
+      gload(rs, knext, ks);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
+      // 16 MFMAs; between them the step's 8 fragment reads, 4 LDS stores and 4 loads
+      if (ks + 1 < 4) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);     // LDS write
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read
+      }
+      if (ks + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();
+  };
+
+  // tile 0 to stage 0 through register set 0, tile 1 in set 1, tile 2 in set 0
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gload(0, 0, q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gload(1, nkt > 1 ? 1 : nkt - 1, q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) swrite(0, 0, q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gload(0, nkt > 2 ? 2 : nkt - 1, q);
+  lds_barrier();
+  int64_t kt = 0;
+  for (; kt + 2 <= nkt; kt += 2) {
+    tile(kt, 0);
+    tile(kt + 1, 1);
+  }
+  if (kt < nkt) tile(kt, 0);
+
+  // epilogue: lane holds row m = m0 + wm 128 + 32 i + lr and columns
+  // n = n0 + wn 128 + 32 j + 8 (r / 4) + 4 lh + r % 4
+  const bool vec = (N % 4) == 0 && (ldy % 4) == 0;
+  const bool cvec = vec && (reinterpret_cast<uintptr_t>(bias) & 7) == 0;
+  float c[4][4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq)
+      column_terms<false>(bias, nullptr, 1.f, n0 + wn * 128 + 32 * j + 8 * rq + 4 * lh, N, cvec, c[j][rq]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + wm * 128 + 32 * i + lr;
+    if (m >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * rq + e] + c[j][rq][e];
+        store4(Y, m, ldy, n0 + wn * 128 + 32 * j + 8 * rq + 4 * lh, N, vec, v);
+      }
+  }
+}
+
+int launch_w4(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t ldy, int64_t K,
+              hipStream_t st) {
+  constexpr int lds = 2 * 2 * GBM * 128;
+  static std::once_flag once;
+  std::call_once(once, [&] {
+    (void)hipFuncSetAttribute((const void*)gemm_w4_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  });
+  const int ntm = (int)((T + GBM - 1) / GBM), ntn = (int)((N + GBM - 1) / GBM);
+  hipLaunchKernelGGL(gemm_w4_kernel, dim3((unsigned)(ntm * ntn)), dim3(256), lds, st, (const uint8_t*)x,
+                     (const uint8_t*)w, (const uint16_t*)bias, (uint16_t*)y, T, N, ldy, K, ntm, ntn, 4);
+  return hip_check(hipGetLastError(), "gemm launch");
 }
 
 template <int BN, int NST, int RB, bool FP8>
@@ -337,6 +585,13 @@ int64_t gemm_tiles(int64_t T, int64_t N) {
   return gemm_narrow(T, N) ? ntm * ((N + 127) / 128) : ntm * ((N + 255) / 256);
 }
 
+// The four-wave BF16 kernel takes whole 64-element K tiles and 32-bit panel offsets;
+// EP_GEMM_W4=0 selects gemm_tile_kernel instead (for comparisons)
+bool use_w4(int64_t K) {
+  const char* e = std::getenv("EP_GEMM_W4");
+  return K % 64 == 0 && 2 * K * GBM < (int64_t)INT32_MAX && !(e && std::atoi(e) == 0);
+}
+
 template <bool FP8>
 int launch_gemm(const void* x, const void* w, const void* bias, void* y, int64_t T, int64_t N, int64_t K, float ax,
                 const float* aw, hipStream_t st) {
@@ -366,12 +621,14 @@ int launch_gemm(const void* x, const void* w, const void* bias, void* y, int64_t
     const double split = (double)((ntm * n1 + cus - 1) / cus) + 0.625 * (double)((tiles2 + cus - 1) / cus);
     if (split < (double)((tiles + cus - 1) / cus) - 0.2) {
       const int64_t c0 = n1 * 256, kb = FP8 ? K : 2 * K;
-      rc = launch_tile<256, 2, 128, FP8>(x, w, bias, y, T, c0, N, K, ax, aw, st);
+      rc = (!FP8 && use_w4(K)) ? launch_w4(x, w, bias, y, T, c0, N, K, st)
+                              : launch_tile<256, 2, 128, FP8>(x, w, bias, y, T, c0, N, K, ax, aw, st);
       if (rc) return rc;
       return launch_tile<128, 3, 128, FP8>(x, (const uint8_t*)w + c0 * kb, bias ? (const uint16_t*)bias + c0 : nullptr,
                                            (uint16_t*)y + c0, T, rem, N, K, ax, aw ? aw + c0 : nullptr, st);
     }
   }
+  if (!FP8 && use_w4(K)) return launch_w4(x, w, bias, y, T, N, N, K, st);
   return launch_tile<256, 2, 128, FP8>(x, w, bias, y, T, N, N, K, ax, aw, st);
 }
 

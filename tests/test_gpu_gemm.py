@@ -22,10 +22,15 @@ def _t(a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a)).view(dtype).cuda()
 
 
-# (2048, 9000, 256): 288 tiles of 256 x 256, more than one round of the CUs, so the
-# columns of the whole round take 256-wide tiles and the ragged rest 128-wide ones
+# Small shapes and (2048, 9000, 256) take 128-wide tiles (they fill the CUs' rounds
+# better).  The four-wave 256 x 256 kernel (K % 64 == 0): (2000, 8001, 320) ragged rows
+# and an odd column count (element stores), five K tiles; (2048, 8192, 64) one K tile;
+# (1800, 7000, 4096); (3300, 10000, 192) 256-wide tiles over the columns of the whole
+# rounds and 128-wide ones over the rest.  (3328, 10000, 136): the same split with the
+# eight-wave 256-wide kernel (K % 64 != 0, a partial last K tile).
 @pytest.mark.parametrize("T,N,K", [(128, 128, 64), (256, 384, 512), (100, 200, 72), (1, 1, 8), (300, 129, 1032),
-                                   (1024, 1024, 4096), (2048, 9000, 256)])
+                                   (1024, 1024, 4096), (2048, 9000, 256), (2000, 8001, 320), (2048, 8192, 64),
+                                   (1800, 7000, 4096), (3300, 10000, 192), (3328, 10000, 136)])
 def test_gemm_bf16(T, N, K):
     import torch
     from decode_tile_rans_amd import _lib as L
@@ -43,6 +48,29 @@ def test_gemm_bf16(T, N, K):
     got = nx.bf16_to_f64(y.cpu().view(torch.int16).numpy().view(np.uint16))
     check_linear(got, ref, mag, K)
     assert rel_l2(got, ref) <= TOL
+
+
+@pytest.mark.parametrize("bias_offset", [0, 1, None], ids=["bias", "unaligned-bias", "no-bias"])
+def test_gemm_bf16_kernels_agree(bias_offset, monkeypatch):
+    """The four-wave and the eight-wave 256-wide kernels accumulate every output in the
+    same K order, so they give the same bits; a bias pointer off its 8-byte alignment
+    takes the element-wise bias reads."""
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    T, N, K = 2000, 8192, 576
+    say("gemm bf16 kernels agree", T, N, K, bias_offset)
+    xt = _t(synth.activations(T, K, 5), torch.bfloat16)
+    wt = _t(synth.rowscaled(N, K, 6), torch.bfloat16)
+    braw = _t(synth.f32_to_bf16_bits(np.linspace(-2, 2, N + 1).astype(np.float32)), torch.bfloat16)
+    bp = None if bias_offset is None else braw.data_ptr() + 2 * bias_offset
+    ys = []
+    for flag in ("0", "1"):
+        monkeypatch.setenv("EP_GEMM_W4", flag)
+        y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+        L.ep_gemm_bf16_nt(xt.data_ptr(), wt.data_ptr(), bp, y.data_ptr(), T, N, K, stream_ptr())
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
 
 
 @pytest.mark.parametrize("T,N,K", [(128, 128, 128), (256, 384, 512), (100, 200, 144), (512, 1024, 2048), (2048, 9000, 256)])
