@@ -332,20 +332,23 @@ __global__ void __launch_bounds__(64 * gemm_waves(BN), 1) gemm_tile_kernel(const
 }
 
 // ------------------------------------------- BF16 GEMM, 256 x 256 tiles of four waves
-// Each wave owns 128 x 128 outputs (4 x 4 MFMA 32x32x16 blocks: 256 accumulators per
-// lane, held in AGPRs), one wave per SIMD, so a K step's eight fragments feed 16 MFMAs
-// (LDS reads per MFMA: two thirds of the 8-wave tile's).  Operands go HBM -> registers
-// -> LDS through buffer loads (an SGPR descriptor per panel, 32-bit lane offsets):
-// tile kt + 3's loads are issued while tile kt is multiplied, into the register set
-// that held tile kt + 1, which that same tile writes to the LDS stage tile kt - 1 used.
-// Each K step's share of those stores and loads sits between its MFMAs, and since every
-// LDS access is an ordinary read or write the compiler waits for exactly the fragments
-// an MFMA needs (a direct-to-LDS load in flight would make it wait for all).  LDS: two
-// stages of (256 + 256) rows x 128 bytes (128 KB), the 16-byte chunks of a row swizzled
-// as in gemm_tile_kernel.  Whole K tiles only (K % 64 == 0).
-// Measured at 4096 x 14336 x 4096 against gemm_tile_kernel (same process, bit-identical
-// outputs): 0.412 vs 0.425 ms; 4096^3 0.119 vs 0.132 ms; 4096 x 4096 x 14336 0.366 vs
-// 0.385 ms.
+// Each wave owns 128 x 128 outputs (8 x 8 MFMA 16x16x32 blocks: 256 accumulators per
+// lane, held in AGPRs), one wave per SIMD, so a 32-element K step's sixteen fragments
+// feed 64 MFMAs (LDS reads per MFMA: two thirds of the 8-wave tile's).  Operands go HBM
+// -> registers -> LDS through buffer loads (an SGPR descriptor per panel, 32-bit lane
+// offsets): tile kt + 2's loads are issued while tile kt is multiplied, into the
+// registers that held tile kt + 1, which that same tile writes to the LDS stage tile
+// kt - 1 used.  Each K step's share of those stores and loads sits between its MFMAs,
+// and since every LDS access is an ordinary read or write the compiler waits for
+// exactly the fragments an MFMA needs (a direct-to-LDS load in flight would make it wait
+// for all).  LDS: two stages of (256 + 256) rows x 128 bytes (128 KB), the 16-byte chunks
+// of a row swizzled as in gemm_tile_kernel (conflict-free for 16-row fragments too).
+// Whole K tiles only (K % 64 == 0).
+// Measured against gemm_tile_kernel (same process, bit-identical outputs):
+// 4096 x 14336 x 4096 0.395 vs 0.423 ms, 4096^3 0.113 vs 0.124 ms, 4096 x 4096 x 14336
+// 0.347 vs 0.388 ms.  Also measured and not kept: 32x32x16 blocks (0.412 ms at the first
+// shape), a second register set for a two-tile load lead (1-3 %), and direct-to-LDS loads
+// into per-stage LDS arrays (no faster than the register path).
 __global__ void __launch_bounds__(256, 1) gemm_w4_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
                                                       const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
                                                       int64_t T, int64_t N, int64_t ldy, int64_t K, int ntm, int ntn,
@@ -392,22 +395,22 @@ __global__ void __launch_bounds__(256, 1) gemm_w4_kernel(const uint8_t* __restri
   };
   const __amdgpu_buffer_rsrc_t xr = rsrc(X + m0 * KB, rows_a * KB);
   const __amdgpu_buffer_rsrc_t wr = rsrc(W + n0 * KB, rows_b * KB);
-  u32x4 ra[2][NL], rb[2][NL];   // two register sets: tiles kt + 1 and kt + 2 in flight
-  // whole K tiles only (the launcher sends K % 64 != 0 to gemm_tile_kernel); part q of
-  // four: loads 2q and 2q + 1 of each operand
-  auto gload = [&](int rs, int64_t kt, int q) {
+  u32x4 ra[NL], rb[NL];
+  // whole K tiles only (the launcher sends K % 64 != 0 to gemm_tile_kernel); half h:
+  // loads 4h .. 4h + 3 of each operand
+  auto gload = [&](int64_t kt, int h) {
     const int kb = (int)(kt * RB);
 #pragma unroll
-    for (int i = 2 * q; i < 2 * q + 2; ++i) ra[rs][i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)offA[i], kb, 0);
+    for (int i = 4 * h; i < 4 * h + 4; ++i) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)offA[i], kb, 0);
 #pragma unroll
-    for (int i = 2 * q; i < 2 * q + 2; ++i) rb[rs][i] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)offB[i], kb, 0);
+    for (int i = 4 * h; i < 4 * h + 4; ++i) rb[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)offB[i], kb, 0);
   };
-  auto swrite = [&](int rs, int st, int q) {
+  auto swrite = [&](int st, int h) {
     uint8_t* s0 = lds + st * STAGE + (wave * NL) * 1024 + lane * 16;
 #pragma unroll
-    for (int i = 2 * q; i < 2 * q + 2; ++i) *(u32x4*)(s0 + i * 1024) = ra[rs][i];
+    for (int i = 4 * h; i < 4 * h + 4; ++i) *(u32x4*)(s0 + i * 1024) = ra[i];
 #pragma unroll
-    for (int i = 2 * q; i < 2 * q + 2; ++i) *(u32x4*)(s0 + OPB + i * 1024) = rb[rs][i];
+    for (int i = 4 * h; i < 4 * h + 4; ++i) *(u32x4*)(s0 + OPB + i * 1024) = rb[i];
   };
   // every wave's stores to LDS are done, then all waves meet (a plain s_barrier: the
   // register loads of the next tile stay in flight)
@@ -418,79 +421,76 @@ __global__ void __launch_bounds__(256, 1) gemm_w4_kernel(const uint8_t* __restri
     asm volatile("" ::: "memory");
   };
 
-  f32x16 acc[4][4];
+  typedef __attribute__((ext_vector_type(4))) float f32x4;
+  f32x4 acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
-  // fragment of MFMA block i (rows 32 i + lane % 32 of this wave's 128) at K step ks:
-  // logical chunk 2 ks + lane / 32 of the row; (row >> 1) & 7 is (lane % 32 >> 1) & 7
-  const int lr = lane & 31, lh = lane >> 5, sw = (lr >> 1) & 7;
+  // fragment of MFMA block i (rows 16 i + lane % 16 of this wave's 128) at K step ks
+  // (32 elements): logical chunk 4 ks + lane / 16 of the row; (row >> 1) & 7 is
+  // (lane % 16 >> 1) & 7
+  const int lr = lane & 15, lq = lane >> 4, sw = (lr >> 1) & 7;
   const uint32_t rowA = (uint32_t)(wm * 128 + lr) * RB, rowB = OPB + (uint32_t)(wn * 128 + lr) * RB;
-  uint32_t cofs[4];
+  uint32_t cofs[2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) cofs[ks] = (uint32_t)(((2 * ks + lh) ^ sw) << 4);
+  for (int ks = 0; ks < 2; ++ks) cofs[ks] = (uint32_t)(((4 * ks + lq) ^ sw) << 4);
   auto frags = [&](int st, int ks, bf16x8* fa, bf16x8* fb) {
     const uint8_t* s = lds + st * STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(s + rowA + i * 32 * RB + cofs[ks]);
+    for (int i = 0; i < 8; ++i) fa[i] = *(const bf16x8*)(s + rowA + i * 16 * RB + cofs[ks]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = *(const bf16x8*)(s + rowB + j * 32 * RB + cofs[ks]);
+    for (int j = 0; j < 8; ++j) fb[j] = *(const bf16x8*)(s + rowB + j * 16 * RB + cofs[ks]);
   };
-  // tile kt sits in stage st, tile kt + 1 in register set st ^ 1, tile kt + 2 in set st.
-  // K step ks: request step ks + 1's fragments, move a quarter of tile kt + 1 from its
-  // registers into the other stage and reload them with tile kt + 3 (past the end: the
-  // last tile again, never used), then the step's 16 MFMAs, with the LDS and buffer
-  // traffic spread between them
+  // tile kt sits in stage st and tile kt + 1 in the registers.  K step ks (of two):
+  // step 1's fragments requested during step 0, half of tile kt + 1 moved from the
+  // registers to the other stage and those registers reloaded with tile kt + 2 (past the
+  // end: the last tile again, never used), spread between the step's 64 MFMAs
   auto tile = [&](int64_t kt, int st) {
-    bf16x8 fa[2][4], fb[2][4];
+    bf16x8 fa[2][8], fb[2][8];
     frags(st, 0, fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
-    const int64_t knext = kt + 3 < nkt ? kt + 3 : nkt - 1;
-    const int rs = st ^ 1;   // the register set holding tile kt + 1
+    const int64_t knext = kt + 2 < nkt ? kt + 2 : nkt - 1;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks + 1 < 4) frags(st, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-      swrite(rs, st ^ 1, ks);
-      gload(rs, knext, ks);
+    for (int ks = 0; ks < 2; ++ks) {
+      if (ks == 0) frags(st, 1, fa[1], fb[1]);
+      swrite(st ^ 1, ks);
+      gload(knext, ks);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
-      // 16 MFMAs; between them the step's 8 fragment reads, 4 LDS stores and 4 loads
-      if (ks + 1 < 4) {
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+      if (ks == 0) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        for (int r = 0; r < 16; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 8; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);     // LDS write
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read
       }
-      if (ks + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      else __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+      if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x008, 56, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     lds_barrier();
   };
 
-  // tile 0 to stage 0 through register set 0, tile 1 in set 1, tile 2 in set 0
+  // tile 0 to stage 0, tile 1 in the registers
 #pragma unroll
-  for (int q = 0; q < 4; ++q) gload(0, 0, q);
+  for (int h = 0; h < 2; ++h) gload(0, h);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) gload(1, nkt > 1 ? 1 : nkt - 1, q);
+  for (int h = 0; h < 2; ++h) swrite(0, h);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) swrite(0, 0, q);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) gload(0, nkt > 2 ? 2 : nkt - 1, q);
+  for (int h = 0; h < 2; ++h) gload(nkt > 1 ? 1 : 0, h);
   lds_barrier();
   int64_t kt = 0;
   for (; kt + 2 <= nkt; kt += 2) {
@@ -499,29 +499,24 @@ __global__ void __launch_bounds__(256, 1) gemm_w4_kernel(const uint8_t* __restri
   }
   if (kt < nkt) tile(kt, 0);
 
-  // epilogue: lane holds row m = m0 + wm 128 + 32 i + lr and columns
-  // n = n0 + wn 128 + 32 j + 8 (r / 4) + 4 lh + r % 4
+  // epilogue: lane holds row m = m0 + wm 128 + 16 i + lane % 16 and columns
+  // n = n0 + wn 128 + 16 j + 4 (lane / 16) + r
   const bool vec = (N % 4) == 0 && (ldy % 4) == 0;
   const bool cvec = vec && (reinterpret_cast<uintptr_t>(bias) & 7) == 0;
-  float c[4][4][4];
+  float c[8][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 8; ++j) column_terms<false>(bias, nullptr, 1.f, n0 + wn * 128 + 16 * j + 4 * lq, N, cvec, c[j]);
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq)
-      column_terms<false>(bias, nullptr, 1.f, n0 + wn * 128 + 32 * j + 8 * rq + 4 * lh, N, cvec, c[j][rq]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + wm * 128 + 32 * i + lr;
+  for (int i = 0; i < 8; ++i) {
+    const int64_t m = m0 + wm * 128 + 16 * i + lr;
     if (m >= T) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j) {
+      float v[4];
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * rq + e] + c[j][rq][e];
-        store4(Y, m, ldy, n0 + wn * 128 + 32 * j + 8 * rq + 4 * lh, N, vec, v);
-      }
+      for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] + c[j][e];
+      store4(Y, m, ldy, n0 + wn * 128 + 16 * j + 4 * lq, N, vec, v);
+    }
   }
 }
 
