@@ -347,8 +347,10 @@ __global__ void __launch_bounds__(64 * gemm_waves(BN), 1) gemm_tile_kernel(const
 // Measured against gemm_tile_kernel (same process, bit-identical outputs):
 // 4096 x 14336 x 4096 0.395 vs 0.423 ms, 4096^3 0.113 vs 0.124 ms, 4096 x 4096 x 14336
 // 0.347 vs 0.388 ms.  Also measured and not kept: 32x32x16 blocks (0.412 ms at the first
-// shape), a second register set for a two-tile load lead (1-3 %), and direct-to-LDS loads
-// into per-stage LDS arrays (no faster than the register path).
+// shape), a second register set for a two-tile load lead (1-3 %), direct-to-LDS loads
+// into per-stage LDS arrays (no faster than the register path), and the same tile for
+// FP8 codes with 16x16x128 blocks (bit-identical to gemm_tile_kernel but 4-15 % slower:
+// a K tile is a single MFMA step, so its fragments cannot be requested a step ahead).
 __global__ void __launch_bounds__(256, 1) gemm_w4_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
                                                       const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
                                                       int64_t T, int64_t N, int64_t ldy, int64_t K, int ntm, int ntn,
