@@ -106,9 +106,9 @@ def test_workgroup_sizes(waves):
     _check(f"waves={waves}", synth.rowscaled(257, 1024, 8), nx.DT_BF16, 4.0, S=8, env={"EP_DECODE_WAVES": waves})
 
 
-# Two chains per lane (the forward and backward chain of one region, interleaved): the
-# launch takes this shape by itself from 512 blocks on; here it is forced on small cases
-# that cover odd chain counts (a region with a forward chain only), chains that finish a
+# Two chains per lane (two blocks interleaved, 64-byte rings without a mirror, reads
+# wrapping): a spread launch takes this shape by itself when its blocks fit one round of
+# it; here it is forced on small cases that cover odd chain counts, chains that finish a
 # group earlier than their partner, several blocks per workgroup, escapes and containers.
 ILP2_CASES = [
     ("ragged 37x13", lambda: synth.rowscaled(37, 13, 50), nx.DT_BF16, 4.0, None, "1"),
