@@ -420,6 +420,7 @@ def fused_linear(target_bpp, reps=10):
     # second stream while this layer's GEMM runs, against the same GEMMs on plain weights
     seq = linear_sequence(c, wbits, target_bpp, timeit)
     small = small_batch(c, w, x, ws, need, wd, sp, timeit)
+    prefill = prefill_fused(c, w, x, ws, need, sp, timeit)
     sweep = token_sweep(c, w, ws, need, sp, timeit)
     return {
         "workload": "CompressedLinear prefill 14336x4096 weight @%.1f bpp, 4096 tokens" % target_bpp,
@@ -432,6 +433,7 @@ def fused_linear(target_bpp, reps=10):
         "gemm_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 1),
         "sequence_overlapped": seq,
         "small_batch": small,
+        "prefill_fused": prefill,
         "token_sweep": sweep,
     }
 
@@ -457,6 +459,35 @@ def token_sweep(c, w, ws, need, sp, timeit):
         out.append({"tokens": T, "ms_decode_plus_gemm": round(t_f, 4), "ms_gemm": round(t_p, 4),
                     "overhead_pct": round(100.0 * (t_f / t_p - 1.0), 2)})
         del x, y
+    return out
+
+
+def prefill_fused(c, w, x, ws, need, sp, timeit):
+    """The same layer on 16..256 tokens: the fused prefill product (each K slab of W decoded
+    into an LDS operand tile of the MFMA product; weights never written) against decode
+    then our GEMM (ep_compressed_linear_forward), our GEMM and hipBLASLt on the plain
+    BF16 weight."""
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    R, C = c.shape
+    out = []
+
+    def best(fn):
+        return min(timeit(fn) for _ in range(3))
+
+    for T in (16, 32, 64, 128, 192, 256):
+        xs = x[:T].contiguous()
+        y = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
+        t_mma = best(lambda: L.ep_compressed_linear_prefill(c.handle, xs.data_ptr(), T, None, y.data_ptr(), sp))
+        t_two = best(lambda: L.ep_compressed_linear_forward(c.handle, xs.data_ptr(), T, None, y.data_ptr(),
+                                                             ws.data_ptr(), need, sp))
+        t_gemm = best(lambda: L.ep_gemm_bf16_nt(xs.data_ptr(), w.data_ptr(), None, y.data_ptr(), T, R, C, sp))
+        t_plain = best(lambda: torch.matmul(xs, w.t()))
+        out.append({"tokens": T, "ms_fused_prefill": round(t_mma, 4), "ms_decode_then_gemm": round(t_two, 4),
+                    "ms_our_gemm_plain_bf16": round(t_gemm, 4), "ms_hipblaslt_plain_bf16": round(t_plain, 4),
+                    "fused_speedup_vs_decode_then_gemm": round(t_two / t_mma, 3),
+                    "fused_tflops": round(2.0 * T * R * C / (t_mma * 1e-3) / 1e12, 1),
+                    "fused_blob_gbs": round(c.nbytes / (t_mma * 1e-3) / 1e9, 1)})
     return out
 
 

@@ -37,6 +37,7 @@ SIGNATURES = {
     "ep_matvec_workspace_bytes": (_sz, [_vp, _i64]),
     "ep_compressed_matvec": (_int, [_vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "ep_compressed_matvec_noalloc": (_int, [_vp, _vp, _i64, _vp, _vp, _vp]),
+    "ep_compressed_linear_prefill": (_int, [_vp, _vp, _i64, _vp, _vp, _vp]),
     "ep_test_cast": (_int, [_int, _vp, _vp, _i64, _int, _vp]),
     "ep_matvec_batch_workspace_bytes": (_sz, [C.POINTER(_vp), _int, _i64]),
     "ep_compressed_matvec_batch": (_int, [C.POINTER(_vp), _int, _vp, _i64, C.POINTER(_vp), C.POINTER(_vp), _vp, _sz,
@@ -161,6 +162,10 @@ def ep_compressed_matvec(blob, dev_x, T, dev_bias, dev_y, dev_ws, ws_bytes, stre
 
 def ep_compressed_matvec_noalloc(blob, dev_x, T, dev_bias, dev_y, stream=0):
     check(lib().ep_compressed_matvec_noalloc(blob, dev_x, T, dev_bias, dev_y, stream))
+
+
+def ep_compressed_linear_prefill(blob, dev_x, T, dev_bias, dev_y, stream=0):
+    check(lib().ep_compressed_linear_prefill(blob, dev_x, T, dev_bias, dev_y, stream))
 
 
 def _ptrs(seq):

@@ -23,6 +23,7 @@
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -45,10 +46,18 @@ enum OutKind { OUT_BF16 = 0, OUT_BF16_SAT = 1, OUT_FP16 = 2, OUT_FP32 = 3, OUT_F
                // weights are multiplied into per-chain partial sums and never stored
                OUT_MV1 = 8, OUT_MV2 = 9, OUT_MV4 = 10, OUT_MV8 = 11,
                // BF16 stored through the caches (a GEMM reads the weights right after)
-               OUT_BF16_L2 = 12 };
+               OUT_BF16_L2 = 12,
+               // fused prefill product: each K slab of BF16 weights goes to an LDS operand
+               // tile that MFMAs multiply by up to 128 (MMA1) or 256 (MMA2) activation rows
+               OUT_MMA1 = 13, OUT_MMA2 = 14 };
 template <int OUT>
 constexpr int mv_tokens() {
   return (OUT >= OUT_MV1 && OUT <= OUT_MV8) ? 1 << (OUT - OUT_MV1) : 0;
+}
+// 16-row activation blocks per wave of the fused prefill product (0: another output)
+template <int OUT>
+constexpr int mma_blocks() {
+  return OUT == OUT_MMA1 ? 1 : OUT == OUT_MMA2 ? 2 : 0;
 }
 template <int OUT>
 constexpr int out_elem_bytes() {
@@ -87,6 +96,8 @@ struct DecJob {
   // sums out[(chain * mv_slots + row - first row of the chain) * tokens + t]
   const uint16_t* mv_x;
   uint32_t mv_T, mv_slots, mv_sat;
+  const uint16_t* bias;        // fused prefill product: BF16 bias of the R outputs, or null
+  uint32_t big_h;              // some |128 h_r| overflows float: reconstruct as h u
 };
 
 // ---------------------------------------------------------------- container stores
@@ -701,6 +712,10 @@ struct GroupCtx {
   uint32_t G;
   int S;
   bool rowwise;
+  // fused prefill product: LDS address of the operand tiles, of this lane's row in the
+  // first one and that row's chunk swizzle; the workgroup's first output column
+  uint32_t bt_base, bt_row, bt_swz;
+  int64_t mma_n0;
 };
 
 // Fused matrix-vector product: a chain's running dot products of its weights in the
@@ -726,6 +741,88 @@ __device__ __forceinline__ void mv_flush(const DecJob& J, MvAcc& m) {
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) m.a[t] = 0.f;
+}
+
+// ---- fused prefill product (OUT_MMA*): Y[T x R] = X[T x 4096] W^T (+ bias) with W decoded
+// into LDS.  A blob of 4096 columns at S = 8 has one tile per row, so a wave's block of
+// 64 chains is 8 rows of W and, at a chain's group pair kk, kk + 1, the 8 chains of a row
+// yield its columns 64 kk .. 64 kk + 127 in chunks of 8.  A workgroup of 8 waves (64 rows
+// of W, 64 output columns) writes each pair's 64 x 128 BF16 slab to one of two LDS
+// operand tiles (rows of 256 bytes, 16-byte chunks XOR-swizzled by the row), meets at a
+// barrier, and every wave multiplies the slab by its own 16-row blocks of X (wave w: rows
+// 16 (w + 8 b) .. + 15, b < MB), read straight from memory into registers at the start
+// of the pair: v_mfma_f32_16x16x32_bf16 with the W fragment first, so a lane ends with
+// four consecutive output columns of one activation row.  The weights never leave LDS.
+constexpr int kMmaWaves = 8;
+constexpr uint32_t kBRowBytes = 256;
+constexpr uint32_t kBTileBytes = 64 * kBRowBytes;
+constexpr int kPrefillMaxT = 16 * kMmaWaves * 2;   // 256 activation rows
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// activation fragments of slab `it` (columns 128 it .. + 127): block b, K step ks
+template <int MB>
+__device__ __forceinline__ void mma_xload(const DecJob& J, int it, int wave, int lane, u32x4 (&xf)[MB][4]) {
+  const int lr = lane & 15, lq = lane >> 4;
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    const uint32_t t = (uint32_t)((wave + kMmaWaves * b) * 16 + lr);
+    const uint32_t tt = t < J.mv_T ? t : J.mv_T - 1u;
+    const uint16_t* xp = J.mv_x + (int64_t)tt * J.C + it * 128 + 8 * lq;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) xf[b][ks] = *(const u32x4*)(xp + 32 * ks);
+  }
+}
+// the slab in operand tile `buf` times this wave's activation blocks
+template <int MB>
+__device__ __forceinline__ void mma_slab(const GroupCtx& X, uint32_t buf, int lane, const u32x4 (&xf)[MB][4],
+                                         f32x4 (&acc)[MB][4]) {
+  const uint32_t lr = (uint32_t)lane & 15u, lq = (uint32_t)lane >> 4;
+  const uint32_t base = X.bt_base + buf * kBTileBytes;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const uint32_t row = 16u * (uint32_t)cb + lr;   // (row & 15 == lr)
+      const uint32_t a = base + row * kBRowBytes + ((((uint32_t)ks * 4u + lq) ^ lr) << 4);
+      const bf16x8 wf = *(const EP_LDS bf16x8*)(uintptr_t)a;
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+        acc[b][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, __builtin_bit_cast(bf16x8, xf[b][ks]), acc[b][cb], 0, 0, 0);
+    }
+  }
+}
+// outputs: lane l holds activation row 16 (w + 8 b) + l % 16, output columns
+// mma_n0 + 16 cb + 4 (l / 16) .. + 3; bias added, rounded to BF16 (nearest even)
+template <int MB>
+__device__ __forceinline__ void mma_store(const GroupCtx& X, int wave, int lane, const f32x4 (&acc)[MB][4]) {
+  const DecJob& J = *X.J;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int64_t N = J.R;
+  uint16_t* Y = (uint16_t*)J.out;
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    const int64_t t = (int64_t)(wave + kMmaWaves * b) * 16 + lr;
+    if (t >= (int64_t)J.mv_T) continue;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int64_t n = X.mma_n0 + 16 * cb + 4 * lq;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float bb = (J.bias && n + e < N) ? __uint_as_float((uint32_t)J.bias[n + e] << 16) : 0.f;
+        v[e] = acc[b][cb][e] + bb;
+      }
+      uint16_t* yp = Y + t * N + n;
+      if ((N & 3) == 0 && n + 3 < N) {
+        *(uint2*)yp = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) yp[e] = (uint16_t)(pack_bf16x2(v[e], 0.f) & 0xFFFFu);
+      }
+    }
+  }
 }
 
 // Row scale of group kk: move to the next row at a precomputed group count, then issue
@@ -935,7 +1032,31 @@ __device__ __forceinline__ void decode_group(const GroupCtx& X, int kk, Chain* r
         else w[i] = LY::w_of(e[c][i], rs[c].h, rs[c].nh);
       }
     }
-    if constexpr (NT > 0) {
+    if constexpr (NARROW && !ESC && OUT != OUT_COORDS) {
+      // rows whose -128 h_r overflows: the plain product (a branch uniform per blob)
+      if (J.big_h) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = rs[c].h * (float)LY::u_of(e[c][i]);
+      }
+    }
+    if constexpr (mma_blocks<OUT>() > 0) {
+      // the weights as the BF16 container holds them, to this row's chunk of the slab
+      // (every lane writes, also past the matrix: those rows feed no stored output)
+      uint32_t p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a = w[2 * i], b = w[2 * i + 1];
+        if (J.mv_sat) {
+          a = fminf(fmaxf(a, -3.38953139e38f), 3.38953139e38f);
+          b = fminf(fmaxf(b, -3.38953139e38f), 3.38953139e38f);
+        }
+        f32x2 fv = {a, b};
+        p[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(fv, bf16x2));
+      }
+      const uint32_t chunk = (((uint32_t)kk & 1u) << 3) | ((uint32_t)threadIdx.x & 7u);
+      const uint32_t at = X.bt_row + (((uint32_t)kk >> 1) & 1u) * kBTileBytes + ((chunk ^ X.bt_swz) << 4);
+      lds_st128(at, make_uint4(p[0], p[1], p[2], p[3]));
+    } else if constexpr (NT > 0) {
       if (act) {
         // the weights as the BF16 container holds them, then two products per dot step
         uint32_t p[4];
@@ -1142,12 +1263,25 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
   int nmax = ngr[0];
 #pragma unroll
   for (int c = 1; c < ILP; ++c) nmax = ngr[c] > nmax ? ngr[c] : nmax;
+  // fused prefill product: every lane of the workgroup runs all 64 groups (the slab
+  // barriers are workgroup-wide); chains past the matrix decode rows no output reads
+  constexpr int MB = mma_blocks<OUT>();
+  f32x4 macc[MB > 0 ? MB : 1][4];
+  u32x4 xf[MB > 0 ? MB : 1][4];
+  if constexpr (MB > 0) {
+    nmax = kTileGroups / 8;   // (S = 8)
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) macc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // two groups per iteration: the stream service runs before every even group, and
   // (blobs with escapes) before every odd one too
   // (the row scale of a group is settled before its service, so that its load is
   // followed by a fixed sequence of memory operations)
   for (int kk = 0; kk < nmax; kk += 2) {
+    if constexpr (MB > 0) mma_xload<MB>(J, kk >> 1, wave, lane, xf);
     if constexpr (OUT != OUT_BYTES) row_scale<ILP>(X, kk, rs, ngr);
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
@@ -1169,6 +1303,10 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
     }
 #pragma unroll
     for (int c = 0; c < ILP; ++c) ch_settle<MIR>(rd[c]);
+    if constexpr (MB > 0) {
+      __syncthreads();   // the pair's slab is in LDS (and the tile written next is free)
+      mma_slab<MB>(X, ((uint32_t)kk >> 1) & 1u, lane, xf, macc);
+    }
   }
   if constexpr (NT > 0) {
 #pragma unroll
@@ -1178,13 +1316,14 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
 #pragma unroll
   for (int c = 0; c < ILP; ++c)
     if (live[c] && ngr[c] > 0 && rd[c].x != kL) atomicAdd(J.err, 1u);
+  if constexpr (MB > 0) mma_store<MB>(X, wave, lane, macc);
 }
 
 // A workgroup stages the decode tables of its job into LDS once, then its waves take
 // the workgroup's blocks in turn (wave w: blocks w ILP, (w + W) ILP, ...).  Each job
 // gives every workgroup `bpw` consecutive blocks (the last one fewer).
 template <int OUT, bool ESC, bool C8, bool NARROW, int ILP, bool SEL>
-__global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
+__device__ __forceinline__ void decode_kernel_body(const DecBatch& B) {
   extern __shared__ __align__(16) uint32_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1220,6 +1359,17 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   X.rowwise = (uint32_t)X.S <= X.G;
   X.ctx_mask = J.ctx_mask;
   int64_t b = wg_blk0 + (int64_t)wave * ILP;
+  if constexpr (mma_blocks<OUT>() > 0) {
+    // fused prefill product: 8 waves of one block each (8 rows of W: S = 8, one tile a
+    // row), the operand tiles after the rings; waves past the matrix run too (barriers)
+    X.bt_base = X.lds0 + (uint32_t)kTabBytes + (uint32_t)(nwaves * 64 * ring_bytes<1>());
+    const uint32_t rho = (uint32_t)(wave * 8 + (lane >> 3));
+    X.bt_row = X.bt_base + rho * kBRowBytes;
+    X.bt_swz = rho & 15u;
+    X.mma_n0 = wg_blk0 * 8;
+    decode_blocks<OUT, ESC, C8, NARROW, ILP, SEL>(X, b, wg_blk1, lane, wave, st, true);
+    return;
+  }
   if (b >= wg_blk1) {   // a wave without blocks still stages its share
     st.issue();
     st.commit();
@@ -1227,6 +1377,15 @@ __global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
   }
   for (bool first = true; b < wg_blk1; b += (int64_t)nwaves * ILP, first = false)
     decode_blocks<OUT, ESC, C8, NARROW, ILP, SEL>(X, b, wg_blk1, lane, wave, st, first);
+}
+template <int OUT, bool ESC, bool C8, bool NARROW, int ILP, bool SEL>
+__global__ void __launch_bounds__(1024) decode_kernel(const DecBatch B) {
+  decode_kernel_body<OUT, ESC, C8, NARROW, ILP, SEL>(B);
+}
+// the fused prefill product: 8 waves a workgroup, so a lane may hold 256 registers
+template <int OUT, bool ESC, bool C8, bool NARROW, int ILP, bool SEL>
+__global__ void __launch_bounds__(64 * kMmaWaves) mma_kernel(const DecBatch B) {
+  decode_kernel_body<OUT, ESC, C8, NARROW, ILP, SEL>(B);
 }
 
 // ---------------------------------------------------------------- launch helpers
@@ -1253,8 +1412,11 @@ struct Shape {
 
 template <int OUT, bool ESC, bool C8, bool NARROW, int ILP, bool SEL>
 int launch_t(const DecBatch& B, int64_t n_wg, int waves, hipStream_t st) {
-  auto kern = decode_kernel<OUT, ESC, C8, NARROW, ILP, SEL>;
-  size_t lds = (size_t)kTabBytes + (size_t)waves * 64 * ILP * ring_bytes<ILP>();
+  void (*kern)(const DecBatch);
+  if constexpr (mma_blocks<OUT>() > 0) kern = mma_kernel<OUT, ESC, C8, NARROW, ILP, SEL>;
+  else kern = decode_kernel<OUT, ESC, C8, NARROW, ILP, SEL>;
+  size_t lds = (size_t)kTabBytes + (size_t)waves * 64 * ILP * ring_bytes<ILP>() +
+               (mma_blocks<OUT>() > 0 ? 2 * (size_t)kBTileBytes : 0);
   static std::once_flag once;
   std::call_once(once, [&] {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max_bytes());
@@ -1352,6 +1514,7 @@ DecJob make_job(const Blob& b, void* out) {
   j.ctx_mask = b.kind == kKindTileAns ? (uint32_t)(b.n_ctx - 1) : 0u;
   // TileANS stages only its contexts' tables
   j.tab_words = b.d_tab_words;
+  j.big_h = b.d_big_h ? 1u : 0u;
   return j;
 }
 
@@ -1674,6 +1837,50 @@ int decompress_beside(const Blob& b, void* dst, ep_stream st, int64_t max_wg) {
   return decode_one(b, dst, 0, b.n_chains, gemm_out_kind(b), (hipStream_t)st, max_wg);
 }
 
+// ---------------------------------------------------------------- fused prefill product
+bool prefill_supported(const Blob& b, int64_t T) {
+  return b.kind == kKindLossy && b.dtype == EP_BF16 && b.S == 8 && b.C == 8 * kTileGroups && T >= 1 &&
+         T <= kPrefillMaxT;
+}
+
+template <int OUT>
+int launch_mma(bool esc, bool narrow, const DecBatch& B, int64_t n_wg, hipStream_t st) {
+  if (narrow)
+    return esc ? launch_t<OUT, true, true, true, 1, false>(B, n_wg, kMmaWaves, st)
+               : launch_t<OUT, false, true, true, 1, false>(B, n_wg, kMmaWaves, st);
+  return esc ? launch_t<OUT, true, true, false, 1, false>(B, n_wg, kMmaWaves, st)
+             : launch_t<OUT, false, true, false, 1, false>(B, n_wg, kMmaWaves, st);
+}
+
+int prefill_launch(const Blob& b, const void* x, int64_t T, const void* bias, void* y, ep_stream stream) {
+  int rc = check_uploaded(b);
+  if (rc) return rc;
+  if (!prefill_supported(b, T))
+    return fail(EP_E_ARG, "the fused prefill product takes lossy BF16 blobs of 4096 columns at 8 chains per tile "
+                "and 1.." + std::to_string(kPrefillMaxT) + " activation rows");
+  if (!x || !y) return fail(EP_E_ARG, "null activations or output");
+  if (reinterpret_cast<uintptr_t>(x) & 15) return fail(EP_E_ARG, "activations must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(y) & 7) || (reinterpret_cast<uintptr_t>(bias) & 1))
+    return fail(EP_E_ARG, "output must be 8-byte aligned and bias 2-byte aligned");
+  if ((rc = check_gpu_pointer(x, "activations")) || (rc = check_gpu_pointer(y, "output")) ||
+      (bias && (rc = check_gpu_pointer(bias, "bias"))))
+    return rc;
+  DecJob j = make_job(b, y);
+  j.mv_x = (const uint16_t*)x;
+  j.mv_T = (uint32_t)T;
+  j.mv_sat = (b.flags & kFlagSat) ? 1u : 0u;
+  j.bias = (const uint16_t*)bias;
+  DecBatch B{};
+  B.j[0] = j;
+  B.n = 1;
+  B.bpw = kMmaWaves;   // one block (8 rows of W) per wave
+  const int64_t n_wg = (b.n_blocks + kMmaWaves - 1) / kMmaWaves;
+  const bool esc = (b.flags & kFlagEsc) != 0, narrow = b.k <= 5;
+  const hipStream_t st = (hipStream_t)stream;
+  return T <= kPrefillMaxT / 2 ? launch_mma<OUT_MMA1>(esc, narrow, B, n_wg, st)
+                               : launch_mma<OUT_MMA2>(esc, narrow, B, n_wg, st);
+}
+
 // ---------------------------------------------------------------- the fused product without a workspace
 // Partial sums of ep_compressed_matvec_noalloc: one file-scope device array (every GPU the
 // library runs on holds its own copy until the process ends).  Host code never passes
@@ -1763,6 +1970,11 @@ int ep_blob_upload(ep_blob* blob, ep_stream stream) {
     if (split) build_split_tables(b.model, (uint32_t*)&host[o_tab]);
     else build_slot_tables(b.model, (uint32_t*)&host[o_tab], b.k <= 5);
     half_scales(b, (float*)&host[o_hr]);
+    // (the escape-free narrow kernel reconstructs fma(u + 128, h, -128 h), which needs
+    // -128 h finite; rows beyond that take the plain product h u)
+    const float* hr = (const float*)&host[o_hr];
+    for (int64_t r = 0; r < b.R; ++r)
+      if (!(std::fabs(hr[r]) < 3.4028234663852886e38f / 128.f)) b.d_big_h = true;
   }
   std::memcpy(&host[o_boff], &b.bytes[b.off_boff], 4 * (size_t)b.n_blocks);
   std::memcpy(&host[o_full], &b.bytes[b.off_full], fw * (size_t)b.n_chains);
@@ -1899,6 +2111,13 @@ int64_t ep_blob_device_errors(const ep_blob* blob) {
 size_t ep_linear_workspace_bytes(const ep_blob* blob) {
   if (!blob) return 0;
   return (size_t)blob->b.R * (size_t)blob->b.C * 2 + 256;
+}
+
+int ep_compressed_linear_prefill(const ep_blob* w, const void* x, int64_t T, const void* bias, void* y,
+                                 ep_stream stream) {
+  set_error("");
+  if (!w) return fail(EP_E_ARG, "null blob");
+  return prefill_launch(w->b, x, T, bias, y, stream);
 }
 
 // The fused product with its partial sums in the library's scratch array (no allocation,

@@ -133,6 +133,7 @@ struct Blob {
   const uint16_t* d_stream = nullptr;
   size_t d_bytes = 0;                  // size of the device allocation
   uint32_t d_tab_words = 0;            // u32 words of its decode tables
+  bool d_big_h = false;                // some row half-scale h_r has |128 h_r| beyond float range
   const uint32_t* d_boff = nullptr;    // the stored chain area: block offsets (u32),
   const void* d_full = nullptr;        //   full chunks per chain (u8 at S >= 8, else u16),
   const uint8_t* d_nib = nullptr;      //   tail nibbles,
@@ -185,6 +186,10 @@ int matvec_forward(const Blob& b, const void* x, int64_t T, const void* bias, vo
 int decompress_beside(const Blob& b, void* dst, ep_stream st, int64_t max_wg);
 // the whole blob for a GEMM that reads the weights next (stores kept in the caches)
 int decompress_for_gemm(const Blob& b, void* dst, ep_stream st);
+// Fused prefill product (decode.hip): Y = X W^T (+ bias) for 1..256 activation rows with
+// W decoded into LDS operand tiles of an MFMA product (4096 columns, S = 8); no workspace.
+bool prefill_supported(const Blob& b, int64_t T);
+int prefill_launch(const Blob& b, const void* x, int64_t T, const void* bias, void* y, ep_stream st);
 
 }  // namespace ep
 

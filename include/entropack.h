@@ -174,7 +174,9 @@ int64_t ep_blob_device_errors(const ep_blob* blob);
  * (>= ep_linear_workspace_bytes bytes), then an MFMA BF16 GEMM with fp32
  * accumulation runs on the same stream.  With T <= 8, when ep_compressed_matvec takes
  * the blob and its partial sums fit ep_linear_workspace_bytes, that fused product runs
- * instead (same result up to fp32 summation order).  x, y, bias and dev_ws must be
+ * instead; otherwise, when ep_compressed_linear_prefill takes the blob and T (4096 cols,
+ * S = 8, T <= 256), that one (same result up to fp32 summation order; dev_ws unused).
+ * x, y, bias and dev_ws must be
  * device, managed or pinned memory (EP_E_ARG otherwise, for every T, before any
  * launch).  Asynchronous. */
 size_t ep_linear_workspace_bytes(const ep_blob* blob);
@@ -185,7 +187,8 @@ int ep_compressed_linear_forward(const ep_blob* w, const void* dev_x, int64_t T,
 /* A sequence of compressed linear layers, y_i = x_i W_i^T (+ bias_i), i = 0..n-1
  * ([README] 快速开始 layer(x), applied layer after layer as a model runs them; [ABS]:
  * decoding cost grows with the weight count, so it should hide behind the GEMMs).
- * Each layer is decoded, then multiplied.  The decode of layer i+1 runs on `side`, beside
+ * Each layer is decoded, then multiplied (layers that ep_compressed_linear_forward
+ * sends to a fused product run that product on `main` instead).  The decode of layer i+1 runs on `side`, beside
  * the GEMM of layer i on `main`, when that GEMM has fewer output tiles than the GPU has
  * CUs (its workgroups leave CUs idle), on at most as many workgroups as there are idle
  * CUs; otherwise it runs on `main` before its GEMM (a decode workgroup cannot share a CU with a GEMM workgroup: their LDS needs add
@@ -215,6 +218,20 @@ int ep_compressed_linear_seq_forward(const ep_blob* const* w, int n, const void*
 size_t ep_matvec_workspace_bytes(const ep_blob* w, int64_t T);
 int ep_compressed_matvec(const ep_blob* w, const void* dev_x, int64_t T, const void* dev_bias,
                          void* dev_y, void* dev_ws, size_t ws_bytes, ep_stream stream);
+
+/* Fused decode and product for prefill-sized activations ([SUM]: symbol decode,
+ * inverse lattice and row rescale fused on the GPU with no intermediate tensor; [ABS]:
+ * the method targets prefill, where a GEMM follows the decode): y = x W^T (+ bias) with
+ * every K slab of W's BF16 weights decoded into an LDS operand tile that MFMAs multiply
+ * by the activations, so the weights are decoded once and never written to memory.
+ * Takes lossy BF16 blobs of exactly 4096 cols at S = 8 (one tile per row) and
+ * 1 <= T <= 256; EP_E_ARG otherwise (ep_compressed_linear_forward covers the rest).
+ * x is T x 4096 BF16 (16-byte aligned), y is T x rows BF16 (8-byte aligned), bias rows
+ * BF16 or NULL; all device, managed or pinned memory (EP_E_ARG otherwise, before any
+ * launch).  No workspace.  fp32 accumulation (its order differs from the GEMM's), bias
+ * added, rounded to BF16 (nearest even).  Asynchronous. */
+int ep_compressed_linear_prefill(const ep_blob* w, const void* dev_x, int64_t T, const void* dev_bias,
+                                 void* dev_y, ep_stream stream);
 
 /* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): ep_compressed_matvec with its partial sums in the

@@ -183,6 +183,18 @@ def test_saturating_bf16():
     blob, _, _ = _check("bf16 near max", src, nx.DT_BF16, 2.0)
 
 
+@pytest.mark.parametrize("dt", [nx.DT_BF16, nx.DT_FP32])
+def test_huge_row_scales_narrow(dt):
+    # escape-free narrow tables (1 bpp, k = 3) with row half-scales h_r near 1e38: the
+    # kernel's fma(u + 128, h, -128 h) would overflow in -128 h, so these blobs take the
+    # plain product (BF16: the container also saturates)
+    w = np.clip(synth.rowscaled_f32(48, 512, 94) * np.float32(1e38 / 0.02), -3.3e38, 3.3e38).astype(np.float32)
+    src = synth.f32_to_bf16_bits(w) if dt == nx.DT_BF16 else w
+    b = oracle.parse_blob(oracle.compress(src, dt, 1.0))
+    assert b.k <= 5 and not (b.flags & 1)
+    _check(f"huge row scales {dt}", src, dt, 1.0)
+
+
 def test_tile_independence():
     src = synth.rowscaled(512, 1032, 12)
     blob = oracle.compress(src, nx.DT_BF16, 4.0, chains_per_tile=8)

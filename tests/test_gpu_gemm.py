@@ -205,22 +205,25 @@ def test_python_api_module_and_state_dict():
 # (T, [(rows = out, cols = in), ...]): at 200 tokens every GEMM leaves CUs idle, so every
 # decode after the first runs on the side stream; at 4096 tokens the 4096-row layers'
 # GEMMs take 256 tiles (one per CU) and the next decode runs in order on the main stream,
-# while the 512-row layer's 32-tile GEMM lets the decode after it go to the side stream
+# while the 512-row layer's 32-tile GEMM lets the decode after it go to the side stream;
+# at 200 tokens with S = 8 the 4096-column layers take the fused prefill product between
+# decoded ones (chains per tile: None = the encoder's default)
 SEQ_CASES = [
-    (200, [(512, 768), (768, 512), (1024, 768), (768, 1024), (512, 768)]),
-    (4096, [(4096, 256), (512, 256), (4096, 256), (4096, 256)]),
+    (200, [(512, 768), (768, 512), (1024, 768), (768, 1024), (512, 768)], None),
+    (4096, [(4096, 256), (512, 256), (4096, 256), (4096, 256)], None),
+    (200, [(512, 4096), (4096, 512), (768, 512), (264, 4096), (512, 768)], 8),
 ]
 
 
-@pytest.mark.parametrize("T,shapes", SEQ_CASES, ids=["side", "mixed"])
-def test_compressed_linear_sequence(T, shapes):
+@pytest.mark.parametrize("T,shapes,S", SEQ_CASES, ids=["side", "mixed", "prefill"])
+def test_compressed_linear_sequence(T, shapes, S):
     """A sequence of layers: every output is bit-identical to the one-layer path and
     every element within the per-element bound of the oracle GEMM."""
     import torch
     from decode_tile_rans_amd import _lib as L
     dbs, xs, ys, refs, mags, bs = [], [], [], [], [], []
     for i, (R, C) in enumerate(shapes):
-        blob = oracle.compress(synth.rowscaled(R, C, 40 + i), nx.DT_BF16, 3.0 + 0.5 * i)
+        blob = oracle.compress(synth.rowscaled(R, C, 40 + i), nx.DT_BF16, 3.0 + 0.5 * i, chains_per_tile=S)
         _, w_hat, _ = oracle.decode(blob)
         x = synth.activations(T, C, 60 + i)
         b = synth.f32_to_bf16_bits(np.linspace(-0.25, 0.25, R).astype(np.float32)) if i % 2 == 0 else None
