@@ -298,14 +298,15 @@ def traffic_per_launch(coords_per_launch):
     return (info["fetch_bytes_per_param"] + info["write_bytes_per_param"]) * coords_per_launch
 
 
-def valu_issue(params_per_s):
+def valu_issue(params_per_s, key="valu_lane_ops_per_param"):
     """The decode against the chip's VALU issue rate (256 CUs x 64 lanes x 2.4 GHz lane
     operations per second) at the measured SQ_INSTS_VALU x 64 lane operations per
-    parameter; None without a current counter summary."""
+    parameter of the kernel variant `key` names (the roofline launch's two chains per
+    lane, or the timed step's one); None without a current counter summary."""
     info = decode_counters()
-    if info is None or "valu_lane_ops_per_param" not in info:
+    if info is None or key not in info:
         return None
-    ops = info["valu_lane_ops_per_param"]
+    ops = info[key]
     ceiling = VALU_LANE_OPS_PER_S / ops
     return {"lane_ops_per_param": ops, "peak_lane_ops_per_s": VALU_LANE_OPS_PER_S,
             "ceiling_params_per_s": round(ceiling), "achieved_params_per_s": round(params_per_s),
@@ -420,7 +421,7 @@ def fused_linear(target_bpp, reps=10):
     # second stream while this layer's GEMM runs, against the same GEMMs on plain weights
     seq = linear_sequence(c, wbits, target_bpp, timeit)
     small = small_batch(c, w, x, ws, need, wd, sp, timeit)
-    prefill = prefill_fused(c, w, x, ws, need, sp, timeit)
+    prefill = prefill_fused(c, w, x, wd, sp, timeit)
     sweep = token_sweep(c, w, ws, need, sp, timeit)
     return {
         "workload": "CompressedLinear prefill 14336x4096 weight @%.1f bpp, 4096 tokens" % target_bpp,
@@ -462,11 +463,11 @@ def token_sweep(c, w, ws, need, sp, timeit):
     return out
 
 
-def prefill_fused(c, w, x, ws, need, sp, timeit):
+def prefill_fused(c, w, x, wd, sp, timeit):
     """The same layer on 16..256 tokens: the fused prefill product (each K slab of W decoded
-    into an LDS operand tile of the MFMA product; weights never written) against decode
-    then our GEMM (ep_compressed_linear_forward), our GEMM and hipBLASLt on the plain
-    BF16 weight."""
+    into an LDS operand tile of the MFMA product; weights never written; what
+    ep_compressed_linear_forward takes at these sizes) against decode to memory then our
+    GEMM, our GEMM alone and hipBLASLt on the plain BF16 weight."""
     import torch
     from decode_tile_rans_amd import _lib as L
     R, C = c.shape
@@ -479,8 +480,8 @@ def prefill_fused(c, w, x, ws, need, sp, timeit):
         xs = x[:T].contiguous()
         y = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
         t_mma = best(lambda: L.ep_compressed_linear_prefill(c.handle, xs.data_ptr(), T, None, y.data_ptr(), sp))
-        t_two = best(lambda: L.ep_compressed_linear_forward(c.handle, xs.data_ptr(), T, None, y.data_ptr(),
-                                                             ws.data_ptr(), need, sp))
+        t_two = best(lambda: (L.ep_decompress(c.handle, wd, sp),
+                                L.ep_gemm_bf16_nt(xs.data_ptr(), wd, None, y.data_ptr(), T, R, C, sp)))
         t_gemm = best(lambda: L.ep_gemm_bf16_nt(xs.data_ptr(), w.data_ptr(), None, y.data_ptr(), T, R, C, sp))
         t_plain = best(lambda: torch.matmul(xs, w.t()))
         out.append({"tokens": T, "ms_fused_prefill": round(t_mma, 4), "ms_decode_then_gemm": round(t_two, 4),
@@ -808,14 +809,15 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (lambda t: round(t) if t else None)(traffic_per_launch(n_params / len(units))),
                      "kernel": "decode_kernel (BF16 out)", "avg_launch_ms": round(kern_ms / len(units), 5),
-                     "launch_shape": "one stream, blocks spread evenly over the CUs (EP_DECODE_SPREAD=1)",
+                     "launch_shape": "one stream, blocks spread evenly over the CUs (EP_DECODE_SPREAD=1): the "
+                                     "9-matrix launches at two chains per lane, every block resident at once",
                      "frac_one_block_per_wave": round(alg_bytes / (sum(launch_ms_std) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "avg_launch_ms_one_block_per_wave": round(sum(launch_ms_std) / len(units), 5),
                      "algorithmic_bytes_per_launch": round(alg_bytes / len(units)),
                      "step_effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
                      "step_effective_frac": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "valu_issue_per_launch": valu_issue(n_params / (kern_ms * 1e-3)),
-                     "valu_issue_step": valu_issue(n_params / (ms * 1e-3)),
+                     "valu_issue_step": valu_issue(n_params / (ms * 1e-3), "valu_lane_ops_per_param_step"),
                      "practical_ceilings": practical_ceilings()},
     }
     if not a.no_layer_mode:
