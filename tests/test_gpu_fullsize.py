@@ -209,6 +209,38 @@ def test_fused_linear_full_size():
         L.ep_blob_free(h)
 
 
+@pytest.mark.timeout(600)
+def test_fused_prefill_full_size():
+    # the 14336 x 4096 layer at 256 tokens through the fused prefill product (what the
+    # linear entry takes at this size): every output element within the bound of the
+    # float64 product with the oracle's decoded weights
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    R, C, T = 14336, 4096, 256
+    say("fused prefill full size: encode", R, C, T)
+    wbits = synth.rowscaled(R, C, 5)
+    h = _product_blob(wbits, nx.DT_BF16, 4.0)
+    try:
+        blob = L.ep_serialize(h)
+        L.ep_blob_upload(h, stream_ptr())
+        xb = synth.activations(T, C, 52)
+        x = torch.from_numpy(xb).view(torch.bfloat16).cuda()
+        bias = synth.f32_to_bf16_bits(np.linspace(-1.0, 1.0, R).astype(np.float32))
+        bt = torch.from_numpy(bias).view(torch.bfloat16).cuda()
+        y = torch.full((T, R), 7.0, dtype=torch.bfloat16, device="cuda")
+        L.ep_compressed_linear_prefill(h, x.data_ptr(), T, bt.data_ptr(), y.data_ptr(), stream_ptr())
+        torch.cuda.synchronize()
+        say("fused prefill full size: oracle")
+        _, w_hat, _ = oracle.decode(blob)
+        xf, wf = nx.bf16_to_f64(xb), nx.bf16_to_f64(w_hat)
+        ref = linear_ref(xf, wf, nx.bf16_to_f64(bias))
+        mag = np.abs(xf) @ np.abs(wf).T
+        check_linear(nx.bf16_to_f64(to_np(y, nx.DT_BF16)), ref, mag, C)
+        assert L.ep_blob_device_errors(h) == 0
+    finally:
+        L.ep_blob_free(h)
+
+
 SWEEP = [("bf16@2.3", nx.DT_BF16, 2.3), ("bf16@3.0", nx.DT_BF16, 3.0), ("bf16@5.0", nx.DT_BF16, 5.0),
          ("bf16@8.0", nx.DT_BF16, 8.0), ("fp8@5.0", nx.DT_FP8, 5.0), ("int8@4.0", nx.DT_INT8, 4.0)]
 
