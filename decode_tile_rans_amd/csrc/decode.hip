@@ -774,9 +774,14 @@ __device__ __forceinline__ void mma_xload(const DecJob& J, int it, int wave, int
   }
 }
 // the slab in operand tile `buf` times this wave's activation blocks
+// (a wave whose activation blocks all lie past the T rows skips the slab: no LDS reads,
+// no MFMAs; a branch uniform per wave.  Its activation loads stay unconditional, so the
+// memory counters the decode's waits rely on do not depend on T: with those loads
+// conditional too, the kernel was slower, not faster)
 template <int MB>
-__device__ __forceinline__ void mma_slab(const GroupCtx& X, uint32_t buf, int lane, const u32x4 (&xf)[MB][4],
+__device__ __forceinline__ void mma_slab(const GroupCtx& X, uint32_t buf, int wave, int lane, const u32x4 (&xf)[MB][4],
                                          f32x4 (&acc)[MB][4]) {
+  if ((uint32_t)(wave * 16) >= X.J->mv_T) return;
   const uint32_t lr = (uint32_t)lane & 15u, lq = (uint32_t)lane >> 4;
   const uint32_t base = X.bt_base + buf * kBTileBytes;
 #pragma unroll
@@ -1305,7 +1310,7 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
     for (int c = 0; c < ILP; ++c) ch_settle<MIR>(rd[c]);
     if constexpr (MB > 0) {
       __syncthreads();   // the pair's slab is in LDS (and the tile written next is free)
-      mma_slab<MB>(X, ((uint32_t)kk >> 1) & 1u, lane, xf, macc);
+      mma_slab<MB>(X, ((uint32_t)kk >> 1) & 1u, wave, lane, xf, macc);
     }
   }
   if constexpr (NT > 0) {
