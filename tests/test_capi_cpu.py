@@ -340,3 +340,21 @@ def test_tileans_validation():
             L.ep_blob_distortion(h)
     finally:
         L.ep_blob_free(h)
+
+
+def test_device_entries_refuse_blobs_not_uploaded():
+    """The decode and fused-product entries check the blob's device copy first, so a blob
+    never uploaded is refused (EP_E_STATE) before any device call."""
+    if not hasattr(L.lib(), "ep_compressed_linear_prefill"):
+        pytest.skip("host-only build: no device entry points")
+    src = np.ascontiguousarray(synth.rowscaled(64, 4096, 31))
+    h = L.ep_compress(src.ctypes.data, nx.DT_BF16, 64, 4096, 4.0, 8)
+    try:
+        for call in (lambda: L.ep_compressed_linear_prefill(h, 16, 16, 0, 16),
+                     lambda: L.ep_decompress(h, 16),
+                     lambda: L.ep_test_decode_coords(h, 16)):
+            with pytest.raises(L.EPError) as e:
+                call()
+            assert e.value.name == "EP_E_STATE"
+    finally:
+        L.ep_blob_free(h)
