@@ -489,7 +489,30 @@ def prefill_fused(c, w, x, wd, sp, timeit):
                     "fused_speedup_vs_decode_then_gemm": round(t_two / t_mma, 3),
                     "fused_tflops": round(2.0 * T * R * C / (t_mma * 1e-3) / 1e12, 1),
                     "fused_blob_gbs": round(c.nbytes / (t_mma * 1e-3) / 1e9, 1)})
-    return out
+    # a weight of 8192 columns (two tiles a row): 8192 x 8192 @4.0 (seed 6)
+    import synth
+    import decode_tile_rans_amd as ep
+    os.environ["EP_NUM_THREADS"] = str(min(16, os.cpu_count() or 1))
+    c2 = ep.compress(synth.rowscaled(8192, 8192, 6), 4.0, dtype=torch.bfloat16)
+    os.environ.pop("EP_NUM_THREADS", None)
+    c2.upload()
+    R2, C2 = c2.shape
+    x2 = torch.from_numpy(synth.activations(256, C2, 53)).view(torch.bfloat16).cuda()
+    w2 = torch.empty((R2, C2), dtype=torch.bfloat16, device="cuda")
+    L.ep_decompress(c2.handle, w2.data_ptr(), sp)
+    wd2 = torch.empty((R2, C2), dtype=torch.bfloat16, device="cuda")
+    out2 = []
+    for T in (16, 64, 128, 256):
+        xs = x2[:T].contiguous()
+        y = torch.empty((T, R2), dtype=torch.bfloat16, device="cuda")
+        t_mma = best(lambda: L.ep_compressed_linear_prefill(c2.handle, xs.data_ptr(), T, None, y.data_ptr(), sp))
+        t_two = best(lambda: (L.ep_decompress(c2.handle, wd2.data_ptr(), sp),
+                                L.ep_gemm_bf16_nt(xs.data_ptr(), wd2.data_ptr(), None, y.data_ptr(), T, R2, C2, sp)))
+        t_gemm = best(lambda: L.ep_gemm_bf16_nt(xs.data_ptr(), w2.data_ptr(), None, y.data_ptr(), T, R2, C2, sp))
+        out2.append({"tokens": T, "ms_fused_prefill": round(t_mma, 4), "ms_decode_then_gemm": round(t_two, 4),
+                     "ms_our_gemm_plain_bf16": round(t_gemm, 4),
+                     "fused_speedup_vs_decode_then_gemm": round(t_two / t_mma, 3)})
+    return {"layer_14336x4096": out, "layer_8192x8192": out2}
 
 
 def small_batch(c, w, x, ws, need, wd, sp, timeit):

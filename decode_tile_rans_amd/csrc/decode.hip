@@ -48,8 +48,9 @@ enum OutKind { OUT_BF16 = 0, OUT_BF16_SAT = 1, OUT_FP16 = 2, OUT_FP32 = 3, OUT_F
                // BF16 stored through the caches (a GEMM reads the weights right after)
                OUT_BF16_L2 = 12,
                // fused prefill product: each K slab of BF16 weights goes to an LDS operand
-               // tile that MFMAs multiply by up to 128 (MMA1) or 256 (MMA2) activation rows
-               OUT_MMA1 = 13, OUT_MMA2 = 14 };
+               // tile that MFMAs multiply by up to 128 (MMA1) or 256 (MMA2) activation rows;
+               // 4096 columns (one tile a row), or 8192 (two tiles a row: MMA1X2, MMA2X2)
+               OUT_MMA1 = 13, OUT_MMA2 = 14, OUT_MMA1X2 = 15, OUT_MMA2X2 = 16 };
 template <int OUT>
 constexpr int mv_tokens() {
   return (OUT >= OUT_MV1 && OUT <= OUT_MV8) ? 1 << (OUT - OUT_MV1) : 0;
@@ -57,7 +58,12 @@ constexpr int mv_tokens() {
 // 16-row activation blocks per wave of the fused prefill product (0: another output)
 template <int OUT>
 constexpr int mma_blocks() {
-  return OUT == OUT_MMA1 ? 1 : OUT == OUT_MMA2 ? 2 : 0;
+  return (OUT == OUT_MMA1 || OUT == OUT_MMA1X2) ? 1 : (OUT == OUT_MMA2 || OUT == OUT_MMA2X2) ? 2 : 0;
+}
+// tiles per row of W in the fused prefill product (4096 columns a tile)
+template <int OUT>
+constexpr int mma_tiles_per_row() {
+  return (OUT == OUT_MMA1X2 || OUT == OUT_MMA2X2) ? 2 : 1;
 }
 template <int OUT>
 constexpr int out_elem_bytes() {
@@ -743,12 +749,14 @@ __device__ __forceinline__ void mv_flush(const DecJob& J, MvAcc& m) {
   for (int t = 0; t < NT; ++t) m.a[t] = 0.f;
 }
 
-// ---- fused prefill product (OUT_MMA*): Y[T x R] = X[T x 4096] W^T (+ bias) with W decoded
-// into LDS.  A blob of 4096 columns at S = 8 has one tile per row, so a wave's block of
-// 64 chains is 8 rows of W and, at a chain's group pair kk, kk + 1, the 8 chains of a row
-// yield its columns 64 kk .. 64 kk + 127 in chunks of 8.  A workgroup of 8 waves (64 rows
-// of W, 64 output columns) writes each pair's 64 x 128 BF16 slab to one of two LDS
-// operand tiles (rows of 256 bytes, 16-byte chunks XOR-swizzled by the row), meets at a
+// ---- fused prefill product (OUT_MMA*): Y[T x R] = X[T x C] W^T (+ bias) with W decoded
+// into LDS, C = 4096 TP (TP = 1 or 2 tiles a row).  At S = 8 a tile is 4096 consecutive
+// columns of one row, so a wave's block of 64 chains is 8 tiles (8 / TP rows of W) and,
+// at a chain's group pair kk, kk + 1, the 8 chains of a tile yield the tile's columns
+// 64 kk .. 64 kk + 127 in chunks of 8.  A workgroup of 8 waves (64 tiles: 64 / TP rows of
+// W and as many output columns) writes each pair's slab (per row, TP segments of 128
+// columns: one at 128 i of each tile) to one of two LDS operand tiles (rows of 256 TP
+// bytes, the 16-byte chunks of each segment XOR-swizzled by the row), meets at a
 // barrier, and every wave multiplies the slab by its own 16-row blocks of X (wave w: rows
 // 16 (w + 8 b) .. + 15, b < MB), read straight from memory into registers at the start
 // of the pair: v_mfma_f32_16x16x32_bf16 with the W fragment first, so a lane ends with
@@ -760,9 +768,10 @@ constexpr int kPrefillMaxT = 16 * kMmaWaves * 2;   // 256 activation rows
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-// activation fragments of slab `it` (columns 128 it .. + 127): block b, K step ks
-template <int MB>
-__device__ __forceinline__ void mma_xload(const DecJob& J, int it, int wave, int lane, u32x4 (&xf)[MB][4]) {
+// activation fragments of slab `it` (columns 4096 sg + 128 it .. + 127 of segment sg):
+// block b, segment sg, K step ks
+template <int MB, int TP>
+__device__ __forceinline__ void mma_xload(const DecJob& J, int it, int wave, int lane, u32x4 (&xf)[MB][TP][4]) {
   const int lr = lane & 15, lq = lane >> 4;
 #pragma unroll
   for (int b = 0; b < MB; ++b) {
@@ -770,7 +779,9 @@ __device__ __forceinline__ void mma_xload(const DecJob& J, int it, int wave, int
     const uint32_t tt = t < J.mv_T ? t : J.mv_T - 1u;
     const uint16_t* xp = J.mv_x + (int64_t)tt * J.C + it * 128 + 8 * lq;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) xf[b][ks] = *(const u32x4*)(xp + 32 * ks);
+    for (int sg = 0; sg < TP; ++sg)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) xf[b][sg][ks] = *(const u32x4*)(xp + 8 * kTileGroups * sg + 32 * ks);
   }
 }
 // the slab in operand tile `buf` times this wave's activation blocks
@@ -778,29 +789,34 @@ __device__ __forceinline__ void mma_xload(const DecJob& J, int it, int wave, int
 // no MFMAs; a branch uniform per wave.  Its activation loads stay unconditional, so the
 // memory counters the decode's waits rely on do not depend on T: with those loads
 // conditional too, the kernel was slower, not faster)
-template <int MB>
-__device__ __forceinline__ void mma_slab(const GroupCtx& X, uint32_t buf, int wave, int lane, const u32x4 (&xf)[MB][4],
-                                         f32x4 (&acc)[MB][4]) {
+template <int MB, int TP>
+__device__ __forceinline__ void mma_slab(const GroupCtx& X, uint32_t buf, int wave, int lane,
+                                         const u32x4 (&xf)[MB][TP][4], f32x4 (&acc)[MB][4 / TP]) {
   if ((uint32_t)(wave * 16) >= X.J->mv_T) return;
   const uint32_t lr = (uint32_t)lane & 15u, lq = (uint32_t)lane >> 4;
   const uint32_t base = X.bt_base + buf * kBTileBytes;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int sg = 0; sg < TP; ++sg) {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const uint32_t row = 16u * (uint32_t)cb + lr;   // (row & 15 == lr)
-      const uint32_t a = base + row * kBRowBytes + ((((uint32_t)ks * 4u + lq) ^ lr) << 4);
-      const bf16x8 wf = *(const EP_LDS bf16x8*)(uintptr_t)a;
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int b = 0; b < MB; ++b)
-        acc[b][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, __builtin_bit_cast(bf16x8, xf[b][ks]), acc[b][cb], 0, 0, 0);
+      for (int cb = 0; cb < 4 / TP; ++cb) {
+        const uint32_t row = 16u * (uint32_t)cb + lr;   // (row & 15 == lr)
+        const uint32_t a = base + row * (kBRowBytes * TP) + (uint32_t)sg * kBRowBytes +
+                           ((((uint32_t)ks * 4u + lq) ^ lr) << 4);
+        const bf16x8 wf = *(const EP_LDS bf16x8*)(uintptr_t)a;
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+          acc[b][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, __builtin_bit_cast(bf16x8, xf[b][sg][ks]), acc[b][cb],
+                                                               0, 0, 0);
+      }
     }
   }
 }
 // outputs: lane l holds activation row 16 (w + 8 b) + l % 16, output columns
 // mma_n0 + 16 cb + 4 (l / 16) .. + 3; bias added, rounded to BF16 (nearest even)
-template <int MB>
-__device__ __forceinline__ void mma_store(const GroupCtx& X, int wave, int lane, const f32x4 (&acc)[MB][4]) {
+template <int MB, int TP>
+__device__ __forceinline__ void mma_store(const GroupCtx& X, int wave, int lane, const f32x4 (&acc)[MB][4 / TP]) {
   const DecJob& J = *X.J;
   const int lr = lane & 15, lq = lane >> 4;
   const int64_t N = J.R;
@@ -810,7 +826,7 @@ __device__ __forceinline__ void mma_store(const GroupCtx& X, int wave, int lane,
     const int64_t t = (int64_t)(wave + kMmaWaves * b) * 16 + lr;
     if (t >= (int64_t)J.mv_T) continue;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < 4 / TP; ++cb) {
       const int64_t n = X.mma_n0 + 16 * cb + 4 * lq;
       float v[4];
 #pragma unroll
@@ -1270,15 +1286,15 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
   for (int c = 1; c < ILP; ++c) nmax = ngr[c] > nmax ? ngr[c] : nmax;
   // fused prefill product: every lane of the workgroup runs all 64 groups (the slab
   // barriers are workgroup-wide); chains past the matrix decode rows no output reads
-  constexpr int MB = mma_blocks<OUT>();
-  f32x4 macc[MB > 0 ? MB : 1][4];
-  u32x4 xf[MB > 0 ? MB : 1][4];
+  constexpr int MB = mma_blocks<OUT>(), TP = mma_tiles_per_row<OUT>();
+  f32x4 macc[MB > 0 ? MB : 1][4 / TP];
+  u32x4 xf[MB > 0 ? MB : 1][TP][4];
   if constexpr (MB > 0) {
     nmax = kTileGroups / 8;   // (S = 8)
 #pragma unroll
     for (int b = 0; b < MB; ++b)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) macc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < 4 / TP; ++cb) macc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // two groups per iteration: the stream service runs before every even group, and
@@ -1286,7 +1302,7 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
   // (the row scale of a group is settled before its service, so that its load is
   // followed by a fixed sequence of memory operations)
   for (int kk = 0; kk < nmax; kk += 2) {
-    if constexpr (MB > 0) mma_xload<MB>(J, kk >> 1, wave, lane, xf);
+    if constexpr (MB > 0) mma_xload<MB, TP>(J, kk >> 1, wave, lane, xf);
     if constexpr (OUT != OUT_BYTES) row_scale<ILP>(X, kk, rs, ngr);
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
@@ -1310,7 +1326,7 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
     for (int c = 0; c < ILP; ++c) ch_settle<MIR>(rd[c]);
     if constexpr (MB > 0) {
       __syncthreads();   // the pair's slab is in LDS (and the tile written next is free)
-      mma_slab<MB>(X, ((uint32_t)kk >> 1) & 1u, wave, lane, xf, macc);
+      mma_slab<MB, TP>(X, ((uint32_t)kk >> 1) & 1u, wave, lane, xf, macc);
     }
   }
   if constexpr (NT > 0) {
@@ -1321,7 +1337,7 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
 #pragma unroll
   for (int c = 0; c < ILP; ++c)
     if (live[c] && ngr[c] > 0 && rd[c].x != kL) atomicAdd(J.err, 1u);
-  if constexpr (MB > 0) mma_store<MB>(X, wave, lane, macc);
+  if constexpr (MB > 0) mma_store<MB, TP>(X, wave, lane, macc);
 }
 
 // A workgroup stages the decode tables of its job into LDS once, then its waves take
@@ -1367,11 +1383,12 @@ __device__ __forceinline__ void decode_kernel_body(const DecBatch& B) {
   if constexpr (mma_blocks<OUT>() > 0) {
     // fused prefill product: 8 waves of one block each (8 rows of W: S = 8, one tile a
     // row), the operand tiles after the rings; waves past the matrix run too (barriers)
+    constexpr uint32_t TP = (uint32_t)mma_tiles_per_row<OUT>();
     X.bt_base = X.lds0 + (uint32_t)kTabBytes + (uint32_t)(nwaves * 64 * ring_bytes<1>());
-    const uint32_t rho = (uint32_t)(wave * 8 + (lane >> 3));
-    X.bt_row = X.bt_base + rho * kBRowBytes;
+    const uint32_t tile = (uint32_t)(wave * 8 + (lane >> 3)), rho = tile / TP;   // (tile, row) in the workgroup
+    X.bt_row = X.bt_base + rho * kBRowBytes * TP + (tile % TP) * kBRowBytes;
     X.bt_swz = rho & 15u;
-    X.mma_n0 = wg_blk0 * 8;
+    X.mma_n0 = wg_blk0 * 8 / (int64_t)TP;
     decode_blocks<OUT, ESC, C8, NARROW, ILP, SEL>(X, b, wg_blk1, lane, wave, st, true);
     return;
   }
@@ -1844,8 +1861,8 @@ int decompress_beside(const Blob& b, void* dst, ep_stream st, int64_t max_wg) {
 
 // ---------------------------------------------------------------- fused prefill product
 bool prefill_supported(const Blob& b, int64_t T) {
-  return b.kind == kKindLossy && b.dtype == EP_BF16 && b.S == 8 && b.C == 8 * kTileGroups && T >= 1 &&
-         T <= kPrefillMaxT;
+  return b.kind == kKindLossy && b.dtype == EP_BF16 && b.S == 8 && (b.C == 8 * kTileGroups || b.C == 16 * kTileGroups) &&
+         T >= 1 && T <= kPrefillMaxT;
 }
 
 template <int OUT>
@@ -1861,8 +1878,8 @@ int prefill_launch(const Blob& b, const void* x, int64_t T, const void* bias, vo
   int rc = check_uploaded(b);
   if (rc) return rc;
   if (!prefill_supported(b, T))
-    return fail(EP_E_ARG, "the fused prefill product takes lossy BF16 blobs of 4096 columns at 8 chains per tile "
-                "and 1.." + std::to_string(kPrefillMaxT) + " activation rows");
+    return fail(EP_E_ARG, "the fused prefill product takes lossy BF16 blobs of 4096 or 8192 columns at 8 chains "
+                "per tile and 1.." + std::to_string(kPrefillMaxT) + " activation rows");
   if (!x || !y) return fail(EP_E_ARG, "null activations or output");
   if (reinterpret_cast<uintptr_t>(x) & 15) return fail(EP_E_ARG, "activations must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(y) & 7) || (reinterpret_cast<uintptr_t>(bias) & 1))
@@ -1882,8 +1899,11 @@ int prefill_launch(const Blob& b, const void* x, int64_t T, const void* bias, vo
   const int64_t n_wg = (b.n_blocks + kMmaWaves - 1) / kMmaWaves;
   const bool esc = (b.flags & kFlagEsc) != 0, narrow = b.k <= 5;
   const hipStream_t st = (hipStream_t)stream;
-  return T <= kPrefillMaxT / 2 ? launch_mma<OUT_MMA1>(esc, narrow, B, n_wg, st)
-                               : launch_mma<OUT_MMA2>(esc, narrow, B, n_wg, st);
+  if (b.C == 8 * kTileGroups)
+    return T <= kPrefillMaxT / 2 ? launch_mma<OUT_MMA1>(esc, narrow, B, n_wg, st)
+                                 : launch_mma<OUT_MMA2>(esc, narrow, B, n_wg, st);
+  return T <= kPrefillMaxT / 2 ? launch_mma<OUT_MMA1X2>(esc, narrow, B, n_wg, st)
+                               : launch_mma<OUT_MMA2X2>(esc, narrow, B, n_wg, st);
 }
 
 // ---------------------------------------------------------------- the fused product without a workspace

@@ -187,7 +187,7 @@ int decompress_beside(const Blob& b, void* dst, ep_stream st, int64_t max_wg);
 // the whole blob for a GEMM that reads the weights next (stores kept in the caches)
 int decompress_for_gemm(const Blob& b, void* dst, ep_stream st);
 // Fused prefill product (decode.hip): Y = X W^T (+ bias) for 1..256 activation rows with
-// W decoded into LDS operand tiles of an MFMA product (4096 columns, S = 8); no workspace.
+// W decoded into LDS operand tiles of an MFMA product (4096 or 8192 columns, S = 8); no workspace.
 bool prefill_supported(const Blob& b, int64_t T);
 int prefill_launch(const Blob& b, const void* x, int64_t T, const void* bias, void* y, ep_stream st);
 

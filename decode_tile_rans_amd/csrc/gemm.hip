@@ -658,7 +658,7 @@ int ep_gemm_fp8_nt(const void* xq, const void* wq, float a_x, const float* aw, v
 static bool use_matvec(const ep_blob* w, int64_t T) {
   return matvec_supported(w->b, T) && matvec_workspace_bytes(w->b, T) <= ep_linear_workspace_bytes(w);
 }
-// up to 256 activation rows (4096 columns, S = 8): the fused prefill product, which
+// up to 256 activation rows (4096 or 8192 columns, S = 8): the fused prefill product, which
 // decodes every K slab of W into the MFMA product's LDS operand (1.1-1.6x faster than
 // decode then GEMM on a 14336 x 4096 layer)
 static bool use_prefill(const ep_blob* w, int64_t T) { return !use_matvec(w, T) && prefill_supported(w->b, T); }

@@ -174,7 +174,7 @@ int64_t ep_blob_device_errors(const ep_blob* blob);
  * (>= ep_linear_workspace_bytes bytes), then an MFMA BF16 GEMM with fp32
  * accumulation runs on the same stream.  With T <= 8, when ep_compressed_matvec takes
  * the blob and its partial sums fit ep_linear_workspace_bytes, that fused product runs
- * instead; otherwise, when ep_compressed_linear_prefill takes the blob and T (4096 cols,
+ * instead; otherwise, when ep_compressed_linear_prefill takes the blob and T (4096 or 8192 cols,
  * S = 8, T <= 256), that one (same result up to fp32 summation order; dev_ws unused).
  * x, y, bias and dev_ws must be
  * device, managed or pinned memory (EP_E_ARG otherwise, for every T, before any
@@ -224,7 +224,7 @@ int ep_compressed_matvec(const ep_blob* w, const void* dev_x, int64_t T, const v
  * the method targets prefill, where a GEMM follows the decode): y = x W^T (+ bias) with
  * every K slab of W's BF16 weights decoded into an LDS operand tile that MFMAs multiply
  * by the activations, so the weights are decoded once and never written to memory.
- * Takes lossy BF16 blobs of exactly 4096 cols at S = 8 (one tile per row) and
+ * Takes lossy BF16 blobs of 4096 or 8192 cols at S = 8 (one or two tiles per row) and
  * 1 <= T <= 256; EP_E_ARG otherwise (ep_compressed_linear_forward covers the rest).
  * x is T x 4096 BF16 (16-byte aligned), y is T x rows BF16 (8-byte aligned), bias rows
  * BF16 or NULL; all device, managed or pinned memory (EP_E_ARG otherwise, before any

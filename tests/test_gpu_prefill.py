@@ -1,11 +1,12 @@
 """GPU tests of the fused prefill product (ep_compressed_linear_prefill): y = x W^T + b for
-1..256 activation rows with each K slab of W decoded into an LDS operand tile of an MFMA
-product, against the float64 oracle product of the oracle's decoded weights.
+1..256 activation rows and 4096 or 8192 columns, with each K slab of W decoded into an LDS
+operand tile of an MFMA product, against the float64 oracle product of the oracle's
+decoded weights.
 
 The weights the product uses are the BF16 container values (bit-exact against the oracle
 in the decode tests); only the fp32 accumulation order differs from the oracle's exact
 sum.  Bound per output element: half a BF16 ulp of the result (<= 2^-8 |y|) plus the fp32
-summation error, far below 2^-14 sum_i |x_i w_i| for 4096 products.  A slab written to
+summation error, far below 2^-14 sum_i |x_i w_i| for 4096 or 8192 products.  A slab written to
 the wrong rows or columns, a dropped group of 8 weights or a wrong activation row moves
 an output by about 8/4096 of that sum or more, far outside the bound."""
 import numpy as np
@@ -48,7 +49,7 @@ def _run(blob, T, seed, with_bias, x_log2=0):
     import torch
     from decode_tile_rans_amd import _lib as L
     _, w_hat, _ = oracle.decode(blob)
-    R = w_hat.shape[0]
+    R, C = w_hat.shape
     x = synth.activations(T, C, seed + 1)
     if x_log2:   # (scaled by a power of two: exact in BF16)
         x = synth.f32_to_bf16_bits((nx.bf16_to_f64(x) * 2.0 ** x_log2).astype(np.float32))
@@ -89,6 +90,23 @@ def test_prefill_matches_oracle(R, T, bpp, seed):
     b = oracle.parse_blob(blob)
     if bpp >= 8:
         assert b.flags & 1    # escape symbols exercised
+    _run(blob, T, seed, seed % 2 == 1)
+
+
+# 8192 columns (two tiles a row: 32 rows of W a workgroup, two K segments a slab)
+CASES_8192 = [
+    (32, 16, 4.0, 221),
+    (100, 128, 4.0, 222),
+    (70, 129, 3.0, 223),
+    (40, 256, 5.0, 224),
+    (36, 50, 8.0, 225),
+]
+
+
+@pytest.mark.parametrize("R,T,bpp,seed", CASES_8192)
+def test_prefill_8192_columns(R, T, bpp, seed):
+    say("prefill 8192", R, T, bpp, seed)
+    blob = oracle.compress(synth.rowscaled(R, 2 * C, seed), nx.DT_BF16, bpp, chains_per_tile=8)
     _run(blob, T, seed, seed % 2 == 1)
 
 
@@ -153,6 +171,7 @@ def test_prefill_refusals():
         L.ep_compressed_linear_prefill(db.h, xh.ctypes.data, 8, 0, y.data_ptr(), stream_ptr())
     # other widths, chains per tile other than 8, FP16 blobs: not taken
     for b in (oracle.compress(synth.rowscaled(64, 2048, 212), nx.DT_BF16, 4.0, chains_per_tile=8),
+              oracle.compress(synth.rowscaled(16, 3 * C, 212), nx.DT_BF16, 4.0, chains_per_tile=8),
               oracle.compress(synth.rowscaled(64, C, 212), nx.DT_BF16, 4.0, chains_per_tile=4),
               oracle.compress((np.random.default_rng(9).standard_normal((64, C)) * 0.02).astype(np.float16)
                               .view(np.uint16), nx.DT_FP16, 4.0, chains_per_tile=8)):
