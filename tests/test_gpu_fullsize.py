@@ -210,15 +210,16 @@ def test_fused_linear_full_size():
 
 
 @pytest.mark.timeout(600)
-def test_fused_prefill_full_size():
-    # the 14336 x 4096 layer at 256 tokens through the fused prefill product (what the
-    # linear entry takes at this size): every output element within the bound of the
-    # float64 product with the oracle's decoded weights
+@pytest.mark.parametrize("R,C,T,seed", [(14336, 4096, 256, 5), (8192, 8192, 96, 6)])
+def test_fused_prefill_full_size(R, C, T, seed):
+    # the 14336 x 4096 layer at 256 tokens and an 8192 x 8192 one (two tiles a row) at 96
+    # through the fused prefill product (what the linear entry takes at these sizes):
+    # every output element within the bound of the float64 product with the oracle's
+    # decoded weights
     import torch
     from decode_tile_rans_amd import _lib as L
-    R, C, T = 14336, 4096, 256
     say("fused prefill full size: encode", R, C, T)
-    wbits = synth.rowscaled(R, C, 5)
+    wbits = synth.rowscaled(R, C, seed)
     h = _product_blob(wbits, nx.DT_BF16, 4.0)
     try:
         blob = L.ep_serialize(h)
