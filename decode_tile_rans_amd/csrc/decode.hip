@@ -102,6 +102,8 @@ struct DecJob {
   // sums out[(chain * mv_slots + row - first row of the chain) * tokens + t]
   const uint16_t* mv_x;
   uint32_t mv_T, mv_slots, mv_sat;
+  uint32_t mv_direct;          // rows of whole tiles: the product is summed in the wave, out = y
+  uint32_t mv_lanes;           // lanes of one row (8 per tile) when mv_direct
   const uint16_t* bias;        // fused prefill product: BF16 bias of the R outputs, or null
   uint32_t big_h;              // some |128 h_r| overflows float: reconstruct as h u
 };
@@ -1330,9 +1332,37 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
     }
   }
   if constexpr (NT > 0) {
+    if (J.mv_direct) {
+      // rows of whole tiles (S = 8, one or two tiles a row): a row's running sums sit in
+      // mv_lanes consecutive lanes of this wave (its tiles' chains in order), each chain
+      // having stayed on the row; the row's first lane adds them in the finishing
+      // kernel's order (tiles, then chains, from 0), adds the bias and rounds to BF16
+      static_assert(ILP == 1, "the fused product runs one chain per lane");
+      const int l0 = lane & ~(int)(J.mv_lanes - 1u);
+      const int64_t row = (blk0 * 64 + l0) / (int64_t)J.mv_lanes;
+      // (lanes outer, activation rows inner: the NT sums advance side by side)
+      float sum[NT];
 #pragma unroll
-    for (int c = 0; c < ILP; ++c)
-      if (live[c] && ngr[c] > 0) mv_flush<NT>(J, mv[c]);
+      for (int t = 0; t < NT; ++t) sum[t] = 0.f;
+#pragma unroll 8
+      for (int q = 0; q < (int)J.mv_lanes; ++q) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sum[t] += __shfl(mv[0].a[t], l0 + q, 64);
+      }
+      if (lane == l0 && row < (int64_t)J.R) {
+        const float bb = J.bias ? __uint_as_float((uint32_t)J.bias[row] << 16) : 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if ((uint32_t)t >= J.mv_T) break;
+          const __bf16 o = (__bf16)(J.bias ? sum[t] + bb : sum[t]);
+          ((uint16_t*)J.out)[(int64_t)t * J.R + row] = __builtin_bit_cast(uint16_t, o);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < ILP; ++c)
+        if (live[c] && ngr[c] > 0) mv_flush<NT>(J, mv[c]);
+    }
   }
 #pragma unroll
   for (int c = 0; c < ILP; ++c)
@@ -1760,6 +1790,15 @@ size_t matvec_workspace_bytes(const Blob& b, int64_t T) {
   return (size_t)b.n_chains * (size_t)matvec_slots(b) * (size_t)nt * 4 + 256;
 }
 
+// Rows of whole tiles (4096 or 8192 columns at S = 8): a row's chains sit in one wave, so
+// the decode kernel sums them itself (same order and bits as matvec_finish_kernel) and no
+// finishing launch follows.  EP_MATVEC_DIRECT=0 keeps the finishing kernel (comparisons).
+bool matvec_direct(const Blob& b) {
+  if (const char* e = std::getenv("EP_MATVEC_DIRECT"))
+    if (std::atoi(e) == 0) return false;
+  return b.S == 8 && (b.C == 8 * kTileGroups || b.C == 16 * kTileGroups);
+}
+
 bool matvec_supported(const Blob& b, int64_t T) {
   return b.kind == kKindLossy && b.dtype == EP_BF16 && T >= 1 && T <= kMatvecMaxT && b.C % 8 == 0 &&
          b.S <= (b.C + 7) / 8;
@@ -1810,11 +1849,15 @@ int matvec_batch_launch(const Blob* const* bs, int n, const void* x, int64_t T, 
       for (int q = 0; q < B.n; ++q) {
         const int i = idx[q];
         const Blob& b = *bs[i];
-        DecJob j = make_job(b, part[i]);
+        const bool direct = matvec_direct(b);
+        DecJob j = make_job(b, direct ? y[i] : (void*)part[i]);
         j.mv_x = (const uint16_t*)x;
         j.mv_T = (uint32_t)T;
         j.mv_slots = (uint32_t)matvec_slots(b);
         j.mv_sat = (b.flags & kFlagSat) ? 1u : 0u;
+        j.mv_direct = direct ? 1u : 0u;
+        j.mv_lanes = (uint32_t)(b.C / (8 * kTileGroups)) * 8u;
+        j.bias = (const uint16_t*)(bias ? bias[i] : nullptr);
         j.wg_begin = wg;
         wg += (j.n_blocks + sh.bpw - 1) / sh.bpw;
         B.j[q] = j;
@@ -1824,6 +1867,7 @@ int matvec_batch_launch(const Blob* const* bs, int n, const void* x, int64_t T, 
   }
   for (int i = 0; i < n; ++i) {
     const Blob& b = *bs[i];
+    if (matvec_direct(b)) continue;   // summed inside the decode kernel
     hipLaunchKernelGGL(matvec_finish_kernel, dim3((unsigned)((b.R + 255) / 256), (unsigned)T), dim3(256), 0, st, part[i],
                        (const uint16_t*)(bias ? bias[i] : nullptr), (uint16_t*)y[i], T, b.R, (int64_t)((b.C + 7) / 8),
                        (int)__builtin_ctz((unsigned)b.S), b.n_groups(), matvec_slots(b), nt);

@@ -321,3 +321,31 @@ def test_linear_falls_back_when_product_not_taken():
     L.ep_compressed_linear_forward(db.h, xt.data_ptr(), T, 0, y.data_ptr(), ws.data_ptr(), need, stream_ptr())
     torch.cuda.synchronize()
     _check(_bits(y), x, w_hat, None)
+
+
+@pytest.mark.parametrize("R,C,T", [(200, 4096, 1), (130, 4096, 3), (96, 8192, 8), (40, 8192, 5)])
+def test_matvec_rows_of_whole_tiles_summed_in_kernel(R, C, T, monkeypatch):
+    """Rows of whole tiles (4096 / 8192 columns at S = 8): the decode kernel adds a row's
+    chain sums itself, in the finishing kernel's order, so the output equals the
+    two-kernel path bit for bit and stays within the oracle bound."""
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    say("matvec in-kernel sums", R, C, T)
+    blob = oracle.compress(synth.rowscaled(R, C, 120 + T), nx.DT_BF16, 4.0, chains_per_tile=8)
+    _, w_hat, _ = oracle.decode(blob)
+    x = synth.activations(T, C, 121)
+    bias = synth.f32_to_bf16_bits(np.linspace(-0.5, 0.5, R).astype(np.float32))
+    db = DevBlob(blob)
+    xt, bt = _t(x, torch.bfloat16), _t(bias, torch.bfloat16)
+    need = L.ep_matvec_workspace_bytes(db.h, T)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ys = []
+    for flag in ("1", "0"):
+        monkeypatch.setenv("EP_MATVEC_DIRECT", flag)
+        y = torch.full((T, R), 7.0, dtype=torch.bfloat16, device="cuda")
+        L.ep_compressed_matvec(db.h, xt.data_ptr(), T, bt.data_ptr(), y.data_ptr(), ws.data_ptr(), need, stream_ptr())
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
+    _check(_bits(ys[0]), x, w_hat, bias)
+    assert db.errors() == 0
