@@ -527,17 +527,18 @@ def small_batch(c, w, x, ws, need, wd, sp, timeit):
     def best(fn):
         return min(timeit(fn) for _ in range(3))
 
-    for T in (1, 2, 4, 8):
+    for T in (1, 2, 4, 5, 8):
         xs = x[:T].contiguous()
         y = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
         nmv = L.ep_matvec_workspace_bytes(c.handle, T)
         t_mv = best(lambda: L.ep_compressed_matvec(c.handle, xs.data_ptr(), T, None, y.data_ptr(), ws.data_ptr(),
                                                      nmv, sp))
+        t_pf = best(lambda: L.ep_compressed_linear_prefill(c.handle, xs.data_ptr(), T, None, y.data_ptr(), sp))
         t_two = best(lambda: (L.ep_decompress(c.handle, wd, sp),
                                 L.ep_gemm_bf16_nt(xs.data_ptr(), wd, None, y.data_ptr(), T, R, C, sp)))
         t_plain = best(lambda: torch.matmul(xs, w.t()))
-        out.append({"tokens": T, "ms_fused": round(t_mv, 4), "ms_decode_then_gemm": round(t_two, 4),
-                    "ms_hipblaslt_plain_bf16": round(t_plain, 4),
+        out.append({"tokens": T, "ms_fused": round(t_mv, 4), "ms_fused_prefill_kernel": round(t_pf, 4),
+                    "ms_decode_then_gemm": round(t_two, 4), "ms_hipblaslt_plain_bf16": round(t_plain, 4),
                     "fused_speedup_vs_decode_then_gemm": round(t_two / t_mv, 3),
                     "fused_blob_gbs": round(c.nbytes / (t_mv * 1e-3) / 1e9, 1),
                     "plain_weight_gbs": round(2.0 * R * C / (t_plain * 1e-3) / 1e9, 1)})

@@ -1344,7 +1344,6 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
       float sum[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) sum[t] = 0.f;
-#pragma unroll 8
       for (int q = 0; q < (int)J.mv_lanes; ++q) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) sum[t] += __shfl(mv[0].a[t], l0 + q, 64);

@@ -174,7 +174,8 @@ int64_t ep_blob_device_errors(const ep_blob* blob);
  * (>= ep_linear_workspace_bytes bytes), then an MFMA BF16 GEMM with fp32
  * accumulation runs on the same stream.  With T <= 8, when ep_compressed_matvec takes
  * the blob and its partial sums fit ep_linear_workspace_bytes, that fused product runs
- * instead; otherwise, when ep_compressed_linear_prefill takes the blob and T (4096 or 8192 cols,
+ * instead (for T >= 5 only where ep_compressed_linear_prefill does not take it);
+ * otherwise, when ep_compressed_linear_prefill takes the blob and T (4096 or 8192 cols,
  * S = 8, T <= 256), that one (same result up to fp32 summation order; dev_ws unused).
  * x, y, bias and dev_ws must be
  * device, managed or pinned memory (EP_E_ARG otherwise, for every T, before any

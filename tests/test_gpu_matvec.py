@@ -86,14 +86,16 @@ def test_matvec_matches_oracle(R, C, T, bpp, S, seed):
     L.ep_compressed_matvec(db.h, xt.data_ptr(), T, bp, y.data_ptr(), ws.data_ptr(), need, stream_ptr())
     torch.cuda.synchronize()
     assert np.array_equal(_bits(y), first)
-    # the linear layer entry takes the fused path when its partial sums fit its workspace,
-    # else decodes and runs the GEMM (same result within the bound)
+    # the linear layer entry takes the fused path when its partial sums fit its workspace
+    # (5-8 rows of whole-tile rows: the fused prefill product), else decodes and runs the
+    # GEMM (same result within the bound)
     n1 = L.ep_linear_workspace_bytes(db.h)
     w1 = torch.empty(n1, dtype=torch.uint8, device="cuda")
     y1 = torch.empty_like(y)
     L.ep_compressed_linear_forward(db.h, xt.data_ptr(), T, bp, y1.data_ptr(), w1.data_ptr(), n1, stream_ptr())
     torch.cuda.synchronize()
-    if need <= n1:
+    prefill = T > 4 and S == 8 and C in (4096, 8192)
+    if need <= n1 and not prefill:
         assert np.array_equal(_bits(y1), first)
     else:
         _check(_bits(y1), x, w_hat, bias)
