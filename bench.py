@@ -423,6 +423,7 @@ def fused_linear(target_bpp, reps=10):
     small = small_batch(c, w, x, ws, need, wd, sp, timeit)
     prefill = prefill_fused(c, w, x, wd, sp, timeit)
     sweep = token_sweep(c, w, ws, need, sp, timeit)
+    s16 = chains_per_tile_16(c, w, x, target_bpp, sp, timeit)
     return {
         "workload": "CompressedLinear prefill 14336x4096 weight @%.1f bpp, 4096 tokens" % target_bpp,
         "actual_bpp": round(c.actual_bpp, 4),
@@ -436,7 +437,49 @@ def fused_linear(target_bpp, reps=10):
         "small_batch": small,
         "prefill_fused": prefill,
         "token_sweep": sweep,
+        "chains_per_tile_8_vs_16": s16,
     }
+
+
+def chains_per_tile_16(c8, w, x, target_bpp, sp, timeit):
+    """The same weight encoded with 16 chains per tile instead of 8: half the symbols per
+    chain (a lone launch is bound by that depth) for a larger blob.  Lone decode, the
+    one-token product and decode + GEMM at the activations' token count, the two blobs
+    timed in alternating rounds (best of three each)."""
+    import torch
+    import decode_tile_rans_amd as ep
+    from decode_tile_rans_amd import _lib as L
+    R, C = w.shape
+    T = x.shape[0]
+    c16 = ep.compress(w, target_bpp, chains_per_tile=16, stream=torch.cuda.current_stream())
+    c16.upload()
+    need = max(L.ep_linear_workspace_bytes(c.handle) for c in (c8, c16))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    dec = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    y1 = torch.empty((1, R), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
+    fns = {}
+    for S, c in ((8, c8), (16, c16)):
+        h = c.handle
+        fns[(S, "ms_decode")] = lambda h=h: L.ep_decompress(h, dec.data_ptr(), sp)
+        fns[(S, "ms_fused_1_token")] = lambda h=h: L.ep_compressed_linear_forward(
+            h, x.data_ptr(), 1, None, y1.data_ptr(), ws.data_ptr(), need, sp)
+        fns[(S, "ms_decode_plus_gemm")] = lambda h=h: L.ep_compressed_linear_forward(
+            h, x.data_ptr(), T, None, y.data_ptr(), ws.data_ptr(), need, sp)
+    fns[("plain", "ms_gemm_plain_bf16")] = lambda: L.ep_gemm_bf16_nt(x.data_ptr(), w.data_ptr(), None, y.data_ptr(),
+                                                                     T, R, C, sp)
+    best = {k: float("inf") for k in fns}
+    for _ in range(3):
+        for k, f in fns.items():
+            best[k] = min(best[k], timeit(f))
+    torch.cuda.synchronize()
+    if c16.device_errors():
+        raise SystemExit("decode of the 16-chain blob reported failed chains")
+    out = {"tokens": T, "ms_gemm_plain_bf16": round(best[("plain", "ms_gemm_plain_bf16")], 4)}
+    for S, c in ((8, c8), (16, c16)):
+        out[f"chains_{S}"] = {"actual_bpp": round(c.actual_bpp, 4),
+                              **{k: round(v, 4) for (s, k), v in best.items() if s == S}}
+    return out
 
 
 def token_sweep(c, w, ws, need, sp, timeit):

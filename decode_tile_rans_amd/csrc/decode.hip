@@ -103,7 +103,7 @@ struct DecJob {
   const uint16_t* mv_x;
   uint32_t mv_T, mv_slots, mv_sat;
   uint32_t mv_direct;          // rows of whole tiles: the product is summed in the wave, out = y
-  uint32_t mv_lanes;           // lanes of one row (8 per tile) when mv_direct
+  uint32_t mv_lanes;           // lanes of one row (S per tile) when mv_direct
   const uint16_t* bias;        // fused prefill product: BF16 bias of the R outputs, or null
   uint32_t big_h;              // some |128 h_r| overflows float: reconstruct as h u
 };
@@ -1333,7 +1333,7 @@ __device__ __forceinline__ void decode_blocks(const GroupCtx& X, int64_t blk0, i
   }
   if constexpr (NT > 0) {
     if (J.mv_direct) {
-      // rows of whole tiles (S = 8, one or two tiles a row): a row's running sums sit in
+      // rows of whole tiles (S = 8 or 16, one or two tiles a row): a row's running sums sit in
       // mv_lanes consecutive lanes of this wave (its tiles' chains in order), each chain
       // having stayed on the row; the row's first lane adds them in the finishing
       // kernel's order (tiles, then chains, from 0), adds the bias and rounds to BF16
@@ -1795,7 +1795,8 @@ size_t matvec_workspace_bytes(const Blob& b, int64_t T) {
 bool matvec_direct(const Blob& b) {
   if (const char* e = std::getenv("EP_MATVEC_DIRECT"))
     if (std::atoi(e) == 0) return false;
-  return b.S == 8 && (b.C == 8 * kTileGroups || b.C == 16 * kTileGroups);
+  // (a row's chains, S per tile, one or two tiles a row, fill 8 to 32 consecutive lanes)
+  return (b.S == 8 || b.S == 16) && (b.C == 8 * kTileGroups || b.C == 16 * kTileGroups);
 }
 
 bool matvec_supported(const Blob& b, int64_t T) {
@@ -1855,7 +1856,7 @@ int matvec_batch_launch(const Blob* const* bs, int n, const void* x, int64_t T, 
         j.mv_slots = (uint32_t)matvec_slots(b);
         j.mv_sat = (b.flags & kFlagSat) ? 1u : 0u;
         j.mv_direct = direct ? 1u : 0u;
-        j.mv_lanes = (uint32_t)(b.C / (8 * kTileGroups)) * 8u;
+        j.mv_lanes = (uint32_t)(b.C / (8 * kTileGroups)) * (uint32_t)b.S;
         j.bias = (const uint16_t*)(bias ? bias[i] : nullptr);
         j.wg_begin = wg;
         wg += (j.n_blocks + sh.bpw - 1) / sh.bpw;

@@ -216,7 +216,7 @@ int ep_compressed_linear_seq_forward(const ep_blob* const* w, int n, const void*
  * in dev_ws (>= ep_matvec_workspace_bytes(w, T) bytes, which returns 0 when the blob or
  * T is not taken); a second kernel adds a row's partial sums in a fixed order, adds the
  * bias and rounds to BF16, so repeated calls give identical bits.  For rows of whole
- * tiles (4096 or 8192 cols at S = 8) a row's chains share one wavefront and the decode
+ * tiles (4096 or 8192 cols at S = 8 or 16) a row's chains share one wavefront and the decode
  * kernel adds their sums itself, in the same order (same bits; dev_ws unused).
  * Asynchronous. */
 size_t ep_matvec_workspace_bytes(const ep_blob* w, int64_t T);

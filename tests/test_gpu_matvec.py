@@ -325,15 +325,16 @@ def test_linear_falls_back_when_product_not_taken():
     _check(_bits(y), x, w_hat, None)
 
 
-@pytest.mark.parametrize("R,C,T", [(200, 4096, 1), (130, 4096, 3), (96, 8192, 8), (40, 8192, 5)])
-def test_matvec_rows_of_whole_tiles_summed_in_kernel(R, C, T, monkeypatch):
-    """Rows of whole tiles (4096 / 8192 columns at S = 8): the decode kernel adds a row's
+@pytest.mark.parametrize("R,C,T,S", [(200, 4096, 1, 8), (130, 4096, 3, 8), (96, 8192, 8, 8), (40, 8192, 5, 8),
+                                     (200, 4096, 1, 16), (70, 4096, 4, 16), (96, 8192, 2, 16), (33, 8192, 7, 16)])
+def test_matvec_rows_of_whole_tiles_summed_in_kernel(R, C, T, S, monkeypatch):
+    """Rows of whole tiles (4096 / 8192 columns at S = 8 or 16): the decode kernel adds a row's
     chain sums itself, in the finishing kernel's order, so the output equals the
     two-kernel path bit for bit and stays within the oracle bound."""
     import torch
     from decode_tile_rans_amd import _lib as L
-    say("matvec in-kernel sums", R, C, T)
-    blob = oracle.compress(synth.rowscaled(R, C, 120 + T), nx.DT_BF16, 4.0, chains_per_tile=8)
+    say("matvec in-kernel sums", R, C, T, S)
+    blob = oracle.compress(synth.rowscaled(R, C, 120 + T), nx.DT_BF16, 4.0, chains_per_tile=S)
     _, w_hat, _ = oracle.decode(blob)
     x = synth.activations(T, C, 121)
     bias = synth.f32_to_bf16_bits(np.linspace(-0.5, 0.5, R).astype(np.float32))
