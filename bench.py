@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true", help="skip the 8192^2 container and chains-per-tile sweep")
     p.add_argument("--matrices", type=int, default=276, help="first N matrices of the stack (profiling runs)")
     p.add_argument("--streams", type=int, default=3, help="HIP streams the block launches rotate over")
+    p.add_argument("--chains-per-tile", type=int, default=0,
+                   help="chains per tile of the stack's blobs (0: the encoder's choice, 8 for these sizes)")
     p.add_argument("--gemm-only", action="store_true",
                    help="only run the BF16 and FP8 GEMMs at 4096 x 14336 x 4096 and hipBLASLt (counter runs)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -189,7 +191,7 @@ def container_sweep(reps=10):
     return out
 
 
-def build_stack(n, target_bpp):
+def build_stack(n, target_bpp, chains_per_tile=0):
     """Draw the stack on the GPU and compress it there (the GPU encoder's batch entry,
     whose blobs equal the host encoder's byte for byte), upload the blobs."""
     import torch
@@ -200,7 +202,7 @@ def build_stack(n, target_bpp):
     comps = []
     for i0 in range(0, n, 32):
         ws = [synth.dit_stack_torch(i) for i in range(i0, min(n, i0 + 32))]
-        comps += ep.compress_many(ws, target_bpp)
+        comps += ep.compress_many(ws, target_bpp, chains_per_tile=chains_per_tile)
         del ws
     for c in comps:
         c.upload()
@@ -276,10 +278,16 @@ def time_stack(comps, blocks, outs, steps, warmup, per_layer=False, n_streams=1)
     return wall / steps * 1e3, launch_ms, units
 
 
+_COUNTERS_APPLY = [True]   # false when the stack's blobs differ from the counted ones
+
+
 def decode_counters():
     """The committed rocprofv3 counter summary of the decode kernel (HBM bytes and VALU
-    instructions per parameter), or None when the kernel source changed since then."""
+    instructions per parameter), or None when the kernel source changed since then (or
+    the stack is encoded with another chain count than the counted one)."""
     import hashlib
+    if not _COUNTERS_APPLY[0]:
+        return None
     try:
         info = json.load(open(os.path.join(ROOT, "profiles", "decode_traffic.json")))
         src = open(os.path.join(ROOT, "decode_tile_rans_amd", "csrc", "decode.hip"), "rb").read()
@@ -836,7 +844,8 @@ def main():
     if a.gemm_only:
         gemm_only()
         return
-    comps, blocks = build_stack(a.matrices, a.target_bpp)
+    comps, blocks = build_stack(a.matrices, a.target_bpp, a.chains_per_tile)
+    _COUNTERS_APPLY[0] = comps[0].chains_per_tile == 8
     outs = [torch.empty(c.shape, dtype=torch.bfloat16, device="cuda") for c in comps]
     n_params = sum(c.shape[0] * c.shape[1] for c in comps)
     blob_bytes = sum(c.nbytes for c in comps)
@@ -871,7 +880,7 @@ def main():
                    "actual_bpp": round(8.0 * blob_bytes / n_params, 4),
                    "resident_bpp": round(8.0 * sum(c.device_bytes for c in comps) / n_params, 4),
                    "launches_per_step": len(units),
-                   "streams": a.streams},
+                   "streams": a.streams, "chains_per_tile": comps[0].chains_per_tile},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (lambda t: round(t) if t else None)(traffic_per_launch(n_params / len(units))),
