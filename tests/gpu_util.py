@@ -101,9 +101,10 @@ def linear_bound(ref, mag, K, scale_roundings=0):
 
 
 def check_linear(got, ref, mag, K, scale_roundings=0):
-    """Every output within linear_bound; names the first offending element."""
+    """Every output within linear_bound; names the first offending element.  A NaN in
+    the output, the reference or the bound counts as a failure (never a vacuous pass)."""
     err = np.abs(np.asarray(got, np.float64) - ref)
     bound = linear_bound(ref, mag, K, scale_roundings)
-    bad = np.argwhere(err > bound)
+    bad = np.argwhere(~(err <= bound))
     assert bad.size == 0, (f"{len(bad)} of {err.size} outputs off, first {tuple(bad[0])}: "
                            f"got {got[tuple(bad[0])]} ref {ref[tuple(bad[0])]} bound {bound[tuple(bad[0])]}")

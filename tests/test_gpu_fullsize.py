@@ -64,7 +64,7 @@ def _coords(h, R, C):
 
 def _full_parity(h, got_bits, dt, what):
     """Every element and coordinate of a device decode against the oracle's decode of
-    the same blob."""
+    the same blob; returns (blob, coordinates, container values)."""
     from decode_tile_rans_amd import _lib as L
     blob = L.ep_serialize(h)
     say("oracle decode", what, len(blob))
@@ -199,7 +199,7 @@ def test_fused_linear_full_size():
         # the decoded weights the GEMM read: the 256-byte aligned start of the workspace
         off = (256 - ws.data_ptr() % 256) % 256
         wdec = ws[off:off + 2 * R * C].cpu().numpy().view(np.uint16).reshape(R, C)
-        _, w_hat, _ = _full_parity(h, wdec, nx.DT_BF16, "14336x4096 linear weight")
+        _, _, w_hat = _full_parity(h, wdec, nx.DT_BF16, "14336x4096 linear weight")   # (blob, coords, weights)
         rows = np.random.default_rng(1).choice(T, 256, replace=False)
         xf, wf = nx.bf16_to_f64(xb[rows]), nx.bf16_to_f64(w_hat)
         ref = linear_ref(xf, wf)
@@ -240,6 +240,45 @@ def test_fused_prefill_full_size(R, C, T, seed):
         assert L.ep_blob_device_errors(h) == 0
     finally:
         L.ep_blob_free(h)
+
+
+@pytest.mark.timeout(600)
+def test_sixteen_chains_full_size():
+    # the 14336 x 4096 layer encoded with 16 chains per tile: every decoded weight and
+    # coordinate against the oracle's decode of the same blob, and the fused product on
+    # 1 and 3 tokens (rows summed inside the decode kernel) within the float64 bound
+    import torch
+    from decode_tile_rans_amd import _lib as L
+    R, C = 14336, 4096
+    say("16 chains per tile full size: encode", R, C)
+    wbits = synth.rowscaled(R, C, 5)
+    h = _product_blob(wbits, nx.DT_BF16, 4.0, 16)
+    try:
+        assert L.ep_blob_params(h)[0] == 16
+        data = L.ep_serialize(h)
+    finally:
+        L.ep_blob_free(h)
+    db = DevBlob(data)
+    full = db.decode()
+    _, _, w_hat = _full_parity(db.h, full, nx.DT_BF16, "14336x4096 at S = 16")
+    wf = nx.bf16_to_f64(w_hat)
+    bias = synth.f32_to_bf16_bits(np.linspace(-1.0, 1.0, R).astype(np.float32))
+    bt = torch.from_numpy(bias).view(torch.bfloat16).cuda()
+    for T in (1, 3):
+        say("16 chains per tile full size: product", T)
+        xb = synth.activations(T, C, 53 + T)
+        x = torch.from_numpy(xb).view(torch.bfloat16).cuda()
+        y = torch.full((T, R), 7.0, dtype=torch.bfloat16, device="cuda")
+        need = L.ep_linear_workspace_bytes(db.h)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        L.ep_compressed_linear_forward(db.h, x.data_ptr(), T, bt.data_ptr(), y.data_ptr(), ws.data_ptr(), need,
+                                       stream_ptr())
+        torch.cuda.synchronize()
+        xf = nx.bf16_to_f64(xb)
+        ref = linear_ref(xf, wf, nx.bf16_to_f64(bias))
+        mag = np.abs(xf) @ np.abs(wf).T
+        check_linear(nx.bf16_to_f64(to_np(y, nx.DT_BF16)), ref, mag, C)
+    assert db.errors() == 0
 
 
 SWEEP = [("bf16@2.3", nx.DT_BF16, 2.3), ("bf16@3.0", nx.DT_BF16, 3.0), ("bf16@5.0", nx.DT_BF16, 5.0),

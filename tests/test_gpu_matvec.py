@@ -37,7 +37,7 @@ def _check(got_bits, x, w_hat, bias):
     got = nx.bf16_to_f64(got_bits)
     err = np.abs(got - ref)
     bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -14 * mag + 1e-30
-    bad = np.argwhere(err > bound)
+    bad = np.argwhere(~(err <= bound))   # a NaN anywhere fails
     assert bad.size == 0, f"{len(bad)} outputs off, first {bad[0]}: got {got[tuple(bad[0])]} ref {ref[tuple(bad[0])]}"
 
 
