@@ -431,7 +431,7 @@ def fused_linear(target_bpp, reps=10):
     small = small_batch(c, w, x, ws, need, wd, sp, timeit)
     prefill = prefill_fused(c, w, x, wd, sp, timeit)
     sweep = token_sweep(c, w, ws, need, sp, timeit)
-    s16 = chains_per_tile_16(c, w, x, target_bpp, sp, timeit)
+    s16 = chains_per_tile_8_vs_16(c, w, x, target_bpp, sp, timeit)
     return {
         "workload": "CompressedLinear prefill 14336x4096 weight @%.1f bpp, 4096 tokens" % target_bpp,
         "actual_bpp": round(c.actual_bpp, 4),
@@ -449,7 +449,7 @@ def fused_linear(target_bpp, reps=10):
     }
 
 
-def chains_per_tile_16(c8, w, x, target_bpp, sp, timeit):
+def chains_per_tile_8_vs_16(c8, w, x, target_bpp, sp, timeit):
     """The same weight encoded with 16 chains per tile instead of 8: half the symbols per
     chain (a lone launch is bound by that depth) for a larger blob.  Lone decode, the
     one-token product and decode + GEMM at the activations' token count, the two blobs
