@@ -56,6 +56,9 @@ CASES = [
     (37, 72, 7, 4.0, 8, 107),
     (96, 2048, 6, 5.0, 4, 108),
     (250, 1000, 8, 3.5, 2, 109),
+    (300, 3840, 3, 4.0, 16, 110),
+    (130, 1032, 5, 2.3, 16, 111),
+    (96, 2048, 1, 8.0, 16, 112),
 ]
 
 
