@@ -229,18 +229,20 @@ def _single(L, db, x, T, bias):
     return y
 
 
-@pytest.mark.parametrize("specs,T", [
+@pytest.mark.parametrize("specs,T,C", [
     # (rows, target bpp, chains per tile) sharing 768 columns: narrow and wide tables,
     # with and without escapes, several chain counts, in one call
-    ([(384, 4.0, 8), (640, 8.0, 8), (200, 2.3, 1), (1000, 5.0, 4)], 3),
+    ([(384, 4.0, 8), (640, 8.0, 8), (200, 2.3, 1), (1000, 5.0, 4)], 3, 768),
     # more blobs than one launch takes
-    ([(64 + 8 * i, 3.0 + 0.25 * (i % 4), 8) for i in range(14)], 1),
+    ([(64 + 8 * i, 3.0 + 0.25 * (i % 4), 8) for i in range(14)], 1, 768),
+    # rows of whole tiles (row sums in the decode kernel at 8 and 16 chains per tile)
+    # beside a blob whose sums take the finishing kernel, in one call
+    ([(96, 4.0, 8), (64, 4.0, 16), (40, 3.0, 4), (33, 5.0, 16)], 2, 4096),
 ])
-def test_matvec_batch_equals_single_calls(specs, T):
+def test_matvec_batch_equals_single_calls(specs, T, C):
     import torch
     from decode_tile_rans_amd import _lib as L
-    C = 768
-    say("matvec batch", len(specs), T)
+    say("matvec batch", len(specs), T, C)
     dbs, biases, blobs = [], [], []
     for i, (R, bpp, S) in enumerate(specs):
         blob = oracle.compress(synth.rowscaled(R, C, 200 + i), nx.DT_BF16, bpp, chains_per_tile=S)
